@@ -1,0 +1,164 @@
+"""Plain CPU definitions of the quantized linear layer (test infrastructure).
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg may use this
+module; the HIP library never imports it and it imports nothing from the HIP
+side.
+
+Sources (pages; each function cites the passage it follows):
+
+* [pymllm-setup]  "pymllm Setup and Usage" -- Overview (BF16, W4A16 and
+  W8A8_INT8 schemes; INT8 tensor-core compute), section "W8A8 first-run JIT
+  compilation" (per-token int8 activation quantizer; int8 scaled matmul).
+* [lmdeploy-ovw]  LMDeploy toolkit overview (devpress) -- section 2.5
+  "Weight quantization (AWQ)" (4-bit weights, group size 128).
+* [lmdeploy-hw]   "LMDeploy multimodal LLM 4-bit quantization deployment
+  guide" (mlqm) -- section 2.2 (AWQ w4a16; scale and weight consumed in one
+  kernel), section 3.2 (per-layer bits / group_size, -1 = no grouping).
+
+Layouts (all row-major, contiguous):
+    x        fp16  [M, K]        activations
+    qweight  int32 [K, N/8]      uint4 weights, 8 per word along N
+    scales   fp16  [K/G, N]      per-group scales
+    qzeros   int32 [K/G, N/8]    uint4 zero points, packed like qweight
+    xq       int8  [M, K]        quantized activations
+    s_tok    fp32  [M]           per-token scales
+    wq       int8  [N, K]        int8 weights, one row per output channel
+    s_ch     fp32  [N]           per-output-channel scales
+"""
+
+import numpy as np
+
+NIBBLES_PER_WORD = 8
+
+
+def unpack_int4(packed):
+    """Split each 32-bit word into its eight 4-bit fields.
+
+    Reading (the pages give no bit layout): field j of word c, counted from
+    the least significant bit, is column ``8*c + j``; fields are unsigned
+    (0..15). The same layout holds for weights and zero points.
+
+    packed: integer array [R, C] (int32 bit patterns) -> uint8 [R, 8*C].
+    """
+    packed = np.asarray(packed)
+    if packed.ndim != 2:
+        raise ValueError("packed must be 2-D")
+    words = packed.astype(np.int64) & 0xFFFFFFFF  # reinterpret as unsigned
+    rows, cols = words.shape
+    out = np.empty((rows, cols * NIBBLES_PER_WORD), dtype=np.uint8)
+    for j in range(NIBBLES_PER_WORD):
+        out[:, j::NIBBLES_PER_WORD] = (words >> (4 * j)) & 0xF
+    return out
+
+
+def dequant_w4(qweight, scales, qzeros, group):
+    """W4A16 group dequantization, w[k, n] = (q[k, n] - z[k // G, n]) * s[k // G, n].
+
+    [lmdeploy-ovw] section 2.5 and [lmdeploy-hw] section 2.2: asymmetric
+    4-bit weights with one scale and one zero point per group of G
+    consecutive input channels (k) of each output column n. G = 128 on the
+    pages; ``group = -1`` ([lmdeploy-hw] section 3.2) means one group
+    spanning all of K.
+
+    The product is formed in float32; it is exact there because |q - z| <= 15
+    and an fp16 scale has an 11-bit significand (pinned exhaustively in the
+    tests). Returns float32 [K, N].
+    """
+    q = unpack_int4(qweight).astype(np.float32)
+    K, N = q.shape
+    G = K if group == -1 else int(group)
+    if G <= 0 or K % G != 0:
+        raise ValueError("K must be a multiple of the group size")
+    z = unpack_int4(qzeros).astype(np.float32)
+    s = np.asarray(scales).astype(np.float32)
+    if z.shape != (K // G, N) or s.shape != (K // G, N):
+        raise ValueError("scales / qzeros shape does not match [K/G, N]")
+    g = np.arange(K) // G
+    return (q - z[g, :]) * s[g, :]
+
+
+def w4a16_ref(x, qweight, scales, qzeros, group):
+    """W4A16 linear layer, y = x @ W_deq, unrounded, in float64.
+
+    [lmdeploy-ovw] section 2.5 (4-bit weights with 16-bit activations) and
+    [pymllm-setup] Overview (the W4A16 scheme). Activations are fp16 and are
+    widened exactly; the dequantized weights are exact (``dequant_w4``); the
+    matmul accumulates in float64. The result is NOT rounded to fp16: a GPU
+    output is compared with this value directly.
+
+    x: fp16 [M, K] -> float64 [M, N].
+    """
+    w = dequant_w4(qweight, scales, qzeros, group).astype(np.float64)
+    xf = np.asarray(x).astype(np.float64)
+    if xf.ndim != 2 or xf.shape[1] != w.shape[0]:
+        raise ValueError("x must be [M, K]")
+    return xf @ w
+
+
+def quant_per_token_int8_ref(x):
+    """Dynamic symmetric per-token int8 quantization.
+
+    [pymllm-setup] Overview (W8A8_INT8 runs activations in int8) and section
+    "W8A8 first-run JIT compilation" (the per-token int8 quantizer that feeds
+    the int8 scaled matmul). For each row m of x (one token):
+
+        a[m]     = max_k |x[m, k]|                  (exact)
+        s[m]     = fl32(a[m] / 127)                 (IEEE binary32 divide)
+        q[m, k]  = clamp(rne(fl32(x[m, k] / s[m])), -127, 127)
+
+    Readings (the pages print no formula): divide by the scale rather than
+    multiply by 127/a; round half to even; clamp to [-127, 127] (-128 is
+    never produced); an all-zero row gets s = 0 and q = 0.
+
+    The same function quantizes int8 weights per output channel when it is
+    given the rows of W [N, K].
+
+    x: fp16 (or fp32) [M, K] -> (int8 [M, K], float32 [M]).
+    """
+    xf = np.asarray(x).astype(np.float32)
+    if xf.ndim != 2:
+        raise ValueError("x must be 2-D")
+    a = np.max(np.abs(xf), axis=1) if xf.shape[1] else np.zeros(xf.shape[0], np.float32)
+    s = np.divide(a, np.float32(127.0), dtype=np.float32)
+    q = np.zeros(xf.shape, dtype=np.int8)
+    nz = s > 0
+    if np.any(nz):
+        quotient = np.divide(xf[nz], s[nz, None], dtype=np.float32)
+        q[nz] = np.clip(np.rint(quotient), -127, 127).astype(np.int8)
+    return q, s.astype(np.float32)
+
+
+def w8a8_acc_ref(xq, wq):
+    """Integer accumulator acc[m, n] = sum_k xq[m, k] * wq[n, k].
+
+    [pymllm-setup] Overview (int8 x int8 products on INT8 tensor cores) and
+    section "W8A8 first-run JIT compilation" (int8 matmul). Computed as a
+    float64 matrix product: every product and every partial sum is an integer
+    of magnitude below 2**53, so each float64 operation is exact whatever the
+    summation order. The result must fit a signed 32-bit accumulator.
+
+    xq: int8 [M, K], wq: int8 [N, K] -> int64 [M, N].
+    """
+    a = np.asarray(xq).astype(np.float64)
+    b = np.asarray(wq).astype(np.float64)
+    if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError("xq must be [M, K] and wq [N, K]")
+    if a.shape[1] * 127 * 127 >= 2 ** 53:
+        raise ValueError("K too large for exact float64 accumulation")
+    acc = (a @ b.T).astype(np.int64)
+    if acc.size and np.max(np.abs(acc)) >= 2 ** 31:
+        raise OverflowError("accumulator exceeds int32")
+    return acc
+
+
+def w8a8_ref(xq, s_tok, wq, s_ch):
+    """W8A8 scaled matmul, y[m, n] = acc[m, n] * s_tok[m] * s_ch[n], unrounded float64.
+
+    [pymllm-setup] section "W8A8 first-run JIT compilation": the int8 GEMM
+    with a scale epilogue ("scaled_mm"); per-token activation scales and
+    per-output-channel weight scales. Not rounded to fp16.
+    """
+    acc = w8a8_acc_ref(xq, wq).astype(np.float64)
+    st = np.asarray(s_tok).astype(np.float64)
+    sc = np.asarray(s_ch).astype(np.float64)
+    return acc * st[:, None] * sc[None, :]

@@ -1,0 +1,383 @@
+"""Pins for the CPU oracle: checks against values that do not come from it.
+
+Each ``check_*`` takes the oracle function(s) under test as arguments, so the
+same check runs on the real oracle (it must pass) and on copies with a
+planted mistake (it must fail; see ``test_oracle.py``). Nothing here calls
+the oracle's own helpers to produce an expected value: expected values come
+from hand-written fixtures under ``tests/golden/``, independent pure-Python
+loops, exact rational arithmetic (``fractions.Fraction``), closed forms and
+special cases that reduce to a textbook matmul.
+"""
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ----------------------------------------------------------------------------
+# independent helpers (pure Python ints / Fractions; no NumPy arithmetic)
+# ----------------------------------------------------------------------------
+
+def loop_pack(fields):
+    """Pack a [R, 8C] array of 0..15 values into int32 [R, C]; field j of word c = column 8c+j."""
+    fields = [[int(v) for v in row] for row in np.asarray(fields)]
+    rows = len(fields)
+    cols = len(fields[0]) // 8 if rows else 0
+    out = np.zeros((rows, cols), dtype=np.int32)
+    for r in range(rows):
+        for c in range(cols):
+            word = 0
+            for j in range(8):
+                v = fields[r][8 * c + j]
+                assert 0 <= v <= 15
+                word |= v << (4 * j)
+            if word >= 2 ** 31:
+                word -= 2 ** 32
+            out[r, c] = word
+    return out
+
+
+def loop_field(word, j):
+    """Field j of a 32-bit word, computed on a Python int."""
+    return (int(word) & 0xFFFFFFFF) >> (4 * j) & 0xF
+
+
+def round_half_even(fr):
+    """Nearest integer to a Fraction, ties to even."""
+    fl = math.floor(fr)
+    rem = fr - fl
+    if rem > Fraction(1, 2):
+        return fl + 1
+    if rem < Fraction(1, 2):
+        return fl
+    return fl if fl % 2 == 0 else fl + 1
+
+
+def round_to_binary32(fr):
+    """Correctly rounded IEEE binary32 value (ties to even) of a Fraction in the normal range."""
+    if fr == 0:
+        return Fraction(0)
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    assert -126 <= e <= 127, "outside the normal binary32 range"
+    ulp = Fraction(2) ** (e - 23)
+    m = round_half_even(a / ulp)
+    return sign * m * ulp
+
+
+def exact_quant_row(xs):
+    """Per-token quantization of one row, evaluated in exact rational arithmetic.
+
+    s = binary32(absmax / 127); q = clamp(rne(binary32(x / s)), -127, 127).
+    """
+    fx = [Fraction(float(v)) for v in xs]
+    a = max(abs(v) for v in fx)
+    if a == 0:
+        return [0] * len(fx), Fraction(0)
+    s = round_to_binary32(a / 127)
+    q = []
+    for v in fx:
+        t = round_to_binary32(v / s) if v != 0 else Fraction(0)
+        q.append(max(-127, min(127, round_half_even(t))))
+    return q, s
+
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line)
+    return rows
+
+
+def _fp16_values_between(lo, hi):
+    """Every finite fp16 value v with lo <= v <= hi (lo >= 0)."""
+    bits = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16)
+    return bits[(bits >= lo) & (bits <= hi)]
+
+
+# ----------------------------------------------------------------------------
+# unpack
+# ----------------------------------------------------------------------------
+
+def check_nibble_golden(unpack):
+    for line in _read_golden("nibble_layout.txt"):
+        word_s, fields_s = line.split(":")
+        word = int(word_s.strip(), 16)
+        if word >= 2 ** 31:
+            word -= 2 ** 32
+        expect = [int(v) for v in fields_s.split()]
+        got = unpack(np.array([[word]], dtype=np.int32))
+        assert got.shape == (1, 8), got.shape
+        assert [int(v) for v in got[0]] == expect, (hex(word), got[0], expect)
+
+
+def check_pack_roundtrip(unpack):
+    rng = np.random.default_rng(1234)
+    fields = rng.integers(0, 16, size=(7, 48))
+    packed = loop_pack(fields)
+    got = unpack(packed)
+    assert got.shape == fields.shape
+    assert np.array_equal(got.astype(np.int64), fields)
+    # a single set field at every position of every word
+    for j in range(8):
+        f = np.zeros((1, 16), dtype=np.int64)
+        f[0, j] = 9
+        f[0, 8 + j] = 15
+        assert np.array_equal(unpack(loop_pack(f)).astype(np.int64), f)
+    # all-zero and all-ones words
+    assert np.array_equal(unpack(np.zeros((2, 3), np.int32)), np.zeros((2, 24)))
+    assert np.array_equal(unpack(np.full((2, 3), -1, np.int32)), np.full((2, 24), 15))
+
+
+# ----------------------------------------------------------------------------
+# dequant and W4A16 matmul
+# ----------------------------------------------------------------------------
+
+def check_dequant_exact(dequant):
+    """(q - z) * s is exact in float32 for every (q, z) pair and every fp16 scale in [0.005, 0.02]."""
+    svals = _fp16_values_between(0.005, 0.02)
+    n = (len(svals) + 7) // 8 * 8
+    svals = np.concatenate([svals, svals[: n - len(svals)]])
+    G = 16
+    K = 16 * G  # group g has zero point g; row k has q = k % 16
+    q_fields = np.tile((np.arange(K) % 16)[:, None], (1, n))
+    z_fields = np.tile(np.arange(16)[:, None], (1, n))
+    qweight = loop_pack(q_fields)
+    qzeros = loop_pack(z_fields)
+    scales = np.tile(svals[None, :], (16, 1)).astype(np.float16)
+    w = dequant(qweight, scales, qzeros, G)
+    assert w.dtype == np.float32
+    diff = (np.arange(K) % 16 - np.arange(K) // G).astype(np.float64)
+    expect = diff[:, None] * svals.astype(np.float64)[None, :]
+    assert np.array_equal(w.astype(np.float64), expect)
+
+
+def _tiny_w4_case(seed, M=3, K=256, N=16, G=128):
+    rng = np.random.default_rng(seed)
+    q = rng.integers(0, 16, size=(K, N))
+    z = rng.integers(0, 16, size=(K // G, N))
+    s = rng.uniform(0.005, 0.02, size=(K // G, N)).astype(np.float16)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    return x, q, z, s
+
+
+def check_w4a16_bruteforce(w4a16):
+    for seed, (M, K, N, G) in enumerate([(3, 256, 16, 128), (2, 384, 24, 128), (1, 128, 8, 128),
+                                        (2, 64, 16, 32)]):
+        x, q, z, s = _tiny_w4_case(seed, M, K, N, G)
+        qweight, qzeros = loop_pack(q), loop_pack(z)
+        y = w4a16(x, qweight, s, qzeros, G)
+        assert y.shape == (M, N) and y.dtype == np.float64
+        for m in range(M):
+            for n in range(N):
+                terms = []
+                for k in range(K):
+                    qv = loop_field(qweight[k, n // 8], n % 8)
+                    zv = loop_field(qzeros[k // G, n // 8], n % 8)
+                    terms.append(float(x[m, k]) * (qv - zv) * float(s[k // G, n]))
+                ref = math.fsum(terms)
+                assert abs(y[m, n] - ref) <= 1e-12 * (1.0 + abs(ref)), (m, n, y[m, n], ref)
+
+
+def check_w4a16_special_cases(w4a16):
+    rng = np.random.default_rng(7)
+    M, K, N, G = 4, 256, 32, 128
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    # q == z everywhere -> y == 0 exactly
+    z = rng.integers(0, 16, size=(K // G, N))
+    q = np.repeat(z, G, axis=0)
+    s = rng.uniform(0.005, 0.02, size=(K // G, N)).astype(np.float16)
+    y = w4a16(x, loop_pack(q), s, loop_pack(z), G)
+    assert np.array_equal(y, np.zeros((M, N)))
+    # z = 0, s = 1, one-hot columns -> y[:, n] = x[:, perm[n]]
+    perm = rng.permutation(K)[:N]
+    q = np.zeros((K, N), dtype=np.int64)
+    q[perm, np.arange(N)] = 1
+    ones = np.ones((K // G, N), np.float16)
+    zero = np.zeros((K // G, N), np.int64)
+    y = w4a16(x, loop_pack(q), ones, loop_pack(zero), G)
+    assert np.array_equal(y, x[:, perm].astype(np.float64))
+    # x = identity (M = K) -> y = W_deq, built here by loops
+    Kc, Nc = 128, 8
+    q = rng.integers(0, 16, size=(Kc, Nc))
+    z = rng.integers(0, 16, size=(1, Nc))
+    s = rng.uniform(0.005, 0.02, size=(1, Nc)).astype(np.float16)
+    eye = np.eye(Kc, dtype=np.float16)
+    y = w4a16(eye, loop_pack(q), s, loop_pack(z), 128)
+    for k in range(Kc):
+        for n in range(Nc):
+            assert y[k, n] == (int(q[k, n]) - int(z[0, n])) * float(s[0, n])
+    # doubling every scale doubles y exactly
+    x, q, z, s = _tiny_w4_case(11, 3, 256, 16, 128)
+    y1 = w4a16(x, loop_pack(q), s, loop_pack(z), 128)
+    y2 = w4a16(x, loop_pack(q), (s.astype(np.float32) * 2).astype(np.float16), loop_pack(z), 128)
+    assert np.array_equal(y2, 2.0 * y1)
+
+
+# ----------------------------------------------------------------------------
+# per-token int8 quantization
+# ----------------------------------------------------------------------------
+
+def check_quant_golden(quant):
+    for line in _read_golden("quant_rows.txt"):
+        xs, ss, qs = [p.split() for p in line.split("|")]
+        x = np.array([[float(v) for v in xs]], dtype=np.float16)
+        assert np.array_equal(x.astype(np.float64)[0], [float(v) for v in xs]), "fixture not exact in fp16"
+        q, s = quant(x)
+        assert q.dtype == np.int8 and s.dtype == np.float32
+        assert s[0] == np.float32(ss[0]), (xs, s[0], ss[0])
+        assert [int(v) for v in q[0]] == [int(v) for v in qs], (xs, q[0], qs)
+
+
+def check_quant_exact_rational(quant):
+    """Random rows (with outlier channels) against exact rational arithmetic."""
+    rng = np.random.default_rng(99)
+    x = rng.standard_normal((6, 96)).astype(np.float32)
+    x[:, rng.choice(96, 2, replace=False)] *= 20
+    x[3] *= 1e-3
+    x[4] *= 300
+    x = x.astype(np.float16)
+    q, s = quant(x)
+    for m in range(x.shape[0]):
+        eq, es = exact_quant_row(x[m])
+        assert Fraction(float(s[m])) == es, (m, s[m], es)
+        assert [int(v) for v in q[m]] == eq, m
+
+
+def check_quant_exhaustive(quant):
+    """One row per absmax a: every fp16 value in [-a, a]; each code against exact arithmetic.
+
+    This covers every element whose binary32 quotient lands on a half-integer
+    (decided by round-half-to-even) and every element where dividing by s and
+    multiplying by 127/a disagree.
+    """
+    for a in (1.0, 0.7001953125, 3.0, 57.46875):
+        vals = _fp16_values_between(0.0, a)
+        row = np.concatenate([vals, -vals[vals > 0]]).astype(np.float16)
+        q, s = quant(row[None, :])
+        es = round_to_binary32(Fraction(a) / 127)
+        assert Fraction(float(s[0])) == es
+        sf = float(es)
+        for i, v in enumerate(row):
+            fv = Fraction(float(v))
+            t = round_to_binary32(fv / es) if v != 0 else Fraction(0)
+            e = max(-127, min(127, round_half_even(t)))
+            if int(q[0, i]) != e:
+                raise AssertionError(f"a={a} x={float(v)} q={int(q[0, i])} expected {e} (s={sf})")
+
+
+def check_quant_invariants(quant):
+    rng = np.random.default_rng(5)
+    # |x| >= 0.025 so that every power-of-two rescaling below stays exact in fp16
+    mag = rng.uniform(0.5, 1.0, size=(8, 200)) * rng.uniform(0.05, 50, size=(8, 1))
+    x = (rng.choice([-1.0, 1.0], size=(8, 200)) * mag).astype(np.float16)
+    q, s = quant(x)
+    # the absmax element maps to +-127
+    for m in range(8):
+        i = int(np.argmax(np.abs(x[m].astype(np.float32))))
+        assert abs(int(q[m, i])) == 127 and np.sign(q[m, i]) == np.sign(x[m, i])
+    # odd symmetry
+    qn, sn = quant(-x)
+    assert np.array_equal(sn, s) and np.array_equal(qn, -q)
+    # power-of-two equivariance: quant(2^j x) = (q, 2^j s)
+    for j in (-3, -1, 1, 2):
+        xj = (x.astype(np.float32) * np.float32(2.0 ** j)).astype(np.float16)
+        assert np.array_equal(xj.astype(np.float32), x.astype(np.float32) * np.float32(2.0 ** j))
+        qj, sj = quant(xj)
+        assert np.array_equal(qj, q) and np.array_equal(sj, s * np.float32(2.0 ** j))
+    # rows q0 * 2^-j with |q0| = 127 somewhere round-trip exactly
+    for j in range(0, 9):
+        q0 = rng.integers(-127, 128, size=(3, 64))
+        q0[:, 5] = 127
+        q0[1, 5] = -127
+        xr = (q0 * 2.0 ** -j).astype(np.float16)
+        qr, sr = quant(xr)
+        assert np.array_equal(qr.astype(np.int64), q0)
+        assert np.all(sr == np.float32(2.0 ** -j))
+    # all-zero row
+    qz, sz = quant(np.zeros((2, 32), np.float16))
+    assert np.all(qz == 0) and np.all(sz == 0)
+    # range
+    assert q.min() >= -127 and q.max() <= 127
+
+
+# ----------------------------------------------------------------------------
+# int32 accumulator and W8A8 output
+# ----------------------------------------------------------------------------
+
+def check_acc_bruteforce(acc_fn):
+    rng = np.random.default_rng(3)
+    for M, N, K in [(3, 5, 32), (2, 7, 64), (4, 3, 1500)]:
+        xq = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+        wq = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+        acc = acc_fn(xq, wq)
+        for m in range(M):
+            for n in range(N):
+                ref = sum(int(xq[m, k]) * int(wq[n, k]) for k in range(K))
+                assert int(acc[m, n]) == ref
+
+
+def check_acc_special(acc_fn):
+    rng = np.random.default_rng(4)
+    K = 64
+    xq = rng.integers(-127, 128, size=(5, K)).astype(np.int8)
+    assert np.array_equal(acc_fn(xq, np.eye(K, dtype=np.int8)), xq.astype(np.int64))
+    K = 12288
+    plus = np.full((2, K), 127, np.int8)
+    minus = np.full((3, K), -127, np.int8)
+    assert np.all(acc_fn(plus, minus) == -16129 * K)
+    assert np.all(acc_fn(minus, minus) == 16129 * K)
+    # the largest K whose worst case still fits int32
+    K = (2 ** 31 - 1) // 16129
+    assert np.all(acc_fn(np.full((1, K), 127, np.int8), np.full((1, K), 127, np.int8)) == 16129 * K)
+
+
+def check_w8a8_bruteforce(w8a8):
+    rng = np.random.default_rng(8)
+    M, N, K = 3, 5, 96
+    xq = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    wq = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    st = rng.uniform(0.001, 0.1, size=M).astype(np.float32)
+    sc = rng.uniform(1e-4, 1e-3, size=N).astype(np.float32)
+    y = w8a8(xq, st, wq, sc)
+    assert y.shape == (M, N) and y.dtype == np.float64
+    for m in range(M):
+        for n in range(N):
+            acc = sum(int(xq[m, k]) * int(wq[n, k]) for k in range(K))
+            exact = Fraction(acc) * Fraction(float(st[m])) * Fraction(float(sc[n]))
+            assert abs(Fraction(y[m, n]) - exact) <= abs(exact) * Fraction(1, 2 ** 50)
+
+
+def check_w8a8_linearity(w8a8):
+    rng = np.random.default_rng(9)
+    M, N, K = 4, 6, 128
+    xq = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    wq = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    st = rng.uniform(0.001, 0.1, size=M).astype(np.float32)
+    sc = rng.uniform(1e-4, 1e-3, size=N).astype(np.float32)
+    y = w8a8(xq, st, wq, sc)
+    assert np.array_equal(w8a8(xq, st * np.float32(4), wq, sc), 4 * y)
+    assert np.array_equal(w8a8(xq, st, wq, sc * np.float32(0.5)), 0.5 * y)
+    # scaling one token's scale scales only that row
+    st2 = st.copy()
+    st2[1] *= 8
+    y2 = w8a8(xq, st2, wq, sc)
+    assert np.array_equal(y2[1], 8 * y[1]) and np.array_equal(np.delete(y2, 1, 0), np.delete(y, 1, 0))
+    # unit scales give the accumulator itself
+    ones_m, ones_n = np.ones(M, np.float32), np.ones(N, np.float32)
+    acc = w8a8(xq, ones_m, wq, ones_n)
+    for m in range(M):
+        for n in range(N):
+            assert acc[m, n] == sum(int(xq[m, k]) * int(wq[n, k]) for k in range(K))

@@ -1,0 +1,243 @@
+"""The CPU oracle against its pins, and the pins against planted mistakes.
+
+The first group runs every pin on the oracle as written. The second plants a
+plausible mistake in a copy of one oracle function (on the CPU, never on the
+GPU path) and asserts that at least one pin fails, which shows that the pins
+can tell a right oracle from a wrong one.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import oracle_pins as P
+
+# ---------------------------------------------------------------------------
+# the oracle passes every pin
+# ---------------------------------------------------------------------------
+
+
+def test_nibble_golden():
+    P.check_nibble_golden(oracle.unpack_int4)
+
+
+def test_pack_roundtrip():
+    P.check_pack_roundtrip(oracle.unpack_int4)
+
+
+def test_dequant_exact():
+    P.check_dequant_exact(oracle.dequant_w4)
+
+
+def test_w4a16_bruteforce():
+    P.check_w4a16_bruteforce(oracle.w4a16_ref)
+
+
+def test_w4a16_special_cases():
+    P.check_w4a16_special_cases(oracle.w4a16_ref)
+
+
+def test_quant_golden():
+    P.check_quant_golden(oracle.quant_per_token_int8_ref)
+
+
+def test_quant_exact_rational():
+    P.check_quant_exact_rational(oracle.quant_per_token_int8_ref)
+
+
+def test_quant_exhaustive():
+    P.check_quant_exhaustive(oracle.quant_per_token_int8_ref)
+
+
+def test_quant_invariants():
+    P.check_quant_invariants(oracle.quant_per_token_int8_ref)
+
+
+def test_acc_bruteforce():
+    P.check_acc_bruteforce(oracle.w8a8_acc_ref)
+
+
+def test_acc_special():
+    P.check_acc_special(oracle.w8a8_acc_ref)
+
+
+def test_w8a8_bruteforce():
+    P.check_w8a8_bruteforce(oracle.w8a8_ref)
+
+
+def test_w8a8_linearity():
+    P.check_w8a8_linearity(oracle.w8a8_ref)
+
+
+def test_acc_overflow_guard():
+    K = (2 ** 31 - 1) // 16129 + 1
+    with pytest.raises(OverflowError):
+        oracle.w8a8_acc_ref(np.full((1, K), 127, np.int8), np.full((1, K), 127, np.int8))
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes are caught
+# ---------------------------------------------------------------------------
+
+
+def _unpack_reversed(packed):
+    words = np.asarray(packed).astype(np.int64) & 0xFFFFFFFF
+    out = np.empty((words.shape[0], words.shape[1] * 8), np.uint8)
+    for j in range(8):
+        out[:, j::8] = (words >> (4 * (7 - j))) & 0xF
+    return out
+
+
+def _unpack_signed(packed):
+    u = oracle.unpack_int4(packed).astype(np.int16)
+    return np.where(u >= 8, u - 16, u)
+
+
+def _unpack_blocked(packed):
+    # columns of a word laid out in blocks instead of interleaved
+    words = np.asarray(packed).astype(np.int64) & 0xFFFFFFFF
+    R, C = words.shape
+    out = np.empty((R, C * 8), np.uint8)
+    for j in range(8):
+        out[:, j * C:(j + 1) * C] = (words >> (4 * j)) & 0xF
+    return out
+
+
+def _dequant_with(unpack, mode):
+    def f(qweight, scales, qzeros, group):
+        q = unpack(qweight).astype(np.float32)
+        K, N = q.shape
+        G = int(group)
+        z = unpack(qzeros).astype(np.float32)
+        s = np.asarray(scales).astype(np.float32)
+        g = np.arange(K) // G
+        if mode == "group_mod":
+            g = np.arange(K) % (K // G)
+        if mode == "no_zero":
+            return q * s[g]
+        if mode == "plus_zero":
+            return (q + z[g]) * s[g]
+        if mode == "fp16_product":
+            return ((q - z[g]) * s[g]).astype(np.float16).astype(np.float32)
+        if mode == "zero_offset":
+            return (q - (z[g] + 1)) * s[g]
+        return (q - z[g]) * s[g]
+    return f
+
+
+def _w4a16_with(dequant, mode="ok"):
+    def f(x, qweight, scales, qzeros, group):
+        w = dequant(qweight, scales, qzeros, group)
+        if mode == "fp32_acc":
+            return (np.asarray(x).astype(np.float32) @ w).astype(np.float64)
+        y = np.asarray(x).astype(np.float64) @ w.astype(np.float64)
+        if mode == "fp16_out":
+            return y.astype(np.float16).astype(np.float64)
+        return y
+    return f
+
+
+def _quant_with(mode):
+    def f(x):
+        xf = np.asarray(x).astype(np.float32)
+        a = np.max(np.abs(xf), axis=1)
+        s = np.divide(a, np.float32(127.0), dtype=np.float32)
+        if mode == "scale_128":
+            s = np.divide(a, np.float32(128.0), dtype=np.float32)
+        q = np.zeros(xf.shape, np.int8)
+        nz = s > 0
+        if mode == "mul_recip":
+            t = xf[nz] * np.divide(np.float32(127.0), a[nz], dtype=np.float32)[:, None]
+        elif mode == "fp64_div":
+            t = xf[nz].astype(np.float64) / s[nz, None].astype(np.float64)
+        else:
+            t = np.divide(xf[nz], s[nz, None], dtype=np.float32)
+        if mode == "half_away":
+            r = np.sign(t) * np.floor(np.abs(t) + np.float32(0.5))
+        elif mode == "trunc":
+            r = np.trunc(t)
+        else:
+            r = np.rint(t)
+        q[nz] = np.clip(r, -127, 127).astype(np.int8)
+        return q, s
+    return f
+
+
+def _acc_fp32(xq, wq):
+    return (np.asarray(xq).astype(np.float32) @ np.asarray(wq).astype(np.float32).T).astype(np.int64)
+
+
+def _w8a8_with(mode):
+    def f(xq, s_tok, wq, s_ch):
+        acc = oracle.w8a8_acc_ref(xq, wq).astype(np.float64)
+        st = np.asarray(s_tok).astype(np.float64)
+        sc = np.asarray(s_ch).astype(np.float64)
+        if mode == "swap_scales":
+            M, N = acc.shape
+            return acc * np.resize(sc, M)[:, None] * np.resize(st, N)[None, :]
+        if mode == "fp16_out":
+            return (acc * st[:, None] * sc[None, :]).astype(np.float16).astype(np.float64)
+        if mode == "tok_only":
+            return acc * st[:, None]
+        return acc * st[:, None] * sc[None, :]
+    return f
+
+
+def _fails(*checks):
+    for check in checks:
+        try:
+            check()
+        except AssertionError:
+            return True
+    return False
+
+
+UNPACK_MUTANTS = [_unpack_reversed, _unpack_signed, _unpack_blocked]
+
+
+@pytest.mark.parametrize("mutant", UNPACK_MUTANTS, ids=lambda f: f.__name__)
+def test_unpack_mutants_caught(mutant):
+    assert _fails(lambda: P.check_nibble_golden(mutant), lambda: P.check_pack_roundtrip(mutant))
+
+
+@pytest.mark.parametrize("mode", ["group_mod", "no_zero", "plus_zero", "fp16_product", "zero_offset"])
+def test_dequant_mutants_caught(mode):
+    d = _dequant_with(oracle.unpack_int4, mode)
+    w = _w4a16_with(d)
+    assert _fails(lambda: P.check_dequant_exact(d), lambda: P.check_w4a16_bruteforce(w),
+                  lambda: P.check_w4a16_special_cases(w))
+
+
+@pytest.mark.parametrize("mode", ["fp32_acc", "fp16_out"])
+def test_w4a16_mutants_caught(mode):
+    w = _w4a16_with(oracle.dequant_w4, mode)
+    assert _fails(lambda: P.check_w4a16_bruteforce(w), lambda: P.check_w4a16_special_cases(w))
+
+
+def test_w4a16_unpack_mutants_caught_downstream():
+    for mutant in UNPACK_MUTANTS:
+        w = _w4a16_with(_dequant_with(mutant, "ok"))
+        assert _fails(lambda: P.check_w4a16_bruteforce(w), lambda: P.check_w4a16_special_cases(w))
+
+
+@pytest.mark.parametrize("mode", ["scale_128", "mul_recip", "fp64_div", "half_away", "trunc"])
+def test_quant_mutants_caught(mode):
+    q = _quant_with(mode)
+    assert _fails(lambda: P.check_quant_golden(q), lambda: P.check_quant_invariants(q),
+                  lambda: P.check_quant_exact_rational(q), lambda: P.check_quant_exhaustive(q))
+
+
+def test_quant_correct_copy_passes():
+    q = _quant_with("ok")
+    P.check_quant_golden(q)
+    P.check_quant_exhaustive(q)
+
+
+def test_acc_mutant_caught():
+    assert _fails(lambda: P.check_acc_bruteforce(_acc_fp32), lambda: P.check_acc_special(_acc_fp32))
+
+
+@pytest.mark.parametrize("mode", ["swap_scales", "fp16_out", "tok_only"])
+def test_w8a8_mutants_caught(mode):
+    w = _w8a8_with(mode)
+    assert _fails(lambda: P.check_w8a8_bruteforce(w), lambda: P.check_w8a8_linearity(w))
