@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized linear layer on one MI355X; prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Headline workload: the W4A16 decode GEMV of an 8B-shaped MLP gate+up
+projection, M in {1, 4, 16} tokens, K = 4096, N = 24576, group 128 (fp16
+activations with 0.5% x20 outlier channels; uniform 4-bit weights and zero
+points; fp16 scales in [0.005, 0.02]). One step = one GEMV at each of
+M = 1, 4, 16. Every call reads a different one of `--sets` weight sets
+(52 MB each, 520 MB in all), so a set is read again only after more than the
+256 MB Infinity Cache and the 32 MB of L2 have been swept: the weight stream
+comes from HBM. Inputs are resident in HBM before the timed region. The
+steps are captured once in a HIP graph and replayed, so host launch overhead
+is not timed.
+
+value = algorithmic bytes of a step (x + qweight + scales + qzeros + y, for
+the three calls) / wall time of a step, between device synchronizations.
+
+Also reported (same line):
+  roofline     the GEMV kernel: algorithmic bytes per launch / average launch
+               duration from HIP events around the timed graph replay, against
+               8 TB/s; `traffic` = FETCH_SIZE + WRITE_SIZE per launch from a
+               committed rocprofv3 counter summary when it matches the current
+               kernel source, else null.
+  prefill      W8A8 prefill (per-token quant + scaled int8 GEMM, M=2048,
+               K=N=4096) and W4A16 prefill GEMMs (M=4096, K=4096/12288,
+               N=4096): kernel time and TOPS against the dense MFMA peaks.
+  cpu_baseline the CPU oracle on one step of the same workload (one weight
+               set), repeated for about 10 s, in the same unit.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+FP16_PEAK_TFLOPS = 2500.0
+INT8_PEAK_TOPS = 5000.0
+
+METRIC = "W4A16 decode GEMV GB/s (% HBM peak); W8A8/W4A16 prefill TOPS (% MFMA peak)"
+GEMV_K, GEMV_N, GROUP = 4096, 24576, 128
+GEMV_MS = (1, 4, 16)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_c1_traffic.json")
+GEMV_SOURCES = ["w4a16_gemv.hip", "w4a16_common.h", "device_common.h"]
+
+
+def w4a16_bytes(M, K, N, G=GROUP):
+    return M * K * 2 + K * N // 2 + (K // G) * N * 2 + (K // G) * (N // 8) * 4 + M * N * 2
+
+
+def gemv_source_hash():
+    h = hashlib.sha256()
+    for f in GEMV_SOURCES:
+        with open(os.path.join(ROOT, "weight_activation_quantized_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=10, help="rotating weight sets (52 MB each)")
+    ap.add_argument("--prefill-reps", type=int, default=20)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-kernel", action="store_true",
+                    help="also run a plain 256 MB device copy (counter calibration under rocprofv3)")
+    return ap.parse_args(argv)
+
+
+def capture(torch, fn, n_calls_hint=""):
+    """Capture fn() into a HIP graph (after one eager run) and return it."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def timed_replay(torch, g):
+    """Replay g once between synchronizations; return (wall s, event s)."""
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return t1 - t0, ev0.elapsed_time(ev1) / 1e3
+
+
+def bench_gemv(torch, mq, synth, args, log):
+    dev = torch.device("cuda", 0)
+    log(f"generating {args.sets} weight sets of K={GEMV_K} N={GEMV_N}")
+    sets = []
+    for s in range(args.sets):
+        w = synth.w4a16_weights(GEMV_K, GEMV_N, GROUP, tag=1, seed=1000 + s)
+        sets.append({k: torch.from_numpy(v).to(dev) for k, v in w.items()})
+    xs, ys, wss = {}, {}, {}
+    for M in GEMV_MS:
+        x = synth.w4a16_inputs(M, GEMV_K, 8, GROUP, outlier_frac=0.005, tag=1, seed=M)["x"]
+        xs[M] = torch.from_numpy(x).to(dev)
+        ys[M] = torch.empty((M, GEMV_N), dtype=torch.float16, device=dev)
+        nbytes = mq.w4a16_gemv_workspace_bytes(M, GEMV_N, GEMV_K, GROUP)
+        wss[M] = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    counter = [0]
+
+    def steps(n):
+        def run():
+            for _ in range(n):
+                for M in GEMV_MS:
+                    w = sets[counter[0] % len(sets)]
+                    counter[0] += 1
+                    mq.w4a16_gemv(xs[M], w["qweight"], w["scales"], w["qzeros"], GROUP, out=ys[M],
+                                  workspace=wss[M])
+        return run
+
+    log(f"capturing warmup ({args.warmup}) and timed ({args.steps}) steps")
+    g_warm = capture(torch, steps(max(args.warmup, 1)))
+    g_timed = capture(torch, steps(args.steps))
+    g_warm.replay()
+    torch.cuda.synchronize()
+    log("timed region")
+    wall, ev = timed_replay(torch, g_timed)
+    step_bytes = sum(w4a16_bytes(M, GEMV_K, GEMV_N) for M in GEMV_MS)
+    launches = args.steps * len(GEMV_MS)
+    splits = {M: (mq.w4a16_gemv_workspace_bytes(M, GEMV_N, GEMV_K, GROUP) // (4 * M * GEMV_N)) or 1
+              for M in GEMV_MS}
+    return {
+        "wall_s": wall, "event_s": ev, "step_bytes": step_bytes, "launches": launches,
+        "kernel_avg_us": ev / launches * 1e6, "splits": splits,
+        "bytes_per_launch_avg": step_bytes / len(GEMV_MS),
+    }, sets, xs
+
+
+def bench_prefill(torch, mq, synth, oracle_free_quant, args, log):
+    """W8A8 prefill (quant + GEMM) and W4A16 prefill GEMMs; kernel times from event-timed graph replays."""
+    dev = torch.device("cuda", 0)
+    out = {}
+    R = args.prefill_reps
+
+    def time_fn(fn):
+        g = capture(torch, lambda: [fn() for _ in range(R)])
+        g.replay()
+        _, ev = timed_replay(torch, g)
+        return ev / R
+
+    # W8A8: M=2048, K=N=4096; weights quantized per output channel on the GPU
+    M, K, N = 2048, 4096, 4096
+    d = synth.w8a8_inputs(M, K, N, outlier_frac=0.01, tag=2)
+    x = torch.from_numpy(d["x"]).to(dev)
+    wq, s_ch = oracle_free_quant(torch.from_numpy(d["wf"]).to(dev))
+    xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+    s_tok = torch.empty((M,), dtype=torch.float32, device=dev)
+    y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    log("prefill: w8a8 quant")
+    t_q = time_fn(lambda: mq.quant_per_token_int8(x, out=xq, s_out=s_tok))
+    log("prefill: w8a8 gemm")
+    t_g = time_fn(lambda: mq.w8a8_scaled_mm(xq, s_tok, wq, s_ch, out=y))
+    ops = 2.0 * M * N * K
+    out["w8a8_c2"] = {
+        "shape": [M, N, K], "quant_us": t_q * 1e6, "quant_GBps": (M * K * 3 + M * 4) / t_q / 1e9,
+        "gemm_us": t_g * 1e6, "gemm_TOPS": ops / t_g / 1e12,
+        "gemm_frac_int8_peak": ops / t_g / 1e12 / INT8_PEAK_TOPS,
+        "layer_TOPS": ops / (t_q + t_g) / 1e12,
+    }
+    del x, wq, s_ch, xq, s_tok, y
+    for name, K in (("w4a16_c3a", 4096), ("w4a16_c3b", 12288)):
+        M, N = 4096, 4096
+        dd = synth.w4a16_inputs(M, K, N, GROUP, tag=3 if K == 4096 else 4)
+        t = {k: torch.from_numpy(v).to(dev) for k, v in dd.items()}
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        log(f"prefill: {name}")
+        tg = time_fn(lambda: mq.w4a16_gemm(t["x"], t["qweight"], t["scales"], t["qzeros"], GROUP, out=y))
+        ops = 2.0 * M * N * K
+        out[name] = {"shape": [M, N, K], "gemm_us": tg * 1e6, "gemm_TFLOPS": ops / tg / 1e12,
+                     "gemm_frac_fp16_peak": ops / tg / 1e12 / FP16_PEAK_TFLOPS}
+        del t, y
+    return out
+
+
+def cpu_baseline(args, log):
+    import numpy as np
+
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    w = synth.w4a16_weights(GEMV_K, GEMV_N, GROUP, tag=1, seed=1000)
+    xs = {M: synth.w4a16_inputs(M, GEMV_K, 8, GROUP, outlier_frac=0.005, tag=1, seed=M)["x"] for M in GEMV_MS}
+    reps, t_total = 0, 0.0
+    while True:
+        t0 = time.perf_counter()
+        for M in GEMV_MS:
+            y = oracle.w4a16_ref(xs[M], w["qweight"], w["scales"], w["qzeros"], GROUP)
+            assert np.all(np.isfinite(y))
+        t_total += time.perf_counter() - t0
+        reps += 1
+        if t_total >= args.cpu_seconds or reps >= 20:
+            break
+    step_bytes = sum(w4a16_bytes(M, GEMV_K, GEMV_N) for M in GEMV_MS)
+    log(f"cpu baseline: {reps} steps in {t_total:.1f} s")
+    return {"value": step_bytes * reps / t_total / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} step(s) of the same workload (M=1,4,16 on one weight set), "
+                      f"{t_total:.1f} s; NumPy dequant is single-threaded, BLAS used {threads} thread(s)"}
+
+
+def load_traffic(launch_bytes):
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("source_hash") != gemv_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(json.dumps({"error": f"--gpus {args.gpus}: this benchmark runs on one GPU only; "
+                                   "the layer's shards are the single-GPU kernels at smaller N or K"}))
+        return 2
+    rank = int(os.environ.get("RANK", "0"))
+
+    def log(msg):
+        sys.stderr.write(f"[bench] {msg}\n")
+        sys.stderr.flush()
+
+    import torch
+
+    import synth
+    import weight_activation_quantized_amd as mq
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 1
+    mq.library()  # fail loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+
+    res, sets, xs = bench_gemv(torch, mq, synth, args, log)
+    if args.copy_kernel:
+        a = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+    del sets
+    torch.cuda.empty_cache()
+
+    ms_per_step = res["wall_s"] / args.steps * 1e3
+    value = res["step_bytes"] / (res["wall_s"] / args.steps) / 1e9
+    achieved = res["bytes_per_launch_avg"] / (res["kernel_avg_us"] * 1e-6) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": "W4A16 decode GEMV (8B MLP gate+up): M in {1,4,16}, K=4096, N=24576, group 128; "
+                        f"{args.sets} rotating weight sets (cold HBM); one step = one GEMV per M",
+            "M": list(GEMV_MS), "K": GEMV_K, "N": GEMV_N, "group": GROUP, "weight_sets": args.sets,
+            "gemv_splits": res["splits"], "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": load_traffic(res["bytes_per_launch_avg"]),
+            "kernel": "w4a16_gemv_kernel", "avg_launch_us": round(res["kernel_avg_us"], 3),
+            "algorithmic_bytes_per_launch": res["bytes_per_launch_avg"],
+        },
+    }
+    if not args.no_prefill:
+        line["prefill"] = bench_prefill(torch, mq, synth, mq.quant_per_token_int8, args, log)
+    if not args.no_cpu_baseline and rank == 0:
+        line["cpu_baseline"] = cpu_baseline(args, log)
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,183 @@
+/*
+ * mq.h -- C ABI of the quantized linear layer library (libmq.so) for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Two paths of the quantized linear layer that LLM inference runtimes use:
+ *
+ *   W4A16      asymmetric 4-bit weights with per-group fp16 scales and 4-bit
+ *              zero points, fp16 activations, fp16 output. A GEMM for
+ *              prefill-shaped inputs and a GEMV for decode (M <= 16).
+ *              Source: LMDeploy toolkit overview, section 2.5 "Weight
+ *              quantization (AWQ)" (4-bit weights, groups of 128); LMDeploy
+ *              4-bit deployment guide, section 2.2 (scale and weight are
+ *              consumed inside one kernel); pymllm Setup and Usage, Overview
+ *              (the W4A16 scheme).
+ *
+ *   W8A8_INT8  dynamic per-token symmetric int8 activation quantization,
+ *              then an int8 GEMM with int32 accumulation and a per-token x
+ *              per-output-channel scale epilogue to fp16.
+ *              Source: pymllm Setup and Usage, Overview (int8 activations
+ *              and weights on INT8 matrix units) and section "W8A8 first-run
+ *              JIT compilation" (a per-token int8 quantizer feeding an int8
+ *              scaled matmul).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - fp16 values are IEEE binary16 passed as uint16_t bit patterns.
+ * - Every tensor is row-major and densely packed (no strides).
+ * - Every tensor pointer is a DEVICE pointer on the calling thread's current
+ *   HIP device, owned by the caller. The library never allocates, frees,
+ *   copies to or from the host, or synchronizes. The caller keeps every
+ *   buffer alive until the stream has executed the work.
+ * - `stream` is a hipStream_t passed as void*; NULL means the default
+ *   stream. Work is enqueued asynchronously on it and the call returns.
+ *   No memset nodes are issued, so calls may be captured into a HIP graph.
+ * - Arguments are validated on the host BEFORE any HIP call. A rejected call
+ *   enqueues nothing and leaves every output untouched.
+ * - M == 0 (and N == 0 where allowed) is a valid empty problem: MQ_OK,
+ *   nothing is enqueued.
+ * - Outputs must not overlap any input or each other (MQ_ERR_ALIAS).
+ * - Asynchronous device faults are reported by HIP at the caller's next
+ *   synchronization, not by these calls.
+ * - Thread safety: the library holds no mutable global state besides the
+ *   thread-local error message; calls from several threads are safe.
+ *   Results are deterministic: the same inputs give the same bits.
+ */
+#ifndef MQ_H
+#define MQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MQ_ABI_VERSION 1
+
+typedef enum mq_status {
+  MQ_OK = 0,
+  MQ_ERR_NULL = 1,        /* a required pointer is NULL */
+  MQ_ERR_SHAPE = 2,       /* a size is negative, too large or breaks a divisibility rule */
+  MQ_ERR_ALIGN = 3,       /* a pointer is not aligned as documented */
+  MQ_ERR_UNSUPPORTED = 4, /* valid in principle but not provided (e.g. group != 128, GEMV M > 16) */
+  MQ_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
+  MQ_ERR_ALIAS = 6,       /* an output overlaps an input or another output */
+  MQ_ERR_HIP = 7          /* the HIP runtime refused the launch (message in mq_last_error) */
+} mq_status;
+
+/* MQ_ABI_VERSION of the built library. */
+int mq_abi_version(void);
+
+/* Static, human-readable name of a status code. Never NULL. */
+const char* mq_status_string(mq_status s);
+
+/* Detail for the last non-OK call made by this thread ("" if none). The
+ * pointer stays valid until this thread's next call into the library. */
+const char* mq_last_error(void);
+
+/*
+ * Per-token symmetric int8 quantization.
+ * Source: pymllm Setup and Usage, section "W8A8 first-run JIT compilation"
+ * (the per-token int8 activation quantizer). For each row m:
+ *     s_tok[m] = fl32(max_k |x[m,k]| / 127)              (IEEE binary32 divide)
+ *     xq[m,k]  = clamp(rne(fl32(x[m,k] / s_tok[m])), -127, 127)
+ * with rne = round half to even; an all-zero row gives s_tok = 0, xq = 0.
+ * Results are bit-exact to that definition. Inputs must be finite.
+ *
+ *   x      [M, K] fp16   in
+ *   xq     [M, K] int8   out
+ *   s_tok  [M]    fp32   out
+ * Requires: 0 <= M < 2^31; 16 <= K <= 2^20, K % 16 == 0; x, xq 16-byte
+ * aligned; s_tok 4-byte aligned.
+ */
+mq_status mq_quant_per_token_int8(const uint16_t* x, int8_t* xq, float* s_tok,
+                                  int64_t M, int64_t K, void* stream);
+
+/*
+ * W8A8 scaled int8 GEMM.
+ * Source: pymllm Setup and Usage, section "W8A8 first-run JIT compilation"
+ * (int8 GEMM with a scale epilogue). acc[m,n] = sum_k xq[m,k] * wq[n,k] in
+ * exact int32, then
+ *     y[m,n] = fp16_rne( fl32( fl32(acc[m,n]) * s_tok[m] ) * s_ch[n] )
+ *
+ *   xq     [M, K] int8   in   (activations, one row per token)
+ *   s_tok  [M]    fp32   in   (per-token scales)
+ *   wq     [N, K] int8   in   (weights, one row per output channel)
+ *   s_ch   [N]    fp32   in   (per-output-channel scales)
+ *   y      [M, N] fp16   out
+ * Requires: 0 <= M, N < 2^31; 16 <= K <= 133144 (the int32 accumulator
+ * bound 127*127*K < 2^31), K % 16 == 0; xq, wq, y 16-byte aligned; s_tok,
+ * s_ch 4-byte aligned.
+ */
+mq_status mq_w8a8_scaled_mm(const int8_t* xq, const float* s_tok, const int8_t* wq,
+                            const float* s_ch, uint16_t* y,
+                            int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * Debug entry: the raw int32 accumulator of the W8A8 GEMM,
+ *     acc[m,n] = sum_k xq[m,k] * wq[n,k]   (exact)
+ * Same operands, layouts and requirements as mq_w8a8_scaled_mm; acc is
+ * [M, N] int32, 16-byte aligned.
+ */
+mq_status mq_w8a8_mm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc,
+                         int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * W4A16 GEMM (prefill-shaped M).
+ * Source: LMDeploy toolkit overview, section 2.5 (4-bit AWQ weights, group
+ * size 128); LMDeploy 4-bit deployment guide, section 2.2 (dequantization
+ * fused into the matmul kernel).
+ *     q[k,n]  = field (n % 8) of qweight[k, n/8]     (field j = bits 4j..4j+3)
+ *     z[g,n]  = field (n % 8) of qzeros[g, n/8]
+ *     w[k,n]  = (q[k,n] - z[k/G,n]) * scales[k/G,n]
+ *     y[m,n]  = fp16( sum_k x[m,k] * w[k,n] )   accumulated in fp32
+ * The weight is rounded once to fp16 before the fp16 matrix multiply;
+ * outputs match the exact result within relative Frobenius error 1e-3 and
+ * max-abs error 5e-2 at the documented input distributions.
+ *
+ *   x        [M, K]     fp16   in
+ *   qweight  [K, N/8]   int32  in   (8 unsigned 4-bit weights per word along N)
+ *   scales   [K/G, N]   fp16   in
+ *   qzeros   [K/G, N/8] int32  in   (unsigned 4-bit zero points, packed like qweight)
+ *   y        [M, N]     fp16   out
+ * Requires: group == 128; 0 <= M < 2^31; 8 <= N < 2^31, N % 8 == 0;
+ * 128 <= K <= 2^20, K % 128 == 0; x, scales, y 16-byte aligned; qweight,
+ * qzeros 4-byte aligned.
+ */
+mq_status mq_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
+                        const int32_t* qzeros, uint16_t* y,
+                        int64_t M, int64_t N, int64_t K, int64_t group, void* stream);
+
+/*
+ * Workspace size in bytes that mq_w4a16_gemv needs for this problem (0 when
+ * it needs none). Returns 0 as well for problems mq_w4a16_gemv rejects.
+ * Pure host function.
+ */
+size_t mq_w4a16_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group);
+
+/*
+ * W4A16 GEMV for decode (1 <= M <= 16). Same definition, operands and
+ * layouts as mq_w4a16_gemm, except that the weights are not rounded to
+ * fp16: each group's sum of x * (q - z) is formed exactly in fp32 and then
+ * scaled in fp32. K is split across workgroups; the partial sums go to
+ * `workspace` (fp32) and are summed in a fixed order, so results are
+ * deterministic.
+ *
+ *   workspace        device buffer of at least
+ *                    mq_w4a16_gemv_workspace_bytes(M, N, K, group) bytes,
+ *                    16-byte aligned; may be NULL when that size is 0. Its
+ *                    contents on entry do not matter; it must not overlap
+ *                    any operand and must not be used by concurrent calls.
+ * Requires: as mq_w4a16_gemm, and M <= 16 (M > 16 -> MQ_ERR_UNSUPPORTED).
+ */
+mq_status mq_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
+                        const int32_t* qzeros, uint16_t* y,
+                        int64_t M, int64_t N, int64_t K, int64_t group,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MQ_H */

@@ -1,0 +1,169 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments before touching the GPU.
+
+Pointers passed here are fake integer addresses: every call in this file is
+rejected by host-side validation, so nothing is dereferenced and no HIP call
+is made. The one test that lets a call through to HIP runs only on a host
+without a GPU.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import weight_activation_quantized_amd as mq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mq.h")
+
+OK, NULL, SHAPE, ALIGN, UNSUP, WS, ALIAS, HIP = range(8)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mq.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["mq_quant_per_token_int8", "mq_w8a8_scaled_mm", "mq_w8a8_mm_i32", "mq_w4a16_gemm",
+              "mq_w4a16_gemv", "mq_w4a16_gemv_workspace_bytes", "mq_abi_version",
+              "mq_status_string", "mq_last_error"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", mq.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.mq_abi_version() == 1
+    names = [lib.mq_status_string(i).decode() for i in range(8)]
+    assert names == ["MQ_OK", "MQ_ERR_NULL", "MQ_ERR_SHAPE", "MQ_ERR_ALIGN", "MQ_ERR_UNSUPPORTED",
+                     "MQ_ERR_WORKSPACE", "MQ_ERR_ALIAS", "MQ_ERR_HIP"]
+    assert lib.mq_status_string(99).decode() == "MQ_ERR_UNKNOWN"
+
+
+# fake, well-aligned, far-apart device addresses
+A, B, C, D, E, F = (0x10_0000_0000 * (i + 1) for i in range(6))
+
+
+def _err(lib):
+    return lib.mq_last_error().decode()
+
+
+def test_quant_validation(lib):
+    q = lib.mq_quant_per_token_int8
+    assert q(None, B, C, 4, 64, None) == NULL
+    assert q(A, B, C, -1, 64, None) == SHAPE
+    assert q(A, B, C, 4, 8, None) == SHAPE          # K < 16
+    assert q(A, B, C, 4, 72, None) == SHAPE         # K % 16
+    assert q(A, B, C, 4, (1 << 20) + 16, None) == SHAPE
+    assert "K=" in _err(lib)
+    assert q(A + 8, B, C, 4, 64, None) == ALIGN
+    assert q(A, B + 4, C, 4, 64, None) == ALIGN
+    assert q(A, B, C + 2, 4, 64, None) == ALIGN
+    assert q(A, A + 64, C, 4, 64, None) == ALIAS    # xq inside x
+    assert q(A, B, B + 64, 4, 64, None) == ALIAS    # s_tok inside xq
+    assert q(A, B, C, 0, 64, None) == OK            # empty problem: nothing enqueued
+    assert _err(lib) == ""
+
+
+def test_w8a8_validation(lib):
+    s = lib.mq_w8a8_scaled_mm
+    assert s(A, None, C, D, E, 4, 8, 64, None) == NULL
+    assert s(A, B, C, D, E, 4, 8, 60, None) == SHAPE
+    assert s(A, B, C, D, E, 4, 8, 133144 + 16, None) == SHAPE
+    assert s(A, B, C, D, E, 4, -8, 64, None) == SHAPE
+    assert s(A + 1, B, C, D, E, 4, 8, 64, None) == ALIGN
+    assert s(A, B + 1, C, D, E, 4, 8, 64, None) == ALIGN
+    assert s(A, B, C, D, E + 2, 4, 8, 64, None) == ALIGN
+    assert s(A, B, C, D, C + 16, 4, 8, 64, None) == ALIAS
+    assert s(A, B, C, D, E, 0, 8, 64, None) == OK
+    assert s(A, B, C, D, E, 4, 0, 64, None) == OK
+    i = lib.mq_w8a8_mm_i32
+    assert i(A, None, C, 4, 8, 64, None) == NULL
+    assert i(A, B, A + 16, 4, 8, 64, None) == ALIAS
+    assert i(A, B, C + 8, 4, 8, 64, None) == ALIGN
+    assert i(A, B, C, 4, 8, 40, None) == SHAPE
+
+
+def test_w4a16_gemm_validation(lib):
+    g = lib.mq_w4a16_gemm
+    assert g(A, B, C, D, None, 4, 64, 256, 128, None) == NULL
+    assert g(A, B, C, D, E, 4, 64, 256, 64, None) == UNSUP      # group 64 not provided
+    assert g(A, B, C, D, E, 4, 64, 256, -1, None) == UNSUP
+    assert g(A, B, C, D, E, 4, 60, 256, 128, None) == SHAPE     # N % 8
+    assert g(A, B, C, D, E, 4, 64, 200, 128, None) == SHAPE     # K % 128
+    assert g(A, B, C, D, E, 4, 64, 0, 128, None) == SHAPE
+    assert g(A + 8, B, C, D, E, 4, 64, 256, 128, None) == ALIGN
+    assert g(A, B + 2, C, D, E, 4, 64, 256, 128, None) == ALIGN
+    assert g(A, B, C, D, B + 16, 4, 64, 256, 128, None) == ALIAS
+    assert g(A, B, C, D, E, 0, 64, 256, 128, None) == OK
+
+
+def test_w4a16_gemv_validation(lib):
+    v = lib.mq_w4a16_gemv
+    ws = lib.mq_w4a16_gemv_workspace_bytes
+    assert v(A, B, C, D, E, 17, 64, 256, 128, F, 1 << 20, None) == UNSUP
+    assert "M <= 16" in _err(lib)
+    # a problem that needs a workspace: small N -> K split across workgroups
+    need = ws(1, 128, 4096, 128)
+    assert need > 0
+    assert v(A, B, C, D, E, 1, 128, 4096, 128, None, 0, None) == WS
+    assert v(A, B, C, D, E, 1, 128, 4096, 128, F, need - 4, None) == WS
+    assert v(A, B, C, D, E, 1, 128, 4096, 128, F + 4, need, None) == ALIGN
+    assert v(A, B, C, D, E, 1, 128, 4096, 128, A, need, None) == ALIAS   # workspace over x
+    assert v(A, B, C, D, E, 1, 128, 4096, 128, E, need, None) == ALIAS   # workspace over y
+    assert v(A, B, C, D, E, 0, 128, 4096, 128, None, 0, None) == OK
+
+
+def test_gemv_workspace_plan(lib):
+    ws = lib.mq_w4a16_gemv_workspace_bytes
+    # rejected problems need nothing
+    assert ws(0, 512, 512, 128) == 0
+    assert ws(17, 512, 512, 128) == 0
+    assert ws(4, 512, 512, 64) == 0
+    # the workspace is splits * M * N fp32 partials, with splits dividing K/128
+    for M, N, K in [(1, 24576, 4096), (4, 24576, 4096), (16, 24576, 4096), (1, 6144, 4096),
+                    (8, 4096, 4096), (1, 4096, 12288), (4, 512, 512), (3, 424, 384)]:
+        b = ws(M, N, K, 128)
+        assert b % (4 * M * N) == 0
+        splits = b // (4 * M * N) or 1
+        assert (K // 128) % splits == 0
+        # enough workgroups to cover the chip, unless K has run out of groups
+        strips = -(-(N // 8) // 16)
+        assert strips * splits >= 256 or splits == K // 128
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="lets a launch through; only meaningful without a GPU")
+def test_valid_call_without_gpu_reports_hip_error(lib):
+    st = lib.mq_quant_per_token_int8(A, B, C, 4, 64, None)
+    assert st == HIP
+    assert "hip" in _err(lib).lower()
+
+
+def test_python_wrapper_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(4, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        mq.quant_per_token_int8(x)
+
+
+def test_mqerror_carries_status():
+    e = mq.MqError(SHAPE, "K=3 bad")
+    assert e.status == SHAPE and e.status_name == "MQ_ERR_SHAPE" and "K=3" in str(e)

@@ -1,0 +1,239 @@
+"""Quantized linear layers for AMD Instinct MI355X (gfx950): W4A16 and W8A8_INT8.
+
+A thin binding over the C ABI of ``libmq.so`` (declared in ``include/mq.h``).
+Every step of the computation runs in the library's HIP kernels; this module
+only checks tensor metadata, allocates outputs with ``torch.empty`` and passes
+device pointers and the current HIP stream. There is no fallback: if the
+library is missing or the tensors are not on a GPU, the call raises.
+
+Entry points (same names as the C ABI, without the ``mq_`` prefix):
+
+    quant_per_token_int8(x)                          -> (xq, s_tok)
+    w8a8_scaled_mm(xq, s_tok, wq, s_ch)              -> y  (fp16)
+    w8a8_mm_i32(xq, wq)                              -> acc (int32)
+    w4a16_gemm(x, qweight, scales, qzeros, group)    -> y  (fp16)
+    w4a16_gemv(x, qweight, scales, qzeros, group)    -> y  (fp16), M <= 16
+    w4a16_gemv_workspace_bytes(M, N, K, group)       -> int
+
+and two compositions used by a model's linear layer:
+
+    w4a16_linear(x, qweight, scales, qzeros, group)  GEMV for M <= 16, else GEMM
+    w8a8_linear(x, wq, s_ch)                         quantize x per token, then scaled GEMM
+"""
+
+import ctypes
+import os
+
+__all__ = [
+    "MqError", "library", "LIB_PATH",
+    "quant_per_token_int8", "w8a8_scaled_mm", "w8a8_mm_i32",
+    "w4a16_gemm", "w4a16_gemv", "w4a16_gemv_workspace_bytes",
+    "w4a16_linear", "w8a8_linear", "GEMV_MAX_M",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmq.so")
+GEMV_MAX_M = 16
+
+STATUS_NAMES = {
+    0: "MQ_OK", 1: "MQ_ERR_NULL", 2: "MQ_ERR_SHAPE", 3: "MQ_ERR_ALIGN", 4: "MQ_ERR_UNSUPPORTED",
+    5: "MQ_ERR_WORKSPACE", 6: "MQ_ERR_ALIAS", 7: "MQ_ERR_HIP",
+}
+
+
+class MqError(RuntimeError):
+    """A libmq call returned a non-OK status."""
+
+    def __init__(self, status, detail):
+        self.status = int(status)
+        self.status_name = STATUS_NAMES.get(self.status, f"status {status}")
+        self.detail = detail
+        super().__init__(f"{self.status_name}: {detail}")
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_PROTOTYPES = {
+    "mq_abi_version": (ctypes.c_int, []),
+    "mq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "mq_last_error": (ctypes.c_char_p, []),
+    "mq_quant_per_token_int8": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
+    "mq_w8a8_scaled_mm": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "mq_w8a8_mm_i32": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P]),
+    "mq_w4a16_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
+    "mq_w4a16_gemv_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I64]),
+    "mq_w4a16_gemv": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
+}
+
+
+def library():
+    """The loaded ``libmq.so`` (ctypes) with prototypes set. Raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m weight_activation_quantized_amd._build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _PROTOTYPES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        detail = library().mq_last_error()
+        raise MqError(status, detail.decode() if detail else "")
+
+
+# ---------------------------------------------------------------------------
+# torch-facing wrappers
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_tensor(t, name, dtype, ndim):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D (got shape {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream_of(t, stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _out(out, shape, dtype, like, name):
+    torch = _torch()
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    _dev_tensor(out, name, dtype, len(shape))
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(out.shape)})")
+    return out
+
+
+def quant_per_token_int8(x, out=None, s_out=None, stream=None):
+    """Per-token int8 quantization of fp16 x[M, K] -> (xq int8 [M, K], s_tok fp32 [M])."""
+    torch = _torch()
+    _dev_tensor(x, "x", torch.float16, 2)
+    M, K = x.shape
+    xq = _out(out, (M, K), torch.int8, x, "out")
+    s = _out(s_out, (M,), torch.float32, x, "s_out")
+    with torch.cuda.device(x.device):
+        _check(library().mq_quant_per_token_int8(x.data_ptr(), xq.data_ptr(), s.data_ptr(), M, K,
+                                                 _stream_of(x, stream)))
+    return xq, s
+
+
+def w8a8_scaled_mm(xq, s_tok, wq, s_ch, out=None, stream=None):
+    """y[M, N] fp16 = (xq[M, K] . wq[N, K]^T) * s_tok[:, None] * s_ch[None, :]."""
+    torch = _torch()
+    _dev_tensor(xq, "xq", torch.int8, 2)
+    _dev_tensor(wq, "wq", torch.int8, 2)
+    _dev_tensor(s_tok, "s_tok", torch.float32, 1)
+    _dev_tensor(s_ch, "s_ch", torch.float32, 1)
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K or s_tok.shape[0] != M or s_ch.shape[0] != N:
+        raise ValueError("shape mismatch between xq, s_tok, wq and s_ch")
+    y = _out(out, (M, N), torch.float16, xq, "out")
+    with torch.cuda.device(xq.device):
+        _check(library().mq_w8a8_scaled_mm(xq.data_ptr(), s_tok.data_ptr(), wq.data_ptr(), s_ch.data_ptr(),
+                                           y.data_ptr(), M, N, K, _stream_of(xq, stream)))
+    return y
+
+
+def w8a8_mm_i32(xq, wq, out=None, stream=None):
+    """Debug: raw int32 accumulator acc[M, N] = xq[M, K] . wq[N, K]^T."""
+    torch = _torch()
+    _dev_tensor(xq, "xq", torch.int8, 2)
+    _dev_tensor(wq, "wq", torch.int8, 2)
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("xq and wq must share K")
+    acc = _out(out, (M, N), torch.int32, xq, "out")
+    with torch.cuda.device(xq.device):
+        _check(library().mq_w8a8_mm_i32(xq.data_ptr(), wq.data_ptr(), acc.data_ptr(), M, N, K,
+                                        _stream_of(xq, stream)))
+    return acc
+
+
+def _w4a16_shapes(x, qweight, scales, qzeros, group):
+    torch = _torch()
+    _dev_tensor(x, "x", torch.float16, 2)
+    _dev_tensor(qweight, "qweight", torch.int32, 2)
+    _dev_tensor(scales, "scales", torch.float16, 2)
+    _dev_tensor(qzeros, "qzeros", torch.int32, 2)
+    M, K = x.shape
+    N = qweight.shape[1] * 8
+    if qweight.shape[0] != K:
+        raise ValueError("qweight must be [K, N/8]")
+    G = K if group == -1 else group
+    if G <= 0 or K % G:
+        raise ValueError("K must be a multiple of the group size")
+    if tuple(scales.shape) != (K // G, N) or tuple(qzeros.shape) != (K // G, N // 8):
+        raise ValueError("scales must be [K/G, N] and qzeros [K/G, N/8]")
+    return M, N, K
+
+
+def w4a16_gemm(x, qweight, scales, qzeros, group=128, out=None, stream=None):
+    """W4A16 GEMM: y[M, N] fp16 = x[M, K] . dequant(qweight, scales, qzeros)."""
+    torch = _torch()
+    M, N, K = _w4a16_shapes(x, qweight, scales, qzeros, group)
+    y = _out(out, (M, N), torch.float16, x, "out")
+    with torch.cuda.device(x.device):
+        _check(library().mq_w4a16_gemm(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), qzeros.data_ptr(),
+                                       y.data_ptr(), M, N, K, group, _stream_of(x, stream)))
+    return y
+
+
+def w4a16_gemv_workspace_bytes(M, N, K, group=128):
+    """Workspace bytes ``w4a16_gemv`` needs (0 if none)."""
+    return int(library().mq_w4a16_gemv_workspace_bytes(M, N, K, group))
+
+
+def w4a16_gemv(x, qweight, scales, qzeros, group=128, out=None, workspace=None, stream=None):
+    """W4A16 GEMV for decode (M <= 16). ``workspace``: a uint8 GPU tensor, allocated if None."""
+    torch = _torch()
+    M, N, K = _w4a16_shapes(x, qweight, scales, qzeros, group)
+    y = _out(out, (M, N), torch.float16, x, "out")
+    need = w4a16_gemv_workspace_bytes(M, N, K, group)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    with torch.cuda.device(x.device):
+        _check(library().mq_w4a16_gemv(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), qzeros.data_ptr(),
+                                       y.data_ptr(), M, N, K, group, ws_ptr, ws_bytes, _stream_of(x, stream)))
+    return y
+
+
+def w4a16_linear(x, qweight, scales, qzeros, group=128, out=None, stream=None):
+    """W4A16 linear layer: the GEMV for M <= 16 (decode), the GEMM otherwise (prefill)."""
+    if x.shape[0] <= GEMV_MAX_M:
+        return w4a16_gemv(x, qweight, scales, qzeros, group, out=out, stream=stream)
+    return w4a16_gemm(x, qweight, scales, qzeros, group, out=out, stream=stream)
+
+
+def w8a8_linear(x, wq, s_ch, out=None, stream=None):
+    """W8A8_INT8 linear layer: per-token int8 quantization of x, then the scaled int8 GEMM."""
+    xq, s_tok = quant_per_token_int8(x, stream=stream)
+    return w8a8_scaled_mm(xq, s_tok, wq, s_ch, out=out, stream=stream)

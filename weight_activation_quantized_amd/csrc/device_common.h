@@ -1,0 +1,67 @@
+// Device-side types and helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mq {
+
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
+__device__ __forceinline__ uint32_t as_u32(f16x2 h) { return __builtin_bit_cast(uint32_t, h); }
+
+// Byte permute of two dwords: output byte i = byte sel[i] of the 8-byte value
+// {hi:lo} (selectors 0-3 pick bytes of lo, 4-7 bytes of hi).
+__device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Two packed fp16 values built from two 4-bit fields sitting in bits 0-3 (or
+// 4-7) of each 16-bit half: OR-ing them into the mantissa of 1024.0 (0x6400)
+// gives exactly 1024 + q (or 1024 + 16*q).
+__device__ __forceinline__ uint32_t nib_lo_to_f16x2(uint32_t v) {
+  return (v & 0x000F000Fu) | 0x64006400u;
+}
+__device__ __forceinline__ uint32_t nib_hi_to_f16x2(uint32_t v) {
+  return (v & 0x00F000F0u) | 0x64006400u;
+}
+
+}  // namespace mq
+
+#include <tuple>
+#include <utility>
+
+namespace mq {
+
+// Launch `kernel` and return the launch status directly (no reliance on the
+// thread's sticky last-error state). Arguments are converted to the kernel's
+// parameter types first.
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
+                         hipStream_t stream, Args&&... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count mismatch");
+  std::tuple<KArgs...> values(static_cast<KArgs>(std::forward<Args>(args))...);
+  void* ptrs[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+  std::apply([&](auto&... v) {
+    int i = 0;
+    ((ptrs[i++] = static_cast<void*>(&v)), ...);
+  }, values);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, shmem, stream);
+}
+
+}  // namespace mq

@@ -1,0 +1,40 @@
+// Internal launcher declarations shared by the C-ABI layer (mq_api.cpp) and
+// the kernel translation units. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mq {
+
+// Per-token int8 quantization of x[M,K] (fp16) into xq[M,K] and s_tok[M].
+hipError_t launch_quant_per_token_int8(const uint16_t* x, int8_t* xq, float* s_tok,
+                                       int64_t M, int64_t K, hipStream_t stream);
+
+// int8 GEMM acc = xq[M,K] . wq[N,K]^T. Exactly one of y (scaled fp16 output,
+// needs s_tok and s_ch) and acc (raw int32 output) is non-null.
+hipError_t launch_w8a8_gemm(const int8_t* xq, const float* s_tok, const int8_t* wq,
+                            const float* s_ch, uint16_t* y, int32_t* acc,
+                            int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// W4A16 GEMM y[M,N] = x[M,K] . dequant(qweight, scales, qzeros) with group 128.
+hipError_t launch_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
+                             const int32_t* qzeros, uint16_t* y,
+                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// W4A16 GEMV launch plan: K is cut into `splits` slices across workgroups,
+// each workgroup has `waves` wavefronts that share its K slice.
+struct GemvPlan {
+  int splits;
+  int waves;
+  size_t workspace_bytes;
+};
+GemvPlan plan_w4a16_gemv(int64_t M, int64_t N, int64_t K);
+
+hipError_t launch_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
+                             const int32_t* qzeros, uint16_t* y,
+                             int64_t M, int64_t N, int64_t K, const GemvPlan& plan,
+                             void* workspace, hipStream_t stream);
+
+}  // namespace mq

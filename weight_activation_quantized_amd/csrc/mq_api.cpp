@@ -1,0 +1,228 @@
+// C ABI of libmq: argument validation (host only, before any HIP call),
+// status strings, thread-local error detail, and dispatch to the kernels.
+// The operations and their sources are documented in include/mq.h.
+#include "mq.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+mq_status fail(mq_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+mq_status ok() {
+  g_last_error[0] = '\0';
+  return MQ_OK;
+}
+
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+constexpr int64_t kMaxK = int64_t{1} << 20;
+constexpr int64_t kMaxKInt8 = 133144;            // 127 * 127 * K < 2^31
+constexpr int64_t kMaxElems = int64_t{1} << 40;  // bound on M*N, M*K, K*N
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Range {
+  const void* p;
+  size_t bytes;
+  const char* name;
+};
+
+bool overlap(const Range& a, const Range& b) {
+  if (a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Every output must be disjoint from every input and from the other outputs.
+template <size_t NI, size_t NO>
+mq_status check_alias(const Range (&in)[NI], const Range (&out)[NO]) {
+  for (size_t o = 0; o < NO; ++o) {
+    for (size_t i = 0; i < NI; ++i)
+      if (overlap(out[o], in[i]))
+        return fail(MQ_ERR_ALIAS, "output %s overlaps input %s", out[o].name, in[i].name);
+    for (size_t p = o + 1; p < NO; ++p)
+      if (overlap(out[o], out[p]))
+        return fail(MQ_ERR_ALIAS, "output %s overlaps output %s", out[o].name, out[p].name);
+  }
+  return MQ_OK;
+}
+
+mq_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MQ_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+mq_status check_mk(int64_t M, int64_t K, int64_t k_min, int64_t k_max, int64_t k_mult) {
+  if (M < 0 || M > kMaxDim) return fail(MQ_ERR_SHAPE, "M=%lld out of range", (long long)M);
+  if (K < k_min || K > k_max) return fail(MQ_ERR_SHAPE, "K=%lld out of [%lld, %lld]", (long long)K,
+                                          (long long)k_min, (long long)k_max);
+  if (K % k_mult) return fail(MQ_ERR_SHAPE, "K=%lld is not a multiple of %lld", (long long)K, (long long)k_mult);
+  if (M * K > kMaxElems) return fail(MQ_ERR_SHAPE, "M*K too large");
+  return MQ_OK;
+}
+
+mq_status check_w4a16(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
+                      const int32_t* qzeros, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t group) {
+  if (!x || !qweight || !scales || !qzeros || !y) return fail(MQ_ERR_NULL, "a tensor pointer is NULL");
+  if (group != 128)
+    return fail(MQ_ERR_UNSUPPORTED, "group=%lld (only 128 is provided)", (long long)group);
+  mq_status s = check_mk(M, K, 128, kMaxK, 128);
+  if (s != MQ_OK) return s;
+  if (N < 8 || N > kMaxDim || N % 8)
+    return fail(MQ_ERR_SHAPE, "N=%lld must be a positive multiple of 8", (long long)N);
+  if (M * N > kMaxElems || K * N > kMaxElems) return fail(MQ_ERR_SHAPE, "problem too large");
+  if (!aligned(x, 16) || !aligned(scales, 16) || !aligned(y, 16))
+    return fail(MQ_ERR_ALIGN, "x, scales and y must be 16-byte aligned");
+  if (!aligned(qweight, 4) || !aligned(qzeros, 4))
+    return fail(MQ_ERR_ALIGN, "qweight and qzeros must be 4-byte aligned");
+  const size_t G = static_cast<size_t>(K / group);
+  const Range in[] = {{x, static_cast<size_t>(M * K) * 2, "x"},
+                      {qweight, static_cast<size_t>(K * (N / 8)) * 4, "qweight"},
+                      {scales, G * static_cast<size_t>(N) * 2, "scales"},
+                      {qzeros, G * static_cast<size_t>(N / 8) * 4, "qzeros"}};
+  const Range out[] = {{y, static_cast<size_t>(M * N) * 2, "y"}};
+  return check_alias(in, out);
+}
+
+mq_status check_w8a8(const int8_t* xq, const int8_t* wq, const void* out, size_t out_elem,
+                     int64_t M, int64_t N, int64_t K) {
+  mq_status s = check_mk(M, K, 16, kMaxKInt8, 16);
+  if (s != MQ_OK) return s;
+  if (N < 0 || N > kMaxDim) return fail(MQ_ERR_SHAPE, "N=%lld out of range", (long long)N);
+  if (M * N > kMaxElems || K * N > kMaxElems) return fail(MQ_ERR_SHAPE, "problem too large");
+  if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(out, 16))
+    return fail(MQ_ERR_ALIGN, "xq, wq and the output must be 16-byte aligned");
+  (void)out_elem;
+  return MQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mq_abi_version(void) { return MQ_ABI_VERSION; }
+
+const char* mq_status_string(mq_status s) {
+  switch (s) {
+    case MQ_OK: return "MQ_OK";
+    case MQ_ERR_NULL: return "MQ_ERR_NULL";
+    case MQ_ERR_SHAPE: return "MQ_ERR_SHAPE";
+    case MQ_ERR_ALIGN: return "MQ_ERR_ALIGN";
+    case MQ_ERR_UNSUPPORTED: return "MQ_ERR_UNSUPPORTED";
+    case MQ_ERR_WORKSPACE: return "MQ_ERR_WORKSPACE";
+    case MQ_ERR_ALIAS: return "MQ_ERR_ALIAS";
+    case MQ_ERR_HIP: return "MQ_ERR_HIP";
+  }
+  return "MQ_ERR_UNKNOWN";
+}
+
+const char* mq_last_error(void) { return g_last_error; }
+
+mq_status mq_quant_per_token_int8(const uint16_t* x, int8_t* xq, float* s_tok,
+                                  int64_t M, int64_t K, void* stream) {
+  if (!x || !xq || !s_tok) return fail(MQ_ERR_NULL, "a tensor pointer is NULL");
+  mq_status s = check_mk(M, K, 16, kMaxK, 16);
+  if (s != MQ_OK) return s;
+  if (!aligned(x, 16) || !aligned(xq, 16)) return fail(MQ_ERR_ALIGN, "x and xq must be 16-byte aligned");
+  if (!aligned(s_tok, 4)) return fail(MQ_ERR_ALIGN, "s_tok must be 4-byte aligned");
+  const Range in[] = {{x, static_cast<size_t>(M * K) * 2, "x"}};
+  const Range out[] = {{xq, static_cast<size_t>(M * K), "xq"}, {s_tok, static_cast<size_t>(M) * 4, "s_tok"}};
+  s = check_alias(in, out);
+  if (s != MQ_OK) return s;
+  if (M == 0) return ok();
+  return hip_status(mq::launch_quant_per_token_int8(x, xq, s_tok, M, K, as_stream(stream)),
+                    "quant_per_token_int8 launch");
+}
+
+mq_status mq_w8a8_scaled_mm(const int8_t* xq, const float* s_tok, const int8_t* wq,
+                            const float* s_ch, uint16_t* y,
+                            int64_t M, int64_t N, int64_t K, void* stream) {
+  if (!xq || !s_tok || !wq || !s_ch || !y) return fail(MQ_ERR_NULL, "a tensor pointer is NULL");
+  mq_status s = check_w8a8(xq, wq, y, 2, M, N, K);
+  if (s != MQ_OK) return s;
+  if (!aligned(s_tok, 4) || !aligned(s_ch, 4)) return fail(MQ_ERR_ALIGN, "s_tok and s_ch must be 4-byte aligned");
+  const Range in[] = {{xq, static_cast<size_t>(M * K), "xq"},
+                      {s_tok, static_cast<size_t>(M) * 4, "s_tok"},
+                      {wq, static_cast<size_t>(N * K), "wq"},
+                      {s_ch, static_cast<size_t>(N) * 4, "s_ch"}};
+  const Range out[] = {{y, static_cast<size_t>(M * N) * 2, "y"}};
+  s = check_alias(in, out);
+  if (s != MQ_OK) return s;
+  if (M == 0 || N == 0) return ok();
+  return hip_status(mq::launch_w8a8_gemm(xq, s_tok, wq, s_ch, y, nullptr, M, N, K, as_stream(stream)),
+                    "w8a8_scaled_mm launch");
+}
+
+mq_status mq_w8a8_mm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc,
+                         int64_t M, int64_t N, int64_t K, void* stream) {
+  if (!xq || !wq || !acc) return fail(MQ_ERR_NULL, "a tensor pointer is NULL");
+  mq_status s = check_w8a8(xq, wq, acc, 4, M, N, K);
+  if (s != MQ_OK) return s;
+  const Range in[] = {{xq, static_cast<size_t>(M * K), "xq"}, {wq, static_cast<size_t>(N * K), "wq"}};
+  const Range out[] = {{acc, static_cast<size_t>(M * N) * 4, "acc"}};
+  s = check_alias(in, out);
+  if (s != MQ_OK) return s;
+  if (M == 0 || N == 0) return ok();
+  return hip_status(mq::launch_w8a8_gemm(xq, nullptr, wq, nullptr, nullptr, acc, M, N, K, as_stream(stream)),
+                    "w8a8_mm_i32 launch");
+}
+
+mq_status mq_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
+                        const int32_t* qzeros, uint16_t* y,
+                        int64_t M, int64_t N, int64_t K, int64_t group, void* stream) {
+  mq_status s = check_w4a16(x, qweight, scales, qzeros, y, M, N, K, group);
+  if (s != MQ_OK) return s;
+  if (M == 0) return ok();
+  return hip_status(mq::launch_w4a16_gemm(x, qweight, scales, qzeros, y, M, N, K, as_stream(stream)),
+                    "w4a16_gemm launch");
+}
+
+size_t mq_w4a16_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group) {
+  if (group != 128 || M < 1 || M > 16 || N < 8 || N % 8 || N > kMaxDim || K < 128 || K > kMaxK || K % 128)
+    return 0;
+  return mq::plan_w4a16_gemv(M, N, K).workspace_bytes;
+}
+
+mq_status mq_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
+                        const int32_t* qzeros, uint16_t* y,
+                        int64_t M, int64_t N, int64_t K, int64_t group,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  mq_status s = check_w4a16(x, qweight, scales, qzeros, y, M, N, K, group);
+  if (s != MQ_OK) return s;
+  if (M > 16) return fail(MQ_ERR_UNSUPPORTED, "GEMV needs M <= 16 (got %lld); use mq_w4a16_gemm", (long long)M);
+  if (M == 0) return ok();
+  const mq::GemvPlan plan = mq::plan_w4a16_gemv(M, N, K);
+  if (plan.workspace_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.workspace_bytes)
+      return fail(MQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.workspace_bytes,
+                  workspace ? workspace_bytes : static_cast<size_t>(0));
+    if (!aligned(workspace, 16)) return fail(MQ_ERR_ALIGN, "workspace must be 16-byte aligned");
+    const size_t G = static_cast<size_t>(K / group);
+    const Range in[] = {{x, static_cast<size_t>(M * K) * 2, "x"},
+                        {qweight, static_cast<size_t>(K * (N / 8)) * 4, "qweight"},
+                        {scales, G * static_cast<size_t>(N) * 2, "scales"},
+                        {qzeros, G * static_cast<size_t>(N / 8) * 4, "qzeros"}};
+    const Range out[] = {{y, static_cast<size_t>(M * N) * 2, "y"}, {workspace, plan.workspace_bytes, "workspace"}};
+    s = check_alias(in, out);
+    if (s != MQ_OK) return s;
+  }
+  return hip_status(mq::launch_w4a16_gemv(x, qweight, scales, qzeros, y, M, N, K, plan,
+                                          plan.workspace_bytes ? workspace : nullptr, as_stream(stream)),
+                    "w4a16_gemv launch");
+}
+
+}  // extern "C"

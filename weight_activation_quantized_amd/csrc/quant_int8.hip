@@ -1,0 +1,140 @@
+// Per-token symmetric int8 quantization for gfx950.
+//
+// Source: pymllm Setup and Usage, section "W8A8 first-run JIT compilation"
+// (per-token int8 activation quantizer in front of the int8 scaled matmul).
+// For every row m: s[m] = fl32(absmax(x[m,:]) / 127) and
+// q[m,k] = clamp(rne(fl32(x[m,k] / s[m])), -127, 127); all-zero rows give
+// s = 0, q = 0. The quotient is an IEEE binary32 division (no reciprocal
+// shortcut) and rintf rounds half to even, so the codes are bit-exact.
+//
+// One wavefront per row, four rows per workgroup. Each lane holds its share
+// of the row in registers (16-byte chunks of 8 fp16), so x is read from HBM
+// exactly once: absmax by a wavefront butterfly, then quantize from registers
+// and store 8 codes per 8-byte store. Rows longer than 64*8*32 elements take
+// a two-pass variant that re-reads x.
+#include "device_common.h"
+#include "launch.h"
+
+namespace mq {
+namespace {
+
+constexpr int kRowsPerBlock = 4;
+
+__device__ __forceinline__ float chunk_absmax(u32x4 v, float m) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    f16x2 h = as_f16x2(v[w]);
+    m = fmaxf(m, fabsf(static_cast<float>(h[0])));
+    m = fmaxf(m, fabsf(static_cast<float>(h[1])));
+  }
+  return m;
+}
+
+__device__ __forceinline__ uint32_t quant4(f16x2 a, f16x2 b, float s) {
+  // s > 0 here; IEEE division then round-half-even.
+  float q0 = rintf(static_cast<float>(a[0]) / s);
+  float q1 = rintf(static_cast<float>(a[1]) / s);
+  float q2 = rintf(static_cast<float>(b[0]) / s);
+  float q3 = rintf(static_cast<float>(b[1]) / s);
+  q0 = fminf(fmaxf(q0, -127.f), 127.f);
+  q1 = fminf(fmaxf(q1, -127.f), 127.f);
+  q2 = fminf(fmaxf(q2, -127.f), 127.f);
+  q3 = fminf(fmaxf(q3, -127.f), 127.f);
+  uint32_t r = static_cast<uint32_t>(static_cast<int32_t>(q0)) & 0xFFu;
+  r |= (static_cast<uint32_t>(static_cast<int32_t>(q1)) & 0xFFu) << 8;
+  r |= (static_cast<uint32_t>(static_cast<int32_t>(q2)) & 0xFFu) << 16;
+  r |= (static_cast<uint32_t>(static_cast<int32_t>(q3)) & 0xFFu) << 24;
+  return r;
+}
+
+__device__ __forceinline__ u32x2 quant_chunk(u32x4 v, float s) {
+  u32x2 out;
+  if (s > 0.f) {
+    out[0] = quant4(as_f16x2(v[0]), as_f16x2(v[1]), s);
+    out[1] = quant4(as_f16x2(v[2]), as_f16x2(v[3]), s);
+  } else {
+    out[0] = 0u;
+    out[1] = 0u;
+  }
+  return out;
+}
+
+// CPL = 16-byte chunks per lane kept in registers (row length <= 512*CPL).
+template <int CPL>
+__global__ __launch_bounds__(256) void quant_rows_regs(const uint16_t* __restrict__ x,
+                                                       int8_t* __restrict__ xq,
+                                                       float* __restrict__ s_tok, int M, int K) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const int nchunk = K >> 3;
+  const uint16_t* xr = x + static_cast<size_t>(row) * K;
+  int8_t* qr = xq + static_cast<size_t>(row) * K;
+
+  u32x4 v[CPL];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + kWave * i;
+    if (c < nchunk) {
+      v[i] = *reinterpret_cast<const u32x4*>(xr + 8 * c);
+    } else {
+      v[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+    amax = chunk_absmax(v[i], amax);
+  }
+  amax = wave_max(amax);
+  const float s = amax / 127.0f;
+  if (lane == 0) s_tok[row] = s;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + kWave * i;
+    if (c < nchunk) *reinterpret_cast<u32x2*>(qr + 8 * c) = quant_chunk(v[i], s);
+  }
+}
+
+// Any row length: absmax pass, then a second pass that re-reads x.
+__global__ __launch_bounds__(256) void quant_rows_stream(const uint16_t* __restrict__ x,
+                                                         int8_t* __restrict__ xq,
+                                                         float* __restrict__ s_tok, int M, int K) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const int nchunk = K >> 3;
+  const uint16_t* xr = x + static_cast<size_t>(row) * K;
+  int8_t* qr = xq + static_cast<size_t>(row) * K;
+  float amax = 0.f;
+  for (int c = lane; c < nchunk; c += kWave)
+    amax = chunk_absmax(*reinterpret_cast<const u32x4*>(xr + 8 * c), amax);
+  amax = wave_max(amax);
+  const float s = amax / 127.0f;
+  if (lane == 0) s_tok[row] = s;
+  for (int c = lane; c < nchunk; c += kWave)
+    *reinterpret_cast<u32x2*>(qr + 8 * c) = quant_chunk(*reinterpret_cast<const u32x4*>(xr + 8 * c), s);
+}
+
+}  // namespace
+
+hipError_t launch_quant_per_token_int8(const uint16_t* x, int8_t* xq, float* s_tok,
+                                       int64_t M, int64_t K, hipStream_t stream) {
+  const int m = static_cast<int>(M), k = static_cast<int>(K);
+  const dim3 grid((m + kRowsPerBlock - 1) / kRowsPerBlock), block(256);
+  const int per_lane = ((k >> 3) + kWave - 1) / kWave;
+  if (per_lane <= 1) {
+    return launch_kernel(quant_rows_regs<1>, grid, block, 0, stream, x, xq, s_tok, m, k);
+  } else if (per_lane <= 2) {
+    return launch_kernel(quant_rows_regs<2>, grid, block, 0, stream, x, xq, s_tok, m, k);
+  } else if (per_lane <= 4) {
+    return launch_kernel(quant_rows_regs<4>, grid, block, 0, stream, x, xq, s_tok, m, k);
+  } else if (per_lane <= 8) {
+    return launch_kernel(quant_rows_regs<8>, grid, block, 0, stream, x, xq, s_tok, m, k);
+  } else if (per_lane <= 16) {
+    return launch_kernel(quant_rows_regs<16>, grid, block, 0, stream, x, xq, s_tok, m, k);
+  } else if (per_lane <= 32) {
+    return launch_kernel(quant_rows_regs<32>, grid, block, 0, stream, x, xq, s_tok, m, k);
+  } else {
+    return launch_kernel(quant_rows_stream, grid, block, 0, stream, x, xq, s_tok, m, k);
+  }
+}
+
+}  // namespace mq

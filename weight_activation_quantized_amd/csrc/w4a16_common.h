@@ -1,0 +1,79 @@
+// 4-bit weight unpacking into MFMA B-operand fragments (gfx950).
+//
+// Weight layout (LMDeploy toolkit overview, section 2.5: 4-bit weights in
+// groups of 128 input channels; the pages give no bit layout, so field j of
+// word c, least significant first, is column 8c+j): qweight[K, N/8] int32,
+// scales[K/128, N] fp16, qzeros[K/128, N/8] int32 packed like qweight.
+//
+// The packing runs along N while an MFMA B fragment wants 8 consecutive k of
+// one column in one lane. A lane therefore loads one word from each of 8
+// consecutive rows of the same packed column and transposes in registers:
+// for each row pair it gathers matching bytes of the two words with one
+// v_perm_b32, then each 4-bit field becomes an fp16 by OR-ing it into the
+// mantissa of 1024.0. Fields in bits 0-3 of a byte give 1024 + q, fields in
+// bits 4-7 give 1024 + 16q (no shift needed); the odd-field fragments carry
+// a factor 16 that is removed with the scale. Subtracting the zero point as
+// (1024 + z) or (1024 + 16z) is exact in fp16, so a fragment holds q - z (or
+// 16(q - z)) exactly.
+#pragma once
+
+#include "device_common.h"
+
+namespace mq {
+
+constexpr int kGroup = 128;
+
+// -(1024 + z_p) (even p) or -(1024 + 16 z_p) (odd p), replicated in both
+// fp16 halves, for the 8 fields of zero-point word zw.
+__device__ __forceinline__ void zero_bias(uint32_t zw, uint32_t (&negz)[8]) {
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const uint32_t e = (p & 1) ? (((zw >> (4 * (p - 1))) & 0xF0u) | 0xE400u)
+                               : (((zw >> (4 * p)) & 0x0Fu) | 0xE400u);
+    negz[p] = e | (e << 16);
+  }
+}
+
+// Fragments of (q - z), or 16 (q - z) for odd p, for one 32-row k-step.
+// w[e] is the word of row 8h + e; b[p][e] belongs to field p of row 8h + e.
+__device__ __forceinline__ void unpack_step(const uint32_t (&w)[8], const uint32_t (&negz)[8],
+                                            f16x8 (&b)[8]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t lo = byte_perm(w[2 * t + 1], w[2 * t], 0x05040100u);  // bytes 0,1 of both rows
+    const uint32_t hi = byte_perm(w[2 * t + 1], w[2 * t], 0x07060302u);  // bytes 2,3 of both rows
+    const uint32_t lo8 = lo >> 8, hi8 = hi >> 8;
+    const uint32_t v[8] = {nib_lo_to_f16x2(lo),  nib_hi_to_f16x2(lo),  nib_lo_to_f16x2(lo8),
+                           nib_hi_to_f16x2(lo8), nib_lo_to_f16x2(hi),  nib_hi_to_f16x2(hi),
+                           nib_lo_to_f16x2(hi8), nib_hi_to_f16x2(hi8)};
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const f16x2 d = as_f16x2(v[p]) + as_f16x2(negz[p]);
+      b[p][2 * t] = d[0];
+      b[p][2 * t + 1] = d[1];
+    }
+  }
+}
+
+// As unpack_step, then multiplied by the per-column fp16 scale pair sc2[p]
+// (s for even p, s/16 for odd p): each fragment element is fp16((q - z) * s).
+__device__ __forceinline__ void unpack_step_scaled(const uint32_t (&w)[8], const uint32_t (&negz)[8],
+                                                   const uint32_t (&sc2)[8], f16x8 (&b)[8]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t lo = byte_perm(w[2 * t + 1], w[2 * t], 0x05040100u);
+    const uint32_t hi = byte_perm(w[2 * t + 1], w[2 * t], 0x07060302u);
+    const uint32_t lo8 = lo >> 8, hi8 = hi >> 8;
+    const uint32_t v[8] = {nib_lo_to_f16x2(lo),  nib_hi_to_f16x2(lo),  nib_lo_to_f16x2(lo8),
+                           nib_hi_to_f16x2(lo8), nib_lo_to_f16x2(hi),  nib_hi_to_f16x2(hi),
+                           nib_lo_to_f16x2(hi8), nib_hi_to_f16x2(hi8)};
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const f16x2 d = (as_f16x2(v[p]) + as_f16x2(negz[p])) * as_f16x2(sc2[p]);
+      b[p][2 * t] = d[0];
+      b[p][2 * t + 1] = d[1];
+    }
+  }
+}
+
+}  // namespace mq
