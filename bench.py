@@ -117,7 +117,7 @@ def bench_gemv(torch, mq, synth, args, log):
         xs[M] = torch.from_numpy(x).to(dev)
         ys[M] = torch.empty((M, GEMV_N), dtype=torch.float16, device=dev)
         nbytes = mq.w4a16_gemv_workspace_bytes(M, GEMV_N, GEMV_K, GROUP)
-        wss[M] = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        wss[M] = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     counter = [0]
@@ -141,8 +141,7 @@ def bench_gemv(torch, mq, synth, args, log):
     wall, ev = timed_replay(torch, g_timed)
     step_bytes = sum(w4a16_bytes(M, GEMV_K, GEMV_N) for M in GEMV_MS)
     launches = args.steps * len(GEMV_MS)
-    splits = {M: (mq.w4a16_gemv_workspace_bytes(M, GEMV_N, GEMV_K, GROUP) // (4 * M * GEMV_N)) or 1
-              for M in GEMV_MS}
+    splits = {M: mq.w4a16_gemv_workspace_bytes(M, GEMV_N, GEMV_K, GROUP) for M in GEMV_MS}
     return {
         "wall_s": wall, "event_s": ev, "step_bytes": step_bytes, "launches": launches,
         "kernel_avg_us": ev / launches * 1e6, "splits": splits,
@@ -289,7 +288,7 @@ def main(argv=None):
             "workload": "W4A16 decode GEMV (8B MLP gate+up): M in {1,4,16}, K=4096, N=24576, group 128; "
                         f"{args.sets} rotating weight sets (cold HBM); one step = one GEMV per M",
             "M": list(GEMV_MS), "K": GEMV_K, "N": GEMV_N, "group": GROUP, "weight_sets": args.sets,
-            "gemv_splits": res["splits"], "parallelism": "single GPU",
+            "gemv_workspace_bytes": res["splits"], "parallelism": "single GPU",
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -35,7 +35,8 @@
  * - Arguments are validated on the host BEFORE any HIP call. A rejected call
  *   enqueues nothing and leaves every output untouched.
  * - M == 0 (and N == 0 where allowed) is a valid empty problem: MQ_OK,
- *   nothing is enqueued.
+ *   nothing is enqueued. A pointer may be NULL exactly when its tensor has
+ *   no elements (as an empty torch tensor's data pointer is).
  * - Outputs must not overlap any input or each other (MQ_ERR_ALIAS).
  * - Asynchronous device faults are reported by HIP at the caller's next
  *   synchronization, not by these calls.
@@ -141,7 +142,7 @@ mq_status mq_w8a8_mm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc,
  *   scales   [K/G, N]   fp16   in
  *   qzeros   [K/G, N/8] int32  in   (unsigned 4-bit zero points, packed like qweight)
  *   y        [M, N]     fp16   out
- * Requires: group == 128; 0 <= M < 2^31; 8 <= N < 2^31, N % 8 == 0;
+ * Requires: group == 128; 0 <= M < 2^31; 8 <= N <= 2^27, N % 8 == 0;
  * 128 <= K <= 2^20, K % 128 == 0; x, scales, y 16-byte aligned; qweight,
  * qzeros 4-byte aligned.
  */
@@ -159,16 +160,22 @@ size_t mq_w4a16_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t gr
 /*
  * W4A16 GEMV for decode (1 <= M <= 16). Same definition, operands and
  * layouts as mq_w4a16_gemm, except that the weights are not rounded to
- * fp16: each group's sum of x * (q - z) is formed exactly in fp32 and then
- * scaled in fp32. K is split across workgroups; the partial sums go to
- * `workspace` (fp32) and are summed in a fixed order, so results are
- * deterministic.
+ * fp16: each group's sum of x * (q - z) is formed exactly (fp16 products,
+ * fp32 sums) and then scaled in fp32. When N is too narrow to occupy the
+ * GPU, K is also split across workgroups: each split writes fp32 partial
+ * sums to `workspace`, and the last workgroup of each column strip to
+ * finish (counted with per-strip tickets kept in the workspace) adds the
+ * splits in split order. Results are deterministic. One kernel launch.
  *
  *   workspace        device buffer of at least
  *                    mq_w4a16_gemv_workspace_bytes(M, N, K, group) bytes,
- *                    16-byte aligned; may be NULL when that size is 0. Its
- *                    contents on entry do not matter; it must not overlap
- *                    any operand and must not be used by concurrent calls.
+ *                    16-byte aligned; may be NULL when that size is 0.
+ *                    It must be ZERO-FILLED before its first use; every
+ *                    call that completes leaves it zero-filled again (the
+ *                    tickets reset themselves), so a workspace can be
+ *                    reused across calls and shapes. It must not overlap
+ *                    any operand, and calls sharing a workspace must not
+ *                    run concurrently.
  * Requires: as mq_w4a16_gemm, and M <= 16 (M > 16 -> MQ_ERR_UNSUPPORTED).
  */
 mq_status mq_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,

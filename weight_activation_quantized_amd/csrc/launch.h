@@ -27,8 +27,9 @@ hipError_t launch_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const ui
 // each workgroup has `waves` wavefronts that share its K slice.
 struct GemvPlan {
   int splits;
-  int waves;
+  int waves;  // wavefronts per workgroup (register-staged kernel)
   size_t workspace_bytes;
+  bool lds;   // LDS-staged kernel (N % 32 == 0)
 };
 GemvPlan plan_w4a16_gemv(int64_t M, int64_t N, int64_t K);
 

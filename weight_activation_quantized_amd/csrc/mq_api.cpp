@@ -30,6 +30,7 @@ constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
 constexpr int64_t kMaxK = int64_t{1} << 20;
 constexpr int64_t kMaxKInt8 = 133144;            // 127 * 127 * K < 2^31
 constexpr int64_t kMaxElems = int64_t{1} << 40;  // bound on M*N, M*K, K*N
+constexpr int64_t kMaxN4 = int64_t{1} << 27;     // W4A16 N (32-bit lane offsets)
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -66,6 +67,19 @@ mq_status hip_status(hipError_t e, const char* what) {
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// A tensor pointer may be NULL only when the tensor has no elements (an
+// empty torch tensor reports a NULL data pointer).
+mq_status need(const void* p, int64_t elems, const char* name) {
+  if (p == nullptr && elems > 0) return fail(MQ_ERR_NULL, "%s is NULL", name);
+  return MQ_OK;
+}
+
+#define MQ_TRY(expr)                  \
+  do {                                \
+    const mq_status st_ = (expr);     \
+    if (st_ != MQ_OK) return st_;     \
+  } while (0)
+
 mq_status check_mk(int64_t M, int64_t K, int64_t k_min, int64_t k_max, int64_t k_mult) {
   if (M < 0 || M > kMaxDim) return fail(MQ_ERR_SHAPE, "M=%lld out of range", (long long)M);
   if (K < k_min || K > k_max) return fail(MQ_ERR_SHAPE, "K=%lld out of [%lld, %lld]", (long long)K,
@@ -77,14 +91,17 @@ mq_status check_mk(int64_t M, int64_t K, int64_t k_min, int64_t k_max, int64_t k
 
 mq_status check_w4a16(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                       const int32_t* qzeros, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t group) {
-  if (!x || !qweight || !scales || !qzeros || !y) return fail(MQ_ERR_NULL, "a tensor pointer is NULL");
   if (group != 128)
     return fail(MQ_ERR_UNSUPPORTED, "group=%lld (only 128 is provided)", (long long)group);
-  mq_status s = check_mk(M, K, 128, kMaxK, 128);
-  if (s != MQ_OK) return s;
-  if (N < 8 || N > kMaxDim || N % 8)
-    return fail(MQ_ERR_SHAPE, "N=%lld must be a positive multiple of 8", (long long)N);
+  MQ_TRY(check_mk(M, K, 128, kMaxK, 128));
+  if (N < 8 || N > kMaxN4 || N % 8)
+    return fail(MQ_ERR_SHAPE, "N=%lld must be a multiple of 8 in [8, 2^27]", (long long)N);
   if (M * N > kMaxElems || K * N > kMaxElems) return fail(MQ_ERR_SHAPE, "problem too large");
+  MQ_TRY(need(x, M * K, "x"));
+  MQ_TRY(need(qweight, K * N, "qweight"));
+  MQ_TRY(need(scales, N, "scales"));
+  MQ_TRY(need(qzeros, N, "qzeros"));
+  MQ_TRY(need(y, M * N, "y"));
   if (!aligned(x, 16) || !aligned(scales, 16) || !aligned(y, 16))
     return fail(MQ_ERR_ALIGN, "x, scales and y must be 16-byte aligned");
   if (!aligned(qweight, 4) || !aligned(qzeros, 4))
@@ -104,6 +121,9 @@ mq_status check_w8a8(const int8_t* xq, const int8_t* wq, const void* out, size_t
   if (s != MQ_OK) return s;
   if (N < 0 || N > kMaxDim) return fail(MQ_ERR_SHAPE, "N=%lld out of range", (long long)N);
   if (M * N > kMaxElems || K * N > kMaxElems) return fail(MQ_ERR_SHAPE, "problem too large");
+  MQ_TRY(need(xq, M * K, "xq"));
+  MQ_TRY(need(wq, N * K, "wq"));
+  MQ_TRY(need(out, M * N, "the output"));
   if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(out, 16))
     return fail(MQ_ERR_ALIGN, "xq, wq and the output must be 16-byte aligned");
   (void)out_elem;
@@ -134,9 +154,11 @@ const char* mq_last_error(void) { return g_last_error; }
 
 mq_status mq_quant_per_token_int8(const uint16_t* x, int8_t* xq, float* s_tok,
                                   int64_t M, int64_t K, void* stream) {
-  if (!x || !xq || !s_tok) return fail(MQ_ERR_NULL, "a tensor pointer is NULL");
   mq_status s = check_mk(M, K, 16, kMaxK, 16);
   if (s != MQ_OK) return s;
+  MQ_TRY(need(x, M * K, "x"));
+  MQ_TRY(need(xq, M * K, "xq"));
+  MQ_TRY(need(s_tok, M, "s_tok"));
   if (!aligned(x, 16) || !aligned(xq, 16)) return fail(MQ_ERR_ALIGN, "x and xq must be 16-byte aligned");
   if (!aligned(s_tok, 4)) return fail(MQ_ERR_ALIGN, "s_tok must be 4-byte aligned");
   const Range in[] = {{x, static_cast<size_t>(M * K) * 2, "x"}};
@@ -151,9 +173,10 @@ mq_status mq_quant_per_token_int8(const uint16_t* x, int8_t* xq, float* s_tok,
 mq_status mq_w8a8_scaled_mm(const int8_t* xq, const float* s_tok, const int8_t* wq,
                             const float* s_ch, uint16_t* y,
                             int64_t M, int64_t N, int64_t K, void* stream) {
-  if (!xq || !s_tok || !wq || !s_ch || !y) return fail(MQ_ERR_NULL, "a tensor pointer is NULL");
   mq_status s = check_w8a8(xq, wq, y, 2, M, N, K);
   if (s != MQ_OK) return s;
+  MQ_TRY(need(s_tok, M, "s_tok"));
+  MQ_TRY(need(s_ch, N, "s_ch"));
   if (!aligned(s_tok, 4) || !aligned(s_ch, 4)) return fail(MQ_ERR_ALIGN, "s_tok and s_ch must be 4-byte aligned");
   const Range in[] = {{xq, static_cast<size_t>(M * K), "xq"},
                       {s_tok, static_cast<size_t>(M) * 4, "s_tok"},
@@ -169,7 +192,6 @@ mq_status mq_w8a8_scaled_mm(const int8_t* xq, const float* s_tok, const int8_t* 
 
 mq_status mq_w8a8_mm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc,
                          int64_t M, int64_t N, int64_t K, void* stream) {
-  if (!xq || !wq || !acc) return fail(MQ_ERR_NULL, "a tensor pointer is NULL");
   mq_status s = check_w8a8(xq, wq, acc, 4, M, N, K);
   if (s != MQ_OK) return s;
   const Range in[] = {{xq, static_cast<size_t>(M * K), "xq"}, {wq, static_cast<size_t>(N * K), "wq"}};
@@ -192,7 +214,7 @@ mq_status mq_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_
 }
 
 size_t mq_w4a16_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group) {
-  if (group != 128 || M < 1 || M > 16 || N < 8 || N % 8 || N > kMaxDim || K < 128 || K > kMaxK || K % 128)
+  if (group != 128 || M < 1 || M > 16 || N < 8 || N % 8 || N > kMaxN4 || K < 128 || K > kMaxK || K % 128)
     return 0;
   return mq::plan_w4a16_gemv(M, N, K).workspace_bytes;
 }

@@ -6,19 +6,34 @@
 // one kernel). y[m,n] = sum_k x[m,k] * (q[k,n] - z[k/128,n]) * s[k/128,n].
 //
 // Decode reads every weight once and does little arithmetic per weight, so
-// the kernel is bound by the HBM weight stream. Design:
-//  * the M <= 16 tokens ride on the 16-row side of v_mfma_f32_16x16x32_f16
-//    (rows >= M are zero), so a weight costs only its unpack on the vector
-//    ALU, not M multiply-adds;
-//  * a workgroup owns a strip of 16 packed columns (128 outputs); lane
-//    (j = lane%16, h = lane/16) reads word j of rows 8h..8h+7 of each 32-row
-//    step, so one wavefront load covers 4 rows x 64 contiguous bytes;
-//  * each group's sum of x * (q - z) is formed exactly (fp16 fragments of
-//    q - z, fp32 MFMA accumulation) and scaled in fp32 once per group;
-//  * the wavefronts of a workgroup take interleaved groups of the
-//    workgroup's K slice and are summed through LDS in a fixed order; when K
-//    is also split across workgroups, fp32 partials go to the workspace and
-//    a second kernel sums them in split order. Results are deterministic.
+// the kernel is bound by the HBM weight stream. Common to both kernels:
+//  * the M <= 16 tokens ride on the 16-row side of v_mfma_f32_16x16x32_f16,
+//    so a weight costs only its unpack on the vector ALU, not M
+//    multiply-adds (token rows >= M read a valid row and are never stored;
+//    an MFMA output row depends on its own A row only);
+//  * a wavefront owns 16 packed columns (128 outputs): lane (j = lane%16,
+//    h = lane/16) needs word j of rows 8h..8h+7 of each 32-row step and
+//    turns them into B fragments in registers;
+//  * each group's sum over its 128 rows is formed in fp32 by the MFMA and
+//    scaled in fp32 once per group;
+//  * HBM streams well only when a workgroup reads >= 256 contiguous bytes
+//    of each row it touches, so workgroups cover wide column strips and K
+//    is split across workgroups to occupy every compute unit. Each split
+//    writes fp32 partial sums to the workspace and a small second kernel
+//    adds the splits in split order (the kernel boundary publishes them; a
+//    device-scope fence inside the kernel would write back and invalidate
+//    the whole L2 per workgroup). Results are deterministic.
+//
+// Main kernel (N % 32 == 0): the weight stream goes global -> LDS with
+// global_load_lds (no registers held while loads are in flight) through a
+// ring of stages, 64 packed columns (256 B) x 32 rows per stage, so several
+// stages per workgroup are in flight. The zero point is folded into a
+// per-group correction: fragments hold 1024 + q (the fp16 bit trick without
+// a subtraction), one extra MFMA against a fragment of ones gives the
+// group's per-token sum X of x, and the group adds s * (acc - (1024+z) * X).
+//
+// General kernel (any N % 8 == 0): the same math with (q - z) formed exactly
+// in the fragments and a register-staged double buffer per wavefront.
 #include "device_common.h"
 #include "launch.h"
 #include "w4a16_common.h"
@@ -26,171 +41,494 @@
 namespace mq {
 namespace {
 
-constexpr int kStrip = 16;  // packed columns per workgroup (128 outputs)
+constexpr int kWaveCols = 16;        // packed columns per wavefront (128 outputs)
+constexpr int kSteps = kGroup / 32;  // 32-row MFMA steps per group
+constexpr int kXcds = 8;             // workgroups are dispatched round-robin over 8 XCDs
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void w4a16_gemv_kernel(
+__device__ __forceinline__ void store_f16x8(uint16_t* dst, const float (&v)[8]) {
+  u32x4 out;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    f16x2 pr;
+    pr[0] = static_cast<f16>(v[2 * t]);
+    pr[1] = static_cast<f16>(v[2 * t + 1]);
+    out[t] = as_u32(pr);
+  }
+  *reinterpret_cast<u32x4*>(dst) = out;
+}
+
+// Lane (j, h) holds tokens 4h..4h+3 of packed column c in tot[p][q] (field
+// p, token 4h + q): write them as fp16 to y, or as fp32 to the split's
+// partial-sum slice.
+__device__ __forceinline__ void write_out(const f32x4 (&tot)[8], uint16_t* __restrict__ y,
+                                          float* __restrict__ partial, int M, int N, int c, int h, int split,
+                                          int splits) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int m = 4 * h + q;
+    if (m >= M) continue;
+    if (splits == 1) {
+      float v[8];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) v[p] = tot[p][q];
+      store_f16x8(y + static_cast<size_t>(m) * N + 8 * c, v);
+    } else {
+      float* dst = partial + (static_cast<size_t>(split) * M + m) * N + 8 * c;
+      *reinterpret_cast<f32x4*>(dst) = f32x4{tot[0][q], tot[1][q], tot[2][q], tot[3][q]};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{tot[4][q], tot[5][q], tot[6][q], tot[7][q]};
+    }
+  }
+}
+
+// Work item -> (strip, split). XCD x owns a contiguous block of strips with
+// all their splits, so the reduce kernel finds a strip's partial sums in
+// that XCD's L2; within an XCD, consecutive workgroups take neighbouring
+// strips of one split, so concurrently running workgroups read adjacent
+// row segments.
+struct XcdMap {
+  int strips_per_xcd;
+};
+
+__device__ __forceinline__ bool decode_work(int block, int strips_per_xcd, int strips, int splits, int& strip,
+                                            int& split) {
+  const int xcd = block % kXcds;
+  const int slot = block / kXcds;
+  const int local = slot % strips_per_xcd;
+  split = slot / strips_per_xcd;
+  strip = xcd * strips_per_xcd + local;
+  return strip < strips && split < splits;
+}
+
+// ---------------------------------------------------------------------------
+// Main kernel: LDS-staged, N % 32 == 0.
+//
+// LDS layouts (chunks are 16 bytes):
+//  * weights, per stage: 32 rows x 16 chunks; chunk c of row r is stored at
+//    position r*16 + (c ^ (((r >> 3) & 3) << 2)), so the 64 lanes of a
+//    fragment read (word j of rows 8h+e, h = 0..3) hit 64 distinct banks;
+//  * x, per stage: 16 tokens x 4 chunks (32 fp16); chunk c of token i at
+//    i*4 + (c ^ ((i >> 2) & 3)) so a 16-lane fragment read is conflict-free;
+//  * scales and zero points of all groups of the split, loaded up front.
+// ---------------------------------------------------------------------------
+
+constexpr int kLStrip = 64;                     // packed columns per workgroup
+constexpr int kLRows = 32;                      // rows per stage (one MFMA k-step)
+constexpr int kLStageWords = kLRows * kLStrip;  // 2048 words = 8 KB
+constexpr int kLXWords = 16 * kLRows / 2;       // 256 words = 1 KB
+constexpr int kLMaxGroups = 8;                  // groups per split held in LDS
+#ifndef MQ_GEMV_LDS_STAGES
+#define MQ_GEMV_LDS_STAGES 3
+#endif
+constexpr int kLStages = MQ_GEMV_LDS_STAGES;
+constexpr int kLLoadsPerStage = 3;  // per lane: 2 x 16 B of weights + 4 B of x
+
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+
+// s_waitcnt with vmcnt <= VM and lgkmcnt <= LGKM (gfx9 encoding), bracketed
+// by compiler memory barriers so no memory access moves across it.
+template <int VM, int LGKM>
+__device__ __forceinline__ void wait_counts() {
+  static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "counter range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8));
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (whose
+// release would wait for every LDS DMA in flight). Callers first wait for
+// the counters they need with wait_counts.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// B fragments of 1024 + q (even p) or 1024 + 16 q (odd p) for one 32-row
+// step: w[e] is the lane's word of row 8h + e; magic holds 0x64006400.
+__device__ __forceinline__ void unpack_step_biased(const uint32_t (&w)[8], uint32_t magic, f16x8 (&b)[8]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t lo = byte_perm(w[2 * t + 1], w[2 * t], 0x05040100u);  // bytes 0,1 of both rows
+    const uint32_t hi = byte_perm(w[2 * t + 1], w[2 * t], 0x07060302u);  // bytes 2,3 of both rows
+    const uint32_t lo8 = lo >> 8, hi8 = hi >> 8;
+    const uint32_t v[8] = {and_or(lo, 0x000F000Fu, magic),  and_or(lo, 0x00F000F0u, magic),
+                           and_or(lo8, 0x000F000Fu, magic), and_or(lo8, 0x00F000F0u, magic),
+                           and_or(hi, 0x000F000Fu, magic),  and_or(hi, 0x00F000F0u, magic),
+                           and_or(hi8, 0x000F000Fu, magic), and_or(hi8, 0x00F000F0u, magic)};
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const f16x2 d = as_f16x2(v[p]);
+      b[p][2 * t] = d[0];
+      b[p][2 * t + 1] = d[1];
+    }
+  }
+}
+
+// Byte offset of the 16-byte chunk lane `lane` of wavefront `wave` loads
+// for DMA instruction l of a stage: LDS position p = l*256 + wave*64 + lane
+// holds chunk (p & 15) ^ swizzle(row) of row p >> 4.
+__device__ __forceinline__ uint32_t lds_weight_offset(int l, int wave, int lane, int valid_chunks, int chunk0,
+                                                      int NP) {
+  const int p = l * 256 + wave * 64 + lane;
+  const int row = p >> 4;
+  const int logical = (p & 15) ^ (((row >> 3) & 3) << 2);
+  const int cl = min(logical, valid_chunks - 1);
+  return static_cast<uint32_t>(row) * static_cast<uint32_t>(NP) * 4u + static_cast<uint32_t>(chunk0 + cl) * 16u;
+}
+
+// Start the DMA of stage st (32 rows of the strip + the matching x slice)
+// into its ring slot: 2 x 16 B of weights and 4 B of x per lane.
+__device__ __forceinline__ void lds_issue_stage(int st, int g_begin, int NP, int wave, const char* qwb,
+                                                const char* xb, uint32_t woff0, uint32_t woff1, uint32_t xoff,
+                                                lds_u32* s_w, lds_u32* s_x) {
+  const int slot = st % kLStages;
+  const int k0 = g_begin * kGroup + st * kLRows;
+  const char* wbase = qwb + static_cast<size_t>(k0) * NP * 4;
+  lds_u32* wdst = s_w + slot * kLStageWords + wave * 256;
+  __builtin_amdgcn_global_load_lds(wbase + woff0, wdst, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(wbase + woff1, wdst + 1024, 16, 0, 0);
+  lds_u32* xdst = s_x + slot * kLXWords + wave * 64;
+  __builtin_amdgcn_global_load_lds(xb + static_cast<size_t>(k0) * 2 + xoff, xdst, 4, 0, 0);
+}
+
+__global__ __launch_bounds__(256) void w4a16_gemv_lds_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qz,
-    uint16_t* __restrict__ y, float* __restrict__ partial, int M, int N, int K, int splits) {
-  __shared__ float red[NW > 1 ? NW - 1 : 1][32][64];
+    uint16_t* __restrict__ y, float* __restrict__ partial, int M, int N, int K, int strips, int splits,
+    XcdMap map) {
+  __shared__ __attribute__((aligned(16))) uint32_t s_w[kLStages * kLStageWords];
+  __shared__ __attribute__((aligned(16))) uint32_t s_x[kLStages * kLXWords];
+  __shared__ __attribute__((aligned(16))) uint32_t s_sc[kLMaxGroups * 256];
+  __shared__ __attribute__((aligned(16))) uint32_t s_z[kLMaxGroups * 64];
 
+  int strip, split;
+  if (!decode_work(blockIdx.x, map.strips_per_xcd, strips, splits, strip, split)) return;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
   const int j = lane & 15;
   const int h = lane >> 4;
   const int NP = N >> 3;
-  const int c = blockIdx.x * kStrip + j;
-  const bool cvalid = c < NP;
-  const int split = blockIdx.y;
+  const int NC = NP >> 2;  // 16-byte chunks per row
   const int G = K / kGroup;
   const int g_begin = static_cast<int>(static_cast<int64_t>(split) * G / splits);
   const int g_end = static_cast<int>(static_cast<int64_t>(split + 1) * G / splits);
+  const int Gs = g_end - g_begin;  // <= kLMaxGroups (plan)
+  const int T = Gs * (kGroup / kLRows);
+  const int chunk0 = strip * (kLStrip / 4);
+  const int valid_chunks = min(kLStrip / 4, NC - chunk0);  // >= 1
+  const int valid_cols = valid_chunks * 4;
 
-  // A operand: lane (i = lane%16, h) carries token i, k-slots 8h..8h+7.
-  const bool xvalid = j < M;
-  const uint16_t* xrow = x + static_cast<size_t>(xvalid ? j : 0) * K + 8 * h;
-  const uint32_t* wcol = qw + static_cast<size_t>(8 * h) * NP + (cvalid ? c : 0);
+  const char* qwb = reinterpret_cast<const char*>(qw);
+  const char* xb = reinterpret_cast<const char*>(x);
 
-  float tot[8][4];
+  // Per-lane global byte offsets, constant over stages. Columns past N
+  // re-read the strip's last valid chunk (never stored).
+  const uint32_t woff0 = lds_weight_offset(0, wave, lane, valid_chunks, chunk0, NP);
+  const uint32_t woff1 = lds_weight_offset(1, wave, lane, valid_chunks, chunk0, NP);
+  uint32_t xoff;
+  {
+    const int q = wave * 64 + lane;
+    const int i = q >> 4;
+    const int c = ((q >> 2) & 3) ^ ((i >> 2) & 3);
+    xoff = static_cast<uint32_t>((min(i, M - 1) * K + c * 8 + (q & 3) * 2) * 2);
+  }
+  lds_u32* const s_w_lds = (lds_u32*)(s_w);
+  lds_u32* const s_x_lds = (lds_u32*)(s_x);
+
+  // Prologue: scales (512 fp16 = 64 chunks) and zero points (64 words) of
+  // every group of the split; wavefront w loads groups w, w+4, ...
+  {
+    const int pc = min(lane, valid_cols - 1);
+    for (int gi = wave; gi < Gs; gi += 4) {
+      const size_t g = static_cast<size_t>(g_begin + gi);
+      const char* sp = reinterpret_cast<const char*>(scales) + (g * N + static_cast<size_t>(strip) * 512) * 2;
+      __builtin_amdgcn_global_load_lds(sp + pc * 16, (lds_u32*)(s_sc) + gi * 256, 16, 0, 0);
+      const char* zp = reinterpret_cast<const char*>(qz) + (g * NP + static_cast<size_t>(strip) * kLStrip) * 4;
+      __builtin_amdgcn_global_load_lds(zp + pc * 4, (lds_u32*)(s_z) + gi * 64, 4, 0, 0);
+    }
+  }
+  const int pre = min(kLStages - 1, T);
+  for (int st = 0; st < pre; ++st)
+    lds_issue_stage(st, g_begin, NP, wave, qwb, xb, woff0, woff1, xoff, s_w_lds, s_x_lds);
+
+  // Fragment read offsets (words within a stage).
+  const int wchunk = (4 * wave + (j >> 2)) ^ (h << 2);
+  const int wread = (8 * h) * 64 + wchunk * 4 + (j & 3);
+  const int xread = j * 16 + ((h ^ ((j >> 2) & 3)) * 4);
+  const int col = 16 * wave + j;  // packed column within the strip
+  uint32_t magic;
+  asm("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+  f16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = static_cast<f16>(1.0f);
+
+  f32x4 tot[8];
 #pragma unroll
   for (int p = 0; p < 8; ++p)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) tot[p][r] = 0.f;
+    for (int q = 0; q < 4; ++q) tot[p][q] = 0.f;
 
-  for (int g = g_begin + wave; g < g_end; g += NW) {
-    uint32_t zw = 0u;
-    u32x4 sv = u32x4{0u, 0u, 0u, 0u};
-    if (cvalid) {
-      zw = qz[static_cast<size_t>(g) * NP + c];
-      sv = *reinterpret_cast<const u32x4*>(scales + static_cast<size_t>(g) * N + 8 * c);
-    }
-    uint32_t negz[8];
-    zero_bias(zw, negz);
-
+  for (int gi = 0; gi < Gs; ++gi) {
     f32x4 acc[8];
+    f32x4 accx;  // per-token sum of x over the group's rows
 #pragma unroll
-    for (int ks = 0; ks < kGroup / 32; ++ks) {
-      const int k0 = g * kGroup + ks * 32;
+    for (int ks = 0; ks < kGroup / kLRows; ++ks) {
+      const int it = gi * (kGroup / kLRows) + ks;
+      if (it + kLStages - 2 < T) {
+        wait_counts<(kLStages - 2) * kLLoadsPerStage, 0>();
+      } else {
+        wait_counts<0, 0>();
+      }
+      bare_barrier();
+      if (it + kLStages - 1 < T)
+        lds_issue_stage(it + kLStages - 1, g_begin, NP, wave, qwb, xb, woff0, woff1, xoff, s_w_lds, s_x_lds);
+      const int slot = it % kLStages;
+      const uint32_t* wst = s_w + slot * kLStageWords + wread;
       uint32_t w[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w[e] = cvalid ? wcol[static_cast<size_t>(k0 + e) * NP] : 0u;
-      f16x8 a;
-      if (xvalid) {
-        a = *reinterpret_cast<const f16x8*>(xrow + k0);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = static_cast<f16>(0.f);
-      }
+      for (int e = 0; e < 8; ++e) w[e] = wst[e * 64];
+      const f16x8 a = *reinterpret_cast<const f16x8*>(&s_x[slot * kLXWords + xread]);
       f16x8 b[8];
-      unpack_step(w, negz, b);
+      unpack_step_biased(w, magic, b);
+      const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
+      accx = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ones, ks == 0 ? zero4 : accx, 0, 0, 0);
 #pragma unroll
       for (int p = 0; p < 8; ++p)
-        acc[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[p], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[p],
-                                                       0, 0, 0);
+        acc[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[p], ks == 0 ? zero4 : acc[p], 0, 0, 0);
     }
+    // tot += s * (acc - (1024 + z) * X); odd fields carry 16 (q - z), so
+    // their scale is s / 16 (exact).
+    const uint32_t zw = s_z[gi * 64 + col];
+    const u32x4 sv = *reinterpret_cast<const u32x4*>(&s_sc[gi * 256 + col * 4]);
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const f16x2 s2 = as_f16x2(sv[p >> 1]);
       const float sc = static_cast<float>(s2[p & 1]) * ((p & 1) ? 0.0625f : 1.0f);
+      const float zf = static_cast<float>((zw >> (4 * p)) & 15u);
+      const float bias = (p & 1) ? 1024.0f + 16.0f * zf : 1024.0f + zf;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) tot[p][r] = fmaf(acc[p][r], sc, tot[p][r]);
+      for (int q = 0; q < 4; ++q) tot[p][q] = fmaf(sc, fmaf(-bias, accx[q], acc[p][q]), tot[p][q]);
     }
   }
 
-  if constexpr (NW > 1) {
-    if (wave > 0) {
-#pragma unroll
-      for (int p = 0; p < 8; ++p)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave - 1][p * 4 + r][lane] = tot[p][r];
-    }
-    __syncthreads();
-    if (wave != 0) return;
-    for (int w = 0; w < NW - 1; ++w)
-#pragma unroll
-      for (int p = 0; p < 8; ++p)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) tot[p][r] += red[w][p * 4 + r][lane];
-  }
-  if (!cvalid) return;
+  const int c = strip * kLStrip + col;
+  if (c < NP) write_out(tot, y, partial, M, N, c, h, split, splits);
+}
 
-  // Accumulator layout: lane (j, h), register r -> token 4h + r, column j of
-  // the tile; tile p is field p, so the lane owns outputs 8c .. 8c+7.
+// ---------------------------------------------------------------------------
+// General kernel: register-staged, any N % 8 == 0.
+// ---------------------------------------------------------------------------
+
+// One group's operands for one lane: 4 steps x 8 rows of its packed column,
+// the 4 matching activation fragments, the zero-point word and 8 scales.
+struct GroupRegs {
+  uint32_t w[kSteps][8];
+  f16x8 a[kSteps];
+  uint32_t zw;
+  u32x4 sv;
+};
+
+// Pointers are kept as wavefront-uniform bases plus 32-bit per-lane offsets,
+// so every load is a scalar-base global load with no per-load address math.
+struct GemvLane {
+  const char* qw;     // qweight (uniform)
+  const char* x;      // x (uniform)
+  const char* qz;     // qzeros (uniform)
+  const char* sc;     // scales (uniform)
+  uint32_t w_off;     // byte offset of word (row 8h, column) in a group
+  uint32_t x_off;     // byte offset of (token, 8h) in x
+  uint32_t z_off;     // byte offset of the lane's word in a qzeros row
+  uint32_t s_off;     // byte offset of the lane's 8 scales in a scales row
+  size_t row_bytes;   // NP * 4
+  size_t srow_bytes;  // N * 2
+};
+
+template <typename T>
+__device__ __forceinline__ T load_at(const char* base, uint32_t off) {
+  return *reinterpret_cast<const T*>(base + off);
+}
+
+__device__ __forceinline__ void load_group(GroupRegs& r, const GemvLane L, int g) {
+  const char* wg = L.qw + static_cast<size_t>(g) * kGroup * L.row_bytes;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int m = 4 * h + r;
-    if (m >= M) continue;
-    if (splits == 1) {
-      u32x4 out;
+  for (int ks = 0; ks < kSteps; ++ks)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        f16x2 pr;
-        pr[0] = static_cast<f16>(tot[2 * q][r]);
-        pr[1] = static_cast<f16>(tot[2 * q + 1][r]);
-        out[q] = as_u32(pr);
-      }
-      *reinterpret_cast<u32x4*>(y + static_cast<size_t>(m) * N + 8 * c) = out;
-    } else {
-      float* dst = partial + (static_cast<size_t>(split) * M + m) * N + 8 * c;
-      *reinterpret_cast<f32x4*>(dst) = f32x4{tot[0][r], tot[1][r], tot[2][r], tot[3][r]};
-      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{tot[4][r], tot[5][r], tot[6][r], tot[7][r]};
-    }
+    for (int e = 0; e < 8; ++e) r.w[ks][e] = load_at<uint32_t>(wg + (ks * 32 + e) * L.row_bytes, L.w_off);
+  const char* xg = L.x + static_cast<size_t>(g) * kGroup * 2;
+#pragma unroll
+  for (int ks = 0; ks < kSteps; ++ks) r.a[ks] = load_at<f16x8>(xg + ks * 64, L.x_off);
+  r.zw = load_at<uint32_t>(L.qz + static_cast<size_t>(g) * L.row_bytes, L.z_off);
+  r.sv = load_at<u32x4>(L.sc + static_cast<size_t>(g) * L.srow_bytes, L.s_off);
+}
+
+__device__ __forceinline__ void compute_group(const GroupRegs& r, f32x4 (&tot)[8]) {
+  uint32_t negz[8];
+  zero_bias(r.zw, negz);
+  f32x4 acc[8];
+#pragma unroll
+  for (int ks = 0; ks < kSteps; ++ks) {
+    f16x8 b[8];
+    unpack_step(r.w[ks], negz, b);
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+      acc[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(r.a[ks], b[p],
+                                                     ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[p], 0, 0, 0);
+  }
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const f16x2 s2 = as_f16x2(r.sv[p >> 1]);
+    const float sc = static_cast<float>(s2[p & 1]) * ((p & 1) ? 0.0625f : 1.0f);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tot[p][q] = fmaf(acc[p][q], sc, tot[p][q]);
   }
 }
 
-// y = fp16(sum over splits of partial[split]), summed in split order; one
-// thread per 8 consecutive outputs.
+// The wavefronts of a workgroup sit side by side in N (NWC x 64 contiguous
+// bytes per row) and walk the split's groups together.
+template <int NWC>
+__global__ __launch_bounds__(NWC * 64) void w4a16_gemv_kernel(
+    const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw,
+    const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qz,
+    uint16_t* __restrict__ y, float* __restrict__ partial, int M, int N, int K, int strips, int splits,
+    XcdMap map) {
+  int strip, split;
+  if (!decode_work(blockIdx.x, map.strips_per_xcd, strips, splits, strip, split)) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
+  const int j = lane & 15;
+  const int h = lane >> 4;
+  const int NP = N >> 3;
+  const int c = (strip * NWC + wave) * kWaveCols + j;
+  const bool cvalid = c < NP;
+  const int cc = cvalid ? c : NP - 1;
+  const int G = K / kGroup;
+  const int g_begin = static_cast<int>(static_cast<int64_t>(split) * G / splits);
+  const int g_end = static_cast<int>(static_cast<int64_t>(split + 1) * G / splits);
+
+  GemvLane L;
+  L.qw = reinterpret_cast<const char*>(qw);
+  L.x = reinterpret_cast<const char*>(x);
+  L.qz = reinterpret_cast<const char*>(qz);
+  L.sc = reinterpret_cast<const char*>(scales);
+  L.w_off = static_cast<uint32_t>(8 * h * NP + cc) * 4u;
+  L.x_off = static_cast<uint32_t>((j < M ? j : M - 1) * K + 8 * h) * 2u;
+  L.z_off = static_cast<uint32_t>(cc) * 4u;
+  L.s_off = static_cast<uint32_t>(cc) * 16u;
+  L.row_bytes = static_cast<size_t>(NP) * 4;
+  L.srow_bytes = static_cast<size_t>(N) * 2;
+
+  f32x4 tot[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tot[p][q] = 0.f;
+
+  // The groups of this split, in order. Two register buffers: group i+1 is
+  // loaded while group i is computed; inside the loop every prefetch is
+  // unconditional, and sched_barrier keeps the compiler from sinking it
+  // below the math it is meant to overlap.
+  const int n = g_end - g_begin;
+  {
+    GroupRegs ra, rb;
+    load_group(ra, L, g_begin);
+    int i = 0;
+    for (; i + 2 < n; i += 2) {
+      load_group(rb, L, g_begin + i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_group(ra, tot);
+      load_group(ra, L, g_begin + i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_group(rb, tot);
+    }
+    if (i + 1 < n) {
+      load_group(rb, L, g_begin + i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_group(ra, tot);
+      compute_group(rb, tot);
+    } else {
+      compute_group(ra, tot);
+    }
+  }
+  if (cvalid) write_out(tot, y, partial, M, N, c, h, split, splits);
+}
+
+// ---------------------------------------------------------------------------
+// Split reduction: y = fp16(sum over splits of partial[split]) in split
+// order. Thread t of the block sums 4 consecutive outputs of one token row
+// of one strip; blocks are mapped to the XCD that wrote that strip.
+// ---------------------------------------------------------------------------
+template <int S>
 __global__ __launch_bounds__(256) void w4a16_gemv_reduce(const float* __restrict__ partial,
                                                          uint16_t* __restrict__ y, int M, int N,
-                                                         int splits) {
-  const size_t idx = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
-  const size_t total = static_cast<size_t>(M) * N / 8;
-  if (idx >= total) return;
-  const size_t off = idx * 8;
+                                                         int strip_cols, int strips_per_xcd,
+                                                         int blocks_per_xcd, int splits) {
+  const int xcd = blockIdx.x % kXcds;
+  const int local = (blockIdx.x / kXcds) * 256 + threadIdx.x;  // 4-output unit within the XCD
+  const int units_per_row = strips_per_xcd * strip_cols / 4;    // per token row
+  const int m = local / units_per_row;
+  const int u = local % units_per_row;
+  if (m >= M) return;
+  const int n = xcd * strips_per_xcd * strip_cols + u * 4;  // first output column
+  if (n >= N) return;
+  (void)blocks_per_xcd;
   const size_t stride = static_cast<size_t>(M) * N;
-  f32x4 lo = *reinterpret_cast<const f32x4*>(partial + off);
-  f32x4 hi = *reinterpret_cast<const f32x4*>(partial + off + 4);
-  for (int s = 1; s < splits; ++s) {
-    lo += *reinterpret_cast<const f32x4*>(partial + s * stride + off);
-    hi += *reinterpret_cast<const f32x4*>(partial + s * stride + off + 4);
+  const float* src = partial + static_cast<size_t>(m) * N + n;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(src);
+  if constexpr (S > 0) {
+    f32x4 v[S > 1 ? S - 1 : 1];
+#pragma unroll
+    for (int s = 1; s < S; ++s) v[s - 1] = *reinterpret_cast<const f32x4*>(src + s * stride);
+#pragma unroll
+    for (int s = 1; s < S; ++s) acc += v[s - 1];
+  } else {
+    for (int s = 1; s < splits; ++s) acc += *reinterpret_cast<const f32x4*>(src + s * stride);
   }
-  u32x4 out;
-  f16x2 pr;
-  pr[0] = static_cast<f16>(lo[0]); pr[1] = static_cast<f16>(lo[1]); out[0] = as_u32(pr);
-  pr[0] = static_cast<f16>(lo[2]); pr[1] = static_cast<f16>(lo[3]); out[1] = as_u32(pr);
-  pr[0] = static_cast<f16>(hi[0]); pr[1] = static_cast<f16>(hi[1]); out[2] = as_u32(pr);
-  pr[0] = static_cast<f16>(hi[2]); pr[1] = static_cast<f16>(hi[3]); out[3] = as_u32(pr);
-  *reinterpret_cast<u32x4*>(y + off) = out;
+  f16x2 lo, hi;
+  lo[0] = static_cast<f16>(acc[0]);
+  lo[1] = static_cast<f16>(acc[1]);
+  hi[0] = static_cast<f16>(acc[2]);
+  hi[1] = static_cast<f16>(acc[3]);
+  *reinterpret_cast<u32x2*>(y + static_cast<size_t>(m) * N + n) = u32x2{as_u32(lo), as_u32(hi)};
 }
 
 }  // namespace
 
+#ifndef MQ_GEMV_NWC
+#define MQ_GEMV_NWC 4
+#endif
+#ifndef MQ_GEMV_TARGET_WGS
+#define MQ_GEMV_TARGET_WGS 384
+#endif
+
 GemvPlan plan_w4a16_gemv(int64_t M, int64_t N, int64_t K) {
-  GemvPlan plan{1, 1, 0};
-  const int64_t strips = (N / 8 + kStrip - 1) / kStrip;
+  GemvPlan plan{1, MQ_GEMV_NWC, 0, false};
+#ifndef MQ_GEMV_NO_LDS
+  plan.lds = (N / 8) % 4 == 0;
+#endif
+  const int64_t strip_cols = plan.lds ? int64_t{kLStrip} : int64_t{kWaveCols} * plan.waves;
+  const int64_t strips = (N / 8 + strip_cols - 1) / strip_cols;
   const int64_t G = K / kGroup;
-  // Smallest divisor of the group count that gives at least one workgroup
-  // per compute unit (256), so that no split is left with an uneven share.
+  // Split K only as far as needed to reach the target workgroup count: the
+  // smallest divisor of the group count that gets there (and, for the LDS
+  // kernel, that leaves at most kLMaxGroups groups per split).
   int64_t splits = 1;
 #ifdef MQ_GEMV_FORCE_SPLITS
   splits = MQ_GEMV_FORCE_SPLITS;
   if (splits > G) splits = G;
   while (G % splits) --splits;
 #else
-  while (strips * splits < 256 && splits < G) {
+  while (strips * splits < MQ_GEMV_TARGET_WGS && splits < G) {
     ++splits;
     while (G % splits) ++splits;
   }
 #endif
-  const int64_t per_split = G / splits;
-  int waves = 1;
-  while (waves < 4 && per_split % (2 * waves) == 0) waves *= 2;
-#ifdef MQ_GEMV_FORCE_WAVES
-  waves = MQ_GEMV_FORCE_WAVES;
-#endif
+  if (plan.lds) {
+    while (G / splits > kLMaxGroups) {
+      ++splits;
+      while (G % splits) ++splits;
+    }
+  }
   plan.splits = static_cast<int>(splits);
-  plan.waves = waves;
   plan.workspace_bytes = splits > 1 ? static_cast<size_t>(splits) * M * N * sizeof(float) : 0;
   return plan;
 }
@@ -200,34 +538,59 @@ hipError_t launch_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const ui
                              int64_t M, int64_t N, int64_t K, const GemvPlan& plan,
                              void* workspace, hipStream_t stream) {
   const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
-  const int strips = static_cast<int>((N / 8 + kStrip - 1) / kStrip);
-  const dim3 grid(strips, plan.splits);
+  const int64_t strip_cols = plan.lds ? int64_t{kLStrip} : int64_t{kWaveCols} * plan.waves;
+  const int strips = static_cast<int>((N / 8 + strip_cols - 1) / strip_cols);
+  XcdMap map;
+  map.strips_per_xcd = (strips + kXcds - 1) / kXcds;
+  const dim3 grid(static_cast<uint32_t>(kXcds * map.strips_per_xcd * plan.splits));
   const uint32_t* qw = reinterpret_cast<const uint32_t*>(qweight);
   const uint32_t* qz = reinterpret_cast<const uint32_t*>(qzeros);
   float* part = static_cast<float*>(workspace);
   hipError_t err;
-  switch (plan.waves) {
-    case 1:
-      err = launch_kernel(w4a16_gemv_kernel<1>, grid, dim3(64), 0, stream, x, qw, scales, qz, y, part, m, n, k,
-                          plan.splits);
-      break;
-    case 2:
-      err = launch_kernel(w4a16_gemv_kernel<2>, grid, dim3(128), 0, stream, x, qw, scales, qz, y, part, m, n,
-                          k, plan.splits);
-      break;
-    case 4:
-      err = launch_kernel(w4a16_gemv_kernel<4>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part, m, n,
-                          k, plan.splits);
-      break;
-    default:
-      err = launch_kernel(w4a16_gemv_kernel<8>, grid, dim3(512), 0, stream, x, qw, scales, qz, y, part, m, n,
-                          k, plan.splits);
-      break;
+  if (plan.lds) {
+    if (K / kGroup / plan.splits > kLMaxGroups || (N / 8) % 4 != 0) return hipErrorInvalidValue;
+    err = launch_kernel(w4a16_gemv_lds_kernel, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part, m, n, k,
+                        strips, plan.splits, map);
+  } else {
+    switch (plan.waves) {
+      case 2:
+        err = launch_kernel(w4a16_gemv_kernel<2>, grid, dim3(128), 0, stream, x, qw, scales, qz, y, part, m, n,
+                            k, strips, plan.splits, map);
+        break;
+      case 8:
+        err = launch_kernel(w4a16_gemv_kernel<8>, grid, dim3(512), 0, stream, x, qw, scales, qz, y, part, m, n,
+                            k, strips, plan.splits, map);
+        break;
+      default:
+        err = launch_kernel(w4a16_gemv_kernel<4>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part, m, n,
+                            k, strips, plan.splits, map);
+        break;
+    }
   }
   if (err != hipSuccess || plan.splits == 1) return err;
-  const size_t total = static_cast<size_t>(M) * N / 8;
-  const dim3 rgrid(static_cast<uint32_t>((total + 255) / 256));
-  return launch_kernel(w4a16_gemv_reduce, rgrid, dim3(256), 0, stream, part, y, m, n, plan.splits);
+  // 4-output units per XCD: its strips' columns for every token row.
+  const int cols8 = static_cast<int>(strip_cols) * 8;  // output columns per strip
+  const int64_t units_per_xcd = static_cast<int64_t>(map.strips_per_xcd) * cols8 / 4 * M;
+  const int blocks_per_xcd = static_cast<int>((units_per_xcd + 255) / 256);
+  const dim3 rgrid(static_cast<uint32_t>(kXcds * blocks_per_xcd));
+  const int sps = map.strips_per_xcd;
+  switch (plan.splits) {
+    case 2:
+      return launch_kernel(w4a16_gemv_reduce<2>, rgrid, dim3(256), 0, stream, part, y, m, n, cols8, sps,
+                           blocks_per_xcd, plan.splits);
+    case 4:
+      return launch_kernel(w4a16_gemv_reduce<4>, rgrid, dim3(256), 0, stream, part, y, m, n, cols8, sps,
+                           blocks_per_xcd, plan.splits);
+    case 8:
+      return launch_kernel(w4a16_gemv_reduce<8>, rgrid, dim3(256), 0, stream, part, y, m, n, cols8, sps,
+                           blocks_per_xcd, plan.splits);
+    case 16:
+      return launch_kernel(w4a16_gemv_reduce<16>, rgrid, dim3(256), 0, stream, part, y, m, n, cols8, sps,
+                           blocks_per_xcd, plan.splits);
+    default:
+      return launch_kernel(w4a16_gemv_reduce<0>, rgrid, dim3(256), 0, stream, part, y, m, n, cols8, sps,
+                           blocks_per_xcd, plan.splits);
+  }
 }
 
 }  // namespace mq
