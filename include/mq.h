@@ -160,22 +160,21 @@ size_t mq_w4a16_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t gr
 /*
  * W4A16 GEMV for decode (1 <= M <= 16). Same definition, operands and
  * layouts as mq_w4a16_gemm, except that the weights are not rounded to
- * fp16: each group's sum of x * (q - z) is formed exactly (fp16 products,
- * fp32 sums) and then scaled in fp32. When N is too narrow to occupy the
- * GPU, K is also split across workgroups: each split writes fp32 partial
- * sums to `workspace`, and the last workgroup of each column strip to
- * finish (counted with per-strip tickets kept in the workspace) adds the
- * splits in split order. Results are deterministic. One kernel launch.
+ * fp16: per group of 128 rows the kernel forms, in fp32, the sum of
+ * x * (q - z) and scales it by s in fp32. (For N % 32 == 0 the sum is
+ * taken as sum(x * (1024 + q)) - (1024 + z) * sum(x), with exact fp16
+ * products; otherwise (q - z) is formed exactly first.) Outputs meet the
+ * same tolerance as mq_w4a16_gemm. K is split across workgroups when N is
+ * too narrow to occupy the GPU: each split writes fp32 partial sums to
+ * `workspace` and a second kernel on the same stream adds the splits in
+ * split order. Results are deterministic.
  *
  *   workspace        device buffer of at least
  *                    mq_w4a16_gemv_workspace_bytes(M, N, K, group) bytes,
  *                    16-byte aligned; may be NULL when that size is 0.
- *                    It must be ZERO-FILLED before its first use; every
- *                    call that completes leaves it zero-filled again (the
- *                    tickets reset themselves), so a workspace can be
- *                    reused across calls and shapes. It must not overlap
- *                    any operand, and calls sharing a workspace must not
- *                    run concurrently.
+ *                    Its contents on entry do not matter. It must not
+ *                    overlap any operand, and calls sharing a workspace
+ *                    must be ordered (same stream or synchronized).
  * Requires: as mq_w4a16_gemm, and M <= 16 (M > 16 -> MQ_ERR_UNSUPPORTED).
  */
 mq_status mq_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,

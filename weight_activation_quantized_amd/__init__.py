@@ -213,17 +213,16 @@ def w4a16_gemv_workspace_bytes(M, N, K, group=128):
 def w4a16_gemv(x, qweight, scales, qzeros, group=128, out=None, workspace=None, stream=None):
     """W4A16 GEMV for decode (M <= 16).
 
-    ``workspace``: a zero-filled uint8 GPU tensor of at least
-    ``w4a16_gemv_workspace_bytes`` bytes (allocated zero-filled if None). The
-    call leaves it zero-filled, so it can be reused by later calls that do
-    not run concurrently with this one.
+    ``workspace``: a uint8 GPU tensor of at least ``w4a16_gemv_workspace_bytes``
+    bytes (allocated if None); its contents do not matter. Calls sharing a
+    workspace must be ordered on the GPU (for example, the same stream).
     """
     torch = _torch()
     M, N, K = _w4a16_shapes(x, qweight, scales, qzeros, group)
     y = _out(out, (M, N), torch.float16, x, "out")
     need = w4a16_gemv_workspace_bytes(M, N, K, group)
     if workspace is None and need:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     with torch.cuda.device(x.device):
