@@ -85,7 +85,8 @@ def _w8a8_operands(M, K, N, tag, outliers=0.01):
 
 
 @pytest.mark.parametrize("M,N,K", [(2048, 4096, 4096), (200, 300, 272), (1, 8, 16), (3, 1, 64),
-                                   (129, 257, 4112), (64, 6144, 4096)])
+                                   (129, 257, 4112), (64, 6144, 4096), (300, 1000, 400), (513, 130, 48),
+                                   (600, 2050, 96), (1300, 384, 256)])
 def test_w8a8_acc_bitexact(M, N, K):
     xq, _, wq, _ = _w8a8_operands(M, K, N, tag=M + N + K)
     announce(f"w8a8 i32 M={M} N={N} K={K}")

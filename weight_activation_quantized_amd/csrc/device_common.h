@@ -13,6 +13,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// LDS (address space 3) views for the direct global -> LDS loads.
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWave = 64;
 
@@ -49,6 +55,25 @@ __device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask, uint32_t m
   uint32_t r;
   asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "s"(mask), "v"(magic));
   return r;
+}
+
+// s_waitcnt with vmcnt <= VM and lgkmcnt <= LGKM (gfx9 encoding), bracketed
+// by compiler memory barriers so no memory access moves across it.
+template <int VM, int LGKM>
+__device__ __forceinline__ void wait_counts() {
+  static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "counter range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8));
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (whose
+// release would wait for every LDS DMA in flight). Callers first wait for
+// the counters they need with wait_counts.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 }  // namespace mq

@@ -122,27 +122,6 @@ constexpr int kLMaxGroups = 8;                  // groups per split held in LDS
 constexpr int kLStages = MQ_GEMV_LDS_STAGES;
 constexpr int kLLoadsPerStage = 3;  // per lane: 2 x 16 B of weights + 4 B of x
 
-typedef __attribute__((address_space(3))) uint32_t lds_u32;
-
-// s_waitcnt with vmcnt <= VM and lgkmcnt <= LGKM (gfx9 encoding), bracketed
-// by compiler memory barriers so no memory access moves across it.
-template <int VM, int LGKM>
-__device__ __forceinline__ void wait_counts() {
-  static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "counter range");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8));
-  asm volatile("" ::: "memory");
-}
-
-// Workgroup barrier without the memory fence of __syncthreads (whose
-// release would wait for every LDS DMA in flight). Callers first wait for
-// the counters they need with wait_counts.
-__device__ __forceinline__ void bare_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // B fragments of 1024 + q (even p) or 1024 + 16 q (odd p) for one 32-row
 // step: w[e] is the lane's word of row 8h + e; magic holds 0x64006400.
 __device__ __forceinline__ void unpack_step_biased(const uint32_t (&w)[8], uint32_t magic, f16x8 (&b)[8]) {
