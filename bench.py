@@ -18,11 +18,15 @@ value = algorithmic bytes of a step (x + qweight + scales + qzeros + y, for
 the three calls) / wall time of a step, between device synchronizations.
 
 Also reported (same line):
-  roofline     the GEMV kernel: algorithmic bytes per launch / average launch
-               duration from HIP events around the timed graph replay, against
-               8 TB/s; `traffic` = FETCH_SIZE + WRITE_SIZE per launch from a
-               committed rocprofv3 counter summary when it matches the current
-               kernel source, else null.
+  roofline     one GEMV call, the unit that dominates the step: its main
+               kernel (w4a16_gemv_lds_kernel) and, when K is split across
+               workgroups, the split reduction (w4a16_gemv_reduce) that follows
+               it on the same stream. achieved = algorithmic bytes per call /
+               average call duration from HIP events recorded on that stream
+               around the timed graph replay, against 8 TB/s; `traffic` =
+               FETCH_SIZE + WRITE_SIZE per call (both kernels) from a committed
+               rocprofv3 counter summary when it matches the current kernel
+               source, else null.
   prefill      W8A8 prefill (per-token quant + scaled int8 GEMM, M=2048,
                K=N=4096) and W4A16 prefill GEMMs (M=4096, K=4096/12288,
                N=4096): kernel time and TOPS against the dense MFMA peaks.
@@ -294,7 +298,8 @@ def main(argv=None):
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": load_traffic(res["bytes_per_launch_avg"]),
-            "kernel": "w4a16_gemv_kernel", "avg_launch_us": round(res["kernel_avg_us"], 3),
+            "kernel": "w4a16_gemv call (w4a16_gemv_lds_kernel + w4a16_gemv_reduce)",
+            "avg_launch_us": round(res["kernel_avg_us"], 3),
             "algorithmic_bytes_per_launch": res["bytes_per_launch_avg"],
         },
     }

@@ -157,7 +157,8 @@ def test_w4a16_gemv_decode_c1(M):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 128, 8), (3, 384, 424), (7, 384, 424), (13, 1024, 1032),
-                                   (16, 256, 4096), (2, 4096, 6144), (5, 12288, 4096), (16, 128, 24576)])
+                                   (16, 256, 4096), (2, 4096, 6144), (5, 12288, 4096), (16, 128, 24576),
+                                   (3, 4096, 128), (5, 2048, 136), (16, 8192, 520)])
 def test_w4a16_gemv_shapes(M, K, N):
     d = _w4(M, K, N, outliers=0.005, tag=M * 7 + K + N)
     assert_fp16_close(_run_w4(mq.w4a16_gemv, d, "shape"), _ref_w4(d), f"gemv M={M} K={K} N={N}")
