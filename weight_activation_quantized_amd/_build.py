@@ -37,6 +37,13 @@ FLAGS = [
     f"-I{CSRC}",
 ]
 
+# Per-source extra flags. The GEMV starts its nine MFMAs of a step from zero
+# every step; the VGPR form gives each its own destination (otherwise they
+# share one AGPR quad and wait on each other's copy-out).
+SOURCE_FLAGS = {
+    "w4a16_gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
 
 def _run(cmd):
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -53,7 +60,7 @@ def build(out=LIB_PATH, defines=(), build_dir=BUILD_DIR, jobs=None, verbose=Fals
 
     def compile_one(src):
         obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-        _run([HIPCC, *FLAGS, *dflags, "-c", os.path.join(CSRC, src), "-o", obj])
+        _run([HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), *dflags, "-c", os.path.join(CSRC, src), "-o", obj])
         return obj
 
     jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 2) // 2))
