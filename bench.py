@@ -61,10 +61,13 @@ def w4a16_bytes(M, K, N, G=GROUP):
 
 
 def gemv_source_hash():
+    """Hash of what the GEMV kernels are built from: their sources and flags."""
+    from weight_activation_quantized_amd import _build
     h = hashlib.sha256()
     for f in GEMV_SOURCES:
         with open(os.path.join(ROOT, "weight_activation_quantized_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
+    h.update(repr((_build.FLAGS[:-2], _build.SOURCE_FLAGS.get("w4a16_gemv.hip", []))).encode())
     return h.hexdigest()[:16]
 
 
