@@ -86,7 +86,11 @@ def _w8a8_operands(M, K, N, tag, outliers=0.01):
 
 @pytest.mark.parametrize("M,N,K", [(2048, 4096, 4096), (200, 300, 272), (1, 8, 16), (3, 1, 64),
                                    (129, 257, 4112), (64, 6144, 4096), (300, 1000, 400), (513, 130, 48),
-                                   (600, 2050, 96), (1300, 384, 256)])
+                                   (600, 2050, 96), (1300, 384, 256),
+                                   # decode-shaped: one, two and four 16-token tiles, ragged N and K
+                                   (1, 6144, 4096), (8, 4096, 12288), (17, 24576, 4096), (33, 1000, 400),
+                                   (5, 130, 48), (64, 4096, 16), (16, 17, 4112), (32, 4096, 12288),
+                                   (48, 6144, 4096), (20, 6200, 272), (64, 24576, 128)])
 def test_w8a8_acc_bitexact(M, N, K):
     xq, _, wq, _ = _w8a8_operands(M, K, N, tag=M + N + K)
     announce(f"w8a8 i32 M={M} N={N} K={K}")
@@ -97,7 +101,9 @@ def test_w8a8_acc_bitexact(M, N, K):
     assert bad.size == 0, f"{len(bad)} accumulators differ, first at {bad[:3].tolist()}"
 
 
-@pytest.mark.parametrize("M,N,K", [(2048, 4096, 4096), (200, 300, 272), (1, 8, 16), (129, 257, 4112)])
+@pytest.mark.parametrize("M,N,K", [(2048, 4096, 4096), (200, 300, 272), (1, 8, 16), (129, 257, 4112),
+                                   (1, 24576, 4096), (8, 6144, 4096), (64, 4096, 12288), (40, 1000, 400),
+                                   (64, 8192, 4096), (30, 6176, 4112)])
 def test_w8a8_scaled(M, N, K):
     xq, s_tok, wq, s_ch = _w8a8_operands(M, K, N, tag=7 * M + N + K)
     announce(f"w8a8 scaled M={M} N={N} K={K}")

@@ -18,6 +18,14 @@ hipError_t launch_w8a8_gemm(const int8_t* xq, const float* s_tok, const int8_t* 
                             const float* s_ch, uint16_t* y, int32_t* acc,
                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+// Decode-shaped form of the same product (M <= kW8A8GemvMaxM), bound by the
+// weight stream; launch_w8a8_gemm dispatches to it where w8a8_use_gemv says.
+constexpr int64_t kW8A8GemvMaxM = 64;
+bool w8a8_use_gemv(int64_t M, int64_t N);
+hipError_t launch_w8a8_gemv(const int8_t* xq, const float* s_tok, const int8_t* wq,
+                            const float* s_ch, uint16_t* y, int32_t* acc,
+                            int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 // W4A16 GEMM y[M,N] = x[M,K] . dequant(qweight, scales, qzeros) with group 128.
 hipError_t launch_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                              const int32_t* qzeros, uint16_t* y,

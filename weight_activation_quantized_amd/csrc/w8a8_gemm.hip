@@ -364,6 +364,7 @@ __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __res
 hipError_t launch_w8a8_gemm(const int8_t* xq, const float* s_tok, const int8_t* wq,
                             const float* s_ch, uint16_t* y, int32_t* acc,
                             int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (w8a8_use_gemv(M, N)) return launch_w8a8_gemv(xq, s_tok, wq, s_ch, y, acc, M, N, K, stream);
   const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
   const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
   const int tiles_n = static_cast<int>((N + kBN - 1) / kBN);

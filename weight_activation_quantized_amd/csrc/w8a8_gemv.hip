@@ -1,0 +1,213 @@
+// W8A8 int8 GEMM for decode-shaped M (M <= 64) on gfx950.
+//
+// Source: pymllm Setup and Usage, Overview (int8 activations and weights on
+// INT8 matrix units) and section "W8A8 first-run JIT compilation" (int8
+// scaled matmul). acc[m,n] = sum_k xq[m,k] * wq[n,k] (exact int32);
+// y[m,n] = fp16(fl32(fl32(acc) * s_tok[m]) * s_ch[n]).
+//
+// With few tokens the layer is bound by the weight stream (N*K bytes), so
+// this kernel reads every weight byte once with as many bytes in flight as
+// possible:
+// - A workgroup owns 16 (or, for more tokens and large N, 32) output
+//   channels; its four wavefronts split K into four contiguous quarters, so
+//   each wavefront streams 16 or 32 weight rows of K/4 contiguous bytes. The int32 partial sums of the four quarters are
+//   added in LDS (integer addition: exact, order-free).
+// - v_mfma_i32_16x16x64_i8 with the weight rows as the A operand (lane
+//   (i = lane%16, h = lane/16) takes 16 consecutive k of row i, one 16-byte
+//   load) and up to four 16-token tiles of xq as B operands. Every
+//   workgroup reads all of xq (from L2); past 16 tokens these re-reads,
+//   not HBM, limit the kernel.
+// - Two register sets of k-steps alternate: the loads of one are issued
+//   before the MFMAs of the other, so about 4-8 KB of weights per
+//   wavefront stay in flight. Buffer loads past a descriptor's
+//   size return zero (rows past N, tokens past M); k-chunks past the
+//   wavefront's quarter are sent past the end too.
+#include "device_common.h"
+#include "launch.h"
+
+namespace mq {
+namespace {
+
+constexpr int kQuarters = 4;              // wavefronts, one K quarter each
+constexpr uint32_t kOob = 0x80000000u;    // a buffer offset past every tile: the load returns 0
+constexpr int kBufferFlags = 0x00020000;  // gfx9 buffer descriptor word 3 (raw 32-bit data)
+
+// 64-byte k-steps per register set: two sets alternate, so one set's loads
+// are in flight while the other's MFMAs run. With kLoads 16-byte loads per
+// lane and k-step, about 16 loads per set keeps both sets in the register
+// file (140-150 VGPRs).
+template <int kLoads>
+constexpr int steps_per_set() {
+  return 16 / kLoads < 2 ? 2 : (16 / kLoads > 8 ? 8 : 16 / kLoads);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(n), kBufferFlags);
+}
+
+// One register set: kU k-steps of kA 16-byte weight chunks (one per 16
+// channels) and kT 16-byte activation chunks (one per 16 tokens) per lane.
+template <int kU, int kA, int kT>
+struct Frags {
+  i32x4 w[kU][kA];
+  i32x4 x[kU][kT];
+};
+
+// The wavefront's K range [k_begin, k_end) in 64-byte steps j = 0 .. n64-1;
+// lane group h takes bytes 16 h .. 16 h + 15 of a step. Steps at or past
+// n64, and the lanes of a ragged last step that fall past k_end, load zeros.
+struct Walk {
+  int k_begin, k_end, n64;
+  __device__ __forceinline__ int chunk(int j, int h) const {
+    const int kc = k_begin + 64 * j + 16 * h;
+    return (j < n64 && kc < k_end) ? kc : -1;
+  }
+};
+
+template <int kU, int kA, int kT>
+__device__ __forceinline__ void issue(Frags<kU, kA, kT>& f, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rx,
+                                      int i, int h, int K, const Walk& wk, int j0) {
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const int kc = wk.chunk(j0 + u, h);
+#pragma unroll
+    for (int a = 0; a < kA; ++a)
+      f.w[u][a] = __builtin_bit_cast(
+          i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, kc >= 0 ? static_cast<uint32_t>((16 * a + i) * K + kc) : kOob, 0, 0));
+#pragma unroll
+    for (int t = 0; t < kT; ++t)
+      f.x[u][t] = __builtin_bit_cast(
+          i32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, kc >= 0 ? static_cast<uint32_t>((16 * t + i) * K + kc) : kOob, 0, 0));
+  }
+}
+
+template <int kU, int kA, int kT>
+__device__ __forceinline__ void mfmas(const Frags<kU, kA, kT>& f, i32x4 (&acc)[kA][kT]) {
+#pragma unroll
+  for (int u = 0; u < kU; ++u)
+#pragma unroll
+    for (int a = 0; a < kA; ++a)
+#pragma unroll
+      for (int t = 0; t < kT; ++t)
+        acc[a][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.w[u][a], f.x[u][t], acc[a][t], 0, 0, 0);
+}
+
+// A workgroup owns 16 kA output channels and all M <= 16 kT tokens.
+template <bool kScaled, int kA, int kT>
+__global__ __launch_bounds__(256) void w8a8_gemv_kernel(const int8_t* __restrict__ xq,
+                                                        const float* __restrict__ s_tok,
+                                                        const int8_t* __restrict__ wq,
+                                                        const float* __restrict__ s_ch,
+                                                        uint16_t* __restrict__ y,
+                                                        int32_t* __restrict__ acc_out, int M, int N, int K) {
+  constexpr int kCh = 16 * kA;
+  __shared__ int32_t part[kQuarters][kCh][16 * kT];
+
+  const int n0 = static_cast<int>(blockIdx.x) * kCh;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = lane & 15, h = lane >> 4;
+
+  // This wavefront's K quarter, in whole 64-byte steps.
+  Walk wk;
+  const int kq = (K / kQuarters + 63) / 64 * 64;
+  wk.k_begin = wave * kq;
+  wk.k_end = min(K, wk.k_begin + kq);
+  wk.n64 = (wk.k_end - wk.k_begin + 63) / 64;  // <= 0 when the quarter is empty
+
+  // Weights: rows n0 .. n0 + kCh - 1 (rows past N read zero).
+  const __amdgpu_buffer_rsrc_t rw = rsrc(wq + static_cast<size_t>(n0) * K, static_cast<int64_t>(min(kCh, N - n0)) * K);
+  const __amdgpu_buffer_rsrc_t rx = rsrc(xq, static_cast<int64_t>(M) * K);
+
+  i32x4 acc[kA][kT];
+#pragma unroll
+  for (int a = 0; a < kA; ++a)
+#pragma unroll
+    for (int t = 0; t < kT; ++t) acc[a][t] = i32x4{0, 0, 0, 0};
+
+  constexpr int kU = steps_per_set<kA + kT>();
+  const int sets = (wk.n64 + kU - 1) / kU;
+  Frags<kU, kA, kT> fa, fb;
+  issue(fa, rw, rx, i, h, K, wk, 0);
+  // No early exit between the halves: a branch there lets the compiler sink
+  // the loads of the second set below the first set's MFMAs. A set past the
+  // end loads zeros.
+  for (int s = 0; s < sets; s += 2) {
+    issue(fb, rw, rx, i, h, K, wk, (s + 1) * kU);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(fa, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(fa, rw, rx, i, h, K, wk, (s + 2) * kU);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(fb, acc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // D[n][m] of a 16x16 tile: lane (j, hh) register r holds channel 4 hh + r
+  // of token j.
+#pragma unroll
+  for (int a = 0; a < kA; ++a)
+#pragma unroll
+    for (int t = 0; t < kT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[wave][16 * a + 4 * h + r][16 * t + i] = acc[a][t][r];
+  __syncthreads();
+
+  for (int e = threadIdx.x; e < kCh * 16 * kT; e += blockDim.x) {
+    const int nl = e % kCh, m = e / kCh;
+    const int n = n0 + nl;
+    if (m >= M || n >= N) continue;
+    const int32_t v = part[0][nl][m] + part[1][nl][m] + part[2][nl][m] + part[3][nl][m];
+    const size_t o = static_cast<size_t>(m) * N + n;
+    if constexpr (kScaled) {
+      const float f = (static_cast<float>(v) * s_tok[m]) * s_ch[n];
+      y[o] = __builtin_bit_cast(uint16_t, static_cast<f16>(f));
+    } else {
+      acc_out[o] = v;
+    }
+  }
+}
+
+template <bool kScaled, int kA, int kT>
+hipError_t launch_one(const int8_t* xq, const float* s_tok, const int8_t* wq, const float* s_ch, uint16_t* y,
+                      int32_t* acc, int M, int N, int K, hipStream_t stream) {
+  const dim3 grid(static_cast<uint32_t>((N + 16 * kA - 1) / (16 * kA))), block(256);
+  return launch_kernel(w8a8_gemv_kernel<kScaled, kA, kT>, grid, block, 0, stream, xq, s_tok, wq, s_ch, y, acc, M, N, K);
+}
+
+template <bool kScaled>
+hipError_t launch_tiles(const int8_t* xq, const float* s_tok, const int8_t* wq, const float* s_ch, uint16_t* y,
+                        int32_t* acc, int M, int N, int K, hipStream_t stream) {
+  // Every workgroup reads all of xq, so xq is read N / (16 kA) times over
+  // (from L2): 32 channels per workgroup halves that, but only pays while
+  // the grid still has about 192 or more workgroups.
+  const bool wide = N >= 32 * 192;
+  if (M <= 16) return launch_one<kScaled, 1, 1>(xq, s_tok, wq, s_ch, y, acc, M, N, K, stream);
+  if (M <= 32)
+    return wide ? launch_one<kScaled, 2, 2>(xq, s_tok, wq, s_ch, y, acc, M, N, K, stream)
+                : launch_one<kScaled, 1, 2>(xq, s_tok, wq, s_ch, y, acc, M, N, K, stream);
+  return wide ? launch_one<kScaled, 2, 4>(xq, s_tok, wq, s_ch, y, acc, M, N, K, stream)
+              : launch_one<kScaled, 1, 4>(xq, s_tok, wq, s_ch, y, acc, M, N, K, stream);
+}
+
+}  // namespace
+
+bool w8a8_use_gemv(int64_t M, int64_t N) {
+  // Measured crossover against the tiled GEMM: up to 32 tokens always; 33-64
+  // tokens unless N is so large that the GEMM's 128-channel tiles already
+  // fill the chip and its smaller activation re-read wins.
+  if (M <= 32) return true;
+  return M <= kW8A8GemvMaxM && N < 16384;
+}
+
+hipError_t launch_w8a8_gemv(const int8_t* xq, const float* s_tok, const int8_t* wq,
+                            const float* s_ch, uint16_t* y, int32_t* acc,
+                            int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (M > kW8A8GemvMaxM) return hipErrorInvalidValue;
+  const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+  if (y != nullptr) return launch_tiles<true>(xq, s_tok, wq, s_ch, y, nullptr, m, n, k, stream);
+  return launch_tiles<false>(xq, nullptr, wq, nullptr, nullptr, acc, m, n, k, stream);
+}
+
+}  // namespace mq
