@@ -184,6 +184,23 @@ __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __res
         acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(FW[a], FX[b], acc[a][b], 0, 0, 0);      \
   } while (0)
 
+#define MQ_MFMAS_HALF(FX, FW, A)                                                                  \
+  do {                                                                                            \
+    _Pragma("unroll") for (int b = 0; b < 4; ++b)                                                 \
+        acc[A][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(FW[A], FX[b], acc[A][b], 0, 0, 0);      \
+  } while (0)
+
+  // Instruction-level interleave of a block: G times (two MFMAs, ND
+  // fragment reads), then the remaining MFMAs.
+#define MQ_SCHED(G, ND, REST)                                                                     \
+  do {                                                                                            \
+    _Pragma("unroll") for (int i_ = 0; i_ < (G); ++i_) {                                          \
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                          \
+      __builtin_amdgcn_sched_group_barrier(0x100, (ND), 0);                                       \
+    }                                                                                             \
+    __builtin_amdgcn_sched_group_barrier(0x008, (REST), 0);                                       \
+  } while (0)
+
   // Group g's stages are g, g + 2, g + 4, ... in slots s % kSlots (even
   // slots for group 0, odd for group 1). Prologue: stages g and g + 2.
   // Round p: the group computes stage 2p + g and fills stage 2p + g + 4 into
@@ -205,7 +222,45 @@ __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __res
   if (g < nst) MQ_READ_FRAGS(g, 0, fx0, fw0);
 
   static_assert(kSub == 2, "a round below is written for two k-steps per stage");
-  for (int p = 0; p < rounds; ++p) {
+  static_assert(kLoadsPerSub == 3, "the interleave below places three fills per k-step");
+  // Steady rounds: stages s + 2 and s + kAhead exist for both groups, so the
+  // round has no branches and the compiler waits for exactly the LDS reads
+  // each MFMA needs. The second k-step issues half its MFMAs, then waits for
+  // stage s + 2 and meets the barrier, then reads stage s + 2's first
+  // fragments under the other half, so the matrix unit has work queued
+  // across the barrier and the read latency.
+  const int steady = nst > kAhead ? (nst - kAhead) / 2 : 0;
+  int p = 0;
+  for (; p < steady; ++p) {
+    const int s = 2 * p + g;
+    // k-step 0: the first three fills of stage s + kAhead go out together
+    // (spread between MFMAs they stall the wave whenever the texture unit's
+    // queue is full), then stage s's second fragments are read between the
+    // MFMAs of its first.
+    __builtin_amdgcn_sched_barrier(0);
+    MQ_ISSUE(s + kAhead, 0, kLoadsPerSub);
+    __builtin_amdgcn_sched_barrier(0);
+    MQ_READ_FRAGS(s, 1, fx1, fw1);
+    MQ_MFMAS(fx0, fw0);
+    MQ_SCHED(3, 2, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    // k-step 1: the other three fills, half the MFMAs, the barrier, then
+    // stage s + 2's first fragments under the other half.
+    MQ_ISSUE(s + kAhead, kLoadsPerSub, kLoads);
+    __builtin_amdgcn_sched_barrier(0);
+    MQ_MFMAS_HALF(fx1, fw1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_counts<kLoads, 0>();
+    bare_barrier();
+    MQ_READ_FRAGS(s + 2, 0, fx0, fw0);
+    MQ_MFMAS_HALF(fx1, fw1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (; p < rounds; ++p) {
     const int s = 2 * p + g;
     const bool valid = s < nst;
     const int fill_stage = s + kAhead;
@@ -234,6 +289,8 @@ __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __res
 #undef MQ_ISSUE
 #undef MQ_READ_FRAGS
 #undef MQ_MFMAS
+#undef MQ_MFMAS_HALF
+#undef MQ_SCHED
 
   // Epilogue. D[n][m] of a 32x32 tile: lane (j, h) register r holds channel
   // 8 (r / 4) + 4 h + r % 4 of token j, so the lane's tokens are
