@@ -15,19 +15,21 @@
 //   operand, so the 32x32 result tile is D[n][m]: a lane holds four
 //   consecutive output channels of one token.
 // - A workgroup computes 256 tokens x 128 channels with eight wavefronts in
-//   two groups of four ("ping-pong"). Within a group the wavefronts split
-//   the tile 2 x 2 (128 x 64 each, 128 int32 accumulators per lane); group g
-//   takes the K stages s with s % 2 == g. Each SIMD runs one wavefront of
-//   each group, so while one waits on LDS, a fill or a barrier, the other
-//   keeps the matrix unit busy. The groups' partial sums are added (exact
-//   int32) through LDS at the end.
+//   two groups of four. Within a group the wavefronts split the tile 2 x 2
+//   (128 x 64 each, 128 int32 accumulators per lane); group g takes the k
+//   half g of every stage. Each SIMD runs one wavefront of each group, so
+//   while one waits on LDS or a barrier the other keeps the matrix unit
+//   busy. The groups' partial sums are added (exact int32) through LDS at
+//   the end.
 // - Tiles move HBM -> LDS with buffer_load ... lds (no register staging)
-//   into a ring of six 64-byte-deep stages (24 KB each); a group's fills of
-//   the stage four ahead are spread over the MFMA k-steps of its current
-//   stage. Buffer loads past the descriptor's size return zero, so ragged
-//   M, N and K edges arrive as zero rows and columns with no per-lane
-//   predication.
-// - LDS rows are 64 bytes; the 16-byte chunk index is XOR-swizzled by the
+//   into a ring of three 128-byte-deep stages (48 KB each): each load
+//   instruction fills 8 rows x 128 bytes. On the MI355X a compute unit
+//   streams such tiles from L2 at about 94 GB/s, against about 57 GB/s for
+//   16 rows x 64 bytes, and the fill rate bounds this kernel. Two stages are
+//   in flight while one is computed. Buffer loads past the descriptor's size
+//   return zero, so ragged M, N and K edges arrive as zero rows and columns
+//   with no per-lane predication.
+// - LDS rows are 128 bytes; the 16-byte chunk index is XOR-swizzled by the
 //   row so that the 32 rows of a fragment read fall on distinct banks.
 // - The epilogue stages the workgroup's output tile in LDS and writes whole
 //   rows with 16-byte stores.
@@ -45,22 +47,21 @@ namespace {
 constexpr int kBM = 256;        // tokens per workgroup tile
 constexpr int kBN = 128;        // output channels per workgroup tile
 constexpr int kGroupWaves = 4;  // wavefronts per group (2 x 2 of 128 tokens x 64 channels)
-constexpr int kThreads = 2 * kGroupWaves * 64;
-constexpr int kGroupM = 4;  // token tiles per group in the tile order
-constexpr int kBK = 64;     // K bytes per stage
-constexpr int kSlots = 6;   // LDS ring depth (stages)
-constexpr int kAhead = 4;   // a group fills the stage four ahead of the one it computes
-constexpr int kChunks = kBK / 16;                          // 16-byte chunks per tile row
-constexpr int kRowsPerLoad = 1024 / kBK;                   // rows one 64 x 16 B load fills
-constexpr int kLoadsX = kBM / kRowsPerLoad / kGroupWaves;  // per wave per stage
-constexpr int kLoadsW = kBN / kRowsPerLoad / kGroupWaves;
+constexpr int kWaves = 2 * kGroupWaves;
+constexpr int kThreads = kWaves * 64;
+constexpr int kGroupM = 4;   // token tiles per group in the tile order
+constexpr int kBK = 128;     // K bytes per stage (128-byte row segments)
+constexpr int kSlots = 3;    // LDS ring depth (stages)
+constexpr int kChunks = kBK / 16;                      // 16-byte chunks per tile row
+constexpr int kRowsPerLoad = 1024 / kBK;               // rows one 64 x 16 B load fills
+constexpr int kLoadsX = kBM / kRowsPerLoad / kWaves;   // per wave per stage
+constexpr int kLoadsW = kBN / kRowsPerLoad / kWaves;
 constexpr int kLoads = kLoadsX + kLoadsW;
 constexpr int kStageBytes = (kBM + kBN) * kBK;
-constexpr int kSub = kBK / 32;  // MFMA k-steps per stage
-constexpr int kLoadsPerSub = kLoads / kSub;
-static_assert(kLoads % kSub == 0 && kLoads < 64, "load split / vmcnt range");
-static_assert(kSlots % 2 == 0 && kSlots >= kAhead + 2, "each group owns every other slot");
+constexpr int kSubPerGroup = kBK / 2 / 32;  // MFMA k-steps per group and stage
+static_assert(kLoads < 32, "vmcnt range");
 static_assert(kSlots * kStageBytes <= 160 * 1024, "LDS capacity");
+static_assert(kSubPerGroup == 2, "a round below is written for two k-steps per group");
 
 constexpr uint32_t kOob = 0x80000000u;    // a buffer offset past every tile: the load returns 0
 constexpr int kBufferFlags = 0x00020000;  // gfx9 buffer descriptor word 3 (raw 32-bit data)
@@ -70,11 +71,11 @@ typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
 typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
-// XOR applied to the 16-byte chunk index of tile row r (64-byte rows). For
-// the fragment reads (32 rows, one chunk each) it makes any 8 and any 16
-// consecutive rows land on distinct 16-byte bank groups of a 128- or
-// 256-byte LDS window. It depends on r mod 16 only.
-__device__ __forceinline__ int chunk_swizzle(int r) { return ((r >> 2) & 3) ^ (r & 2); }
+// XOR applied to the 16-byte chunk index of tile row r (128-byte rows).
+// A fragment read takes one chunk of 32 consecutive rows; rows 2 apart share
+// banks, and (r / 2) mod 8 spreads any 16 consecutive rows over the 16
+// distinct 16-byte bank groups of a 256-byte window. Depends on r mod 16.
+__device__ __forceinline__ int chunk_swizzle(int r) { return (r >> 1) & 7; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const int8_t* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(base), 0, bytes, kBufferFlags);
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __res
   const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(wq + static_cast<size_t>(n0) * K, min(kBN, N - n0) * K);
 
   // Fill l of this wave (l < kLoadsX: token rows, else channel rows) covers
-  // tile rows (r + 4u) * kRowsPerLoad .. with u = l or l - kLoadsX; lane L
+  // tile rows (wave + 8u) * kRowsPerLoad .. with u = l or l - kLoadsX; lane L
   // writes physical chunk L % kChunks of row L / kChunks, so it fetches the
   // logical chunk that the swizzle places there.
   uint32_t loff[kLoads];
@@ -128,16 +129,17 @@ __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __res
 #pragma unroll
   for (int l = 0; l < kLoads; ++l) {
     const int u = l < kLoadsX ? l : l - kLoadsX;
-    const int row = (r + kGroupWaves * u) * kRowsPerLoad + lane / kChunks;
+    const int row = (wave + kWaves * u) * kRowsPerLoad + lane / kChunks;
     lk[l] = 16 * ((lane % kChunks) ^ chunk_swizzle(row));
     loff[l] = static_cast<uint32_t>(row * K + lk[l]);
   }
 
-  // Fragment reads: lane (fi, fh) reads chunk 2t + fh of row fi (+32 b).
+  // Fragment reads: group g takes chunks 4g .. 4g + 3 of each stage; for its
+  // k-step t lane (fi, fh) reads chunk 4g + 2t + fh of row fi (+32 b).
   const int fi = lane & 31, fh = lane >> 5;
-  int coff[kSub];
+  int coff[kSubPerGroup];
 #pragma unroll
-  for (int t = 0; t < kSub; ++t) coff[t] = 16 * ((2 * t + fh) ^ chunk_swizzle(fi));
+  for (int t = 0; t < kSubPerGroup; ++t) coff[t] = 16 * ((4 * g + 2 * t + fh) ^ chunk_swizzle(fi));
   const int xrow0 = (wm * 128 + fi) * kBK;
   const int wrow0 = kBM * kBK + (wn * 64 + fi) * kBK;
 
@@ -148,9 +150,8 @@ __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __res
     for (int b = 0; b < 4; ++b) acc[a][b] = i32x16{};
 
   const int nst = (K + kBK - 1) / kBK;
-  const int rounds = (nst + 1) / 2;
 
-  // Fills [L0, L1) of stage S (issued by the four waves of S's group).
+  // Fills [L0, L1) of stage S (every wave issues its share).
 #define MQ_ISSUE(S, L0, L1)                                                                      \
   do {                                                                                           \
     const int k0_ = (S) * kBK;                                                                   \
@@ -160,10 +161,10 @@ __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __res
       const uint32_t off_ = lk[l] < krem_ ? loff[l] + k0_ : kOob;                                \
       if (l < kLoadsX) {                                                                         \
         __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                \
-            rx, (lds_void*)(dst_ + (r + kGroupWaves * l) * 1024), 16, off_, 0, 0, 0);            \
+            rx, (lds_void*)(dst_ + (wave + kWaves * l) * 1024), 16, off_, 0, 0, 0);              \
       } else {                                                                                   \
         __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                \
-            rw, (lds_void*)(dst_ + kBM * kBK + (r + kGroupWaves * (l - kLoadsX)) * 1024), 16,    \
+            rw, (lds_void*)(dst_ + kBM * kBK + (wave + kWaves * (l - kLoadsX)) * 1024), 16,      \
             off_, 0, 0, 0);                                                                      \
       }                                                                                          \
     }                                                                                            \
@@ -190,28 +191,16 @@ __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __res
         acc[A][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(FW[A], FX[b], acc[A][b], 0, 0, 0);      \
   } while (0)
 
-  // Instruction-level interleave of a block: G times (two MFMAs, ND
-  // fragment reads), then the remaining MFMAs.
-#define MQ_SCHED(G, ND, REST)                                                                     \
-  do {                                                                                            \
-    _Pragma("unroll") for (int i_ = 0; i_ < (G); ++i_) {                                          \
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                          \
-      __builtin_amdgcn_sched_group_barrier(0x100, (ND), 0);                                       \
-    }                                                                                             \
-    __builtin_amdgcn_sched_group_barrier(0x008, (REST), 0);                                       \
-  } while (0)
-
-  // Group g's stages are g, g + 2, g + 4, ... in slots s % kSlots (even
-  // slots for group 0, odd for group 1). Prologue: stages g and g + 2.
-  // Round p: the group computes stage 2p + g and fills stage 2p + g + 4 into
-  // the slot of stage 2p + g - 2, which every wave of the group finished
-  // reading before the barrier that ended round p - 1. Each wave's loads
-  // complete in issue order, so waiting for stage x leaves only the stage
-  // issued after it (if any) in flight. Both groups run the same number of
-  // rounds and barriers.
-  if (g < nst) MQ_ISSUE(g, 0, kLoads);
-  if (g + 2 < nst) MQ_ISSUE(g + 2, 0, kLoads);
-  if (g + 2 < nst) {
+  // Stage s sits in slot s % 3. Both groups compute every stage, group g on
+  // its k half. Round s: every wave issues its fills of stage s + 2 into the
+  // slot of stage s - 1 (which every wave finished reading before the barrier
+  // that ended round s - 1), computes its half of stage s, waits for its own
+  // loads of stage s + 1 (loads complete in issue order, so only stage s + 2
+  // stays in flight) and meets the barrier, after which stage s + 1 is
+  // complete and readable.
+  MQ_ISSUE(0, 0, kLoads);
+  if (1 < nst) {
+    MQ_ISSUE(1, 0, kLoads);
     wait_counts<kLoads, 0>();
   } else {
     wait_counts<0, 0>();
@@ -219,40 +208,30 @@ __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __res
   bare_barrier();
 
   i32x4 fx0[4], fw0[2], fx1[4], fw1[2];
-  if (g < nst) MQ_READ_FRAGS(g, 0, fx0, fw0);
+  MQ_READ_FRAGS(0, 0, fx0, fw0);
 
-  static_assert(kSub == 2, "a round below is written for two k-steps per stage");
-  static_assert(kLoadsPerSub == 3, "the interleave below places three fills per k-step");
-  // Steady rounds: stages s + 2 and s + kAhead exist for both groups, so the
-  // round has no branches and the compiler waits for exactly the LDS reads
-  // each MFMA needs. The second k-step issues half its MFMAs, then waits for
-  // stage s + 2 and meets the barrier, then reads stage s + 2's first
-  // fragments under the other half, so the matrix unit has work queued
-  // across the barrier and the read latency.
-  const int steady = nst > kAhead ? (nst - kAhead) / 2 : 0;
-  int p = 0;
-  for (; p < steady; ++p) {
-    const int s = 2 * p + g;
-    // k-step 0: the first three fills of stage s + kAhead go out together
-    // (spread between MFMAs they stall the wave whenever the texture unit's
-    // queue is full), then stage s's second fragments are read between the
-    // MFMAs of its first.
+  // Steady rounds (stages s + 1 and s + 2 exist): no branches, so the
+  // compiler waits for exactly the LDS reads each MFMA needs. Half of the
+  // second k-step's MFMAs are issued before the barrier and half after it,
+  // under the reads of stage s + 1's first fragments.
+  int s = 0;
+  for (; s + 2 < nst; ++s) {
     __builtin_amdgcn_sched_barrier(0);
-    MQ_ISSUE(s + kAhead, 0, kLoadsPerSub);
+    MQ_ISSUE(s + 2, 0, kLoads);
     __builtin_amdgcn_sched_barrier(0);
     MQ_READ_FRAGS(s, 1, fx1, fw1);
     MQ_MFMAS(fx0, fw0);
-    MQ_SCHED(3, 2, 2);
-    __builtin_amdgcn_sched_barrier(0);
-    // k-step 1: the other three fills, half the MFMAs, the barrier, then
-    // stage s + 2's first fragments under the other half.
-    MQ_ISSUE(s + kAhead, kLoadsPerSub, kLoads);
+    _Pragma("unroll") for (int i_ = 0; i_ < 3; ++i_) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
     MQ_MFMAS_HALF(fx1, fw1, 0);
     __builtin_amdgcn_sched_barrier(0);
     wait_counts<kLoads, 0>();
     bare_barrier();
-    MQ_READ_FRAGS(s + 2, 0, fx0, fw0);
+    MQ_READ_FRAGS(s + 1, 0, fx0, fw0);
     MQ_MFMAS_HALF(fx1, fw1, 1);
     __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -260,37 +239,21 @@ __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __res
     __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
-  for (; p < rounds; ++p) {
-    const int s = 2 * p + g;
-    const bool valid = s < nst;
-    const int fill_stage = s + kAhead;
-    const bool fill = fill_stage < nst;
-    // k-step 0
-    if (fill) MQ_ISSUE(fill_stage, 0, kLoadsPerSub);
-    if (valid) {
-      MQ_READ_FRAGS(s, 1, fx1, fw1);
-      MQ_MFMAS(fx0, fw0);
-    }
-    // k-step 1
-    if (fill) MQ_ISSUE(fill_stage, kLoadsPerSub, kLoads);
-    if (p + 1 < rounds) {
-      // The group's next stage must have landed (every wave's share), and
-      // every wave must be done reading stage s before it is refilled.
-      if (fill) {
-        wait_counts<kLoads, 0>();
-      } else {
-        wait_counts<0, 0>();
-      }
+  // Last two stages (or fewer): nothing left to fill.
+  for (; s < nst; ++s) {
+    MQ_READ_FRAGS(s, 1, fx1, fw1);
+    MQ_MFMAS(fx0, fw0);
+    if (s + 1 < nst) {
+      wait_counts<0, 0>();
       bare_barrier();
-      if (s + 2 < nst) MQ_READ_FRAGS(s + 2, 0, fx0, fw0);
+      MQ_READ_FRAGS(s + 1, 0, fx0, fw0);
     }
-    if (valid) MQ_MFMAS(fx1, fw1);
+    MQ_MFMAS(fx1, fw1);
   }
 #undef MQ_ISSUE
 #undef MQ_READ_FRAGS
 #undef MQ_MFMAS
 #undef MQ_MFMAS_HALF
-#undef MQ_SCHED
 
   // Epilogue. D[n][m] of a 32x32 tile: lane (j, h) register r holds channel
   // 8 (r / 4) + 4 h + r % 4 of token j, so the lane's tokens are
