@@ -216,8 +216,11 @@ __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __res
   // under the reads of stage s + 1's first fragments.
   int s = 0;
   for (; s + 2 < nst; ++s) {
+    // Three fills of stage s + 2 go out at the start of each k-step: a burst
+    // of all six stalls the wave on the texture unit's full command queue,
+    // and single fills between MFMAs stall it more often.
     __builtin_amdgcn_sched_barrier(0);
-    MQ_ISSUE(s + 2, 0, kLoads);
+    MQ_ISSUE(s + 2, 0, kLoads / 2);
     __builtin_amdgcn_sched_barrier(0);
     MQ_READ_FRAGS(s, 1, fx1, fw1);
     MQ_MFMAS(fx0, fw0);
@@ -226,6 +229,8 @@ __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __res
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    MQ_ISSUE(s + 2, kLoads / 2, kLoads);
     __builtin_amdgcn_sched_barrier(0);
     MQ_MFMAS_HALF(fx1, fw1, 0);
     __builtin_amdgcn_sched_barrier(0);
