@@ -264,8 +264,12 @@ __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __res
   // 8 (r / 4) + 4 h + r % 4 of token j, so the lane's tokens are
   // wm*128 + 32 b + j and its channels wn*64 + 32 a + 8 q + 4 h + i.
   const int j = lane & 31, h = lane >> 5;
+  // Each group finishes two of the four 32-token blocks b of its wave's
+  // 128 x 64 block: group 0 blocks 0 and 1, group 1 blocks 2 and 3. It
+  // hands its partial sums of the other two blocks to the other group
+  // through LDS (exact int32 adds), then scales and stages its own two.
   float sc[2][4][4], st[4];
-  if (kScaled && g == 0) {
+  if (kScaled) {
     // Every scale is loaded up front (indices clamped into range; results
     // out of range are not stored) and consumed after the partial-sum
     // exchange, so the loads overlap it.
@@ -280,77 +284,79 @@ __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __res
     for (int b = 0; b < 4; ++b) st[b] = s_tok[min(mb + 32 * b, M - 1)];
   }
 
-  // Group 1's partial sums -> LDS -> added into group 0's accumulators.
-  wait_counts<0, 0>();  // every wave is done reading the ring
-  bare_barrier();
-  if (g == 1) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = wm * 128 + 32 * b + j, col = wn * 64 + 32 * a + 8 * q + 4 * h;
-          *(lds_i32x4*)(sm + row * kPartPitch + col * 4) =
-              i32x4{acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]};
-        }
+  // The waits below are for LDS traffic only (vmcnt 63: the scale loads
+  // stay in flight).
+#define MQ_PART_WRITE(B)                                                                             \
+  _Pragma("unroll") for (int a = 0; a < 2; ++a) _Pragma("unroll") for (int q = 0; q < 4; ++q) {      \
+    const int row = wm * 128 + 32 * (B) + j, col = wn * 64 + 32 * a + 8 * q + 4 * h;                \
+    *(lds_i32x4*)(sm + row * kPartPitch + col * 4) =                                                \
+        i32x4{acc[a][B][4 * q], acc[a][B][4 * q + 1], acc[a][B][4 * q + 2], acc[a][B][4 * q + 3]};   \
   }
-  wait_counts<0, 0>();
-  bare_barrier();
-  if (g == 0) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = wm * 128 + 32 * b + j, col = wn * 64 + 32 * a + 8 * q + 4 * h;
-          const i32x4 v = *(const lds_i32x4*)(sm + row * kPartPitch + col * 4);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[a][b][4 * q + i] += v[i];
-        }
+#define MQ_PART_ADD(B)                                                                               \
+  _Pragma("unroll") for (int a = 0; a < 2; ++a) _Pragma("unroll") for (int q = 0; q < 4; ++q) {      \
+    const int row = wm * 128 + 32 * (B) + j, col = wn * 64 + 32 * a + 8 * q + 4 * h;                \
+    const i32x4 v = *(const lds_i32x4*)(sm + row * kPartPitch + col * 4);                           \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) acc[a][B][4 * q + i] += v[i];                      \
   }
-  wait_counts<0, 0>();  // the partial sums are consumed before the area is reused
-  bare_barrier();
+#define MQ_STAGE(B)                                                                                  \
+  _Pragma("unroll") for (int a = 0; a < 2; ++a) _Pragma("unroll") for (int q = 0; q < 4; ++q) {      \
+    const int row = wm * 128 + 32 * (B) + j, col = wn * 64 + 32 * a + 8 * q + 4 * h;                \
+    lds_i8* const dst = sm + row * kPitch + col * static_cast<int>(sizeof(OutT));                   \
+    if constexpr (kScaled) {                                                                         \
+      uint32_t hv[4];                                                                                \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                \
+        const float v = (static_cast<float>(acc[a][B][4 * q + i]) * st[B]) * sc[a][q][i];            \
+        hv[i] = __builtin_bit_cast(uint16_t, static_cast<f16>(v));                                   \
+      }                                                                                              \
+      *(lds_u32x2*)(dst) = u32x2{hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};                      \
+    } else {                                                                                         \
+      *(lds_i32x4*)(dst) =                                                                           \
+          i32x4{acc[a][B][4 * q], acc[a][B][4 * q + 1], acc[a][B][4 * q + 2], acc[a][B][4 * q + 3]}; \
+    }                                                                                                \
+  }
 
-  // Group 0 stages the output tile (fp16 after scaling, or int32) in LDS.
+  wait_counts<63, 0>();  // every wave is done reading the ring
+  bare_barrier();
   if (g == 0) {
-    if constexpr (kScaled) {
-      // Settle the scale loads here (vmcnt also counts stores, so a wait
-      // among the stores below would drain them as well).
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(sc[a][q][i]));
-#pragma unroll
-      for (int b = 0; b < 4; ++b) asm volatile("" : "+v"(st[b]));
-    }
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int row = wm * 128 + 32 * b + j;
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = wn * 64 + 32 * a + 8 * q + 4 * h;
-          lds_i8* const dst = sm + row * kPitch + col * static_cast<int>(sizeof(OutT));
-          if constexpr (kScaled) {
-            uint32_t hv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float v = (static_cast<float>(acc[a][b][4 * q + i]) * st[b]) * sc[a][q][i];
-              hv[i] = __builtin_bit_cast(uint16_t, static_cast<f16>(v));
-            }
-            *(lds_u32x2*)(dst) = u32x2{hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};
-          } else {
-            *(lds_i32x4*)(dst) = i32x4{acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2],
-                                       acc[a][b][4 * q + 3]};
-          }
-        }
-    }
+    MQ_PART_WRITE(2)
+    MQ_PART_WRITE(3)
+  } else {
+    MQ_PART_WRITE(0)
+    MQ_PART_WRITE(1)
   }
+  wait_counts<63, 0>();
+  bare_barrier();
+  if (g == 0) {
+    MQ_PART_ADD(0)
+    MQ_PART_ADD(1)
+  } else {
+    MQ_PART_ADD(2)
+    MQ_PART_ADD(3)
+  }
+  wait_counts<63, 0>();  // the partial sums are consumed before the area is reused
+  bare_barrier();
+  if constexpr (kScaled) {
+    // Settle the scale loads here (vmcnt also counts stores, so a wait
+    // among the stores below would drain them as well).
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(sc[a][q][i]));
+#pragma unroll
+    for (int b = 0; b < 4; ++b) asm volatile("" : "+v"(st[b]));
+  }
+  if (g == 0) {
+    MQ_STAGE(0)
+    MQ_STAGE(1)
+  } else {
+    MQ_STAGE(2)
+    MQ_STAGE(3)
+  }
+#undef MQ_PART_WRITE
+#undef MQ_PART_ADD
+#undef MQ_STAGE
   wait_counts<0, 0>();
   bare_barrier();
 
