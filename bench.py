@@ -30,6 +30,11 @@ Also reported (same line):
   prefill      W8A8 prefill (per-token quant + scaled int8 GEMM, M=2048,
                K=N=4096) and W4A16 prefill GEMMs (M=4096, K=4096/12288,
                N=4096): kernel time and TOPS against the dense MFMA peaks.
+  layers       the linear layers of an 8B-shaped decoder layer (qkv 4096->6144,
+               o_proj 4096->4096, gate_up 4096->24576, down 12288->4096) at
+               M = 1, 8, 64 and 2048 under W4A16 (GEMV up to 16 tokens, GEMM
+               above) and W8A8_INT8 (quantize + scaled GEMM): microseconds per
+               call with weights rotating over copies of >= 640 MB in all.
   cpu_baseline the CPU oracle on one step of the same workload (one weight
                set), repeated for about 10 s, in the same unit.
 """
@@ -79,6 +84,7 @@ def parse_args(argv=None):
     ap.add_argument("--sets", type=int, default=10, help="rotating weight sets (52 MB each)")
     ap.add_argument("--prefill-reps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-layers", action="store_true", help="skip the decoder-layer linear set")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-kernel", action="store_true",
@@ -202,6 +208,79 @@ def bench_prefill(torch, mq, synth, oracle_free_quant, args, log):
     return out
 
 
+def bench_layers(torch, mq, synth, args, log):
+    """The linear layers of an 8B-shaped decoder layer at decode batches 1, 8, 64 and a
+    2048-token prefill, under W4A16 (GEMV for M <= 16, GEMM above) and W8A8_INT8
+    (quantize + scaled GEMM). Weights rotate over copies totalling >= 640 MB so every
+    call reads them from HBM; times are per call from event-timed graph replays."""
+    dev = torch.device("cuda", 0)
+    R = 20
+    out = {"w4a16": {}, "w8a8": {}}
+
+    def time_calls(fn):
+        g = capture(torch, lambda: [fn(r) for r in range(R)])
+        g.replay()
+        best = min(timed_replay(torch, g)[1] for _ in range(3))
+        return best / R
+
+    def copies(tensors, nbytes):
+        n = max(2, -(-640 * 2**20 // nbytes))
+        return [tensors] + [{k: v.clone() for k, v in tensors.items()} for _ in range(n - 1)]
+
+    for li, (name, shp) in enumerate(synth.LAYER_SET.items()):
+        K, N = shp["K"], shp["N"]
+        log(f"layers: {name} K={K} N={N}")
+        w = synth.w4a16_weights(K, N, GROUP, tag=300 + li)
+        w = {k: torch.from_numpy(v).to(dev) for k, v in w.items()}
+        wsets = copies(w, K * N // 2)
+        del w
+        out["w4a16"][name] = {}
+        for M in synth.LAYER_SET_MS:
+            x = torch.from_numpy(synth.w4a16_inputs(M, K, 8, GROUP, outlier_frac=0.005, tag=310 + li,
+                                                    seed=M)["x"]).to(dev)
+            y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            if M <= mq.GEMV_MAX_M:
+                ws = torch.zeros(max(mq.w4a16_gemv_workspace_bytes(M, N, K, GROUP), 16), dtype=torch.uint8,
+                                 device=dev)
+
+                def fn(r, x=x, y=y, ws=ws):
+                    s = wsets[r % len(wsets)]
+                    mq.w4a16_gemv(x, s["qweight"], s["scales"], s["qzeros"], GROUP, out=y, workspace=ws)
+            else:
+                def fn(r, x=x, y=y):
+                    s = wsets[r % len(wsets)]
+                    mq.w4a16_gemm(x, s["qweight"], s["scales"], s["qzeros"], GROUP, out=y)
+            t = time_calls(fn)
+            nbytes = w4a16_bytes(M, K, N)
+            out["w4a16"][name][str(M)] = {"us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
+                                          "TFLOPS": round(2.0 * M * N * K / t / 1e12, 1)}
+        del wsets
+        torch.cuda.empty_cache()
+
+        d = synth.w8a8_inputs(8, K, N, outlier_frac=0.01, tag=320 + li)
+        wq, s_ch = mq.quant_per_token_int8(torch.from_numpy(d["wf"]).to(dev))
+        qsets = copies({"wq": wq, "s_ch": s_ch}, K * N)
+        del wq, s_ch
+        out["w8a8"][name] = {}
+        for M in synth.LAYER_SET_MS:
+            x = torch.from_numpy(synth.w8a8_inputs(M, K, 8, outlier_frac=0.01, tag=330 + li, seed=M)["x"]).to(dev)
+            xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+            st = torch.empty((M,), dtype=torch.float32, device=dev)
+            y = torch.empty((M, N), dtype=torch.float16, device=dev)
+
+            def fn(r, x=x, xq=xq, st=st, y=y):
+                s = qsets[r % len(qsets)]
+                mq.quant_per_token_int8(x, out=xq, s_out=st)
+                mq.w8a8_scaled_mm(xq, st, s["wq"], s["s_ch"], out=y)
+            t = time_calls(fn)
+            nbytes = M * K * 2 + K * N + N * 4 + M * N * 2
+            out["w8a8"][name][str(M)] = {"us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
+                                         "TOPS": round(2.0 * M * N * K / t / 1e12, 1)}
+        del qsets
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(args, log):
     import numpy as np
 
@@ -308,6 +387,8 @@ def main(argv=None):
     }
     if not args.no_prefill:
         line["prefill"] = bench_prefill(torch, mq, synth, mq.quant_per_token_int8, args, log)
+    if not args.no_layers:
+        line["layers"] = bench_layers(torch, mq, synth, args, log)
     if not args.no_cpu_baseline and rank == 0:
         line["cpu_baseline"] = cpu_baseline(args, log)
     print(json.dumps(line))

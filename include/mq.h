@@ -6,7 +6,7 @@
  *
  *   W4A16      asymmetric 4-bit weights with per-group fp16 scales and 4-bit
  *              zero points, fp16 activations, fp16 output. A GEMM for
- *              prefill-shaped inputs and a GEMV for decode (M <= 16).
+ *              prefill-shaped inputs and a GEMV for decode (M <= 64).
  *              Source: LMDeploy toolkit overview, section 2.5 "Weight
  *              quantization (AWQ)" (4-bit weights, groups of 128); LMDeploy
  *              4-bit deployment guide, section 2.2 (scale and weight are
@@ -61,7 +61,7 @@ typedef enum mq_status {
   MQ_ERR_NULL = 1,        /* a required pointer is NULL */
   MQ_ERR_SHAPE = 2,       /* a size is negative, too large or breaks a divisibility rule */
   MQ_ERR_ALIGN = 3,       /* a pointer is not aligned as documented */
-  MQ_ERR_UNSUPPORTED = 4, /* valid in principle but not provided (e.g. group != 128, GEMV M > 16) */
+  MQ_ERR_UNSUPPORTED = 4, /* valid in principle but not provided (e.g. group != 128, GEMV M > 64) */
   MQ_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
   MQ_ERR_ALIAS = 6,       /* an output overlaps an input or another output */
   MQ_ERR_HIP = 7          /* the HIP runtime refused the launch (message in mq_last_error) */
@@ -158,7 +158,7 @@ mq_status mq_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_
 size_t mq_w4a16_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group);
 
 /*
- * W4A16 GEMV for decode (1 <= M <= 16). Same definition, operands and
+ * W4A16 GEMV for decode (1 <= M <= 64). Same definition, operands and
  * layouts as mq_w4a16_gemm, except that the weights are not rounded to
  * fp16: per group of 128 rows the kernel forms, in fp32, the sum of
  * x * (q - z) and scales it by s in fp32. (For N % 32 == 0 the sum is
@@ -167,7 +167,9 @@ size_t mq_w4a16_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t gr
  * same tolerance as mq_w4a16_gemm. K is split across workgroups when N is
  * too narrow to occupy the GPU: each split writes fp32 partial sums to
  * `workspace` and a second kernel on the same stream adds the splits in
- * split order. Results are deterministic.
+ * split order. Results are deterministic. Up to 64 tokens share one pass
+ * over the weights (four 16-token MFMA tiles per weight fragment; for
+ * N % 32 != 0 the tokens are taken 16 at a time).
  *
  *   workspace        device buffer of at least
  *                    mq_w4a16_gemv_workspace_bytes(M, N, K, group) bytes,
@@ -175,7 +177,7 @@ size_t mq_w4a16_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t gr
  *                    Its contents on entry do not matter. It must not
  *                    overlap any operand, and calls sharing a workspace
  *                    must be ordered (same stream or synchronized).
- * Requires: as mq_w4a16_gemm, and M <= 16 (M > 16 -> MQ_ERR_UNSUPPORTED).
+ * Requires: as mq_w4a16_gemm, and M <= 64 (M > 64 -> MQ_ERR_UNSUPPORTED).
  */
 mq_status mq_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                         const int32_t* qzeros, uint16_t* y,

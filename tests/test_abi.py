@@ -133,8 +133,8 @@ def test_w4a16_gemm_validation(lib):
 def test_w4a16_gemv_validation(lib):
     v = lib.mq_w4a16_gemv
     ws = lib.mq_w4a16_gemv_workspace_bytes
-    assert v(A, B, C, D, E, 17, 64, 256, 128, F, 1 << 20, None) == UNSUP
-    assert "M <= 16" in _err(lib)
+    assert v(A, B, C, D, E, 65, 64, 256, 128, F, 1 << 20, None) == UNSUP
+    assert "M <= 64" in _err(lib)
     # a problem that needs a workspace: small N -> K split across workgroups
     need = ws(1, 128, 4096, 128)
     assert need > 0
@@ -150,13 +150,14 @@ def test_gemv_workspace_plan(lib):
     ws = lib.mq_w4a16_gemv_workspace_bytes
     # rejected problems need nothing
     assert ws(0, 512, 512, 128) == 0
-    assert ws(17, 512, 512, 128) == 0
+    assert ws(65, 512, 512, 128) == 0
     assert ws(4, 512, 512, 64) == 0
     # the workspace holds splits * M * N fp32 partial sums, with splits a
     # divisor of K/128; the LDS-staged kernel (N % 32 == 0) keeps at most 16
     # groups per split
     for M, N, K in [(1, 24576, 4096), (4, 24576, 4096), (16, 24576, 4096), (1, 6144, 4096),
-                    (8, 4096, 4096), (1, 4096, 12288), (4, 512, 512), (3, 424, 384)]:
+                    (8, 4096, 4096), (1, 4096, 12288), (4, 512, 512), (3, 424, 384),
+                    (64, 24576, 4096), (64, 4096, 12288), (33, 6144, 4096), (40, 424, 384)]:
         b = ws(M, N, K, 128)
         assert b % (4 * M * N) == 0
         splits = b // (4 * M * N) or 1

@@ -6,7 +6,7 @@ and a 2048-token prefill, under W4A16 (group 128) and W8A8_INT8.
 W4A16 inputs: decode batches use N(0, 1) activations with 0.5% x20 outlier
 channels, the prefill plain N(0, 1); W8A8 uses 1% x20 outlier channels at
 every batch. Each case goes through the layer entry point a model would call
-(GEMV for M <= 16, GEMM above; quantize + scaled GEMM for W8A8).
+(GEMV for M <= 64, GEMM above; quantize + scaled GEMM for W8A8).
 """
 
 import numpy as np

@@ -164,7 +164,11 @@ def test_w4a16_gemv_decode_c1(M):
 
 @pytest.mark.parametrize("M,K,N", [(1, 128, 8), (3, 384, 424), (7, 384, 424), (13, 1024, 1032),
                                    (16, 256, 4096), (2, 4096, 6144), (5, 12288, 4096), (16, 128, 24576),
-                                   (3, 4096, 128), (5, 2048, 136), (16, 8192, 520)])
+                                   (3, 4096, 128), (5, 2048, 136), (16, 8192, 520),
+                                   # two to four 16-token tiles; ragged token tails; N % 32 != 0
+                                   # (16-token slices); many and few splits
+                                   (17, 384, 424), (32, 4096, 6144), (33, 1024, 1032), (48, 12288, 4096),
+                                   (64, 4096, 24576), (64, 4096, 4096), (63, 256, 4096), (40, 2048, 136)])
 def test_w4a16_gemv_shapes(M, K, N):
     d = _w4(M, K, N, outliers=0.005, tag=M * 7 + K + N)
     assert_fp16_close(_run_w4(mq.w4a16_gemv, d, "shape"), _ref_w4(d), f"gemv M={M} K={K} N={N}")
@@ -231,6 +235,9 @@ def test_linear_dispatch_and_empty():
     x17 = np.concatenate([d["x"], d["x"][:1]])
     y17 = host(mq.w4a16_linear(dev(x17), *args))
     assert_fp16_close(y17, oracle.w4a16_ref(x17, d["qweight"], d["scales"], d["qzeros"], 128), "linear M=17")
+    x65 = np.concatenate([d["x"]] * 4 + [d["x"][:1]])  # past the GEMV: the GEMM
+    y65 = host(mq.w4a16_linear(dev(x65), *args))
+    assert_fp16_close(y65, oracle.w4a16_ref(x65, d["qweight"], d["scales"], d["qzeros"], 128), "linear M=65")
     # empty problems: valid, nothing written
     out = torch.full((0, 264), 1.0, dtype=torch.float16, device="cuda")
     x0 = torch.empty((0, 256), dtype=torch.float16, device="cuda")
@@ -241,7 +248,7 @@ def test_linear_dispatch_and_empty():
 
 
 def test_gemv_rejects_large_m():
-    d = _w4(17, 256, 264, tag=44)
+    d = _w4(65, 256, 264, tag=44)
     with pytest.raises(mq.MqError) as e:
-        _run_w4(mq.w4a16_gemv, d, "M=17")
+        _run_w4(mq.w4a16_gemv, d, "M=65")
     assert e.value.status_name == "MQ_ERR_UNSUPPORTED"

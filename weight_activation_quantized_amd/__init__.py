@@ -12,12 +12,12 @@ Entry points (same names as the C ABI, without the ``mq_`` prefix):
     w8a8_scaled_mm(xq, s_tok, wq, s_ch)              -> y  (fp16)
     w8a8_mm_i32(xq, wq)                              -> acc (int32)
     w4a16_gemm(x, qweight, scales, qzeros, group)    -> y  (fp16)
-    w4a16_gemv(x, qweight, scales, qzeros, group)    -> y  (fp16), M <= 16
+    w4a16_gemv(x, qweight, scales, qzeros, group)    -> y  (fp16), M <= 64
     w4a16_gemv_workspace_bytes(M, N, K, group)       -> int
 
 and two compositions used by a model's linear layer:
 
-    w4a16_linear(x, qweight, scales, qzeros, group)  GEMV for M <= 16, else GEMM
+    w4a16_linear(x, qweight, scales, qzeros, group)  GEMV for M <= 64, else GEMM
     w8a8_linear(x, wq, s_ch)                         quantize x per token, then scaled GEMM
 """
 
@@ -32,7 +32,7 @@ __all__ = [
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmq.so")
-GEMV_MAX_M = 16
+GEMV_MAX_M = 64
 
 STATUS_NAMES = {
     0: "MQ_OK", 1: "MQ_ERR_NULL", 2: "MQ_ERR_SHAPE", 3: "MQ_ERR_ALIGN", 4: "MQ_ERR_UNSUPPORTED",
@@ -211,7 +211,7 @@ def w4a16_gemv_workspace_bytes(M, N, K, group=128):
 
 
 def w4a16_gemv(x, qweight, scales, qzeros, group=128, out=None, workspace=None, stream=None):
-    """W4A16 GEMV for decode (M <= 16).
+    """W4A16 GEMV for decode (M <= 64).
 
     ``workspace``: a uint8 GPU tensor of at least ``w4a16_gemv_workspace_bytes``
     bytes (allocated if None); its contents do not matter. Calls sharing a
@@ -232,7 +232,7 @@ def w4a16_gemv(x, qweight, scales, qzeros, group=128, out=None, workspace=None, 
 
 
 def w4a16_linear(x, qweight, scales, qzeros, group=128, out=None, stream=None):
-    """W4A16 linear layer: the GEMV for M <= 16 (decode), the GEMM otherwise (prefill)."""
+    """W4A16 linear layer: the GEMV for M <= 64 (decode), the GEMM otherwise (prefill)."""
     if x.shape[0] <= GEMV_MAX_M:
         return w4a16_gemv(x, qweight, scales, qzeros, group, out=out, stream=stream)
     return w4a16_gemm(x, qweight, scales, qzeros, group, out=out, stream=stream)

@@ -31,6 +31,9 @@ hipError_t launch_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const ui
                              const int32_t* qzeros, uint16_t* y,
                              int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+// Largest token count the W4A16 GEMV takes (four 16-token MFMA tiles).
+constexpr int64_t kGemvMaxM = 64;
+
 // W4A16 GEMV launch plan: K is cut into `splits` slices across workgroups,
 // each workgroup has `waves` wavefronts that share its K slice.
 struct GemvPlan {

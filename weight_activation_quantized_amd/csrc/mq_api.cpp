@@ -214,7 +214,7 @@ mq_status mq_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_
 }
 
 size_t mq_w4a16_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group) {
-  if (group != 128 || M < 1 || M > 16 || N < 8 || N % 8 || N > kMaxN4 || K < 128 || K > kMaxK || K % 128)
+  if (group != 128 || M < 1 || M > mq::kGemvMaxM || N < 8 || N % 8 || N > kMaxN4 || K < 128 || K > kMaxK || K % 128)
     return 0;
   return mq::plan_w4a16_gemv(M, N, K).workspace_bytes;
 }
@@ -225,7 +225,9 @@ mq_status mq_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const uint16_
                         void* workspace, size_t workspace_bytes, void* stream) {
   mq_status s = check_w4a16(x, qweight, scales, qzeros, y, M, N, K, group);
   if (s != MQ_OK) return s;
-  if (M > 16) return fail(MQ_ERR_UNSUPPORTED, "GEMV needs M <= 16 (got %lld); use mq_w4a16_gemm", (long long)M);
+  if (M > mq::kGemvMaxM)
+    return fail(MQ_ERR_UNSUPPORTED, "GEMV needs M <= %lld (got %lld); use mq_w4a16_gemm",
+                (long long)mq::kGemvMaxM, (long long)M);
   if (M == 0) return ok();
   const mq::GemvPlan plan = mq::plan_w4a16_gemv(M, N, K);
   if (plan.workspace_bytes > 0) {

@@ -34,6 +34,8 @@
 //
 // General kernel (any N % 8 == 0): the same math with (q - z) formed exactly
 // in the fragments and a register-staged double buffer per wavefront.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 #include "w4a16_common.h"
@@ -57,15 +59,15 @@ __device__ __forceinline__ void store_f16x8(uint16_t* dst, const float (&v)[8]) 
   *reinterpret_cast<u32x4*>(dst) = out;
 }
 
-// Lane (j, h) holds tokens 4h..4h+3 of packed column c in tot[p][q] (field
-// p, token 4h + q): write them as fp16 to y, or as fp32 to the split's
-// partial-sum slice.
+// Lane (j, h) holds tokens m0+4h..m0+4h+3 of packed column c in tot[p][q]
+// (field p, token m0 + 4h + q): write them as fp16 to y, or as fp32 to the
+// split's partial-sum slice.
 __device__ __forceinline__ void write_out(const f32x4 (&tot)[8], uint16_t* __restrict__ y,
                                           float* __restrict__ partial, int M, int N, int c, int h, int split,
-                                          int splits) {
+                                          int splits, int m0 = 0) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int m = 4 * h + q;
+    const int m = m0 + 4 * h + q;
     if (m >= M) continue;
     if (splits == 1) {
       float v[8];
@@ -120,7 +122,9 @@ constexpr int kLMaxGroups = 8;                  // groups per split held in LDS
 #define MQ_GEMV_LDS_STAGES 3
 #endif
 constexpr int kLStages = MQ_GEMV_LDS_STAGES;
-constexpr int kLLoadsPerStage = 3;  // per lane: 2 x 16 B of weights + 4 B of x
+// Per lane and stage: 2 x 16 B of weights + 4 B of x per 16-token tile.
+template <int T>
+constexpr int lds_loads_per_stage() { return 2 + T; }
 
 // B fragments of 1024 + q (even p) or 1024 + 16 q (odd p) for one 32-row
 // step: w[e] is the lane's word of row 8h + e; magic holds 0x64006400.
@@ -155,28 +159,37 @@ __device__ __forceinline__ uint32_t lds_weight_offset(int l, int wave, int lane,
   return static_cast<uint32_t>(row) * static_cast<uint32_t>(NP) * 4u + static_cast<uint32_t>(chunk0 + cl) * 16u;
 }
 
-// Start the DMA of stage st (32 rows of the strip + the matching x slice)
-// into its ring slot: 2 x 16 B of weights and 4 B of x per lane.
+// Start the DMA of stage st (32 rows of the strip + the matching x slice of
+// each 16-token tile) into its ring slot: 2 x 16 B of weights and 4 B of x
+// per tile and lane.
+template <int T>
 __device__ __forceinline__ void lds_issue_stage(int st, int g_begin, int NP, int wave, const char* qwb,
-                                                const char* xb, uint32_t woff0, uint32_t woff1, uint32_t xoff,
-                                                lds_u32* s_w, lds_u32* s_x) {
+                                                const char* xb, uint32_t woff0, uint32_t woff1,
+                                                const uint32_t (&xoff)[T], lds_u32* s_w, lds_u32* s_x) {
   const int slot = st % kLStages;
   const int k0 = g_begin * kGroup + st * kLRows;
   const char* wbase = qwb + static_cast<size_t>(k0) * NP * 4;
   lds_u32* wdst = s_w + slot * kLStageWords + wave * 256;
   __builtin_amdgcn_global_load_lds(wbase + woff0, wdst, 16, 0, 0);
   __builtin_amdgcn_global_load_lds(wbase + woff1, wdst + 1024, 16, 0, 0);
-  lds_u32* xdst = s_x + slot * kLXWords + wave * 64;
-  __builtin_amdgcn_global_load_lds(xb + static_cast<size_t>(k0) * 2 + xoff, xdst, 4, 0, 0);
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    lds_u32* xdst = s_x + (slot * T + t) * kLXWords + wave * 64;
+    __builtin_amdgcn_global_load_lds(xb + static_cast<size_t>(k0) * 2 + xoff[t], xdst, 4, 0, 0);
+  }
 }
 
+// kT = number of 16-token tiles (M <= 16 kT); every weight fragment, once
+// unpacked, feeds the MFMAs of all kT tiles.
+template <int kT>
 __global__ __launch_bounds__(256) void w4a16_gemv_lds_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qz,
     uint16_t* __restrict__ y, float* __restrict__ partial, int M, int N, int K, int strips, int splits,
     XcdMap map) {
+  constexpr int kLLoadsPerStage = lds_loads_per_stage<kT>();
   __shared__ __attribute__((aligned(16))) uint32_t s_w[kLStages * kLStageWords];
-  __shared__ __attribute__((aligned(16))) uint32_t s_x[kLStages * kLXWords];
+  __shared__ __attribute__((aligned(16))) uint32_t s_x[kLStages * kT * kLXWords];
   __shared__ __attribute__((aligned(16))) uint32_t s_sc[kLMaxGroups * 256];
   __shared__ __attribute__((aligned(16))) uint32_t s_z[kLMaxGroups * 64];
 
@@ -204,12 +217,14 @@ __global__ __launch_bounds__(256) void w4a16_gemv_lds_kernel(
   // re-read the strip's last valid chunk (never stored).
   const uint32_t woff0 = lds_weight_offset(0, wave, lane, valid_chunks, chunk0, NP);
   const uint32_t woff1 = lds_weight_offset(1, wave, lane, valid_chunks, chunk0, NP);
-  uint32_t xoff;
+  uint32_t xoff[kT];
   {
     const int q = wave * 64 + lane;
     const int i = q >> 4;
     const int c = ((q >> 2) & 3) ^ ((i >> 2) & 3);
-    xoff = static_cast<uint32_t>((min(i, M - 1) * K + c * 8 + (q & 3) * 2) * 2);
+#pragma unroll
+    for (int t = 0; t < kT; ++t)
+      xoff[t] = static_cast<uint32_t>((min(16 * t + i, M - 1) * K + c * 8 + (q & 3) * 2) * 2);
   }
   lds_u32* const s_w_lds = (lds_u32*)(s_w);
   lds_u32* const s_x_lds = (lds_u32*)(s_x);
@@ -241,15 +256,17 @@ __global__ __launch_bounds__(256) void w4a16_gemv_lds_kernel(
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = static_cast<f16>(1.0f);
 
-  f32x4 tot[8];
+  f32x4 tot[kT][8];
 #pragma unroll
-  for (int p = 0; p < 8; ++p)
+  for (int t = 0; t < kT; ++t)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) tot[p][q] = 0.f;
+    for (int p = 0; p < 8; ++p)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tot[t][p][q] = 0.f;
 
   for (int gi = 0; gi < Gs; ++gi) {
-    f32x4 acc[8];
-    f32x4 accx;  // per-token sum of x over the group's rows
+    f32x4 acc[kT][8];
+    f32x4 accx[kT];  // per-token sum of x over the group's rows
 #pragma unroll
     for (int ks = 0; ks < kGroup / kLRows; ++ks) {
       const int it = gi * (kGroup / kLRows) + ks;
@@ -266,14 +283,19 @@ __global__ __launch_bounds__(256) void w4a16_gemv_lds_kernel(
       uint32_t w[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) w[e] = wst[e * 64];
-      const f16x8 a = *reinterpret_cast<const f16x8*>(&s_x[slot * kLXWords + xread]);
+      f16x8 a[kT];
+#pragma unroll
+      for (int t = 0; t < kT; ++t) a[t] = *reinterpret_cast<const f16x8*>(&s_x[(slot * kT + t) * kLXWords + xread]);
       f16x8 b[8];
       unpack_step_biased(w, magic, b);
       const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
-      accx = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ones, ks == 0 ? zero4 : accx, 0, 0, 0);
 #pragma unroll
-      for (int p = 0; p < 8; ++p)
-        acc[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[p], ks == 0 ? zero4 : acc[p], 0, 0, 0);
+      for (int t = 0; t < kT; ++t) {
+        accx[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], ones, ks == 0 ? zero4 : accx[t], 0, 0, 0);
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+          acc[t][p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], b[p], ks == 0 ? zero4 : acc[t][p], 0, 0, 0);
+      }
     }
     // tot += s * (acc - (1024 + z) * X); odd fields carry 16 (q - z), so
     // their scale is s / 16 (exact).
@@ -286,12 +308,17 @@ __global__ __launch_bounds__(256) void w4a16_gemv_lds_kernel(
       const float zf = static_cast<float>((zw >> (4 * p)) & 15u);
       const float bias = (p & 1) ? 1024.0f + 16.0f * zf : 1024.0f + zf;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) tot[p][q] = fmaf(sc, fmaf(-bias, accx[q], acc[p][q]), tot[p][q]);
+      for (int t = 0; t < kT; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tot[t][p][q] = fmaf(sc, fmaf(-bias, accx[t][q], acc[t][p][q]), tot[t][p][q]);
     }
   }
 
   const int c = strip * kLStrip + col;
-  if (c < NP) write_out(tot, y, partial, M, N, c, h, split, splits);
+  if (c < NP) {
+#pragma unroll
+    for (int t = 0; t < kT; ++t) write_out(tot[t], y, partial, M, N, c, h, split, splits, 16 * t);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -506,6 +533,30 @@ GemvPlan plan_w4a16_gemv(int64_t M, int64_t N, int64_t K) {
       ++splits;
       while (G % splits) ++splits;
     }
+    if (M > 16) {
+      // More tokens: each split's fp32 partial sums (M x N, written and read
+      // once) grow with M while the weight stream does not, and the MFMA work
+      // per workgroup grows too. Pick the split count (a divisor of the group
+      // count, at most kLMaxGroups groups per split) with the smallest modelled
+      // time: max(HBM bytes / 5 TB/s, MFMA work / (busy CUs x 2.25 TFLOP/s))
+      // plus about 2 us for the reduce kernel. Both rates are the ones this
+      // kernel pair reaches on the MI355X (stream and 16x16x32 fp16 MFMA with
+      // the unpack).
+      const double mpad = static_cast<double>((M + 15) / 16 * 16);
+      double best = 1e30;
+      int64_t best_s = splits;
+      for (int64_t s = splits; s <= G; ++s) {
+        if (G % s) continue;
+        const double bytes = static_cast<double>(K) * N / 2 + (s > 1 ? 2.0 * s * M * N * 4 : 0.0);
+        const double wgs = static_cast<double>(strips * s < 256 ? strips * s : 256);
+        const double t = std::max(bytes / 5e12, 2.0 * mpad * N * K / (wgs * 2.25e12)) + (s > 1 ? 2e-6 : 0.0);
+        if (t < best) {
+          best = t;
+          best_s = s;
+        }
+      }
+      splits = best_s;
+    }
   }
   plan.splits = static_cast<int>(splits);
   plan.workspace_bytes = splits > 1 ? static_cast<size_t>(splits) * M * N * sizeof(float) : 0;
@@ -527,9 +578,35 @@ hipError_t launch_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const ui
   float* part = static_cast<float*>(workspace);
   hipError_t err;
   if (plan.lds) {
-    if (K / kGroup / plan.splits > kLMaxGroups || (N / 8) % 4 != 0) return hipErrorInvalidValue;
-    err = launch_kernel(w4a16_gemv_lds_kernel, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part, m, n, k,
-                        strips, plan.splits, map);
+    if (K / kGroup / plan.splits > kLMaxGroups || (N / 8) % 4 != 0 || M > kGemvMaxM) return hipErrorInvalidValue;
+    switch ((m + 15) / 16) {
+      case 1:
+        err = launch_kernel(w4a16_gemv_lds_kernel<1>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part, m, n,
+                            k, strips, plan.splits, map);
+        break;
+      case 2:
+        err = launch_kernel(w4a16_gemv_lds_kernel<2>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part, m, n,
+                            k, strips, plan.splits, map);
+        break;
+      case 3:
+        err = launch_kernel(w4a16_gemv_lds_kernel<3>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part, m, n,
+                            k, strips, plan.splits, map);
+        break;
+      default:
+        err = launch_kernel(w4a16_gemv_lds_kernel<4>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part, m, n,
+                            k, strips, plan.splits, map);
+        break;
+    }
+  } else if (M > 16) {
+    // The register-staged kernel takes 16 tokens at a time: run it on
+    // consecutive 16-token slices (same stream, so they share the workspace).
+    for (int64_t m0 = 0; m0 < M; m0 += 16) {
+      const int64_t ms = M - m0 < 16 ? M - m0 : 16;
+      err = launch_w4a16_gemv(x + m0 * K, qweight, scales, qzeros, y + m0 * N, ms, N, K,
+                              plan_w4a16_gemv(ms, N, K), workspace, stream);
+      if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
   } else {
     switch (plan.waves) {
       case 2:
