@@ -54,12 +54,14 @@ constexpr int kBK = 128;     // K bytes per stage (128-byte row segments)
 constexpr int kSlots = 3;    // LDS ring depth (stages)
 constexpr int kChunks = kBK / 16;                      // 16-byte chunks per tile row
 constexpr int kRowsPerLoad = 1024 / kBK;               // rows one 64 x 16 B load fills
-constexpr int kLoadsX = kBM / kRowsPerLoad / kWaves;   // per wave per stage
-constexpr int kLoadsW = kBN / kRowsPerLoad / kWaves;
+// Group 0 issues every fill (group 1 never waits on the texture unit, so
+// its MFMAs keep running while group 0 stalls on a full fill queue).
+constexpr int kLoadsX = kBM / kRowsPerLoad / kGroupWaves;  // per filling wave per stage
+constexpr int kLoadsW = kBN / kRowsPerLoad / kGroupWaves;
 constexpr int kLoads = kLoadsX + kLoadsW;
 constexpr int kStageBytes = (kBM + kBN) * kBK;
 constexpr int kSubPerGroup = kBK / 2 / 32;  // MFMA k-steps per group and stage
-static_assert(kLoads < 32, "vmcnt range");
+static_assert(kLoads < 32 && kLoads % 2 == 0, "vmcnt range / two bursts per round");
 static_assert(kSlots * kStageBytes <= 160 * 1024, "LDS capacity");
 static_assert(kSubPerGroup == 2, "a round below is written for two k-steps per group");
 
@@ -120,16 +122,16 @@ __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __res
   const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(xq + static_cast<size_t>(m0) * K, min(kBM, M - m0) * K);
   const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(wq + static_cast<size_t>(n0) * K, min(kBN, N - n0) * K);
 
-  // Fill l of this wave (l < kLoadsX: token rows, else channel rows) covers
-  // tile rows (wave + 8u) * kRowsPerLoad .. with u = l or l - kLoadsX; lane L
-  // writes physical chunk L % kChunks of row L / kChunks, so it fetches the
-  // logical chunk that the swizzle places there.
+  // Fill l of group 0's wave r (l < kLoadsX: token rows, else channel rows)
+  // covers tile rows (r + 4u) * kRowsPerLoad .. with u = l or l - kLoadsX;
+  // lane L writes physical chunk L % kChunks of row L / kChunks, so it
+  // fetches the logical chunk that the swizzle places there.
   uint32_t loff[kLoads];
   int lk[kLoads];
 #pragma unroll
   for (int l = 0; l < kLoads; ++l) {
     const int u = l < kLoadsX ? l : l - kLoadsX;
-    const int row = (wave + kWaves * u) * kRowsPerLoad + lane / kChunks;
+    const int row = (r + kGroupWaves * u) * kRowsPerLoad + lane / kChunks;
     lk[l] = 16 * ((lane % kChunks) ^ chunk_swizzle(row));
     loff[l] = static_cast<uint32_t>(row * K + lk[l]);
   }
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __res
 
   const int nst = (K + kBK - 1) / kBK;
 
-  // Fills [L0, L1) of stage S (every wave issues its share).
+  // Fills [L0, L1) of stage S (issued by group 0's waves).
 #define MQ_ISSUE(S, L0, L1)                                                                      \
   do {                                                                                           \
     const int k0_ = (S) * kBK;                                                                   \
@@ -161,10 +163,10 @@ __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __res
       const uint32_t off_ = lk[l] < krem_ ? loff[l] + k0_ : kOob;                                \
       if (l < kLoadsX) {                                                                         \
         __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                \
-            rx, (lds_void*)(dst_ + (wave + kWaves * l) * 1024), 16, off_, 0, 0, 0);              \
+            rx, (lds_void*)(dst_ + (r + kGroupWaves * l) * 1024), 16, off_, 0, 0, 0);            \
       } else {                                                                                   \
         __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                \
-            rw, (lds_void*)(dst_ + kBM * kBK + (wave + kWaves * (l - kLoadsX)) * 1024), 16,      \
+            rw, (lds_void*)(dst_ + kBM * kBK + (r + kGroupWaves * (l - kLoadsX)) * 1024), 16,    \
             off_, 0, 0, 0);                                                                      \
       }                                                                                          \
     }                                                                                            \
@@ -192,15 +194,18 @@ __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __res
   } while (0)
 
   // Stage s sits in slot s % 3. Both groups compute every stage, group g on
-  // its k half. Round s: every wave issues its fills of stage s + 2 into the
-  // slot of stage s - 1 (which every wave finished reading before the barrier
-  // that ended round s - 1), computes its half of stage s, waits for its own
-  // loads of stage s + 1 (loads complete in issue order, so only stage s + 2
-  // stays in flight) and meets the barrier, after which stage s + 1 is
-  // complete and readable.
-  MQ_ISSUE(0, 0, kLoads);
+  // its k half. Round s: group 0's waves issue the fills of stage s + 2 into
+  // the slot of stage s - 1 (which every wave finished reading before the
+  // barrier that ended round s - 1); every wave computes its half of stage
+  // s; group 0's waves wait for their own loads of stage s + 1 (loads
+  // complete in issue order, so only stage s + 2 stays in flight; group 1
+  // has none to wait for) and all meet the barrier, after which stage s + 1
+  // is complete and readable.
+  if (g == 0) {
+    MQ_ISSUE(0, 0, kLoads);
+    if (1 < nst) MQ_ISSUE(1, 0, kLoads);
+  }
   if (1 < nst) {
-    MQ_ISSUE(1, 0, kLoads);
     wait_counts<kLoads, 0>();
   } else {
     wait_counts<0, 0>();
@@ -215,35 +220,43 @@ __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __res
   // second k-step's MFMAs are issued before the barrier and half after it,
   // under the reads of stage s + 1's first fragments.
   int s = 0;
-  for (; s + 2 < nst; ++s) {
-    // Three fills of stage s + 2 go out at the start of each k-step: a burst
-    // of all six stalls the wave on the texture unit's full command queue,
-    // and single fills between MFMAs stall it more often.
-    __builtin_amdgcn_sched_barrier(0);
-    MQ_ISSUE(s + 2, 0, kLoads / 2);
-    __builtin_amdgcn_sched_barrier(0);
-    MQ_READ_FRAGS(s, 1, fx1, fw1);
-    MQ_MFMAS(fx0, fw0);
-    _Pragma("unroll") for (int i_ = 0; i_ < 3; ++i_) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    MQ_ISSUE(s + 2, kLoads / 2, kLoads);
-    __builtin_amdgcn_sched_barrier(0);
-    MQ_MFMAS_HALF(fx1, fw1, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_counts<kLoads, 0>();
-    bare_barrier();
-    MQ_READ_FRAGS(s + 1, 0, fx0, fw0);
-    MQ_MFMAS_HALF(fx1, fw1, 1);
-    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
-    __builtin_amdgcn_sched_barrier(0);
+  // One steady round; FILL: this wave issues fills (group 0). Half of the
+  // fills of stage s + 2 go out at the start of each k-step: one burst of
+  // all of them stalls the wave on the texture unit's full command queue
+  // for longer, and single fills between MFMAs stall it more often.
+#define MQ_STEADY(FILL) \
+  for (; s + 2 < nst; ++s) { \
+    __builtin_amdgcn_sched_barrier(0); \
+    if (FILL) MQ_ISSUE(s + 2, 0, kLoads / 2); \
+    __builtin_amdgcn_sched_barrier(0); \
+    MQ_READ_FRAGS(s, 1, fx1, fw1); \
+    MQ_MFMAS(fx0, fw0); \
+    _Pragma("unroll") for (int i_ = 0; i_ < 3; ++i_) { \
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0); \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); \
+    } \
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0); \
+    __builtin_amdgcn_sched_barrier(0); \
+    if (FILL) MQ_ISSUE(s + 2, kLoads / 2, kLoads); \
+    __builtin_amdgcn_sched_barrier(0); \
+    MQ_MFMAS_HALF(fx1, fw1, 0); \
+    __builtin_amdgcn_sched_barrier(0); \
+    wait_counts<kLoads, 0>(); \
+    bare_barrier(); \
+    MQ_READ_FRAGS(s + 1, 0, fx0, fw0); \
+    MQ_MFMAS_HALF(fx1, fw1, 1); \
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0); \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); \
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0); \
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0); \
+    __builtin_amdgcn_sched_barrier(0); \
   }
+  if (g == 0) {
+    MQ_STEADY(true)
+  } else {
+    MQ_STEADY(false)
+  }
+#undef MQ_STEADY
   // Last two stages (or fewer): nothing left to fill.
   for (; s < nst; ++s) {
     MQ_READ_FRAGS(s, 1, fx1, fw1);
