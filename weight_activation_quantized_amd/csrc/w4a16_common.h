@@ -23,6 +23,22 @@ namespace mq {
 
 constexpr int kGroup = 128;
 
+// The two field masks and the 1024.0 pattern, held in VGPRs: gfx9 VOP3
+// encodings take no literal constants, so with literal masks the compiler
+// splits each (v & mask) | magic into v_and_b32 + v_or_b32; with register
+// operands it emits one v_and_or_b32 (a third fewer VALU ops in the unpack).
+// The values come from non-volatile asm the compiler can hoist out of loops.
+struct NibConst {
+  uint32_t lo, hi, magic;
+};
+__device__ __forceinline__ NibConst nib_const() {
+  NibConst c;
+  asm("v_mov_b32 %0, 0x000f000f" : "=v"(c.lo));
+  asm("v_mov_b32 %0, 0x00f000f0" : "=v"(c.hi));
+  asm("v_mov_b32 %0, 0x64006400" : "=v"(c.magic));
+  return c;
+}
+
 // -(1024 + z_p) (even p) or -(1024 + 16 z_p) (odd p), replicated in both
 // fp16 halves, for the 8 fields of zero-point word zw.
 __device__ __forceinline__ void zero_bias(uint32_t zw, uint32_t (&negz)[8]) {
@@ -38,14 +54,15 @@ __device__ __forceinline__ void zero_bias(uint32_t zw, uint32_t (&negz)[8]) {
 // w[e] is the word of row 8h + e; b[p][e] belongs to field p of row 8h + e.
 __device__ __forceinline__ void unpack_step(const uint32_t (&w)[8], const uint32_t (&negz)[8],
                                             f16x8 (&b)[8]) {
+  const NibConst c = nib_const();
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const uint32_t lo = byte_perm(w[2 * t + 1], w[2 * t], 0x05040100u);  // bytes 0,1 of both rows
     const uint32_t hi = byte_perm(w[2 * t + 1], w[2 * t], 0x07060302u);  // bytes 2,3 of both rows
     const uint32_t lo8 = lo >> 8, hi8 = hi >> 8;
-    const uint32_t v[8] = {nib_lo_to_f16x2(lo),  nib_hi_to_f16x2(lo),  nib_lo_to_f16x2(lo8),
-                           nib_hi_to_f16x2(lo8), nib_lo_to_f16x2(hi),  nib_hi_to_f16x2(hi),
-                           nib_lo_to_f16x2(hi8), nib_hi_to_f16x2(hi8)};
+    const uint32_t v[8] = {(lo & c.lo) | c.magic,  (lo & c.hi) | c.magic,  (lo8 & c.lo) | c.magic,
+                           (lo8 & c.hi) | c.magic, (hi & c.lo) | c.magic,  (hi & c.hi) | c.magic,
+                           (hi8 & c.lo) | c.magic, (hi8 & c.hi) | c.magic};
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const f16x2 d = as_f16x2(v[p]) + as_f16x2(negz[p]);
@@ -59,14 +76,15 @@ __device__ __forceinline__ void unpack_step(const uint32_t (&w)[8], const uint32
 // (s for even p, s/16 for odd p): each fragment element is fp16((q - z) * s).
 __device__ __forceinline__ void unpack_step_scaled(const uint32_t (&w)[8], const uint32_t (&negz)[8],
                                                    const uint32_t (&sc2)[8], f16x8 (&b)[8]) {
+  const NibConst c = nib_const();
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const uint32_t lo = byte_perm(w[2 * t + 1], w[2 * t], 0x05040100u);
     const uint32_t hi = byte_perm(w[2 * t + 1], w[2 * t], 0x07060302u);
     const uint32_t lo8 = lo >> 8, hi8 = hi >> 8;
-    const uint32_t v[8] = {nib_lo_to_f16x2(lo),  nib_hi_to_f16x2(lo),  nib_lo_to_f16x2(lo8),
-                           nib_hi_to_f16x2(lo8), nib_lo_to_f16x2(hi),  nib_hi_to_f16x2(hi),
-                           nib_lo_to_f16x2(hi8), nib_hi_to_f16x2(hi8)};
+    const uint32_t v[8] = {(lo & c.lo) | c.magic,  (lo & c.hi) | c.magic,  (lo8 & c.lo) | c.magic,
+                           (lo8 & c.hi) | c.magic, (hi & c.lo) | c.magic,  (hi & c.hi) | c.magic,
+                           (hi8 & c.lo) | c.magic, (hi8 & c.hi) | c.magic};
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const f16x2 d = (as_f16x2(v[p]) + as_f16x2(negz[p])) * as_f16x2(sc2[p]);
