@@ -123,6 +123,37 @@ def test_w8a8_extreme_accumulators():
     assert acc.max() == 16129 * K and acc.min() == -16129 * K
 
 
+@pytest.mark.parametrize("M", [3, 300], ids=["decode_kernel", "tiled_gemm"])
+def test_w8a8_largest_k(M):
+    # K = 133136, the largest multiple of 16 whose worst-case accumulator
+    # (127 * 127 * K) still fits int32: all +-127 rows hit the bound exactly.
+    K, N = 133136, 40
+    rng = np.random.default_rng(M)
+    xq = rng.integers(-127, 128, size=(M, K), dtype=np.int8)
+    wq = rng.integers(-127, 128, size=(N, K), dtype=np.int8)
+    xq[0] = 127
+    wq[0] = 127
+    wq[1] = -127
+    announce(f"w8a8 largest K M={M}")
+    acc = host(mq.w8a8_mm_i32(dev(xq), dev(wq)))
+    ref = oracle.w8a8_acc_ref(xq, wq)
+    assert np.array_equal(acc.astype(np.int64), ref)
+    assert acc[0, 0] == 16129 * K and acc[0, 1] == -16129 * K
+
+
+@pytest.mark.parametrize("fn,M,N", [(mq.w4a16_gemv, 2, 264), (mq.w4a16_gemv, 5, 256), (mq.w4a16_gemv, 40, 256),
+                                    (mq.w4a16_gemm, 100, 264)],
+                         ids=["gemv_regs", "gemv_lds", "gemv_lds_3tiles", "gemm"])
+def test_w4a16_long_k(fn, M, N):
+    # K = 65536 (512 groups): many splits per strip, long stage loops. The
+    # activations are scaled by 1/4 (exact in fp16) and carry no outliers so
+    # that |y| stays well below 128: above it half an fp16 ulp (0.0625)
+    # alone exceeds the 5e-2 max-abs bound.
+    d = _w4(M, 65536, N, outliers=0.0, tag=N + M)
+    d["x"] = (d["x"] * np.float16(0.25)).astype(np.float16)
+    assert_fp16_close(_run_w4(fn, d, "long K"), _ref_w4(d), f"{fn.__name__} M={M} K=65536 N={N}")
+
+
 def test_w8a8_linear_end_to_end():
     d = synth.w8a8_inputs(300, 4096, 1024, outlier_frac=0.01, tag=22)
     wq, s_ch = oracle.quant_per_token_int8_ref(d["wf"])
