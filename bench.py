@@ -154,10 +154,10 @@ def bench_gemv(torch, mq, synth, args, log):
     wall, ev = timed_replay(torch, g_timed)
     step_bytes = sum(w4a16_bytes(M, GEMV_K, GEMV_N) for M in GEMV_MS)
     launches = args.steps * len(GEMV_MS)
-    splits = {M: mq.w4a16_gemv_workspace_bytes(M, GEMV_N, GEMV_K, GROUP) for M in GEMV_MS}
+    workspace_bytes = {M: mq.w4a16_gemv_workspace_bytes(M, GEMV_N, GEMV_K, GROUP) for M in GEMV_MS}
     return {
         "wall_s": wall, "event_s": ev, "step_bytes": step_bytes, "launches": launches,
-        "kernel_avg_us": ev / launches * 1e6, "splits": splits,
+        "kernel_avg_us": ev / launches * 1e6, "workspace_bytes": workspace_bytes,
         "bytes_per_launch_avg": step_bytes / len(GEMV_MS),
     }, sets, xs
 
@@ -374,7 +374,7 @@ def main(argv=None):
             "workload": "W4A16 decode GEMV (8B MLP gate+up): M in {1,4,16}, K=4096, N=24576, group 128; "
                         f"{args.sets} rotating weight sets (cold HBM); one step = one GEMV per M",
             "M": list(GEMV_MS), "K": GEMV_K, "N": GEMV_N, "group": GROUP, "weight_sets": args.sets,
-            "gemv_workspace_bytes": res["splits"], "parallelism": "single GPU",
+            "gemv_workspace_bytes": res["workspace_bytes"], "parallelism": "single GPU",
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -110,6 +110,10 @@ mq_status mq_quant_per_token_int8(const uint16_t* x, int8_t* xq, float* s_tok,
  * Requires: 0 <= M, N < 2^31; 16 <= K <= 133144 (the int32 accumulator
  * bound 127*127*K < 2^31), K % 16 == 0; xq, wq, y 16-byte aligned; s_tok,
  * s_ch 4-byte aligned.
+ * The kernel is chosen by shape (a weight-streaming kernel for up to 32
+ * tokens, and for 33-64 tokens while N < 16384; a tiled GEMM otherwise).
+ * Both compute the exact accumulator and the same epilogue, so results are
+ * identical whichever runs, and deterministic.
  */
 mq_status mq_w8a8_scaled_mm(const int8_t* xq, const float* s_tok, const int8_t* wq,
                             const float* s_ch, uint16_t* y,
