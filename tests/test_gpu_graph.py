@@ -1,0 +1,105 @@
+"""Every entry point captured in a HIP graph and replayed.
+
+The entry points are asynchronous and allocate and clear nothing, so a
+caller may capture them (the benchmark does). Here each path is captured
+once with static buffers; between replays the test rewrites the inputs with
+eager copies and runs the same calls eagerly on other outputs. Every replay
+must match the eager result bit for bit (the kernels are deterministic) and
+the oracle within the usual tolerance.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import weight_activation_quantized_amd as mq
+from tests.gpu_util import announce, assert_fp16_close
+
+pytestmark = pytest.mark.gpu
+
+REPLAYS = 3
+
+
+def _capture(torch, fn):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()  # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def test_graph_replays_w4a16():
+    import torch
+    K = 4096
+    cases = [("gemv_split", 16, 6144), ("gemv_tiles", 40, 4096), ("gemm", 200, 1024)]
+    for name, M, N in cases:
+        d = synth.w4a16_inputs(M, K, N, group=128, outlier_frac=0.005, tag=500 + N)
+        w = {k: torch.from_numpy(d[k]).cuda() for k in ("qweight", "scales", "qzeros")}
+        x = torch.from_numpy(d["x"]).cuda()
+        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        gemv = M <= mq.GEMV_MAX_M
+        ws = torch.empty(max(mq.w4a16_gemv_workspace_bytes(M, N, K), 16), dtype=torch.uint8, device="cuda")
+
+        def call(out, x=x):
+            if gemv:
+                mq.w4a16_gemv(x, w["qweight"], w["scales"], w["qzeros"], 128, out=out, workspace=ws)
+            else:
+                mq.w4a16_gemm(x, w["qweight"], w["scales"], w["qzeros"], 128, out=out)
+
+        announce(f"graph w4a16 {name} M={M} N={N}")
+        g = _capture(torch, lambda: call(y))
+        rng = np.random.default_rng(7)
+        for r in range(REPLAYS):
+            xr = rng.standard_normal((M, K)).astype(np.float16)
+            x.copy_(torch.from_numpy(xr))
+            eager = torch.empty_like(y)
+            call(eager)
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y, eager), f"{name}: replay {r} differs from the eager call"
+            ref = oracle.w4a16_ref(xr, d["qweight"], d["scales"], d["qzeros"], 128)
+            assert_fp16_close(y.cpu().numpy(), ref, f"graph {name} replay {r}")
+
+
+def test_graph_replays_w8a8():
+    import torch
+    K = 1024
+    for name, M, N in (("decode", 8, 4096), ("tiled", 300, 640)):
+        d = synth.w8a8_inputs(M, K, N, outlier_frac=0.01, tag=600 + N)
+        wq_np, s_ch_np = oracle.quant_per_token_int8_ref(d["wf"])
+        wq, s_ch = torch.from_numpy(wq_np).cuda(), torch.from_numpy(s_ch_np).cuda()
+        x = torch.from_numpy(d["x"]).cuda()
+        xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+        st = torch.empty((M,), dtype=torch.float32, device="cuda")
+        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+
+        def layer(xq, st, y, acc):
+            mq.quant_per_token_int8(x, out=xq, s_out=st)
+            mq.w8a8_scaled_mm(xq, st, wq, s_ch, out=y)
+            mq.w8a8_mm_i32(xq, wq, out=acc)
+
+        announce(f"graph w8a8 {name} M={M} N={N}")
+        g = _capture(torch, lambda: layer(xq, st, y, acc))
+        rng = np.random.default_rng(11)
+        for r in range(REPLAYS):
+            xr = (rng.standard_normal((M, K)) * (1 + r)).astype(np.float16)
+            x.copy_(torch.from_numpy(xr))
+            e = [torch.empty_like(t) for t in (xq, st, y, acc)]
+            layer(*e)
+            g.replay()
+            torch.cuda.synchronize()
+            for got, want, what in zip((xq, st, y, acc), e, ("xq", "s_tok", "y", "acc")):
+                assert torch.equal(got, want), f"{name}: replay {r} {what} differs from the eager call"
+            xq_ref, s_ref = oracle.quant_per_token_int8_ref(xr)
+            assert np.array_equal(xq.cpu().numpy(), xq_ref)
+            assert np.array_equal(acc.cpu().numpy().astype(np.int64), oracle.w8a8_acc_ref(xq_ref, wq_np))
+            assert_fp16_close(y.cpu().numpy(), oracle.w8a8_ref(xq_ref, s_ref, wq_np, s_ch_np),
+                              f"graph w8a8 {name} replay {r}")
