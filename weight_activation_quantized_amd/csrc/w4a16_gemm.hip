@@ -7,24 +7,28 @@
 //
 // Design:
 // - v_mfma_f32_32x32x16_f16 (on gfx950 about 1.5x the rate of the 16x16x32
-//   form). A workgroup computes 64 tokens x 1024 outputs with four
-//   wavefronts side by side in N; a wavefront owns 64 x 256 (two 32-token
-//   A fragments x eight field tiles, 256 fp32 accumulators per lane), so
-//   every weight is dequantized exactly once per workgroup.
-// - Field tiles: lane (j = lane%32, h = lane/32) of the B operand takes word
-//   j (packed column j of the wavefront) of rows 8h..8h+7 of a 16-row k-step
-//   and unpacks it into eight fp16 fragments, one per 4-bit field p; tile p
-//   then covers outputs 8c + p of the 32 packed columns c. The unpack is
-//   exact and each weight is rounded once, to fp16((q - z) * s).
+//   form). A workgroup computes 64 tokens x 1024 outputs with eight
+//   wavefronts side by side in N, two per SIMD; a wavefront owns 64 x 128
+//   (two 32-token A fragments x four B tiles, 128 fp32 accumulators per
+//   lane), so every weight is dequantized exactly once per workgroup and one
+//   wavefront's unpack overlaps the other's MFMAs on each SIMD.
+// - B tiles: lane (j = lane%32, h = lane/32) takes packed column j%16 of the
+//   wavefront's 16 and field parity j/16; it reads that column's words of
+//   rows 8h..8h+7 of a 16-row k-step and unpacks its four fields
+//   p = 2q + j/16 into four fp16 fragments, so tile q covers fields 2q and
+//   2q + 1 of the 16 columns. The unpack is exact and each weight is rounded
+//   once, to fp16((q - z) * s).
 // - Everything moves HBM -> LDS with buffer_load ... lds through a ring of
-//   kStages 32-row stages: the x rows (shared by the four wavefronts), each
-//   wavefront's raw packed words, scales and zero points. Loads past a
-//   buffer descriptor's size return zero (ragged M); columns past N read
-//   valid memory and are never stored.
+//   kStages 32-row stages: the x rows (shared by all wavefronts) and, per
+//   32-column area, its raw packed words, scales and zero points. The first
+//   four wavefronts issue all the fills, one area each; the other four only
+//   compute. Loads past a buffer descriptor's size return zero (ragged M);
+//   columns past N read valid memory and are never stored.
 // - x rows are 64 bytes per stage with the 16-byte chunk index XOR-swizzled
 //   by the row (conflict-free fragment reads). Raw weight rows are 128
 //   bytes; k-row r is stored at LDS row r with bits 0 and 3 swapped, so the
 //   two lane halves (rows 8h + e) read opposite halves of the banks.
+// - The output tile is staged in LDS as fp16 and written as whole rows.
 // - Workgroups are dispatched round-robin over the 8 XCDs; tiles are
 //   remapped so an XCD runs consecutive token tiles of one weight tile.
 #include "device_common.h"
@@ -34,24 +38,29 @@
 namespace mq {
 namespace {
 
-constexpr int kBM = 64;                    // tokens per workgroup tile
-constexpr int kWaves = 4;                  // side by side in N
-constexpr int kWaveCols = 32;              // packed columns per wavefront (256 outputs)
-constexpr int kTileCols = kWaves * kWaveCols;  // 128 packed columns (1024 outputs)
-constexpr int kRows = 32;                  // K rows per stage (two 16-row MFMA k-steps)
+constexpr int kBM = 64;         // tokens per workgroup tile
+constexpr int kAreas = 4;       // DMA areas of 32 packed columns (128-byte weight rows)
+constexpr int kAreaCols = 32;   // packed columns per area
+constexpr int kTileCols = kAreas * kAreaCols;  // 128 packed columns (1024 outputs)
+constexpr int kWaves = 8;       // two per area (16 packed columns each), two per SIMD
+constexpr int kWaveCols = 16;   // packed columns per wavefront
+constexpr int kThreads = kWaves * 64;
+constexpr int kRows = 32;       // K rows per stage (two 16-row MFMA k-steps)
 #ifndef MQ_W4_STAGES
 #define MQ_W4_STAGES 6
 #endif
 constexpr int kStages = MQ_W4_STAGES;
-constexpr int kABytes = kBM * kRows * 2;       // x rows: 64 x 64 B
-constexpr int kBBytes = kRows * kWaveCols * 4;  // a wavefront's raw words: 32 x 128 B
-constexpr int kSBytes = 1024;                   // a wavefront's scales (512 B used)
-constexpr int kZBytes = 256;                    // a wavefront's zero points (128 B used)
-constexpr int kWaveBytes = kBBytes + kSBytes + kZBytes;
-constexpr int kSlotBytes = kABytes + kWaves * kWaveBytes;
-constexpr int kLoads = 7;  // per wavefront per stage: 1 x, 4 weights, 1 scales, 1 zero points
+constexpr int kABytes = kBM * kRows * 2;         // x rows: 64 x 64 B
+constexpr int kBBytes = kRows * kAreaCols * 4;   // an area's raw words: 32 x 128 B
+constexpr int kSBytes = 1024;                    // an area's scales (512 B used)
+constexpr int kZBytes = 256;                     // an area's zero points (128 B used)
+constexpr int kAreaBytes = kBBytes + kSBytes + kZBytes;
+constexpr int kSlotBytes = kABytes + kAreas * kAreaBytes;
+constexpr int kLoads = 7;  // per filling wavefront (one per area) and stage: 1 x, 4 weights, 1 scales, 1 zeros
+constexpr int kOutPitch = kTileCols * 8 * 2 + 16;  // bytes per staged output row
 static_assert(kStages >= 2 && (kStages - 2) * kLoads < 64, "ring depth / vmcnt range");
 static_assert(kStages * kSlotBytes <= 160 * 1024, "LDS capacity");
+static_assert(kBM * kOutPitch <= kStages * kSlotBytes, "output staging fits the ring");
 
 constexpr int kBufferFlags = 0x00020000;  // gfx9 buffer descriptor word 3 (raw 32-bit data)
 
@@ -72,26 +81,51 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(n), kBufferFlags);
 }
 
+// A lane handles one 4-bit field parity par (lanes 16-31 of each half-wave
+// the odd fields): its four fields are p = 2q + par, q = 0..3.
 struct GroupParams {
-  uint32_t negz[8];  // -(1024 + z) (even p) or -(1024 + 16 z) (odd p), both halves
-  uint32_t sc2[8];   // s (even p) or s / 16 (odd p), both halves
+  uint32_t negz[4];  // -(1024 + z_p) (even p) or -(1024 + 16 z_p) (odd p), both halves
+  uint32_t sc2[4];   // s_p (even p) or s_p / 16 (odd p), both halves
 };
 
-__device__ __forceinline__ void make_group_params(uint32_t zw, u32x4 sv, GroupParams& gp) {
-  zero_bias(zw, gp.negz);
+__device__ __forceinline__ void make_group_params(uint32_t zw, u32x4 sv, int par, GroupParams& gp) {
+  const uint32_t zmask = par ? 0xF0u : 0x0Fu;
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const f16x2 s2 = as_f16x2(sv[p >> 1]);
-    f16 s = s2[p & 1];
-    if (p & 1) s = s * static_cast<f16>(0.0625f);  // exact: power-of-two rescale of a normal fp16
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t e = ((zw >> (8 * q)) & zmask) | 0xE400u;
+    gp.negz[q] = e | (e << 16);
+    const f16x2 s2 = as_f16x2(sv[q]);
+    f16 sc = par ? s2[1] * static_cast<f16>(0.0625f) : s2[0];  // exact: power-of-two rescale
     f16x2 rep;
-    rep[0] = s;
-    rep[1] = s;
-    gp.sc2[p] = as_u32(rep);
+    rep[0] = sc;
+    rep[1] = sc;
+    gp.sc2[q] = as_u32(rep);
   }
 }
 
-__global__ __launch_bounds__(256) void w4a16_gemm_kernel(const uint16_t* __restrict__ x,
+// Fragments fp16((q - z) * s) of the lane's four fields for one 16-row
+// k-step: w[e] is the lane's word of row 8h + e. The byte permute gathers
+// bytes 0-1 (2-3) of a row pair; field p sits in byte p / 2 of a word, low
+// nibble for even p, high nibble (giving 1024 + 16 q) for odd p, selected
+// by the lane's mask.
+__device__ __forceinline__ void unpack_fields(const uint32_t (&w)[8], const GroupParams& gp, uint32_t mask,
+                                              uint32_t magic, f16x8 (&b)[4]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t lo = byte_perm(w[2 * t + 1], w[2 * t], 0x05040100u);
+    const uint32_t hi = byte_perm(w[2 * t + 1], w[2 * t], 0x07060302u);
+    const uint32_t src[4] = {lo, lo >> 8, hi, hi >> 8};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t v = (src[q] & mask) | magic;
+      const f16x2 d = (as_f16x2(v) + as_f16x2(gp.negz[q])) * as_f16x2(gp.sc2[q]);
+      b[q][2 * t] = d[0];
+      b[q][2 * t + 1] = d[1];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __restrict__ x,
                                                          const uint32_t* __restrict__ qw,
                                                          const uint16_t* __restrict__ scales,
                                                          const uint32_t* __restrict__ qz,
@@ -119,23 +153,25 @@ __global__ __launch_bounds__(256) void w4a16_gemm_kernel(const uint16_t* __restr
   // or, past the last row, zero.
   const __amdgpu_buffer_rsrc_t rx = rsrc(x + static_cast<size_t>(m0) * K, static_cast<int64_t>(min(kBM, M - m0)) * K * 2);
 
-  // Per-lane parts of the DMA source offsets.
-  //  x: wave w fills rows 16w .. 16w+15; lane L -> row 16w + L/4, physical
-  //     chunk L%4, which holds logical chunk (L%4) ^ swizzle(row).
-  const int xa_row = 16 * wave + lane / 4;
+  // DMA: wavefront a < kAreas fills area a (packed columns 32a .. 32a+31) and
+  // x rows 16a .. 16a+15 of every stage; the other four only compute.
+  const bool filler = wave < kAreas;
+  const int fa = filler ? wave : 0;
+  //  x: lane L -> row 16a + L/4, physical chunk L%4, which holds logical
+  //     chunk (L%4) ^ swizzle(row).
+  const int xa_row = 16 * fa + lane / 4;
   const uint32_t xa_off = static_cast<uint32_t>(xa_row * K + 8 * ((lane % 4) ^ chunk_swizzle(xa_row))) * 2u;
-  //  weights: load u fills LDS rows 8u .. 8u+7 of the wave's area; lane L ->
-  //     LDS row 8u + L/8 = k-row raw_row(.), 16-byte chunk L%8 (words 4(L%8)..).
+  //  weights: load u fills LDS rows 8u .. 8u+7 of the area; lane L -> LDS
+  //     row 8u + L/8 = k-row raw_row(.), 16-byte chunk L%8 (words 4(L%8)..).
   uint32_t wr_off[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u)
-    wr_off[u] = static_cast<uint32_t>(raw_row(8 * u + lane / 8) * NP + kWaveCols * wave + 4 * (lane % 8)) * 4u;
-  //  scales: lane L -> the 8 scales of packed column (L % 32) of the wave;
+    wr_off[u] = static_cast<uint32_t>(raw_row(8 * u + lane / 8) * NP + kAreaCols * fa + 4 * (lane % 8)) * 4u;
+  //  scales: lane L -> the 8 scales of packed column (L % 32) of the area;
   //  zero points: lane L -> word (L % 32).
-  const uint32_t s_off = static_cast<uint32_t>(8 * (kWaveCols * wave + lane % 32)) * 2u;
-  const uint32_t z_off = static_cast<uint32_t>(kWaveCols * wave + lane % 32) * 4u;
-
-  lds_i8* const wave_area = sm + kABytes + wave * kWaveBytes;  // + slot offset
+  const uint32_t s_off = static_cast<uint32_t>(8 * (kAreaCols * fa + lane % 32)) * 2u;
+  const uint32_t z_off = static_cast<uint32_t>(kAreaCols * fa + lane % 32) * 4u;
+  lds_i8* const fill_area = sm + kABytes + fa * kAreaBytes;  // + slot offset
 
 #define MQ_ISSUE(ST)                                                                                 \
   do {                                                                                               \
@@ -148,19 +184,25 @@ __global__ __launch_bounds__(256) void w4a16_gemm_kernel(const uint16_t* __restr
                                             (static_cast<int64_t>(G - g_) * N - c0 * 8) * 2);         \
     const __amdgpu_buffer_rsrc_t rz_ =                                                               \
         rsrc(qz + static_cast<size_t>(g_) * NP + c0, (static_cast<int64_t>(G - g_) * NP - c0) * 4);  \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(sm + so_ + wave * 1024), 16,            \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(sm + so_ + fa * 1024), 16,              \
                                              xa_off + k0_ * 2, 0, 0, 0);                             \
     _Pragma("unroll") for (int u = 0; u < 4; ++u)                                                    \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw_, (lds_void*)(wave_area + so_ + u * 1024), 16,   \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw_, (lds_void*)(fill_area + so_ + u * 1024), 16,   \
                                                  wr_off[u], 0, 0, 0);                                \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (lds_void*)(wave_area + so_ + kBBytes), 16, s_off, \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (lds_void*)(fill_area + so_ + kBBytes), 16, s_off, \
                                              0, 0, 0);                                               \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rz_, (lds_void*)(wave_area + so_ + kBBytes + kSBytes), 4, \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rz_, (lds_void*)(fill_area + so_ + kBBytes + kSBytes), 4, \
                                              z_off, 0, 0, 0);                                        \
   } while (0)
 
-  // Fragment read offsets within a slot.
+  // Compute: wavefront w takes packed columns 16w .. 16w+15 of the tile (half
+  // w % 2 of area w / 2). Lane (j = lane%32, h = lane/32) of a B fragment
+  // takes packed column 16w + j%16 and field parity par = j / 16, so MFMA
+  // tile q covers fields 2q (lanes j < 16) and 2q + 1 (j >= 16) of the
+  // wavefront's 16 columns: the eight fields of 16 columns in four tiles.
   const int fi = lane & 31, fh = lane >> 5;
+  const int par = fi >> 4;
+  const int col_in_area = 16 * (wave & 1) + (fi & 15);
   // x fragments: row fi (+32) of the tile, k-step t -> logical chunk 2t + fh.
   int xoff[2][2];
 #pragma unroll
@@ -170,18 +212,27 @@ __global__ __launch_bounds__(256) void w4a16_gemm_kernel(const uint16_t* __restr
       const int row = 32 * a + fi;
       xoff[a][t] = row * 64 + 16 * ((2 * t + fh) ^ chunk_swizzle(row));
     }
-  // raw words: k-row 16t + 8fh + e of packed column fi.
-  const int wbase = kABytes + wave * kWaveBytes + 4 * fi;
+  // raw words: k-row 16t + 8fh + e of the lane's packed column.
+  const int area = kABytes + (wave >> 1) * kAreaBytes;
+  const int wbase = area + 4 * col_in_area;
+  uint32_t mask, magic;
+  asm("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+  {
+    uint32_t mlo, mhi;
+    asm("v_mov_b32 %0, 0x000f000f" : "=v"(mlo));
+    asm("v_mov_b32 %0, 0x00f000f0" : "=v"(mhi));
+    mask = par ? mhi : mlo;
+  }
 
-  f32x16 acc[2][8];
+  f32x16 acc[2][4];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int p = 0; p < 8; ++p) acc[a][p] = f32x16{};
+    for (int q = 0; q < 4; ++q) acc[a][q] = f32x16{};
 
   const int nst = K / kRows;
 
-  // Operands of one 16-row k-step: the two x fragments and the eight
+  // Operands of one 16-row k-step: the two x fragments and the four
   // dequantized weight fragments.
 #define MQ_READ_A(S, T, AF)                                                                      \
   do {                                                                                           \
@@ -197,38 +248,41 @@ __global__ __launch_bounds__(256) void w4a16_gemm_kernel(const uint16_t* __restr
 #define MQ_READ_GP(S, GP)                                                                        \
   do {                                                                                           \
     const lds_i8* const sl_ = sm + ((S) % kStages) * kSlotBytes;                                 \
-    const u32x4 sv_ = *(const lds_u32x4*)(sl_ + wbase - 4 * fi + kBBytes + 16 * fi);             \
-    const uint32_t zw_ = *(const lds_word*)(sl_ + wbase + kBBytes + kSBytes);                    \
-    make_group_params(zw_, sv_, GP);                                                             \
+    const u32x4 sv_ = *(const lds_u32x4*)(sl_ + area + kBBytes + 16 * col_in_area);              \
+    const uint32_t zw_ = *(const lds_word*)(sl_ + area + kBBytes + kSBytes + 4 * col_in_area);   \
+    make_group_params(zw_, sv_, par, GP);                                                        \
   } while (0)
 #define MQ_MFMAS(AF, B)                                                                          \
   do {                                                                                           \
-    _Pragma("unroll") for (int a = 0; a < 2; ++a) _Pragma("unroll") for (int p = 0; p < 8; ++p)  \
-        acc[a][p] = __builtin_amdgcn_mfma_f32_32x32x16_f16(AF[a], B[p], acc[a][p], 0, 0, 0);     \
+    _Pragma("unroll") for (int a = 0; a < 2; ++a) _Pragma("unroll") for (int q = 0; q < 4; ++q)  \
+        acc[a][q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(AF[a], B[q], acc[a][q], 0, 0, 0);     \
   } while (0)
 // Keeps the unpacked fragments in the block that computes them (otherwise
 // they are sunk next to their use, out of reach of the MFMAs they are meant
 // to overlap).
-#define MQ_PIN(B) _Pragma("unroll") for (int p_ = 0; p_ < 8; ++p_) asm volatile("" : "+v"(B[p_]))
-// Schedule of a block: its LDS reads first, then the 16 MFMAs each followed
+#define MQ_PIN(B) _Pragma("unroll") for (int q_ = 0; q_ < 4; ++q_) asm volatile("" : "+v"(B[q_]))
+// Schedule of a block: its LDS reads first, then the 8 MFMAs each followed
 // by a share of the unpack arithmetic.
 #define MQ_INTERLEAVE(NDS, NVALU)                                                                \
   do {                                                                                           \
     __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);                                         \
-    _Pragma("unroll") for (int i_ = 0; i_ < 16; ++i_) {                                          \
+    _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                                           \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                         \
       __builtin_amdgcn_sched_group_barrier(0x002, NVALU, 0);                                     \
     }                                                                                            \
   } while (0)
 
   // Software pipeline: the weights of the next k-step are unpacked while the
-  // current k-step's MFMAs run, in the same basic block, so the VALU and the
-  // matrix unit overlap within the single wavefront per SIMD. Stage s + 1 is
-  // waited for (and the slot of stage s refilled) in the middle of stage s.
-  // The prologue fills every slot.
+  // current k-step's MFMAs run, in the same basic block; two wavefronts per
+  // SIMD overlap one's unpack with the other's MFMAs. Stage s + 1 is waited
+  // for (and the slot of stage s refilled) in the middle of stage s. The
+  // prologue fills every slot. Only the filling wavefronts have loads to
+  // wait for; the others pass their waits at once and meet the barrier.
+  if (filler) {
 #pragma unroll
-  for (int st = 0; st < kStages; ++st)
-    if (st < nst) MQ_ISSUE(st);
+    for (int st = 0; st < kStages; ++st)
+      if (st < nst) MQ_ISSUE(st);
+  }
   if (nst >= kStages) {
     wait_counts<(kStages - 1) * kLoads, 0>();
   } else {
@@ -237,29 +291,29 @@ __global__ __launch_bounds__(256) void w4a16_gemm_kernel(const uint16_t* __restr
   bare_barrier();
 
   GroupParams gp;
-  f16x8 a0[2], b0[8];
+  f16x8 a0[2], b0[4];
   {
     uint32_t w[8];
     MQ_READ_GP(0, gp);
     MQ_READ_A(0, 0, a0);
     MQ_READ_W(0, 0, w);
-    unpack_step_scaled(w, gp.negz, gp.sc2, b0);
+    unpack_fields(w, gp, mask, magic, b0);
   }
   for (int s = 0; s < nst; ++s) {
     // k-step 1 of stage s: unpack while k-step 0's MFMAs run.
-    f16x8 a1[2], b1[8];
+    f16x8 a1[2], b1[4];
     {
       __builtin_amdgcn_sched_barrier(0);
       uint32_t w[8];
       MQ_READ_A(s, 1, a1);
       MQ_READ_W(s, 1, w);
-      unpack_step_scaled(w, gp.negz, gp.sc2, b1);
+      unpack_fields(w, gp, mask, magic, b1);
       MQ_MFMAS(a0, b0);
       MQ_PIN(b1);
-      MQ_INTERLEAVE(10, 7);
+      MQ_INTERLEAVE(10, 8);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // Stage s + 1 must have landed (every wave's share), and every wave is
+    // Stage s + 1 must have landed (every filler's share), and every wave is
     // done reading stage s, whose slot takes stage s + kStages. (After the
     // last stage this reads a slot it does not use.)
     if (s + kStages - 1 < nst) {
@@ -268,7 +322,7 @@ __global__ __launch_bounds__(256) void w4a16_gemm_kernel(const uint16_t* __restr
       wait_counts<0, 0>();
     }
     bare_barrier();
-    if (s + kStages < nst) MQ_ISSUE(s + kStages);
+    if (filler && s + kStages < nst) MQ_ISSUE(s + kStages);
     // k-step 0 of stage s + 1: unpack while k-step 1's MFMAs run.
     {
       __builtin_amdgcn_sched_barrier(0);
@@ -276,7 +330,7 @@ __global__ __launch_bounds__(256) void w4a16_gemm_kernel(const uint16_t* __restr
       MQ_READ_GP(s + 1, gp);
       MQ_READ_A(s + 1, 0, a0);
       MQ_READ_W(s + 1, 0, w);
-      unpack_step_scaled(w, gp.negz, gp.sc2, b0);
+      unpack_fields(w, gp, mask, magic, b0);
       MQ_MFMAS(a1, b1);
       MQ_PIN(b0);
       MQ_INTERLEAVE(12, 10);
@@ -291,28 +345,38 @@ __global__ __launch_bounds__(256) void w4a16_gemm_kernel(const uint16_t* __restr
 #undef MQ_PIN
 #undef MQ_ISSUE
 
-  // D[m][c] of a 32x32 tile: lane (jj, hh) register r holds token
-  // 8 (r / 4) + 4 hh + r % 4 of packed column jj; the eight field tiles give
-  // the column's 8 consecutive outputs.
-  const int jj = lane & 31, hh = lane >> 5;
-  const int c = c0 + kWaveCols * wave + jj;
-  if (c >= NP) return;
+  // Epilogue. D[m][j] of a 32x32 tile: lane (jj, hh) register r holds token
+  // 8 (r / 4) + 4 hh + r % 4 of B column jj, i.e. output 8 (16 w + jj % 16)
+  // + 2 q + jj / 16 of the tile. The tile is staged in LDS as fp16 and
+  // written out as whole rows with 16-byte stores.
+  wait_counts<0, 0>();
+  bare_barrier();  // every wave is done reading the ring
+  {
+    const int jj = lane & 31, hh = lane >> 5;
+    const int ncol = 8 * (kWaveCols * wave + (jj & 15)) + (jj >> 4);
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + 32 * a + 8 * (r / 4) + 4 * hh + (r % 4);
-      if (m >= M) continue;
-      u32x4 out;
+      for (int r = 0; r < 16; ++r) {
+        const int mt = 32 * a + 8 * (r / 4) + 4 * hh + (r % 4);
+        lds_i8* const row = sm + mt * kOutPitch;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        f16x2 pr;
-        pr[0] = static_cast<f16>(acc[a][2 * q][r]);
-        pr[1] = static_cast<f16>(acc[a][2 * q + 1][r]);
-        out[q] = as_u32(pr);
+        for (int q = 0; q < 4; ++q) {
+          const f16 v = static_cast<f16>(acc[a][q][r]);
+          *(__attribute__((address_space(3))) f16*)(row + 2 * (ncol + 2 * q)) = v;
+        }
       }
-      *reinterpret_cast<u32x4*>(y + static_cast<size_t>(m) * N + 8 * c) = out;
-    }
+  }
+  wait_counts<0, 0>();
+  bare_barrier();
+  constexpr int kPieces = kTileCols;  // 16-byte pieces (8 outputs) per row
+  for (int i = threadIdx.x; i < kBM * kPieces; i += kThreads) {
+    const int mt = i / kPieces, pc = i % kPieces;
+    const int m = m0 + mt, c = c0 + pc;
+    if (m >= M || c >= NP) continue;
+    *reinterpret_cast<u32x4*>(y + static_cast<size_t>(m) * N + 8 * c) =
+        *(const lds_u32x4*)(sm + mt * kOutPitch + 16 * pc);
+  }
 }
 
 }  // namespace
@@ -324,7 +388,7 @@ hipError_t launch_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const ui
   const int tiles_n = static_cast<int>((N / 8 + kTileCols - 1) / kTileCols);
   const int64_t tiles = static_cast<int64_t>(tiles_m) * tiles_n;
   const int per_xcd = static_cast<int>((tiles + 7) / 8);
-  return launch_kernel(w4a16_gemm_kernel, dim3(static_cast<uint32_t>(8 * per_xcd)), dim3(256), 0, stream, x,
+  return launch_kernel(w4a16_gemm_kernel, dim3(static_cast<uint32_t>(8 * per_xcd)), dim3(kThreads), 0, stream, x,
                        reinterpret_cast<const uint32_t*>(qweight), scales,
                        reinterpret_cast<const uint32_t*>(qzeros), y, static_cast<int>(M),
                        static_cast<int>(N), static_cast<int>(K), tiles_m, tiles_n, per_xcd);
