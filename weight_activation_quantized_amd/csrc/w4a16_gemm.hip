@@ -56,9 +56,10 @@ constexpr int kSBytes = 1024;                    // an area's scales (512 B used
 constexpr int kZBytes = 256;                     // an area's zero points (128 B used)
 constexpr int kAreaBytes = kBBytes + kSBytes + kZBytes;
 constexpr int kSlotBytes = kABytes + kAreas * kAreaBytes;
-constexpr int kLoads = 7;  // per filling wavefront (one per area) and stage: 1 x, 4 weights, 1 scales, 1 zeros
+constexpr int kLoadsW = 5;  // per filling wavefront (one per area) and stage: 1 x, 4 weights
+                            // (+ 1 scales and 1 zero-point load at a group's first stage)
 constexpr int kOutPitch = kTileCols * 8 * 2 + 16;  // bytes per staged output row
-static_assert(kStages >= 2 && (kStages - 2) * kLoads < 64, "ring depth / vmcnt range");
+static_assert(kStages >= 2 && (kStages - 1) * (kLoadsW + 2) < 64, "ring depth / vmcnt range");
 static_assert(kStages * kSlotBytes <= 160 * 1024, "LDS capacity");
 static_assert(kBM * kOutPitch <= kStages * kSlotBytes, "output staging fits the ring");
 
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
   const uint32_t z_off = static_cast<uint32_t>(kAreaCols * fa + lane % 32) * 4u;
   lds_i8* const fill_area = sm + kABytes + fa * kAreaBytes;  // + slot offset
 
-#define MQ_ISSUE(ST)                                                                                 \
+#define MQ_ISSUE(ST, SZ)                                                                             \
   do {                                                                                               \
     const int k0_ = (ST) * kRows;                                                                    \
     const int g_ = k0_ / kGroup;                                                                     \
@@ -189,10 +190,12 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
     _Pragma("unroll") for (int u = 0; u < 4; ++u)                                                    \
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rw_, (lds_void*)(fill_area + so_ + u * 1024), 16,   \
                                                  wr_off[u], 0, 0, 0);                                \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (lds_void*)(fill_area + so_ + kBBytes), 16, s_off, \
-                                             0, 0, 0);                                               \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rz_, (lds_void*)(fill_area + so_ + kBBytes + kSBytes), 4, \
-                                             z_off, 0, 0, 0);                                        \
+    if (SZ) {                                                                                        \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (lds_void*)(fill_area + so_ + kBBytes), 16,      \
+                                               s_off, 0, 0, 0);                                      \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rz_, (lds_void*)(fill_area + so_ + kBBytes + kSBytes), \
+                                               4, z_off, 0, 0, 0);                                   \
+    }                                                                                                \
   } while (0)
 
   // Compute: wavefront w takes packed columns 16w .. 16w+15 of the tile (half
@@ -278,13 +281,19 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
   // for (and the slot of stage s refilled) in the middle of stage s. The
   // prologue fills every slot. Only the filling wavefronts have loads to
   // wait for; the others pass their waits at once and meet the barrier.
+  // A group (128 rows) is four stages: its scales and zero points are
+  // loaded with its first stage only and turned into the lanes' factors once
+  // per group, so the stage loop runs four stages per iteration, unrolled.
+  static_assert(kStages == 6 && kGroup == 4 * kRows, "wait counts below assume 6 stages, 4 per group");
+  constexpr int kWaitPrologue = 5 * kLoadsW + 2;  // stages 1-5 may stay in flight; one starts a group
+  constexpr int kWaitLoop = 4 * kLoadsW + 2;      // stages s+2 .. s+5; exactly one starts a group
   if (filler) {
 #pragma unroll
     for (int st = 0; st < kStages; ++st)
-      if (st < nst) MQ_ISSUE(st);
+      if (st < nst) MQ_ISSUE(st, st % 4 == 0);
   }
   if (nst >= kStages) {
-    wait_counts<(kStages - 1) * kLoads, 0>();
+    wait_counts<kWaitPrologue, 0>();
   } else {
     wait_counts<0, 0>();
   }
@@ -299,42 +308,51 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
     MQ_READ_W(0, 0, w);
     unpack_fields(w, gp, mask, magic, b0);
   }
-  for (int s = 0; s < nst; ++s) {
-    // k-step 1 of stage s: unpack while k-step 0's MFMAs run.
-    f16x8 a1[2], b1[4];
-    {
-      __builtin_amdgcn_sched_barrier(0);
-      uint32_t w[8];
-      MQ_READ_A(s, 1, a1);
-      MQ_READ_W(s, 1, w);
-      unpack_fields(w, gp, mask, magic, b1);
-      MQ_MFMAS(a0, b0);
-      MQ_PIN(b1);
-      MQ_INTERLEAVE(10, 8);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // Stage s + 1 must have landed (every filler's share), and every wave is
-    // done reading stage s, whose slot takes stage s + kStages. (After the
-    // last stage this reads a slot it does not use.)
-    if (s + kStages - 1 < nst) {
-      wait_counts<(kStages - 2) * kLoads, 0>();
-    } else {
-      wait_counts<0, 0>();
-    }
-    bare_barrier();
-    if (filler && s + kStages < nst) MQ_ISSUE(s + kStages);
-    // k-step 0 of stage s + 1: unpack while k-step 1's MFMAs run.
-    {
-      __builtin_amdgcn_sched_barrier(0);
-      uint32_t w[8];
-      MQ_READ_GP(s + 1, gp);
-      MQ_READ_A(s + 1, 0, a0);
-      MQ_READ_W(s + 1, 0, w);
-      unpack_fields(w, gp, mask, magic, b0);
-      MQ_MFMAS(a1, b1);
-      MQ_PIN(b0);
-      MQ_INTERLEAVE(12, 10);
-      __builtin_amdgcn_sched_barrier(0);
+  for (int s0 = 0; s0 < nst; s0 += 4) {
+#pragma unroll
+    for (int ss = 0; ss < 4; ++ss) {
+      const int s = s0 + ss;
+      // k-step 1 of stage s: unpack while k-step 0's MFMAs run.
+      f16x8 a1[2], b1[4];
+      {
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t w[8];
+        MQ_READ_A(s, 1, a1);
+        MQ_READ_W(s, 1, w);
+        unpack_fields(w, gp, mask, magic, b1);
+        MQ_MFMAS(a0, b0);
+        MQ_PIN(b1);
+        MQ_INTERLEAVE(10, 8);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // Stage s + 1 must have landed (every filler's share), and every wave
+      // is done reading stage s, whose slot takes stage s + kStages. (After
+      // the last stage this reads a slot it does not use.)
+      if (s + kStages - 1 < nst) {
+        wait_counts<kWaitLoop, 0>();
+      } else {
+        wait_counts<0, 0>();
+      }
+      bare_barrier();
+      if (filler && s + kStages < nst) MQ_ISSUE(s + kStages, (ss + kStages) % 4 == 0);
+      // k-step 0 of stage s + 1: unpack while k-step 1's MFMAs run; a new
+      // group's factors first when stage s + 1 starts one.
+      {
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t w[8];
+        if (ss == 3) MQ_READ_GP(s + 1, gp);
+        MQ_READ_A(s + 1, 0, a0);
+        MQ_READ_W(s + 1, 0, w);
+        unpack_fields(w, gp, mask, magic, b0);
+        MQ_MFMAS(a1, b1);
+        MQ_PIN(b0);
+        if (ss == 3) {
+          MQ_INTERLEAVE(12, 10);
+        } else {
+          MQ_INTERLEAVE(10, 8);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 #undef MQ_READ_A
