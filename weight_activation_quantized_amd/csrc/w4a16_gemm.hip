@@ -46,10 +46,7 @@ constexpr int kWaves = 8;       // two per area (16 packed columns each), two pe
 constexpr int kWaveCols = 16;   // packed columns per wavefront
 constexpr int kThreads = kWaves * 64;
 constexpr int kRows = 32;       // K rows per stage (two 16-row MFMA k-steps)
-#ifndef MQ_W4_STAGES
-#define MQ_W4_STAGES 6
-#endif
-constexpr int kStages = MQ_W4_STAGES;
+constexpr int kStages = 6;      // LDS ring depth (stages)
 constexpr int kABytes = kBM * kRows * 2;         // x rows: 64 x 64 B
 constexpr int kBBytes = kRows * kAreaCols * 4;   // an area's raw words: 32 x 128 B
 constexpr int kSBytes = 1024;                    // an area's scales (512 B used)

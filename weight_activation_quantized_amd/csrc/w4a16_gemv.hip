@@ -118,10 +118,7 @@ constexpr int kLRows = 32;                      // rows per stage (one MFMA k-st
 constexpr int kLStageWords = kLRows * kLStrip;  // 2048 words = 8 KB
 constexpr int kLXWords = 16 * kLRows / 2;       // 256 words = 1 KB
 constexpr int kLMaxGroups = 8;                  // groups per split held in LDS
-#ifndef MQ_GEMV_LDS_STAGES
-#define MQ_GEMV_LDS_STAGES 3
-#endif
-constexpr int kLStages = MQ_GEMV_LDS_STAGES;
+constexpr int kLStages = 3;  // ring depth (4, 6 and 8 stages measured slower)
 // Per lane and stage: 2 x 16 B of weights + 4 B of x per 16-token tile.
 template <int T>
 constexpr int lds_loads_per_stage() { return 2 + T; }
@@ -499,18 +496,12 @@ __global__ __launch_bounds__(256) void w4a16_gemv_reduce(const float* __restrict
 
 }  // namespace
 
-#ifndef MQ_GEMV_NWC
-#define MQ_GEMV_NWC 4
-#endif
-#ifndef MQ_GEMV_TARGET_WGS
-#define MQ_GEMV_TARGET_WGS 384
-#endif
+constexpr int kGemvWaves = 4;         // register-staged kernel: wavefronts per workgroup
+constexpr int64_t kTargetWgs = 384;   // 1.5 workgroups per CU (192: slower; 768: no faster)
 
 GemvPlan plan_w4a16_gemv(int64_t M, int64_t N, int64_t K) {
-  GemvPlan plan{1, MQ_GEMV_NWC, 0, false};
-#ifndef MQ_GEMV_NO_LDS
+  GemvPlan plan{1, kGemvWaves, 0, false};
   plan.lds = (N / 8) % 4 == 0;
-#endif
   const int64_t strip_cols = plan.lds ? int64_t{kLStrip} : int64_t{kWaveCols} * plan.waves;
   const int64_t strips = (N / 8 + strip_cols - 1) / strip_cols;
   const int64_t G = K / kGroup;
@@ -518,16 +509,10 @@ GemvPlan plan_w4a16_gemv(int64_t M, int64_t N, int64_t K) {
   // smallest divisor of the group count that gets there (and, for the LDS
   // kernel, that leaves at most kLMaxGroups groups per split).
   int64_t splits = 1;
-#ifdef MQ_GEMV_FORCE_SPLITS
-  splits = MQ_GEMV_FORCE_SPLITS;
-  if (splits > G) splits = G;
-  while (G % splits) --splits;
-#else
-  while (strips * splits < MQ_GEMV_TARGET_WGS && splits < G) {
+  while (strips * splits < kTargetWgs && splits < G) {
     ++splits;
     while (G % splits) ++splits;
   }
-#endif
   if (plan.lds) {
     while (G / splits > kLMaxGroups) {
       ++splits;
