@@ -4,8 +4,9 @@
 // (per-token int8 activation quantizer in front of the int8 scaled matmul).
 // For every row m: s[m] = fl32(absmax(x[m,:]) / 127) and
 // q[m,k] = clamp(rne(fl32(x[m,k] / s[m])), -127, 127); all-zero rows give
-// s = 0, q = 0. The quotient is an IEEE binary32 division (no reciprocal
-// shortcut) and rintf rounds half to even, so the codes are bit-exact.
+// s = 0, q = 0. The codes are those of the IEEE binary32 quotient rounded
+// half to even, bit for bit: a reciprocal product decides every element that
+// is not close to a half-integer, the IEEE division the rest.
 //
 // One wavefront per row, four rows per workgroup. Each lane holds its share
 // of the row in registers (16-byte chunks of 8 fp16), so x is read from HBM
@@ -30,28 +31,47 @@ __device__ __forceinline__ float chunk_absmax(u32x4 v, float m) {
   return m;
 }
 
-__device__ __forceinline__ uint32_t quant4(f16x2 a, f16x2 b, float s) {
-  // s > 0 here; IEEE division then round-half-even.
-  float q0 = rintf(static_cast<float>(a[0]) / s);
-  float q1 = rintf(static_cast<float>(a[1]) / s);
-  float q2 = rintf(static_cast<float>(b[0]) / s);
-  float q3 = rintf(static_cast<float>(b[1]) / s);
+// Distance from a half-integer below which an element takes the IEEE
+// division (see code_of).
+constexpr float kTieMargin = 1.0f / 4096.0f;
+
+// rne(fl32(v / s)) for s > 0, |v| <= 127.5 s. The product p = v * r with
+// r = rcp(s) (within 1 ulp of 1/s) differs from the exact quotient by at
+// most 2^-22 relative, i.e. < 3.1e-5 for quotients up to 127.5, and the
+// correctly rounded quotient is within half an ulp (< 3.9e-6) of it. So when
+// p is more than kTieMargin away from every half-integer, the rounded
+// quotient lies on the same side of the nearest half-integer as p and rounds
+// to the same integer; only elements within the margin (about 1 in 2000)
+// take the IEEE division, whose correctly rounded result decides ties.
+__device__ __forceinline__ float code_of(float v, float s, float r) {
+  const float p = v * r;
+  const float t = rintf(p);
+  if (0.5f - fabsf(p - t) < kTieMargin) return rintf(v / s);
+  return t;
+}
+
+__device__ __forceinline__ uint32_t quant4(f16x2 a, f16x2 b, float s, float r) {
+  // s > 0 here: the codes of the IEEE quotient, rounded half to even.
+  float q0 = code_of(static_cast<float>(a[0]), s, r);
+  float q1 = code_of(static_cast<float>(a[1]), s, r);
+  float q2 = code_of(static_cast<float>(b[0]), s, r);
+  float q3 = code_of(static_cast<float>(b[1]), s, r);
   q0 = fminf(fmaxf(q0, -127.f), 127.f);
   q1 = fminf(fmaxf(q1, -127.f), 127.f);
   q2 = fminf(fmaxf(q2, -127.f), 127.f);
   q3 = fminf(fmaxf(q3, -127.f), 127.f);
-  uint32_t r = static_cast<uint32_t>(static_cast<int32_t>(q0)) & 0xFFu;
-  r |= (static_cast<uint32_t>(static_cast<int32_t>(q1)) & 0xFFu) << 8;
-  r |= (static_cast<uint32_t>(static_cast<int32_t>(q2)) & 0xFFu) << 16;
-  r |= (static_cast<uint32_t>(static_cast<int32_t>(q3)) & 0xFFu) << 24;
-  return r;
+  uint32_t packed = static_cast<uint32_t>(static_cast<int32_t>(q0)) & 0xFFu;
+  packed |= (static_cast<uint32_t>(static_cast<int32_t>(q1)) & 0xFFu) << 8;
+  packed |= (static_cast<uint32_t>(static_cast<int32_t>(q2)) & 0xFFu) << 16;
+  packed |= (static_cast<uint32_t>(static_cast<int32_t>(q3)) & 0xFFu) << 24;
+  return packed;
 }
 
-__device__ __forceinline__ u32x2 quant_chunk(u32x4 v, float s) {
+__device__ __forceinline__ u32x2 quant_chunk(u32x4 v, float s, float r) {
   u32x2 out;
   if (s > 0.f) {
-    out[0] = quant4(as_f16x2(v[0]), as_f16x2(v[1]), s);
-    out[1] = quant4(as_f16x2(v[2]), as_f16x2(v[3]), s);
+    out[0] = quant4(as_f16x2(v[0]), as_f16x2(v[1]), s, r);
+    out[1] = quant4(as_f16x2(v[2]), as_f16x2(v[3]), s, r);
   } else {
     out[0] = 0u;
     out[1] = 0u;
@@ -85,11 +105,12 @@ __global__ __launch_bounds__(256) void quant_rows_regs(const uint16_t* __restric
   }
   amax = wave_max(amax);
   const float s = amax / 127.0f;
+  const float r = __builtin_amdgcn_rcpf(s);
   if (lane == 0) s_tok[row] = s;
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
     const int c = lane + kWave * i;
-    if (c < nchunk) *reinterpret_cast<u32x2*>(qr + 8 * c) = quant_chunk(v[i], s);
+    if (c < nchunk) *reinterpret_cast<u32x2*>(qr + 8 * c) = quant_chunk(v[i], s, r);
   }
 }
 
@@ -108,9 +129,10 @@ __global__ __launch_bounds__(256) void quant_rows_stream(const uint16_t* __restr
     amax = chunk_absmax(*reinterpret_cast<const u32x4*>(xr + 8 * c), amax);
   amax = wave_max(amax);
   const float s = amax / 127.0f;
+  const float r = __builtin_amdgcn_rcpf(s);
   if (lane == 0) s_tok[row] = s;
   for (int c = lane; c < nchunk; c += kWave)
-    *reinterpret_cast<u32x2*>(qr + 8 * c) = quant_chunk(*reinterpret_cast<const u32x4*>(xr + 8 * c), s);
+    *reinterpret_cast<u32x2*>(qr + 8 * c) = quant_chunk(*reinterpret_cast<const u32x4*>(xr + 8 * c), s, r);
 }
 
 }  // namespace
