@@ -10,8 +10,9 @@
  *              Source: LMDeploy toolkit overview, section 2.5 "Weight
  *              quantization (AWQ)" (4-bit weights, groups of 128); LMDeploy
  *              4-bit deployment guide, section 2.2 (scale and weight are
- *              consumed inside one kernel); pymllm Setup and Usage, Overview
- *              (the W4A16 scheme).
+ *              consumed inside one kernel) and section 3.2 (per-layer group
+ *              size, 64 for the vision tower's attention); pymllm Setup and
+ *              Usage, Overview (the W4A16 scheme).
  *
  *   W8A8_INT8  dynamic per-token symmetric int8 activation quantization,
  *              then an int8 GEMM with int32 accumulation and a per-token x
@@ -61,7 +62,7 @@ typedef enum mq_status {
   MQ_ERR_NULL = 1,        /* a required pointer is NULL */
   MQ_ERR_SHAPE = 2,       /* a size is negative, too large or breaks a divisibility rule */
   MQ_ERR_ALIGN = 3,       /* a pointer is not aligned as documented */
-  MQ_ERR_UNSUPPORTED = 4, /* valid in principle but not provided (e.g. group != 128, GEMV M > 64) */
+  MQ_ERR_UNSUPPORTED = 4, /* valid in principle but not provided (e.g. group not in {32, 64, 128}, GEMV M > 64) */
   MQ_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
   MQ_ERR_ALIAS = 6,       /* an output overlaps an input or another output */
   MQ_ERR_HIP = 7          /* the HIP runtime refused the launch (message in mq_last_error) */
@@ -132,7 +133,9 @@ mq_status mq_w8a8_mm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc,
  * W4A16 GEMM (prefill-shaped M).
  * Source: LMDeploy toolkit overview, section 2.5 (4-bit AWQ weights, group
  * size 128); LMDeploy 4-bit deployment guide, section 2.2 (dequantization
- * fused into the matmul kernel).
+ * fused into the matmul kernel) and section 3.2 (group size per layer: 64
+ * for the vision tower's attention projection, 128 for the language model).
+ * G = group: the number of consecutive k sharing one scale and zero point.
  *     q[k,n]  = field (n % 8) of qweight[k, n/8]     (field j = bits 4j..4j+3)
  *     z[g,n]  = field (n % 8) of qzeros[g, n/8]
  *     w[k,n]  = (q[k,n] - z[k/G,n]) * scales[k/G,n]
@@ -146,9 +149,10 @@ mq_status mq_w8a8_mm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc,
  *   scales   [K/G, N]   fp16   in
  *   qzeros   [K/G, N/8] int32  in   (unsigned 4-bit zero points, packed like qweight)
  *   y        [M, N]     fp16   out
- * Requires: group == 128; 0 <= M < 2^31; 8 <= N <= 2^27, N % 8 == 0;
- * 128 <= K <= 2^20, K % 128 == 0; x, scales, y 16-byte aligned; qweight,
- * qzeros 4-byte aligned.
+ * Requires: group in {32, 64, 128} (anything else, -1 included ->
+ * MQ_ERR_UNSUPPORTED); 0 <= M < 2^31; 8 <= N <= 2^27, N % 8 == 0;
+ * 128 <= K <= 2^20, K % 128 == 0 (so K % group == 0); x, scales, y 16-byte
+ * aligned; qweight, qzeros 4-byte aligned.
  */
 mq_status mq_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                         const int32_t* qzeros, uint16_t* y,
@@ -164,7 +168,7 @@ size_t mq_w4a16_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t gr
 /*
  * W4A16 GEMV for decode (1 <= M <= 64). Same definition, operands and
  * layouts as mq_w4a16_gemm, except that the weights are not rounded to
- * fp16: per group of 128 rows the kernel forms, in fp32, the sum of
+ * fp16: per group of G rows the kernel forms, in fp32, the sum of
  * x * (q - z) and scales it by s in fp32. (For N % 32 == 0 the sum is
  * taken as sum(x * (1024 + q)) - (1024 + z) * sum(x), with exact fp16
  * products; otherwise (q - z) is formed exactly first.) Outputs meet the

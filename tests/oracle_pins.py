@@ -175,7 +175,7 @@ def _tiny_w4_case(seed, M=3, K=256, N=16, G=128):
 
 def check_w4a16_bruteforce(w4a16):
     for seed, (M, K, N, G) in enumerate([(3, 256, 16, 128), (2, 384, 24, 128), (1, 128, 8, 128),
-                                        (2, 64, 16, 32)]):
+                                        (2, 64, 16, 32), (2, 256, 16, 64)]):
         x, q, z, s = _tiny_w4_case(seed, M, K, N, G)
         qweight, qzeros = loop_pack(q), loop_pack(z)
         y = w4a16(x, qweight, s, qzeros, G)

@@ -118,8 +118,13 @@ def test_w8a8_validation(lib):
 def test_w4a16_gemm_validation(lib):
     g = lib.mq_w4a16_gemm
     assert g(A, B, C, D, None, 4, 64, 256, 128, None) == NULL
-    assert g(A, B, C, D, E, 4, 64, 256, 64, None) == UNSUP      # group 64 not provided
-    assert g(A, B, C, D, E, 4, 64, 256, -1, None) == UNSUP
+    # groups of 32, 64 and 128 rows are provided; others (and -1, one group
+    # over all of K) are not
+    for group in (96, 256, 16, 0, -1):
+        assert g(A, B, C, D, E, 4, 64, 256, group, None) == UNSUP, group
+    assert g(A, B, C, D, E, 4, 64, 192, 64, None) == SHAPE      # K % 128, also for smaller groups
+    for group in (32, 64, 128):
+        assert g(A, B, C, D, E, 0, 64, 256, group, None) == OK
     assert g(A, B, C, D, E, 4, 60, 256, 128, None) == SHAPE     # N % 8
     assert g(A, B, C, D, E, 4, (1 << 27) + 8, 256, 128, None) == SHAPE
     assert g(A, B, C, D, E, 4, 64, 200, 128, None) == SHAPE     # K % 128
@@ -151,19 +156,22 @@ def test_gemv_workspace_plan(lib):
     # rejected problems need nothing
     assert ws(0, 512, 512, 128) == 0
     assert ws(65, 512, 512, 128) == 0
-    assert ws(4, 512, 512, 64) == 0
+    assert ws(4, 512, 512, 96) == 0
+    assert ws(4, 512, 512, -1) == 0
     # the workspace holds splits * M * N fp32 partial sums, with splits a
-    # divisor of K/128; the LDS-staged kernel (N % 32 == 0) keeps at most 16
-    # groups per split
-    for M, N, K in [(1, 24576, 4096), (4, 24576, 4096), (16, 24576, 4096), (1, 6144, 4096),
-                    (8, 4096, 4096), (1, 4096, 12288), (4, 512, 512), (3, 424, 384),
-                    (64, 24576, 4096), (64, 4096, 12288), (33, 6144, 4096), (40, 424, 384)]:
-        b = ws(M, N, K, 128)
-        assert b % (4 * M * N) == 0
-        splits = b // (4 * M * N) or 1
-        assert (K // 128) % splits == 0
-        if N % 32 == 0:
-            assert (K // 128) // splits <= 16
+    # divisor of the group count K/G; the LDS-staged kernel (N % 32 == 0)
+    # keeps at most 1024 rows per split
+    for group in (32, 64, 128):
+        for M, N, K in [(1, 24576, 4096), (4, 24576, 4096), (16, 24576, 4096), (1, 6144, 4096),
+                        (8, 4096, 4096), (1, 4096, 12288), (4, 512, 512), (3, 424, 384),
+                        (64, 24576, 4096), (64, 4096, 12288), (33, 6144, 4096), (40, 424, 384),
+                        (1, 3072, 1024), (16, 3072, 1024)]:
+            b = ws(M, N, K, group)
+            assert b % (4 * M * N) == 0
+            splits = b // (4 * M * N) or 1
+            assert (K // group) % splits == 0
+            if N % 32 == 0:
+                assert K // splits <= 1024
 
 
 @pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="lets a launch through; only meaningful without a GPU")

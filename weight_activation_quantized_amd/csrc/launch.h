@@ -26,10 +26,11 @@ hipError_t launch_w8a8_gemv(const int8_t* xq, const float* s_tok, const int8_t* 
                             const float* s_ch, uint16_t* y, int32_t* acc,
                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
-// W4A16 GEMM y[M,N] = x[M,K] . dequant(qweight, scales, qzeros) with group 128.
+// W4A16 GEMM y[M,N] = x[M,K] . dequant(qweight, scales, qzeros), groups of
+// `group` rows (32, 64 or 128; K % 128 == 0).
 hipError_t launch_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                              const int32_t* qzeros, uint16_t* y,
-                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                             int64_t M, int64_t N, int64_t K, int64_t group, hipStream_t stream);
 
 // Largest token count the W4A16 GEMV takes (four 16-token MFMA tiles).
 constexpr int64_t kGemvMaxM = 64;
@@ -41,8 +42,9 @@ struct GemvPlan {
   int waves;  // wavefronts per workgroup (register-staged kernel)
   size_t workspace_bytes;
   bool lds;   // LDS-staged kernel (N % 32 == 0)
+  int group;  // rows per group: 32, 64 or 128
 };
-GemvPlan plan_w4a16_gemv(int64_t M, int64_t N, int64_t K);
+GemvPlan plan_w4a16_gemv(int64_t M, int64_t N, int64_t K, int64_t group);
 
 hipError_t launch_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                              const int32_t* qzeros, uint16_t* y,

@@ -91,8 +91,8 @@ mq_status check_mk(int64_t M, int64_t K, int64_t k_min, int64_t k_max, int64_t k
 
 mq_status check_w4a16(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                       const int32_t* qzeros, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t group) {
-  if (group != 128)
-    return fail(MQ_ERR_UNSUPPORTED, "group=%lld (only 128 is provided)", (long long)group);
+  if (group != 32 && group != 64 && group != 128)
+    return fail(MQ_ERR_UNSUPPORTED, "group=%lld (32, 64 and 128 are provided)", (long long)group);
   MQ_TRY(check_mk(M, K, 128, kMaxK, 128));
   if (N < 8 || N > kMaxN4 || N % 8)
     return fail(MQ_ERR_SHAPE, "N=%lld must be a multiple of 8 in [8, 2^27]", (long long)N);
@@ -209,14 +209,15 @@ mq_status mq_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_
   mq_status s = check_w4a16(x, qweight, scales, qzeros, y, M, N, K, group);
   if (s != MQ_OK) return s;
   if (M == 0) return ok();
-  return hip_status(mq::launch_w4a16_gemm(x, qweight, scales, qzeros, y, M, N, K, as_stream(stream)),
+  return hip_status(mq::launch_w4a16_gemm(x, qweight, scales, qzeros, y, M, N, K, group, as_stream(stream)),
                     "w4a16_gemm launch");
 }
 
 size_t mq_w4a16_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group) {
-  if (group != 128 || M < 1 || M > mq::kGemvMaxM || N < 8 || N % 8 || N > kMaxN4 || K < 128 || K > kMaxK || K % 128)
+  if ((group != 32 && group != 64 && group != 128) || M < 1 || M > mq::kGemvMaxM || N < 8 || N % 8 ||
+      N > kMaxN4 || K < 128 || K > kMaxK || K % 128)
     return 0;
-  return mq::plan_w4a16_gemv(M, N, K).workspace_bytes;
+  return mq::plan_w4a16_gemv(M, N, K, group).workspace_bytes;
 }
 
 mq_status mq_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
@@ -229,7 +230,7 @@ mq_status mq_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const uint16_
     return fail(MQ_ERR_UNSUPPORTED, "GEMV needs M <= %lld (got %lld); use mq_w4a16_gemm",
                 (long long)mq::kGemvMaxM, (long long)M);
   if (M == 0) return ok();
-  const mq::GemvPlan plan = mq::plan_w4a16_gemv(M, N, K);
+  const mq::GemvPlan plan = mq::plan_w4a16_gemv(M, N, K, group);
   if (plan.workspace_bytes > 0) {
     if (!workspace || workspace_bytes < plan.workspace_bytes)
       return fail(MQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.workspace_bytes,

@@ -1,9 +1,10 @@
 // 4-bit weight unpacking into MFMA B-operand fragments (gfx950).
 //
 // Weight layout (LMDeploy toolkit overview, section 2.5: 4-bit weights in
-// groups of 128 input channels; the pages give no bit layout, so field j of
-// word c, least significant first, is column 8c+j): qweight[K, N/8] int32,
-// scales[K/128, N] fp16, qzeros[K/128, N/8] int32 packed like qweight.
+// groups of G = 128 input channels; LMDeploy 4-bit deployment guide, section
+// 3.2: G = 64 for the vision tower; the pages give no bit layout, so field j
+// of word c, least significant first, is column 8c+j): qweight[K, N/8]
+// int32, scales[K/G, N] fp16, qzeros[K/G, N/8] int32 packed like qweight.
 //
 // The packing runs along N while an MFMA B fragment wants 8 consecutive k of
 // one column in one lane. A lane therefore loads one word from each of 8
@@ -20,8 +21,6 @@
 #include "device_common.h"
 
 namespace mq {
-
-constexpr int kGroup = 128;
 
 // The two field masks and the 1024.0 pattern, held in VGPRs: gfx9 VOP3
 // encodings take no literal constants, so with literal masks the compiler

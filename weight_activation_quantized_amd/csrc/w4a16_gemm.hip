@@ -3,7 +3,10 @@
 // Source: LMDeploy toolkit overview, section 2.5 (AWQ 4-bit weights, group
 // size 128) and LMDeploy 4-bit deployment guide, sections 2.2-2.3 (scales
 // and weights consumed inside the matmul kernel; a real low-bit kernel rather
-// than fake quantization). y[m,n] = sum_k x[m,k] * fp16((q - z) * s).
+// than fake quantization) and section 3.2 (group size 64 for the vision
+// tower's attention). y[m,n] = sum_k x[m,k] * fp16((q - z) * s) with one
+// (s, z) per group of G = 32, 64 or 128 consecutive k; the kernel is
+// instantiated per group size.
 //
 // Design:
 // - v_mfma_f32_32x32x16_f16 (on gfx950 about 1.5x the rate of the 16x16x32
@@ -123,6 +126,8 @@ __device__ __forceinline__ void unpack_fields(const uint32_t (&w)[8], const Grou
   }
 }
 
+// kSPG = 32-row stages per group (group size 32 kSPG).
+template <int kSPG>
 __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __restrict__ x,
                                                          const uint32_t* __restrict__ qw,
                                                          const uint16_t* __restrict__ scales,
@@ -138,8 +143,10 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
   if (t_id >= tiles_m * tiles_n) return;
   const int m0 = (t_id % tiles_m) * kBM;
   const int c0 = (t_id / tiles_m) * kTileCols;  // first packed column
+  constexpr int kGS = kSPG * kRows;  // rows per group
+  static_assert(4 % kSPG == 0, "a group is 1, 2 or 4 stages");
   const int NP = N >> 3;
-  const int G = K / kGroup;
+  const int G = K / kGS;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -174,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
 #define MQ_ISSUE(ST, SZ)                                                                             \
   do {                                                                                               \
     const int k0_ = (ST) * kRows;                                                                    \
-    const int g_ = k0_ / kGroup;                                                                     \
+    const int g_ = k0_ / kGS;                                                                        \
     const int so_ = ((ST) % kStages) * kSlotBytes;                                                   \
     const __amdgpu_buffer_rsrc_t rw_ =                                                               \
         rsrc(qw + static_cast<size_t>(k0_) * NP + c0, (static_cast<int64_t>(K - k0_) * NP - c0) * 4); \
@@ -278,16 +285,23 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
   // for (and the slot of stage s refilled) in the middle of stage s. The
   // prologue fills every slot. Only the filling wavefronts have loads to
   // wait for; the others pass their waits at once and meet the barrier.
-  // A group (128 rows) is four stages: its scales and zero points are
-  // loaded with its first stage only and turned into the lanes' factors once
-  // per group, so the stage loop runs four stages per iteration, unrolled.
-  static_assert(kStages == 6 && kGroup == 4 * kRows, "wait counts below assume 6 stages, 4 per group");
-  constexpr int kWaitPrologue = 5 * kLoadsW + 2;  // stages 1-5 may stay in flight; one starts a group
-  constexpr int kWaitLoop = 4 * kLoadsW + 2;      // stages s+2 .. s+5; exactly one starts a group
+  // A group is kSPG stages: its scales and zero points are loaded with its
+  // first stage only and turned into the lanes' factors once per group. The
+  // stage loop runs four stages per iteration, unrolled, so which stages
+  // start a group is known at compile time (K % 128 == 0).
+  // Wait counts: a stage carries kLoadsW loads, plus 2 when it starts a
+  // group. Stages 1-5 may stay in flight after the prologue; stages s+2 ..
+  // s+5 in the loop, four consecutive stages of which exactly 4 / kSPG start
+  // a group.
+  static_assert(kStages == 6, "wait counts below assume 6 stages");
+  constexpr int kStartsIn1to5 = kSPG == 1 ? 5 : (kSPG == 2 ? 2 : 1);
+  constexpr int kWaitPrologue = 5 * kLoadsW + 2 * kStartsIn1to5;
+  constexpr int kWaitLoop = 4 * kLoadsW + 2 * (4 / kSPG);
+  static_assert(kWaitPrologue < 64 && kWaitLoop < 64, "vmcnt range");
   if (filler) {
 #pragma unroll
     for (int st = 0; st < kStages; ++st)
-      if (st < nst) MQ_ISSUE(st, st % 4 == 0);
+      if (st < nst) MQ_ISSUE(st, st % kSPG == 0);
   }
   if (nst >= kStages) {
     wait_counts<kWaitPrologue, 0>();
@@ -331,19 +345,20 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
         wait_counts<0, 0>();
       }
       bare_barrier();
-      if (filler && s + kStages < nst) MQ_ISSUE(s + kStages, (ss + kStages) % 4 == 0);
+      if (filler && s + kStages < nst) MQ_ISSUE(s + kStages, (ss + kStages) % kSPG == 0);
       // k-step 0 of stage s + 1: unpack while k-step 1's MFMAs run; a new
       // group's factors first when stage s + 1 starts one.
       {
         __builtin_amdgcn_sched_barrier(0);
         uint32_t w[8];
-        if (ss == 3) MQ_READ_GP(s + 1, gp);
+        const bool new_group = ss % kSPG == kSPG - 1;  // stage s + 1 starts a group (folded when unrolled)
+        if (new_group) MQ_READ_GP(s + 1, gp);
         MQ_READ_A(s + 1, 0, a0);
         MQ_READ_W(s + 1, 0, w);
         unpack_fields(w, gp, mask, magic, b0);
         MQ_MFMAS(a1, b1);
         MQ_PIN(b0);
-        if (ss == 3) {
+        if (new_group) {
           MQ_INTERLEAVE(12, 10);
         } else {
           MQ_INTERLEAVE(10, 8);
@@ -398,15 +413,27 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
 
 hipError_t launch_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                              const int32_t* qzeros, uint16_t* y,
-                             int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                             int64_t M, int64_t N, int64_t K, int64_t group, hipStream_t stream) {
+  if (K % 128 || (group != 32 && group != 64 && group != 128)) return hipErrorInvalidValue;
   const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
   const int tiles_n = static_cast<int>((N / 8 + kTileCols - 1) / kTileCols);
   const int64_t tiles = static_cast<int64_t>(tiles_m) * tiles_n;
   const int per_xcd = static_cast<int>((tiles + 7) / 8);
-  return launch_kernel(w4a16_gemm_kernel, dim3(static_cast<uint32_t>(8 * per_xcd)), dim3(kThreads), 0, stream, x,
-                       reinterpret_cast<const uint32_t*>(qweight), scales,
-                       reinterpret_cast<const uint32_t*>(qzeros), y, static_cast<int>(M),
-                       static_cast<int>(N), static_cast<int>(K), tiles_m, tiles_n, per_xcd);
+  const dim3 grid(static_cast<uint32_t>(8 * per_xcd));
+  const uint32_t* qw = reinterpret_cast<const uint32_t*>(qweight);
+  const uint32_t* qz = reinterpret_cast<const uint32_t*>(qzeros);
+  const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+  switch (group) {
+    case 32:
+      return launch_kernel(w4a16_gemm_kernel<1>, grid, dim3(kThreads), 0, stream, x, qw, scales, qz, y, m, n, k,
+                           tiles_m, tiles_n, per_xcd);
+    case 64:
+      return launch_kernel(w4a16_gemm_kernel<2>, grid, dim3(kThreads), 0, stream, x, qw, scales, qz, y, m, n, k,
+                           tiles_m, tiles_n, per_xcd);
+    default:
+      return launch_kernel(w4a16_gemm_kernel<4>, grid, dim3(kThreads), 0, stream, x, qw, scales, qz, y, m, n, k,
+                           tiles_m, tiles_n, per_xcd);
+  }
 }
 
 }  // namespace mq

@@ -1,9 +1,12 @@
-// W4A16 GEMV for decode (M <= 16) on gfx950.
+// W4A16 GEMV for decode (M <= 64) on gfx950.
 //
 // Source: LMDeploy toolkit overview, section 2.5 (AWQ 4-bit weights, group
 // size 128, 4-bit inference speedup from the smaller weight stream) and
 // LMDeploy 4-bit deployment guide, section 2.2 (scale and weight consumed in
-// one kernel). y[m,n] = sum_k x[m,k] * (q[k,n] - z[k/128,n]) * s[k/128,n].
+// one kernel) and section 3.2 (per-layer group size: 64 for the vision
+// tower's attention, 128 for the language model).
+// y[m,n] = sum_k x[m,k] * (q[k,n] - z[k/G,n]) * s[k/G,n], G in {32, 64, 128};
+// every kernel is instantiated per group size.
 //
 // Decode reads every weight once and does little arithmetic per weight, so
 // the kernel is bound by the HBM weight stream. Common to both kernels:
@@ -44,7 +47,6 @@ namespace mq {
 namespace {
 
 constexpr int kWaveCols = 16;        // packed columns per wavefront (128 outputs)
-constexpr int kSteps = kGroup / 32;  // 32-row MFMA steps per group
 constexpr int kXcds = 8;             // workgroups are dispatched round-robin over 8 XCDs
 
 __device__ __forceinline__ void store_f16x8(uint16_t* dst, const float (&v)[8]) {
@@ -117,7 +119,7 @@ constexpr int kLStrip = 64;                     // packed columns per workgroup
 constexpr int kLRows = 32;                      // rows per stage (one MFMA k-step)
 constexpr int kLStageWords = kLRows * kLStrip;  // 2048 words = 8 KB
 constexpr int kLXWords = 16 * kLRows / 2;       // 256 words = 1 KB
-constexpr int kLMaxGroups = 8;                  // groups per split held in LDS
+constexpr int kLMaxRows = 1024;                 // rows per split (their scales and zero points sit in LDS)
 constexpr int kLStages = 3;  // ring depth (4, 6 and 8 stages measured slower)
 // Per lane and stage: 2 x 16 B of weights + 4 B of x per 16-token tile.
 template <int T>
@@ -158,13 +160,13 @@ __device__ __forceinline__ uint32_t lds_weight_offset(int l, int wave, int lane,
 
 // Start the DMA of stage st (32 rows of the strip + the matching x slice of
 // each 16-token tile) into its ring slot: 2 x 16 B of weights and 4 B of x
-// per tile and lane.
+// per tile and lane. row_begin is the split's first row.
 template <int T>
-__device__ __forceinline__ void lds_issue_stage(int st, int g_begin, int NP, int wave, const char* qwb,
+__device__ __forceinline__ void lds_issue_stage(int st, int row_begin, int NP, int wave, const char* qwb,
                                                 const char* xb, uint32_t woff0, uint32_t woff1,
                                                 const uint32_t (&xoff)[T], lds_u32* s_w, lds_u32* s_x) {
   const int slot = st % kLStages;
-  const int k0 = g_begin * kGroup + st * kLRows;
+  const int k0 = row_begin + st * kLRows;
   const char* wbase = qwb + static_cast<size_t>(k0) * NP * 4;
   lds_u32* wdst = s_w + slot * kLStageWords + wave * 256;
   __builtin_amdgcn_global_load_lds(wbase + woff0, wdst, 16, 0, 0);
@@ -177,18 +179,22 @@ __device__ __forceinline__ void lds_issue_stage(int st, int g_begin, int NP, int
 }
 
 // kT = number of 16-token tiles (M <= 16 kT); every weight fragment, once
-// unpacked, feeds the MFMAs of all kT tiles.
-template <int kT>
+// unpacked, feeds the MFMAs of all kT tiles. kGS = group size (a multiple
+// of the 32-row step).
+template <int kT, int kGS>
 __global__ __launch_bounds__(256) void w4a16_gemv_lds_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qz,
     uint16_t* __restrict__ y, float* __restrict__ partial, int M, int N, int K, int strips, int splits,
     XcdMap map) {
   constexpr int kLLoadsPerStage = lds_loads_per_stage<kT>();
+  constexpr int kSPG = kGS / kLRows;             // 32-row steps per group
+  constexpr int kMaxGroups = kLMaxRows / kGS;    // groups per split held in LDS
+  static_assert(kGS % kLRows == 0 && kLMaxRows % kGS == 0, "group size");
   __shared__ __attribute__((aligned(16))) uint32_t s_w[kLStages * kLStageWords];
   __shared__ __attribute__((aligned(16))) uint32_t s_x[kLStages * kT * kLXWords];
-  __shared__ __attribute__((aligned(16))) uint32_t s_sc[kLMaxGroups * 256];
-  __shared__ __attribute__((aligned(16))) uint32_t s_z[kLMaxGroups * 64];
+  __shared__ __attribute__((aligned(16))) uint32_t s_sc[kMaxGroups * 256];
+  __shared__ __attribute__((aligned(16))) uint32_t s_z[kMaxGroups * 64];
 
   int strip, split;
   if (!decode_work(blockIdx.x, map.strips_per_xcd, strips, splits, strip, split)) return;
@@ -198,11 +204,12 @@ __global__ __launch_bounds__(256) void w4a16_gemv_lds_kernel(
   const int h = lane >> 4;
   const int NP = N >> 3;
   const int NC = NP >> 2;  // 16-byte chunks per row
-  const int G = K / kGroup;
+  const int G = K / kGS;
   const int g_begin = static_cast<int>(static_cast<int64_t>(split) * G / splits);
   const int g_end = static_cast<int>(static_cast<int64_t>(split + 1) * G / splits);
-  const int Gs = g_end - g_begin;  // <= kLMaxGroups (plan)
-  const int T = Gs * (kGroup / kLRows);
+  const int Gs = g_end - g_begin;  // <= kMaxGroups (plan)
+  const int T = Gs * kSPG;
+  const int row_begin = g_begin * kGS;
   const int chunk0 = strip * (kLStrip / 4);
   const int valid_chunks = min(kLStrip / 4, NC - chunk0);  // >= 1
   const int valid_cols = valid_chunks * 4;
@@ -240,7 +247,7 @@ __global__ __launch_bounds__(256) void w4a16_gemv_lds_kernel(
   }
   const int pre = min(kLStages - 1, T);
   for (int st = 0; st < pre; ++st)
-    lds_issue_stage(st, g_begin, NP, wave, qwb, xb, woff0, woff1, xoff, s_w_lds, s_x_lds);
+    lds_issue_stage(st, row_begin, NP, wave, qwb, xb, woff0, woff1, xoff, s_w_lds, s_x_lds);
 
   // Fragment read offsets (words within a stage).
   const int wchunk = (4 * wave + (j >> 2)) ^ (h << 2);
@@ -265,8 +272,8 @@ __global__ __launch_bounds__(256) void w4a16_gemv_lds_kernel(
     f32x4 acc[kT][8];
     f32x4 accx[kT];  // per-token sum of x over the group's rows
 #pragma unroll
-    for (int ks = 0; ks < kGroup / kLRows; ++ks) {
-      const int it = gi * (kGroup / kLRows) + ks;
+    for (int ks = 0; ks < kSPG; ++ks) {
+      const int it = gi * kSPG + ks;
       if (it + kLStages - 2 < T) {
         wait_counts<(kLStages - 2) * kLLoadsPerStage, 0>();
       } else {
@@ -274,7 +281,7 @@ __global__ __launch_bounds__(256) void w4a16_gemv_lds_kernel(
       }
       bare_barrier();
       if (it + kLStages - 1 < T)
-        lds_issue_stage(it + kLStages - 1, g_begin, NP, wave, qwb, xb, woff0, woff1, xoff, s_w_lds, s_x_lds);
+        lds_issue_stage(it + kLStages - 1, row_begin, NP, wave, qwb, xb, woff0, woff1, xoff, s_w_lds, s_x_lds);
       const int slot = it % kLStages;
       const uint32_t* wst = s_w + slot * kLStageWords + wread;
       uint32_t w[8];
@@ -322,11 +329,13 @@ __global__ __launch_bounds__(256) void w4a16_gemv_lds_kernel(
 // General kernel: register-staged, any N % 8 == 0.
 // ---------------------------------------------------------------------------
 
-// One group's operands for one lane: 4 steps x 8 rows of its packed column,
-// the 4 matching activation fragments, the zero-point word and 8 scales.
+// One group's operands for one lane: S steps (S = G / 32) x 8 rows of its
+// packed column, the S matching activation fragments, the zero-point word
+// and 8 scales.
+template <int S>
 struct GroupRegs {
-  uint32_t w[kSteps][8];
-  f16x8 a[kSteps];
+  uint32_t w[S][8];
+  f16x8 a[S];
   uint32_t zw;
   u32x4 sv;
 };
@@ -351,25 +360,27 @@ __device__ __forceinline__ T load_at(const char* base, uint32_t off) {
   return *reinterpret_cast<const T*>(base + off);
 }
 
-__device__ __forceinline__ void load_group(GroupRegs& r, const GemvLane L, int g) {
-  const char* wg = L.qw + static_cast<size_t>(g) * kGroup * L.row_bytes;
+template <int S>
+__device__ __forceinline__ void load_group(GroupRegs<S>& r, const GemvLane L, int g) {
+  const char* wg = L.qw + static_cast<size_t>(g) * (32 * S) * L.row_bytes;
 #pragma unroll
-  for (int ks = 0; ks < kSteps; ++ks)
+  for (int ks = 0; ks < S; ++ks)
 #pragma unroll
     for (int e = 0; e < 8; ++e) r.w[ks][e] = load_at<uint32_t>(wg + (ks * 32 + e) * L.row_bytes, L.w_off);
-  const char* xg = L.x + static_cast<size_t>(g) * kGroup * 2;
+  const char* xg = L.x + static_cast<size_t>(g) * (32 * S) * 2;
 #pragma unroll
-  for (int ks = 0; ks < kSteps; ++ks) r.a[ks] = load_at<f16x8>(xg + ks * 64, L.x_off);
+  for (int ks = 0; ks < S; ++ks) r.a[ks] = load_at<f16x8>(xg + ks * 64, L.x_off);
   r.zw = load_at<uint32_t>(L.qz + static_cast<size_t>(g) * L.row_bytes, L.z_off);
   r.sv = load_at<u32x4>(L.sc + static_cast<size_t>(g) * L.srow_bytes, L.s_off);
 }
 
-__device__ __forceinline__ void compute_group(const GroupRegs& r, f32x4 (&tot)[8]) {
+template <int S>
+__device__ __forceinline__ void compute_group(const GroupRegs<S>& r, f32x4 (&tot)[8]) {
   uint32_t negz[8];
   zero_bias(r.zw, negz);
   f32x4 acc[8];
 #pragma unroll
-  for (int ks = 0; ks < kSteps; ++ks) {
+  for (int ks = 0; ks < S; ++ks) {
     f16x8 b[8];
     unpack_step(r.w[ks], negz, b);
 #pragma unroll
@@ -387,8 +398,8 @@ __device__ __forceinline__ void compute_group(const GroupRegs& r, f32x4 (&tot)[8
 }
 
 // The wavefronts of a workgroup sit side by side in N (NWC x 64 contiguous
-// bytes per row) and walk the split's groups together.
-template <int NWC>
+// bytes per row) and walk the split's groups (of kGS rows) together.
+template <int NWC, int kGS>
 __global__ __launch_bounds__(NWC * 64) void w4a16_gemv_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qz,
@@ -404,7 +415,8 @@ __global__ __launch_bounds__(NWC * 64) void w4a16_gemv_kernel(
   const int c = (strip * NWC + wave) * kWaveCols + j;
   const bool cvalid = c < NP;
   const int cc = cvalid ? c : NP - 1;
-  const int G = K / kGroup;
+  constexpr int kSPG = kGS / 32;  // 32-row MFMA steps per group
+  const int G = K / kGS;
   const int g_begin = static_cast<int>(static_cast<int64_t>(split) * G / splits);
   const int g_end = static_cast<int>(static_cast<int64_t>(split + 1) * G / splits);
 
@@ -432,7 +444,7 @@ __global__ __launch_bounds__(NWC * 64) void w4a16_gemv_kernel(
   // below the math it is meant to overlap.
   const int n = g_end - g_begin;
   {
-    GroupRegs ra, rb;
+    GroupRegs<kSPG> ra, rb;
     load_group(ra, L, g_begin);
     int i = 0;
     for (; i + 2 < n; i += 2) {
@@ -499,22 +511,23 @@ __global__ __launch_bounds__(256) void w4a16_gemv_reduce(const float* __restrict
 constexpr int kGemvWaves = 4;         // register-staged kernel: wavefronts per workgroup
 constexpr int64_t kTargetWgs = 384;   // 1.5 workgroups per CU (192: slower; 768: no faster)
 
-GemvPlan plan_w4a16_gemv(int64_t M, int64_t N, int64_t K) {
-  GemvPlan plan{1, kGemvWaves, 0, false};
+GemvPlan plan_w4a16_gemv(int64_t M, int64_t N, int64_t K, int64_t group) {
+  GemvPlan plan{1, kGemvWaves, 0, false, static_cast<int>(group)};
   plan.lds = (N / 8) % 4 == 0;
   const int64_t strip_cols = plan.lds ? int64_t{kLStrip} : int64_t{kWaveCols} * plan.waves;
   const int64_t strips = (N / 8 + strip_cols - 1) / strip_cols;
-  const int64_t G = K / kGroup;
+  const int64_t G = K / group;
+  const int64_t max_groups = kLMaxRows / group;  // per split, LDS kernel
   // Split K only as far as needed to reach the target workgroup count: the
   // smallest divisor of the group count that gets there (and, for the LDS
-  // kernel, that leaves at most kLMaxGroups groups per split).
+  // kernel, that leaves at most kLMaxRows rows per split).
   int64_t splits = 1;
   while (strips * splits < kTargetWgs && splits < G) {
     ++splits;
     while (G % splits) ++splits;
   }
   if (plan.lds) {
-    while (G / splits > kLMaxGroups) {
+    while (G / splits > max_groups) {
       ++splits;
       while (G % splits) ++splits;
     }
@@ -522,7 +535,7 @@ GemvPlan plan_w4a16_gemv(int64_t M, int64_t N, int64_t K) {
       // More tokens: each split's fp32 partial sums (M x N, written and read
       // once) grow with M while the weight stream does not, and the MFMA work
       // per workgroup grows too. Pick the split count (a divisor of the group
-      // count, at most kLMaxGroups groups per split) with the smallest modelled
+      // count, at most kLMaxRows rows per split) with the smallest modelled
       // time: max(HBM bytes / 5 TB/s, MFMA work / (busy CUs x 2.25 TFLOP/s))
       // plus about 2 us for the reduce kernel. Both rates are the ones this
       // kernel pair reaches on the MI355X (stream and 16x16x32 fp16 MFMA with
@@ -548,6 +561,43 @@ GemvPlan plan_w4a16_gemv(int64_t M, int64_t N, int64_t K) {
   return plan;
 }
 
+namespace {
+
+template <int kGS>
+hipError_t launch_gemv_main(const uint16_t* x, const uint32_t* qw, const uint16_t* scales, const uint32_t* qz,
+                            uint16_t* y, float* part, int m, int n, int k, const GemvPlan& plan, int strips,
+                            XcdMap map, dim3 grid, hipStream_t stream) {
+  if (plan.lds) {
+    switch ((m + 15) / 16) {
+      case 1:
+        return launch_kernel(w4a16_gemv_lds_kernel<1, kGS>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part,
+                             m, n, k, strips, plan.splits, map);
+      case 2:
+        return launch_kernel(w4a16_gemv_lds_kernel<2, kGS>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part,
+                             m, n, k, strips, plan.splits, map);
+      case 3:
+        return launch_kernel(w4a16_gemv_lds_kernel<3, kGS>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part,
+                             m, n, k, strips, plan.splits, map);
+      default:
+        return launch_kernel(w4a16_gemv_lds_kernel<4, kGS>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part,
+                             m, n, k, strips, plan.splits, map);
+    }
+  }
+  switch (plan.waves) {
+    case 2:
+      return launch_kernel(w4a16_gemv_kernel<2, kGS>, grid, dim3(128), 0, stream, x, qw, scales, qz, y, part, m, n,
+                           k, strips, plan.splits, map);
+    case 8:
+      return launch_kernel(w4a16_gemv_kernel<8, kGS>, grid, dim3(512), 0, stream, x, qw, scales, qz, y, part, m, n,
+                           k, strips, plan.splits, map);
+    default:
+      return launch_kernel(w4a16_gemv_kernel<4, kGS>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part, m, n,
+                           k, strips, plan.splits, map);
+  }
+}
+
+}  // namespace
+
 hipError_t launch_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                              const int32_t* qzeros, uint16_t* y,
                              int64_t M, int64_t N, int64_t K, const GemvPlan& plan,
@@ -561,52 +611,32 @@ hipError_t launch_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const ui
   const uint32_t* qw = reinterpret_cast<const uint32_t*>(qweight);
   const uint32_t* qz = reinterpret_cast<const uint32_t*>(qzeros);
   float* part = static_cast<float*>(workspace);
-  hipError_t err;
-  if (plan.lds) {
-    if (K / kGroup / plan.splits > kLMaxGroups || (N / 8) % 4 != 0 || M > kGemvMaxM) return hipErrorInvalidValue;
-    switch ((m + 15) / 16) {
-      case 1:
-        err = launch_kernel(w4a16_gemv_lds_kernel<1>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part, m, n,
-                            k, strips, plan.splits, map);
-        break;
-      case 2:
-        err = launch_kernel(w4a16_gemv_lds_kernel<2>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part, m, n,
-                            k, strips, plan.splits, map);
-        break;
-      case 3:
-        err = launch_kernel(w4a16_gemv_lds_kernel<3>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part, m, n,
-                            k, strips, plan.splits, map);
-        break;
-      default:
-        err = launch_kernel(w4a16_gemv_lds_kernel<4>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part, m, n,
-                            k, strips, plan.splits, map);
-        break;
-    }
-  } else if (M > 16) {
+  if (plan.group != 32 && plan.group != 64 && plan.group != 128) return hipErrorInvalidValue;
+  if (K % plan.group || M < 1 || M > kGemvMaxM) return hipErrorInvalidValue;
+  if (plan.lds && (K / plan.group / plan.splits > kLMaxRows / plan.group || (N / 8) % 4 != 0))
+    return hipErrorInvalidValue;
+  if (!plan.lds && M > 16) {
     // The register-staged kernel takes 16 tokens at a time: run it on
     // consecutive 16-token slices (same stream, so they share the workspace).
     for (int64_t m0 = 0; m0 < M; m0 += 16) {
       const int64_t ms = M - m0 < 16 ? M - m0 : 16;
-      err = launch_w4a16_gemv(x + m0 * K, qweight, scales, qzeros, y + m0 * N, ms, N, K,
-                              plan_w4a16_gemv(ms, N, K), workspace, stream);
-      if (err != hipSuccess) return err;
+      const hipError_t e = launch_w4a16_gemv(x + m0 * K, qweight, scales, qzeros, y + m0 * N, ms, N, K,
+                                             plan_w4a16_gemv(ms, N, K, plan.group), workspace, stream);
+      if (e != hipSuccess) return e;
     }
     return hipSuccess;
-  } else {
-    switch (plan.waves) {
-      case 2:
-        err = launch_kernel(w4a16_gemv_kernel<2>, grid, dim3(128), 0, stream, x, qw, scales, qz, y, part, m, n,
-                            k, strips, plan.splits, map);
-        break;
-      case 8:
-        err = launch_kernel(w4a16_gemv_kernel<8>, grid, dim3(512), 0, stream, x, qw, scales, qz, y, part, m, n,
-                            k, strips, plan.splits, map);
-        break;
-      default:
-        err = launch_kernel(w4a16_gemv_kernel<4>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part, m, n,
-                            k, strips, plan.splits, map);
-        break;
-    }
+  }
+  hipError_t err;
+  switch (plan.group) {
+    case 32:
+      err = launch_gemv_main<32>(x, qw, scales, qz, y, part, m, n, k, plan, strips, map, grid, stream);
+      break;
+    case 64:
+      err = launch_gemv_main<64>(x, qw, scales, qz, y, part, m, n, k, plan, strips, map, grid, stream);
+      break;
+    default:
+      err = launch_gemv_main<128>(x, qw, scales, qz, y, part, m, n, k, plan, strips, map, grid, stream);
+      break;
   }
   if (err != hipSuccess || plan.splits == 1) return err;
   // 4-output units per XCD: its strips' columns for every token row.
