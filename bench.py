@@ -35,6 +35,11 @@ Also reported (same line):
                M = 1, 8, 64 and 2048 under W4A16 (GEMV up to 16 tokens, GEMM
                above) and W8A8_INT8 (quantize + scaled GEMM): microseconds per
                call with weights rotating over copies of >= 640 MB in all.
+  groups       W4A16 with groups of 64 and 32 rows (LMDeploy quantizes the
+               vision tower's attention with groups of 64): the gate+up GEMV
+               (M = 1, 4, 16) in GB/s, a ViT-L fused qkv projection (K=1024,
+               N=3072) at 1 and 16 tokens (GEMV) and 577 and 4096 tokens
+               (GEMM), and the 4096^3 prefill GEMM, cold weights, graph replays.
   cpu_baseline the CPU oracle on one step of the same workload (one weight
                set), repeated for about 10 s, in the same unit.
 """
@@ -85,6 +90,7 @@ def parse_args(argv=None):
     ap.add_argument("--prefill-reps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-layers", action="store_true", help="skip the decoder-layer linear set")
+    ap.add_argument("--no-groups", action="store_true", help="skip the group-64 / group-32 measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-kernel", action="store_true",
@@ -283,6 +289,59 @@ def bench_layers(torch, mq, synth, args, log):
     return out
 
 
+def bench_groups(torch, mq, synth, log):
+    """W4A16 with groups of 64 and 32 rows: GEMV and GEMM shapes, cold weights
+    (copies totalling >= 640 MB), microseconds per call from graph replays."""
+    dev = torch.device("cuda", 0)
+    R = 20
+
+    def time_calls(fn):
+        g = capture(torch, lambda: [fn(r) for r in range(R)])
+        g.replay()
+        best = min(timed_replay(torch, g)[1] for _ in range(3))
+        return best / R
+
+    out = {}
+    shapes = [("gate_up", 4096, 24576, (1, 4, 16)), ("vit_qkv", 1024, 3072, (1, 16, 577, 4096)),
+              ("o_proj_prefill", 4096, 4096, (4096,))]
+    for G in (64, 32):
+        out[f"g{G}"] = {}
+        for name, K, N, Ms in shapes:
+            log(f"groups: G={G} {name} K={K} N={N}")
+            w = {k: torch.from_numpy(v).to(dev) for k, v in synth.w4a16_weights(K, N, G, tag=400 + G).items()}
+            wbytes = K * N // 2
+            n = max(2, -(-640 * 2**20 // wbytes))
+            wsets = [w] + [{k: v.clone() for k, v in w.items()} for _ in range(n - 1)]
+            del w
+            res = {}
+            for M in Ms:
+                x = torch.from_numpy(synth.w4a16_inputs(M, K, 8, G, outlier_frac=0.005 if M <= 64 else 0.0,
+                                                        tag=410 + G, seed=M)["x"]).to(dev)
+                y = torch.empty((M, N), dtype=torch.float16, device=dev)
+                if M <= mq.GEMV_MAX_M:
+                    ws = torch.zeros(max(mq.w4a16_gemv_workspace_bytes(M, N, K, G), 16), dtype=torch.uint8,
+                                     device=dev)
+
+                    def fn(r, x=x, y=y, ws=ws):
+                        s = wsets[r % len(wsets)]
+                        mq.w4a16_gemv(x, s["qweight"], s["scales"], s["qzeros"], G, out=y, workspace=ws)
+                else:
+                    def fn(r, x=x, y=y):
+                        s = wsets[r % len(wsets)]
+                        mq.w4a16_gemm(x, s["qweight"], s["scales"], s["qzeros"], G, out=y)
+                t = time_calls(fn)
+                nbytes = w4a16_bytes(M, K, N, G)
+                flops = 2.0 * M * N * K
+                res[str(M)] = {"us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
+                               "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBPS, 4),
+                               "TFLOPS": round(flops / t / 1e12, 1),
+                               "fp16_frac": round(flops / t / 1e12 / FP16_PEAK_TFLOPS, 4)}
+            out[f"g{G}"][name] = res
+            del wsets
+            torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(args, log):
     import numpy as np
 
@@ -391,6 +450,8 @@ def main(argv=None):
         line["prefill"] = bench_prefill(torch, mq, synth, mq.quant_per_token_int8, args, log)
     if not args.no_layers:
         line["layers"] = bench_layers(torch, mq, synth, args, log)
+    if not args.no_groups:
+        line["groups"] = bench_groups(torch, mq, synth, log)
     if not args.no_cpu_baseline and rank == 0:
         line["cpu_baseline"] = cpu_baseline(args, log)
     print(json.dumps(line))
