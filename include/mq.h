@@ -192,6 +192,55 @@ mq_status mq_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const uint16_
                         int64_t M, int64_t N, int64_t K, int64_t group,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Column-blocked weight layout for decode, and the GEMV that reads it.
+ * Source: LMDeploy 4-bit deployment guide, deployment steps (the AWQ model
+ * is converted once into the inference engine's own weight format before it
+ * is served) and section 2.2 (scale and weight consumed in one kernel).
+ *
+ * mq_w4a16_block_weights reorders the bytes of qweight [K, N/8] (nothing
+ * inside a byte changes; byte g of word (k, c) holds the 4-bit weights of
+ * columns 8c+2g and 8c+2g+1 of row k) into 1 KB slots, one per 64-row pair
+ * P and 32-output strip s (S = N/32 strips), the slots of all strips for one
+ * pair next to each other:
+ *     blocked_bytes[((P*S + s)*64 + 16h + j)*16 + 8b + e]
+ *         = byte (j/4) of qweight[64P + 32b + 8h + e, 4s + j%4]
+ * for P < K/64, s < S, h < 4, j < 16, b < 2, e < 8 (little-endian words). Scales and zero points keep their layouts. Run it
+ * once when the weights are loaded; the result serves every
+ * mq_w4a16_gemv_blocked call on those weights.
+ *
+ *   qweight          [K, N/8] int32  in,  4-byte aligned
+ *   qweight_blocked  K*N/8    int32  out, 16-byte aligned, must not overlap qweight
+ * Requires: N % 32 == 0, K % 128 == 0 (-> MQ_ERR_SHAPE otherwise).
+ */
+mq_status mq_w4a16_block_weights(const int32_t* qweight, int32_t* qweight_blocked, int64_t N, int64_t K,
+                                 void* stream);
+
+/* Workspace for mq_w4a16_gemv_blocked (0: none needed, or a rejected problem). */
+size_t mq_w4a16_gemv_blocked_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group);
+
+/*
+ * W4A16 GEMV for decode (1 <= M <= 64) on blocked weights. Same definition,
+ * scales, zero points, arithmetic (fp32 group sums of x * (1024 + q), then
+ * s * (sum - (1024 + z) * sum(x)) per group) and tolerance as mq_w4a16_gemv;
+ * qweight_blocked is the output of mq_w4a16_block_weights for these weights.
+ * Each workgroup streams one 32-output strip over its K range as one
+ * contiguous run of bytes; K is split across workgroups (fp32 partials in
+ * `workspace`, added in split order by a second kernel) only when the layer
+ * has too few strips for two workgroups per compute unit. Up to 32 tokens share one pass over
+ * the weights; larger M takes one pass per 32 tokens. Deterministic.
+ *
+ *   workspace   >= mq_w4a16_gemv_blocked_workspace_bytes(M, N, K, group)
+ *               bytes, 16-byte aligned (may be NULL when that is 0); same
+ *               rules as mq_w4a16_gemv's workspace.
+ * Requires: as mq_w4a16_gemv, and N % 32 == 0 (-> MQ_ERR_SHAPE),
+ * qweight_blocked 16-byte aligned.
+ */
+mq_status mq_w4a16_gemv_blocked(const uint16_t* x, const int32_t* qweight_blocked, const uint16_t* scales,
+                                const int32_t* qzeros, uint16_t* y,
+                                int64_t M, int64_t N, int64_t K, int64_t group,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

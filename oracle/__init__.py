@@ -32,6 +32,7 @@ arithmetic, closed forms, special cases that reduce to a textbook matmul).
 
 from .ref import (  # noqa: F401
     NIBBLES_PER_WORD,
+    block_weights_ref,
     dequant_w4,
     quant_per_token_int8_ref,
     unpack_int4,

@@ -95,6 +95,44 @@ def w4a16_ref(x, qweight, scales, qzeros, group):
     return xf @ w
 
 
+def block_weights_ref(qweight):
+    """Column-blocked decode layout of qweight [K, N/8]: its bytes reordered, unchanged.
+
+    [lmdeploy-hw] deployment steps: the AWQ checkpoint is converted once into
+    the inference engine's own weight format before serving. The pages do
+    not describe that format; the reading here is a byte order in which the
+    32 outputs of strip s (packed columns 4s .. 4s+3) over all of K are
+    next to each other in memory for every 64 rows. Byte g of word (k, c)
+    holds the two 4-bit weights of columns 8c + 2g and 8c + 2g + 1 of row k.
+    Rows come in 64-row pairs P; with S = N/32 strips, slot (P, s) holds, for
+    lane L = 16h + j (c = j % 4, g = j // 4), 16 bytes, byte 8b + e being
+    byte g of word (64P + 32b + 8h + e, 4s + c):
+
+        blocked_bytes[((P * S + s) * 64 + L) * 16 + 8 * b + e]
+            = byte g of qweight[64 * P + 32 * b + 8 * h + e, 4 * s + c]
+
+    qweight: int32 [K, N/8] with K % 128 == 0, N % 32 == 0
+    -> int32 [K/64, 8 * N] (the same bytes, little-endian words; row P holds
+    the 64-row pair P of every strip).
+    """
+    qw = np.ascontiguousarray(np.asarray(qweight, dtype=np.int32))
+    if qw.ndim != 2:
+        raise ValueError("qweight must be [K, N/8]")
+    K, NP = qw.shape
+    if K % 128 or NP % 4:
+        raise ValueError("the blocked layout needs K % 128 == 0 and N % 32 == 0")
+    S = NP // 4
+    by = qw.view(np.uint8).reshape(K, NP, 4)  # little-endian: byte g of word (k, c) = by[k, c, g]
+    # index grids over (P, s, h, j, b, e) in the order of the blocked bytes
+    P, s, h, j, b, e = np.meshgrid(np.arange(K // 64), np.arange(S), np.arange(4), np.arange(16),
+                                   np.arange(2), np.arange(8), indexing="ij")
+    rows = 64 * P + 32 * b + 8 * h + e
+    cols = 4 * s + j % 4
+    g = j // 4
+    out = by[rows, cols, g].reshape(K // 64, 64 * S * 16)
+    return np.ascontiguousarray(out).view(np.int32)
+
+
 def quant_per_token_int8_ref(x):
     """Dynamic symmetric per-token int8 quantization.
 

@@ -381,3 +381,49 @@ def check_w8a8_linearity(w8a8):
     for m in range(M):
         for n in range(N):
             assert acc[m, n] == sum(int(xq[m, k]) * int(wq[n, k]) for k in range(K))
+
+
+def check_block_layout(block):
+    """The blocked decode layout moves bytes without changing them, puts the
+    slots of all strips for one 64-row pair next to each other and gives
+    every 16-byte lane slot byte g of eight consecutive rows (twice: two
+    32-row blocks) of one packed column, in the order documented in mq.h."""
+    for K, N in [(128, 32), (256, 96), (384, 64)]:
+        NP = N // 8
+        S = N // 32
+        kk = np.arange(K)[:, None, None]
+        cc = np.arange(NP)[None, :, None]
+        gg = np.arange(4)[None, None, :]
+        # two encodings of the source position in the byte value itself:
+        # (a) the row (K <= 384: row % 256 plus a separate check of row // 256),
+        # (b) the packed column and the byte index
+        for enc in ("row", "colbyte", "rowhigh"):
+            if enc == "row":
+                byt = np.broadcast_to(kk % 256, (K, NP, 4))
+            elif enc == "colbyte":
+                byt = np.broadcast_to(cc * 4 + gg, (K, NP, 4))
+            else:
+                byt = np.broadcast_to(kk // 256, (K, NP, 4))
+            qw = np.ascontiguousarray(byt.astype(np.uint8)).view(np.int32).reshape(K, NP)
+            out = block(qw)
+            assert out.shape == (K // 64, 8 * N) and out.dtype == np.int32
+            ob = np.ascontiguousarray(out).view(np.uint8).reshape(K // 64, S, 4, 16, 2, 8)  # P, s, h, j, b, e
+            for s in range(S):
+                for P in range(K // 64):
+                    for h in range(4):
+                        for j in range(16):
+                            c, g = 4 * s + j % 4, j // 4
+                            for b in range(2):
+                                rows = 64 * P + 32 * b + 8 * h + np.arange(8)
+                                got = ob[P, s, h, j, b]
+                                if enc == "row":
+                                    assert np.array_equal(got, rows % 256)
+                                elif enc == "colbyte":
+                                    assert np.all(got == c * 4 + g)
+                                else:
+                                    assert np.array_equal(got, rows // 256)
+    # bytes are moved, never changed: arbitrary bit patterns survive as a multiset
+    rng = np.random.default_rng(3)
+    qw = rng.integers(-2 ** 31, 2 ** 31, size=(256, 32), dtype=np.int64).astype(np.int32)
+    out = block(qw)
+    assert np.array_equal(np.sort(out.view(np.uint8).ravel()), np.sort(qw.view(np.uint8).ravel()))

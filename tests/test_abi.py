@@ -36,7 +36,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["mq_quant_per_token_int8", "mq_w8a8_scaled_mm", "mq_w8a8_mm_i32", "mq_w4a16_gemm",
-              "mq_w4a16_gemv", "mq_w4a16_gemv_workspace_bytes", "mq_abi_version",
+              "mq_w4a16_gemv", "mq_w4a16_gemv_workspace_bytes", "mq_w4a16_block_weights",
+              "mq_w4a16_gemv_blocked", "mq_w4a16_gemv_blocked_workspace_bytes", "mq_abi_version",
               "mq_status_string", "mq_last_error"]:
         assert n in names
 
@@ -172,6 +173,35 @@ def test_gemv_workspace_plan(lib):
             assert (K // group) % splits == 0
             if N % 32 == 0:
                 assert K // splits <= 1024
+
+
+def test_w4a16_blocked_validation(lib):
+    b = lib.mq_w4a16_block_weights
+    assert b(B, C, 48, 256, None) == SHAPE       # N % 32
+    assert b(B, C, 256, 200, None) == SHAPE      # K % 128
+    assert b(None, C, 256, 256, None) == NULL
+    assert b(B + 4, C + 8, 256, 256, None) == ALIGN   # blocked output needs 16 bytes
+    assert b(B, B + 16, 256, 256, None) == ALIAS
+    assert b(B, C, 0, 256, None) == OK
+    v = lib.mq_w4a16_gemv_blocked
+    ws = lib.mq_w4a16_gemv_blocked_workspace_bytes
+    assert v(A, B, C, D, E, 1, 264, 256, 128, F, 1 << 20, None) == SHAPE   # N % 32
+    assert v(A, B + 4, C, D, E, 1, 256, 256, 128, F, 1 << 20, None) == ALIGN
+    assert v(A, B, C, D, E, 1, 256, 256, 96, F, 1 << 20, None) == UNSUP
+    assert v(A, B, C, D, E, 65, 256, 256, 128, F, 1 << 20, None) == UNSUP
+    assert v(A, B, C, D, E, 0, 256, 256, 128, None, 0, None) == OK
+    # narrow layers split K: they need a workspace, wide ones do not
+    assert ws(1, 24576, 4096, 128) == 0
+    need = ws(1, 4096, 4096, 128)
+    assert need > 0 and need % (4 * 4096) == 0
+    assert v(A, B, C, D, E, 1, 4096, 4096, 128, None, 0, None) == WS
+    assert v(A, B, C, D, E, 1, 4096, 4096, 128, F, need - 4, None) == WS
+    assert ws(1, 264, 4096, 128) == 0 and ws(65, 4096, 4096, 128) == 0
+    # a split divides the chunk count (K/128) and the workspace holds its partials
+    for M, N, K in [(1, 6144, 4096), (16, 4096, 12288), (32, 3072, 1024), (64, 96, 640)]:
+        b = ws(M, N, K, 128)
+        splits = b // (4 * min(M, 32) * N) or 1
+        assert b % (4 * min(M, 32) * N) == 0 and (K // 128) % splits == 0
 
 
 @pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="lets a launch through; only meaningful without a GPU")

@@ -69,6 +69,44 @@ def test_w8a8_linearity():
     P.check_w8a8_linearity(oracle.w8a8_ref)
 
 
+def test_block_layout():
+    P.check_block_layout(oracle.block_weights_ref)
+
+
+def test_block_layout_mutants_caught():
+    # a transposed index in the layout (h and b swapped, rows reversed in a
+    # slot, packed columns rotated, byte index g taken from the wrong lane
+    # bits) must fail the pin
+    def view6(qw):
+        out = oracle.block_weights_ref(qw)
+        return out, np.ascontiguousarray(out).view(np.uint8).reshape(out.shape[0], -1, 4, 16, 2, 8)
+
+    def back(v, out):
+        return np.ascontiguousarray(v).reshape(-1).view(np.int32).reshape(out.shape)
+
+    def swap_hb(qw):
+        out, v = view6(qw)
+        return back(v[:, :, [0, 2, 1, 3]], out)
+
+    def reverse_e(qw):
+        out, v = view6(qw)
+        return back(v[..., ::-1], out)
+
+    def rotate_c(qw):
+        out, v = view6(qw)
+        j = np.arange(16)
+        return back(v[:, :, :, (j // 4) * 4 + (j + 1) % 4], out)
+
+    def swap_g(qw):
+        out, v = view6(qw)
+        j = np.arange(16)
+        return back(v[:, :, :, ((j // 4) ^ 1) * 4 + j % 4], out)
+
+    for mutant in (swap_hb, reverse_e, rotate_c, swap_g):
+        with pytest.raises(AssertionError):
+            P.check_block_layout(mutant)
+
+
 def test_acc_overflow_guard():
     K = (2 ** 31 - 1) // 16129 + 1
     with pytest.raises(OverflowError):

@@ -14,6 +14,9 @@ Entry points (same names as the C ABI, without the ``mq_`` prefix):
     w4a16_gemm(x, qweight, scales, qzeros, group)    -> y  (fp16)
     w4a16_gemv(x, qweight, scales, qzeros, group)    -> y  (fp16), M <= 64
     w4a16_gemv_workspace_bytes(M, N, K, group)       -> int
+    w4a16_block_weights(qweight)                     -> qweight_blocked (decode layout, once per matrix)
+    w4a16_gemv_blocked(x, qweight_blocked, scales, qzeros, group) -> y (fp16), M <= 64
+    w4a16_gemv_blocked_workspace_bytes(M, N, K, group) -> int
 
 and two compositions used by a model's linear layer:
 
@@ -29,6 +32,7 @@ __all__ = [
     "quant_per_token_int8", "w8a8_scaled_mm", "w8a8_mm_i32",
     "w4a16_gemm", "w4a16_gemv", "w4a16_gemv_workspace_bytes",
     "w4a16_linear", "w8a8_linear", "GEMV_MAX_M",
+    "w4a16_block_weights", "w4a16_gemv_blocked", "w4a16_gemv_blocked_workspace_bytes",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmq.so")
@@ -64,6 +68,10 @@ _PROTOTYPES = {
     "mq_w4a16_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
     "mq_w4a16_gemv_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I64]),
     "mq_w4a16_gemv": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
+    "mq_w4a16_block_weights": (ctypes.c_int, [_P, _P, _I64, _I64, _P]),
+    "mq_w4a16_gemv_blocked_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I64]),
+    "mq_w4a16_gemv_blocked": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t,
+                                             _P]),
 }
 
 
@@ -228,6 +236,61 @@ def w4a16_gemv(x, qweight, scales, qzeros, group=128, out=None, workspace=None, 
     with torch.cuda.device(x.device):
         _check(library().mq_w4a16_gemv(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), qzeros.data_ptr(),
                                        y.data_ptr(), M, N, K, group, ws_ptr, ws_bytes, _stream_of(x, stream)))
+    return y
+
+
+def w4a16_block_weights(qweight, out=None, stream=None):
+    """Reorder qweight [K, N/8] into the column-blocked decode layout (N % 32 == 0).
+
+    Returns an int32 tensor of shape [K/64, 8*N]: row P holds the bytes of
+    rows 64P .. 64P+63 of every 32-output strip in the order the blocked GEMV
+    streams them (see ``mq.h``). Run once per weight matrix.
+    """
+    torch = _torch()
+    _dev_tensor(qweight, "qweight", torch.int32, 2)
+    K, NP = qweight.shape
+    N = NP * 8
+    if N % 32:
+        raise ValueError("the blocked layout needs N % 32 == 0")
+    if K % 64:
+        raise ValueError("the blocked layout needs K % 128 == 0")
+    qb = _out(out, (K // 64, 8 * N), torch.int32, qweight, "out")
+    with torch.cuda.device(qweight.device):
+        _check(library().mq_w4a16_block_weights(qweight.data_ptr(), qb.data_ptr(), N, K,
+                                                _stream_of(qweight, stream)))
+    return qb
+
+
+def w4a16_gemv_blocked_workspace_bytes(M, N, K, group=128):
+    """Workspace bytes ``w4a16_gemv_blocked`` needs (0 if none)."""
+    return int(library().mq_w4a16_gemv_blocked_workspace_bytes(M, N, K, group))
+
+
+def w4a16_gemv_blocked(x, qweight_blocked, scales, qzeros, group=128, out=None, workspace=None, stream=None):
+    """W4A16 GEMV for decode (M <= 64) on weights from ``w4a16_block_weights``."""
+    torch = _torch()
+    _dev_tensor(x, "x", torch.float16, 2)
+    _dev_tensor(qweight_blocked, "qweight_blocked", torch.int32, 2)
+    _dev_tensor(scales, "scales", torch.float16, 2)
+    _dev_tensor(qzeros, "qzeros", torch.int32, 2)
+    M, K = x.shape
+    N = scales.shape[1]
+    if group <= 0 or K % group:
+        raise ValueError("K must be a multiple of the group size")
+    if tuple(qweight_blocked.shape) != (K // 64, 8 * N) or N % 32:
+        raise ValueError("qweight_blocked must be [K/64, 8*N] (from w4a16_block_weights)")
+    if tuple(scales.shape) != (K // group, N) or tuple(qzeros.shape) != (K // group, N // 8):
+        raise ValueError("scales must be [K/G, N] and qzeros [K/G, N/8]")
+    y = _out(out, (M, N), torch.float16, x, "out")
+    need = w4a16_gemv_blocked_workspace_bytes(M, N, K, group)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    with torch.cuda.device(x.device):
+        _check(library().mq_w4a16_gemv_blocked(x.data_ptr(), qweight_blocked.data_ptr(), scales.data_ptr(),
+                                               qzeros.data_ptr(), y.data_ptr(), M, N, K, group, ws_ptr, ws_bytes,
+                                               _stream_of(x, stream)))
     return y
 
 

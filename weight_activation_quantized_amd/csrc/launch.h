@@ -46,6 +46,16 @@ struct GemvPlan {
 };
 GemvPlan plan_w4a16_gemv(int64_t M, int64_t N, int64_t K, int64_t group);
 
+// Column-blocked weight layout for the decode GEMV (N % 128 == 0,
+// K % 128 == 0): conversion from [K, N/8], plan and launch.
+hipError_t launch_w4a16_block_weights(const int32_t* qweight, int32_t* blocked, int64_t N, int64_t K,
+                                      hipStream_t stream);
+GemvPlan plan_w4a16_gemv_blocked(int64_t M, int64_t N, int64_t K, int64_t group);
+size_t w4a16_gemv_blocked_workspace(int64_t M, int64_t N, int64_t K, int64_t group);
+hipError_t launch_w4a16_gemv_blocked(const uint16_t* x, const int32_t* blocked, const uint16_t* scales,
+                                     const int32_t* qzeros, uint16_t* y, int64_t M, int64_t N, int64_t K,
+                                     const GemvPlan& plan, void* workspace, hipStream_t stream);
+
 hipError_t launch_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                              const int32_t* qzeros, uint16_t* y,
                              int64_t M, int64_t N, int64_t K, const GemvPlan& plan,

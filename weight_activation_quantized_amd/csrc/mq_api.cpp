@@ -250,4 +250,64 @@ mq_status mq_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const uint16_
                     "w4a16_gemv launch");
 }
 
+mq_status mq_w4a16_block_weights(const int32_t* qweight, int32_t* qweight_blocked, int64_t N, int64_t K,
+                                 void* stream) {
+  if (N < 0 || N > kMaxN4 || N % 32)
+    return fail(MQ_ERR_SHAPE, "N=%lld must be a multiple of 32 in [0, 2^27]", (long long)N);
+  if (K < 0 || K > kMaxK || K % 128)
+    return fail(MQ_ERR_SHAPE, "K=%lld must be a multiple of 128 in [0, 2^20]", (long long)K);
+  if (K * N > kMaxElems) return fail(MQ_ERR_SHAPE, "problem too large");
+  MQ_TRY(need(qweight, K * N, "qweight"));
+  MQ_TRY(need(qweight_blocked, K * N, "qweight_blocked"));
+  if (!aligned(qweight, 4)) return fail(MQ_ERR_ALIGN, "qweight must be 4-byte aligned");
+  if (!aligned(qweight_blocked, 16)) return fail(MQ_ERR_ALIGN, "qweight_blocked must be 16-byte aligned");
+  const size_t bytes = static_cast<size_t>(K * (N / 8)) * 4;
+  const Range in[] = {{qweight, bytes, "qweight"}};
+  const Range out[] = {{qweight_blocked, bytes, "qweight_blocked"}};
+  MQ_TRY(check_alias(in, out));
+  if (K == 0 || N == 0) return ok();
+  return hip_status(mq::launch_w4a16_block_weights(qweight, qweight_blocked, N, K, as_stream(stream)),
+                    "w4a16_block_weights launch");
+}
+
+size_t mq_w4a16_gemv_blocked_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group) {
+  if ((group != 32 && group != 64 && group != 128) || M < 1 || M > mq::kGemvMaxM || N < 32 || N % 32 ||
+      N > kMaxN4 || K < 128 || K > kMaxK || K % 128)
+    return 0;
+  return mq::w4a16_gemv_blocked_workspace(M, N, K, group);
+}
+
+mq_status mq_w4a16_gemv_blocked(const uint16_t* x, const int32_t* qweight_blocked, const uint16_t* scales,
+                                const int32_t* qzeros, uint16_t* y,
+                                int64_t M, int64_t N, int64_t K, int64_t group,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  mq_status s = check_w4a16(x, qweight_blocked, scales, qzeros, y, M, N, K, group);
+  if (s != MQ_OK) return s;
+  if (N % 32) return fail(MQ_ERR_SHAPE, "the blocked layout needs N %% 32 == 0 (got N=%lld)", (long long)N);
+  if (!aligned(qweight_blocked, 16)) return fail(MQ_ERR_ALIGN, "qweight_blocked must be 16-byte aligned");
+  if (M > mq::kGemvMaxM)
+    return fail(MQ_ERR_UNSUPPORTED, "GEMV needs M <= %lld (got %lld); use mq_w4a16_gemm",
+                (long long)mq::kGemvMaxM, (long long)M);
+  if (M == 0) return ok();
+  const size_t need_ws = mq::w4a16_gemv_blocked_workspace(M, N, K, group);
+  if (need_ws > 0) {
+    if (!workspace || workspace_bytes < need_ws)
+      return fail(MQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need_ws,
+                  workspace ? workspace_bytes : static_cast<size_t>(0));
+    if (!aligned(workspace, 16)) return fail(MQ_ERR_ALIGN, "workspace must be 16-byte aligned");
+    const size_t G = static_cast<size_t>(K / group);
+    const Range in[] = {{x, static_cast<size_t>(M * K) * 2, "x"},
+                        {qweight_blocked, static_cast<size_t>(K * (N / 8)) * 4, "qweight_blocked"},
+                        {scales, G * static_cast<size_t>(N) * 2, "scales"},
+                        {qzeros, G * static_cast<size_t>(N / 8) * 4, "qzeros"}};
+    const Range out[] = {{y, static_cast<size_t>(M * N) * 2, "y"}, {workspace, need_ws, "workspace"}};
+    s = check_alias(in, out);
+    if (s != MQ_OK) return s;
+  }
+  const mq::GemvPlan plan = mq::plan_w4a16_gemv_blocked(M, N, K, group);
+  return hip_status(mq::launch_w4a16_gemv_blocked(x, qweight_blocked, scales, qzeros, y, M, N, K, plan,
+                                                  need_ws ? workspace : nullptr, as_stream(stream)),
+                    "w4a16_gemv_blocked launch");
+}
+
 }  // extern "C"

@@ -42,12 +42,12 @@
 #include "device_common.h"
 #include "launch.h"
 #include "w4a16_common.h"
+#include "w4a16_split.h"
 
 namespace mq {
 namespace {
 
 constexpr int kWaveCols = 16;        // packed columns per wavefront (128 outputs)
-constexpr int kXcds = 8;             // workgroups are dispatched round-robin over 8 XCDs
 
 __device__ __forceinline__ void store_f16x8(uint16_t* dst, const float (&v)[8]) {
   u32x4 out;
@@ -82,25 +82,6 @@ __device__ __forceinline__ void write_out(const f32x4 (&tot)[8], uint16_t* __res
       *reinterpret_cast<f32x4*>(dst + 4) = f32x4{tot[4][q], tot[5][q], tot[6][q], tot[7][q]};
     }
   }
-}
-
-// Work item -> (strip, split). XCD x owns a contiguous block of strips with
-// all their splits, so the reduce kernel finds a strip's partial sums in
-// that XCD's L2; within an XCD, consecutive workgroups take neighbouring
-// strips of one split, so concurrently running workgroups read adjacent
-// row segments.
-struct XcdMap {
-  int strips_per_xcd;
-};
-
-__device__ __forceinline__ bool decode_work(int block, int strips_per_xcd, int strips, int splits, int& strip,
-                                            int& split) {
-  const int xcd = block % kXcds;
-  const int slot = block / kXcds;
-  const int local = slot % strips_per_xcd;
-  split = slot / strips_per_xcd;
-  strip = xcd * strips_per_xcd + local;
-  return strip < strips && split < splits;
 }
 
 // ---------------------------------------------------------------------------
@@ -465,45 +446,6 @@ __global__ __launch_bounds__(NWC * 64) void w4a16_gemv_kernel(
     }
   }
   if (cvalid) write_out(tot, y, partial, M, N, c, h, split, splits);
-}
-
-// ---------------------------------------------------------------------------
-// Split reduction: y = fp16(sum over splits of partial[split]) in split
-// order. Thread t of the block sums 4 consecutive outputs of one token row
-// of one strip; blocks are mapped to the XCD that wrote that strip.
-// ---------------------------------------------------------------------------
-template <int S>
-__global__ __launch_bounds__(256) void w4a16_gemv_reduce(const float* __restrict__ partial,
-                                                         uint16_t* __restrict__ y, int M, int N,
-                                                         int strip_cols, int strips_per_xcd,
-                                                         int blocks_per_xcd, int splits) {
-  const int xcd = blockIdx.x % kXcds;
-  const int local = (blockIdx.x / kXcds) * 256 + threadIdx.x;  // 4-output unit within the XCD
-  const int units_per_row = strips_per_xcd * strip_cols / 4;    // per token row
-  const int m = local / units_per_row;
-  const int u = local % units_per_row;
-  if (m >= M) return;
-  const int n = xcd * strips_per_xcd * strip_cols + u * 4;  // first output column
-  if (n >= N) return;
-  (void)blocks_per_xcd;
-  const size_t stride = static_cast<size_t>(M) * N;
-  const float* src = partial + static_cast<size_t>(m) * N + n;
-  f32x4 acc = *reinterpret_cast<const f32x4*>(src);
-  if constexpr (S > 0) {
-    f32x4 v[S > 1 ? S - 1 : 1];
-#pragma unroll
-    for (int s = 1; s < S; ++s) v[s - 1] = *reinterpret_cast<const f32x4*>(src + s * stride);
-#pragma unroll
-    for (int s = 1; s < S; ++s) acc += v[s - 1];
-  } else {
-    for (int s = 1; s < splits; ++s) acc += *reinterpret_cast<const f32x4*>(src + s * stride);
-  }
-  f16x2 lo, hi;
-  lo[0] = static_cast<f16>(acc[0]);
-  lo[1] = static_cast<f16>(acc[1]);
-  hi[0] = static_cast<f16>(acc[2]);
-  hi[1] = static_cast<f16>(acc[3]);
-  *reinterpret_cast<u32x2*>(y + static_cast<size_t>(m) * N + n) = u32x2{as_u32(lo), as_u32(hi)};
 }
 
 }  // namespace

@@ -1,0 +1,422 @@
+// W4A16 decode GEMV on a column-blocked weight layout (gfx950).
+//
+// Source: LMDeploy 4-bit deployment guide, deployment steps (the AWQ model is
+// converted once into the inference engine's own format before serving) and
+// section 2.2 (scale and weight consumed in one kernel); LMDeploy toolkit
+// overview, section 2.5 (4-bit weights in groups; the weight stream is what
+// decode pays for). Same result as the GEMV on the [K, N/8] layout:
+// y[m,n] = sum_k x[m,k] * (q[k,n] - z[k/G,n]) * s[k/G,n], G in {32, 64, 128}.
+//
+// Why a second layout: in [K, N/8] a column strip is a few hundred bytes of
+// every 4*N/8-byte row, so reading it at full HBM speed needs wide strips,
+// and wide strips leave too few workgroups for the GPU unless K is split
+// across workgroups (fp32 partial sums and a second kernel). In the blocked
+// layout a wavefront's share of the weights is one contiguous run of bytes,
+// so a workgroup can own a narrow strip over all of K and no split is needed
+// for wide layers.
+//
+// Blocked layout (the bytes of qweight reordered, nothing inside a byte
+// changes; byte g of word (k, c) holds the weights of columns 8c+2g (low
+// nibble) and 8c+2g+1 (high nibble) of row k):
+//   strip s = packed columns 4s .. 4s+3 (32 outputs), S = N/32 strips; the
+//   rows come in 64-row pairs P; for lane L = 16h + j (h = 0..3, j = 0..15,
+//   c = j % 4, g = j / 4) the slot (P, s) holds 16 bytes, byte 8b + e
+//   (b = 0, 1, e = 0..7) being byte g of qweight[64P + 32b + 8h + e, 4s + c]:
+//     blocked_bytes[((P * S + s) * 64 + L) * 16 + 8b + e]
+//   A wavefront's 1 KB of a pair is contiguous, and the slots of all strips
+//   for one pair are adjacent, so workgroups working on the same rows read
+//   neighbouring memory (as a sweep over the rows of [K, N/8] does).
+//
+// Kernel: a workgroup owns one strip (and, for narrow layers, one of
+// `splits` K ranges); its wavefronts take consecutive 128-row chunks of that
+// range, each streaming its own contiguous bytes into registers (two chunks
+// in flight). Lane (j, h) of an MFMA B fragment (v_mfma_f32_16x16x32_f16,
+// column j, k = 8h..8h+7 of a 32-row block) gets from its 8 bytes of the
+// block both field 2g (tile 0) and field 2g+1 (tile 1) of packed column c:
+// one byte permute per row pair spreads two bytes into the two fp16 halves,
+// and one v_and_or_b32 per field makes 1024 + q (low nibble) or 1024 + 16 q
+// (high nibble). Tokens ride on the 16-row side (rows >= M are zero and
+// never stored). Per group the kernel adds s * (acc - (1024+z) * X) with X
+// the per-token sum of x over the group (one more MFMA against a fragment of
+// ones per block). The wavefronts' sums are added in LDS in wavefront
+// order, so results are deterministic. 32-output strips give 768
+// workgroups for a 24576-wide layer: every CU streams the same share.
+#include <algorithm>
+
+#include "device_common.h"
+#include "launch.h"
+#include "w4a16_common.h"
+#include "w4a16_split.h"
+
+namespace mq {
+namespace {
+
+constexpr int kBStrip = 4;         // packed columns per strip (32 outputs)
+constexpr int kBOut = kBStrip * 8;  // outputs per strip
+constexpr int kBChunkRows = 128;    // rows per chunk (two 64-row pairs, four 32-row blocks)
+
+// ---------------------------------------------------------------------------
+// Layout conversion: one thread per 16-byte lane slot of the blocked layout.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void w4a16_block_weights_kernel(const uint32_t* __restrict__ qw,
+                                                                  u32x4* __restrict__ qb, int K, int NP,
+                                                                  int64_t slots) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= slots) return;
+  const int L = static_cast<int>(t & 63);
+  const int64_t ps = t >> 6;  // P * S + s
+  const int S = NP / kBStrip;
+  const int64_t P = ps / S;
+  const int64_t s = ps % S;
+  const int j = L & 15, h = L >> 4;
+  const int c = j & 3, g = j >> 2;
+  const uint32_t* col = qw + s * kBStrip + c;
+  u32x4 v;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {  // word w: block b = w / 2, rows e = 4 (w % 2) .. +3
+    const int64_t k0 = 64 * P + 32 * (w >> 1) + 8 * h + 4 * (w & 1);
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) word |= ((col[(k0 + e) * NP] >> (8 * g)) & 0xFFu) << (8 * e);
+    v[w] = word;
+  }
+  qb[t] = v;
+}
+
+// One chunk (128 rows) of a lane's operands: its 32 weight bytes (two
+// 16-byte pair slots), the x fragments of each token tile (rows 8h..8h+7 of
+// each 32-row block), and the two scales and the zero-point byte of each
+// group.
+template <int kT, int kGPC>
+struct BChunk {
+  u32x4 w[2];
+  f16x8 a[kT][4];
+  uint32_t sv[kGPC];  // fp16 pair: s of field 2g, s of field 2g+1
+  uint32_t zw[kGPC];  // zero-point word of the packed column (byte g used)
+};
+
+struct BLane {
+  const u32x4* qb;        // the lane's 16-byte slot of the strip's first pair
+  size_t pair_stride;     // slots from one 64-row pair to the next (S * 64)
+  const uint16_t* x[2];   // token row of each tile (nullptr: row >= M)
+  const uint16_t* sc;     // scales + 8 * packed column + 2g
+  const uint32_t* qz;     // qzeros + packed column
+  int N, NP;
+};
+
+template <int kT, int kGS>
+__device__ __forceinline__ void load_chunk(BChunk<kT, kBChunkRows / kGS>& ch, const BLane& L, int chunk) {
+  constexpr int kGPC = kBChunkRows / kGS;
+  const u32x4* wp = L.qb + static_cast<size_t>(2 * chunk) * L.pair_stride;
+  ch.w[0] = wp[0];
+  ch.w[1] = wp[L.pair_stride];
+#pragma unroll
+  for (int t = 0; t < kT; ++t)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      if (L.x[t]) {
+        ch.a[t][b] = *reinterpret_cast<const f16x8*>(L.x[t] + chunk * kBChunkRows + 32 * b);
+      } else {
+        ch.a[t][b] = f16x8{};
+      }
+    }
+#pragma unroll
+  for (int g = 0; g < kGPC; ++g) {
+    const size_t grp = static_cast<size_t>(chunk) * kGPC + g;
+    ch.sv[g] = *reinterpret_cast<const uint32_t*>(L.sc + grp * L.N);
+    ch.zw[g] = L.qz[grp * L.NP];
+  }
+}
+
+// B fragments of one 32-row block from the lane's two words of it (rows
+// 8h+0..3 and 8h+4..7, byte g of each): tile 0 gets 1024 + q of field 2g,
+// tile 1 gets 1024 + 16 q of field 2g+1. The masks and the 1024.0 pattern
+// come in registers (NibConst), so the compiler forms each (v & mask) |
+// magic as one v_and_or_b32 itself. It must be the compiler's instruction,
+// not inline asm: the fragments feed MFMA operands directly, and only for
+// its own instructions does the compiler insert the wait states a VALU
+// write needs before an MFMA reads the register (with an asm v_and_or_b32
+// the MFMA was measured to read the register's old value).
+__device__ __forceinline__ void unpack_block(uint32_t w0, uint32_t w1, const NibConst& c, f16x8 (&bf)[2]) {
+  const uint32_t ws[2] = {w0, w1};
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      // bytes 2t, 2t+1 (rows 4q+2t, 4q+2t+1) into bits 0-7 and 16-23
+      const uint32_t v = byte_perm(ws[q], ws[q], t ? 0x0C030C02u : 0x0C010C00u);
+      const f16x2 lo = as_f16x2((v & c.lo) | c.magic);
+      const f16x2 hi = as_f16x2((v & c.hi) | c.magic);
+      bf[0][4 * q + 2 * t] = lo[0];
+      bf[0][4 * q + 2 * t + 1] = lo[1];
+      bf[1][4 * q + 2 * t] = hi[0];
+      bf[1][4 * q + 2 * t + 1] = hi[1];
+    }
+}
+
+template <int kT, int kGS>
+__device__ __forceinline__ void compute_chunk(const BChunk<kT, kBChunkRows / kGS>& ch, const NibConst& nc,
+                                              const f16x8 ones, int g_lane, f32x4 (&tot)[kT][2]) {
+  constexpr int kGPC = kBChunkRows / kGS;  // groups per chunk
+  constexpr int kBPG = kGS / 32;           // 32-row blocks per group
+  const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int g = 0; g < kGPC; ++g) {
+    f32x4 acc[kT][2];
+    f32x4 accx[kT];
+#pragma unroll
+    for (int bb = 0; bb < kBPG; ++bb) {
+      const int b = g * kBPG + bb;  // block within the chunk: pair b / 2, half b % 2
+      f16x8 bf[2];
+      unpack_block(ch.w[b >> 1][2 * (b & 1)], ch.w[b >> 1][2 * (b & 1) + 1], nc, bf);
+#pragma unroll
+      for (int t = 0; t < kT; ++t) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+          acc[t][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ch.a[t][b], bf[f], bb == 0 ? zero4 : acc[t][f], 0, 0,
+                                                            0);
+        accx[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ch.a[t][b], ones, bb == 0 ? zero4 : accx[t], 0, 0, 0);
+      }
+    }
+    // tot += s * (acc - (1024 + z) * X); field 2g+1 carries 16 (q - z), so
+    // its scale is s / 16 (exact).
+    const f16x2 s2 = as_f16x2(ch.sv[g]);
+    const uint32_t zb = (ch.zw[g] >> (8 * g_lane)) & 0xFFu;
+    const float sc[2] = {static_cast<float>(s2[0]), static_cast<float>(s2[1]) * 0.0625f};
+    const float bias[2] = {1024.0f + static_cast<float>(zb & 15u), 1024.0f + static_cast<float>(zb & 0xF0u)};
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int t = 0; t < kT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tot[t][f][i] = fmaf(sc[f], fmaf(-bias[f], accx[t][i], acc[t][f][i]), tot[t][f][i]);
+  }
+}
+
+// kT 16-token tiles, groups of kGS rows, kW wavefronts per workgroup, kD
+// chunks in flight per wavefront.
+template <int kT, int kGS, int kW, int kD = 2>
+__global__ __launch_bounds__(kW * 64) void w4a16_gemv_blocked_kernel(
+    const uint16_t* __restrict__ x, const u32x4* __restrict__ qb, const uint16_t* __restrict__ scales,
+    const uint32_t* __restrict__ qz, uint16_t* __restrict__ y, float* __restrict__ partial, int M, int N, int K,
+    int strips, int splits, XcdMap map) {
+  constexpr int kGPC = kBChunkRows / kGS;
+  __shared__ float s_red[kW * 16 * kT * kBOut];
+
+  int strip, split;
+  if (!decode_work(blockIdx.x, map.strips_per_xcd, strips, splits, strip, split)) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 15;
+  const int h = lane >> 4;
+  const int c = j & 3, g = j >> 2;
+  const int NP = N >> 3;
+  const int chunks = K / kBChunkRows;
+  const int cps = chunks / splits;  // chunks per split (plan: divides)
+  const int cpw = cps / kW;         // chunks per wavefront (plan: divides, >= 1)
+  const int c0 = split * cps + wave * cpw;
+  const int col = strip * kBStrip + c;  // packed column of the lane
+
+  BLane L;
+  L.qb = qb + static_cast<size_t>(strip) * 64 + lane;
+  L.pair_stride = static_cast<size_t>(NP / kBStrip) * 64;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int m = 16 * t + j;
+    L.x[t] = (t < kT && m < M) ? x + static_cast<size_t>(m) * K + 8 * h : nullptr;
+  }
+  L.sc = scales + static_cast<size_t>(col) * 8 + 2 * g;
+  L.qz = qz + col;
+  L.N = N;
+  L.NP = NP;
+
+  const NibConst nc = nib_const();
+  f16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = static_cast<f16>(1.0f);
+
+  f32x4 tot[kT][2];
+#pragma unroll
+  for (int t = 0; t < kT; ++t)
+#pragma unroll
+    for (int f = 0; f < 2; ++f) tot[t][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // kD chunks in flight per wavefront (a ring of register buffers, the loop
+  // unrolled over the ring): a buffer's next chunk is requested as soon as
+  // the buffer has been consumed; sched_barrier keeps each request ahead of
+  // the math it is meant to overlap. Every request is unconditional: past
+  // the wavefront's last chunk it repeats that chunk (an L2 hit, never
+  // used). A conditional request makes the compiler copy the buffer at the
+  // loop's back edge, which waits for every load in flight. Two chunks
+  // (4 KB per wavefront) measured best: four were slower (the repeated
+  // tail requests and one fewer wavefront per SIMD cost more than the depth
+  // gains).
+  {
+    const int last = c0 + cpw - 1;
+    BChunk<kT, kGPC> cb[kD];
+#pragma unroll
+    for (int d = 0; d < kD; ++d) load_chunk<kT, kGS>(cb[d], L, min(c0 + d, last));
+    for (int i = 0; i < cpw; i += kD) {
+#pragma unroll
+      for (int d = 0; d < kD; ++d) {
+        if (i + d < cpw) compute_chunk<kT, kGS>(cb[d], nc, ones, g, tot);
+        load_chunk<kT, kGS>(cb[d], L, min(c0 + i + d + kD, last));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // Add the wavefronts' sums in wavefront order. Lane (j, h) holds token
+  // 16t + 4h + i of strip output 8c + 2g + f in tot[t][f][i].
+#pragma unroll
+  for (int t = 0; t < kT; ++t)
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        s_red[((wave * 16 * kT) + 16 * t + 4 * h + i) * kBOut + 8 * c + 2 * g + f] = tot[t][f][i];
+  __syncthreads();
+  const int rows = min(M, 16 * kT);
+  for (int idx = threadIdx.x; idx < rows * kBOut; idx += kW * 64) {
+    const int m = idx / kBOut, n = idx % kBOut;
+    float v = s_red[m * kBOut + n];
+#pragma unroll
+    for (int w = 1; w < kW; ++w) v += s_red[(w * 16 * kT + m) * kBOut + n];
+    const size_t o = static_cast<size_t>(strip) * kBOut + n;
+    if (splits == 1) {
+      y[static_cast<size_t>(m) * N + o] = __builtin_bit_cast(uint16_t, static_cast<f16>(v));
+    } else {
+      partial[(static_cast<size_t>(split) * M + m) * N + o] = v;
+    }
+  }
+}
+
+template <int kT, int kGS>
+hipError_t launch_blocked_main(const uint16_t* x, const u32x4* qb, const uint16_t* scales, const uint32_t* qz,
+                               uint16_t* y, float* part, int m, int n, int k, const GemvPlan& plan, int strips,
+                               XcdMap map, dim3 grid, hipStream_t stream) {
+  switch (plan.waves) {
+    case 1:
+      return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 1>, grid, dim3(64), 0, stream, x, qb, scales, qz, y,
+                           part, m, n, k, strips, plan.splits, map);
+    case 2:
+      return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 2>, grid, dim3(128), 0, stream, x, qb, scales, qz, y,
+                           part, m, n, k, strips, plan.splits, map);
+    default:
+      return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 4>, grid, dim3(256), 0, stream, x, qb, scales, qz, y,
+                           part, m, n, k, strips, plan.splits, map);
+  }
+}
+
+template <int kGS>
+hipError_t launch_blocked_group(const uint16_t* x, const u32x4* qb, const uint16_t* scales, const uint32_t* qz,
+                                uint16_t* y, float* part, int m, int n, int k, const GemvPlan& plan, int strips,
+                                XcdMap map, dim3 grid, hipStream_t stream) {
+  if (m <= 16) return launch_blocked_main<1, kGS>(x, qb, scales, qz, y, part, m, n, k, plan, strips, map, grid, stream);
+  return launch_blocked_main<2, kGS>(x, qb, scales, qz, y, part, m, n, k, plan, strips, map, grid, stream);
+}
+
+}  // namespace
+
+constexpr int kBlockedMaxTokens = 32;  // tokens per pass over the weights (two 16-token tiles)
+constexpr int64_t kBlockedMinWgs = 512;  // two workgroups per CU before K is split
+
+GemvPlan plan_w4a16_gemv_blocked(int64_t M, int64_t N, int64_t K, int64_t group) {
+  GemvPlan plan{1, 1, 0, false, static_cast<int>(group)};
+  const int64_t strips = N / kBOut;
+  const int64_t chunks = K / kBChunkRows;
+  // Split K only when the layer has too few strips for two workgroups per
+  // CU: the smallest divisor of the chunk count that gets there (else the
+  // largest); four wavefronts per workgroup when the split's chunks allow.
+  for (int64_t s = 1; s <= chunks; ++s) {
+    if (chunks % s) continue;
+    plan.splits = static_cast<int>(s);
+    if (strips * s >= kBlockedMinWgs) break;
+  }
+  const int64_t cps = chunks / plan.splits;
+  plan.waves = cps % 4 == 0 ? 4 : (cps % 2 == 0 ? 2 : 1);
+  (void)M;
+  const int64_t mt = std::min(M, int64_t{kBlockedMaxTokens});
+  plan.workspace_bytes = plan.splits > 1 ? static_cast<size_t>(plan.splits) * mt * N * sizeof(float) : 0;
+  return plan;
+}
+
+size_t w4a16_gemv_blocked_workspace(int64_t M, int64_t N, int64_t K, int64_t group) {
+  // the largest need over the 32-token passes
+  size_t ws = 0;
+  for (int64_t m0 = 0; m0 < M; m0 += kBlockedMaxTokens)
+    ws = std::max(ws, plan_w4a16_gemv_blocked(std::min(M - m0, int64_t{kBlockedMaxTokens}), N, K, group)
+                          .workspace_bytes);
+  return ws;
+}
+
+hipError_t launch_w4a16_block_weights(const int32_t* qweight, int32_t* blocked, int64_t N, int64_t K,
+                                      hipStream_t stream) {
+  if (N % kBOut || K % kBChunkRows) return hipErrorInvalidValue;
+  const int64_t slots = (N / 8) * K / 4;  // 16-byte slots
+  const int64_t blocks = (slots + 255) / 256;
+  return launch_kernel(w4a16_block_weights_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream,
+                       reinterpret_cast<const uint32_t*>(qweight), reinterpret_cast<u32x4*>(blocked),
+                       static_cast<int>(K), static_cast<int>(N / 8), slots);
+}
+
+hipError_t launch_w4a16_gemv_blocked(const uint16_t* x, const int32_t* blocked, const uint16_t* scales,
+                                     const int32_t* qzeros, uint16_t* y, int64_t M, int64_t N, int64_t K,
+                                     const GemvPlan& plan, void* workspace, hipStream_t stream) {
+  if (N % kBOut || K % kBChunkRows || M < 1 || M > kGemvMaxM || plan.waves < 1) return hipErrorInvalidValue;
+  if (plan.group != 32 && plan.group != 64 && plan.group != 128) return hipErrorInvalidValue;
+  if ((K / kBChunkRows) % (static_cast<int64_t>(plan.splits) * plan.waves)) return hipErrorInvalidValue;
+  if (M > kBlockedMaxTokens) {
+    // Up to 32 tokens per pass over the weights; later passes re-read them.
+    for (int64_t m0 = 0; m0 < M; m0 += kBlockedMaxTokens) {
+      const int64_t ms = std::min(M - m0, int64_t{kBlockedMaxTokens});
+      const hipError_t e = launch_w4a16_gemv_blocked(x + m0 * K, blocked, scales, qzeros, y + m0 * N, ms, N, K,
+                                                     plan_w4a16_gemv_blocked(ms, N, K, plan.group), workspace,
+                                                     stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+  const int strips = static_cast<int>(N / kBOut);
+  XcdMap map;
+  map.strips_per_xcd = (strips + kXcds - 1) / kXcds;
+  const dim3 grid(static_cast<uint32_t>(kXcds * map.strips_per_xcd * plan.splits));
+  const u32x4* qb = reinterpret_cast<const u32x4*>(blocked);
+  const uint32_t* qz = reinterpret_cast<const uint32_t*>(qzeros);
+  float* part = static_cast<float*>(workspace);
+  hipError_t err;
+  switch (plan.group) {
+    case 32:
+      err = launch_blocked_group<32>(x, qb, scales, qz, y, part, m, n, k, plan, strips, map, grid, stream);
+      break;
+    case 64:
+      err = launch_blocked_group<64>(x, qb, scales, qz, y, part, m, n, k, plan, strips, map, grid, stream);
+      break;
+    default:
+      err = launch_blocked_group<128>(x, qb, scales, qz, y, part, m, n, k, plan, strips, map, grid, stream);
+      break;
+  }
+  if (err != hipSuccess || plan.splits == 1) return err;
+  const int cols8 = kBOut;
+  const int64_t units_per_xcd = static_cast<int64_t>(map.strips_per_xcd) * cols8 / 4 * M;
+  const int blocks_per_xcd = static_cast<int>((units_per_xcd + 255) / 256);
+  const dim3 rgrid(static_cast<uint32_t>(kXcds * blocks_per_xcd));
+  const int sps = map.strips_per_xcd;
+  switch (plan.splits) {
+    case 2:
+      return launch_kernel(w4a16_gemv_reduce<2>, rgrid, dim3(256), 0, stream, part, y, m, n, cols8, sps,
+                           blocks_per_xcd, plan.splits);
+    case 4:
+      return launch_kernel(w4a16_gemv_reduce<4>, rgrid, dim3(256), 0, stream, part, y, m, n, cols8, sps,
+                           blocks_per_xcd, plan.splits);
+    case 8:
+      return launch_kernel(w4a16_gemv_reduce<8>, rgrid, dim3(256), 0, stream, part, y, m, n, cols8, sps,
+                           blocks_per_xcd, plan.splits);
+    default:
+      return launch_kernel(w4a16_gemv_reduce<0>, rgrid, dim3(256), 0, stream, part, y, m, n, cols8, sps,
+                           blocks_per_xcd, plan.splits);
+  }
+}
+
+}  // namespace mq
