@@ -47,16 +47,6 @@ __device__ __forceinline__ uint32_t nib_hi_to_f16x2(uint32_t v) {
   return (v & 0x00F000F0u) | 0x64006400u;
 }
 
-// (v & mask) | magic in one v_and_or_b32. gfx9 VOP3 encodings take no
-// literal constants and at most one scalar operand, so left to itself the
-// compiler emits v_and + v_or; here the mask rides in an SGPR and the magic
-// constant in a VGPR that the caller materializes once.
-__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask, uint32_t magic) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "s"(mask), "v"(magic));
-  return r;
-}
-
 // s_waitcnt with vmcnt <= VM and lgkmcnt <= LGKM (gfx9 encoding), bracketed
 // by compiler memory barriers so no memory access moves across it.
 template <int VM, int LGKM>

@@ -43,6 +43,7 @@ struct GemvPlan {
   size_t workspace_bytes;
   bool lds;   // LDS-staged kernel (N % 32 == 0)
   int group;  // rows per group: 32, 64 or 128
+  int strips_per_unit = 1;  // blocked GEMV: adjacent 32-output strips per workgroup
 };
 GemvPlan plan_w4a16_gemv(int64_t M, int64_t N, int64_t K, int64_t group);
 

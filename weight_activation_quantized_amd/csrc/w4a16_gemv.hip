@@ -107,17 +107,20 @@ template <int T>
 constexpr int lds_loads_per_stage() { return 2 + T; }
 
 // B fragments of 1024 + q (even p) or 1024 + 16 q (odd p) for one 32-row
-// step: w[e] is the lane's word of row 8h + e; magic holds 0x64006400.
-__device__ __forceinline__ void unpack_step_biased(const uint32_t (&w)[8], uint32_t magic, f16x8 (&b)[8]) {
+// step: w[e] is the lane's word of row 8h + e. The masks and the 1024.0
+// pattern come in registers (NibConst), so the compiler forms each
+// (v & mask) | magic as one v_and_or_b32 of its own; the fragments feed MFMA
+// operands, and only for its own instructions does the compiler insert the
+// wait states a VALU write needs before an MFMA reads the register.
+__device__ __forceinline__ void unpack_step_biased(const uint32_t (&w)[8], const NibConst& c, f16x8 (&b)[8]) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const uint32_t lo = byte_perm(w[2 * t + 1], w[2 * t], 0x05040100u);  // bytes 0,1 of both rows
     const uint32_t hi = byte_perm(w[2 * t + 1], w[2 * t], 0x07060302u);  // bytes 2,3 of both rows
     const uint32_t lo8 = lo >> 8, hi8 = hi >> 8;
-    const uint32_t v[8] = {and_or(lo, 0x000F000Fu, magic),  and_or(lo, 0x00F000F0u, magic),
-                           and_or(lo8, 0x000F000Fu, magic), and_or(lo8, 0x00F000F0u, magic),
-                           and_or(hi, 0x000F000Fu, magic),  and_or(hi, 0x00F000F0u, magic),
-                           and_or(hi8, 0x000F000Fu, magic), and_or(hi8, 0x00F000F0u, magic)};
+    const uint32_t v[8] = {(lo & c.lo) | c.magic,  (lo & c.hi) | c.magic,  (lo8 & c.lo) | c.magic,
+                           (lo8 & c.hi) | c.magic, (hi & c.lo) | c.magic,  (hi & c.hi) | c.magic,
+                           (hi8 & c.lo) | c.magic, (hi8 & c.hi) | c.magic};
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const f16x2 d = as_f16x2(v[p]);
@@ -235,8 +238,7 @@ __global__ __launch_bounds__(256) void w4a16_gemv_lds_kernel(
   const int wread = (8 * h) * 64 + wchunk * 4 + (j & 3);
   const int xread = j * 16 + ((h ^ ((j >> 2) & 3)) * 4);
   const int col = 16 * wave + j;  // packed column within the strip
-  uint32_t magic;
-  asm("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+  const NibConst nc = nib_const();
   f16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = static_cast<f16>(1.0f);
@@ -272,7 +274,7 @@ __global__ __launch_bounds__(256) void w4a16_gemv_lds_kernel(
 #pragma unroll
       for (int t = 0; t < kT; ++t) a[t] = *reinterpret_cast<const f16x8*>(&s_x[(slot * kT + t) * kLXWords + xread]);
       f16x8 b[8];
-      unpack_step_biased(w, magic, b);
+      unpack_step_biased(w, nc, b);
       const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < kT; ++t) {

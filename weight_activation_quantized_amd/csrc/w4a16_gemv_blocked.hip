@@ -83,16 +83,16 @@ __global__ __launch_bounds__(256) void w4a16_block_weights_kernel(const uint32_t
   qb[t] = v;
 }
 
-// One chunk (128 rows) of a lane's operands: its 32 weight bytes (two
-// 16-byte pair slots), the x fragments of each token tile (rows 8h..8h+7 of
-// each 32-row block), and the two scales and the zero-point byte of each
-// group.
-template <int kT, int kGPC>
+// One chunk (128 rows) of a lane's operands for kSP adjacent strips: 32
+// weight bytes per strip (two 16-byte pair slots), the x fragments of each
+// token tile (rows 8h..8h+7 of each 32-row block, shared by the strips),
+// and per strip the two scales and the zero-point byte of each group.
+template <int kT, int kGPC, int kSP>
 struct BChunk {
-  u32x4 w[2];
+  u32x4 w[kSP][2];
   f16x8 a[kT][4];
-  uint32_t sv[kGPC];  // fp16 pair: s of field 2g, s of field 2g+1
-  uint32_t zw[kGPC];  // zero-point word of the packed column (byte g used)
+  uint32_t sv[kSP][kGPC];  // fp16 pair: s of field 2g, s of field 2g+1
+  uint32_t zw[kSP][kGPC];  // zero-point word of the packed column (byte g used)
 };
 
 struct BLane {
@@ -104,12 +104,15 @@ struct BLane {
   int N, NP;
 };
 
-template <int kT, int kGS>
-__device__ __forceinline__ void load_chunk(BChunk<kT, kBChunkRows / kGS>& ch, const BLane& L, int chunk) {
+template <int kT, int kGS, int kSP>
+__device__ __forceinline__ void load_chunk(BChunk<kT, kBChunkRows / kGS, kSP>& ch, const BLane& L, int chunk) {
   constexpr int kGPC = kBChunkRows / kGS;
   const u32x4* wp = L.qb + static_cast<size_t>(2 * chunk) * L.pair_stride;
-  ch.w[0] = wp[0];
-  ch.w[1] = wp[L.pair_stride];
+#pragma unroll
+  for (int sp = 0; sp < kSP; ++sp) {  // adjacent strips' slots are adjacent
+    ch.w[sp][0] = wp[64 * sp];
+    ch.w[sp][1] = wp[L.pair_stride + 64 * sp];
+  }
 #pragma unroll
   for (int t = 0; t < kT; ++t)
 #pragma unroll
@@ -123,8 +126,11 @@ __device__ __forceinline__ void load_chunk(BChunk<kT, kBChunkRows / kGS>& ch, co
 #pragma unroll
   for (int g = 0; g < kGPC; ++g) {
     const size_t grp = static_cast<size_t>(chunk) * kGPC + g;
-    ch.sv[g] = *reinterpret_cast<const uint32_t*>(L.sc + grp * L.N);
-    ch.zw[g] = L.qz[grp * L.NP];
+#pragma unroll
+    for (int sp = 0; sp < kSP; ++sp) {
+      ch.sv[sp][g] = *reinterpret_cast<const uint32_t*>(L.sc + grp * L.N + kBOut * sp);
+      ch.zw[sp][g] = L.qz[grp * L.NP + kBStrip * sp];
+    }
   }
 }
 
@@ -154,57 +160,68 @@ __device__ __forceinline__ void unpack_block(uint32_t w0, uint32_t w1, const Nib
     }
 }
 
-template <int kT, int kGS>
-__device__ __forceinline__ void compute_chunk(const BChunk<kT, kBChunkRows / kGS>& ch, const NibConst& nc,
-                                              const f16x8 ones, int g_lane, f32x4 (&tot)[kT][2]) {
+template <int kT, int kGS, int kSP>
+__device__ __forceinline__ void compute_chunk(const BChunk<kT, kBChunkRows / kGS, kSP>& ch, const NibConst& nc,
+                                              const f16x8 ones, int g_lane, f32x4 (&tot)[kT][kSP][2]) {
   constexpr int kGPC = kBChunkRows / kGS;  // groups per chunk
   constexpr int kBPG = kGS / 32;           // 32-row blocks per group
   const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int g = 0; g < kGPC; ++g) {
-    f32x4 acc[kT][2];
+    f32x4 acc[kT][kSP][2];
     f32x4 accx[kT];
 #pragma unroll
     for (int bb = 0; bb < kBPG; ++bb) {
       const int b = g * kBPG + bb;  // block within the chunk: pair b / 2, half b % 2
-      f16x8 bf[2];
-      unpack_block(ch.w[b >> 1][2 * (b & 1)], ch.w[b >> 1][2 * (b & 1) + 1], nc, bf);
 #pragma unroll
-      for (int t = 0; t < kT; ++t) {
+      for (int sp = 0; sp < kSP; ++sp) {
+        f16x8 bf[2];
+        unpack_block(ch.w[sp][b >> 1][2 * (b & 1)], ch.w[sp][b >> 1][2 * (b & 1) + 1], nc, bf);
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
-          acc[t][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ch.a[t][b], bf[f], bb == 0 ? zero4 : acc[t][f], 0, 0,
-                                                            0);
-        accx[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ch.a[t][b], ones, bb == 0 ? zero4 : accx[t], 0, 0, 0);
+        for (int t = 0; t < kT; ++t)
+#pragma unroll
+          for (int f = 0; f < 2; ++f)
+            acc[t][sp][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ch.a[t][b], bf[f], bb == 0 ? zero4 : acc[t][sp][f],
+                                                                  0, 0, 0);
       }
+#pragma unroll
+      for (int t = 0; t < kT; ++t)
+        accx[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ch.a[t][b], ones, bb == 0 ? zero4 : accx[t], 0, 0, 0);
     }
     // tot += s * (acc - (1024 + z) * X); field 2g+1 carries 16 (q - z), so
     // its scale is s / 16 (exact).
-    const f16x2 s2 = as_f16x2(ch.sv[g]);
-    const uint32_t zb = (ch.zw[g] >> (8 * g_lane)) & 0xFFu;
-    const float sc[2] = {static_cast<float>(s2[0]), static_cast<float>(s2[1]) * 0.0625f};
-    const float bias[2] = {1024.0f + static_cast<float>(zb & 15u), 1024.0f + static_cast<float>(zb & 0xF0u)};
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+    for (int sp = 0; sp < kSP; ++sp) {
+      const f16x2 s2 = as_f16x2(ch.sv[sp][g]);
+      const uint32_t zb = (ch.zw[sp][g] >> (8 * g_lane)) & 0xFFu;
+      const float sc[2] = {static_cast<float>(s2[0]), static_cast<float>(s2[1]) * 0.0625f};
+      const float bias[2] = {1024.0f + static_cast<float>(zb & 15u), 1024.0f + static_cast<float>(zb & 0xF0u)};
 #pragma unroll
-      for (int t = 0; t < kT; ++t)
+      for (int f = 0; f < 2; ++f)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) tot[t][f][i] = fmaf(sc[f], fmaf(-bias[f], accx[t][i], acc[t][f][i]), tot[t][f][i]);
+        for (int t = 0; t < kT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            tot[t][sp][f][i] = fmaf(sc[f], fmaf(-bias[f], accx[t][i], acc[t][sp][f][i]), tot[t][sp][f][i]);
+    }
   }
 }
 
-// kT 16-token tiles, groups of kGS rows, kW wavefronts per workgroup, kD
-// chunks in flight per wavefront.
-template <int kT, int kGS, int kW, int kD = 2>
+// kT 16-token tiles, groups of kGS rows, kW wavefronts per workgroup, kSP
+// adjacent strips per workgroup (they share every x fragment a wavefront
+// loads), kD chunks in flight per wavefront. `units` counts kSP-strip units.
+template <int kT, int kGS, int kW, int kSP, int kD = 2>
 __global__ __launch_bounds__(kW * 64) void w4a16_gemv_blocked_kernel(
     const uint16_t* __restrict__ x, const u32x4* __restrict__ qb, const uint16_t* __restrict__ scales,
     const uint32_t* __restrict__ qz, uint16_t* __restrict__ y, float* __restrict__ partial, int M, int N, int K,
-    int strips, int splits, XcdMap map) {
+    int units, int splits, XcdMap map) {
   constexpr int kGPC = kBChunkRows / kGS;
-  __shared__ float s_red[kW * 16 * kT * kBOut];
+  constexpr int kUOut = kSP * kBOut;  // outputs per unit
+  __shared__ float s_red[kW * 16 * kT * kUOut];
 
-  int strip, split;
-  if (!decode_work(blockIdx.x, map.strips_per_xcd, strips, splits, strip, split)) return;
+  int unit, split;
+  if (!decode_work(blockIdx.x, map.strips_per_xcd, units, splits, unit, split)) return;
+  const int strip = unit * kSP;  // first strip of the unit
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 15;
@@ -235,11 +252,13 @@ __global__ __launch_bounds__(kW * 64) void w4a16_gemv_blocked_kernel(
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = static_cast<f16>(1.0f);
 
-  f32x4 tot[kT][2];
+  f32x4 tot[kT][kSP][2];
 #pragma unroll
   for (int t = 0; t < kT; ++t)
 #pragma unroll
-    for (int f = 0; f < 2; ++f) tot[t][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < kSP; ++sp)
+#pragma unroll
+      for (int f = 0; f < 2; ++f) tot[t][sp][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // kD chunks in flight per wavefront (a ring of register buffers, the loop
   // unrolled over the ring): a buffer's next chunk is requested as soon as
@@ -253,35 +272,37 @@ __global__ __launch_bounds__(kW * 64) void w4a16_gemv_blocked_kernel(
   // gains).
   {
     const int last = c0 + cpw - 1;
-    BChunk<kT, kGPC> cb[kD];
+    BChunk<kT, kGPC, kSP> cb[kD];
 #pragma unroll
-    for (int d = 0; d < kD; ++d) load_chunk<kT, kGS>(cb[d], L, min(c0 + d, last));
+    for (int d = 0; d < kD; ++d) load_chunk<kT, kGS, kSP>(cb[d], L, min(c0 + d, last));
     for (int i = 0; i < cpw; i += kD) {
 #pragma unroll
       for (int d = 0; d < kD; ++d) {
-        if (i + d < cpw) compute_chunk<kT, kGS>(cb[d], nc, ones, g, tot);
-        load_chunk<kT, kGS>(cb[d], L, min(c0 + i + d + kD, last));
+        if (i + d < cpw) compute_chunk<kT, kGS, kSP>(cb[d], nc, ones, g, tot);
+        load_chunk<kT, kGS, kSP>(cb[d], L, min(c0 + i + d + kD, last));
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
 
   // Add the wavefronts' sums in wavefront order. Lane (j, h) holds token
-  // 16t + 4h + i of strip output 8c + 2g + f in tot[t][f][i].
+  // 16t + 4h + i of output 32sp + 8c + 2g + f of the unit in tot[t][sp][f][i].
 #pragma unroll
   for (int t = 0; t < kT; ++t)
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+    for (int sp = 0; sp < kSP; ++sp)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        s_red[((wave * 16 * kT) + 16 * t + 4 * h + i) * kBOut + 8 * c + 2 * g + f] = tot[t][f][i];
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s_red[((wave * 16 * kT) + 16 * t + 4 * h + i) * kUOut + kBOut * sp + 8 * c + 2 * g + f] = tot[t][sp][f][i];
   __syncthreads();
   const int rows = min(M, 16 * kT);
-  for (int idx = threadIdx.x; idx < rows * kBOut; idx += kW * 64) {
-    const int m = idx / kBOut, n = idx % kBOut;
-    float v = s_red[m * kBOut + n];
+  for (int idx = threadIdx.x; idx < rows * kUOut; idx += kW * 64) {
+    const int m = idx / kUOut, n = idx % kUOut;
+    float v = s_red[m * kUOut + n];
 #pragma unroll
-    for (int w = 1; w < kW; ++w) v += s_red[(w * 16 * kT + m) * kBOut + n];
+    for (int w = 1; w < kW; ++w) v += s_red[(w * 16 * kT + m) * kUOut + n];
     const size_t o = static_cast<size_t>(strip) * kBOut + n;
     if (splits == 1) {
       y[static_cast<size_t>(m) * N + o] = __builtin_bit_cast(uint16_t, static_cast<f16>(v));
@@ -291,29 +312,40 @@ __global__ __launch_bounds__(kW * 64) void w4a16_gemv_blocked_kernel(
   }
 }
 
-template <int kT, int kGS>
+template <int kT, int kGS, int kSP>
 hipError_t launch_blocked_main(const uint16_t* x, const u32x4* qb, const uint16_t* scales, const uint32_t* qz,
-                               uint16_t* y, float* part, int m, int n, int k, const GemvPlan& plan, int strips,
+                               uint16_t* y, float* part, int m, int n, int k, const GemvPlan& plan, int units,
                                XcdMap map, dim3 grid, hipStream_t stream) {
   switch (plan.waves) {
     case 1:
-      return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 1>, grid, dim3(64), 0, stream, x, qb, scales, qz, y,
-                           part, m, n, k, strips, plan.splits, map);
+      return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 1, kSP>, grid, dim3(64), 0, stream, x, qb, scales, qz,
+                           y, part, m, n, k, units, plan.splits, map);
     case 2:
-      return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 2>, grid, dim3(128), 0, stream, x, qb, scales, qz, y,
-                           part, m, n, k, strips, plan.splits, map);
+      return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 2, kSP>, grid, dim3(128), 0, stream, x, qb, scales,
+                           qz, y, part, m, n, k, units, plan.splits, map);
     default:
-      return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 4>, grid, dim3(256), 0, stream, x, qb, scales, qz, y,
-                           part, m, n, k, strips, plan.splits, map);
+      return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 4, kSP>, grid, dim3(256), 0, stream, x, qb, scales,
+                           qz, y, part, m, n, k, units, plan.splits, map);
   }
 }
 
 template <int kGS>
 hipError_t launch_blocked_group(const uint16_t* x, const u32x4* qb, const uint16_t* scales, const uint32_t* qz,
-                                uint16_t* y, float* part, int m, int n, int k, const GemvPlan& plan, int strips,
+                                uint16_t* y, float* part, int m, int n, int k, const GemvPlan& plan, int units,
                                 XcdMap map, dim3 grid, hipStream_t stream) {
-  if (m <= 16) return launch_blocked_main<1, kGS>(x, qb, scales, qz, y, part, m, n, k, plan, strips, map, grid, stream);
-  return launch_blocked_main<2, kGS>(x, qb, scales, qz, y, part, m, n, k, plan, strips, map, grid, stream);
+  if (m <= 16) {
+    switch (plan.strips_per_unit) {
+      case 3:
+        return launch_blocked_main<1, kGS, 3>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+      case 2:
+        return launch_blocked_main<1, kGS, 2>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+      default:
+        return launch_blocked_main<1, kGS, 1>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+    }
+  }
+  if (plan.strips_per_unit == 2)
+    return launch_blocked_main<2, kGS, 2>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+  return launch_blocked_main<2, kGS, 1>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
 }
 
 }  // namespace
@@ -325,18 +357,32 @@ GemvPlan plan_w4a16_gemv_blocked(int64_t M, int64_t N, int64_t K, int64_t group)
   GemvPlan plan{1, 1, 0, false, static_cast<int>(group)};
   const int64_t strips = N / kBOut;
   const int64_t chunks = K / kBChunkRows;
-  // Split K only when the layer has too few strips for two workgroups per
-  // CU: the smallest divisor of the chunk count that gets there (else the
-  // largest); four wavefronts per workgroup when the split's chunks allow.
+  const int64_t mt = std::min(M, int64_t{kBlockedMaxTokens});
+  // Every workgroup loads all of x for its K range, so with more than a few
+  // tokens a workgroup takes several adjacent strips that share those loads
+  // (three for one 16-token tile, two for two; what divides the strips).
+  int sp = 1;
+  if (mt > 4) {
+    if (mt <= 16 && strips % 3 == 0) {
+      sp = 3;
+    } else if (strips % 2 == 0) {
+      sp = 2;
+    }
+  }
+  plan.strips_per_unit = sp;
+  const int64_t units = strips / sp;
+  // Split K only when there are too few units for two single-strip
+  // workgroups (one multi-strip workgroup) per CU: the smallest divisor of
+  // the chunk count that gets there (else the largest); four wavefronts per
+  // workgroup when the split's chunks allow.
+  const int64_t min_wgs = sp == 1 ? kBlockedMinWgs : kBlockedMinWgs / 2;
   for (int64_t s = 1; s <= chunks; ++s) {
     if (chunks % s) continue;
     plan.splits = static_cast<int>(s);
-    if (strips * s >= kBlockedMinWgs) break;
+    if (units * s >= min_wgs) break;
   }
   const int64_t cps = chunks / plan.splits;
   plan.waves = cps % 4 == 0 ? 4 : (cps % 2 == 0 ? 2 : 1);
-  (void)M;
-  const int64_t mt = std::min(M, int64_t{kBlockedMaxTokens});
   plan.workspace_bytes = plan.splits > 1 ? static_cast<size_t>(plan.splits) * mt * N * sizeof(float) : 0;
   return plan;
 }
@@ -378,9 +424,9 @@ hipError_t launch_w4a16_gemv_blocked(const uint16_t* x, const int32_t* blocked, 
     return hipSuccess;
   }
   const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
-  const int strips = static_cast<int>(N / kBOut);
+  const int units = static_cast<int>(N / kBOut / plan.strips_per_unit);
   XcdMap map;
-  map.strips_per_xcd = (strips + kXcds - 1) / kXcds;
+  map.strips_per_xcd = (units + kXcds - 1) / kXcds;
   const dim3 grid(static_cast<uint32_t>(kXcds * map.strips_per_xcd * plan.splits));
   const u32x4* qb = reinterpret_cast<const u32x4*>(blocked);
   const uint32_t* qz = reinterpret_cast<const uint32_t*>(qzeros);
@@ -388,17 +434,17 @@ hipError_t launch_w4a16_gemv_blocked(const uint16_t* x, const int32_t* blocked, 
   hipError_t err;
   switch (plan.group) {
     case 32:
-      err = launch_blocked_group<32>(x, qb, scales, qz, y, part, m, n, k, plan, strips, map, grid, stream);
+      err = launch_blocked_group<32>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
       break;
     case 64:
-      err = launch_blocked_group<64>(x, qb, scales, qz, y, part, m, n, k, plan, strips, map, grid, stream);
+      err = launch_blocked_group<64>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
       break;
     default:
-      err = launch_blocked_group<128>(x, qb, scales, qz, y, part, m, n, k, plan, strips, map, grid, stream);
+      err = launch_blocked_group<128>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
       break;
   }
   if (err != hipSuccess || plan.splits == 1) return err;
-  const int cols8 = kBOut;
+  const int cols8 = kBOut * plan.strips_per_unit;
   const int64_t units_per_xcd = static_cast<int64_t>(map.strips_per_xcd) * cols8 / 4 * M;
   const int blocks_per_xcd = static_cast<int>((units_per_xcd + 255) / 256);
   const dim3 rgrid(static_cast<uint32_t>(kXcds * blocks_per_xcd));
