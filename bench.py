@@ -7,7 +7,10 @@ Headline workload: the W4A16 decode GEMV of an 8B-shaped MLP gate+up
 projection, M in {1, 4, 16} tokens, K = 4096, N = 24576, group 128 (fp16
 activations with 0.5% x20 outlier channels; uniform 4-bit weights and zero
 points; fp16 scales in [0.005, 0.02]). One step = one GEMV at each of
-M = 1, 4, 16. Every call reads a different one of `--sets` weight sets
+M = 1, 4, 16, on weights in the decode layout (mq_w4a16_block_weights, run
+once per weight set before anything is timed, as a serving engine converts
+its checkpoint at load); the same steps on the AWQ [K, N/8] layout
+(mq_w4a16_gemv) are reported as `gemv_awq_layout`. Every call reads a different one of `--sets` weight sets
 (52 MB each, 520 MB in all), so a set is read again only after more than the
 256 MB Infinity Cache and the 32 MB of L2 have been swept: the weight stream
 comes from HBM. Inputs are resident in HBM before the timed region. The
@@ -18,13 +21,12 @@ value = algorithmic bytes of a step (x + qweight + scales + qzeros + y, for
 the three calls) / wall time of a step, between device synchronizations.
 
 Also reported (same line):
-  roofline     one GEMV call, the unit that dominates the step: its main
-               kernel (w4a16_gemv_lds_kernel) and, when K is split across
-               workgroups, the split reduction (w4a16_gemv_reduce) that follows
-               it on the same stream. achieved = algorithmic bytes per call /
+  roofline     one GEMV call, the unit that dominates the step: one launch of
+               w4a16_gemv_blocked_kernel (K is not split at N = 24576, so no
+               reduce kernel follows). achieved = algorithmic bytes per call /
                average call duration from HIP events recorded on that stream
                around the timed graph replay, against 8 TB/s; `traffic` =
-               FETCH_SIZE + WRITE_SIZE per call (both kernels) from a committed
+               FETCH_SIZE + WRITE_SIZE per call from a committed
                rocprofv3 counter summary when it matches the current kernel
                source, else null.
   prefill      W8A8 prefill (per-token quant + scaled int8 GEMM, M=2048,
@@ -32,8 +34,8 @@ Also reported (same line):
                N=4096): kernel time and TOPS against the dense MFMA peaks.
   layers       the linear layers of an 8B-shaped decoder layer (qkv 4096->6144,
                o_proj 4096->4096, gate_up 4096->24576, down 12288->4096) at
-               M = 1, 8, 64 and 2048 under W4A16 (GEMV up to 16 tokens, GEMM
-               above) and W8A8_INT8 (quantize + scaled GEMM): microseconds per
+               M = 1, 8, 64 and 2048 under W4A16 (decode-layout GEMV up to 64
+               tokens, GEMM above) and W8A8_INT8 (quantize + scaled GEMM): microseconds per
                call with weights rotating over copies of >= 640 MB in all.
   groups       W4A16 with groups of 64 and 32 rows (LMDeploy quantizes the
                vision tower's attention with groups of 64): the gate+up GEMV
@@ -63,7 +65,7 @@ METRIC = "W4A16 decode GEMV GB/s (% HBM peak); W8A8/W4A16 prefill TOPS (% MFMA p
 GEMV_K, GEMV_N, GROUP = 4096, 24576, 128
 GEMV_MS = (1, 4, 16)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_c1_traffic.json")
-GEMV_SOURCES = ["w4a16_gemv.hip", "w4a16_common.h", "device_common.h"]
+GEMV_SOURCES = ["w4a16_gemv_blocked.hip", "w4a16_split.h", "w4a16_common.h", "device_common.h"]
 
 
 def w4a16_bytes(M, K, N, G=GROUP):
@@ -77,7 +79,7 @@ def gemv_source_hash():
     for f in GEMV_SOURCES:
         with open(os.path.join(ROOT, "weight_activation_quantized_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
-    h.update(repr((_build.FLAGS[:-2], _build.SOURCE_FLAGS.get("w4a16_gemv.hip", []))).encode())
+    h.update(repr((_build.FLAGS[:-2], _build.SOURCE_FLAGS.get("w4a16_gemv_blocked.hip", []))).encode())
     return h.hexdigest()[:16]
 
 
@@ -124,47 +126,66 @@ def timed_replay(torch, g):
 
 
 def bench_gemv(torch, mq, synth, args, log):
+    """The headline steps on the decode weight layout (converted once per weight
+    set before anything is timed, as at model load), then the same steps on the
+    AWQ [K, N/8] layout for comparison."""
     dev = torch.device("cuda", 0)
     log(f"generating {args.sets} weight sets of K={GEMV_K} N={GEMV_N}")
     sets = []
     for s in range(args.sets):
         w = synth.w4a16_weights(GEMV_K, GEMV_N, GROUP, tag=1, seed=1000 + s)
-        sets.append({k: torch.from_numpy(v).to(dev) for k, v in w.items()})
+        t = {k: torch.from_numpy(v).to(dev) for k, v in w.items()}
+        t["qblocked"] = mq.w4a16_block_weights(t["qweight"])
+        sets.append(t)
     xs, ys, wss = {}, {}, {}
     for M in GEMV_MS:
         x = synth.w4a16_inputs(M, GEMV_K, 8, GROUP, outlier_frac=0.005, tag=1, seed=M)["x"]
         xs[M] = torch.from_numpy(x).to(dev)
         ys[M] = torch.empty((M, GEMV_N), dtype=torch.float16, device=dev)
-        nbytes = mq.w4a16_gemv_workspace_bytes(M, GEMV_N, GEMV_K, GROUP)
+        nbytes = max(mq.w4a16_gemv_blocked_workspace_bytes(M, GEMV_N, GEMV_K, GROUP),
+                     mq.w4a16_gemv_workspace_bytes(M, GEMV_N, GEMV_K, GROUP))
         wss[M] = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     counter = [0]
 
-    def steps(n):
+    def steps(n, blocked):
         def run():
             for _ in range(n):
                 for M in GEMV_MS:
                     w = sets[counter[0] % len(sets)]
                     counter[0] += 1
-                    mq.w4a16_gemv(xs[M], w["qweight"], w["scales"], w["qzeros"], GROUP, out=ys[M],
-                                  workspace=wss[M])
+                    if blocked:
+                        mq.w4a16_gemv_blocked(xs[M], w["qblocked"], w["scales"], w["qzeros"], GROUP, out=ys[M],
+                                              workspace=wss[M])
+                    else:
+                        mq.w4a16_gemv(xs[M], w["qweight"], w["scales"], w["qzeros"], GROUP, out=ys[M],
+                                      workspace=wss[M])
         return run
 
-    log(f"capturing warmup ({args.warmup}) and timed ({args.steps}) steps")
-    g_warm = capture(torch, steps(max(args.warmup, 1)))
-    g_timed = capture(torch, steps(args.steps))
-    g_warm.replay()
-    torch.cuda.synchronize()
-    log("timed region")
-    wall, ev = timed_replay(torch, g_timed)
+    res = {}
+    for blocked in (True, False):
+        name = "blocked" if blocked else "awq"
+        log(f"{name}: capturing warmup ({args.warmup}) and timed ({args.steps}) steps")
+        g_warm = capture(torch, steps(max(args.warmup, 1), blocked))
+        g_timed = capture(torch, steps(args.steps, blocked))
+        g_warm.replay()
+        torch.cuda.synchronize()
+        log(f"{name}: timed region")
+        res[name] = timed_replay(torch, g_timed)
+        del g_warm, g_timed
+    wall, ev = res["blocked"]
     step_bytes = sum(w4a16_bytes(M, GEMV_K, GEMV_N) for M in GEMV_MS)
     launches = args.steps * len(GEMV_MS)
-    workspace_bytes = {M: mq.w4a16_gemv_workspace_bytes(M, GEMV_N, GEMV_K, GROUP) for M in GEMV_MS}
+    workspace_bytes = {M: mq.w4a16_gemv_blocked_workspace_bytes(M, GEMV_N, GEMV_K, GROUP) for M in GEMV_MS}
+    awq_wall, awq_ev = res["awq"]
     return {
         "wall_s": wall, "event_s": ev, "step_bytes": step_bytes, "launches": launches,
         "kernel_avg_us": ev / launches * 1e6, "workspace_bytes": workspace_bytes,
         "bytes_per_launch_avg": step_bytes / len(GEMV_MS),
+        "awq_layout": {"GBps": round(step_bytes / (awq_wall / args.steps) / 1e9, 1),
+                       "us_per_call": round(awq_ev / launches * 1e6, 3),
+                       "kernel": "w4a16_gemv_lds_kernel + w4a16_gemv_reduce (K split 8 ways)"},
     }, sets, xs
 
 
@@ -240,6 +261,7 @@ def bench_layers(torch, mq, synth, args, log):
         log(f"layers: {name} K={K} N={N}")
         w = synth.w4a16_weights(K, N, GROUP, tag=300 + li)
         w = {k: torch.from_numpy(v).to(dev) for k, v in w.items()}
+        w["qblocked"] = mq.w4a16_block_weights(w["qweight"])
         wsets = copies(w, K * N // 2)
         del w
         out["w4a16"][name] = {}
@@ -248,12 +270,12 @@ def bench_layers(torch, mq, synth, args, log):
                                                     seed=M)["x"]).to(dev)
             y = torch.empty((M, N), dtype=torch.float16, device=dev)
             if M <= mq.GEMV_MAX_M:
-                ws = torch.zeros(max(mq.w4a16_gemv_workspace_bytes(M, N, K, GROUP), 16), dtype=torch.uint8,
+                ws = torch.zeros(max(mq.w4a16_gemv_blocked_workspace_bytes(M, N, K, GROUP), 16), dtype=torch.uint8,
                                  device=dev)
 
                 def fn(r, x=x, y=y, ws=ws):
                     s = wsets[r % len(wsets)]
-                    mq.w4a16_gemv(x, s["qweight"], s["scales"], s["qzeros"], GROUP, out=y, workspace=ws)
+                    mq.w4a16_gemv_blocked(x, s["qblocked"], s["scales"], s["qzeros"], GROUP, out=y, workspace=ws)
             else:
                 def fn(r, x=x, y=y):
                     s = wsets[r % len(wsets)]
@@ -309,6 +331,7 @@ def bench_groups(torch, mq, synth, log):
         for name, K, N, Ms in shapes:
             log(f"groups: G={G} {name} K={K} N={N}")
             w = {k: torch.from_numpy(v).to(dev) for k, v in synth.w4a16_weights(K, N, G, tag=400 + G).items()}
+            w["qblocked"] = mq.w4a16_block_weights(w["qweight"])
             wbytes = K * N // 2
             n = max(2, -(-640 * 2**20 // wbytes))
             wsets = [w] + [{k: v.clone() for k, v in w.items()} for _ in range(n - 1)]
@@ -319,12 +342,12 @@ def bench_groups(torch, mq, synth, log):
                                                         tag=410 + G, seed=M)["x"]).to(dev)
                 y = torch.empty((M, N), dtype=torch.float16, device=dev)
                 if M <= mq.GEMV_MAX_M:
-                    ws = torch.zeros(max(mq.w4a16_gemv_workspace_bytes(M, N, K, G), 16), dtype=torch.uint8,
+                    ws = torch.zeros(max(mq.w4a16_gemv_blocked_workspace_bytes(M, N, K, G), 16), dtype=torch.uint8,
                                      device=dev)
 
                     def fn(r, x=x, y=y, ws=ws):
                         s = wsets[r % len(wsets)]
-                        mq.w4a16_gemv(x, s["qweight"], s["scales"], s["qzeros"], G, out=y, workspace=ws)
+                        mq.w4a16_gemv_blocked(x, s["qblocked"], s["scales"], s["qzeros"], G, out=y, workspace=ws)
                 else:
                     def fn(r, x=x, y=y):
                         s = wsets[r % len(wsets)]
@@ -433,7 +456,8 @@ def main(argv=None):
         "data": "synthetic",
         "config": {
             "workload": "W4A16 decode GEMV (8B MLP gate+up): M in {1,4,16}, K=4096, N=24576, group 128; "
-                        f"{args.sets} rotating weight sets (cold HBM); one step = one GEMV per M",
+                        f"{args.sets} rotating weight sets (cold HBM); one step = one GEMV per M; weights in the "
+                        "decode layout (converted once before timing)",
             "M": list(GEMV_MS), "K": GEMV_K, "N": GEMV_N, "group": GROUP, "weight_sets": args.sets,
             "gemv_workspace_bytes": res["workspace_bytes"], "parallelism": "single GPU",
         },
@@ -441,10 +465,11 @@ def main(argv=None):
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": load_traffic(res["bytes_per_launch_avg"]),
-            "kernel": "w4a16_gemv call (w4a16_gemv_lds_kernel + w4a16_gemv_reduce)",
+            "kernel": "w4a16_gemv_blocked_kernel (one launch per call; K is not split at N=24576)",
             "avg_launch_us": round(res["kernel_avg_us"], 3),
             "algorithmic_bytes_per_launch": res["bytes_per_launch_avg"],
         },
+        "gemv_awq_layout": res["awq_layout"],
     }
     if not args.no_prefill:
         line["prefill"] = bench_prefill(torch, mq, synth, mq.quant_per_token_int8, args, log)
