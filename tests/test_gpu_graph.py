@@ -103,3 +103,39 @@ def test_graph_replays_w8a8():
             assert np.array_equal(acc.cpu().numpy().astype(np.int64), oracle.w8a8_acc_ref(xq_ref, wq_np))
             assert_fp16_close(y.cpu().numpy(), oracle.w8a8_ref(xq_ref, s_ref, wq_np, s_ch_np),
                               f"graph w8a8 {name} replay {r}")
+
+
+def test_graph_replays_blocked():
+    # the layout conversion and the blocked GEMV (one launch; K split with a
+    # reduce launch; two-tile multi-strip workgroups) in one graph
+    import torch
+    K = 4096
+    for name, M, N, G in (("wide", 1, 24576, 128), ("split", 16, 4096, 128), ("tiles", 24, 3072, 64)):
+        d = synth.w4a16_inputs(M, K, N, group=G, outlier_frac=0.005, tag=700 + N)
+        qw = torch.from_numpy(d["qweight"]).cuda()
+        s = torch.from_numpy(d["scales"]).cuda()
+        z = torch.from_numpy(d["qzeros"]).cuda()
+        x = torch.from_numpy(d["x"]).cuda()
+        qb = torch.empty((K // 64, 8 * N), dtype=torch.int32, device="cuda")
+        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        ws = torch.empty(max(mq.w4a16_gemv_blocked_workspace_bytes(M, N, K, G), 16), dtype=torch.uint8,
+                         device="cuda")
+
+        def call(out_qb, out_y, x=x):
+            mq.w4a16_block_weights(qw, out=out_qb)
+            mq.w4a16_gemv_blocked(x, out_qb, s, z, G, out=out_y, workspace=ws)
+
+        announce(f"graph blocked {name} M={M} N={N} G={G}")
+        g = _capture(torch, lambda: call(qb, y))
+        rng = np.random.default_rng(13)
+        for r in range(REPLAYS):
+            xr = rng.standard_normal((M, K)).astype(np.float16)
+            x.copy_(torch.from_numpy(xr))
+            eb, ey = torch.empty_like(qb), torch.empty_like(y)
+            call(eb, ey)
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(qb, eb) and torch.equal(y, ey), f"{name}: replay {r} differs from the eager call"
+            assert np.array_equal(qb.cpu().numpy(), oracle.block_weights_ref(d["qweight"]))
+            ref = oracle.w4a16_ref(xr, d["qweight"], d["scales"], d["qzeros"], G)
+            assert_fp16_close(y.cpu().numpy(), ref, f"graph blocked {name} replay {r}")
