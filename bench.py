@@ -35,8 +35,10 @@ Also reported (same line):
   layers       the linear layers of an 8B-shaped decoder layer (qkv 4096->6144,
                o_proj 4096->4096, gate_up 4096->24576, down 12288->4096) at
                M = 1, 8, 64 and 2048 under W4A16 (decode-layout GEMV up to 64
-               tokens, GEMM above) and W8A8_INT8 (quantize + scaled GEMM): microseconds per
-               call with weights rotating over copies of >= 640 MB in all.
+               tokens, GEMM above) and W8A8_INT8 (mq_w8a8_linear: quantizer fused
+               into the decode kernel up to 16 tokens): microseconds per call with
+               weights rotating over copies of >= 640 MB per layer; `set` = the
+               four layers of a scheme in one graph, microseconds per layer set.
   groups       W4A16 with groups of 64 and 32 rows (LMDeploy quantizes the
                vision tower's attention with groups of 64): the gate+up GEMV
                (M = 1, 4, 16) in GB/s, a ViT-L fused qkv projection (K=1024,
@@ -239,12 +241,15 @@ def bench_prefill(torch, mq, synth, oracle_free_quant, args, log):
 
 def bench_layers(torch, mq, synth, args, log):
     """The linear layers of an 8B-shaped decoder layer at decode batches 1, 8, 64 and a
-    2048-token prefill, under W4A16 (GEMV for M <= 16, GEMM above) and W8A8_INT8
-    (quantize + scaled GEMM). Weights rotate over copies totalling >= 640 MB so every
-    call reads them from HBM; times are per call from event-timed graph replays."""
+    2048-token prefill, under W4A16 (decode-layout GEMV for M <= 64, GEMM above) and
+    W8A8_INT8 (mq_w8a8_linear: one fused kernel for M <= 16, quantize + scaled GEMM
+    above). Weights rotate over copies totalling >= 640 MB per layer so every call
+    reads them from HBM; times are per call from event-timed graph replays. `set` is
+    the four layers of one scheme captured together in one graph (qkv, o_proj,
+    gate_up, down in a row, as a decoder layer issues them)."""
     dev = torch.device("cuda", 0)
     R = 20
-    out = {"w4a16": {}, "w8a8": {}}
+    out = {"w4a16": {}, "w8a8": {}, "set": {"w4a16": {}, "w8a8": {}}}
 
     def time_calls(fn):
         g = capture(torch, lambda: [fn(r) for r in range(R)])
@@ -256,6 +261,8 @@ def bench_layers(torch, mq, synth, args, log):
         n = max(2, -(-640 * 2**20 // nbytes))
         return [tensors] + [{k: v.clone() for k, v in tensors.items()} for _ in range(n - 1)]
 
+    fns = {"w4a16": {}, "w8a8": {}}  # scheme -> M -> [per-layer fn]
+    keep = []
     for li, (name, shp) in enumerate(synth.LAYER_SET.items()):
         K, N = shp["K"], shp["N"]
         log(f"layers: {name} K={K} N={N}")
@@ -263,6 +270,7 @@ def bench_layers(torch, mq, synth, args, log):
         w = {k: torch.from_numpy(v).to(dev) for k, v in w.items()}
         w["qblocked"] = mq.w4a16_block_weights(w["qweight"])
         wsets = copies(w, K * N // 2)
+        keep.append(wsets)
         del w
         out["w4a16"][name] = {}
         for M in synth.LAYER_SET_MS:
@@ -273,41 +281,45 @@ def bench_layers(torch, mq, synth, args, log):
                 ws = torch.zeros(max(mq.w4a16_gemv_blocked_workspace_bytes(M, N, K, GROUP), 16), dtype=torch.uint8,
                                  device=dev)
 
-                def fn(r, x=x, y=y, ws=ws):
+                def fn(r, x=x, y=y, ws=ws, wsets=wsets):
                     s = wsets[r % len(wsets)]
                     mq.w4a16_gemv_blocked(x, s["qblocked"], s["scales"], s["qzeros"], GROUP, out=y, workspace=ws)
             else:
-                def fn(r, x=x, y=y):
+                def fn(r, x=x, y=y, wsets=wsets):
                     s = wsets[r % len(wsets)]
                     mq.w4a16_gemm(x, s["qweight"], s["scales"], s["qzeros"], GROUP, out=y)
+            fns["w4a16"].setdefault(M, []).append(fn)
             t = time_calls(fn)
             nbytes = w4a16_bytes(M, K, N)
             out["w4a16"][name][str(M)] = {"us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
                                           "TFLOPS": round(2.0 * M * N * K / t / 1e12, 1)}
-        del wsets
-        torch.cuda.empty_cache()
 
         d = synth.w8a8_inputs(8, K, N, outlier_frac=0.01, tag=320 + li)
         wq, s_ch = mq.quant_per_token_int8(torch.from_numpy(d["wf"]).to(dev))
         qsets = copies({"wq": wq, "s_ch": s_ch}, K * N)
+        keep.append(qsets)
         del wq, s_ch
         out["w8a8"][name] = {}
         for M in synth.LAYER_SET_MS:
             x = torch.from_numpy(synth.w8a8_inputs(M, K, 8, outlier_frac=0.01, tag=330 + li, seed=M)["x"]).to(dev)
-            xq = torch.empty((M, K), dtype=torch.int8, device=dev)
-            st = torch.empty((M,), dtype=torch.float32, device=dev)
             y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            ws = torch.empty(max(mq.w8a8_linear_workspace_bytes(M, K), 16), dtype=torch.uint8, device=dev)
 
-            def fn(r, x=x, xq=xq, st=st, y=y):
+            def fn(r, x=x, y=y, ws=ws, qsets=qsets):
                 s = qsets[r % len(qsets)]
-                mq.quant_per_token_int8(x, out=xq, s_out=st)
-                mq.w8a8_scaled_mm(xq, st, s["wq"], s["s_ch"], out=y)
+                mq.w8a8_linear(x, s["wq"], s["s_ch"], out=y, workspace=ws)
+            fns["w8a8"].setdefault(M, []).append(fn)
             t = time_calls(fn)
             nbytes = M * K * 2 + K * N + N * 4 + M * N * 2
             out["w8a8"][name][str(M)] = {"us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
                                          "TOPS": round(2.0 * M * N * K / t / 1e12, 1)}
-        del qsets
-        torch.cuda.empty_cache()
+    for scheme in ("w4a16", "w8a8"):
+        for M in synth.LAYER_SET_MS:
+            log(f"layers: {scheme} set M={M}")
+            t = time_calls(lambda r, fl=fns[scheme][M]: [f(r) for f in fl])
+            out["set"][scheme][str(M)] = round(t * 1e6, 2)
+    del fns, keep
+    torch.cuda.empty_cache()
     return out
 
 

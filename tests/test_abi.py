@@ -37,7 +37,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["mq_quant_per_token_int8", "mq_w8a8_scaled_mm", "mq_w8a8_mm_i32", "mq_w4a16_gemm",
               "mq_w4a16_gemv", "mq_w4a16_gemv_workspace_bytes", "mq_w4a16_block_weights",
-              "mq_w4a16_gemv_blocked", "mq_w4a16_gemv_blocked_workspace_bytes", "mq_abi_version",
+              "mq_w4a16_gemv_blocked", "mq_w4a16_gemv_blocked_workspace_bytes", "mq_w8a8_linear",
+              "mq_w8a8_linear_workspace_bytes", "mq_abi_version",
               "mq_status_string", "mq_last_error"]:
         assert n in names
 
@@ -173,6 +174,28 @@ def test_gemv_workspace_plan(lib):
             assert (K // group) % splits == 0
             if N % 32 == 0:
                 assert K // splits <= 1024
+
+
+def test_w8a8_linear_validation(lib):
+    f = lib.mq_w8a8_linear
+    ws = lib.mq_w8a8_linear_workspace_bytes
+    assert ws(1, 4096) == 0 and ws(1, 64) == 0 and ws(1, 81904) == 0  # fused: no workspace
+    assert ws(1, 81920) > 0                              # the fused codes must fit 80 KB of LDS
+    assert ws(2, 4096) >= 2 * 4096 + 2 * 4                # two kernels: codes + scales
+    assert ws(17, 4096) >= 17 * 4096 + 17 * 4
+    assert ws(17, 40) == 0                               # rejected shape (K % 16)
+    assert f(A, B, C, E, 4, 64, 40, None, 0, None) == SHAPE     # K % 16
+    assert f(A, B, C, E, 4, 64, 133152, None, 0, None) == SHAPE  # int32 accumulator bound
+    assert f(None, B, C, E, 4, 64, 64, None, 0, None) == NULL
+    assert f(A + 8, B, C, E, 4, 64, 64, None, 0, None) == ALIGN
+    assert f(A, B, C + 2, E, 4, 64, 64, None, 0, None) == ALIGN
+    assert f(A, B, C, A + 16, 1, 64, 64, None, 0, None) == ALIAS
+    need = ws(32, 64)
+    assert f(A, B, C, E, 32, 64, 64, None, 0, None) == WS
+    assert f(A, B, C, E, 32, 64, 64, F, need - 4, None) == WS
+    assert f(A, B, C, E, 32, 64, 64, F + 4, need, None) == ALIGN
+    assert f(A, B, C, E, 32, 64, 64, E, need, None) == ALIAS   # workspace over y
+    assert f(A, B, C, E, 0, 64, 64, None, 0, None) == OK
 
 
 def test_w4a16_blocked_validation(lib):

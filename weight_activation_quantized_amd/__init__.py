@@ -22,6 +22,7 @@ and two compositions used by a model's linear layer:
 
     w4a16_linear(x, qweight, scales, qzeros, group)  GEMV for M <= 64, else GEMM
     w8a8_linear(x, wq, s_ch)                         quantize x per token, then scaled GEMM
+                                                     (one fused kernel for M <= 16)
 """
 
 import ctypes
@@ -33,6 +34,7 @@ __all__ = [
     "w4a16_gemm", "w4a16_gemv", "w4a16_gemv_workspace_bytes",
     "w4a16_linear", "w8a8_linear", "GEMV_MAX_M",
     "w4a16_block_weights", "w4a16_gemv_blocked", "w4a16_gemv_blocked_workspace_bytes",
+    "w8a8_linear_workspace_bytes",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmq.so")
@@ -69,6 +71,8 @@ _PROTOTYPES = {
     "mq_w4a16_gemv_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I64]),
     "mq_w4a16_gemv": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
     "mq_w4a16_block_weights": (ctypes.c_int, [_P, _P, _I64, _I64, _P]),
+    "mq_w8a8_linear_workspace_bytes": (ctypes.c_size_t, [_I64, _I64]),
+    "mq_w8a8_linear": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
     "mq_w4a16_gemv_blocked_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I64]),
     "mq_w4a16_gemv_blocked": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t,
                                              _P]),
@@ -301,7 +305,30 @@ def w4a16_linear(x, qweight, scales, qzeros, group=128, out=None, stream=None):
     return w4a16_gemm(x, qweight, scales, qzeros, group, out=out, stream=stream)
 
 
-def w8a8_linear(x, wq, s_ch, out=None, stream=None):
-    """W8A8_INT8 linear layer: per-token int8 quantization of x, then the scaled int8 GEMM."""
-    xq, s_tok = quant_per_token_int8(x, stream=stream)
-    return w8a8_scaled_mm(xq, s_tok, wq, s_ch, out=out, stream=stream)
+def w8a8_linear_workspace_bytes(M, K):
+    """Workspace bytes ``w8a8_linear`` needs (0 for M <= 16)."""
+    return int(library().mq_w8a8_linear_workspace_bytes(M, K))
+
+
+def w8a8_linear(x, wq, s_ch, out=None, workspace=None, stream=None):
+    """W8A8_INT8 linear layer from fp16 x: per-token int8 quantization, then the
+    scaled int8 GEMM (one fused kernel for M <= 16). Bit-identical to
+    ``w8a8_scaled_mm(*quant_per_token_int8(x), wq, s_ch)``."""
+    torch = _torch()
+    _dev_tensor(x, "x", torch.float16, 2)
+    _dev_tensor(wq, "wq", torch.int8, 2)
+    _dev_tensor(s_ch, "s_ch", torch.float32, 1)
+    M, K = x.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K or s_ch.shape[0] != N:
+        raise ValueError("wq must be [N, K] and s_ch [N]")
+    y = _out(out, (M, N), torch.float16, x, "out")
+    need = w8a8_linear_workspace_bytes(M, K)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    with torch.cuda.device(x.device):
+        _check(library().mq_w8a8_linear(x.data_ptr(), wq.data_ptr(), s_ch.data_ptr(), y.data_ptr(), M, N, K,
+                                        ws_ptr, ws_bytes, _stream_of(x, stream)))
+    return y

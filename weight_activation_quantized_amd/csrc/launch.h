@@ -26,6 +26,17 @@ hipError_t launch_w8a8_gemv(const int8_t* xq, const float* s_tok, const int8_t* 
                             const float* s_ch, uint16_t* y, int32_t* acc,
                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+// Quantizer folded into the decode kernel: y = scaled_mm(quant(x), wq, s_ch)
+// in one launch, bit-identical to the two separate calls, where
+// w8a8_use_fused(M, K): 1 <= M <= kW8A8FusedMaxM and the M x K codes fit a
+// workgroup's 80 KB of LDS. Every workgroup forms all M rows' scales and
+// codes itself, so the fused form pays only for one token (measured: 2-3 us
+// faster per layer at M = 1, 8-20 us slower at M = 8).
+constexpr int64_t kW8A8FusedMaxM = 1;
+bool w8a8_use_fused(int64_t M, int64_t K);
+hipError_t launch_w8a8_gemv_fused(const uint16_t* x, const int8_t* wq, const float* s_ch, uint16_t* y,
+                                  int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 // W4A16 GEMM y[M,N] = x[M,K] . dequant(qweight, scales, qzeros), groups of
 // `group` rows (32, 64 or 128; K % 128 == 0).
 hipError_t launch_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,

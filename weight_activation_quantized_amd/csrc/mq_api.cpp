@@ -250,6 +250,50 @@ mq_status mq_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const uint16_
                     "w4a16_gemv launch");
 }
 
+size_t mq_w8a8_linear_workspace_bytes(int64_t M, int64_t K) {
+  if (M < 0 || M > kMaxDim || K < 16 || K > kMaxKInt8 || K % 16 || M * K > kMaxElems || M == 0 ||
+      mq::w8a8_use_fused(M, K))
+    return 0;
+  return (static_cast<size_t>(M * K) + 255) / 256 * 256 + static_cast<size_t>(M) * 4;
+}
+
+mq_status mq_w8a8_linear(const uint16_t* x, const int8_t* wq, const float* s_ch, uint16_t* y,
+                         int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  mq_status s = check_mk(M, K, 16, kMaxKInt8, 16);
+  if (s != MQ_OK) return s;
+  if (N < 0 || N > kMaxDim) return fail(MQ_ERR_SHAPE, "N=%lld out of range", (long long)N);
+  if (M * N > kMaxElems || K * N > kMaxElems) return fail(MQ_ERR_SHAPE, "problem too large");
+  MQ_TRY(need(x, M * K, "x"));
+  MQ_TRY(need(wq, N * K, "wq"));
+  MQ_TRY(need(s_ch, N, "s_ch"));
+  MQ_TRY(need(y, M * N, "y"));
+  if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(y, 16))
+    return fail(MQ_ERR_ALIGN, "x, wq and y must be 16-byte aligned");
+  if (!aligned(s_ch, 4)) return fail(MQ_ERR_ALIGN, "s_ch must be 4-byte aligned");
+  const size_t ws = mq_w8a8_linear_workspace_bytes(M, K);
+  if (ws > 0) {
+    if (!workspace || workspace_bytes < ws)
+      return fail(MQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws,
+                  workspace ? workspace_bytes : static_cast<size_t>(0));
+    if (!aligned(workspace, 16)) return fail(MQ_ERR_ALIGN, "workspace must be 16-byte aligned");
+  }
+  const Range in[] = {{x, static_cast<size_t>(M * K) * 2, "x"},
+                      {wq, static_cast<size_t>(N * K), "wq"},
+                      {s_ch, static_cast<size_t>(N) * 4, "s_ch"}};
+  const Range out[] = {{y, static_cast<size_t>(M * N) * 2, "y"}, {ws ? workspace : nullptr, ws, "workspace"}};
+  s = check_alias(in, out);
+  if (s != MQ_OK) return s;
+  if (M == 0 || N == 0) return ok();
+  if (mq::w8a8_use_fused(M, K))
+    return hip_status(mq::launch_w8a8_gemv_fused(x, wq, s_ch, y, M, N, K, as_stream(stream)), "w8a8_linear launch");
+  int8_t* xq = static_cast<int8_t*>(workspace);
+  float* s_tok = reinterpret_cast<float*>(static_cast<char*>(workspace) + (static_cast<size_t>(M * K) + 255) / 256 * 256);
+  s = hip_status(mq::launch_quant_per_token_int8(x, xq, s_tok, M, K, as_stream(stream)), "w8a8_linear quant launch");
+  if (s != MQ_OK) return s;
+  return hip_status(mq::launch_w8a8_gemm(xq, s_tok, wq, s_ch, y, nullptr, M, N, K, as_stream(stream)),
+                    "w8a8_linear gemm launch");
+}
+
 mq_status mq_w4a16_block_weights(const int32_t* qweight, int32_t* qweight_blocked, int64_t N, int64_t K,
                                  void* stream) {
   if (N < 0 || N > kMaxN4 || N % 32)

@@ -169,6 +169,149 @@ __global__ __launch_bounds__(256) void w8a8_gemv_kernel(const int8_t* __restrict
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fused decode layer for a single token (the kernel takes M <= 16; every
+// workgroup redoes the M rows' scales and codes, which pays only at M = 1):
+// per-token quantization folded into the weight-streaming kernel (pymllm Setup and Usage, "W8A8 first-run JIT
+// compilation": the quantizer feeds the scaled matmul). Every workgroup
+// first forms s[m] = fl32(absmax(x[m,:]) / 127) for the M rows (x is small
+// and L2-resident at these M), then quantizes the x fragments it streams:
+// q = clamp(rne(fl32(x / s)), -127, 127) with the IEEE binary32 division,
+// s = 0 giving q = 0. Codes, scales, accumulators and outputs are therefore
+// bit-identical to mq_quant_per_token_int8 followed by mq_w8a8_scaled_mm.
+// ---------------------------------------------------------------------------
+
+// Codes of the IEEE binary32 quotient v / s rounded half to even, for s > 0:
+// the product with r = rcp(s) decides every element farther than 2^-12 from
+// a half-integer (its error is below 3.1e-5 for quotients up to 127.5, the
+// correctly rounded quotient's below 3.9e-6), the IEEE division the rest.
+__device__ __forceinline__ float fused_code(float v, float s, float r) {
+  const float p = v * r;
+  const float t = rintf(p);
+  if (0.5f - fabsf(p - t) < 1.0f / 4096.0f) return rintf(v / s);
+  return t;
+}
+
+constexpr int kFusedLds = 80 * 1024;  // most bytes of codes a workgroup holds: M * (K + 16)
+
+// A workgroup owns 16 output channels and all M <= 16 tokens. Prologue: the
+// M per-token scales, then the codes of all M x K activations into LDS (row
+// pitch K + 16 bytes, so the 16 token rows of a fragment read fall on
+// different bank groups). Main loop: as w8a8_gemv_kernel, with the B
+// fragments read from LDS.
+__global__ __launch_bounds__(256) void w8a8_gemv_fused_kernel(const uint16_t* __restrict__ x,
+                                                              const int8_t* __restrict__ wq,
+                                                              const float* __restrict__ s_ch,
+                                                              uint16_t* __restrict__ y, int M, int N, int K) {
+  __shared__ int32_t part[kQuarters][16][16];
+  __shared__ float s_row[16];
+  extern __shared__ __attribute__((aligned(16))) int8_t codes[];  // M * (K + 16) bytes (launch)
+
+  const int n0 = static_cast<int>(blockIdx.x) * 16;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = lane & 15, h = lane >> 4;
+  const int pitch = K + 16;
+
+  // Per-token scales: wavefront w takes rows w, w + 4, ...
+  for (int m = wave; m < 16; m += kQuarters) {
+    float amax = 0.f;
+    if (m < M) {
+      const u32x4* row = reinterpret_cast<const u32x4*>(x + static_cast<size_t>(m) * K);
+      for (int c = lane; c < K / 8; c += 64) {
+        const u32x4 v = row[c];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const f16x2 hv = as_f16x2(v[w]);
+          amax = fmaxf(amax, fabsf(static_cast<float>(hv[0])));
+          amax = fmaxf(amax, fabsf(static_cast<float>(hv[1])));
+        }
+      }
+      amax = wave_max(amax);
+    }
+    if (lane == 0) s_row[m] = amax / 127.0f;  // IEEE binary32 division; rows >= M get 0
+  }
+  __syncthreads();
+  // Codes of every (m, 8-element chunk): 8 bytes to LDS per step.
+  for (int e = threadIdx.x; e < M * (K / 8); e += 256) {
+    const int m = e / (K / 8), c = e % (K / 8);
+    const float sm = s_row[m];
+    const u32x4 v = *reinterpret_cast<const u32x4*>(x + static_cast<size_t>(m) * K + 8 * c);
+    uint32_t packed[2] = {0u, 0u};
+    if (sm > 0.f) {
+      const float r = __builtin_amdgcn_rcpf(sm);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const f16x2 hv = as_f16x2(v[w]);
+        const float q0 = fminf(fmaxf(fused_code(static_cast<float>(hv[0]), sm, r), -127.f), 127.f);
+        const float q1 = fminf(fmaxf(fused_code(static_cast<float>(hv[1]), sm, r), -127.f), 127.f);
+        const uint32_t b = (static_cast<uint32_t>(static_cast<int32_t>(q0)) & 0xFFu) |
+                           ((static_cast<uint32_t>(static_cast<int32_t>(q1)) & 0xFFu) << 8);
+        packed[w >> 1] |= b << (16 * (w & 1));
+      }
+    }
+    *reinterpret_cast<u32x2*>(&codes[m * pitch + 8 * c]) = u32x2{packed[0], packed[1]};
+  }
+  __syncthreads();
+
+  Walk wk;
+  const int kq = (K / kQuarters + 63) / 64 * 64;
+  wk.k_begin = wave * kq;
+  wk.k_end = min(K, wk.k_begin + kq);
+  wk.n64 = (wk.k_end - wk.k_begin + 63) / 64;
+
+  const __amdgpu_buffer_rsrc_t rw = rsrc(wq + static_cast<size_t>(n0) * K, static_cast<int64_t>(min(16, N - n0)) * K);
+  const __amdgpu_buffer_rsrc_t rx = rsrc(x, 0);  // unused: the codes come from LDS
+  (void)rx;
+  const bool has_row = i < M;
+
+  i32x4 acc = i32x4{0, 0, 0, 0};
+  constexpr int kU = 8;
+  const int sets = (wk.n64 + kU - 1) / kU;
+  i32x4 wa[kU], wb[kU];
+  auto issue_w = [&](i32x4 (&w)[kU], int j0) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int kc = wk.chunk(j0 + u, h);
+      w[u] = __builtin_bit_cast(
+          i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, kc >= 0 ? static_cast<uint32_t>(i * K + kc) : kOob, 0, 0));
+    }
+  };
+  auto mma = [&](const i32x4 (&w)[kU], int j0) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int kc = wk.chunk(j0 + u, h);
+      i32x4 b = i32x4{0, 0, 0, 0};
+      if (has_row && kc >= 0) b = *reinterpret_cast<const i32x4*>(&codes[i * pitch + kc]);
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[u], b, acc, 0, 0, 0);
+    }
+  };
+  issue_w(wa, 0);
+  for (int st = 0; st < sets; st += 2) {
+    issue_w(wb, (st + 1) * kU);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(wa, st * kU);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_w(wa, (st + 2) * kU);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(wb, (st + 1) * kU);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // D[n][m]: lane (j, hh) register r holds channel 4 hh + r of token j.
+#pragma unroll
+  for (int r = 0; r < 4; ++r) part[wave][4 * h + r][i] = acc[r];
+  __syncthreads();
+  for (int e = threadIdx.x; e < 16 * 16; e += blockDim.x) {
+    const int nl = e % 16, m = e / 16;
+    const int n = n0 + nl;
+    if (m >= M || n >= N) continue;
+    const int32_t v = part[0][nl][m] + part[1][nl][m] + part[2][nl][m] + part[3][nl][m];
+    const float f = (static_cast<float>(v) * s_row[m]) * s_ch[n];
+    y[static_cast<size_t>(m) * N + n] = __builtin_bit_cast(uint16_t, static_cast<f16>(f));
+  }
+}
+
 template <bool kScaled, int kA, int kT>
 hipError_t launch_one(const int8_t* xq, const float* s_tok, const int8_t* wq, const float* s_ch, uint16_t* y,
                       int32_t* acc, int M, int N, int K, hipStream_t stream) {
@@ -199,6 +342,19 @@ bool w8a8_use_gemv(int64_t M, int64_t N) {
   // fill the chip and its smaller activation re-read wins.
   if (M <= 32) return true;
   return M <= kW8A8GemvMaxM && N < 16384;
+}
+
+bool w8a8_use_fused(int64_t M, int64_t K) {
+  return M >= 1 && M <= kW8A8FusedMaxM && M * (K + 16) <= kFusedLds;
+}
+
+hipError_t launch_w8a8_gemv_fused(const uint16_t* x, const int8_t* wq, const float* s_ch, uint16_t* y,
+                                  int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (!w8a8_use_fused(M, K)) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<uint32_t>((N + 15) / 16)), block(256);
+  const size_t lds = static_cast<size_t>(M * (K + 16));
+  return launch_kernel(w8a8_gemv_fused_kernel, grid, block, lds, stream, x, wq, s_ch, y, static_cast<int>(M),
+                       static_cast<int>(N), static_cast<int>(K));
 }
 
 hipError_t launch_w8a8_gemv(const int8_t* xq, const float* s_tok, const int8_t* wq,
