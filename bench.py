@@ -231,7 +231,9 @@ def bench_prefill(torch, mq, synth, oracle_free_quant, args, log):
         t = {k: torch.from_numpy(v).to(dev) for k, v in dd.items()}
         y = torch.empty((M, N), dtype=torch.float16, device=dev)
         log(f"prefill: {name}")
-        tg = time_fn(lambda: mq.w4a16_gemm(t["x"], t["qweight"], t["scales"], t["qzeros"], GROUP, out=y))
+        ws = torch.empty(max(mq.w4a16_gemm_workspace_bytes(M, N, K, GROUP), 16), dtype=torch.uint8, device=dev)
+        tg = time_fn(lambda: mq.w4a16_gemm(t["x"], t["qweight"], t["scales"], t["qzeros"], GROUP, out=y,
+                                           workspace=ws))
         ops = 2.0 * M * N * K
         out[name] = {"shape": [M, N, K], "gemm_us": tg * 1e6, "gemm_TFLOPS": ops / tg / 1e12,
                      "gemm_frac_fp16_peak": ops / tg / 1e12 / FP16_PEAK_TFLOPS}
@@ -285,9 +287,12 @@ def bench_layers(torch, mq, synth, args, log):
                     s = wsets[r % len(wsets)]
                     mq.w4a16_gemv_blocked(x, s["qblocked"], s["scales"], s["qzeros"], GROUP, out=y, workspace=ws)
             else:
-                def fn(r, x=x, y=y, wsets=wsets):
+                ws = torch.empty(max(mq.w4a16_gemm_workspace_bytes(M, N, K, GROUP), 16), dtype=torch.uint8,
+                                 device=dev)
+
+                def fn(r, x=x, y=y, wsets=wsets, ws=ws):
                     s = wsets[r % len(wsets)]
-                    mq.w4a16_gemm(x, s["qweight"], s["scales"], s["qzeros"], GROUP, out=y)
+                    mq.w4a16_gemm(x, s["qweight"], s["scales"], s["qzeros"], GROUP, out=y, workspace=ws)
             fns["w4a16"].setdefault(M, []).append(fn)
             t = time_calls(fn)
             nbytes = w4a16_bytes(M, K, N)
@@ -361,9 +366,12 @@ def bench_groups(torch, mq, synth, log):
                         s = wsets[r % len(wsets)]
                         mq.w4a16_gemv_blocked(x, s["qblocked"], s["scales"], s["qzeros"], G, out=y, workspace=ws)
                 else:
-                    def fn(r, x=x, y=y):
+                    ws = torch.empty(max(mq.w4a16_gemm_workspace_bytes(M, N, K, G), 16), dtype=torch.uint8,
+                                     device=dev)
+
+                    def fn(r, x=x, y=y, ws=ws):
                         s = wsets[r % len(wsets)]
-                        mq.w4a16_gemm(x, s["qweight"], s["scales"], s["qzeros"], G, out=y)
+                        mq.w4a16_gemm(x, s["qweight"], s["scales"], s["qzeros"], G, out=y, workspace=ws)
                 t = time_calls(fn)
                 nbytes = w4a16_bytes(M, K, N, G)
                 flops = 2.0 * M * N * K

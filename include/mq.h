@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MQ_ABI_VERSION 1
+#define MQ_ABI_VERSION 2
 
 typedef enum mq_status {
   MQ_OK = 0,
@@ -172,14 +172,24 @@ mq_status mq_w8a8_linear(const uint16_t* x, const int8_t* wq, const float* s_ch,
  *   scales   [K/G, N]   fp16   in
  *   qzeros   [K/G, N/8] int32  in   (unsigned 4-bit zero points, packed like qweight)
  *   y        [M, N]     fp16   out
+ *   workspace  optional (may be NULL). When the 64-token x 1024-output
+ *              tiles alone leave most CUs idle (fewer than 192 tiles), K is
+ *              split across workgroups if a workspace of at least
+ *              mq_w4a16_gemm_workspace_bytes(M, N, K, group) bytes is given:
+ *              fp32 partial sums go there and a second kernel on the same
+ *              stream adds them in split order (deterministic). NULL never
+ *              splits. 16-byte aligned, not overlapping any operand; calls
+ *              sharing it must be ordered.
  * Requires: group in {32, 64, 128} (anything else, -1 included ->
  * MQ_ERR_UNSUPPORTED); 0 <= M < 2^31; 8 <= N <= 2^27, N % 8 == 0;
  * 128 <= K <= 2^20, K % 128 == 0 (so K % group == 0); x, scales, y 16-byte
  * aligned; qweight, qzeros 4-byte aligned.
  */
+size_t mq_w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group);
 mq_status mq_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                         const int32_t* qzeros, uint16_t* y,
-                        int64_t M, int64_t N, int64_t K, int64_t group, void* stream);
+                        int64_t M, int64_t N, int64_t K, int64_t group,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Workspace size in bytes that mq_w4a16_gemv needs for this problem (0 when

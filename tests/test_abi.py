@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
     for n in ["mq_quant_per_token_int8", "mq_w8a8_scaled_mm", "mq_w8a8_mm_i32", "mq_w4a16_gemm",
               "mq_w4a16_gemv", "mq_w4a16_gemv_workspace_bytes", "mq_w4a16_block_weights",
               "mq_w4a16_gemv_blocked", "mq_w4a16_gemv_blocked_workspace_bytes", "mq_w8a8_linear",
-              "mq_w8a8_linear_workspace_bytes", "mq_abi_version",
+              "mq_w8a8_linear_workspace_bytes", "mq_w4a16_gemm_workspace_bytes", "mq_abi_version",
               "mq_status_string", "mq_last_error"]:
         assert n in names
 
@@ -53,7 +53,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.mq_abi_version() == 1
+    assert lib.mq_abi_version() == 2
     names = [lib.mq_status_string(i).decode() for i in range(8)]
     assert names == ["MQ_OK", "MQ_ERR_NULL", "MQ_ERR_SHAPE", "MQ_ERR_ALIGN", "MQ_ERR_UNSUPPORTED",
                      "MQ_ERR_WORKSPACE", "MQ_ERR_ALIAS", "MQ_ERR_HIP"]
@@ -92,10 +92,10 @@ def test_empty_problems_accept_null(lib):
     assert lib.mq_w8a8_scaled_mm(None, None, C, D, None, 0, 8, 64, None) == OK
     assert lib.mq_w8a8_scaled_mm(A, B, None, None, None, 4, 0, 64, None) == OK
     assert lib.mq_w8a8_mm_i32(None, B, None, 0, 8, 64, None) == OK
-    assert lib.mq_w4a16_gemm(None, B, C, D, None, 0, 64, 256, 128, None) == OK
+    assert lib.mq_w4a16_gemm(None, B, C, D, None, 0, 64, 256, 128, None, 0, None) == OK
     assert lib.mq_w4a16_gemv(None, B, C, D, None, 0, 64, 256, 128, None, 0, None) == OK
     # weights are never empty (N >= 8, K >= 128)
-    assert lib.mq_w4a16_gemm(None, None, C, D, None, 0, 64, 256, 128, None) == NULL
+    assert lib.mq_w4a16_gemm(None, None, C, D, None, 0, 64, 256, 128, None, 0, None) == NULL
 
 
 def test_w8a8_validation(lib):
@@ -119,22 +119,30 @@ def test_w8a8_validation(lib):
 
 def test_w4a16_gemm_validation(lib):
     g = lib.mq_w4a16_gemm
-    assert g(A, B, C, D, None, 4, 64, 256, 128, None) == NULL
+    assert g(A, B, C, D, None, 4, 64, 256, 128, None, 0, None) == NULL
     # groups of 32, 64 and 128 rows are provided; others (and -1, one group
     # over all of K) are not
     for group in (96, 256, 16, 0, -1):
-        assert g(A, B, C, D, E, 4, 64, 256, group, None) == UNSUP, group
-    assert g(A, B, C, D, E, 4, 64, 192, 64, None) == SHAPE      # K % 128, also for smaller groups
+        assert g(A, B, C, D, E, 4, 64, 256, group, None, 0, None) == UNSUP, group
+    assert g(A, B, C, D, E, 4, 64, 192, 64, None, 0, None) == SHAPE      # K % 128, also for smaller groups
     for group in (32, 64, 128):
-        assert g(A, B, C, D, E, 0, 64, 256, group, None) == OK
-    assert g(A, B, C, D, E, 4, 60, 256, 128, None) == SHAPE     # N % 8
-    assert g(A, B, C, D, E, 4, (1 << 27) + 8, 256, 128, None) == SHAPE
-    assert g(A, B, C, D, E, 4, 64, 200, 128, None) == SHAPE     # K % 128
-    assert g(A, B, C, D, E, 4, 64, 0, 128, None) == SHAPE
-    assert g(A + 8, B, C, D, E, 4, 64, 256, 128, None) == ALIGN
-    assert g(A, B + 2, C, D, E, 4, 64, 256, 128, None) == ALIGN
-    assert g(A, B, C, D, B + 16, 4, 64, 256, 128, None) == ALIAS
-    assert g(A, B, C, D, E, 0, 64, 256, 128, None) == OK
+        assert g(A, B, C, D, E, 0, 64, 256, group, None, 0, None) == OK
+    # the workspace is optional; given for a small grid it must be large enough
+    wsb = lib.mq_w4a16_gemm_workspace_bytes
+    assert wsb(4096, 4096, 4096, 128) == 0               # 256 tiles: never split
+    need = wsb(2048, 4096, 4096, 128)                     # 128 tiles: split
+    assert need > 0 and need % (4 * 2048 * 4096) == 0
+    assert g(A, B, C, D, E, 2048, 4096, 4096, 128, F, need - 4, None) == WS
+    assert g(A, B, C, D, E, 2048, 4096, 4096, 128, F + 4, need, None) == ALIGN
+    assert g(A, B, C, D, E, 2048, 4096, 4096, 128, E, need, None) == ALIAS
+    assert g(A, B, C, D, E, 4, 60, 256, 128, None, 0, None) == SHAPE     # N % 8
+    assert g(A, B, C, D, E, 4, (1 << 27) + 8, 256, 128, None, 0, None) == SHAPE
+    assert g(A, B, C, D, E, 4, 64, 200, 128, None, 0, None) == SHAPE     # K % 128
+    assert g(A, B, C, D, E, 4, 64, 0, 128, None, 0, None) == SHAPE
+    assert g(A + 8, B, C, D, E, 4, 64, 256, 128, None, 0, None) == ALIGN
+    assert g(A, B + 2, C, D, E, 4, 64, 256, 128, None, 0, None) == ALIGN
+    assert g(A, B, C, D, B + 16, 4, 64, 256, 128, None, 0, None) == ALIAS
+    assert g(A, B, C, D, E, 0, 64, 256, 128, None, 0, None) == OK
 
 
 def test_w4a16_gemv_validation(lib):

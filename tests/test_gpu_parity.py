@@ -283,3 +283,25 @@ def test_gemv_rejects_large_m():
     with pytest.raises(mq.MqError) as e:
         _run_w4(mq.w4a16_gemv, d, "M=65")
     assert e.value.status_name == "MQ_ERR_UNSUPPORTED"
+
+
+@pytest.mark.parametrize("M,K,N,G", [(2048, 4096, 4096, 128), (577, 1024, 3072, 64), (2048, 12288, 4096, 128),
+                                     (100, 4096, 1024, 128), (300, 1024, 1032, 32), (65, 2048, 264, 128)])
+def test_w4a16_gemm_split_k(M, K, N, G):
+    # small tile grids split K (fp32 partials, then the reduce kernel): the
+    # result matches the oracle, and the unsplit call (no workspace) within
+    # fp32 summation order
+    import torch
+    d = synth.w4a16_inputs(M, K, N, group=G, tag=M + K + N)
+    splits = mq.w4a16_gemm_workspace_bytes(M, N, K, G) // (4 * M * N)
+    announce(f"w4a16_gemm split K={K} M={M} N={N} G={G} splits={splits}")
+    args = (dev(d["x"]), dev(d["qweight"]), dev(d["scales"]), dev(d["qzeros"]), G)
+    y = host(mq.w4a16_gemm(*args))
+    ref = oracle.w4a16_ref(d["x"], d["qweight"], d["scales"], d["qzeros"], G)
+    assert_fp16_close(y, ref, f"gemm split M={M} K={K} N={N}")
+    y1 = host(mq.w4a16_gemm(*args, workspace=False))
+    assert_fp16_close(y1, ref, f"gemm unsplit M={M} K={K} N={N}")
+    if M in (2048, 577):
+        assert splits >= 2
+    y2 = host(mq.w4a16_gemm(*args))
+    assert np.array_equal(y.view(np.uint16), y2.view(np.uint16)), "split GEMM is not deterministic"

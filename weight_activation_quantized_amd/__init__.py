@@ -11,7 +11,8 @@ Entry points (same names as the C ABI, without the ``mq_`` prefix):
     quant_per_token_int8(x)                          -> (xq, s_tok)
     w8a8_scaled_mm(xq, s_tok, wq, s_ch)              -> y  (fp16)
     w8a8_mm_i32(xq, wq)                              -> acc (int32)
-    w4a16_gemm(x, qweight, scales, qzeros, group)    -> y  (fp16)
+    w4a16_gemm(x, qweight, scales, qzeros, group)    -> y  (fp16); K split on small grids
+    w4a16_gemm_workspace_bytes(M, N, K, group)       -> int
     w4a16_gemv(x, qweight, scales, qzeros, group)    -> y  (fp16), M <= 64
     w4a16_gemv_workspace_bytes(M, N, K, group)       -> int
     w4a16_block_weights(qweight)                     -> qweight_blocked (decode layout, once per matrix)
@@ -34,7 +35,7 @@ __all__ = [
     "w4a16_gemm", "w4a16_gemv", "w4a16_gemv_workspace_bytes",
     "w4a16_linear", "w8a8_linear", "GEMV_MAX_M",
     "w4a16_block_weights", "w4a16_gemv_blocked", "w4a16_gemv_blocked_workspace_bytes",
-    "w8a8_linear_workspace_bytes",
+    "w8a8_linear_workspace_bytes", "w4a16_gemm_workspace_bytes",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmq.so")
@@ -67,7 +68,8 @@ _PROTOTYPES = {
     "mq_quant_per_token_int8": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "mq_w8a8_scaled_mm": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "mq_w8a8_mm_i32": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P]),
-    "mq_w4a16_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
+    "mq_w4a16_gemm_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I64]),
+    "mq_w4a16_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
     "mq_w4a16_gemv_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I64]),
     "mq_w4a16_gemv": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
     "mq_w4a16_block_weights": (ctypes.c_int, [_P, _P, _I64, _I64, _P]),
@@ -206,14 +208,31 @@ def _w4a16_shapes(x, qweight, scales, qzeros, group):
     return M, N, K
 
 
-def w4a16_gemm(x, qweight, scales, qzeros, group=128, out=None, stream=None):
-    """W4A16 GEMM: y[M, N] fp16 = x[M, K] . dequant(qweight, scales, qzeros)."""
+def w4a16_gemm_workspace_bytes(M, N, K, group=128):
+    """Workspace bytes that let ``w4a16_gemm`` split K on small tile grids (0: never splits)."""
+    return int(library().mq_w4a16_gemm_workspace_bytes(M, N, K, group))
+
+
+def w4a16_gemm(x, qweight, scales, qzeros, group=128, out=None, workspace=None, stream=None):
+    """W4A16 GEMM: y[M, N] fp16 = x[M, K] . dequant(qweight, scales, qzeros).
+
+    ``workspace``: a uint8 GPU tensor of at least ``w4a16_gemm_workspace_bytes``
+    bytes (allocated if None and the shape splits K); ``False`` never splits.
+    """
     torch = _torch()
     M, N, K = _w4a16_shapes(x, qweight, scales, qzeros, group)
     y = _out(out, (M, N), torch.float16, x, "out")
+    if workspace is False:
+        workspace = None
+    elif workspace is None:
+        need = w4a16_gemm_workspace_bytes(M, N, K, group) if M else 0
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     with torch.cuda.device(x.device):
         _check(library().mq_w4a16_gemm(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), qzeros.data_ptr(),
-                                       y.data_ptr(), M, N, K, group, _stream_of(x, stream)))
+                                       y.data_ptr(), M, N, K, group, ws_ptr, ws_bytes, _stream_of(x, stream)))
     return y
 
 

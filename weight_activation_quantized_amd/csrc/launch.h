@@ -38,10 +38,15 @@ hipError_t launch_w8a8_gemv_fused(const uint16_t* x, const int8_t* wq, const flo
                                   int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 // W4A16 GEMM y[M,N] = x[M,K] . dequant(qweight, scales, qzeros), groups of
-// `group` rows (32, 64 or 128; K % 128 == 0).
+// `group` rows (32, 64 or 128; K % 128 == 0). With a workspace of
+// w4a16_gemm_workspace(M, N, K) bytes, K is split w4a16_gemm_splits ways
+// when the tiles alone leave most CUs idle (fp32 partials, then a reduce
+// kernel); a NULL workspace never splits.
+int w4a16_gemm_splits(int64_t M, int64_t N, int64_t K);
+size_t w4a16_gemm_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t launch_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                              const int32_t* qzeros, uint16_t* y,
-                             int64_t M, int64_t N, int64_t K, int64_t group, hipStream_t stream);
+                             int64_t M, int64_t N, int64_t K, int64_t group, void* workspace, hipStream_t stream);
 
 // Largest token count the W4A16 GEMV takes (four 16-token MFMA tiles).
 constexpr int64_t kGemvMaxM = 64;

@@ -203,13 +203,41 @@ mq_status mq_w8a8_mm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc,
                     "w8a8_mm_i32 launch");
 }
 
+size_t mq_w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group) {
+  if ((group != 32 && group != 64 && group != 128) || M < 1 || M > kMaxDim || N < 8 || N % 8 || N > kMaxN4 ||
+      K < 128 || K > kMaxK || K % 128 || M * N > kMaxElems)
+    return 0;
+  return mq::w4a16_gemm_workspace(M, N, K);
+}
+
 mq_status mq_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                         const int32_t* qzeros, uint16_t* y,
-                        int64_t M, int64_t N, int64_t K, int64_t group, void* stream) {
+                        int64_t M, int64_t N, int64_t K, int64_t group,
+                        void* workspace, size_t workspace_bytes, void* stream) {
   mq_status s = check_w4a16(x, qweight, scales, qzeros, y, M, N, K, group);
   if (s != MQ_OK) return s;
   if (M == 0) return ok();
-  return hip_status(mq::launch_w4a16_gemm(x, qweight, scales, qzeros, y, M, N, K, group, as_stream(stream)),
+  // A workspace is optional: given (large enough for the split plan), K may
+  // be split for small tile grids; NULL never splits.
+  void* ws = nullptr;
+  if (workspace != nullptr) {
+    const size_t need = mq::w4a16_gemm_workspace(M, N, K);
+    if (need > 0) {
+      if (workspace_bytes < need)
+        return fail(MQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+      if (!aligned(workspace, 16)) return fail(MQ_ERR_ALIGN, "workspace must be 16-byte aligned");
+      const size_t G = static_cast<size_t>(K / group);
+      const Range in[] = {{x, static_cast<size_t>(M * K) * 2, "x"},
+                          {qweight, static_cast<size_t>(K * (N / 8)) * 4, "qweight"},
+                          {scales, G * static_cast<size_t>(N) * 2, "scales"},
+                          {qzeros, G * static_cast<size_t>(N / 8) * 4, "qzeros"}};
+      const Range out[] = {{y, static_cast<size_t>(M * N) * 2, "y"}, {workspace, need, "workspace"}};
+      s = check_alias(in, out);
+      if (s != MQ_OK) return s;
+      ws = workspace;
+    }
+  }
+  return hip_status(mq::launch_w4a16_gemm(x, qweight, scales, qzeros, y, M, N, K, group, ws, as_stream(stream)),
                     "w4a16_gemm launch");
 }
 

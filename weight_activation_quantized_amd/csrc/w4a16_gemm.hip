@@ -127,22 +127,31 @@ __device__ __forceinline__ void unpack_fields(const uint32_t (&w)[8], const Grou
 }
 
 // kSPG = 32-row stages per group (group size 32 kSPG).
+// With splits > 1 the workgroup takes K range `split` of `splits` equal
+// ranges and writes fp32 partial sums to partial[split, M, N] (a second
+// kernel adds them in split order); with splits == 1 it writes y.
 template <int kSPG>
 __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __restrict__ x,
                                                          const uint32_t* __restrict__ qw,
                                                          const uint16_t* __restrict__ scales,
                                                          const uint32_t* __restrict__ qz,
-                                                         uint16_t* __restrict__ y, int M, int N, int K,
-                                                         int tiles_m, int tiles_n, int per_xcd) {
+                                                         uint16_t* __restrict__ y, float* __restrict__ partial,
+                                                         int M, int N, int K, int tiles_m, int tiles_n,
+                                                         int per_xcd, int splits) {
   __shared__ __attribute__((aligned(1024))) int8_t smem[kStages * kSlotBytes];
   lds_i8* const sm = (lds_i8*)(smem);
 
   // Tile of this workgroup: each XCD takes a contiguous run of tiles, token
   // tiles fastest, so its workgroups share weight tiles.
-  const int t_id = static_cast<int>(blockIdx.x & 7) * per_xcd + static_cast<int>(blockIdx.x >> 3);
-  if (t_id >= tiles_m * tiles_n) return;
+  const int w_id = static_cast<int>(blockIdx.x & 7) * per_xcd + static_cast<int>(blockIdx.x >> 3);
+  const int tiles = tiles_m * tiles_n;
+  if (w_id >= tiles * splits) return;
+  const int split = w_id / tiles;
+  const int t_id = w_id % tiles;
   const int m0 = (t_id % tiles_m) * kBM;
   const int c0 = (t_id / tiles_m) * kTileCols;  // first packed column
+  const int k_len = K / splits;                 // multiple of 128 (host plan)
+  const int k_base = split * k_len;
   constexpr int kGS = kSPG * kRows;  // rows per group
   static_assert(4 % kSPG == 0, "a group is 1, 2 or 4 stages");
   const int NP = N >> 3;
@@ -180,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
 
 #define MQ_ISSUE(ST, SZ)                                                                             \
   do {                                                                                               \
-    const int k0_ = (ST) * kRows;                                                                    \
+    const int k0_ = k_base + (ST) * kRows;                                                           \
     const int g_ = k0_ / kGS;                                                                        \
     const int so_ = ((ST) % kStages) * kSlotBytes;                                                   \
     const __amdgpu_buffer_rsrc_t rw_ =                                                               \
@@ -237,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[a][q] = f32x16{};
 
-  const int nst = K / kRows;
+  const int nst = k_len / kRows;
 
   // Operands of one 16-row k-step: the two x fragments and the four
   // dequantized weight fragments.
@@ -378,9 +387,39 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
   // Epilogue. D[m][j] of a 32x32 tile: lane (jj, hh) register r holds token
   // 8 (r / 4) + 4 hh + r % 4 of B column jj, i.e. output 8 (16 w + jj % 16)
   // + 2 q + jj / 16 of the tile. The tile is staged in LDS as fp16 and
-  // written out as whole rows with 16-byte stores.
+  // written out as whole rows with 16-byte stores (fp32 partial sums: two
+  // halves of 32 rows, staged and written the same way).
   wait_counts<0, 0>();
   bare_barrier();  // every wave is done reading the ring
+  if (splits > 1) {
+    constexpr int kPitch32 = kTileCols * 8 * 4 + 16;  // bytes per staged fp32 row
+    static_assert(32 * kPitch32 <= kStages * kSlotBytes, "fp32 half tile fits the ring");
+    const int jj = lane & 31, hh = lane >> 5;
+    const int ncol = 8 * (kWaveCols * wave + (jj & 15)) + (jj >> 4);
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lr = 8 * (r / 4) + 4 * hh + (r % 4);
+        lds_i8* const row = sm + lr * kPitch32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) *(__attribute__((address_space(3))) float*)(row + 4 * (ncol + 2 * q)) = acc[a][q][r];
+      }
+      wait_counts<0, 0>();
+      bare_barrier();
+      constexpr int kPieces32 = kTileCols * 2;  // 16-byte pieces (4 outputs) per row
+      for (int i = threadIdx.x; i < 32 * kPieces32; i += kThreads) {
+        const int lr = i / kPieces32, pc = i % kPieces32;
+        const int m = m0 + 32 * a + lr, c = c0 + pc / 2;
+        if (m >= M || c >= NP) continue;
+        *reinterpret_cast<u32x4*>(partial + (static_cast<size_t>(split) * M + m) * N + 8 * c0 + 4 * pc) =
+            *(const lds_u32x4*)(sm + lr * kPitch32 + 16 * pc);
+      }
+      wait_counts<0, 0>();
+      bare_barrier();  // the next half reuses the staging rows
+    }
+    return;
+  }
   {
     const int jj = lane & 31, hh = lane >> 5;
     const int ncol = 8 * (kWaveCols * wave + (jj & 15)) + (jj >> 4);
@@ -409,31 +448,81 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
   }
 }
 
+
+// Adds the splits' fp32 partial sums in split order and rounds to fp16;
+// one thread per 4 outputs.
+__global__ __launch_bounds__(256) void w4a16_gemm_reduce(const float* __restrict__ partial,
+                                                         uint16_t* __restrict__ y, int64_t mn4, int splits) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= mn4) return;
+  const size_t stride = static_cast<size_t>(mn4) * 4;
+  const float* src = partial + static_cast<size_t>(t) * 4;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(src);
+  for (int sp = 1; sp < splits; ++sp) acc += *reinterpret_cast<const f32x4*>(src + sp * stride);
+  f16x2 lo, hi;
+  lo[0] = static_cast<f16>(acc[0]);
+  lo[1] = static_cast<f16>(acc[1]);
+  hi[0] = static_cast<f16>(acc[2]);
+  hi[1] = static_cast<f16>(acc[3]);
+  *reinterpret_cast<u32x2*>(y + static_cast<size_t>(t) * 4) = u32x2{as_u32(lo), as_u32(hi)};
+}
+
 }  // namespace
+
+int w4a16_gemm_splits(int64_t M, int64_t N, int64_t K) {
+  // Split K only when the tiles leave most CUs idle: the smallest divisor of
+  // K/128 that gives >= 256 workgroups, keeping >= 512 rows (16 stages) per
+  // split and at most 8 splits.
+  const int64_t tiles = ((M + kBM - 1) / kBM) * ((N / 8 + kTileCols - 1) / kTileCols);
+  if (tiles >= 192) return 1;
+  const int64_t chunks = K / 128;
+  int best = 1;
+  for (int64_t s = 2; s <= 8 && K / s >= 512; ++s) {
+    if (chunks % s) continue;
+    best = static_cast<int>(s);
+    if (tiles * s >= 256) break;
+  }
+  return best;
+}
+
+size_t w4a16_gemm_workspace(int64_t M, int64_t N, int64_t K) {
+  const int s = w4a16_gemm_splits(M, N, K);
+  return s > 1 ? static_cast<size_t>(s) * M * N * sizeof(float) : 0;
+}
 
 hipError_t launch_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                              const int32_t* qzeros, uint16_t* y,
-                             int64_t M, int64_t N, int64_t K, int64_t group, hipStream_t stream) {
+                             int64_t M, int64_t N, int64_t K, int64_t group, void* workspace, hipStream_t stream) {
   if (K % 128 || (group != 32 && group != 64 && group != 128)) return hipErrorInvalidValue;
+  const int splits = workspace ? w4a16_gemm_splits(M, N, K) : 1;
   const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
   const int tiles_n = static_cast<int>((N / 8 + kTileCols - 1) / kTileCols);
-  const int64_t tiles = static_cast<int64_t>(tiles_m) * tiles_n;
-  const int per_xcd = static_cast<int>((tiles + 7) / 8);
+  const int64_t work = static_cast<int64_t>(tiles_m) * tiles_n * splits;
+  const int per_xcd = static_cast<int>((work + 7) / 8);
   const dim3 grid(static_cast<uint32_t>(8 * per_xcd));
   const uint32_t* qw = reinterpret_cast<const uint32_t*>(qweight);
   const uint32_t* qz = reinterpret_cast<const uint32_t*>(qzeros);
+  float* part = static_cast<float*>(workspace);
   const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+  hipError_t err;
   switch (group) {
     case 32:
-      return launch_kernel(w4a16_gemm_kernel<1>, grid, dim3(kThreads), 0, stream, x, qw, scales, qz, y, m, n, k,
-                           tiles_m, tiles_n, per_xcd);
+      err = launch_kernel(w4a16_gemm_kernel<1>, grid, dim3(kThreads), 0, stream, x, qw, scales, qz, y, part, m, n, k,
+                          tiles_m, tiles_n, per_xcd, splits);
+      break;
     case 64:
-      return launch_kernel(w4a16_gemm_kernel<2>, grid, dim3(kThreads), 0, stream, x, qw, scales, qz, y, m, n, k,
-                           tiles_m, tiles_n, per_xcd);
+      err = launch_kernel(w4a16_gemm_kernel<2>, grid, dim3(kThreads), 0, stream, x, qw, scales, qz, y, part, m, n, k,
+                          tiles_m, tiles_n, per_xcd, splits);
+      break;
     default:
-      return launch_kernel(w4a16_gemm_kernel<4>, grid, dim3(kThreads), 0, stream, x, qw, scales, qz, y, m, n, k,
-                           tiles_m, tiles_n, per_xcd);
+      err = launch_kernel(w4a16_gemm_kernel<4>, grid, dim3(kThreads), 0, stream, x, qw, scales, qz, y, part, m, n, k,
+                          tiles_m, tiles_n, per_xcd, splits);
+      break;
   }
+  if (err != hipSuccess || splits == 1) return err;
+  const int64_t mn4 = M * N / 4;
+  return launch_kernel(w4a16_gemm_reduce, dim3(static_cast<uint32_t>((mn4 + 255) / 256)), dim3(256), 0, stream,
+                       part, y, mn4, splits);
 }
 
 }  // namespace mq
