@@ -211,8 +211,8 @@ __device__ __forceinline__ void compute_chunk(const BChunk<kT, kBChunkRows / kGS
 
 // kT 16-token tiles, groups of kGS rows, kW wavefronts per workgroup, kSP
 // adjacent strips per workgroup (they share every x fragment a wavefront
-// loads), kD chunks in flight per wavefront. `units` counts kSP-strip units.
-template <int kT, int kGS, int kW, int kSP, int kD = 2>
+// loads). `units` counts kSP-strip units.
+template <int kT, int kGS, int kW, int kSP>
 __global__ __launch_bounds__(kW * 64) void w4a16_gemv_blocked_kernel(
     const uint16_t* __restrict__ x, const u32x4* __restrict__ qb, const uint16_t* __restrict__ scales,
     const uint32_t* __restrict__ qz, uint16_t* __restrict__ y, float* __restrict__ partial, int M, int N, int K,
@@ -262,29 +262,35 @@ __global__ __launch_bounds__(kW * 64) void w4a16_gemv_blocked_kernel(
 #pragma unroll
       for (int f = 0; f < 2; ++f) tot[t][sp][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // kD chunks in flight per wavefront (a ring of register buffers, the loop
-  // unrolled over the ring): a buffer's next chunk is requested as soon as
-  // the buffer has been consumed; sched_barrier keeps each request ahead of
-  // the math it is meant to overlap. Every request is unconditional: past
-  // the wavefront's last chunk it repeats that chunk (an L2 hit, never
-  // used). A conditional request makes the compiler copy the buffer at the
-  // loop's back edge, which waits for every load in flight. Two chunks
-  // (4 KB per wavefront) measured best: four were slower (the repeated
-  // tail requests and one fewer wavefront per SIMD cost more than the depth
-  // gains).
+  // Two chunks in flight per wavefront: a buffer's next chunk is requested
+  // as soon as the buffer has been consumed; sched_barrier keeps each
+  // request ahead of the math it is meant to overlap. The steady loop only
+  // runs while both of its requests are in range, so they are
+  // unconditional (a conditional request inside the loop makes the compiler
+  // copy the buffer at the back edge, which waits for every load in
+  // flight); the last two or three chunks are finished after the loop with
+  // at most one more request. No chunk is requested twice (except when a
+  // wavefront has a single chunk). More in flight per wavefront measured
+  // slower (see the layout notes).
   {
-    const int last = c0 + cpw - 1;
-    BChunk<kT, kGPC, kSP> cb[kD];
-#pragma unroll
-    for (int d = 0; d < kD; ++d) load_chunk<kT, kGS, kSP>(cb[d], L, min(c0 + d, last));
-    for (int i = 0; i < cpw; i += kD) {
-#pragma unroll
-      for (int d = 0; d < kD; ++d) {
-        if (i + d < cpw) compute_chunk<kT, kGS, kSP>(cb[d], nc, ones, g, tot);
-        load_chunk<kT, kGS, kSP>(cb[d], L, min(c0 + i + d + kD, last));
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    BChunk<kT, kGPC, kSP> ca, cb;
+    load_chunk<kT, kGS, kSP>(ca, L, c0);
+    load_chunk<kT, kGS, kSP>(cb, L, min(c0 + 1, c0 + cpw - 1));
+    int i = 0;
+    for (; i + 3 < cpw; i += 2) {
+      compute_chunk<kT, kGS, kSP>(ca, nc, ones, g, tot);
+      load_chunk<kT, kGS, kSP>(ca, L, c0 + i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_chunk<kT, kGS, kSP>(cb, nc, ones, g, tot);
+      load_chunk<kT, kGS, kSP>(cb, L, c0 + i + 3);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // chunks i and (if in range) i + 1 are in flight; at most i + 2 is left
+    compute_chunk<kT, kGS, kSP>(ca, nc, ones, g, tot);
+    if (i + 2 < cpw) load_chunk<kT, kGS, kSP>(ca, L, c0 + i + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 1 < cpw) compute_chunk<kT, kGS, kSP>(cb, nc, ones, g, tot);
+    if (i + 2 < cpw) compute_chunk<kT, kGS, kSP>(ca, nc, ones, g, tot);
   }
 
   // Add the wavefronts' sums in wavefront order. Lane (j, h) holds token
@@ -335,19 +341,27 @@ template <int kGS>
 hipError_t launch_blocked_group(const uint16_t* x, const u32x4* qb, const uint16_t* scales, const uint32_t* qz,
                                 uint16_t* y, float* part, int m, int n, int k, const GemvPlan& plan, int units,
                                 XcdMap map, dim3 grid, hipStream_t stream) {
-  if (m <= 16) {
-    switch (plan.strips_per_unit) {
-      case 3:
-        return launch_blocked_main<1, kGS, 3>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
-      case 2:
-        return launch_blocked_main<1, kGS, 2>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
-      default:
-        return launch_blocked_main<1, kGS, 1>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+  if constexpr (kGS == 32) {
+    // groups of 32: one strip per workgroup (the multi-strip forms do not
+    // fit the register file with four groups per chunk)
+    if (m <= 16)
+      return launch_blocked_main<1, kGS, 1>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+    return launch_blocked_main<2, kGS, 1>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+  } else {
+    if (m <= 16) {
+      switch (plan.strips_per_unit) {
+        case 3:
+          return launch_blocked_main<1, kGS, 3>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+        case 2:
+          return launch_blocked_main<1, kGS, 2>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+        default:
+          return launch_blocked_main<1, kGS, 1>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+      }
     }
+    if (plan.strips_per_unit == 2)
+      return launch_blocked_main<2, kGS, 2>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+    return launch_blocked_main<2, kGS, 1>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
   }
-  if (plan.strips_per_unit == 2)
-    return launch_blocked_main<2, kGS, 2>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
-  return launch_blocked_main<2, kGS, 1>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
 }
 
 }  // namespace
@@ -364,7 +378,7 @@ GemvPlan plan_w4a16_gemv_blocked(int64_t M, int64_t N, int64_t K, int64_t group)
   // tokens a workgroup takes several adjacent strips that share those loads
   // (three for one 16-token tile, two for two; what divides the strips).
   int sp = 1;
-  if (mt > 4) {
+  if (mt > 4 && group >= 64) {
     if (mt <= 16 && strips % 3 == 0) {
       sp = 3;
     } else if (strips % 2 == 0) {

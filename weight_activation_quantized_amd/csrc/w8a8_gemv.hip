@@ -261,8 +261,6 @@ __global__ __launch_bounds__(256) void w8a8_gemv_fused_kernel(const uint16_t* __
   wk.n64 = (wk.k_end - wk.k_begin + 63) / 64;
 
   const __amdgpu_buffer_rsrc_t rw = rsrc(wq + static_cast<size_t>(n0) * K, static_cast<int64_t>(min(16, N - n0)) * K);
-  const __amdgpu_buffer_rsrc_t rx = rsrc(x, 0);  // unused: the codes come from LDS
-  (void)rx;
   const bool has_row = i < M;
 
   i32x4 acc = i32x4{0, 0, 0, 0};
