@@ -212,8 +212,12 @@ __device__ __forceinline__ void compute_chunk(const BChunk<kT, kBChunkRows / kGS
 // kT 16-token tiles, groups of kGS rows, kW wavefronts per workgroup, kSP
 // adjacent strips per workgroup (they share every x fragment a wavefront
 // loads). `units` counts kSP-strip units.
+// Three wavefronts per SIMD for the one-strip, one-tile forms with groups of
+// 64 or 128: a 24576-wide layer has three such workgroups per CU, and all of
+// them must be resident at once for every CU to stream an equal share.
 template <int kT, int kGS, int kW, int kSP>
-__global__ __launch_bounds__(kW * 64) void w4a16_gemv_blocked_kernel(
+__global__ __launch_bounds__(kW * 64)
+__attribute__((amdgpu_waves_per_eu(kT == 1 && kSP == 1 && kGS >= 64 ? 3 : 1))) void w4a16_gemv_blocked_kernel(
     const uint16_t* __restrict__ x, const u32x4* __restrict__ qb, const uint16_t* __restrict__ scales,
     const uint32_t* __restrict__ qz, uint16_t* __restrict__ y, float* __restrict__ partial, int M, int N, int K,
     int units, int splits, XcdMap map) {
