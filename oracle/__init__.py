@@ -34,6 +34,8 @@ from .ref import (  # noqa: F401
     NIBBLES_PER_WORD,
     block_weights_ref,
     dequant_w4,
+    kv_dequant_ref,
+    kv_quant_ref,
     quant_per_token_int8_ref,
     unpack_int4,
     w4a16_ref,

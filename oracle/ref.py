@@ -9,8 +9,10 @@ Sources (pages; each function cites the passage it follows):
 * [pymllm-setup]  "pymllm Setup and Usage" -- Overview (BF16, W4A16 and
   W8A8_INT8 schemes; INT8 tensor-core compute), section "W8A8 first-run JIT
   compilation" (per-token int8 activation quantizer; int8 scaled matmul).
-* [lmdeploy-ovw]  LMDeploy toolkit overview (devpress) -- section 2.5
-  "Weight quantization (AWQ)" (4-bit weights, group size 128).
+* [lmdeploy-ovw]  LMDeploy toolkit overview (devpress) -- section 2.4
+  "KV Cache online quantization" (per-head per-token asymmetric INT8/INT4,
+  min/max computed online) and section 2.5 "Weight quantization (AWQ)"
+  (4-bit weights, group size 128).
 * [lmdeploy-hw]   "LMDeploy multimodal LLM 4-bit quantization deployment
   guide" (mlqm) -- section 2.2 (AWQ w4a16; scale and weight consumed in one
   kernel), section 3.2 (per-layer bits / group_size, -1 = no grouping).
@@ -200,3 +202,60 @@ def w8a8_ref(xq, s_tok, wq, s_ch):
     st = np.asarray(s_tok).astype(np.float64)
     sc = np.asarray(s_ch).astype(np.float64)
     return acc * st[:, None] * sc[None, :]
+
+
+def kv_quant_ref(x, bits):
+    """Online KV-cache quantization of one head's vector per token.
+
+    [lmdeploy-ovw] section 2.4: the fp16 KV cache is quantized per head and
+    per token, asymmetrically, to INT8 or INT4, with min/max scale factors
+    computed online (no calibration). Each row of x is one (token, head)
+    vector. Readings (the pages give no formula): with b bits and
+    qmax = 2**b - 1,
+
+        mn    = min(row), mx = max(row)                      (exact)
+        scale = fl32(fl32(mx - mn) / qmax)                   (IEEE binary32)
+        q     = clamp(rne(fl32(fl32(x - mn) / scale)), 0, qmax)
+        x_hat = q * scale + mn
+
+    a constant row has scale 0 and codes 0 (x_hat = mn exactly). INT4 codes
+    are packed two per byte, element 2i in the low nibble.
+
+    x: fp16 [R, D] -> (codes uint8 [R, D] (bits 8) or [R, D/2] (bits 4),
+                        params float32 [R, 2] = (scale, mn)).
+    """
+    if bits not in (4, 8):
+        raise ValueError("bits must be 4 or 8")
+    xf = np.asarray(x).astype(np.float32)
+    if xf.ndim != 2 or (bits == 4 and xf.shape[1] % 2):
+        raise ValueError("x must be [R, D] (D even for 4 bits)")
+    qmax = np.float32(2 ** bits - 1)
+    mn = np.min(xf, axis=1) if xf.shape[1] else np.zeros(xf.shape[0], np.float32)
+    mx = np.max(xf, axis=1) if xf.shape[1] else np.zeros(xf.shape[0], np.float32)
+    span = np.subtract(mx, mn, dtype=np.float32)
+    scale = np.divide(span, qmax, dtype=np.float32)
+    q = np.zeros(xf.shape, dtype=np.int64)
+    nz = scale > 0
+    if np.any(nz):
+        shifted = np.subtract(xf[nz], mn[nz, None], dtype=np.float32)
+        quotient = np.divide(shifted, scale[nz, None], dtype=np.float32)
+        q[nz] = np.clip(np.rint(quotient), 0, int(qmax)).astype(np.int64)
+    params = np.stack([scale, mn], axis=1).astype(np.float32)
+    if bits == 8:
+        return q.astype(np.uint8), params
+    packed = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    return packed, params
+
+
+def kv_dequant_ref(codes, params, bits):
+    """x_hat = q * scale + mn in float64 (exact products of the stored values);
+    the inverse of kv_quant_ref's packing. Returns float64 [R, D]."""
+    c = np.asarray(codes).astype(np.int64)
+    if bits == 4:
+        q = np.empty((c.shape[0], c.shape[1] * 2), dtype=np.int64)
+        q[:, 0::2] = c & 15
+        q[:, 1::2] = c >> 4
+    else:
+        q = c
+    p = np.asarray(params).astype(np.float64)
+    return q * p[:, 0:1] + p[:, 1:2]

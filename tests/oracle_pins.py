@@ -427,3 +427,112 @@ def check_block_layout(block):
     qw = rng.integers(-2 ** 31, 2 ** 31, size=(256, 32), dtype=np.int64).astype(np.int32)
     out = block(qw)
     assert np.array_equal(np.sort(out.view(np.uint8).ravel()), np.sort(qw.view(np.uint8).ravel()))
+
+
+def _kv_exact(x, bits):
+    """kv_quant by exact rational arithmetic with the same IEEE binary32 roundings."""
+    from fractions import Fraction
+    qmax = 2 ** bits - 1
+    codes, params = [], []
+    for row in np.asarray(x).astype(np.float32):
+        mn, mx = Fraction(float(row.min())), Fraction(float(row.max()))
+        span = round_to_binary32(mx - mn) if mx != mn else Fraction(0)
+        scale = round_to_binary32(span / qmax) if span != 0 else Fraction(0)
+        qs = []
+        for v in row:
+            if scale == 0:
+                qs.append(0)
+                continue
+            d = Fraction(float(v)) - mn
+            d = round_to_binary32(d) if d != 0 else Fraction(0)
+            t = round_to_binary32(d / scale) if d != 0 else Fraction(0)
+            fl = t.numerator // t.denominator
+            frac = t - fl
+            r = fl + (1 if frac > Fraction(1, 2) or (frac == Fraction(1, 2) and fl % 2) else 0)
+            qs.append(min(max(r, 0), qmax))
+        codes.append(qs)
+        params.append((float(scale), float(mn)))
+    return np.array(codes, dtype=np.int64), np.array(params, dtype=np.float64)
+
+
+def _kv_unpack(codes, bits):
+    c = np.asarray(codes).astype(np.int64)
+    if bits == 8:
+        return c
+    q = np.empty((c.shape[0], 2 * c.shape[1]), np.int64)
+    q[:, 0::2] = c & 15
+    q[:, 1::2] = c >> 4
+    return q
+
+
+def check_kv_quant(kvq):
+    rng = np.random.default_rng(11)
+    for bits in (8, 4):
+        qmax = 2 ** bits - 1
+        # exact rational arithmetic on random rows (normal, shifted, wide)
+        x = np.concatenate([rng.standard_normal((4, 16)), 3 + 0.01 * rng.standard_normal((2, 16)),
+                            rng.uniform(-60, 60, (2, 16))]).astype(np.float16)
+        codes, params = kvq(x, bits)
+        q = _kv_unpack(codes, bits)
+        eq, ep = _kv_exact(x, bits)
+        assert np.array_equal(q, eq), bits
+        assert np.array_equal(params.astype(np.float64), ep)
+        # the row minimum codes to 0 and the maximum to qmax
+        for r in range(x.shape[0]):
+            assert q[r, np.argmin(x[r].astype(np.float32))] == 0
+            assert q[r, np.argmax(x[r].astype(np.float32))] == qmax
+        # round trip of values on the code grid: x = mn + j * 2^-e (scale a power of two)
+        j = rng.integers(0, qmax + 1, size=(3, 32))
+        j[:, 0], j[:, 1] = 0, qmax
+        for e, mn in ((3, -1.0), (6, 0.5), (1, -8.0)):
+            grid = (mn + j * 2.0 ** -e).astype(np.float16)
+            assert np.array_equal(grid.astype(np.float64), mn + j * 2.0 ** -e)  # exact in fp16
+            c2, p2 = kvq(grid, bits)
+            assert np.all(p2[:, 0] == np.float32(2.0 ** -e * qmax) / np.float32(qmax))
+            assert np.array_equal(_kv_unpack(c2, bits), j)
+        # exact ties: min 0, max qmax/8 (scale 1/8 exactly), values (j + 1/2)/8:
+        # every quotient is j + 1/2, so rounding half to even decides it
+        jj = np.arange(qmax)
+        tie = np.concatenate([[0.0, qmax / 8.0], (jj + 0.5) / 8.0, [0.0]]).astype(np.float16)[None, :]
+        c6, p6 = kvq(tie, bits)
+        assert p6[0, 0] == np.float32(0.125) and p6[0, 1] == 0
+        want = jj + (jj % 2)  # j + 1/2 -> the even neighbour
+        assert np.array_equal(_kv_unpack(c6, bits)[0, 2:2 + qmax], want)
+        # every fp16 value in [-1, 1] in one row (min -1, max 1, an inexact
+        # scale): against exact rational arithmetic with the same roundings
+        if bits == 4:
+            h = np.arange(0, 0x3C01, 7, dtype=np.uint16)
+        else:
+            h = np.arange(0, 0x3C01, 3, dtype=np.uint16)
+        vals = np.concatenate([h.view(np.float16), (h | 0x8000).view(np.float16)])
+        sweep = np.concatenate([[np.float16(-1), np.float16(1)], vals])
+        if sweep.size % 2:
+            sweep = np.append(sweep, np.float16(0))
+        sweep = sweep[None, :].astype(np.float16)
+        c7, p7 = kvq(sweep, bits)
+        e7, ep7 = _kv_exact(sweep, bits)
+        assert np.array_equal(_kv_unpack(c7, bits), e7) and np.array_equal(p7.astype(np.float64), ep7)
+        # rows where the binary32 quotient rounds to a different code than the
+        # exact one would (found by searching all fp16 values between a min
+        # and a max): the IEEE binary32 division decides
+        near = {8: [-1.953125, 3.802734375, 0.9248046875, 0.0],
+                4: [-3.423828125, 3.794921875, 2.591796875, -2.220703125]}[bits]
+        nr = np.array([near], np.float16)
+        c8, p8 = kvq(nr, bits)
+        e8, ep8 = _kv_exact(nr, bits)
+        assert np.array_equal(_kv_unpack(c8, bits), e8) and np.array_equal(p8.astype(np.float64), ep8)
+        # constant rows: scale 0, codes 0, offset = the value
+        cst = np.full((2, 8), 1.5, np.float16)
+        c3, p3 = kvq(cst, bits)
+        assert np.all(_kv_unpack(c3, bits) == 0) and np.all(p3[:, 0] == 0) and np.all(p3[:, 1] == 1.5)
+        # packing of 4-bit codes: element 2i in the low nibble
+        if bits == 4:
+            row = np.array([[0, 15, 1, 14, 2, 13, 3, 12]], np.float16)
+            c4, _ = kvq(row, 4)
+            assert c4.tolist() == [[0xF0, 0xE1, 0xD2, 0xC3]]
+        # dequantization error is at most half a step (plus binary32 rounding)
+        xs = rng.standard_normal((16, 128)).astype(np.float16)
+        c5, p5 = kvq(xs, bits)
+        xhat = _kv_unpack(c5, bits) * p5[:, 0:1].astype(np.float64) + p5[:, 1:2].astype(np.float64)
+        err = np.abs(xhat - xs.astype(np.float64))
+        assert np.all(err <= 0.5 * p5[:, 0:1] * (1 + 1e-5) + 1e-6)

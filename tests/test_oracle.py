@@ -107,6 +107,45 @@ def test_block_layout_mutants_caught():
             P.check_block_layout(mutant)
 
 
+def test_kv_quant():
+    P.check_kv_quant(oracle.kv_quant_ref)
+
+
+def test_kv_dequant_inverts_packing():
+    rng = np.random.default_rng(5)
+    for bits in (8, 4):
+        x = rng.standard_normal((6, 64)).astype(np.float16)
+        codes, params = oracle.kv_quant_ref(x, bits)
+        xhat = oracle.kv_dequant_ref(codes, params, bits)
+        assert xhat.shape == x.shape
+        assert np.max(np.abs(xhat - x.astype(np.float64))) <= 0.5 * np.max(params[:, 0]) * (1 + 1e-5) + 1e-6
+
+
+@pytest.mark.parametrize("mode", ["round_half_away", "scale_over_2b", "no_offset", "high_nibble_first",
+                                  "float64_divide"])
+def test_kv_quant_mutants_caught(mode):
+    def mutant(x, bits):
+        xf = np.asarray(x).astype(np.float32)
+        qmax = np.float32(2 ** bits - (0 if mode == "scale_over_2b" else 1))
+        mn, mx = xf.min(1), xf.max(1)
+        scale = np.divide(np.subtract(mx, mn, dtype=np.float32), qmax, dtype=np.float32)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            sh = xf if mode == "no_offset" else np.subtract(xf, mn[:, None], dtype=np.float32)
+            if mode == "float64_divide":
+                quo = sh.astype(np.float64) / scale[:, None].astype(np.float64)
+            else:
+                quo = np.divide(sh, scale[:, None], dtype=np.float32)
+            r = np.floor(quo + 0.5) if mode == "round_half_away" else np.rint(quo)
+        q = np.where(scale[:, None] > 0, np.clip(np.nan_to_num(r), 0, 2 ** bits - 1), 0).astype(np.int64)
+        params = np.stack([scale, mn], 1).astype(np.float32)
+        if bits == 8:
+            return q.astype(np.uint8), params
+        lo, hi = (q[:, 1::2], q[:, 0::2]) if mode == "high_nibble_first" else (q[:, 0::2], q[:, 1::2])
+        return (lo | (hi << 4)).astype(np.uint8), params
+    with pytest.raises(AssertionError):
+        P.check_kv_quant(mutant)
+
+
 def test_acc_overflow_guard():
     K = (2 ** 31 - 1) // 16129 + 1
     with pytest.raises(OverflowError):
