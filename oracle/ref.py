@@ -219,7 +219,8 @@ def kv_quant_ref(x, bits):
         x_hat = q * scale + mn
 
     a constant row has scale 0 and codes 0 (x_hat = mn exactly); a zero
-    minimum is stored as +0 (mn + 0). INT4 codes are packed two per byte,
+    minimum or maximum counts as +0 (mn + 0, mx + 0), so a row of signed
+    zeros stores (+0, +0). INT4 codes are packed two per byte,
     element 2i in the low nibble.
 
     x: fp16 [R, D] -> (codes uint8 [R, D] (bits 8) or [R, D/2] (bits 4),
@@ -233,7 +234,8 @@ def kv_quant_ref(x, bits):
     qmax = np.float32(2 ** bits - 1)
     mn = np.min(xf, axis=1) if xf.shape[1] else np.zeros(xf.shape[0], np.float32)
     mx = np.max(xf, axis=1) if xf.shape[1] else np.zeros(xf.shape[0], np.float32)
-    mn = np.add(mn, np.float32(0), dtype=np.float32)  # a zero minimum is stored as +0
+    mn = np.add(mn, np.float32(0), dtype=np.float32)  # a zero minimum (maximum) counts as +0
+    mx = np.add(mx, np.float32(0), dtype=np.float32)
     span = np.subtract(mx, mn, dtype=np.float32)
     scale = np.divide(span, qmax, dtype=np.float32)
     q = np.zeros(xf.shape, dtype=np.int64)

@@ -522,9 +522,10 @@ def check_kv_quant(kvq):
         e8, ep8 = _kv_exact(nr, bits)
         assert np.array_equal(_kv_unpack(c8, bits), e8) and np.array_equal(p8.astype(np.float64), ep8)
         # a row whose minimum is -0 stores +0
-        z = np.array([[-0.0, 0.0, 1.0, 0.5]], np.float16)
+        z = np.array([[-0.0, 0.0, 1.0, 0.5], [-0.0, 0.0, -0.0, 0.0], [0.0, -0.0, -0.0, -0.0]], np.float16)
         _, pz = kvq(z, bits)
-        assert pz[0, 1] == 0 and not np.signbit(pz[0, 1])
+        assert np.all(pz[:, 1] == 0) and not np.any(np.signbit(pz[:, 1]))
+        assert np.all(pz[1:, 0] == 0) and not np.any(np.signbit(pz[1:, 0]))
         # constant rows: scale 0, codes 0, offset = the value
         cst = np.full((2, 8), 1.5, np.float16)
         c3, p3 = kvq(cst, bits)
