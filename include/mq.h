@@ -274,6 +274,28 @@ mq_status mq_w4a16_gemv_blocked(const uint16_t* x, const int32_t* qweight_blocke
                                 int64_t M, int64_t N, int64_t K, int64_t group,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Online KV-cache quantization, per head and per token.
+ * Source: LMDeploy toolkit overview, section 2.4 "KV Cache online
+ * quantization" (fp16 KV cache quantized per head per token, asymmetric,
+ * to INT8 or INT4, min/max scale factors computed online, no calibration).
+ * Each row of x is one (token, head) vector; with b = bits, qmax = 2^b - 1:
+ *     mn = min(row) + 0, mx = max(row) + 0          (a zero counts as +0)
+ *     scale = fl32(fl32(mx - mn) / qmax)             (IEEE binary32)
+ *     q = clamp(rne(fl32(fl32(x - mn) / scale)), 0, qmax); scale 0 -> q = 0
+ * and x is recovered as q * scale + mn.
+ *
+ *   x       [rows, head_dim] fp16  in,  16-byte aligned
+ *   codes   bits 8: [rows, head_dim] uint8; bits 4: [rows, head_dim / 2]
+ *           uint8, element 2i in the low nibble; out, 8- (bits 8) or
+ *           4-byte (bits 4) aligned
+ *   params  [rows, 2] fp32 = (scale, mn)  out, 8-byte aligned
+ * Requires: bits in {8, 4} (else MQ_ERR_UNSUPPORTED); head_dim a power of
+ * two in [8, 512]; 0 <= rows < 2^31. Codes and params are bit-exact.
+ */
+mq_status mq_kv_quant(const uint16_t* x, uint8_t* codes, float* params, int64_t rows, int64_t head_dim,
+                      int32_t bits, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

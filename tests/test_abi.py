@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
     for n in ["mq_quant_per_token_int8", "mq_w8a8_scaled_mm", "mq_w8a8_mm_i32", "mq_w4a16_gemm",
               "mq_w4a16_gemv", "mq_w4a16_gemv_workspace_bytes", "mq_w4a16_block_weights",
               "mq_w4a16_gemv_blocked", "mq_w4a16_gemv_blocked_workspace_bytes", "mq_w8a8_linear",
-              "mq_w8a8_linear_workspace_bytes", "mq_w4a16_gemm_workspace_bytes", "mq_abi_version",
+              "mq_w8a8_linear_workspace_bytes", "mq_w4a16_gemm_workspace_bytes", "mq_kv_quant", "mq_abi_version",
               "mq_status_string", "mq_last_error"]:
         assert n in names
 
@@ -182,6 +182,20 @@ def test_gemv_workspace_plan(lib):
             assert (K // group) % splits == 0
             if N % 32 == 0:
                 assert K // splits <= 1024
+
+
+def test_kv_quant_validation(lib):
+    k = lib.mq_kv_quant
+    assert k(A, B, C, 16, 128, 2, None) == UNSUP
+    assert k(A, B, C, 16, 96, 8, None) == SHAPE       # not a power of two
+    assert k(A, B, C, 16, 1024, 8, None) == SHAPE
+    assert k(None, B, C, 16, 128, 8, None) == NULL
+    assert k(A + 8, B, C, 16, 128, 8, None) == ALIGN
+    assert k(A, B + 4, C, 16, 128, 8, None) == ALIGN   # 8-bit codes: 8-byte stores
+    assert k(A, B + 2, C, 16, 128, 4, None) == ALIGN   # 4-bit codes: 4-byte stores
+    assert k(A, B, C + 4, 16, 128, 8, None) == ALIGN
+    assert k(A, A + 64, C, 16, 128, 8, None) == ALIAS
+    assert k(A, B, C, 0, 128, 8, None) == OK
 
 
 def test_w8a8_linear_validation(lib):

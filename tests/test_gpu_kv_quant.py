@@ -1,0 +1,66 @@
+"""Online KV-cache quantization (mq_kv_quant) on an MI355X: codes and
+(scale, min) bit-exact against the oracle, INT8 and INT4, at a 4096-token
+prefill of a 32-head, 128-dim layer, a decode append, other head sizes and
+the edge rows the oracle's pins cover (ties, binary32-sensitive quotients,
+constant rows, signed zeros, fp16 extremes)."""
+
+import numpy as np
+import pytest
+
+import oracle
+import weight_activation_quantized_amd as mq
+from tests.gpu_util import announce, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(x, bits, what):
+    announce(f"kv_quant {what} bits={bits} shape={x.shape}")
+    codes, params = mq.kv_quant(dev(x), bits)
+    codes, params = host(codes), host(params)
+    rc, rp = oracle.kv_quant_ref(x.reshape(-1, x.shape[-1]), bits)
+    assert np.array_equal(params.reshape(-1, 2).view(np.uint32), rp.view(np.uint32)), f"{what}: params differ"
+    bad = np.argwhere(codes.reshape(rc.shape) != rc)
+    assert bad.size == 0, f"{what}: {len(bad)} code bytes differ, first at {bad[:3].tolist()}"
+    return codes, params
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("shape", [(4096, 32, 128), (128, 32, 128), (37, 8, 64), (5, 3, 256), (1000, 512),
+                                   (7, 8), (3, 16), (9, 32)],
+                         ids=["prefill_4k", "decode_128seq", "h64", "h256", "h512", "h8", "h16", "h32"])
+def test_kv_quant_bitexact(shape, bits):
+    rng = np.random.default_rng(sum(shape) + bits)
+    x = (rng.standard_normal(shape) * rng.uniform(0.1, 4, shape[:-1] + (1,))).astype(np.float16)
+    _check(x, bits, "random")
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_kv_quant_edge_rows(bits):
+    qmax = 2 ** bits - 1
+    D = 512
+    rows = []
+    jj = np.arange(qmax)
+    tie = np.concatenate([[0.0, qmax / 8.0], (jj + 0.5) / 8.0])
+    rows.append(np.resize(tie, D))                                   # exact ties
+    rows.append(np.resize([-1.953125, 3.802734375, 0.9248046875], D))  # binary32-sensitive quotient (8 bits)
+    rows.append(np.resize([-3.423828125, 3.794921875, 2.591796875, -2.220703125], D))
+    rows.append(np.full(D, 1.5))                                     # constant
+    rows.append(np.resize([-0.0, 0.0], D))                           # signed zeros
+    rows.append(np.resize([-0.0, 0.0, 1.0, 0.5], D))
+    rows.append(np.resize([65504.0, -65504.0, 0.0], D))              # fp16 extremes
+    rows.append(np.resize([6e-8, -6e-8, 0.0], D))                    # subnormals
+    x = np.array(rows).astype(np.float16)
+    codes, params = _check(x, bits, "edge rows")
+    assert params[3, 0] == 0 and np.all(codes[3] == 0)
+    assert not np.any(np.signbit(params[4]))
+
+
+def test_kv_quant_dequant_error():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((2048, 128)).astype(np.float16)
+    for bits in (8, 4):
+        codes, params = mq.kv_quant(dev(x), bits)
+        xhat = oracle.kv_dequant_ref(host(codes), host(params), bits)
+        step = host(params)[:, 0:1].astype(np.float64)
+        assert np.all(np.abs(xhat - x.astype(np.float64)) <= 0.5 * step * (1 + 1e-5) + 1e-6)

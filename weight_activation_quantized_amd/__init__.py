@@ -19,6 +19,8 @@ Entry points (same names as the C ABI, without the ``mq_`` prefix):
     w4a16_gemv_blocked(x, qweight_blocked, scales, qzeros, group) -> y (fp16), M <= 64
     w4a16_gemv_blocked_workspace_bytes(M, N, K, group) -> int
 
+    kv_quant(x, bits)                                -> (codes, params) per (token, head) row
+
 and two compositions used by a model's linear layer:
 
     w4a16_linear(x, qweight, scales, qzeros, group)  GEMV for M <= 64, else GEMM
@@ -35,7 +37,7 @@ __all__ = [
     "w4a16_gemm", "w4a16_gemv", "w4a16_gemv_workspace_bytes",
     "w4a16_linear", "w8a8_linear", "GEMV_MAX_M",
     "w4a16_block_weights", "w4a16_gemv_blocked", "w4a16_gemv_blocked_workspace_bytes",
-    "w8a8_linear_workspace_bytes", "w4a16_gemm_workspace_bytes",
+    "w8a8_linear_workspace_bytes", "w4a16_gemm_workspace_bytes", "kv_quant",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmq.so")
@@ -74,6 +76,7 @@ _PROTOTYPES = {
     "mq_w4a16_gemv": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
     "mq_w4a16_block_weights": (ctypes.c_int, [_P, _P, _I64, _I64, _P]),
     "mq_w8a8_linear_workspace_bytes": (ctypes.c_size_t, [_I64, _I64]),
+    "mq_kv_quant": (ctypes.c_int, [_P, _P, _P, _I64, _I64, ctypes.c_int32, _P]),
     "mq_w8a8_linear": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
     "mq_w4a16_gemv_blocked_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I64]),
     "mq_w4a16_gemv_blocked": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t,
@@ -351,3 +354,24 @@ def w8a8_linear(x, wq, s_ch, out=None, workspace=None, stream=None):
         _check(library().mq_w8a8_linear(x.data_ptr(), wq.data_ptr(), s_ch.data_ptr(), y.data_ptr(), M, N, K,
                                         ws_ptr, ws_bytes, _stream_of(x, stream)))
     return y
+
+
+def kv_quant(x, bits=8, codes=None, params=None, stream=None):
+    """Online KV-cache quantization per (token, head) row: x [..., head_dim] fp16
+    -> (codes uint8 [..., head_dim] (8 bits) or [..., head_dim/2] (4 bits, two
+    per byte, element 2i low), params fp32 [..., 2] = (scale, min))."""
+    torch = _torch()
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.float16 or x.device.type != "cuda":
+        raise TypeError("x must be a float16 GPU tensor")
+    if not x.is_contiguous() or x.dim() < 1:
+        raise ValueError("x must be contiguous with at least one dimension")
+    D = x.shape[-1]
+    lead = tuple(x.shape[:-1])
+    rows = x.numel() // D if D else 0
+    cshape = lead + ((D,) if bits == 8 else (D // 2,))
+    codes = _out(codes, cshape, torch.uint8, x, "codes")
+    params = _out(params, lead + (2,), torch.float32, x, "params")
+    with torch.cuda.device(x.device):
+        _check(library().mq_kv_quant(x.data_ptr(), codes.data_ptr(), params.data_ptr(), rows, D, bits,
+                                     _stream_of(x, stream)))
+    return codes, params

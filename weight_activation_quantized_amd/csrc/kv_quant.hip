@@ -1,0 +1,120 @@
+// Online KV-cache quantization for gfx950.
+//
+// Source: LMDeploy toolkit overview, section 2.4 "KV Cache online
+// quantization": the fp16 KV cache is quantized per head and per token,
+// asymmetrically, to INT8 or INT4, with min/max scale factors computed on
+// the fly. One row = one (token, head) vector of D values. With b bits and
+// qmax = 2^b - 1 (the pages give no formula; this is the plain reading):
+//   scale = fl32(fl32(max - min) / qmax),
+//   q     = clamp(rne(fl32(fl32(x - min) / scale)), 0, qmax)   (IEEE binary32),
+// a constant row giving scale 0 and q = 0; (scale, min) are stored per row
+// in fp32 (a zero minimum or maximum counting as +0) and INT4 codes two per
+// byte, element 2i in the low nibble.
+//
+// The kernel is a single pass bound by HBM: a group of D/8 lanes holds one
+// row (one 16-byte load of 8 values per lane), min and max come from a
+// butterfly within the group, and each lane writes its 8 codes (8 bytes, or
+// 4 packed bytes for INT4). x is read once; nothing else is.
+#include "device_common.h"
+#include "launch.h"
+
+namespace mq {
+namespace {
+
+template <int kL>
+__device__ __forceinline__ float group_min(float v) {
+#pragma unroll
+  for (int off = kL / 2; off >= 1; off >>= 1) v = fminf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+template <int kL>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int off = kL / 2; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// kL lanes per row (head_dim = 8 kL), kBits = 8 or 4. 256 threads: 256 / kL
+// rows per workgroup.
+template <int kL, int kBits>
+__global__ __launch_bounds__(256) void kv_quant_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ codes,
+                                                       float* __restrict__ params, int64_t rows) {
+  constexpr int kD = 8 * kL;
+  constexpr float kQmax = static_cast<float>((1 << kBits) - 1);
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (256 / kL) + threadIdx.x / kL;
+  const int lig = threadIdx.x % kL;  // lane within the row's group
+  const bool valid = row < rows;
+  u32x4 v = u32x4{0u, 0u, 0u, 0u};
+  if (valid) v = *reinterpret_cast<const u32x4*>(x + row * kD + 8 * lig);
+  float f[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const f16x2 h = as_f16x2(v[w]);
+    f[2 * w] = static_cast<float>(h[0]);
+    f[2 * w + 1] = static_cast<float>(h[1]);
+  }
+  float mn = f[0], mx = f[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) {
+    mn = fminf(mn, f[e]);
+    mx = fmaxf(mx, f[e]);
+  }
+  // every lane of a group takes part; a zero minimum or maximum becomes +0
+  mn = group_min<kL>(mn) + 0.0f;
+  mx = group_max<kL>(mx) + 0.0f;
+  if (!valid) return;
+  const float scale = (mx - mn) / kQmax;  // IEEE binary32 subtraction and division
+  uint32_t q[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float c = 0.f;
+    if (scale > 0.f) c = fminf(fmaxf(rintf((f[e] - mn) / scale), 0.f), kQmax);
+    q[e] = static_cast<uint32_t>(c);
+  }
+  if constexpr (kBits == 8) {
+    const u32x2 out = u32x2{q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24),
+                            q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24)};
+    *reinterpret_cast<u32x2*>(codes + row * kD + 8 * lig) = out;
+  } else {
+    const uint32_t out = (q[0] | (q[1] << 4)) | ((q[2] | (q[3] << 4)) << 8) | ((q[4] | (q[5] << 4)) << 16) |
+                         ((q[6] | (q[7] << 4)) << 24);
+    *reinterpret_cast<uint32_t*>(codes + row * (kD / 2) + 4 * lig) = out;
+  }
+  if (lig == 0) {
+    float2 p;
+    p.x = scale;
+    p.y = mn;
+    *reinterpret_cast<float2*>(params + 2 * row) = p;
+  }
+}
+
+template <int kBits>
+hipError_t launch_bits(const uint16_t* x, uint8_t* codes, float* params, int64_t rows, int64_t head_dim,
+                       hipStream_t stream) {
+  const int64_t lanes = head_dim / 8;
+  const int64_t rows_per_block = 256 / lanes;
+  const dim3 grid(static_cast<uint32_t>((rows + rows_per_block - 1) / rows_per_block)), block(256);
+  switch (lanes) {
+    case 1: return launch_kernel(kv_quant_kernel<1, kBits>, grid, block, 0, stream, x, codes, params, rows);
+    case 2: return launch_kernel(kv_quant_kernel<2, kBits>, grid, block, 0, stream, x, codes, params, rows);
+    case 4: return launch_kernel(kv_quant_kernel<4, kBits>, grid, block, 0, stream, x, codes, params, rows);
+    case 8: return launch_kernel(kv_quant_kernel<8, kBits>, grid, block, 0, stream, x, codes, params, rows);
+    case 16: return launch_kernel(kv_quant_kernel<16, kBits>, grid, block, 0, stream, x, codes, params, rows);
+    case 32: return launch_kernel(kv_quant_kernel<32, kBits>, grid, block, 0, stream, x, codes, params, rows);
+    case 64: return launch_kernel(kv_quant_kernel<64, kBits>, grid, block, 0, stream, x, codes, params, rows);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_quant(const uint16_t* x, uint8_t* codes, float* params, int64_t rows, int64_t head_dim,
+                           int bits, hipStream_t stream) {
+  if (rows > 0x7fffffff) return hipErrorInvalidValue;
+  if (bits == 8) return launch_bits<8>(x, codes, params, rows, head_dim, stream);
+  if (bits == 4) return launch_bits<4>(x, codes, params, rows, head_dim, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mq

@@ -37,6 +37,12 @@ bool w8a8_use_fused(int64_t M, int64_t K);
 hipError_t launch_w8a8_gemv_fused(const uint16_t* x, const int8_t* wq, const float* s_ch, uint16_t* y,
                                   int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+// Online KV-cache quantization of rows x [rows, head_dim] fp16 to codes
+// (uint8 [rows, head_dim] for 8 bits, packed [rows, head_dim/2] for 4) and
+// params fp32 [rows, 2] = (scale, min); head_dim a power of two in [8, 512].
+hipError_t launch_kv_quant(const uint16_t* x, uint8_t* codes, float* params, int64_t rows, int64_t head_dim,
+                           int bits, hipStream_t stream);
+
 // W4A16 GEMM y[M,N] = x[M,K] . dequant(qweight, scales, qzeros), groups of
 // `group` rows (32, 64 or 128; K % 128 == 0). With a workspace of
 // w4a16_gemm_workspace(M, N, K) bytes, K is split w4a16_gemm_splits ways

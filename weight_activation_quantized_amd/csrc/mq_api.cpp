@@ -278,6 +278,27 @@ mq_status mq_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const uint16_
                     "w4a16_gemv launch");
 }
 
+mq_status mq_kv_quant(const uint16_t* x, uint8_t* codes, float* params, int64_t rows, int64_t head_dim,
+                      int32_t bits, void* stream) {
+  if (bits != 8 && bits != 4) return fail(MQ_ERR_UNSUPPORTED, "bits=%d (8 and 4 are provided)", (int)bits);
+  if (head_dim < 8 || head_dim > 512 || (head_dim & (head_dim - 1)))
+    return fail(MQ_ERR_SHAPE, "head_dim=%lld must be a power of two in [8, 512]", (long long)head_dim);
+  if (rows < 0 || rows > kMaxDim) return fail(MQ_ERR_SHAPE, "rows=%lld out of range", (long long)rows);
+  MQ_TRY(need(x, rows * head_dim, "x"));
+  MQ_TRY(need(codes, rows * head_dim, "codes"));
+  MQ_TRY(need(params, rows, "params"));
+  if (!aligned(x, 16)) return fail(MQ_ERR_ALIGN, "x must be 16-byte aligned");
+  if (!aligned(codes, bits == 8 ? 8 : 4)) return fail(MQ_ERR_ALIGN, "codes must be %d-byte aligned", bits == 8 ? 8 : 4);
+  if (!aligned(params, 8)) return fail(MQ_ERR_ALIGN, "params must be 8-byte aligned");
+  const Range in[] = {{x, static_cast<size_t>(rows * head_dim) * 2, "x"}};
+  const Range out[] = {{codes, static_cast<size_t>(rows * head_dim) * bits / 8, "codes"},
+                       {params, static_cast<size_t>(rows) * 8, "params"}};
+  MQ_TRY(check_alias(in, out));
+  if (rows == 0) return ok();
+  return hip_status(mq::launch_kv_quant(x, codes, params, rows, head_dim, bits, as_stream(stream)),
+                    "kv_quant launch");
+}
+
 size_t mq_w8a8_linear_workspace_bytes(int64_t M, int64_t K) {
   if (M < 0 || M > kMaxDim || K < 16 || K > kMaxKInt8 || K % 16 || M * K > kMaxElems || M == 0 ||
       mq::w8a8_use_fused(M, K))
