@@ -44,6 +44,10 @@ Also reported (same line):
                (M = 1, 4, 16) in GB/s, a ViT-L fused qkv projection (K=1024,
                N=3072) at 1 and 16 tokens (GEMV) and 577 and 4096 tokens
                (GEMM), and the 4096^3 prefill GEMM, cold weights, graph replays.
+  kv_quant     online KV-cache quantization (per head, per token, INT8 and
+               INT4) of one layer's K: a 4096-token prefill (32 heads x 128,
+               rotating copies >= 320 MB) and a 128-sequence decode append;
+               microseconds and GB/s of x + codes + (scale, min).
   cpu_baseline the CPU oracle on one step of the same workload (one weight
                set), repeated for about 10 s, in the same unit.
 """
@@ -95,6 +99,7 @@ def parse_args(argv=None):
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-layers", action="store_true", help="skip the decoder-layer linear set")
     ap.add_argument("--no-groups", action="store_true", help="skip the group-64 / group-32 measurements")
+    ap.add_argument("--no-kv", action="store_true", help="skip the KV-cache quantization measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-kernel", action="store_true",
@@ -385,6 +390,44 @@ def bench_groups(torch, mq, synth, log):
     return out
 
 
+def bench_kv_quant(torch, mq, log):
+    """Online KV-cache quantization of one layer's K (or V): a 4096-token prefill
+    and a 128-sequence decode append, 32 heads x 128, INT8 and INT4. The prefill
+    rotates over copies totalling >= 320 MB, so x comes from HBM."""
+    import numpy as np
+    dev = torch.device("cuda", 0)
+    R = 20
+    out = {}
+
+    def time_calls(fn):
+        g = capture(torch, lambda: [fn(r) for r in range(R)])
+        g.replay()
+        best = min(timed_replay(torch, g)[1] for _ in range(3))
+        return best / R
+
+    rng = np.random.default_rng(77)
+    for name, T in (("prefill_4096", 4096), ("decode_128seq", 128)):
+        shape = (T, 32, 128)
+        x0 = torch.from_numpy(rng.standard_normal(shape).astype(np.float16)).to(dev)
+        nbytes_x = x0.numel() * 2
+        n = max(2, -(-320 * 2**20 // nbytes_x)) if T > 1024 else 2
+        xs = [x0] + [x0.clone() for _ in range(n - 1)]
+        rows = T * 32
+        for bits in (8, 4):
+            codes = torch.empty((T, 32, 128 if bits == 8 else 64), dtype=torch.uint8, device=dev)
+            params = torch.empty((T, 32, 2), dtype=torch.float32, device=dev)
+            log(f"kv_quant: {name} bits={bits}")
+            t = time_calls(lambda r, codes=codes, params=params: mq.kv_quant(xs[r % n], bits, codes=codes,
+                                                                             params=params))
+            nbytes = rows * 128 * 2 + rows * 128 * bits // 8 + rows * 8
+            out[f"{name}_int{bits}"] = {"rows": rows, "head_dim": 128, "us": round(t * 1e6, 2),
+                                        "GBps": round(nbytes / t / 1e9, 1),
+                                        "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBPS, 4)}
+        del xs
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(args, log):
     import numpy as np
 
@@ -497,6 +540,8 @@ def main(argv=None):
         line["layers"] = bench_layers(torch, mq, synth, args, log)
     if not args.no_groups:
         line["groups"] = bench_groups(torch, mq, synth, log)
+    if not args.no_kv:
+        line["kv_quant"] = bench_kv_quant(torch, mq, log)
     if not args.no_cpu_baseline and rank == 0:
         line["cpu_baseline"] = cpu_baseline(args, log)
     print(json.dumps(line))
