@@ -291,7 +291,8 @@ mq_status mq_w4a16_gemv_blocked(const uint16_t* x, const int32_t* qweight_blocke
  *           4-byte (bits 4) aligned
  *   params  [rows, 2] fp32 = (scale, mn)  out, 8-byte aligned
  * Requires: bits in {8, 4} (else MQ_ERR_UNSUPPORTED); head_dim a power of
- * two in [8, 512]; 0 <= rows < 2^31. Codes and params are bit-exact.
+ * two in [8, 512]; 0 <= rows < 2^31 and rows * head_dim < 2^35 (else
+ * MQ_ERR_SHAPE). Codes and params are bit-exact.
  */
 mq_status mq_kv_quant(const uint16_t* x, uint8_t* codes, float* params, int64_t rows, int64_t head_dim,
                       int32_t bits, void* stream);

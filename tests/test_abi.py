@@ -189,6 +189,7 @@ def test_kv_quant_validation(lib):
     assert k(A, B, C, 16, 128, 2, None) == UNSUP
     assert k(A, B, C, 16, 96, 8, None) == SHAPE       # not a power of two
     assert k(A, B, C, 16, 1024, 8, None) == SHAPE
+    assert k(A, B, C, 1 << 26, 512, 8, None) == SHAPE   # 2^35 values: more than 2^32 lanes
     assert k(None, B, C, 16, 128, 8, None) == NULL
     assert k(A + 8, B, C, 16, 128, 8, None) == ALIGN
     assert k(A, B + 4, C, 16, 128, 8, None) == ALIGN   # 8-bit codes: 8-byte stores

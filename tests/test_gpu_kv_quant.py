@@ -56,6 +56,24 @@ def test_kv_quant_edge_rows(bits):
     assert not np.any(np.signbit(params[4]))
 
 
+@pytest.mark.parametrize("bits", [8, 4])
+def test_kv_quant_two_rows_per_group_ragged(bits):
+    """Enough rows for two rows per lane group (the large-call form), with a
+    ragged last workgroup and the edge rows planted among random ones."""
+    qmax = 2 ** bits - 1
+    rng = np.random.default_rng(40 + bits)
+    x = rng.standard_normal((4099 * 33, 128)).astype(np.float16)
+    jj = np.arange(qmax)
+    edge = [np.resize(np.concatenate([[0.0, qmax / 8.0], (jj + 0.5) / 8.0]), 128),
+            np.full(128, -2.5), np.resize([-0.0, 0.0], 128), np.resize([65504.0, -65504.0, 0.0], 128),
+            np.resize([6e-8, -6e-8, 0.0], 128)]
+    at = rng.choice(x.shape[0], size=200, replace=False)
+    for i, r in enumerate(at):
+        x[r] = np.asarray(edge[i % len(edge)], dtype=np.float16)
+    x[-1] = np.asarray(edge[0], dtype=np.float16)
+    _check(x, bits, "two rows per group, ragged")
+
+
 def test_kv_quant_dequant_error():
     rng = np.random.default_rng(2)
     x = rng.standard_normal((2048, 128)).astype(np.float16)

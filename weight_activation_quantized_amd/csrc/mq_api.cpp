@@ -284,6 +284,9 @@ mq_status mq_kv_quant(const uint16_t* x, uint8_t* codes, float* params, int64_t 
   if (head_dim < 8 || head_dim > 512 || (head_dim & (head_dim - 1)))
     return fail(MQ_ERR_SHAPE, "head_dim=%lld must be a power of two in [8, 512]", (long long)head_dim);
   if (rows < 0 || rows > kMaxDim) return fail(MQ_ERR_SHAPE, "rows=%lld out of range", (long long)rows);
+  // one lane per 8 values: the launch holds rows * head_dim / 8 < 2^32 work-items
+  if (rows * head_dim >= (int64_t{1} << 35))
+    return fail(MQ_ERR_SHAPE, "rows * head_dim = %lld must be below 2^35", (long long)(rows * head_dim));
   MQ_TRY(need(x, rows * head_dim, "x"));
   MQ_TRY(need(codes, rows * head_dim, "codes"));
   MQ_TRY(need(params, rows, "params"));
