@@ -14,6 +14,10 @@ pages by eye:
   (LMDeploy overview, section 2.5 "Weight quantization (AWQ)": 4-bit weights,
   groups of 128; LMDeploy 4-bit deployment guide, section 2.2: scales are
   applied inside the same kernel as the weights).
+* ``pack_int4`` / ``reorder_int4_ref`` / ``transpose_int4_ref`` -- bringing
+  4-bit checkpoints packed in another field order or along the other axis
+  into the library's layout (LMDeploy overview, sections 4.1 and 5.5: AWQ
+  model format; pymllm Setup and Usage: compressed-tensors loading).
 * ``quant_per_token_int8_ref`` / ``w8a8_acc_ref`` / ``w8a8_ref`` -- the
   W8A8_INT8 path (pymllm Setup and Usage, Overview: int8 weights and
   activations on INT8 tensor cores; section "W8A8 first-run JIT
@@ -36,7 +40,10 @@ from .ref import (  # noqa: F401
     dequant_w4,
     kv_dequant_ref,
     kv_quant_ref,
+    pack_int4,
     quant_per_token_int8_ref,
+    reorder_int4_ref,
+    transpose_int4_ref,
     unpack_int4,
     w4a16_ref,
     w8a8_acc_ref,

@@ -135,6 +135,71 @@ def block_weights_ref(qweight):
     return np.ascontiguousarray(out).view(np.int32)
 
 
+def pack_int4(q):
+    """Pack 4-bit values into words in the library's order: column ``8*c + j``
+    of q goes to field j (bits 4j..4j+3) of word c -- the inverse of
+    ``unpack_int4``.
+
+    q: integer array [R, 8*C] with values 0..15 -> int32 [R, C].
+    """
+    q = np.asarray(q).astype(np.int64)
+    if q.ndim != 2 or q.shape[1] % NIBBLES_PER_WORD:
+        raise ValueError("q must be [R, 8*C]")
+    if np.any((q < 0) | (q > 15)):
+        raise ValueError("4-bit values must lie in 0..15")
+    words = np.zeros((q.shape[0], q.shape[1] // NIBBLES_PER_WORD), dtype=np.int64)
+    for j in range(NIBBLES_PER_WORD):
+        words |= q[:, j::NIBBLES_PER_WORD] << (4 * j)
+    return words.astype(np.uint32).view(np.int32)
+
+
+def _fields_to_columns(words, field_order):
+    """4-bit matrix [R, 8*C] of words whose field j holds column 8*c + field_order[j]."""
+    order = [int(v) for v in field_order]
+    if sorted(order) != list(range(NIBBLES_PER_WORD)):
+        raise ValueError("field_order must be a permutation of 0..7")
+    f = unpack_int4(words)  # f[:, 8c + j] = field j of word c
+    q = np.empty_like(f)
+    for j in range(NIBBLES_PER_WORD):
+        q[:, order[j]::NIBBLES_PER_WORD] = f[:, j::NIBBLES_PER_WORD]
+    return q
+
+
+def reorder_int4_ref(words, field_order):
+    """Checkpoint words with another field order -> the library's order.
+
+    [lmdeploy-ovw] sections 4.1 and 5.5 load 4-bit checkpoints with
+    ``model_format="awq"``, [lmdeploy-hw] converts them with
+    ``--model-format awq`` before serving, and [pymllm-setup] loads
+    ``compressed-tensors`` checkpoints into its quantized linear path; none
+    of the pages gives those formats' bit layouts. Reading: a checkpoint word
+    packs 8 consecutive columns of one row in some field order, field j
+    holding column ``8*c + field_order[j]``; converting it places each value
+    in its column and repacks in the library's order. The values and the
+    word shape are unchanged.
+
+    words: int32 [R, C] -> int32 [R, C].
+    """
+    return pack_int4(_fields_to_columns(words, field_order))
+
+
+def transpose_int4_ref(words, field_order):
+    """A 4-bit matrix packed along its rows' other axis -> transposed, repacked.
+
+    Same passages as ``reorder_int4_ref``. Reading: a checkpoint that stores
+    weights one output channel per row, packed along the input dimension
+    (words [N, K/8], field j of word c holding k = 8*c + field_order[j]),
+    becomes the library's [K, N/8] layout (field j of word c holding
+    n = 8*c + j) by transposing the 4-bit matrix.
+
+    words: int32 [A, B/8] -> int32 [B, A/8] (A % 8 == 0).
+    """
+    q = _fields_to_columns(words, field_order)
+    if q.shape[0] % NIBBLES_PER_WORD:
+        raise ValueError("the row count must be a multiple of 8")
+    return pack_int4(np.ascontiguousarray(q.T))
+
+
 def quant_per_token_int8_ref(x):
     """Dynamic symmetric per-token int8 quantization.
 

@@ -541,3 +541,65 @@ def check_kv_quant(kvq):
         xhat = _kv_unpack(c5, bits) * p5[:, 0:1].astype(np.float64) + p5[:, 1:2].astype(np.float64)
         err = np.abs(xhat - xs.astype(np.float64))
         assert np.all(err <= 0.5 * p5[:, 0:1] * (1 + 1e-5) + 1e-6)
+
+
+# ----------------------------------------------------------------------------
+# checkpoint layouts (field order, packing axis)
+# ----------------------------------------------------------------------------
+
+CHECKPOINT_ORDER = (0, 2, 4, 6, 1, 3, 5, 7)
+
+
+def _words(vals):
+    return np.array([int(v, 16) for v in vals], dtype=np.uint32).view(np.int32)
+
+
+def _loop_pack_rows(q, order):
+    """Explicit loops: word c of row r holds column 8c + order[j] in field j."""
+    R, C8 = len(q), len(q[0])
+    out = np.zeros((R, C8 // 8), dtype=np.uint32)
+    for r in range(R):
+        for c in range(C8 // 8):
+            w = 0
+            for j in range(8):
+                w |= int(q[r][8 * c + order[j]]) << (4 * j)
+            out[r, c] = w
+    return out.view(np.int32)
+
+
+def _loop_unpack_rows(words):
+    """Explicit loops, library order: column 8c + j is field j of word c."""
+    u = np.asarray(words).view(np.uint32)
+    R, C = u.shape
+    return [[(int(u[r, k // 8]) >> (4 * (k % 8))) & 15 for k in range(8 * C)] for r in range(R)]
+
+
+def check_int4_checkpoint(reorder, transpose, pack):
+    for line in _read_golden("checkpoint_words.txt"):
+        kind, rest = line.split(None, 1)
+        src, dst = [t.split() for t in rest.split("->")]
+        if kind == "reorder":
+            got = reorder(_words(src).reshape(1, 1), CHECKPOINT_ORDER)
+            assert got.view(np.uint32).tolist() == [[int(dst[0], 16)]], line
+        else:
+            got = transpose(_words(src).reshape(8, 1), tuple(range(8)))
+            assert got.view(np.uint32).ravel().tolist() == [int(v, 16) for v in dst], line
+    rng = np.random.default_rng(5)
+    for order in (CHECKPOINT_ORDER, tuple(range(8)), tuple(rng.permutation(8).tolist())):
+        q = rng.integers(0, 16, size=(16, 24))
+        src = _loop_pack_rows(q.tolist(), order)
+        # reorder keeps the matrix and its shape, in the library's order
+        assert _loop_unpack_rows(reorder(src, order)) == q.tolist()
+        # transpose gives q^T packed along the new rows
+        t = transpose(src, order)
+        assert t.shape == (24, 2)
+        assert _loop_unpack_rows(t) == q.T.tolist()
+    # pack is unpack's inverse (unpack is pinned by nibble_layout.txt)
+    q = rng.integers(0, 16, size=(5, 40))
+    w = pack(q)
+    assert w.dtype == np.int32 and w.shape == (5, 5)
+    assert _loop_unpack_rows(w) == q.tolist()
+    # the library order is a fixed point; transposing twice is the identity
+    w = rng.integers(-2 ** 31, 2 ** 31, size=(16, 4), dtype=np.int64).astype(np.int32)
+    assert np.array_equal(reorder(w, tuple(range(8))), w)
+    assert np.array_equal(transpose(transpose(w, tuple(range(8))), tuple(range(8))), w)

@@ -318,3 +318,41 @@ def test_acc_mutant_caught():
 def test_w8a8_mutants_caught(mode):
     w = _w8a8_with(mode)
     assert _fails(lambda: P.check_w8a8_bruteforce(w), lambda: P.check_w8a8_linearity(w))
+
+
+def test_int4_checkpoint_layouts():
+    P.check_int4_checkpoint(oracle.reorder_int4_ref, oracle.transpose_int4_ref, oracle.pack_int4)
+
+
+@pytest.mark.parametrize("mode", ["inverse_order", "no_transpose", "order_on_rows", "high_first"])
+def test_int4_checkpoint_mutants_caught(mode):
+    def fields(words, order):
+        f = oracle.unpack_int4(words)
+        q = np.empty_like(f)
+        inv = [order.index(c) for c in range(8)]
+        use = inv if mode == "inverse_order" else list(order)
+        for j in range(8):
+            q[:, use[j]::8] = f[:, j::8]
+        return q
+
+    def pack(q):
+        if mode == "high_first":
+            q = np.asarray(q)
+            q = q.reshape(q.shape[0], -1, 8)[:, :, ::-1].reshape(q.shape[0], -1)
+        return oracle.pack_int4(q)
+
+    def reorder(words, order):
+        return pack(fields(words, tuple(order)))
+
+    def transpose(words, order):
+        order = tuple(order)
+        if mode == "order_on_rows":
+            q = oracle.unpack_int4(words)
+            return pack(np.ascontiguousarray(q.T))
+        q = fields(words, order)
+        if mode == "no_transpose":
+            return pack(q.reshape(q.shape[1], q.shape[0]))
+        return pack(np.ascontiguousarray(q.T))
+
+    with pytest.raises(AssertionError):
+        P.check_int4_checkpoint(reorder, transpose, pack)
