@@ -297,6 +297,51 @@ mq_status mq_w4a16_gemv_blocked(const uint16_t* x, const int32_t* qweight_blocke
 mq_status mq_kv_quant(const uint16_t* x, uint8_t* codes, float* params, int64_t rows, int64_t head_dim,
                       int32_t bits, void* stream);
 
+/*
+ * Checkpoint-layout adapter: one-time conversions of 4-bit checkpoint
+ * tensors into the layouts above.
+ * Source: the LMDeploy overview (sections 4.1 and 5.5) loads 4-bit
+ * checkpoints in the AWQ model format and the LMDeploy 4-bit deployment
+ * guide converts them before serving; pymllm Setup and Usage loads
+ * compressed-tensors checkpoints into its quantized linear path. The pages
+ * give none of these formats' bit layouts. Reading: a checkpoint packs 8
+ * consecutive 4-bit values of one row into a 32-bit word in some field
+ * order -- field j (bits 4j..4j+3) holds element 8c + order[j] of the row --
+ * either along the output dimension ([K, N/8], as qweight and qzeros here)
+ * or along the input dimension ([N, K/8], one output channel per row).
+ * `order` is a HOST pointer to 8 bytes, a permutation of 0..7; NULL means
+ * the library's order (order[j] = j). For example AWQ-style words use
+ * order = {0, 2, 4, 6, 1, 3, 5, 7}. Results are bit-exact permutations of
+ * the input bits; each call is asynchronous on `stream` like the others,
+ * and dst must not overlap src (MQ_ERR_ALIAS).
+ */
+
+/*
+ * src, dst int32 [words], src in `order`, dst in the library's order (same
+ * shape). Use on qweight [K, N/8] and qzeros [K/G, N/8] of checkpoints packed
+ * along N. 0 <= words < 2^34; src and dst 16-byte aligned; a non-permutation
+ * `order` gives MQ_ERR_UNSUPPORTED.
+ */
+mq_status mq_int4_reorder(const int32_t* src, int32_t* dst, int64_t words, const uint8_t* order, void* stream);
+
+/*
+ * src int32 [A, B/8]: a 4-bit matrix [A, B] packed along B in `order`.
+ * dst int32 [B, A/8]: its transpose packed along A in the library's order,
+ * i.e. field j of dst word (b, c) is element (8c + j, b). Use on weights
+ * stored [N, K/8] (A = N, B = K) to get qweight [K, N/8]. A and B
+ * non-negative multiples of 8 (else MQ_ERR_SHAPE), A <= 65535 * 128,
+ * B < 2^31; src and dst 4-byte aligned.
+ */
+mq_status mq_int4_transpose(const int32_t* src, int32_t* dst, int64_t A, int64_t B, const uint8_t* order,
+                            void* stream);
+
+/*
+ * src [A, B] of 16-bit values (fp16 scales as raw bits) -> dst [B, A].
+ * Use on scales stored [N, K/G] to get scales [K/G, N]. 0 <= A <= 65535 * 64,
+ * 0 <= B <= 2^30; src and dst 2-byte aligned.
+ */
+mq_status mq_u16_transpose(const uint16_t* src, uint16_t* dst, int64_t A, int64_t B, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -39,7 +39,7 @@ def test_header_declares_the_boundary():
               "mq_w4a16_gemv", "mq_w4a16_gemv_workspace_bytes", "mq_w4a16_block_weights",
               "mq_w4a16_gemv_blocked", "mq_w4a16_gemv_blocked_workspace_bytes", "mq_w8a8_linear",
               "mq_w8a8_linear_workspace_bytes", "mq_w4a16_gemm_workspace_bytes", "mq_kv_quant", "mq_abi_version",
-              "mq_status_string", "mq_last_error"]:
+              "mq_status_string", "mq_last_error", "mq_int4_reorder", "mq_int4_transpose", "mq_u16_transpose"]:
         assert n in names
 
 
@@ -267,3 +267,35 @@ def test_python_wrapper_rejects_cpu_tensors():
 def test_mqerror_carries_status():
     e = mq.MqError(SHAPE, "K=3 bad")
     assert e.status == SHAPE and e.status_name == "MQ_ERR_SHAPE" and "K=3" in str(e)
+
+
+def test_checkpoint_layout_validation(lib):
+    import ctypes
+    awq = (ctypes.c_uint8 * 8)(0, 2, 4, 6, 1, 3, 5, 7)
+    dup = (ctypes.c_uint8 * 8)(0, 0, 4, 6, 1, 3, 5, 7)
+    big = (ctypes.c_uint8 * 8)(0, 2, 4, 6, 1, 3, 5, 8)
+    r = lib.mq_int4_reorder
+    assert r(A, B, 16, dup, None) == UNSUP and b"permutation" in lib.mq_last_error()
+    assert r(A, B, 16, big, None) == UNSUP
+    assert r(A, B, -1, awq, None) == SHAPE
+    assert r(A, B, 1 << 34, awq, None) == SHAPE
+    assert r(None, B, 16, awq, None) == NULL
+    assert r(A + 4, B, 16, awq, None) == ALIGN
+    assert r(A, A + 32, 16, awq, None) == ALIAS
+    assert r(A, B, 0, awq, None) == OK and r(A, B, 0, None, None) == OK
+    t = lib.mq_int4_transpose
+    assert t(A, B, 12, 64, awq, None) == SHAPE          # A % 8
+    assert t(A, B, 64, 12, awq, None) == SHAPE          # B % 8
+    assert t(A, B, 65536 * 128, 8, awq, None) == SHAPE  # grid rows
+    assert t(A, B, 64, 64, dup, None) == UNSUP
+    assert t(None, B, 64, 64, None, None) == NULL
+    assert t(A + 2, B, 64, 64, None, None) == ALIGN
+    assert t(A, A + 1024, 64, 64, None, None) == ALIAS  # 2 KB of words overlap
+    assert t(A, B, 0, 64, None, None) == OK
+    u = lib.mq_u16_transpose
+    assert u(A, B, 65536 * 64, 8, None) == SHAPE
+    assert u(A, B, 8, (1 << 30) + 1, None) == SHAPE
+    assert u(None, B, 8, 8, None) == NULL
+    assert u(A + 1, B, 8, 8, None) == ALIGN
+    assert u(A, A + 64, 8, 8, None) == ALIAS
+    assert u(A, B, 0, 8, None) == OK

@@ -21,6 +21,10 @@ Entry points (same names as the C ABI, without the ``mq_`` prefix):
 
     kv_quant(x, bits)                                -> (codes, params) per (token, head) row
 
+    int4_reorder(words, order)                       -> words in the library's field order
+    int4_transpose(words, order)                     -> [B, A/8] from a 4-bit [A, B] packed along B
+    u16_transpose(scales)                            -> [B, A] (fp16 scales [N, K/G] -> [K/G, N])
+
 and two compositions used by a model's linear layer:
 
     w4a16_linear(x, qweight, scales, qzeros, group)  GEMV for M <= 64, else GEMM
@@ -38,6 +42,7 @@ __all__ = [
     "w4a16_linear", "w8a8_linear", "GEMV_MAX_M",
     "w4a16_block_weights", "w4a16_gemv_blocked", "w4a16_gemv_blocked_workspace_bytes",
     "w8a8_linear_workspace_bytes", "w4a16_gemm_workspace_bytes", "kv_quant",
+    "AWQ_FIELD_ORDER", "int4_reorder", "int4_transpose", "u16_transpose",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmq.so")
@@ -78,6 +83,9 @@ _PROTOTYPES = {
     "mq_w8a8_linear_workspace_bytes": (ctypes.c_size_t, [_I64, _I64]),
     "mq_kv_quant": (ctypes.c_int, [_P, _P, _P, _I64, _I64, ctypes.c_int32, _P]),
     "mq_w8a8_linear": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
+    "mq_int4_reorder": (ctypes.c_int, [_P, _P, _I64, _P, _P]),
+    "mq_int4_transpose": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P]),
+    "mq_u16_transpose": (ctypes.c_int, [_P, _P, _I64, _I64, _P]),
     "mq_w4a16_gemv_blocked_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I64]),
     "mq_w4a16_gemv_blocked": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t,
                                              _P]),
@@ -375,3 +383,66 @@ def kv_quant(x, bits=8, codes=None, params=None, stream=None):
         _check(library().mq_kv_quant(x.data_ptr(), codes.data_ptr(), params.data_ptr(), rows, D, bits,
                                      _stream_of(x, stream)))
     return codes, params
+
+
+# Field order of AWQ-style checkpoint words: field j holds element
+# 8c + AWQ_FIELD_ORDER[j] of the row's span (a reading; the pages name the
+# format but not its bits).
+AWQ_FIELD_ORDER = (0, 2, 4, 6, 1, 3, 5, 7)
+
+
+def _order_arg(order):
+    if order is None:
+        return None
+    vals = [int(v) for v in order]
+    if len(vals) != 8:
+        raise ValueError("order must have 8 entries")
+    return (ctypes.c_uint8 * 8)(*[v & 0xFF for v in vals])
+
+
+def int4_reorder(src, order, out=None, stream=None):
+    """int32 words of 4-bit values in another field order (field j holding
+    element 8c + order[j]) -> the library's order, same shape (e.g. an
+    AWQ-style qweight [K, N/8] or qzeros [K/G, N/8])."""
+    torch = _torch()
+    if not isinstance(src, torch.Tensor) or src.dtype != torch.int32 or src.device.type != "cuda":
+        raise TypeError("src must be an int32 GPU tensor")
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    out = _out(out, tuple(src.shape), torch.int32, src, "out")
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    with torch.cuda.device(src.device):
+        _check(library().mq_int4_reorder(src.data_ptr(), out.data_ptr(), src.numel(), _order_arg(order),
+                                         _stream_of(src, stream)))
+    return out
+
+
+def int4_transpose(src, order=None, out=None, stream=None):
+    """int32 [A, B/8] (a 4-bit [A, B] matrix packed along B in `order`) ->
+    int32 [B, A/8], its transpose packed along A in the library's order
+    (e.g. weights stored [N, K/8] -> qweight [K, N/8])."""
+    torch = _torch()
+    _dev_tensor(src, "src", torch.int32, 2)
+    A, B = src.shape[0], src.shape[1] * 8
+    if A % 8:
+        raise ValueError("the row count of src must be a multiple of 8")
+    out = _out(out, (B, A // 8), torch.int32, src, "out")
+    with torch.cuda.device(src.device):
+        _check(library().mq_int4_transpose(src.data_ptr(), out.data_ptr(), A, B, _order_arg(order),
+                                           _stream_of(src, stream)))
+    return out
+
+
+def u16_transpose(src, out=None, stream=None):
+    """[A, B] 16-bit tensor (fp16 scales) -> [B, A] (e.g. scales stored
+    [N, K/G] -> [K/G, N])."""
+    torch = _torch()
+    if not isinstance(src, torch.Tensor) or src.dtype not in (torch.float16, torch.int16, torch.bfloat16):
+        raise TypeError("src must be a 16-bit GPU tensor")
+    _dev_tensor(src, "src", src.dtype, 2)
+    A, B = src.shape
+    out = _out(out, (B, A), src.dtype, src, "out")
+    with torch.cuda.device(src.device):
+        _check(library().mq_u16_transpose(src.data_ptr(), out.data_ptr(), A, B, _stream_of(src, stream)))
+    return out

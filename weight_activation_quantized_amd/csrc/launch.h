@@ -43,6 +43,20 @@ hipError_t launch_w8a8_gemv_fused(const uint16_t* x, const int8_t* wq, const flo
 hipError_t launch_kv_quant(const uint16_t* x, uint8_t* codes, float* params, int64_t rows, int64_t head_dim,
                            int bits, hipStream_t stream);
 
+// Checkpoint-layout adapter (one-time conversions, exact bit permutations).
+// order[j] = the element (0..7 within the word's span) that field j of a
+// source word holds; the result is in the library's order (field j = element j).
+hipError_t launch_int4_reorder(const int32_t* src, int32_t* dst, int64_t words, const uint8_t (&order)[8],
+                               hipStream_t stream);
+// src [A, B/8] packed along B in `order` -> dst [B, A/8] packed along A.
+hipError_t launch_int4_transpose(const int32_t* src, int32_t* dst, int64_t A, int64_t B, const uint8_t (&order)[8],
+                                 hipStream_t stream);
+constexpr int64_t kInt4TransposeMaxA = int64_t{65535} * 128;
+// src [A, B] 16-bit -> dst [B, A].
+hipError_t launch_u16_transpose(const uint16_t* src, uint16_t* dst, int64_t A, int64_t B, hipStream_t stream);
+constexpr int64_t kU16TransposeMaxA = int64_t{65535} * 64;
+constexpr int64_t kU16TransposeMaxB = int64_t{1} << 30;
+
 // W4A16 GEMM y[M,N] = x[M,K] . dequant(qweight, scales, qzeros), groups of
 // `group` rows (32, 64 or 128; K % 128 == 0). With a workspace of
 // w4a16_gemm_workspace(M, N, K) bytes, K is split w4a16_gemm_splits ways

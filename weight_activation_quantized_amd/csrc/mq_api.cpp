@@ -302,6 +302,71 @@ mq_status mq_kv_quant(const uint16_t* x, uint8_t* codes, float* params, int64_t 
                     "kv_quant launch");
 }
 
+namespace {
+
+// A field order: NULL means the library's own (field j = element j);
+// otherwise a permutation of 0..7.
+mq_status field_order(const uint8_t* order, uint8_t (&out)[8]) {
+  for (int j = 0; j < 8; ++j) out[j] = static_cast<uint8_t>(j);
+  if (order == nullptr) return MQ_OK;
+  unsigned seen = 0;
+  for (int j = 0; j < 8; ++j) {
+    if (order[j] > 7 || (seen >> order[j]) & 1u)
+      return fail(MQ_ERR_UNSUPPORTED, "field_order must be a permutation of 0..7");
+    seen |= 1u << order[j];
+    out[j] = order[j];
+  }
+  return MQ_OK;
+}
+
+}  // namespace
+
+mq_status mq_int4_reorder(const int32_t* src, int32_t* dst, int64_t words, const uint8_t* order, void* stream) {
+  uint8_t ord[8];
+  MQ_TRY(field_order(order, ord));
+  if (words < 0 || words >= (int64_t{1} << 34))
+    return fail(MQ_ERR_SHAPE, "words=%lld out of range", (long long)words);
+  MQ_TRY(need(src, words, "src"));
+  MQ_TRY(need(dst, words, "dst"));
+  if (!aligned(src, 16) || !aligned(dst, 16)) return fail(MQ_ERR_ALIGN, "src and dst must be 16-byte aligned");
+  const Range in[] = {{src, static_cast<size_t>(words) * 4, "src"}};
+  const Range out[] = {{dst, static_cast<size_t>(words) * 4, "dst"}};
+  MQ_TRY(check_alias(in, out));
+  if (words == 0) return ok();
+  return hip_status(mq::launch_int4_reorder(src, dst, words, ord, as_stream(stream)), "int4_reorder launch");
+}
+
+mq_status mq_int4_transpose(const int32_t* src, int32_t* dst, int64_t A, int64_t B, const uint8_t* order,
+                            void* stream) {
+  uint8_t ord[8];
+  MQ_TRY(field_order(order, ord));
+  if (A < 0 || B < 0 || A % 8 || B % 8)
+    return fail(MQ_ERR_SHAPE, "A=%lld and B=%lld must be non-negative multiples of 8", (long long)A, (long long)B);
+  if (A > mq::kInt4TransposeMaxA || B > kMaxDim || A * B > kMaxElems)
+    return fail(MQ_ERR_SHAPE, "A=%lld, B=%lld too large", (long long)A, (long long)B);
+  MQ_TRY(need(src, A * B, "src"));
+  MQ_TRY(need(dst, A * B, "dst"));
+  if (!aligned(src, 4) || !aligned(dst, 4)) return fail(MQ_ERR_ALIGN, "src and dst must be 4-byte aligned");
+  const Range in[] = {{src, static_cast<size_t>(A * B) / 2, "src"}};
+  const Range out[] = {{dst, static_cast<size_t>(A * B) / 2, "dst"}};
+  MQ_TRY(check_alias(in, out));
+  if (A == 0 || B == 0) return ok();
+  return hip_status(mq::launch_int4_transpose(src, dst, A, B, ord, as_stream(stream)), "int4_transpose launch");
+}
+
+mq_status mq_u16_transpose(const uint16_t* src, uint16_t* dst, int64_t A, int64_t B, void* stream) {
+  if (A < 0 || B < 0 || A > mq::kU16TransposeMaxA || B > mq::kU16TransposeMaxB || A * B > kMaxElems)
+    return fail(MQ_ERR_SHAPE, "A=%lld, B=%lld out of range", (long long)A, (long long)B);
+  MQ_TRY(need(src, A * B, "src"));
+  MQ_TRY(need(dst, A * B, "dst"));
+  if (!aligned(src, 2) || !aligned(dst, 2)) return fail(MQ_ERR_ALIGN, "src and dst must be 2-byte aligned");
+  const Range in[] = {{src, static_cast<size_t>(A * B) * 2, "src"}};
+  const Range out[] = {{dst, static_cast<size_t>(A * B) * 2, "dst"}};
+  MQ_TRY(check_alias(in, out));
+  if (A == 0 || B == 0) return ok();
+  return hip_status(mq::launch_u16_transpose(src, dst, A, B, as_stream(stream)), "u16_transpose launch");
+}
+
 size_t mq_w8a8_linear_workspace_bytes(int64_t M, int64_t K) {
   if (M < 0 || M > kMaxDim || K < 16 || K > kMaxKInt8 || K % 16 || M * K > kMaxElems || M == 0 ||
       mq::w8a8_use_fused(M, K))
