@@ -48,6 +48,8 @@ Also reported (same line):
                INT4) of one layer's K: a 4096-token prefill (32 heads x 128,
                rotating copies >= 320 MB) and a 128-sequence decode append;
                microseconds and GB/s of x + codes + (scale, min).
+  checkpoint   one-time checkpoint-layout conversions at the 8B gate_up size
+               (field reorder, 4-bit transpose, scale transpose), warm.
   cpu_baseline the CPU oracle on one step of the same workload (one weight
                set), repeated for about 10 s, in the same unit.
 """
@@ -100,6 +102,7 @@ def parse_args(argv=None):
     ap.add_argument("--no-layers", action="store_true", help="skip the decoder-layer linear set")
     ap.add_argument("--no-groups", action="store_true", help="skip the group-64 / group-32 measurements")
     ap.add_argument("--no-kv", action="store_true", help="skip the KV-cache quantization measurements")
+    ap.add_argument("--no-checkpoint", action="store_true", help="skip the checkpoint-layout conversions")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-kernel", action="store_true",
@@ -428,6 +431,35 @@ def bench_kv_quant(torch, mq, log):
     return out
 
 
+def bench_checkpoint(torch, mq, log):
+    """One-time checkpoint-layout conversions at the 8B gate_up size: an
+    AWQ-order qweight [4096, 3072] words reordered, a K-packed [24576, 512]
+    transposed to [4096, 3072], and scales [24576, 32] transposed. Each is
+    run 20 times in a graph (the same buffers: warm), microseconds per call
+    and GB/s of read + write."""
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    w_kn = torch.randint(-2 ** 31, 2 ** 31 - 1, (4096, 3072), dtype=torch.int32, device=dev, generator=g)
+    w_nk = torch.randint(-2 ** 31, 2 ** 31 - 1, (24576, 512), dtype=torch.int32, device=dev, generator=g)
+    s_nk = torch.rand((24576, 32), device=dev, generator=g).half()
+    o1, o2 = torch.empty_like(w_kn), torch.empty((4096, 3072), dtype=torch.int32, device=dev)
+    o3 = torch.empty((32, 24576), dtype=torch.float16, device=dev)
+    R = 20
+    out = {}
+    for name, fn, nbytes in (
+            ("int4_reorder_4096x3072", lambda: mq.int4_reorder(w_kn, mq.AWQ_FIELD_ORDER, out=o1), 2 * w_kn.numel() * 4),
+            ("int4_transpose_24576x4096", lambda: mq.int4_transpose(w_nk, mq.AWQ_FIELD_ORDER, out=o2),
+             2 * w_nk.numel() * 4),
+            ("u16_transpose_24576x32", lambda: mq.u16_transpose(s_nk, out=o3), 2 * s_nk.numel() * 2)):
+        log(f"checkpoint: {name}")
+        gr = capture(torch, lambda fn=fn: [fn() for _ in range(R)])
+        gr.replay()
+        t = min(timed_replay(torch, gr)[1] for _ in range(3)) / R
+        out[name] = {"us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1)}
+    return out
+
+
 def cpu_baseline(args, log):
     import numpy as np
 
@@ -542,6 +574,8 @@ def main(argv=None):
         line["groups"] = bench_groups(torch, mq, synth, log)
     if not args.no_kv:
         line["kv_quant"] = bench_kv_quant(torch, mq, log)
+    if not args.no_checkpoint:
+        line["checkpoint"] = bench_checkpoint(torch, mq, log)
     if not args.no_cpu_baseline and rank == 0:
         line["cpu_baseline"] = cpu_baseline(args, log)
     print(json.dumps(line))

@@ -139,3 +139,66 @@ def test_graph_replays_blocked():
             assert np.array_equal(qb.cpu().numpy(), oracle.block_weights_ref(d["qweight"]))
             ref = oracle.w4a16_ref(xr, d["qweight"], d["scales"], d["qzeros"], G)
             assert_fp16_close(y.cpu().numpy(), ref, f"graph blocked {name} replay {r}")
+
+
+def test_graph_replays_kv_and_checkpoint():
+    # KV-cache quantization (both widths, both row-per-group forms) and the
+    # checkpoint-layout conversions in one graph
+    import torch
+    rng = np.random.default_rng(17)
+    xs = [torch.empty((T, 32, 128), dtype=torch.float16, device="cuda") for T in (2100, 7)]
+    w_kn = torch.empty((64, 96), dtype=torch.int32, device="cuda")
+    w_nk = torch.empty((136, 25), dtype=torch.int32, device="cuda")
+    s_nk = torch.empty((70, 130), dtype=torch.float16, device="cuda")
+    order = mq.AWQ_FIELD_ORDER
+
+    def outs():
+        o = []
+        for x in xs:
+            for bits in (8, 4):
+                o.append(torch.empty(x.shape[:-1] + (128 if bits == 8 else 64,), dtype=torch.uint8, device="cuda"))
+                o.append(torch.empty(x.shape[:-1] + (2,), dtype=torch.float32, device="cuda"))
+        o.append(torch.empty_like(w_kn))
+        o.append(torch.empty((200, 17), dtype=torch.int32, device="cuda"))
+        o.append(torch.empty((130, 70), dtype=torch.float16, device="cuda"))
+        return o
+
+    def run(o):
+        i = 0
+        for x in xs:
+            for bits in (8, 4):
+                mq.kv_quant(x, bits, codes=o[i], params=o[i + 1])
+                i += 2
+        mq.int4_reorder(w_kn, order, out=o[i])
+        mq.int4_transpose(w_nk, order, out=o[i + 1])
+        mq.u16_transpose(s_nk, out=o[i + 2])
+
+    announce("graph kv_quant + checkpoint layouts")
+    static = outs()
+    g = _capture(torch, lambda: run(static))
+    for r in range(REPLAYS):
+        xr = [(rng.standard_normal(tuple(x.shape)) * (1 + r)).astype(np.float16) for x in xs]
+        wk = rng.integers(-2 ** 31, 2 ** 31, size=(64, 96), dtype=np.int64).astype(np.int32)
+        wn = rng.integers(-2 ** 31, 2 ** 31, size=(136, 25), dtype=np.int64).astype(np.int32)
+        sn = rng.uniform(0.005, 0.02, (70, 130)).astype(np.float16)
+        for x, a in zip(xs, xr):
+            x.copy_(torch.from_numpy(a))
+        w_kn.copy_(torch.from_numpy(wk))
+        w_nk.copy_(torch.from_numpy(wn))
+        s_nk.copy_(torch.from_numpy(sn))
+        eager = outs()
+        run(eager)
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (got, want) in enumerate(zip(static, eager)):
+            assert torch.equal(got, want), f"replay {r}: output {k} differs from the eager call"
+        i = 0
+        for a in xr:
+            for bits in (8, 4):
+                rc, rp = oracle.kv_quant_ref(a.reshape(-1, 128), bits)
+                assert np.array_equal(static[i].cpu().numpy().reshape(rc.shape), rc)
+                assert np.array_equal(static[i + 1].cpu().numpy().reshape(-1, 2).view(np.uint32), rp.view(np.uint32))
+                i += 2
+        assert np.array_equal(static[i].cpu().numpy(), oracle.reorder_int4_ref(wk, order))
+        assert np.array_equal(static[i + 1].cpu().numpy(), oracle.transpose_int4_ref(wn, order))
+        assert np.array_equal(static[i + 2].cpu().numpy().view(np.uint16), sn.T.view(np.uint16))
