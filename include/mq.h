@@ -153,6 +153,26 @@ mq_status mq_w8a8_linear(const uint16_t* x, const int8_t* wq, const float* s_ch,
                          int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * bf16 forms of the three entries above, for models whose activations are
+ * bf16. Source: pymllm Setup and Usage, Overview (BF16 is one of the
+ * runtime's schemes beside W4A16 and W8A8_INT8, so the quantized layers sit
+ * among bf16 activations). x is bf16 (raw bits) instead of fp16 and y is
+ * bf16 instead of fp16; everything else -- layouts, requirements, errors,
+ * workspace sizes and the kernels chosen -- is as in the fp16 entry.
+ *   mq_quant_per_token_int8_bf16: bf16 widens exactly to binary32, so the
+ *     scales and codes follow the same definition bit for bit.
+ *   mq_w8a8_scaled_mm_bf16: y[m,n] = bf16_rne( fl32( fl32(acc) * s_tok[m] ) * s_ch[n] ).
+ *   mq_w8a8_linear_bf16: quantizer and scaled GEMM as above, bit-identical to
+ *     the two calls in sequence.
+ */
+mq_status mq_quant_per_token_int8_bf16(const uint16_t* x, int8_t* xq, float* s_tok, int64_t M, int64_t K,
+                                       void* stream);
+mq_status mq_w8a8_scaled_mm_bf16(const int8_t* xq, const float* s_tok, const int8_t* wq, const float* s_ch,
+                                 uint16_t* y, int64_t M, int64_t N, int64_t K, void* stream);
+mq_status mq_w8a8_linear_bf16(const uint16_t* x, const int8_t* wq, const float* s_ch, uint16_t* y, int64_t M,
+                              int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * W4A16 GEMM (prefill-shaped M).
  * Source: LMDeploy toolkit overview, section 2.5 (4-bit AWQ weights, group
  * size 128); LMDeploy 4-bit deployment guide, section 2.2 (dequantization

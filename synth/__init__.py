@@ -13,7 +13,8 @@ configurations:
   zero points uniform 4-bit; fp16 group scales uniform in [0.005, 0.02].
 * W8A8: activations fp16 ~ N(0, 1) with 1% outlier channels x20; float
   weights ~ N(0, 0.02) rounded to fp16 (each side quantizes them per output
-  channel with its own quantizer).
+  channel with its own quantizer). The bf16 form draws the same activations
+  and rounds them to bf16 instead.
 
 Every draw comes from ``numpy.random.default_rng`` seeded by a
 ``SeedSequence`` of integers, with children spawned in a fixed order, so a
@@ -83,6 +84,32 @@ def w8a8_inputs(M, K, N, outlier_frac=0.01, tag=0, seed=0):
         "x": activations(r_x, r_idx, M, K, outlier_frac),
         "wf": wf.astype(np.float16),
     }
+
+
+def bf16_bits(x32):
+    """bfloat16 bit patterns (uint16) of float32 values, rounded to nearest
+    even (finite inputs): how a bf16 activation tensor is drawn."""
+    b = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def bf16_values(bits):
+    """float32 values of bfloat16 bit patterns (exact: the upper half of a binary32)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def w8a8_inputs_bf16(M, K, N, outlier_frac=0.01, tag=0, seed=0):
+    """As ``w8a8_inputs`` with bf16 activations: dict(x_bits uint16 [M,K],
+    x float32 [M,K] (the same values), wf fp16 [N,K])."""
+    r_x, r_idx, r_w = _children(tag, seed, 3)
+    x = r_x.standard_normal((M, K), dtype=np.float32)
+    n_out = int(round(outlier_frac * K))
+    if n_out:
+        idx = r_idx.choice(K, size=n_out, replace=False)
+        x[:, idx] *= np.float32(OUTLIER_GAIN)
+    bits = bf16_bits(x)
+    wf = r_w.normal(0.0, WEIGHT_STD, size=(N, K)).astype(np.float32)
+    return {"x_bits": bits, "x": bf16_values(bits), "wf": wf.astype(np.float16)}
 
 
 # Benchmark workloads (name -> shape recipe). Tags keep seeds of different

@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
               "mq_w4a16_gemv", "mq_w4a16_gemv_workspace_bytes", "mq_w4a16_block_weights",
               "mq_w4a16_gemv_blocked", "mq_w4a16_gemv_blocked_workspace_bytes", "mq_w8a8_linear",
               "mq_w8a8_linear_workspace_bytes", "mq_w4a16_gemm_workspace_bytes", "mq_kv_quant", "mq_abi_version",
-              "mq_status_string", "mq_last_error", "mq_int4_reorder", "mq_int4_transpose", "mq_u16_transpose"]:
+              "mq_status_string", "mq_last_error", "mq_int4_reorder", "mq_int4_transpose", "mq_u16_transpose",
+              "mq_quant_per_token_int8_bf16", "mq_w8a8_scaled_mm_bf16", "mq_w8a8_linear_bf16"]:
         assert n in names
 
 
@@ -299,3 +300,21 @@ def test_checkpoint_layout_validation(lib):
     assert u(A + 1, B, 8, 8, None) == ALIGN
     assert u(A, A + 64, 8, 8, None) == ALIAS
     assert u(A, B, 0, 8, None) == OK
+
+
+def test_bf16_entries_validate_like_fp16(lib):
+    q, q16 = lib.mq_quant_per_token_int8_bf16, lib.mq_quant_per_token_int8
+    for args in ((A, B, C, 4, 40, None), (None, B, C, 4, 64, None), (A + 8, B, C, 4, 64, None),
+                 (A, A + 16, C, 4, 64, None), (A, B, C, 0, 64, None)):
+        assert q(*args) == q16(*args)
+    assert q(A, B, C, 4, 40, None) == SHAPE and q(A, B, C, 0, 64, None) == OK
+    f, f16 = lib.mq_w8a8_scaled_mm_bf16, lib.mq_w8a8_scaled_mm
+    for args in ((A, B, C, D, E, 4, 64, 40, None), (A, B, C, D, A + 16, 4, 64, 64, None),
+                 (A, B, C, D, E + 8, 4, 64, 64, None), (A, B, C, D, E, 0, 64, 64, None)):
+        assert f(*args) == f16(*args)
+    assert f(A, B, C, D, E, 4, 64, 133152, None) == SHAPE
+    g, g16 = lib.mq_w8a8_linear_bf16, lib.mq_w8a8_linear
+    for args in ((A, B, C, E, 4, 64, 40, None, 0, None), (A, B, C, A + 16, 1, 64, 64, None, 0, None),
+                 (A, B, C, E, 32, 64, 64, None, 0, None), (A, B, C, E, 0, 64, 64, None, 0, None)):
+        assert g(*args) == g16(*args)
+    assert g(A, B, C, E, 32, 64, 64, None, 0, None) == WS

@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 import oracle
+import synth
 from tests import oracle_pins as P
 
 # ---------------------------------------------------------------------------
@@ -356,3 +357,17 @@ def test_int4_checkpoint_mutants_caught(mode):
 
     with pytest.raises(AssertionError):
         P.check_int4_checkpoint(reorder, transpose, pack)
+
+
+def test_bf16_input_generator():
+    # bf16 rounding of the generator: exact values stay, ties go to even,
+    # and the values are the upper halves of binary32 words
+    x = np.array([1.0, -2.5, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, 3.0e38, -0.0], np.float32)
+    b = synth.bf16_bits(x)
+    assert b.tolist() == [0x3F80, 0xC020, 0x3F80, 0x3F82, 0x3F80, 0x7F62, 0x8000]
+    v = synth.bf16_values(b)
+    assert v[0] == 1.0 and v[1] == -2.5 and v[3] == np.float32(1.0 + 2 ** -6)
+    d = synth.w8a8_inputs_bf16(3, 64, 8, tag=9)
+    assert np.array_equal(synth.bf16_bits(d["x"]), d["x_bits"])
+    x16 = synth.w8a8_inputs(3, 64, 8, tag=9)["x"].astype(np.float32)  # the same draw rounded to fp16
+    assert np.all(np.abs(d["x"] - x16) <= 2 ** -7 * np.abs(x16) + 1e-7)

@@ -8,8 +8,8 @@ library is missing or the tensors are not on a GPU, the call raises.
 
 Entry points (same names as the C ABI, without the ``mq_`` prefix):
 
-    quant_per_token_int8(x)                          -> (xq, s_tok)
-    w8a8_scaled_mm(xq, s_tok, wq, s_ch)              -> y  (fp16)
+    quant_per_token_int8(x)                          -> (xq, s_tok); x fp16 or bf16
+    w8a8_scaled_mm(xq, s_tok, wq, s_ch)              -> y  (fp16, or bf16 with out_dtype)
     w8a8_mm_i32(xq, wq)                              -> acc (int32)
     w4a16_gemm(x, qweight, scales, qzeros, group)    -> y  (fp16); K split on small grids
     w4a16_gemm_workspace_bytes(M, N, K, group)       -> int
@@ -28,7 +28,7 @@ Entry points (same names as the C ABI, without the ``mq_`` prefix):
 and two compositions used by a model's linear layer:
 
     w4a16_linear(x, qweight, scales, qzeros, group)  GEMV for M <= 64, else GEMM
-    w8a8_linear(x, wq, s_ch)                         quantize x per token, then scaled GEMM
+    w8a8_linear(x, wq, s_ch)                         quantize x (fp16 or bf16) per token, then scaled GEMM
                                                      (one fused kernel for M <= 16)
 """
 
@@ -83,6 +83,9 @@ _PROTOTYPES = {
     "mq_w8a8_linear_workspace_bytes": (ctypes.c_size_t, [_I64, _I64]),
     "mq_kv_quant": (ctypes.c_int, [_P, _P, _P, _I64, _I64, ctypes.c_int32, _P]),
     "mq_w8a8_linear": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
+    "mq_quant_per_token_int8_bf16": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
+    "mq_w8a8_scaled_mm_bf16": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "mq_w8a8_linear_bf16": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
     "mq_int4_reorder": (ctypes.c_int, [_P, _P, _I64, _P, _P]),
     "mq_int4_transpose": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P]),
     "mq_u16_transpose": (ctypes.c_int, [_P, _P, _I64, _I64, _P]),
@@ -154,21 +157,33 @@ def _out(out, shape, dtype, like, name):
     return out
 
 
-def quant_per_token_int8(x, out=None, s_out=None, stream=None):
-    """Per-token int8 quantization of fp16 x[M, K] -> (xq int8 [M, K], s_tok fp32 [M])."""
+def _half_dtype(t, name):
+    """fp16 or bf16: the activation dtypes the entry points take."""
     torch = _torch()
-    _dev_tensor(x, "x", torch.float16, 2)
+    if isinstance(t, torch.Tensor) and t.dtype == torch.bfloat16:
+        return torch.bfloat16
+    if isinstance(t, torch.Tensor) and t.dtype == torch.float16:
+        return torch.float16
+    raise TypeError(f"{name} must be a float16 or bfloat16 tensor")
+
+
+def quant_per_token_int8(x, out=None, s_out=None, stream=None):
+    """Per-token int8 quantization of fp16 or bf16 x[M, K] -> (xq int8 [M, K], s_tok fp32 [M])."""
+    torch = _torch()
+    dt = _half_dtype(x, "x")
+    _dev_tensor(x, "x", dt, 2)
     M, K = x.shape
     xq = _out(out, (M, K), torch.int8, x, "out")
     s = _out(s_out, (M,), torch.float32, x, "s_out")
+    fn = library().mq_quant_per_token_int8_bf16 if dt == torch.bfloat16 else library().mq_quant_per_token_int8
     with torch.cuda.device(x.device):
-        _check(library().mq_quant_per_token_int8(x.data_ptr(), xq.data_ptr(), s.data_ptr(), M, K,
-                                                 _stream_of(x, stream)))
+        _check(fn(x.data_ptr(), xq.data_ptr(), s.data_ptr(), M, K, _stream_of(x, stream)))
     return xq, s
 
 
-def w8a8_scaled_mm(xq, s_tok, wq, s_ch, out=None, stream=None):
-    """y[M, N] fp16 = (xq[M, K] . wq[N, K]^T) * s_tok[:, None] * s_ch[None, :]."""
+def w8a8_scaled_mm(xq, s_tok, wq, s_ch, out=None, stream=None, out_dtype=None):
+    """y[M, N] = (xq[M, K] . wq[N, K]^T) * s_tok[:, None] * s_ch[None, :] in
+    fp16 (default) or bf16 (``out_dtype=torch.bfloat16``, or a bf16 ``out``)."""
     torch = _torch()
     _dev_tensor(xq, "xq", torch.int8, 2)
     _dev_tensor(wq, "wq", torch.int8, 2)
@@ -178,10 +193,15 @@ def w8a8_scaled_mm(xq, s_tok, wq, s_ch, out=None, stream=None):
     N = wq.shape[0]
     if wq.shape[1] != K or s_tok.shape[0] != M or s_ch.shape[0] != N:
         raise ValueError("shape mismatch between xq, s_tok, wq and s_ch")
-    y = _out(out, (M, N), torch.float16, xq, "out")
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.float16
+    if out_dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("out_dtype must be float16 or bfloat16")
+    y = _out(out, (M, N), out_dtype, xq, "out")
+    fn = library().mq_w8a8_scaled_mm_bf16 if out_dtype == torch.bfloat16 else library().mq_w8a8_scaled_mm
     with torch.cuda.device(xq.device):
-        _check(library().mq_w8a8_scaled_mm(xq.data_ptr(), s_tok.data_ptr(), wq.data_ptr(), s_ch.data_ptr(),
-                                           y.data_ptr(), M, N, K, _stream_of(xq, stream)))
+        _check(fn(xq.data_ptr(), s_tok.data_ptr(), wq.data_ptr(), s_ch.data_ptr(), y.data_ptr(), M, N, K,
+                  _stream_of(xq, stream)))
     return y
 
 
@@ -341,26 +361,29 @@ def w8a8_linear_workspace_bytes(M, K):
 
 
 def w8a8_linear(x, wq, s_ch, out=None, workspace=None, stream=None):
-    """W8A8_INT8 linear layer from fp16 x: per-token int8 quantization, then the
-    scaled int8 GEMM (one fused kernel for M <= 16). Bit-identical to
-    ``w8a8_scaled_mm(*quant_per_token_int8(x), wq, s_ch)``."""
+    """W8A8_INT8 linear layer from fp16 or bf16 x (y in x's dtype): per-token
+    int8 quantization, then the scaled int8 GEMM (one fused kernel for one
+    token). Bit-identical to ``w8a8_scaled_mm(*quant_per_token_int8(x), wq,
+    s_ch, out_dtype=x.dtype)``."""
     torch = _torch()
-    _dev_tensor(x, "x", torch.float16, 2)
+    dt = _half_dtype(x, "x")
+    _dev_tensor(x, "x", dt, 2)
     _dev_tensor(wq, "wq", torch.int8, 2)
     _dev_tensor(s_ch, "s_ch", torch.float32, 1)
     M, K = x.shape
     N = wq.shape[0]
     if wq.shape[1] != K or s_ch.shape[0] != N:
         raise ValueError("wq must be [N, K] and s_ch [N]")
-    y = _out(out, (M, N), torch.float16, x, "out")
+    y = _out(out, (M, N), dt, x, "out")
     need = w8a8_linear_workspace_bytes(M, K)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     with torch.cuda.device(x.device):
-        _check(library().mq_w8a8_linear(x.data_ptr(), wq.data_ptr(), s_ch.data_ptr(), y.data_ptr(), M, N, K,
-                                        ws_ptr, ws_bytes, _stream_of(x, stream)))
+        fn = library().mq_w8a8_linear_bf16 if dt == torch.bfloat16 else library().mq_w8a8_linear
+        _check(fn(x.data_ptr(), wq.data_ptr(), s_ch.data_ptr(), y.data_ptr(), M, N, K, ws_ptr, ws_bytes,
+                  _stream_of(x, stream)))
     return y
 
 

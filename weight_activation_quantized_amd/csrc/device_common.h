@@ -31,6 +31,30 @@ __device__ __forceinline__ float wave_max(float v) {
 __device__ __forceinline__ f16x2 as_f16x2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 __device__ __forceinline__ uint32_t as_u32(f16x2 h) { return __builtin_bit_cast(uint32_t, h); }
 
+// A binary32 rounded to nearest even as fp16 or bf16, returned as raw bits.
+template <bool kBf16>
+__device__ __forceinline__ uint16_t half_bits(float v) {
+  if constexpr (kBf16) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+  } else {
+    return __builtin_bit_cast(uint16_t, static_cast<f16>(v));
+  }
+}
+
+// The two 16-bit values of a word (fp16, or bf16 = the upper half of a
+// binary32) as floats; both widen exactly.
+template <bool kBf16>
+__device__ __forceinline__ void word_to_floats(uint32_t w, float& lo, float& hi) {
+  if constexpr (kBf16) {
+    lo = __builtin_bit_cast(float, w << 16);
+    hi = __builtin_bit_cast(float, w & 0xFFFF0000u);
+  } else {
+    const f16x2 h = __builtin_bit_cast(f16x2, w);
+    lo = static_cast<float>(h[0]);
+    hi = static_cast<float>(h[1]);
+  }
+}
+
 // Byte permute of two dwords: output byte i = byte sel[i] of the 8-byte value
 // {hi:lo} (selectors 0-3 pick bytes of lo, 4-7 bytes of hi).
 __device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo, uint32_t sel) {

@@ -8,15 +8,17 @@
 
 namespace mq {
 
-// Per-token int8 quantization of x[M,K] (fp16) into xq[M,K] and s_tok[M].
-hipError_t launch_quant_per_token_int8(const uint16_t* x, int8_t* xq, float* s_tok,
-                                       int64_t M, int64_t K, hipStream_t stream);
+// Per-token int8 quantization of x[M,K] (fp16, or bf16 when bf16) into
+// xq[M,K] and s_tok[M].
+hipError_t launch_quant_per_token_int8(const uint16_t* x, int8_t* xq, float* s_tok, int64_t M, int64_t K, bool bf16,
+                                       hipStream_t stream);
 
-// int8 GEMM acc = xq[M,K] . wq[N,K]^T. Exactly one of y (scaled fp16 output,
-// needs s_tok and s_ch) and acc (raw int32 output) is non-null.
+// int8 GEMM acc = xq[M,K] . wq[N,K]^T. Exactly one of y (scaled output,
+// fp16 or, when bf16, bf16; needs s_tok and s_ch) and acc (raw int32 output)
+// is non-null.
 hipError_t launch_w8a8_gemm(const int8_t* xq, const float* s_tok, const int8_t* wq,
                             const float* s_ch, uint16_t* y, int32_t* acc,
-                            int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                            int64_t M, int64_t N, int64_t K, bool bf16, hipStream_t stream);
 
 // Decode-shaped form of the same product (M <= kW8A8GemvMaxM), bound by the
 // weight stream; launch_w8a8_gemm dispatches to it where w8a8_use_gemv says.
@@ -24,7 +26,7 @@ constexpr int64_t kW8A8GemvMaxM = 64;
 bool w8a8_use_gemv(int64_t M, int64_t N);
 hipError_t launch_w8a8_gemv(const int8_t* xq, const float* s_tok, const int8_t* wq,
                             const float* s_ch, uint16_t* y, int32_t* acc,
-                            int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                            int64_t M, int64_t N, int64_t K, bool bf16, hipStream_t stream);
 
 // Quantizer folded into the decode kernel: y = scaled_mm(quant(x), wq, s_ch)
 // in one launch, bit-identical to the two separate calls, where
@@ -35,7 +37,7 @@ hipError_t launch_w8a8_gemv(const int8_t* xq, const float* s_tok, const int8_t* 
 constexpr int64_t kW8A8FusedMaxM = 1;
 bool w8a8_use_fused(int64_t M, int64_t K);
 hipError_t launch_w8a8_gemv_fused(const uint16_t* x, const int8_t* wq, const float* s_ch, uint16_t* y,
-                                  int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                                  int64_t M, int64_t N, int64_t K, bool bf16, hipStream_t stream);
 
 // Online KV-cache quantization of rows x [rows, head_dim] fp16 to codes
 // (uint8 [rows, head_dim] for 8 bits, packed [rows, head_dim/2] for 4) and

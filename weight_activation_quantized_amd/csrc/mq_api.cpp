@@ -152,8 +152,8 @@ const char* mq_status_string(mq_status s) {
 
 const char* mq_last_error(void) { return g_last_error; }
 
-mq_status mq_quant_per_token_int8(const uint16_t* x, int8_t* xq, float* s_tok,
-                                  int64_t M, int64_t K, void* stream) {
+static mq_status quant_impl(const uint16_t* x, int8_t* xq, float* s_tok, int64_t M, int64_t K, bool bf16,
+                            void* stream) {
   mq_status s = check_mk(M, K, 16, kMaxK, 16);
   if (s != MQ_OK) return s;
   MQ_TRY(need(x, M * K, "x"));
@@ -166,13 +166,21 @@ mq_status mq_quant_per_token_int8(const uint16_t* x, int8_t* xq, float* s_tok,
   s = check_alias(in, out);
   if (s != MQ_OK) return s;
   if (M == 0) return ok();
-  return hip_status(mq::launch_quant_per_token_int8(x, xq, s_tok, M, K, as_stream(stream)),
+  return hip_status(mq::launch_quant_per_token_int8(x, xq, s_tok, M, K, bf16, as_stream(stream)),
                     "quant_per_token_int8 launch");
 }
 
-mq_status mq_w8a8_scaled_mm(const int8_t* xq, const float* s_tok, const int8_t* wq,
-                            const float* s_ch, uint16_t* y,
-                            int64_t M, int64_t N, int64_t K, void* stream) {
+mq_status mq_quant_per_token_int8(const uint16_t* x, int8_t* xq, float* s_tok, int64_t M, int64_t K, void* stream) {
+  return quant_impl(x, xq, s_tok, M, K, false, stream);
+}
+
+mq_status mq_quant_per_token_int8_bf16(const uint16_t* x, int8_t* xq, float* s_tok, int64_t M, int64_t K,
+                                       void* stream) {
+  return quant_impl(x, xq, s_tok, M, K, true, stream);
+}
+
+static mq_status scaled_mm_impl(const int8_t* xq, const float* s_tok, const int8_t* wq, const float* s_ch, uint16_t* y,
+                                int64_t M, int64_t N, int64_t K, bool bf16, void* stream) {
   mq_status s = check_w8a8(xq, wq, y, 2, M, N, K);
   if (s != MQ_OK) return s;
   MQ_TRY(need(s_tok, M, "s_tok"));
@@ -186,8 +194,18 @@ mq_status mq_w8a8_scaled_mm(const int8_t* xq, const float* s_tok, const int8_t* 
   s = check_alias(in, out);
   if (s != MQ_OK) return s;
   if (M == 0 || N == 0) return ok();
-  return hip_status(mq::launch_w8a8_gemm(xq, s_tok, wq, s_ch, y, nullptr, M, N, K, as_stream(stream)),
+  return hip_status(mq::launch_w8a8_gemm(xq, s_tok, wq, s_ch, y, nullptr, M, N, K, bf16, as_stream(stream)),
                     "w8a8_scaled_mm launch");
+}
+
+mq_status mq_w8a8_scaled_mm(const int8_t* xq, const float* s_tok, const int8_t* wq, const float* s_ch, uint16_t* y,
+                            int64_t M, int64_t N, int64_t K, void* stream) {
+  return scaled_mm_impl(xq, s_tok, wq, s_ch, y, M, N, K, false, stream);
+}
+
+mq_status mq_w8a8_scaled_mm_bf16(const int8_t* xq, const float* s_tok, const int8_t* wq, const float* s_ch,
+                                 uint16_t* y, int64_t M, int64_t N, int64_t K, void* stream) {
+  return scaled_mm_impl(xq, s_tok, wq, s_ch, y, M, N, K, true, stream);
 }
 
 mq_status mq_w8a8_mm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc,
@@ -199,7 +217,7 @@ mq_status mq_w8a8_mm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc,
   s = check_alias(in, out);
   if (s != MQ_OK) return s;
   if (M == 0 || N == 0) return ok();
-  return hip_status(mq::launch_w8a8_gemm(xq, nullptr, wq, nullptr, nullptr, acc, M, N, K, as_stream(stream)),
+  return hip_status(mq::launch_w8a8_gemm(xq, nullptr, wq, nullptr, nullptr, acc, M, N, K, false, as_stream(stream)),
                     "w8a8_mm_i32 launch");
 }
 
@@ -374,8 +392,8 @@ size_t mq_w8a8_linear_workspace_bytes(int64_t M, int64_t K) {
   return (static_cast<size_t>(M * K) + 255) / 256 * 256 + static_cast<size_t>(M) * 4;
 }
 
-mq_status mq_w8a8_linear(const uint16_t* x, const int8_t* wq, const float* s_ch, uint16_t* y,
-                         int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+static mq_status linear_impl(const uint16_t* x, const int8_t* wq, const float* s_ch, uint16_t* y, int64_t M,
+                             int64_t N, int64_t K, void* workspace, size_t workspace_bytes, bool bf16, void* stream) {
   mq_status s = check_mk(M, K, 16, kMaxKInt8, 16);
   if (s != MQ_OK) return s;
   if (N < 0 || N > kMaxDim) return fail(MQ_ERR_SHAPE, "N=%lld out of range", (long long)N);
@@ -402,13 +420,25 @@ mq_status mq_w8a8_linear(const uint16_t* x, const int8_t* wq, const float* s_ch,
   if (s != MQ_OK) return s;
   if (M == 0 || N == 0) return ok();
   if (mq::w8a8_use_fused(M, K))
-    return hip_status(mq::launch_w8a8_gemv_fused(x, wq, s_ch, y, M, N, K, as_stream(stream)), "w8a8_linear launch");
+    return hip_status(mq::launch_w8a8_gemv_fused(x, wq, s_ch, y, M, N, K, bf16, as_stream(stream)),
+                      "w8a8_linear launch");
   int8_t* xq = static_cast<int8_t*>(workspace);
   float* s_tok = reinterpret_cast<float*>(static_cast<char*>(workspace) + (static_cast<size_t>(M * K) + 255) / 256 * 256);
-  s = hip_status(mq::launch_quant_per_token_int8(x, xq, s_tok, M, K, as_stream(stream)), "w8a8_linear quant launch");
+  s = hip_status(mq::launch_quant_per_token_int8(x, xq, s_tok, M, K, bf16, as_stream(stream)),
+                 "w8a8_linear quant launch");
   if (s != MQ_OK) return s;
-  return hip_status(mq::launch_w8a8_gemm(xq, s_tok, wq, s_ch, y, nullptr, M, N, K, as_stream(stream)),
+  return hip_status(mq::launch_w8a8_gemm(xq, s_tok, wq, s_ch, y, nullptr, M, N, K, bf16, as_stream(stream)),
                     "w8a8_linear gemm launch");
+}
+
+mq_status mq_w8a8_linear(const uint16_t* x, const int8_t* wq, const float* s_ch, uint16_t* y, int64_t M, int64_t N,
+                         int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  return linear_impl(x, wq, s_ch, y, M, N, K, workspace, workspace_bytes, false, stream);
+}
+
+mq_status mq_w8a8_linear_bf16(const uint16_t* x, const int8_t* wq, const float* s_ch, uint16_t* y, int64_t M,
+                              int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  return linear_impl(x, wq, s_ch, y, M, N, K, workspace, workspace_bytes, true, stream);
 }
 
 mq_status mq_w4a16_block_weights(const int32_t* qweight, int32_t* qweight_blocked, int64_t N, int64_t K,

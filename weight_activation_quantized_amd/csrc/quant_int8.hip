@@ -8,8 +8,10 @@
 // half to even, bit for bit: a reciprocal product decides every element that
 // is not close to a half-integer, the IEEE division the rest.
 //
+// x is fp16 or bf16 (both widen exactly to binary32, so the same codes and
+// scales follow from the same arithmetic).
 // One wavefront per row, four rows per workgroup. Each lane holds its share
-// of the row in registers (16-byte chunks of 8 fp16), so x is read from HBM
+// of the row in registers (16-byte chunks of 8 values), so x is read from HBM
 // exactly once: absmax by a wavefront butterfly, then quantize from registers
 // and store 8 codes per 8-byte store. Rows longer than 64*8*32 elements take
 // a two-pass variant that re-reads x.
@@ -21,12 +23,14 @@ namespace {
 
 constexpr int kRowsPerBlock = 4;
 
+template <bool kBf16>
 __device__ __forceinline__ float chunk_absmax(u32x4 v, float m) {
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    f16x2 h = as_f16x2(v[w]);
-    m = fmaxf(m, fabsf(static_cast<float>(h[0])));
-    m = fmaxf(m, fabsf(static_cast<float>(h[1])));
+    float lo, hi;
+    word_to_floats<kBf16>(v[w], lo, hi);
+    m = fmaxf(m, fabsf(lo));
+    m = fmaxf(m, fabsf(hi));
   }
   return m;
 }
@@ -43,19 +47,28 @@ constexpr float kTieMargin = 1.0f / 4096.0f;
 // quotient lies on the same side of the nearest half-integer as p and rounds
 // to the same integer; only elements within the margin (about 1 in 2000)
 // take the IEEE division, whose correctly rounded result decides ties.
+// Written so that a non-finite p (a binary32-subnormal s, possible for bf16
+// rows with absmax below 127 * 2^-126, whose reciprocal overflows) also
+// takes the division.
 __device__ __forceinline__ float code_of(float v, float s, float r) {
   const float p = v * r;
   const float t = rintf(p);
-  if (0.5f - fabsf(p - t) < kTieMargin) return rintf(v / s);
+  if (!(0.5f - fabsf(p - t) >= kTieMargin)) return rintf(v / s);
   return t;
 }
 
-__device__ __forceinline__ uint32_t quant4(f16x2 a, f16x2 b, float s, float r) {
+// The reciprocal code_of multiplies by: rcp(s) for a normal s; infinity for a
+// binary32-subnormal s (then every product is non-finite and code_of divides).
+__device__ __forceinline__ float code_rcp(float s) {
+  return s < 1.17549435e-38f ? __builtin_inff() : __builtin_amdgcn_rcpf(s);
+}
+
+__device__ __forceinline__ uint32_t quant4(float a0, float a1, float b0, float b1, float s, float r) {
   // s > 0 here: the codes of the IEEE quotient, rounded half to even.
-  float q0 = code_of(static_cast<float>(a[0]), s, r);
-  float q1 = code_of(static_cast<float>(a[1]), s, r);
-  float q2 = code_of(static_cast<float>(b[0]), s, r);
-  float q3 = code_of(static_cast<float>(b[1]), s, r);
+  float q0 = code_of(a0, s, r);
+  float q1 = code_of(a1, s, r);
+  float q2 = code_of(b0, s, r);
+  float q3 = code_of(b1, s, r);
   q0 = fminf(fmaxf(q0, -127.f), 127.f);
   q1 = fminf(fmaxf(q1, -127.f), 127.f);
   q2 = fminf(fmaxf(q2, -127.f), 127.f);
@@ -67,11 +80,15 @@ __device__ __forceinline__ uint32_t quant4(f16x2 a, f16x2 b, float s, float r) {
   return packed;
 }
 
+template <bool kBf16>
 __device__ __forceinline__ u32x2 quant_chunk(u32x4 v, float s, float r) {
   u32x2 out;
   if (s > 0.f) {
-    out[0] = quant4(as_f16x2(v[0]), as_f16x2(v[1]), s, r);
-    out[1] = quant4(as_f16x2(v[2]), as_f16x2(v[3]), s, r);
+    float f[8];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) word_to_floats<kBf16>(v[w], f[2 * w], f[2 * w + 1]);
+    out[0] = quant4(f[0], f[1], f[2], f[3], s, r);
+    out[1] = quant4(f[4], f[5], f[6], f[7], s, r);
   } else {
     out[0] = 0u;
     out[1] = 0u;
@@ -80,7 +97,7 @@ __device__ __forceinline__ u32x2 quant_chunk(u32x4 v, float s, float r) {
 }
 
 // CPL = 16-byte chunks per lane kept in registers (row length <= 512*CPL).
-template <int CPL>
+template <int CPL, bool kBf16>
 __global__ __launch_bounds__(256) void quant_rows_regs(const uint16_t* __restrict__ x,
                                                        int8_t* __restrict__ xq,
                                                        float* __restrict__ s_tok, int M, int K) {
@@ -101,20 +118,21 @@ __global__ __launch_bounds__(256) void quant_rows_regs(const uint16_t* __restric
     } else {
       v[i] = u32x4{0u, 0u, 0u, 0u};
     }
-    amax = chunk_absmax(v[i], amax);
+    amax = chunk_absmax<kBf16>(v[i], amax);
   }
   amax = wave_max(amax);
   const float s = amax / 127.0f;
-  const float r = __builtin_amdgcn_rcpf(s);
+  const float r = code_rcp(s);
   if (lane == 0) s_tok[row] = s;
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
     const int c = lane + kWave * i;
-    if (c < nchunk) *reinterpret_cast<u32x2*>(qr + 8 * c) = quant_chunk(v[i], s, r);
+    if (c < nchunk) *reinterpret_cast<u32x2*>(qr + 8 * c) = quant_chunk<kBf16>(v[i], s, r);
   }
 }
 
 // Any row length: absmax pass, then a second pass that re-reads x.
+template <bool kBf16>
 __global__ __launch_bounds__(256) void quant_rows_stream(const uint16_t* __restrict__ x,
                                                          int8_t* __restrict__ xq,
                                                          float* __restrict__ s_tok, int M, int K) {
@@ -126,37 +144,42 @@ __global__ __launch_bounds__(256) void quant_rows_stream(const uint16_t* __restr
   int8_t* qr = xq + static_cast<size_t>(row) * K;
   float amax = 0.f;
   for (int c = lane; c < nchunk; c += kWave)
-    amax = chunk_absmax(*reinterpret_cast<const u32x4*>(xr + 8 * c), amax);
+    amax = chunk_absmax<kBf16>(*reinterpret_cast<const u32x4*>(xr + 8 * c), amax);
   amax = wave_max(amax);
   const float s = amax / 127.0f;
-  const float r = __builtin_amdgcn_rcpf(s);
+  const float r = code_rcp(s);
   if (lane == 0) s_tok[row] = s;
   for (int c = lane; c < nchunk; c += kWave)
-    *reinterpret_cast<u32x2*>(qr + 8 * c) = quant_chunk(*reinterpret_cast<const u32x4*>(xr + 8 * c), s, r);
+    *reinterpret_cast<u32x2*>(qr + 8 * c) = quant_chunk<kBf16>(*reinterpret_cast<const u32x4*>(xr + 8 * c), s, r);
 }
 
-}  // namespace
-
-hipError_t launch_quant_per_token_int8(const uint16_t* x, int8_t* xq, float* s_tok,
-                                       int64_t M, int64_t K, hipStream_t stream) {
+template <bool kBf16>
+hipError_t launch_quant(const uint16_t* x, int8_t* xq, float* s_tok, int64_t M, int64_t K, hipStream_t stream) {
   const int m = static_cast<int>(M), k = static_cast<int>(K);
   const dim3 grid((m + kRowsPerBlock - 1) / kRowsPerBlock), block(256);
   const int per_lane = ((k >> 3) + kWave - 1) / kWave;
   if (per_lane <= 1) {
-    return launch_kernel(quant_rows_regs<1>, grid, block, 0, stream, x, xq, s_tok, m, k);
+    return launch_kernel(quant_rows_regs<1, kBf16>, grid, block, 0, stream, x, xq, s_tok, m, k);
   } else if (per_lane <= 2) {
-    return launch_kernel(quant_rows_regs<2>, grid, block, 0, stream, x, xq, s_tok, m, k);
+    return launch_kernel(quant_rows_regs<2, kBf16>, grid, block, 0, stream, x, xq, s_tok, m, k);
   } else if (per_lane <= 4) {
-    return launch_kernel(quant_rows_regs<4>, grid, block, 0, stream, x, xq, s_tok, m, k);
+    return launch_kernel(quant_rows_regs<4, kBf16>, grid, block, 0, stream, x, xq, s_tok, m, k);
   } else if (per_lane <= 8) {
-    return launch_kernel(quant_rows_regs<8>, grid, block, 0, stream, x, xq, s_tok, m, k);
+    return launch_kernel(quant_rows_regs<8, kBf16>, grid, block, 0, stream, x, xq, s_tok, m, k);
   } else if (per_lane <= 16) {
-    return launch_kernel(quant_rows_regs<16>, grid, block, 0, stream, x, xq, s_tok, m, k);
+    return launch_kernel(quant_rows_regs<16, kBf16>, grid, block, 0, stream, x, xq, s_tok, m, k);
   } else if (per_lane <= 32) {
-    return launch_kernel(quant_rows_regs<32>, grid, block, 0, stream, x, xq, s_tok, m, k);
+    return launch_kernel(quant_rows_regs<32, kBf16>, grid, block, 0, stream, x, xq, s_tok, m, k);
   } else {
-    return launch_kernel(quant_rows_stream, grid, block, 0, stream, x, xq, s_tok, m, k);
+    return launch_kernel(quant_rows_stream<kBf16>, grid, block, 0, stream, x, xq, s_tok, m, k);
   }
+}
+
+}  // namespace
+
+hipError_t launch_quant_per_token_int8(const uint16_t* x, int8_t* xq, float* s_tok, int64_t M, int64_t K, bool bf16,
+                                       hipStream_t stream) {
+  return bf16 ? launch_quant<true>(x, xq, s_tok, M, K, stream) : launch_quant<false>(x, xq, s_tok, M, K, stream);
 }
 
 }  // namespace mq

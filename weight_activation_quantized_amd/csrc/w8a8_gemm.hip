@@ -83,7 +83,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const int8_t* base
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(base), 0, bytes, kBufferFlags);
 }
 
-template <bool kScaled>
+template <bool kScaled, bool kBf16>
 __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __restrict__ xq,
                                                              const float* __restrict__ s_tok,
                                                              const int8_t* __restrict__ wq,
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __res
       uint32_t hv[4];                                                                                \
       _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                \
         const float v = (static_cast<float>(acc[a][B][4 * q + i]) * st[B]) * sc[a][q][i];            \
-        hv[i] = __builtin_bit_cast(uint16_t, static_cast<f16>(v));                                   \
+        hv[i] = half_bits<kBf16>(v);                                                                 \
       }                                                                                              \
       *(lds_u32x2*)(dst) = u32x2{hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16)};                      \
     } else {                                                                                         \
@@ -407,18 +407,21 @@ __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __res
 
 hipError_t launch_w8a8_gemm(const int8_t* xq, const float* s_tok, const int8_t* wq,
                             const float* s_ch, uint16_t* y, int32_t* acc,
-                            int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  if (w8a8_use_gemv(M, N)) return launch_w8a8_gemv(xq, s_tok, wq, s_ch, y, acc, M, N, K, stream);
+                            int64_t M, int64_t N, int64_t K, bool bf16, hipStream_t stream) {
+  if (w8a8_use_gemv(M, N)) return launch_w8a8_gemv(xq, s_tok, wq, s_ch, y, acc, M, N, K, bf16, stream);
   const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
   const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
   const int tiles_n = static_cast<int>((N + kBN - 1) / kBN);
   const int64_t tiles = static_cast<int64_t>(tiles_m) * tiles_n;
   const int per_xcd = static_cast<int>((tiles + 7) / 8);
   const dim3 grid(static_cast<uint32_t>(8 * per_xcd)), block(kThreads);
-  if (y != nullptr)
-    return launch_kernel(w8a8_gemm_kernel<true>, grid, block, 0, stream, xq, s_tok, wq, s_ch, y,
+  if (y != nullptr && bf16)
+    return launch_kernel(w8a8_gemm_kernel<true, true>, grid, block, 0, stream, xq, s_tok, wq, s_ch, y,
                          static_cast<int32_t*>(nullptr), m, n, k, tiles_m, tiles_n, per_xcd);
-  return launch_kernel(w8a8_gemm_kernel<false>, grid, block, 0, stream, xq, s_tok, wq, s_ch,
+  if (y != nullptr)
+    return launch_kernel(w8a8_gemm_kernel<true, false>, grid, block, 0, stream, xq, s_tok, wq, s_ch, y,
+                         static_cast<int32_t*>(nullptr), m, n, k, tiles_m, tiles_n, per_xcd);
+  return launch_kernel(w8a8_gemm_kernel<false, false>, grid, block, 0, stream, xq, s_tok, wq, s_ch,
                        static_cast<uint16_t*>(nullptr), acc, m, n, k, tiles_m, tiles_n, per_xcd);
 }
 

@@ -94,7 +94,7 @@ __device__ __forceinline__ void mfmas(const Frags<kU, kA, kT>& f, i32x4 (&acc)[k
 }
 
 // A workgroup owns 16 kA output channels and all M <= 16 kT tokens.
-template <bool kScaled, int kA, int kT>
+template <bool kScaled, int kA, int kT, bool kBf16>
 __global__ __launch_bounds__(256) void w8a8_gemv_kernel(const int8_t* __restrict__ xq,
                                                         const float* __restrict__ s_tok,
                                                         const int8_t* __restrict__ wq,
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) void w8a8_gemv_kernel(const int8_t* __restrict
     const size_t o = static_cast<size_t>(m) * N + n;
     if constexpr (kScaled) {
       const float f = (static_cast<float>(v) * s_tok[m]) * s_ch[n];
-      y[o] = __builtin_bit_cast(uint16_t, static_cast<f16>(f));
+      y[o] = half_bits<kBf16>(f);
     } else {
       acc_out[o] = v;
     }
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) void w8a8_gemv_kernel(const int8_t* __restrict
 __device__ __forceinline__ float fused_code(float v, float s, float r) {
   const float p = v * r;
   const float t = rintf(p);
-  if (0.5f - fabsf(p - t) < 1.0f / 4096.0f) return rintf(v / s);
+  if (!(0.5f - fabsf(p - t) >= 1.0f / 4096.0f)) return rintf(v / s);  // non-finite p: divide
   return t;
 }
 
@@ -199,6 +199,7 @@ constexpr int kFusedLds = 80 * 1024;  // most bytes of codes a workgroup holds: 
 // pitch K + 16 bytes, so the 16 token rows of a fragment read fall on
 // different bank groups). Main loop: as w8a8_gemv_kernel, with the B
 // fragments read from LDS.
+template <bool kBf16>
 __global__ __launch_bounds__(256) void w8a8_gemv_fused_kernel(const uint16_t* __restrict__ x,
                                                               const int8_t* __restrict__ wq,
                                                               const float* __restrict__ s_ch,
@@ -222,9 +223,10 @@ __global__ __launch_bounds__(256) void w8a8_gemv_fused_kernel(const uint16_t* __
         const u32x4 v = row[c];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const f16x2 hv = as_f16x2(v[w]);
-          amax = fmaxf(amax, fabsf(static_cast<float>(hv[0])));
-          amax = fmaxf(amax, fabsf(static_cast<float>(hv[1])));
+          float lo, hi;
+          word_to_floats<kBf16>(v[w], lo, hi);
+          amax = fmaxf(amax, fabsf(lo));
+          amax = fmaxf(amax, fabsf(hi));
         }
       }
       amax = wave_max(amax);
@@ -239,12 +241,14 @@ __global__ __launch_bounds__(256) void w8a8_gemv_fused_kernel(const uint16_t* __
     const u32x4 v = *reinterpret_cast<const u32x4*>(x + static_cast<size_t>(m) * K + 8 * c);
     uint32_t packed[2] = {0u, 0u};
     if (sm > 0.f) {
-      const float r = __builtin_amdgcn_rcpf(sm);
+      // a binary32-subnormal scale: infinite reciprocal, so fused_code divides
+      const float r = sm < 1.17549435e-38f ? __builtin_inff() : __builtin_amdgcn_rcpf(sm);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const f16x2 hv = as_f16x2(v[w]);
-        const float q0 = fminf(fmaxf(fused_code(static_cast<float>(hv[0]), sm, r), -127.f), 127.f);
-        const float q1 = fminf(fmaxf(fused_code(static_cast<float>(hv[1]), sm, r), -127.f), 127.f);
+        float lo, hi;
+        word_to_floats<kBf16>(v[w], lo, hi);
+        const float q0 = fminf(fmaxf(fused_code(lo, sm, r), -127.f), 127.f);
+        const float q1 = fminf(fmaxf(fused_code(hi, sm, r), -127.f), 127.f);
         const uint32_t b = (static_cast<uint32_t>(static_cast<int32_t>(q0)) & 0xFFu) |
                            ((static_cast<uint32_t>(static_cast<int32_t>(q1)) & 0xFFu) << 8);
         packed[w >> 1] |= b << (16 * (w & 1));
@@ -306,30 +310,31 @@ __global__ __launch_bounds__(256) void w8a8_gemv_fused_kernel(const uint16_t* __
     if (m >= M || n >= N) continue;
     const int32_t v = part[0][nl][m] + part[1][nl][m] + part[2][nl][m] + part[3][nl][m];
     const float f = (static_cast<float>(v) * s_row[m]) * s_ch[n];
-    y[static_cast<size_t>(m) * N + n] = __builtin_bit_cast(uint16_t, static_cast<f16>(f));
+    y[static_cast<size_t>(m) * N + n] = half_bits<kBf16>(f);
   }
 }
 
-template <bool kScaled, int kA, int kT>
+template <bool kScaled, int kA, int kT, bool kBf16>
 hipError_t launch_one(const int8_t* xq, const float* s_tok, const int8_t* wq, const float* s_ch, uint16_t* y,
                       int32_t* acc, int M, int N, int K, hipStream_t stream) {
   const dim3 grid(static_cast<uint32_t>((N + 16 * kA - 1) / (16 * kA))), block(256);
-  return launch_kernel(w8a8_gemv_kernel<kScaled, kA, kT>, grid, block, 0, stream, xq, s_tok, wq, s_ch, y, acc, M, N, K);
+  return launch_kernel(w8a8_gemv_kernel<kScaled, kA, kT, kBf16>, grid, block, 0, stream, xq, s_tok, wq, s_ch, y, acc,
+                       M, N, K);
 }
 
-template <bool kScaled>
+template <bool kScaled, bool kBf16>
 hipError_t launch_tiles(const int8_t* xq, const float* s_tok, const int8_t* wq, const float* s_ch, uint16_t* y,
                         int32_t* acc, int M, int N, int K, hipStream_t stream) {
   // Every workgroup reads all of xq, so xq is read N / (16 kA) times over
   // (from L2): 32 channels per workgroup halves that, but only pays while
   // the grid still has about 192 or more workgroups.
   const bool wide = N >= 32 * 192;
-  if (M <= 16) return launch_one<kScaled, 1, 1>(xq, s_tok, wq, s_ch, y, acc, M, N, K, stream);
+  if (M <= 16) return launch_one<kScaled, 1, 1, kBf16>(xq, s_tok, wq, s_ch, y, acc, M, N, K, stream);
   if (M <= 32)
-    return wide ? launch_one<kScaled, 2, 2>(xq, s_tok, wq, s_ch, y, acc, M, N, K, stream)
-                : launch_one<kScaled, 1, 2>(xq, s_tok, wq, s_ch, y, acc, M, N, K, stream);
-  return wide ? launch_one<kScaled, 2, 4>(xq, s_tok, wq, s_ch, y, acc, M, N, K, stream)
-              : launch_one<kScaled, 1, 4>(xq, s_tok, wq, s_ch, y, acc, M, N, K, stream);
+    return wide ? launch_one<kScaled, 2, 2, kBf16>(xq, s_tok, wq, s_ch, y, acc, M, N, K, stream)
+                : launch_one<kScaled, 1, 2, kBf16>(xq, s_tok, wq, s_ch, y, acc, M, N, K, stream);
+  return wide ? launch_one<kScaled, 2, 4, kBf16>(xq, s_tok, wq, s_ch, y, acc, M, N, K, stream)
+              : launch_one<kScaled, 1, 4, kBf16>(xq, s_tok, wq, s_ch, y, acc, M, N, K, stream);
 }
 
 }  // namespace
@@ -347,21 +352,25 @@ bool w8a8_use_fused(int64_t M, int64_t K) {
 }
 
 hipError_t launch_w8a8_gemv_fused(const uint16_t* x, const int8_t* wq, const float* s_ch, uint16_t* y,
-                                  int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                                  int64_t M, int64_t N, int64_t K, bool bf16, hipStream_t stream) {
   if (!w8a8_use_fused(M, K)) return hipErrorInvalidValue;
   const dim3 grid(static_cast<uint32_t>((N + 15) / 16)), block(256);
   const size_t lds = static_cast<size_t>(M * (K + 16));
-  return launch_kernel(w8a8_gemv_fused_kernel, grid, block, lds, stream, x, wq, s_ch, y, static_cast<int>(M),
+  if (bf16)
+    return launch_kernel(w8a8_gemv_fused_kernel<true>, grid, block, lds, stream, x, wq, s_ch, y, static_cast<int>(M),
+                         static_cast<int>(N), static_cast<int>(K));
+  return launch_kernel(w8a8_gemv_fused_kernel<false>, grid, block, lds, stream, x, wq, s_ch, y, static_cast<int>(M),
                        static_cast<int>(N), static_cast<int>(K));
 }
 
 hipError_t launch_w8a8_gemv(const int8_t* xq, const float* s_tok, const int8_t* wq,
                             const float* s_ch, uint16_t* y, int32_t* acc,
-                            int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                            int64_t M, int64_t N, int64_t K, bool bf16, hipStream_t stream) {
   if (M > kW8A8GemvMaxM) return hipErrorInvalidValue;
   const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
-  if (y != nullptr) return launch_tiles<true>(xq, s_tok, wq, s_ch, y, nullptr, m, n, k, stream);
-  return launch_tiles<false>(xq, nullptr, wq, nullptr, nullptr, acc, m, n, k, stream);
+  if (y != nullptr && bf16) return launch_tiles<true, true>(xq, s_tok, wq, s_ch, y, nullptr, m, n, k, stream);
+  if (y != nullptr) return launch_tiles<true, false>(xq, s_tok, wq, s_ch, y, nullptr, m, n, k, stream);
+  return launch_tiles<false, false>(xq, nullptr, wq, nullptr, nullptr, acc, m, n, k, stream);
 }
 
 }  // namespace mq
