@@ -55,6 +55,16 @@ constexpr int kBStrip = 4;         // packed columns per strip (32 outputs)
 constexpr int kBOut = kBStrip * 8;  // outputs per strip
 constexpr int kBChunkRows = 128;    // rows per chunk (two 64-row pairs, four 32-row blocks)
 
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) f16x8 lds_f16x8;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+// x staged in LDS (one-tile forms): the workgroup's token rows over its K
+// range, row pitch = 2 * range + 16 bytes (the 16 spreads the rows over the
+// banks); a workgroup may hold at most this many bytes of it.
+constexpr int kXLdsPad = 16;
+constexpr int64_t kXLdsMaxBytes = 128 * 1024;
+
 // ---------------------------------------------------------------------------
 // Layout conversion: one thread per 16-byte lane slot of the blocked layout.
 // ---------------------------------------------------------------------------
@@ -104,7 +114,7 @@ struct BLane {
   int N, NP;
 };
 
-template <int kT, int kGS, int kSP>
+template <int kT, int kGS, int kSP, bool kXL>
 __device__ __forceinline__ void load_chunk(BChunk<kT, kBChunkRows / kGS, kSP>& ch, const BLane& L, int chunk) {
   constexpr int kGPC = kBChunkRows / kGS;
   const u32x4* wp = L.qb + static_cast<size_t>(2 * chunk) * L.pair_stride;
@@ -115,16 +125,20 @@ __device__ __forceinline__ void load_chunk(BChunk<kT, kBChunkRows / kGS, kSP>& c
     ch.w[sp][0] = __builtin_nontemporal_load(wp + 64 * sp);
     ch.w[sp][1] = __builtin_nontemporal_load(wp + L.pair_stride + 64 * sp);
   }
+  // With x in LDS the fragments are read at use (compute_chunk); otherwise
+  // each lane loads its token row's 8 values of each 32-row block.
+  if constexpr (!kXL) {
 #pragma unroll
-  for (int t = 0; t < kT; ++t)
+    for (int t = 0; t < kT; ++t)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      if (L.x[t]) {
-        ch.a[t][b] = *reinterpret_cast<const f16x8*>(L.x[t] + chunk * kBChunkRows + 32 * b);
-      } else {
-        ch.a[t][b] = f16x8{};
+      for (int b = 0; b < 4; ++b) {
+        if (L.x[t]) {
+          ch.a[t][b] = *reinterpret_cast<const f16x8*>(L.x[t] + chunk * kBChunkRows + 32 * b);
+        } else {
+          ch.a[t][b] = f16x8{};
+        }
       }
-    }
+  }
 #pragma unroll
   for (int g = 0; g < kGPC; ++g) {
     const size_t grp = static_cast<size_t>(chunk) * kGPC + g;
@@ -162,12 +176,26 @@ __device__ __forceinline__ void unpack_block(uint32_t w0, uint32_t w1, const Nib
     }
 }
 
-template <int kT, int kGS, int kSP>
+template <int kT, int kGS, int kSP, bool kXL>
 __device__ __forceinline__ void compute_chunk(const BChunk<kT, kBChunkRows / kGS, kSP>& ch, const NibConst& nc,
-                                              const f16x8 ones, int g_lane, f32x4 (&tot)[kT][kSP][2]) {
+                                              const f16x8 ones, int g_lane, f32x4 (&tot)[kT][kSP][2],
+                                              const lds_u8* xl) {
   constexpr int kGPC = kBChunkRows / kGS;  // groups per chunk
   constexpr int kBPG = kGS / 32;           // 32-row blocks per group
   const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
+  // xl: the lane's 16 bytes of block 0 of this chunk in the staged x (its
+  // token row, rows 8h..8h+7), or nullptr for lanes past the last token.
+  f16x8 xa[kT][4];
+#pragma unroll
+  for (int t = 0; t < kT; ++t)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      if constexpr (kXL) {
+        xa[t][b] = xl ? *reinterpret_cast<const lds_f16x8*>(xl + 64 * b) : f16x8{};
+      } else {
+        xa[t][b] = ch.a[t][b];
+      }
+    }
 #pragma unroll
   for (int g = 0; g < kGPC; ++g) {
     f32x4 acc[kT][kSP][2];
@@ -183,12 +211,12 @@ __device__ __forceinline__ void compute_chunk(const BChunk<kT, kBChunkRows / kGS
         for (int t = 0; t < kT; ++t)
 #pragma unroll
           for (int f = 0; f < 2; ++f)
-            acc[t][sp][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ch.a[t][b], bf[f], bb == 0 ? zero4 : acc[t][sp][f],
+            acc[t][sp][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[t][b], bf[f], bb == 0 ? zero4 : acc[t][sp][f],
                                                                   0, 0, 0);
       }
 #pragma unroll
       for (int t = 0; t < kT; ++t)
-        accx[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ch.a[t][b], ones, bb == 0 ? zero4 : accx[t], 0, 0, 0);
+        accx[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[t][b], ones, bb == 0 ? zero4 : accx[t], 0, 0, 0);
     }
     // tot += s * (acc - (1024 + z) * X); field 2g+1 carries 16 (q - z), so
     // its scale is s / 16 (exact).
@@ -215,7 +243,12 @@ __device__ __forceinline__ void compute_chunk(const BChunk<kT, kBChunkRows / kGS
 // Three wavefronts per SIMD for the one-strip, one-tile forms with groups of
 // 64 or 128: a 24576-wide layer has three such workgroups per CU, and all of
 // them must be resident at once for every CU to stream an equal share.
-template <int kT, int kGS, int kW, int kSP>
+// kXL (one-tile forms): the workgroup first copies its token rows of x over
+// its K range into LDS (dynamic shared memory, rows of 2 * range + 16
+// bytes) and the MFMA A fragments are read from there, so the weight stream
+// shares the vector-memory queue with nothing but the scales and zero
+// points (per-chunk x loads cost about 2 us of a 13 us call at N = 24576).
+template <int kT, int kGS, int kW, int kSP, bool kXL>
 __global__ __launch_bounds__(kW * 64)
 __attribute__((amdgpu_waves_per_eu(kT == 1 && kSP == 1 && kGS >= 64 ? 3 : 1))) void w4a16_gemv_blocked_kernel(
     const uint16_t* __restrict__ x, const u32x4* __restrict__ qb, const uint16_t* __restrict__ scales,
@@ -224,6 +257,7 @@ __attribute__((amdgpu_waves_per_eu(kT == 1 && kSP == 1 && kGS >= 64 ? 3 : 1))) v
   constexpr int kGPC = kBChunkRows / kGS;
   constexpr int kUOut = kSP * kBOut;  // outputs per unit
   __shared__ float s_red[kW * 16 * kT * kUOut];
+  extern __shared__ __attribute__((aligned(16))) uint8_t x_dyn[];  // kXL: M rows of staged x
 
   int unit, split;
   if (!decode_work(blockIdx.x, map.strips_per_xcd, units, splits, unit, split)) return;
@@ -278,23 +312,44 @@ __attribute__((amdgpu_waves_per_eu(kT == 1 && kSP == 1 && kGS >= 64 ? 3 : 1))) v
   // slower (see the layout notes).
   {
     BChunk<kT, kGPC, kSP> ca, cb;
-    load_chunk<kT, kGS, kSP>(ca, L, c0);
-    load_chunk<kT, kGS, kSP>(cb, L, min(c0 + 1, c0 + cpw - 1));
+    load_chunk<kT, kGS, kSP, kXL>(ca, L, c0);
+    load_chunk<kT, kGS, kSP, kXL>(cb, L, min(c0 + 1, c0 + cpw - 1));
+    // Staged x: the lane's row (token j, rows 8h.. of each block) at the
+    // split's first chunk; lanes past the last token read nothing.
+    const lds_u8* xrow = nullptr;
+    const int kbase = split * cps;  // first chunk of the split
+    if constexpr (kXL) {
+      lds_u8* const xs = (lds_u8*)(x_dyn);
+      const int kr = cps * kBChunkRows;  // K range of the split
+      const int pitch = 2 * kr + kXLdsPad;
+      const int mt = min(M, 16);
+      const int vpr = kr / 8;  // 16-byte vectors per row
+      for (int e = threadIdx.x; e < mt * vpr; e += kW * 64) {
+        const int m = e / vpr, v = e % vpr;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(x + static_cast<size_t>(m) * K + kbase * kBChunkRows + 8 * v);
+        *(lds_u32x4*)(xs + m * pitch + 16 * v) = val;
+      }
+      __syncthreads();
+      if (j < M) xrow = xs + j * pitch + 16 * h;
+    }
+    auto xl = [&](int chunk) -> const lds_u8* {
+      return (kXL && xrow) ? xrow + (chunk - kbase) * (2 * kBChunkRows) : nullptr;
+    };
     int i = 0;
     for (; i + 3 < cpw; i += 2) {
-      compute_chunk<kT, kGS, kSP>(ca, nc, ones, g, tot);
-      load_chunk<kT, kGS, kSP>(ca, L, c0 + i + 2);
+      compute_chunk<kT, kGS, kSP, kXL>(ca, nc, ones, g, tot, xl(c0 + i));
+      load_chunk<kT, kGS, kSP, kXL>(ca, L, c0 + i + 2);
       __builtin_amdgcn_sched_barrier(0);
-      compute_chunk<kT, kGS, kSP>(cb, nc, ones, g, tot);
-      load_chunk<kT, kGS, kSP>(cb, L, c0 + i + 3);
+      compute_chunk<kT, kGS, kSP, kXL>(cb, nc, ones, g, tot, xl(c0 + i + 1));
+      load_chunk<kT, kGS, kSP, kXL>(cb, L, c0 + i + 3);
       __builtin_amdgcn_sched_barrier(0);
     }
     // chunks i and (if in range) i + 1 are in flight; at most i + 2 is left
-    compute_chunk<kT, kGS, kSP>(ca, nc, ones, g, tot);
-    if (i + 2 < cpw) load_chunk<kT, kGS, kSP>(ca, L, c0 + i + 2);
+    compute_chunk<kT, kGS, kSP, kXL>(ca, nc, ones, g, tot, xl(c0 + i));
+    if (i + 2 < cpw) load_chunk<kT, kGS, kSP, kXL>(ca, L, c0 + i + 2);
     __builtin_amdgcn_sched_barrier(0);
-    if (i + 1 < cpw) compute_chunk<kT, kGS, kSP>(cb, nc, ones, g, tot);
-    if (i + 2 < cpw) compute_chunk<kT, kGS, kSP>(ca, nc, ones, g, tot);
+    if (i + 1 < cpw) compute_chunk<kT, kGS, kSP, kXL>(cb, nc, ones, g, tot, xl(c0 + i + 1));
+    if (i + 2 < cpw) compute_chunk<kT, kGS, kSP, kXL>(ca, nc, ones, g, tot, xl(c0 + i + 2));
   }
 
   // Add the wavefronts' sums in wavefront order. Lane (j, h) holds token
@@ -324,21 +379,42 @@ __attribute__((amdgpu_waves_per_eu(kT == 1 && kSP == 1 && kGS >= 64 ? 3 : 1))) v
   }
 }
 
+template <int kT, int kGS, int kSP, bool kXL>
+hipError_t launch_blocked_xl(const uint16_t* x, const u32x4* qb, const uint16_t* scales, const uint32_t* qz,
+                             uint16_t* y, float* part, int m, int n, int k, const GemvPlan& plan, int units,
+                             XcdMap map, dim3 grid, size_t lds, hipStream_t stream) {
+  switch (plan.waves) {
+    case 1:
+      return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 1, kSP, kXL>, grid, dim3(64), lds, stream, x, qb,
+                           scales, qz, y, part, m, n, k, units, plan.splits, map);
+    case 2:
+      return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 2, kSP, kXL>, grid, dim3(128), lds, stream, x, qb,
+                           scales, qz, y, part, m, n, k, units, plan.splits, map);
+    default:
+      return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 4, kSP, kXL>, grid, dim3(256), lds, stream, x, qb,
+                           scales, qz, y, part, m, n, k, units, plan.splits, map);
+  }
+}
+
+// Bytes of staged x a one-tile call needs (0: x is loaded per chunk): the
+// token rows over the split's K range, if they fit kXLdsMaxBytes.
+int64_t blocked_x_lds_bytes(int64_t M, int64_t K, int splits) {
+  const int64_t bytes = std::min<int64_t>(M, 16) * (2 * (K / splits) + kXLdsPad);
+  return (M <= 16 && bytes <= kXLdsMaxBytes) ? bytes : 0;
+}
+
 template <int kT, int kGS, int kSP>
 hipError_t launch_blocked_main(const uint16_t* x, const u32x4* qb, const uint16_t* scales, const uint32_t* qz,
                                uint16_t* y, float* part, int m, int n, int k, const GemvPlan& plan, int units,
                                XcdMap map, dim3 grid, hipStream_t stream) {
-  switch (plan.waves) {
-    case 1:
-      return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 1, kSP>, grid, dim3(64), 0, stream, x, qb, scales, qz,
-                           y, part, m, n, k, units, plan.splits, map);
-    case 2:
-      return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 2, kSP>, grid, dim3(128), 0, stream, x, qb, scales,
-                           qz, y, part, m, n, k, units, plan.splits, map);
-    default:
-      return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 4, kSP>, grid, dim3(256), 0, stream, x, qb, scales,
-                           qz, y, part, m, n, k, units, plan.splits, map);
+  if constexpr (kT == 1) {
+    const int64_t lds = blocked_x_lds_bytes(m, k, plan.splits);
+    if (lds > 0)
+      return launch_blocked_xl<kT, kGS, kSP, true>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid,
+                                                   static_cast<size_t>(lds), stream);
   }
+  return launch_blocked_xl<kT, kGS, kSP, false>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, 0,
+                                                stream);
 }
 
 template <int kGS>
