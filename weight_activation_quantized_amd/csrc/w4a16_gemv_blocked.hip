@@ -139,13 +139,15 @@ __device__ __forceinline__ void load_chunk(BChunk<kT, kBChunkRows / kGS, kSP>& c
         }
       }
   }
+  if constexpr (!kXL) {  // with kXL the scales and zero points are staged in LDS too
 #pragma unroll
-  for (int g = 0; g < kGPC; ++g) {
-    const size_t grp = static_cast<size_t>(chunk) * kGPC + g;
+    for (int g = 0; g < kGPC; ++g) {
+      const size_t grp = static_cast<size_t>(chunk) * kGPC + g;
 #pragma unroll
-    for (int sp = 0; sp < kSP; ++sp) {
-      ch.sv[sp][g] = *reinterpret_cast<const uint32_t*>(L.sc + grp * L.N + kBOut * sp);
-      ch.zw[sp][g] = L.qz[grp * L.NP + kBStrip * sp];
+      for (int sp = 0; sp < kSP; ++sp) {
+        ch.sv[sp][g] = *reinterpret_cast<const uint32_t*>(L.sc + grp * L.N + kBOut * sp);
+        ch.zw[sp][g] = L.qz[grp * L.NP + kBStrip * sp];
+      }
     }
   }
 }
@@ -179,12 +181,28 @@ __device__ __forceinline__ void unpack_block(uint32_t w0, uint32_t w1, const Nib
 template <int kT, int kGS, int kSP, bool kXL>
 __device__ __forceinline__ void compute_chunk(const BChunk<kT, kBChunkRows / kGS, kSP>& ch, const NibConst& nc,
                                               const f16x8 ones, int g_lane, f32x4 (&tot)[kT][kSP][2],
-                                              const lds_u8* xl) {
+                                              const lds_u8* xl, const lds_u8* scl, const lds_u8* zl) {
   constexpr int kGPC = kBChunkRows / kGS;  // groups per chunk
   constexpr int kBPG = kGS / 32;           // 32-row blocks per group
   const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
   // xl: the lane's 16 bytes of block 0 of this chunk in the staged x (its
   // token row, rows 8h..8h+7), or nullptr for lanes past the last token.
+  // scl / zl (kXL): the lane's scale pair and zero-point word of the chunk's
+  // first group for strip 0 in the staged tables (groups kSP * 64 / kSP * 16
+  // bytes apart, strips 64 / 16 bytes apart).
+  uint32_t sv[kSP][kGPC], zw[kSP][kGPC];
+#pragma unroll
+  for (int sp = 0; sp < kSP; ++sp)
+#pragma unroll
+    for (int g = 0; g < kGPC; ++g) {
+      if constexpr (kXL) {
+        sv[sp][g] = *(const lds_u32*)(scl + (g * kSP + sp) * 64);
+        zw[sp][g] = *(const lds_u32*)(zl + (g * kSP + sp) * 16);
+      } else {
+        sv[sp][g] = ch.sv[sp][g];
+        zw[sp][g] = ch.zw[sp][g];
+      }
+    }
   f16x8 xa[kT][4];
 #pragma unroll
   for (int t = 0; t < kT; ++t)
@@ -222,8 +240,8 @@ __device__ __forceinline__ void compute_chunk(const BChunk<kT, kBChunkRows / kGS
     // its scale is s / 16 (exact).
 #pragma unroll
     for (int sp = 0; sp < kSP; ++sp) {
-      const f16x2 s2 = as_f16x2(ch.sv[sp][g]);
-      const uint32_t zb = (ch.zw[sp][g] >> (8 * g_lane)) & 0xFFu;
+      const f16x2 s2 = as_f16x2(sv[sp][g]);
+      const uint32_t zb = (zw[sp][g] >> (8 * g_lane)) & 0xFFu;
       const float sc[2] = {static_cast<float>(s2[0]), static_cast<float>(s2[1]) * 0.0625f};
       const float bias[2] = {1024.0f + static_cast<float>(zb & 15u), 1024.0f + static_cast<float>(zb & 0xF0u)};
 #pragma unroll
@@ -244,10 +262,11 @@ __device__ __forceinline__ void compute_chunk(const BChunk<kT, kBChunkRows / kGS
 // 64 or 128: a 24576-wide layer has three such workgroups per CU, and all of
 // them must be resident at once for every CU to stream an equal share.
 // kXL (one-tile forms): the workgroup first copies its token rows of x over
-// its K range into LDS (dynamic shared memory, rows of 2 * range + 16
-// bytes) and the MFMA A fragments are read from there, so the weight stream
-// shares the vector-memory queue with nothing but the scales and zero
-// points (per-chunk x loads cost about 2 us of a 13 us call at N = 24576).
+// its K range (rows of 2 * range + 16 bytes), then its strips' scales and
+// zero-point words, into LDS (dynamic shared memory), and reads the MFMA A
+// fragments and the group parameters from there, so the weight stream has
+// the vector-memory queue to itself (per-chunk x loads cost about 2 us and
+// the scale and zero-point loads about 0.7 us of a 13 us call at N = 24576).
 template <int kT, int kGS, int kW, int kSP, bool kXL>
 __global__ __launch_bounds__(kW * 64)
 __attribute__((amdgpu_waves_per_eu(kT == 1 && kSP == 1 && kGS >= 64 ? 3 : 1))) void w4a16_gemv_blocked_kernel(
@@ -317,6 +336,8 @@ __attribute__((amdgpu_waves_per_eu(kT == 1 && kSP == 1 && kGS >= 64 ? 3 : 1))) v
     // Staged x: the lane's row (token j, rows 8h.. of each block) at the
     // split's first chunk; lanes past the last token read nothing.
     const lds_u8* xrow = nullptr;
+    const lds_u8* sc_lane = nullptr;
+    const lds_u8* z_lane = nullptr;
     const int kbase = split * cps;  // first chunk of the split
     if constexpr (kXL) {
       lds_u8* const xs = (lds_u8*)(x_dyn);
@@ -329,27 +350,48 @@ __attribute__((amdgpu_waves_per_eu(kT == 1 && kSP == 1 && kGS >= 64 ? 3 : 1))) v
         const u32x4 val = *reinterpret_cast<const u32x4*>(x + static_cast<size_t>(m) * K + kbase * kBChunkRows + 8 * v);
         *(lds_u32x4*)(xs + m * pitch + 16 * v) = val;
       }
+      // The unit's scales ([group][strip][32] fp16, 64 bytes per strip) and
+      // zero-point words ([group][strip][4], 16 bytes) over the K range.
+      const int ngr = kr / kGS;
+      lds_u8* const sct = xs + mt * pitch;
+      lds_u8* const zt = sct + ngr * kSP * 64;
+      const int grp0 = kbase * kGPC;
+      for (int e = threadIdx.x; e < ngr * kSP * 4; e += kW * 64) {
+        const int gl = e / (kSP * 4), sp = (e / 4) % kSP, v = e % 4;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(scales + static_cast<size_t>(grp0 + gl) * N +
+                                                          (strip + sp) * kBOut + 8 * v);
+        *(lds_u32x4*)(sct + (gl * kSP + sp) * 64 + 16 * v) = val;
+        const uint32_t zv = qz[static_cast<size_t>(grp0 + gl) * NP + (strip + sp) * kBStrip + v];
+        *(lds_u32*)(zt + (gl * kSP + sp) * 16 + 4 * v) = zv;
+      }
       __syncthreads();
       if (j < M) xrow = xs + j * pitch + 16 * h;
+      sc_lane = sct + 16 * c + 4 * g;
+      z_lane = zt + 4 * c;
     }
     auto xl = [&](int chunk) -> const lds_u8* {
       return (kXL && xrow) ? xrow + (chunk - kbase) * (2 * kBChunkRows) : nullptr;
     };
+    auto sl = [&](int chunk) -> const lds_u8* { return sc_lane + (chunk - kbase) * kGPC * kSP * 64; };
+    auto zl = [&](int chunk) -> const lds_u8* { return z_lane + (chunk - kbase) * kGPC * kSP * 16; };
     int i = 0;
     for (; i + 3 < cpw; i += 2) {
-      compute_chunk<kT, kGS, kSP, kXL>(ca, nc, ones, g, tot, xl(c0 + i));
+      compute_chunk<kT, kGS, kSP, kXL>(ca, nc, ones, g, tot, xl(c0 + i), sl(c0 + i), zl(c0 + i));
       load_chunk<kT, kGS, kSP, kXL>(ca, L, c0 + i + 2);
       __builtin_amdgcn_sched_barrier(0);
-      compute_chunk<kT, kGS, kSP, kXL>(cb, nc, ones, g, tot, xl(c0 + i + 1));
+      compute_chunk<kT, kGS, kSP, kXL>(cb, nc, ones, g, tot, xl(c0 + i + 1), sl(c0 + i + 1),
+                                                         zl(c0 + i + 1));
       load_chunk<kT, kGS, kSP, kXL>(cb, L, c0 + i + 3);
       __builtin_amdgcn_sched_barrier(0);
     }
     // chunks i and (if in range) i + 1 are in flight; at most i + 2 is left
-    compute_chunk<kT, kGS, kSP, kXL>(ca, nc, ones, g, tot, xl(c0 + i));
+    compute_chunk<kT, kGS, kSP, kXL>(ca, nc, ones, g, tot, xl(c0 + i), sl(c0 + i), zl(c0 + i));
     if (i + 2 < cpw) load_chunk<kT, kGS, kSP, kXL>(ca, L, c0 + i + 2);
     __builtin_amdgcn_sched_barrier(0);
-    if (i + 1 < cpw) compute_chunk<kT, kGS, kSP, kXL>(cb, nc, ones, g, tot, xl(c0 + i + 1));
-    if (i + 2 < cpw) compute_chunk<kT, kGS, kSP, kXL>(ca, nc, ones, g, tot, xl(c0 + i + 2));
+    if (i + 1 < cpw) compute_chunk<kT, kGS, kSP, kXL>(cb, nc, ones, g, tot, xl(c0 + i + 1), sl(c0 + i + 1),
+                                                         zl(c0 + i + 1));
+    if (i + 2 < cpw) compute_chunk<kT, kGS, kSP, kXL>(ca, nc, ones, g, tot, xl(c0 + i + 2), sl(c0 + i + 2),
+                                                         zl(c0 + i + 2));
   }
 
   // Add the wavefronts' sums in wavefront order. Lane (j, h) holds token
@@ -396,11 +438,17 @@ hipError_t launch_blocked_xl(const uint16_t* x, const u32x4* qb, const uint16_t*
   }
 }
 
-// Bytes of staged x a one-tile call needs (0: x is loaded per chunk): the
-// token rows over the split's K range, if they fit kXLdsMaxBytes.
-int64_t blocked_x_lds_bytes(int64_t M, int64_t K, int splits) {
-  const int64_t bytes = std::min<int64_t>(M, 16) * (2 * (K / splits) + kXLdsPad);
-  return (M <= 16 && bytes <= kXLdsMaxBytes) ? bytes : 0;
+// Bytes of LDS a one-tile call stages (0: x, scales and zero points are
+// loaded per chunk): the token rows of x over the split's K range, then the
+// unit's scales and zero-point words, if x fits kXLdsMaxBytes and all of it
+// fits beside the static reduction buffer in a CU's 160 KB.
+int64_t blocked_x_lds_bytes(int64_t M, int64_t K, int64_t group, int splits, int waves, int strips_per_unit) {
+  const int64_t kr = K / splits;
+  const int64_t xb = std::min<int64_t>(M, 16) * (2 * kr + kXLdsPad);
+  const int64_t szb = (kr / group) * strips_per_unit * (64 + 16);
+  const int64_t red = int64_t{waves} * 16 * strips_per_unit * kBOut * 4;
+  if (M > 16 || xb > kXLdsMaxBytes || xb + szb + red > 160 * 1024) return 0;
+  return xb + szb;
 }
 
 template <int kT, int kGS, int kSP>
@@ -408,7 +456,7 @@ hipError_t launch_blocked_main(const uint16_t* x, const u32x4* qb, const uint16_
                                uint16_t* y, float* part, int m, int n, int k, const GemvPlan& plan, int units,
                                XcdMap map, dim3 grid, hipStream_t stream) {
   if constexpr (kT == 1) {
-    const int64_t lds = blocked_x_lds_bytes(m, k, plan.splits);
+    const int64_t lds = blocked_x_lds_bytes(m, k, kGS, plan.splits, plan.waves, kSP);
     if (lds > 0)
       return launch_blocked_xl<kT, kGS, kSP, true>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid,
                                                    static_cast<size_t>(lds), stream);
