@@ -61,9 +61,14 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 // x staged in LDS (one-tile forms): the workgroup's token rows over its K
 // range, row pitch = 2 * range + 16 bytes (the 16 spreads the rows over the
-// banks); a workgroup may hold at most this many bytes of it.
+// banks). Only for up to 4 tokens: the copy happens before the stream
+// starts, and with 16 tokens (128 KB per workgroup at K = 4096) it held the
+// stream back more than the per-chunk x loads did (13.9 against 12.3 us per
+// call averaged over 1, 4 and 16 tokens); with 1 and 4 tokens it saves 1.3
+// and 0.7 us.
 constexpr int kXLdsPad = 16;
-constexpr int64_t kXLdsMaxBytes = 128 * 1024;
+constexpr int64_t kXLdsMaxTokens = 4;
+constexpr int64_t kLdsPerWorkgroup = 160 * 1024;
 
 // ---------------------------------------------------------------------------
 // Layout conversion: one thread per 16-byte lane slot of the blocked layout.
@@ -440,14 +445,14 @@ hipError_t launch_blocked_xl(const uint16_t* x, const u32x4* qb, const uint16_t*
 
 // Bytes of LDS a one-tile call stages (0: x, scales and zero points are
 // loaded per chunk): the token rows of x over the split's K range, then the
-// unit's scales and zero-point words, if x fits kXLdsMaxBytes and all of it
-// fits beside the static reduction buffer in a CU's 160 KB.
+// unit's scales and zero-point words, if all of it fits beside the static
+// reduction buffer in a workgroup's 160 KB.
 int64_t blocked_x_lds_bytes(int64_t M, int64_t K, int64_t group, int splits, int waves, int strips_per_unit) {
   const int64_t kr = K / splits;
   const int64_t xb = std::min<int64_t>(M, 16) * (2 * kr + kXLdsPad);
   const int64_t szb = (kr / group) * strips_per_unit * (64 + 16);
   const int64_t red = int64_t{waves} * 16 * strips_per_unit * kBOut * 4;
-  if (M > 16 || xb > kXLdsMaxBytes || xb + szb + red > 160 * 1024) return 0;
+  if (M > kXLdsMaxTokens || xb + szb + red > kLdsPerWorkgroup) return 0;
   return xb + szb;
 }
 
