@@ -30,13 +30,14 @@ Also reported (same line):
                rocprofv3 counter summary when it matches the current kernel
                source, else null.
   prefill      W8A8 prefill (per-token quant + scaled int8 GEMM, M=2048,
-               K=N=4096) and W4A16 prefill GEMMs (M=4096, K=4096/12288,
-               N=4096): kernel time and TOPS against the dense MFMA peaks.
+               K=N=4096; also with bf16 activations and output) and W4A16
+               prefill GEMMs (M=4096, K=4096/12288, N=4096): kernel time and
+               TOPS against the dense MFMA peaks.
   layers       the linear layers of an 8B-shaped decoder layer (qkv 4096->6144,
                o_proj 4096->4096, gate_up 4096->24576, down 12288->4096) at
                M = 1, 8, 64 and 2048 under W4A16 (decode-layout GEMV up to 64
                tokens, GEMM above) and W8A8_INT8 (mq_w8a8_linear: quantizer fused
-               into the decode kernel up to 16 tokens): microseconds per call with
+               into the decode kernel for one token): microseconds per call with
                weights rotating over copies of >= 640 MB per layer; `set` = the
                four layers of a scheme in one graph, microseconds per layer set.
   groups       W4A16 with groups of 64 and 32 rows (LMDeploy quantizes the
@@ -202,6 +203,7 @@ def bench_gemv(torch, mq, synth, args, log):
 def bench_prefill(torch, mq, synth, oracle_free_quant, args, log):
     """W8A8 prefill (quant + GEMM) and W4A16 prefill GEMMs; kernel times from event-timed graph replays
     (the median of three)."""
+    import numpy as np
     dev = torch.device("cuda", 0)
     out = {}
     R = args.prefill_reps
@@ -232,7 +234,18 @@ def bench_prefill(torch, mq, synth, oracle_free_quant, args, log):
         "gemm_frac_int8_peak": ops / t_g / 1e12 / INT8_PEAK_TOPS,
         "layer_TOPS": ops / (t_q + t_g) / 1e12,
     }
-    del x, wq, s_ch, xq, s_tok, y
+    # the same layer with bf16 activations and output (same draws rounded to bf16)
+    db = synth.w8a8_inputs_bf16(M, K, N, outlier_frac=0.01, tag=2)
+    xb = torch.from_numpy(db["x_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    yb = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    log("prefill: w8a8 bf16 quant + gemm")
+    t_qb = time_fn(lambda: mq.quant_per_token_int8(xb, out=xq, s_out=s_tok))
+    t_gb = time_fn(lambda: mq.w8a8_scaled_mm(xq, s_tok, wq, s_ch, out=yb))
+    out["w8a8_c2_bf16"] = {
+        "shape": [M, N, K], "quant_us": t_qb * 1e6, "gemm_us": t_gb * 1e6, "gemm_TOPS": ops / t_gb / 1e12,
+        "gemm_frac_int8_peak": ops / t_gb / 1e12 / INT8_PEAK_TOPS,
+    }
+    del x, wq, s_ch, xq, s_tok, y, xb, yb
     for name, K in (("w4a16_c3a", 4096), ("w4a16_c3b", 12288)):
         M, N = 4096, 4096
         dd = synth.w4a16_inputs(M, K, N, GROUP, tag=3 if K == 4096 else 4)
