@@ -202,3 +202,52 @@ def test_graph_replays_kv_and_checkpoint():
         assert np.array_equal(static[i].cpu().numpy(), oracle.reorder_int4_ref(wk, order))
         assert np.array_equal(static[i + 1].cpu().numpy(), oracle.transpose_int4_ref(wn, order))
         assert np.array_equal(static[i + 2].cpu().numpy().view(np.uint16), sn.T.view(np.uint16))
+
+
+def test_graph_replays_w8a8_bf16():
+    # bf16 activations: quantizer, scaled GEMM (decode and tiled kernels) and
+    # the one-token fused layer in one graph
+    import torch
+    K, N = 1024, 640
+    rng = np.random.default_rng(19)
+    d = synth.w8a8_inputs_bf16(4, K, N, tag=611)
+    wq_np, s_ch_np = oracle.quant_per_token_int8_ref(d["wf"])
+    wq, s_ch = torch.from_numpy(wq_np).cuda(), torch.from_numpy(s_ch_np).cuda()
+    xs = [torch.empty((M, K), dtype=torch.bfloat16, device="cuda") for M in (8, 300, 1)]
+
+    def outs():
+        o = []
+        for x in xs[:2]:
+            M = x.shape[0]
+            o += [torch.empty((M, K), dtype=torch.int8, device="cuda"),
+                  torch.empty((M,), dtype=torch.float32, device="cuda"),
+                  torch.empty((M, N), dtype=torch.bfloat16, device="cuda")]
+        o.append(torch.empty((1, N), dtype=torch.bfloat16, device="cuda"))
+        return o
+
+    def run(o):
+        for i, x in enumerate(xs[:2]):
+            mq.quant_per_token_int8(x, out=o[3 * i], s_out=o[3 * i + 1])
+            mq.w8a8_scaled_mm(o[3 * i], o[3 * i + 1], wq, s_ch, out=o[3 * i + 2])
+        mq.w8a8_linear(xs[2], wq, s_ch, out=o[6])
+
+    announce("graph w8a8 bf16")
+    static = outs()
+    g = _capture(torch, lambda: run(static))
+    for r in range(REPLAYS):
+        xr = [synth.bf16_bits((rng.standard_normal(tuple(x.shape)) * (1 + r)).astype(np.float32)) for x in xs]
+        for x, b in zip(xs, xr):
+            x.copy_(torch.from_numpy(b.view(np.int16)).view(torch.bfloat16))
+        eager = outs()
+        run(eager)
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (got, want) in enumerate(zip(static, eager)):
+            assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), f"replay {r}: output {k} differs"
+        for i in range(2):
+            q_ref, s_ref = oracle.quant_per_token_int8_ref(synth.bf16_values(xr[i]))
+            assert np.array_equal(static[3 * i].cpu().numpy(), q_ref)
+            assert np.array_equal(static[3 * i + 1].cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+            y64 = oracle.w8a8_ref(q_ref, s_ref, wq_np, s_ch_np)
+            yb = synth.bf16_values(static[3 * i + 2].view(torch.int16).cpu().numpy().view(np.uint16))
+            assert np.all(np.abs(yb - y64) <= (2.0 ** -8 + 2.0 ** -20) * np.abs(y64))
