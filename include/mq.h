@@ -318,6 +318,17 @@ mq_status mq_kv_quant(const uint16_t* x, uint8_t* codes, float* params, int64_t 
                       int32_t bits, void* stream);
 
 /*
+ * bf16 form of mq_kv_quant for a bf16 KV cache: x is bf16 (raw bits), which
+ * widens exactly to binary32, so the same definition gives the codes and
+ * (scale, min) bit for bit; everything else is as in mq_kv_quant. A row
+ * whose scale is subnormal in binary32 is quantized by the IEEE division;
+ * rows whose max - min overflows binary32 are outside the contract, as are
+ * non-finite inputs.
+ */
+mq_status mq_kv_quant_bf16(const uint16_t* x, uint8_t* codes, float* params, int64_t rows, int64_t head_dim,
+                           int32_t bits, void* stream);
+
+/*
  * Checkpoint-layout adapter: one-time conversions of 4-bit checkpoint
  * tensors into the layouts above.
  * Source: the LMDeploy overview (sections 4.1 and 5.5) loads 4-bit

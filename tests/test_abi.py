@@ -40,7 +40,8 @@ def test_header_declares_the_boundary():
               "mq_w4a16_gemv_blocked", "mq_w4a16_gemv_blocked_workspace_bytes", "mq_w8a8_linear",
               "mq_w8a8_linear_workspace_bytes", "mq_w4a16_gemm_workspace_bytes", "mq_kv_quant", "mq_abi_version",
               "mq_status_string", "mq_last_error", "mq_int4_reorder", "mq_int4_transpose", "mq_u16_transpose",
-              "mq_quant_per_token_int8_bf16", "mq_w8a8_scaled_mm_bf16", "mq_w8a8_linear_bf16"]:
+              "mq_quant_per_token_int8_bf16", "mq_w8a8_scaled_mm_bf16", "mq_w8a8_linear_bf16",
+              "mq_kv_quant_bf16"]:
         assert n in names
 
 
@@ -318,3 +319,11 @@ def test_bf16_entries_validate_like_fp16(lib):
                  (A, B, C, E, 32, 64, 64, None, 0, None), (A, B, C, E, 0, 64, 64, None, 0, None)):
         assert g(*args) == g16(*args)
     assert g(A, B, C, E, 32, 64, 64, None, 0, None) == WS
+
+
+def test_kv_quant_bf16_validates_like_fp16(lib):
+    k, k16 = lib.mq_kv_quant_bf16, lib.mq_kv_quant
+    for args in ((A, B, C, 16, 128, 2, None), (A, B, C, 16, 96, 8, None), (None, B, C, 16, 128, 8, None),
+                 (A + 8, B, C, 16, 128, 8, None), (A, A + 64, C, 16, 128, 8, None), (A, B, C, 0, 128, 8, None),
+                 (A, B, C, 1 << 26, 512, 8, None)):
+        assert k(*args) == k16(*args)

@@ -82,3 +82,41 @@ def test_kv_quant_dequant_error():
         xhat = oracle.kv_dequant_ref(host(codes), host(params), bits)
         step = host(params)[:, 0:1].astype(np.float64)
         assert np.all(np.abs(xhat - x.astype(np.float64)) <= 0.5 * step * (1 + 1e-5) + 1e-6)
+
+
+def _check_bf16(bits16, bits, what):
+    import torch
+    import synth
+    x = torch.from_numpy(np.ascontiguousarray(bits16).view(np.int16)).cuda().view(torch.bfloat16)
+    announce(f"kv_quant bf16 {what} bits={bits} shape={bits16.shape}")
+    codes, params = mq.kv_quant(x, bits)
+    codes, params = host(codes), host(params)
+    xf = synth.bf16_values(bits16).reshape(-1, bits16.shape[-1])
+    rc, rp = oracle.kv_quant_ref(xf, bits)
+    assert np.array_equal(params.reshape(-1, 2).view(np.uint32), rp.view(np.uint32)), f"{what}: params differ"
+    assert np.array_equal(codes.reshape(rc.shape), rc), f"{what}: codes differ"
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("shape", [(4096, 32, 128), (2100, 32, 128), (37, 8, 64), (9, 512)],
+                         ids=["prefill_4k", "two_rows_ragged", "h64", "h512"])
+def test_kv_quant_bf16_bitexact(shape, bits):
+    import synth
+    rng = np.random.default_rng(sum(shape) + 100 * bits)
+    x = (rng.standard_normal(shape) * rng.uniform(0.1, 4, shape[:-1] + (1,))).astype(np.float32)
+    _check_bf16(synth.bf16_bits(x), bits, "random")
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_kv_quant_bf16_edge_rows(bits):
+    import synth
+    qmax = 2 ** bits - 1
+    D = 256
+    jj = np.arange(min(qmax, 127))
+    rows = [np.resize(np.concatenate([[0.0, qmax / 8.0], (jj + 0.5) / 8.0]), D),   # ties (where bf16 holds them)
+            np.full(D, -3.25),                                                     # constant
+            np.resize([-0.0, 0.0], D),                                             # signed zeros
+            np.resize([0.0, 2.0 ** -130, 2.0 ** -129, 3 * 2.0 ** -131], D),          # subnormal scale
+            np.resize([1.0e38, -1.0e38, 0.0], D),                                  # wide but finite span
+            np.resize([2.0 ** -126, -(2.0 ** -126), 2.0 ** -127], D)]
+    _check_bf16(synth.bf16_bits(np.array(rows, np.float32)), bits, "edge rows")

@@ -82,6 +82,7 @@ _PROTOTYPES = {
     "mq_w4a16_block_weights": (ctypes.c_int, [_P, _P, _I64, _I64, _P]),
     "mq_w8a8_linear_workspace_bytes": (ctypes.c_size_t, [_I64, _I64]),
     "mq_kv_quant": (ctypes.c_int, [_P, _P, _P, _I64, _I64, ctypes.c_int32, _P]),
+    "mq_kv_quant_bf16": (ctypes.c_int, [_P, _P, _P, _I64, _I64, ctypes.c_int32, _P]),
     "mq_w8a8_linear": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
     "mq_quant_per_token_int8_bf16": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "mq_w8a8_scaled_mm_bf16": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
@@ -389,11 +390,12 @@ def w8a8_linear(x, wq, s_ch, out=None, workspace=None, stream=None):
 
 def kv_quant(x, bits=8, codes=None, params=None, stream=None):
     """Online KV-cache quantization per (token, head) row: x [..., head_dim] fp16
-    -> (codes uint8 [..., head_dim] (8 bits) or [..., head_dim/2] (4 bits, two
-    per byte, element 2i low), params fp32 [..., 2] = (scale, min))."""
+    or bf16 -> (codes uint8 [..., head_dim] (8 bits) or [..., head_dim/2] (4
+    bits, two per byte, element 2i low), params fp32 [..., 2] = (scale, min))."""
     torch = _torch()
-    if not isinstance(x, torch.Tensor) or x.dtype != torch.float16 or x.device.type != "cuda":
-        raise TypeError("x must be a float16 GPU tensor")
+    if (not isinstance(x, torch.Tensor) or x.dtype not in (torch.float16, torch.bfloat16)
+            or x.device.type != "cuda"):
+        raise TypeError("x must be a float16 or bfloat16 GPU tensor")
     if not x.is_contiguous() or x.dim() < 1:
         raise ValueError("x must be contiguous with at least one dimension")
     D = x.shape[-1]
@@ -403,8 +405,8 @@ def kv_quant(x, bits=8, codes=None, params=None, stream=None):
     codes = _out(codes, cshape, torch.uint8, x, "codes")
     params = _out(params, lead + (2,), torch.float32, x, "params")
     with torch.cuda.device(x.device):
-        _check(library().mq_kv_quant(x.data_ptr(), codes.data_ptr(), params.data_ptr(), rows, D, bits,
-                                     _stream_of(x, stream)))
+        fn = library().mq_kv_quant_bf16 if x.dtype == torch.bfloat16 else library().mq_kv_quant
+        _check(fn(x.data_ptr(), codes.data_ptr(), params.data_ptr(), rows, D, bits, _stream_of(x, stream)))
     return codes, params
 
 

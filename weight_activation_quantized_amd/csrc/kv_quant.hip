@@ -16,7 +16,8 @@
 // group), min and max come from a butterfly within the group, and each lane
 // writes its 8 codes (8 bytes, or 4 packed bytes for INT4). The codes come
 // from a reciprocal product, with the IEEE division only near half-integers.
-// x is read once; nothing else is.
+// x is fp16 or bf16 (both widen exactly to binary32). x is read once;
+// nothing else is.
 #include "device_common.h"
 #include "launch.h"
 
@@ -46,18 +47,24 @@ __device__ __forceinline__ float group_max(float v) {
 // the margin (ties among them) take the division.
 constexpr float kKvTieMargin = 1.0f / 4096.0f;
 
+// Written so that a non-finite p also divides: a binary32-subnormal scale
+// (possible for bf16 rows) gets an infinite reciprocal (kv_rcp).
 __device__ __forceinline__ float kv_code(float d, float scale, float r) {
   const float p = d * r;
   const float t = rintf(p);
-  if (0.5f - fabsf(p - t) < kKvTieMargin) return rintf(d / scale);
+  if (!(0.5f - fabsf(p - t) >= kKvTieMargin)) return rintf(d / scale);
   return t;
+}
+
+__device__ __forceinline__ float kv_rcp(float scale) {
+  return scale < 1.17549435e-38f ? __builtin_inff() : __builtin_amdgcn_rcpf(scale);
 }
 
 // kL lanes per row (head_dim = 8 kL), kBits = 8 or 4, kR rows per lane group.
 // 256 threads: kR * 256 / kL rows per workgroup; the kR loads of a lane are
 // issued before any is used, and for each r the workgroup's 256 lanes read
 // one contiguous 4 KB span.
-template <int kL, int kBits, int kR>
+template <int kL, int kBits, int kR, bool kBf16>
 __global__ __launch_bounds__(256) void kv_quant_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ codes,
                                                        float* __restrict__ params, int64_t rows) {
   constexpr int kD = 8 * kL;
@@ -77,11 +84,7 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(const uint16_t* __restric
     const int64_t row = row0 + r * kRowsPerPass;
     float f[8];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const f16x2 h = as_f16x2(v[r][w]);
-      f[2 * w] = static_cast<float>(h[0]);
-      f[2 * w + 1] = static_cast<float>(h[1]);
-    }
+    for (int w = 0; w < 4; ++w) word_to_floats<kBf16>(v[r][w], f[2 * w], f[2 * w + 1]);
     float mn = f[0], mx = f[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) {
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(const uint16_t* __restric
     const float scale = (mx - mn) / kQmax;  // IEEE binary32 subtraction and division
     uint32_t q[8];
     if (scale > 0.f) {
-      const float rs = __builtin_amdgcn_rcpf(scale);
+      const float rs = kv_rcp(scale);
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         q[e] = static_cast<uint32_t>(fminf(fmaxf(kv_code(f[e] - mn, scale, rs), 0.f), kQmax));
@@ -121,20 +124,20 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(const uint16_t* __restric
   }
 }
 
-template <int kBits, int kR>
+template <int kBits, int kR, bool kBf16>
 hipError_t launch_rows(const uint16_t* x, uint8_t* codes, float* params, int64_t rows, int64_t head_dim,
                        hipStream_t stream) {
   const int64_t lanes = head_dim / 8;
   const int64_t rows_per_block = kR * (256 / lanes);
   const dim3 grid(static_cast<uint32_t>((rows + rows_per_block - 1) / rows_per_block)), block(256);
   switch (lanes) {
-    case 1: return launch_kernel(kv_quant_kernel<1, kBits, kR>, grid, block, 0, stream, x, codes, params, rows);
-    case 2: return launch_kernel(kv_quant_kernel<2, kBits, kR>, grid, block, 0, stream, x, codes, params, rows);
-    case 4: return launch_kernel(kv_quant_kernel<4, kBits, kR>, grid, block, 0, stream, x, codes, params, rows);
-    case 8: return launch_kernel(kv_quant_kernel<8, kBits, kR>, grid, block, 0, stream, x, codes, params, rows);
-    case 16: return launch_kernel(kv_quant_kernel<16, kBits, kR>, grid, block, 0, stream, x, codes, params, rows);
-    case 32: return launch_kernel(kv_quant_kernel<32, kBits, kR>, grid, block, 0, stream, x, codes, params, rows);
-    case 64: return launch_kernel(kv_quant_kernel<64, kBits, kR>, grid, block, 0, stream, x, codes, params, rows);
+    case 1: return launch_kernel(kv_quant_kernel<1, kBits, kR, kBf16>, grid, block, 0, stream, x, codes, params, rows);
+    case 2: return launch_kernel(kv_quant_kernel<2, kBits, kR, kBf16>, grid, block, 0, stream, x, codes, params, rows);
+    case 4: return launch_kernel(kv_quant_kernel<4, kBits, kR, kBf16>, grid, block, 0, stream, x, codes, params, rows);
+    case 8: return launch_kernel(kv_quant_kernel<8, kBits, kR, kBf16>, grid, block, 0, stream, x, codes, params, rows);
+    case 16: return launch_kernel(kv_quant_kernel<16, kBits, kR, kBf16>, grid, block, 0, stream, x, codes, params, rows);
+    case 32: return launch_kernel(kv_quant_kernel<32, kBits, kR, kBf16>, grid, block, 0, stream, x, codes, params, rows);
+    case 64: return launch_kernel(kv_quant_kernel<64, kBits, kR, kBf16>, grid, block, 0, stream, x, codes, params, rows);
     default: return hipErrorInvalidValue;
   }
 }
@@ -143,21 +146,26 @@ hipError_t launch_rows(const uint16_t* x, uint8_t* codes, float* params, int64_t
 // (eight per CU); smaller calls keep one row per group so every CU has work.
 // Measured at 131072 rows of 128 (INT8 / INT4): one row 12.7 / 12.1 us, two
 // 12.0 / 11.9, four 12.8 / 14.1, eight 15.2 / 15.3.
-template <int kBits>
+template <int kBits, bool kBf16>
 hipError_t launch_bits(const uint16_t* x, uint8_t* codes, float* params, int64_t rows, int64_t head_dim,
                        hipStream_t stream) {
   const int64_t rows_per_pass = 256 / (head_dim / 8);
-  if (rows >= 2048 * 2 * rows_per_pass) return launch_rows<kBits, 2>(x, codes, params, rows, head_dim, stream);
-  return launch_rows<kBits, 1>(x, codes, params, rows, head_dim, stream);
+  if (rows >= 2048 * 2 * rows_per_pass)
+    return launch_rows<kBits, 2, kBf16>(x, codes, params, rows, head_dim, stream);
+  return launch_rows<kBits, 1, kBf16>(x, codes, params, rows, head_dim, stream);
 }
 
 }  // namespace
 
 hipError_t launch_kv_quant(const uint16_t* x, uint8_t* codes, float* params, int64_t rows, int64_t head_dim,
-                           int bits, hipStream_t stream) {
+                           int bits, bool bf16, hipStream_t stream) {
   if (rows > 0x7fffffff) return hipErrorInvalidValue;
-  if (bits == 8) return launch_bits<8>(x, codes, params, rows, head_dim, stream);
-  if (bits == 4) return launch_bits<4>(x, codes, params, rows, head_dim, stream);
+  if (bits == 8)
+    return bf16 ? launch_bits<8, true>(x, codes, params, rows, head_dim, stream)
+                : launch_bits<8, false>(x, codes, params, rows, head_dim, stream);
+  if (bits == 4)
+    return bf16 ? launch_bits<4, true>(x, codes, params, rows, head_dim, stream)
+                : launch_bits<4, false>(x, codes, params, rows, head_dim, stream);
   return hipErrorInvalidValue;
 }
 

@@ -41,9 +41,10 @@ hipError_t launch_w8a8_gemv_fused(const uint16_t* x, const int8_t* wq, const flo
 
 // Online KV-cache quantization of rows x [rows, head_dim] fp16 to codes
 // (uint8 [rows, head_dim] for 8 bits, packed [rows, head_dim/2] for 4) and
-// params fp32 [rows, 2] = (scale, min); head_dim a power of two in [8, 512].
+// params fp32 [rows, 2] = (scale, min); head_dim a power of two in [8, 512];
+// x is fp16, or bf16 when bf16.
 hipError_t launch_kv_quant(const uint16_t* x, uint8_t* codes, float* params, int64_t rows, int64_t head_dim,
-                           int bits, hipStream_t stream);
+                           int bits, bool bf16, hipStream_t stream);
 
 // Checkpoint-layout adapter (one-time conversions, exact bit permutations).
 // order[j] = the element (0..7 within the word's span) that field j of a

@@ -296,8 +296,8 @@ mq_status mq_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const uint16_
                     "w4a16_gemv launch");
 }
 
-mq_status mq_kv_quant(const uint16_t* x, uint8_t* codes, float* params, int64_t rows, int64_t head_dim,
-                      int32_t bits, void* stream) {
+static mq_status kv_quant_impl(const uint16_t* x, uint8_t* codes, float* params, int64_t rows, int64_t head_dim,
+                               int32_t bits, bool bf16, void* stream) {
   if (bits != 8 && bits != 4) return fail(MQ_ERR_UNSUPPORTED, "bits=%d (8 and 4 are provided)", (int)bits);
   if (head_dim < 8 || head_dim > 512 || (head_dim & (head_dim - 1)))
     return fail(MQ_ERR_SHAPE, "head_dim=%lld must be a power of two in [8, 512]", (long long)head_dim);
@@ -316,8 +316,18 @@ mq_status mq_kv_quant(const uint16_t* x, uint8_t* codes, float* params, int64_t 
                        {params, static_cast<size_t>(rows) * 8, "params"}};
   MQ_TRY(check_alias(in, out));
   if (rows == 0) return ok();
-  return hip_status(mq::launch_kv_quant(x, codes, params, rows, head_dim, bits, as_stream(stream)),
+  return hip_status(mq::launch_kv_quant(x, codes, params, rows, head_dim, bits, bf16, as_stream(stream)),
                     "kv_quant launch");
+}
+
+mq_status mq_kv_quant(const uint16_t* x, uint8_t* codes, float* params, int64_t rows, int64_t head_dim,
+                      int32_t bits, void* stream) {
+  return kv_quant_impl(x, codes, params, rows, head_dim, bits, false, stream);
+}
+
+mq_status mq_kv_quant_bf16(const uint16_t* x, uint8_t* codes, float* params, int64_t rows, int64_t head_dim,
+                           int32_t bits, void* stream) {
+  return kv_quant_impl(x, codes, params, rows, head_dim, bits, true, stream);
 }
 
 namespace {
