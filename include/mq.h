@@ -108,9 +108,13 @@ mq_status mq_quant_per_token_int8(const uint16_t* x, int8_t* xq, float* s_tok,
  *   wq     [N, K] int8   in   (weights, one row per output channel)
  *   s_ch   [N]    fp32   in   (per-output-channel scales)
  *   y      [M, N] fp16   out
- * Requires: 0 <= M, N < 2^31; 16 <= K <= 133144 (the int32 accumulator
- * bound 127*127*K < 2^31), K % 16 == 0; xq, wq, y 16-byte aligned; s_tok,
- * s_ch 4-byte aligned.
+ * Requires: 0 <= M, N < 2^31; 16 <= K <= 133136, K % 16 == 0 (133136 is
+ * the largest multiple of 16 with 127*127*K < 2^31); xq, wq, y 16-byte
+ * aligned; s_tok, s_ch 4-byte aligned.
+ * Codes are expected in [-127, 127], the range the per-token quantizer
+ * produces. Any int8 is accepted, but a code of -128 keeps the int32
+ * accumulator exact only while 128*128*K < 2^31, i.e. K <= 131056; above
+ * that an accumulator fed with -128 codes may wrap.
  * The kernel is chosen by shape (a weight-streaming kernel for up to 32
  * tokens, and for 33-64 tokens while N < 16384; a tiled GEMM otherwise).
  * Both compute the exact accumulator and the same epilogue, so results are
@@ -146,7 +150,7 @@ mq_status mq_w8a8_mm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc,
  *   workspace  >= mq_w8a8_linear_workspace_bytes(M, K) bytes (0 for the
  *              one-kernel case: may be NULL), 16-byte aligned, not
  *              overlapping any operand; its contents on entry do not matter.
- * Requires: as mq_w8a8_scaled_mm (K % 16 == 0, K <= 133144).
+ * Requires: as mq_w8a8_scaled_mm (K % 16 == 0, K <= 133136).
  */
 size_t mq_w8a8_linear_workspace_bytes(int64_t M, int64_t K);
 mq_status mq_w8a8_linear(const uint16_t* x, const int8_t* wq, const float* s_ch, uint16_t* y,
@@ -183,9 +187,15 @@ mq_status mq_w8a8_linear_bf16(const uint16_t* x, const int8_t* wq, const float* 
  *     z[g,n]  = field (n % 8) of qzeros[g, n/8]
  *     w[k,n]  = (q[k,n] - z[k/G,n]) * scales[k/G,n]
  *     y[m,n]  = fp16( sum_k x[m,k] * w[k,n] )   accumulated in fp32
- * The weight is rounded once to fp16 before the fp16 matrix multiply;
- * outputs match the exact result within relative Frobenius error 1e-3 and
- * max-abs error 5e-2 at the documented input distributions.
+ * The weight is rounded once to fp16, fp16((q - z) * s), before the fp16
+ * matrix multiply, for every fp16 scale. Outputs match the exact result
+ * within relative Frobenius error 1e-3 and max-abs error 5e-2 at the
+ * documented input distributions and for scales down to about 2^-16.
+ * Range of the fp16 weight: |(q - z) * s| must stay below 65520 (15 * |s|
+ * < 65520 always holds for |s| <= 4096), else that weight becomes +-inf;
+ * products below 2^-14 are fp16 subnormals (multiples of 2^-24), so with
+ * scales much below 2^-16 the relative error of the weights, and of y,
+ * grows. The GEMVs below apply s in fp32 and have neither limit.
  *
  *   x        [M, K]     fp16   in
  *   qweight  [K, N/8]   int32  in   (8 unsigned 4-bit weights per word along N)

@@ -10,7 +10,8 @@ configurations:
 
 * W4A16: activations fp16 ~ N(0, 1), optionally with a fraction of input
   channels (the same channels for every token) multiplied by 20; weights and
-  zero points uniform 4-bit; fp16 group scales uniform in [0.005, 0.02].
+  zero points uniform 4-bit; fp16 group scales uniform in [0.005, 0.02]
+  (or log-uniform over a stated range of powers of two).
 * W8A8: activations fp16 ~ N(0, 1) with 1% outlier channels x20; float
   weights ~ N(0, 0.02) rounded to fp16 (each side quantizes them per output
   channel with its own quantizer). The bf16 form draws the same activations
@@ -49,7 +50,17 @@ def random_words(rng, shape):
     return rng.integers(0, 2 ** 32, size=shape, dtype=np.uint32).view(np.int32)
 
 
-def w4a16_inputs(M, K, N, group=128, outlier_frac=0.0, tag=0, seed=0):
+def group_scales(rng, shape, scale_log2=None):
+    """fp16 group scales: uniform in [0.005, 0.02], or, with
+    ``scale_log2 = (lo, hi)``, 2**u with u uniform in [lo, hi] (log-uniform
+    magnitudes, as small or large as real checkpoints hold)."""
+    if scale_log2 is None:
+        return rng.uniform(SCALE_LO, SCALE_HI, size=shape).astype(np.float16)
+    lo, hi = scale_log2
+    return np.exp2(rng.uniform(lo, hi, size=shape)).astype(np.float16)
+
+
+def w4a16_inputs(M, K, N, group=128, outlier_frac=0.0, tag=0, seed=0, scale_log2=None):
     """Inputs of one W4A16 layer: dict(x, qweight, scales, qzeros)."""
     if N % 8:
         raise ValueError("N must be a multiple of 8")
@@ -60,18 +71,18 @@ def w4a16_inputs(M, K, N, group=128, outlier_frac=0.0, tag=0, seed=0):
     return {
         "x": activations(r_x, r_idx, M, K, outlier_frac),
         "qweight": random_words(r_q, (K, N // 8)),
-        "scales": r_s.uniform(SCALE_LO, SCALE_HI, size=(K // G, N)).astype(np.float16),
+        "scales": group_scales(r_s, (K // G, N), scale_log2),
         "qzeros": random_words(r_z, (K // G, N // 8)),
     }
 
 
-def w4a16_weights(K, N, group=128, tag=0, seed=0):
+def w4a16_weights(K, N, group=128, tag=0, seed=0, scale_log2=None):
     """Weights only (qweight, scales, qzeros), drawn as in ``w4a16_inputs``."""
     G = K if group == -1 else group
     _, _, r_q, r_s, r_z = _children(tag, seed, 5)
     return {
         "qweight": random_words(r_q, (K, N // 8)),
-        "scales": r_s.uniform(SCALE_LO, SCALE_HI, size=(K // G, N)).astype(np.float16),
+        "scales": group_scales(r_s, (K // G, N), scale_log2),
         "qzeros": random_words(r_z, (K // G, N // 8)),
     }
 

@@ -164,6 +164,28 @@ def check_dequant_exact(dequant):
     assert np.array_equal(w.astype(np.float64), expect)
 
 
+def check_dequant_exact_full_range(dequant):
+    """(q - z) * s is exact in float32 for every (q, z) pair and every finite
+    fp16 scale of either sign, subnormals included (an 11-bit significand
+    times an integer below 16 needs at most 15 bits, and the smallest product,
+    2^-24, is a normal binary32)."""
+    pos = np.arange(1, 0x7C00, dtype=np.uint16)
+    svals = np.concatenate([pos, pos | np.uint16(0x8000)]).view(np.float16)
+    n = (len(svals) + 7) // 8 * 8
+    svals = np.concatenate([svals, svals[: n - len(svals)]])
+    G = 16
+    K = 16 * G  # group g has zero point g; row k has q = k % 16
+    # every word of a row holds the same eight fields, so pack one word per row and repeat it
+    qweight = np.tile(loop_pack(np.tile((np.arange(K) % 16)[:, None], (1, 8))), (1, n // 8))
+    qzeros = np.tile(loop_pack(np.tile(np.arange(16)[:, None], (1, 8))), (1, n // 8))
+    scales = np.tile(svals[None, :], (16, 1)).astype(np.float16)
+    w = dequant(qweight, scales, qzeros, G)
+    assert w.dtype == np.float32
+    diff = (np.arange(K) % 16 - np.arange(K) // G).astype(np.float64)
+    expect = diff[:, None] * svals.astype(np.float64)[None, :]
+    assert np.array_equal(w.astype(np.float64), expect)
+
+
 def _tiny_w4_case(seed, M=3, K=256, N=16, G=128):
     rng = np.random.default_rng(seed)
     q = rng.integers(0, 16, size=(K, N))

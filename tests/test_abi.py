@@ -104,7 +104,8 @@ def test_w8a8_validation(lib):
     s = lib.mq_w8a8_scaled_mm
     assert s(A, None, C, D, E, 4, 8, 64, None) == NULL
     assert s(A, B, C, D, E, 4, 8, 60, None) == SHAPE
-    assert s(A, B, C, D, E, 4, 8, 133144 + 16, None) == SHAPE
+    assert s(A, B, C, D, E, 4, 8, 133136 + 16, None) == SHAPE
+    assert s(A, B, C, D, E + 2, 4, 8, 133136, None) == ALIGN      # the largest K passes the shape check
     assert s(A, B, C, D, E, 4, -8, 64, None) == SHAPE
     assert s(A + 1, B, C, D, E, 4, 8, 64, None) == ALIGN
     assert s(A, B + 1, C, D, E, 4, 8, 64, None) == ALIGN

@@ -30,6 +30,10 @@ def test_dequant_exact():
     P.check_dequant_exact(oracle.dequant_w4)
 
 
+def test_dequant_exact_full_scale_range():
+    P.check_dequant_exact_full_range(oracle.dequant_w4)
+
+
 def test_w4a16_bruteforce():
     P.check_w4a16_bruteforce(oracle.w4a16_ref)
 
@@ -284,6 +288,7 @@ def test_dequant_mutants_caught(mode):
     w = _w4a16_with(d)
     assert _fails(lambda: P.check_dequant_exact(d), lambda: P.check_w4a16_bruteforce(w),
                   lambda: P.check_w4a16_special_cases(w))
+    assert _fails(lambda: P.check_dequant_exact_full_range(d))
 
 
 @pytest.mark.parametrize("mode", ["fp32_acc", "fp16_out"])

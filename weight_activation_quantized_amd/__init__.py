@@ -29,7 +29,7 @@ and two compositions used by a model's linear layer:
 
     w4a16_linear(x, qweight, scales, qzeros, group)  GEMV for M <= 64, else GEMM
     w8a8_linear(x, wq, s_ch)                         quantize x (fp16 or bf16) per token, then scaled GEMM
-                                                     (one fused kernel for M <= 16)
+                                                     (one fused kernel for M = 1; a workspace otherwise)
 """
 
 import ctypes
@@ -357,7 +357,7 @@ def w4a16_linear(x, qweight, scales, qzeros, group=128, out=None, stream=None):
 
 
 def w8a8_linear_workspace_bytes(M, K):
-    """Workspace bytes ``w8a8_linear`` needs (0 for M <= 16)."""
+    """Workspace bytes ``w8a8_linear`` needs (0 when one fused kernel runs: M = 1, K <= 81904)."""
     return int(library().mq_w8a8_linear_workspace_bytes(M, K))
 
 

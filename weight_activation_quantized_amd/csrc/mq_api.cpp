@@ -28,7 +28,7 @@ mq_status ok() {
 
 constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
 constexpr int64_t kMaxK = int64_t{1} << 20;
-constexpr int64_t kMaxKInt8 = 133144;            // 127 * 127 * K < 2^31
+constexpr int64_t kMaxKInt8 = 133136;            // largest multiple of 16 with 127 * 127 * K < 2^31
 constexpr int64_t kMaxElems = int64_t{1} << 40;  // bound on M*N, M*K, K*N
 constexpr int64_t kMaxN4 = int64_t{1} << 27;     // W4A16 N (32-bit lane offsets)
 

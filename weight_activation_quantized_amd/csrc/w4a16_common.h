@@ -71,26 +71,4 @@ __device__ __forceinline__ void unpack_step(const uint32_t (&w)[8], const uint32
   }
 }
 
-// As unpack_step, then multiplied by the per-column fp16 scale pair sc2[p]
-// (s for even p, s/16 for odd p): each fragment element is fp16((q - z) * s).
-__device__ __forceinline__ void unpack_step_scaled(const uint32_t (&w)[8], const uint32_t (&negz)[8],
-                                                   const uint32_t (&sc2)[8], f16x8 (&b)[8]) {
-  const NibConst c = nib_const();
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const uint32_t lo = byte_perm(w[2 * t + 1], w[2 * t], 0x05040100u);
-    const uint32_t hi = byte_perm(w[2 * t + 1], w[2 * t], 0x07060302u);
-    const uint32_t lo8 = lo >> 8, hi8 = hi >> 8;
-    const uint32_t v[8] = {(lo & c.lo) | c.magic,  (lo & c.hi) | c.magic,  (lo8 & c.lo) | c.magic,
-                           (lo8 & c.hi) | c.magic, (hi & c.lo) | c.magic,  (hi & c.hi) | c.magic,
-                           (hi8 & c.lo) | c.magic, (hi8 & c.hi) | c.magic};
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const f16x2 d = (as_f16x2(v[p]) + as_f16x2(negz[p])) * as_f16x2(sc2[p]);
-      b[p][2 * t] = d[0];
-      b[p][2 * t + 1] = d[1];
-    }
-  }
-}
-
 }  // namespace mq

@@ -19,8 +19,12 @@
 //   wavefront's 16 and field parity j/16; it reads that column's words of
 //   rows 8h..8h+7 of a 16-row k-step and unpacks its four fields
 //   p = 2q + j/16 into four fp16 fragments, so tile q covers fields 2q and
-//   2q + 1 of the 16 columns. The unpack is exact and each weight is rounded
-//   once, to fp16((q - z) * s).
+//   2q + 1 of the 16 columns. A field in bits 0-3 of a 16-bit half, OR-ed
+//   into the pattern of 1024.0, reads as 1024 + q; a field in bits 4-7,
+//   OR-ed into the pattern of 64.0, reads as 64 + q (the mantissa step at
+//   64 is 1/16). Subtracting 1024 + z (64 + z) leaves q - z exactly, and the
+//   one multiply by s rounds each weight once, to fp16((q - z) * s), for
+//   every fp16 scale (subnormal products included).
 // - Everything moves HBM -> LDS with buffer_load ... lds through a ring of
 //   kStages 32-row stages: the x rows (shared by all wavefronts) and, per
 //   32-column area, its raw packed words, scales and zero points. The first
@@ -85,21 +89,25 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
 // A lane handles one 4-bit field parity par (lanes 16-31 of each half-wave
 // the odd fields): its four fields are p = 2q + par, q = 0..3.
 struct GroupParams {
-  uint32_t negz[4];  // -(1024 + z_p) (even p) or -(1024 + 16 z_p) (odd p), both halves
-  uint32_t sc2[4];   // s_p (even p) or s_p / 16 (odd p), both halves
+  uint32_t negz[4];  // -(1024 + z_p) (even p) or -(64 + z_p) (odd p), both halves
+  uint32_t sc2[4];   // s_p, both halves
 };
 
+// Zero point z of field p sits in bits 0-3 (even p) or 4-7 (odd p) of byte
+// p / 2 of zw: OR-ed into the sign and exponent of -1024.0 (0xE400) or
+// -64.0 (0xD400) it reads as -(1024 + z) or -(64 + z), the same encodings
+// as the weight fields.
 __device__ __forceinline__ void make_group_params(uint32_t zw, u32x4 sv, int par, GroupParams& gp) {
   const uint32_t zmask = par ? 0xF0u : 0x0Fu;
+  const uint32_t zbase = par ? 0xD400u : 0xE400u;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint32_t e = ((zw >> (8 * q)) & zmask) | 0xE400u;
+    const uint32_t e = ((zw >> (8 * q)) & zmask) | zbase;
     gp.negz[q] = e | (e << 16);
     const f16x2 s2 = as_f16x2(sv[q]);
-    f16 sc = par ? s2[1] * static_cast<f16>(0.0625f) : s2[0];  // exact: power-of-two rescale
     f16x2 rep;
-    rep[0] = sc;
-    rep[1] = sc;
+    rep[0] = s2[par];
+    rep[1] = s2[par];
     gp.sc2[q] = as_u32(rep);
   }
 }
@@ -107,8 +115,8 @@ __device__ __forceinline__ void make_group_params(uint32_t zw, u32x4 sv, int par
 // Fragments fp16((q - z) * s) of the lane's four fields for one 16-row
 // k-step: w[e] is the lane's word of row 8h + e. The byte permute gathers
 // bytes 0-1 (2-3) of a row pair; field p sits in byte p / 2 of a word, low
-// nibble for even p, high nibble (giving 1024 + 16 q) for odd p, selected
-// by the lane's mask.
+// nibble for even p, high nibble for odd p, selected by the lane's mask;
+// the lane's magic (1024.0 or 64.0) makes either read as an offset q.
 __device__ __forceinline__ void unpack_fields(const uint32_t (&w)[8], const GroupParams& gp, uint32_t mask,
                                               uint32_t magic, f16x8 (&b)[4]) {
 #pragma unroll
@@ -232,12 +240,14 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
   const int area = kABytes + (wave >> 1) * kAreaBytes;
   const int wbase = area + 4 * col_in_area;
   uint32_t mask, magic;
-  asm("v_mov_b32 %0, 0x64006400" : "=v"(magic));
   {
-    uint32_t mlo, mhi;
+    uint32_t mlo, mhi, glo, ghi;
     asm("v_mov_b32 %0, 0x000f000f" : "=v"(mlo));
     asm("v_mov_b32 %0, 0x00f000f0" : "=v"(mhi));
+    asm("v_mov_b32 %0, 0x64006400" : "=v"(glo));  // 1024.0: a field in bits 0-3 reads 1024 + q
+    asm("v_mov_b32 %0, 0x54005400" : "=v"(ghi));  // 64.0: a field in bits 4-7 reads 64 + q
     mask = par ? mhi : mlo;
+    magic = par ? ghi : glo;
   }
 
   f32x16 acc[2][4];
