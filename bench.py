@@ -51,8 +51,18 @@ Also reported (same line):
                microseconds and GB/s of x + codes + (scale, min).
   checkpoint   one-time checkpoint-layout conversions at the 8B gate_up size
                (field reorder, 4-bit transpose, scale transpose), warm.
+  roofline_prefill  the prefill GEMMs against their MFMA peaks: the W8A8 GEMM
+               at M=2048, K=N=4096 (int8, 5.0 POP/s) and the W4A16 GEMMs at
+               M=4096, N=4096, K=4096/12288 (fp16, 2.5 PFLOP/s); achieved =
+               2MNK / event-timed average launch; HBM traffic and MFMA-busy
+               fraction from a committed rocprofv3 counter summary while it
+               matches the kernel sources, else null.
+  fp16_matmul_context  torch.matmul in fp16 at the decode and prefill shapes,
+               context for the 4-bit vs fp16 ratio (not a target).
   cpu_baseline the CPU oracle on one step of the same workload (one weight
-               set), repeated for about 10 s, in the same unit.
+               set), on every core of this process's affinity set and again
+               on one thread, about --cpu-seconds in all, in the same unit;
+               with the host's CPU model.
 """
 
 import argparse
@@ -74,6 +84,10 @@ METRIC = "W4A16 decode GEMV GB/s (% HBM peak); W8A8/W4A16 prefill TOPS (% MFMA p
 GEMV_K, GEMV_N, GROUP = 4096, 24576, 128
 GEMV_MS = (1, 4, 16)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_c1_traffic.json")
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_gemm_counters.json")
+# Reading of "int8 weights from N(0, 0.02)": drawn in fp32, rounded to fp16 (the
+# served dtype), then quantized per output channel by the per-token quantizer.
+W8A8_WEIGHTS = "fp32 N(0, 0.02) rounded to fp16, then symmetric int8 per output channel (absmax/127)"
 GEMV_SOURCES = ["w4a16_gemv_blocked.hip", "w4a16_split.h", "w4a16_common.h", "device_common.h"]
 
 
@@ -105,6 +119,7 @@ def parse_args(argv=None):
     ap.add_argument("--no-kv", action="store_true", help="skip the KV-cache quantization measurements")
     ap.add_argument("--no-checkpoint", action="store_true", help="skip the checkpoint-layout conversions")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp16-context", action="store_true", help="skip the torch fp16 matmul context timings")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-kernel", action="store_true",
                     help="also run a plain 256 MB device copy (counter calibration under rocprofv3)")
@@ -233,6 +248,7 @@ def bench_prefill(torch, mq, synth, oracle_free_quant, args, log):
         "gemm_us": t_g * 1e6, "gemm_TOPS": ops / t_g / 1e12,
         "gemm_frac_int8_peak": ops / t_g / 1e12 / INT8_PEAK_TOPS,
         "layer_TOPS": ops / (t_q + t_g) / 1e12,
+        "weights": W8A8_WEIGHTS,
     }
     # the same layer with bf16 activations and output (same draws rounded to bf16)
     db = synth.w8a8_inputs_bf16(M, K, N, outlier_frac=0.01, tag=2)
@@ -473,33 +489,95 @@ def bench_checkpoint(torch, mq, log):
     return out
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(args, log):
+    """The oracle on one step of the headline workload (one weight set), on the
+    host cores this process may run on: BLAS threads = len(sched_getaffinity),
+    then again with one thread. Each leg repeats the step for about
+    --cpu-seconds / 2 (at least once)."""
     import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    affinity = len(os.sched_getaffinity(0))
     w = synth.w4a16_weights(GEMV_K, GEMV_N, GROUP, tag=1, seed=1000)
     xs = {M: synth.w4a16_inputs(M, GEMV_K, 8, GROUP, outlier_frac=0.005, tag=1, seed=M)["x"] for M in GEMV_MS}
-    reps, t_total = 0, 0.0
-    while True:
-        t0 = time.perf_counter()
-        for M in GEMV_MS:
-            y = oracle.w4a16_ref(xs[M], w["qweight"], w["scales"], w["qzeros"], GROUP)
-            assert np.all(np.isfinite(y))
-        t_total += time.perf_counter() - t0
-        reps += 1
-        if t_total >= args.cpu_seconds or reps >= 20:
-            break
     step_bytes = sum(w4a16_bytes(M, GEMV_K, GEMV_N) for M in GEMV_MS)
-    log(f"cpu baseline: {reps} steps in {t_total:.1f} s")
-    return {"value": step_bytes * reps / t_total / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} step(s) of the same workload (M=1,4,16 on one weight set), "
-                      f"{t_total:.1f} s; NumPy dequant is single-threaded, BLAS used {threads} thread(s)"}
+
+    def leg(threads):
+        with threadpool_limits(limits=threads):
+            used = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+            reps, t_total = 0, 0.0
+            while True:
+                t0 = time.perf_counter()
+                for M in GEMV_MS:
+                    y = oracle.w4a16_ref(xs[M], w["qweight"], w["scales"], w["qzeros"], GROUP)
+                    assert np.all(np.isfinite(y))
+                t_total += time.perf_counter() - t0
+                reps += 1
+                if t_total >= args.cpu_seconds / 2 or reps >= 20:
+                    break
+        log(f"cpu baseline: {reps} steps in {t_total:.1f} s with {used} BLAS thread(s)")
+        return step_bytes * reps / t_total / 1e9, used, reps, t_total
+
+    v_all, used_all, reps_all, t_all = leg(affinity)
+    v_one, _, reps_one, t_one = leg(1)
+    return {"value": round(v_all, 4), "unit": "GB/s", "cores": used_all, "kind": "oracle",
+            "sample": f"{reps_all} step(s) of the headline workload (M=1,4,16 against one 52 MB weight set) in "
+                      f"{t_all:.1f} s; NumPy unpack/dequant single-threaded, float64 BLAS matmul on "
+                      f"{used_all} thread(s)",
+            "cpu_model": cpu_model(), "affinity_cores": affinity,
+            "single_thread": {"value": round(v_one, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"{reps_one} step(s) in {t_one:.1f} s"}}
+
+
+def bench_fp16_context(torch, synth, log):
+    """Context only: torch.matmul in fp16 (hipBLASLt) at the headline decode
+    shapes (weights [K, N] fp16, two rotating 201 MB copies so each call reads
+    HBM) and at the two W4A16 prefill shapes, microseconds per call from graph
+    replays; for the 4-bit vs fp16 ratio the pages quote for whole models."""
+    dev = torch.device("cuda", 0)
+    R = 20
+    out = {}
+
+    def time_calls(fn):
+        g = capture(torch, lambda: [fn(r) for r in range(R)])
+        g.replay()
+        return min(timed_replay(torch, g)[1] for _ in range(3)) / R
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    ws = [(torch.randn((GEMV_K, GEMV_N), device=dev, generator=gen) * 0.02).half() for _ in range(2)]
+    for M in GEMV_MS:
+        x = torch.from_numpy(synth.w4a16_inputs(M, GEMV_K, 8, GROUP, outlier_frac=0.005, tag=1, seed=M)["x"]).to(dev)
+        y = torch.empty((M, GEMV_N), dtype=torch.float16, device=dev)
+        log(f"fp16 context: matmul M={M} K={GEMV_K} N={GEMV_N}")
+        t = time_calls(lambda r, x=x, y=y: torch.matmul(x, ws[r % 2], out=y))
+        nbytes = M * GEMV_K * 2 + GEMV_K * GEMV_N * 2 + M * GEMV_N * 2
+        out[f"decode_M{M}"] = {"us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1)}
+    del ws
+    for name, K in (("prefill_c3a", 4096), ("prefill_c3b", 12288)):
+        M, N = 4096, 4096
+        x = (torch.randn((M, K), device=dev, generator=gen)).half()
+        w = (torch.randn((K, N), device=dev, generator=gen) * 0.02).half()
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        log(f"fp16 context: matmul {name}")
+        t = time_calls(lambda r, x=x, w=w, y=y: torch.matmul(x, w, out=y))
+        out[name] = {"us": round(t * 1e6, 2), "TFLOPS": round(2.0 * M * N * K / t / 1e12, 1)}
+        del x, w, y
+    torch.cuda.empty_cache()
+    return out
 
 
 def load_traffic(launch_bytes):
@@ -510,6 +588,50 @@ def load_traffic(launch_bytes):
     if t.get("source_hash") != gemv_source_hash():
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+PREFILL_SOURCES = {"w8a8_c2": ["w8a8_gemm.hip", "device_common.h", "launch.h"],
+                   "w4a16_c3a": ["w4a16_gemm.hip", "w4a16_common.h", "device_common.h", "launch.h"],
+                   "w4a16_c3b": ["w4a16_gemm.hip", "w4a16_common.h", "device_common.h", "launch.h"]}
+
+
+def source_hash(files):
+    from weight_activation_quantized_amd import _build
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "weight_activation_quantized_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    h.update(repr(_build.FLAGS[:-2]).encode())
+    return h.hexdigest()[:16]
+
+
+def prefill_roofline(prefill):
+    """Roofline objects for the prefill GEMMs: achieved = 2MNK per launch /
+    event-timed average launch duration, against the dense MFMA peak of the
+    kernel's operand type; `traffic` and MFMA-busy from the committed counter
+    summary while it matches the kernel's sources, else null."""
+    counters = {}
+    if os.path.exists(PREFILL_TRAFFIC_FILE):
+        with open(PREFILL_TRAFFIC_FILE) as f:
+            counters = json.load(f).get("kernels", {})
+    out = {}
+    for key, kernel, peak, unit in (("w8a8_c2", "w8a8_gemm_kernel<true, false>", INT8_PEAK_TOPS, "TOP/s"),
+                                    ("w4a16_c3a", "w4a16_gemm_kernel<4>", FP16_PEAK_TFLOPS, "TFLOP/s"),
+                                    ("w4a16_c3b", "w4a16_gemm_kernel<4>", FP16_PEAK_TFLOPS, "TFLOP/s")):
+        p = prefill.get(key)
+        if not p:
+            continue
+        M, N, K = p["shape"]
+        ach = p.get("gemm_TOPS", p.get("gemm_TFLOPS"))
+        c = counters.get(key, {})
+        fresh = c.get("source_hash") == source_hash(PREFILL_SOURCES[key])
+        out[key] = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": unit,
+                    "frac": round(ach / peak, 4),
+                    "traffic": c.get("hbm_bytes_per_launch") if fresh else None,
+                    "mfma_busy": c.get("mfma_busy") if fresh else None,
+                    "kernel": kernel, "avg_launch_us": round(p["gemm_us"], 3),
+                    "algorithmic_ops_per_launch": 2 * M * N * K}
+    return out
 
 
 def main(argv=None):
@@ -568,6 +690,7 @@ def main(argv=None):
                         "decode layout (converted once before timing)",
             "M": list(GEMV_MS), "K": GEMV_K, "N": GEMV_N, "group": GROUP, "weight_sets": args.sets,
             "gemv_workspace_bytes": res["workspace_bytes"], "parallelism": "single GPU",
+            "w8a8_weights": W8A8_WEIGHTS,
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -581,6 +704,9 @@ def main(argv=None):
     }
     if not args.no_prefill:
         line["prefill"] = bench_prefill(torch, mq, synth, mq.quant_per_token_int8, args, log)
+        line["roofline_prefill"] = prefill_roofline(line["prefill"])
+    if not args.no_fp16_context:
+        line["fp16_matmul_context"] = bench_fp16_context(torch, synth, log)
     if not args.no_layers:
         line["layers"] = bench_layers(torch, mq, synth, args, log)
     if not args.no_groups:
