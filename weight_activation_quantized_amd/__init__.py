@@ -45,7 +45,9 @@ __all__ = [
     "AWQ_FIELD_ORDER", "int4_reorder", "int4_transpose", "u16_transpose",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmq.so")
+# The in-tree build; MQ_LIBRARY names another build of the same library (for
+# example the host-sanitized one that the CPU tests load).
+LIB_PATH = os.environ.get("MQ_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmq.so")
 GEMV_MAX_M = 64
 
 STATUS_NAMES = {

@@ -137,7 +137,13 @@ extern "C" {
 int mq_abi_version(void) { return MQ_ABI_VERSION; }
 
 const char* mq_status_string(mq_status s) {
-  switch (s) {
+  // A C caller may pass any int (a C enum is an int); in C++ a value outside
+  // the enumerators' range must not be read as mq_status, so the argument's
+  // bytes are read as an int first.
+  int v;
+  static_assert(sizeof(v) == sizeof(s), "mq_status is passed as an int");
+  std::memcpy(&v, &s, sizeof(v));
+  switch (v) {
     case MQ_OK: return "MQ_OK";
     case MQ_ERR_NULL: return "MQ_ERR_NULL";
     case MQ_ERR_SHAPE: return "MQ_ERR_SHAPE";
