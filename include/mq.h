@@ -177,6 +177,27 @@ mq_status mq_w8a8_linear_bf16(const uint16_t* x, const int8_t* wq, const float* 
                               int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Allocation-free form of mq_w8a8_linear (fp16), for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid hipMalloc. Same operands, result (bit for bit),
+ * kernels and requirements as mq_w8a8_linear, without the workspace
+ * arguments: for more than one token the quantizer's codes and per-token
+ * scales go to a scratch array that the library holds on each GPU it runs
+ * on, MQ_NOALLOC_SCRATCH_BYTES (32 MiB + 256 KiB) long, from the first call
+ * on that device until the process ends. The call allocates nothing and
+ * issues no memset (the scratch is fully written before it is read).
+ * Requires mq_w8a8_linear_workspace_bytes(M, K) <= MQ_NOALLOC_SCRATCH_BYTES
+ * (e.g. 2048 tokens at K = 12288), else MQ_ERR_WORKSPACE before any HIP
+ * call. Every call on one GPU shares that GPU's scratch: calls that may
+ * overlap in time on one GPU (different streams without ordering, several
+ * host threads) race and must be serialized by the caller; calls on one
+ * stream are ordered and safe.
+ */
+#define MQ_NOALLOC_SCRATCH_BYTES 33816576
+mq_status mq_w8a8_linear_noalloc(const uint16_t* x, const int8_t* wq, const float* s_ch, uint16_t* y, int64_t M,
+                                 int64_t N, int64_t K, void* stream);
+
+/*
  * W4A16 GEMM (prefill-shaped M).
  * Source: LMDeploy toolkit overview, section 2.5 (4-bit AWQ weights, group
  * size 128); LMDeploy 4-bit deployment guide, section 2.2 (dequantization

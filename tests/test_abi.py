@@ -41,7 +41,7 @@ def test_header_declares_the_boundary():
               "mq_w8a8_linear_workspace_bytes", "mq_w4a16_gemm_workspace_bytes", "mq_kv_quant", "mq_abi_version",
               "mq_status_string", "mq_last_error", "mq_int4_reorder", "mq_int4_transpose", "mq_u16_transpose",
               "mq_quant_per_token_int8_bf16", "mq_w8a8_scaled_mm_bf16", "mq_w8a8_linear_bf16",
-              "mq_kv_quant_bf16"]:
+              "mq_kv_quant_bf16", "mq_w8a8_linear_noalloc"]:
         assert n in names
 
 
@@ -328,3 +328,18 @@ def test_kv_quant_bf16_validates_like_fp16(lib):
                  (A + 8, B, C, 16, 128, 8, None), (A, A + 64, C, 16, 128, 8, None), (A, B, C, 0, 128, 8, None),
                  (A, B, C, 1 << 26, 512, 8, None)):
         assert k(*args) == k16(*args)
+
+
+def test_w8a8_linear_noalloc_validation(lib):
+    f = lib.mq_w8a8_linear_noalloc
+    assert f(A, None, C, D, 4, 8, 64, None) == NULL
+    assert f(A, B, C, D, 4, 8, 60, None) == SHAPE
+    assert f(A + 8, B, C, D, 4, 8, 64, None) == ALIGN
+    assert f(A, B, C, A + 16, 4, 8, 64, None) == ALIAS
+    # the scratch holds mq_w8a8_linear_workspace_bytes(M, K) <= MQ_NOALLOC_SCRATCH_BYTES
+    assert mq.NOALLOC_SCRATCH_BYTES == 33816576
+    assert lib.mq_w8a8_linear_workspace_bytes(2048, 12288) <= mq.NOALLOC_SCRATCH_BYTES
+    assert lib.mq_w8a8_linear_workspace_bytes(4096, 12288) > mq.NOALLOC_SCRATCH_BYTES
+    assert f(A, B, C, D, 4096, 8, 12288, None) == WS       # rejected before any HIP call
+    assert "scratch" in _err(lib)
+    assert f(A, B, C, D, 0, 8, 64, None) == OK             # empty problem: nothing enqueued, no lookup

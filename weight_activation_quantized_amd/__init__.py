@@ -30,6 +30,7 @@ and two compositions used by a model's linear layer:
     w4a16_linear(x, qweight, scales, qzeros, group)  GEMV for M <= 64, else GEMM
     w8a8_linear(x, wq, s_ch)                         quantize x (fp16 or bf16) per token, then scaled GEMM
                                                      (one fused kernel for M = 1; a workspace otherwise)
+    w8a8_linear_noalloc(x, wq, s_ch)                 the same (fp16) with the library's own scratch: no allocation
 """
 
 import ctypes
@@ -43,6 +44,7 @@ __all__ = [
     "w4a16_block_weights", "w4a16_gemv_blocked", "w4a16_gemv_blocked_workspace_bytes",
     "w8a8_linear_workspace_bytes", "w4a16_gemm_workspace_bytes", "kv_quant",
     "AWQ_FIELD_ORDER", "int4_reorder", "int4_transpose", "u16_transpose",
+    "w8a8_linear_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 # The in-tree build; MQ_LIBRARY names another build of the same library (for
@@ -89,6 +91,7 @@ _PROTOTYPES = {
     "mq_quant_per_token_int8_bf16": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P]),
     "mq_w8a8_scaled_mm_bf16": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "mq_w8a8_linear_bf16": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
+    "mq_w8a8_linear_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "mq_int4_reorder": (ctypes.c_int, [_P, _P, _I64, _P, _P]),
     "mq_int4_transpose": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P]),
     "mq_u16_transpose": (ctypes.c_int, [_P, _P, _I64, _I64, _P]),
@@ -387,6 +390,32 @@ def w8a8_linear(x, wq, s_ch, out=None, workspace=None, stream=None):
         fn = library().mq_w8a8_linear_bf16 if dt == torch.bfloat16 else library().mq_w8a8_linear
         _check(fn(x.data_ptr(), wq.data_ptr(), s_ch.data_ptr(), y.data_ptr(), M, N, K, ws_ptr, ws_bytes,
                   _stream_of(x, stream)))
+    return y
+
+
+# Bytes of the library-owned scratch behind ``w8a8_linear_noalloc`` (per GPU).
+NOALLOC_SCRATCH_BYTES = 33816576
+
+
+def w8a8_linear_noalloc(x, wq, s_ch, out=None, stream=None):
+    """``w8a8_linear`` for fp16 x without a workspace: the library keeps the
+    codes and per-token scales in its own scratch array on each GPU (for
+    callers that cannot allocate, e.g. under graph capture). Needs
+    ``w8a8_linear_workspace_bytes(M, K) <= NOALLOC_SCRATCH_BYTES``. Calls that
+    may overlap in time on one GPU share that scratch and must be serialized
+    by the caller (one stream suffices). With ``out`` given, allocates nothing."""
+    torch = _torch()
+    _dev_tensor(x, "x", torch.float16, 2)
+    _dev_tensor(wq, "wq", torch.int8, 2)
+    _dev_tensor(s_ch, "s_ch", torch.float32, 1)
+    M, K = x.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K or s_ch.shape[0] != N:
+        raise ValueError("wq must be [N, K] and s_ch [N]")
+    y = _out(out, (M, N), torch.float16, x, "out")
+    with torch.cuda.device(x.device):
+        _check(library().mq_w8a8_linear_noalloc(x.data_ptr(), wq.data_ptr(), s_ch.data_ptr(), y.data_ptr(), M, N, K,
+                                                _stream_of(x, stream)))
     return y
 
 

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(HERE, "libmq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["mq_api.cpp", "quant_int8.hip", "w8a8_gemm.hip", "w8a8_gemv.hip", "w4a16_gemv.hip",
-           "w4a16_gemv_blocked.hip", "w4a16_gemm.hip", "kv_quant.hip", "int4_layout.hip"]
+           "w4a16_gemv_blocked.hip", "w4a16_gemm.hip", "kv_quant.hip", "int4_layout.hip", "w8a8_noalloc.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

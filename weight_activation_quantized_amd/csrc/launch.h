@@ -39,6 +39,11 @@ bool w8a8_use_fused(int64_t M, int64_t K);
 hipError_t launch_w8a8_gemv_fused(const uint16_t* x, const int8_t* wq, const float* s_ch, uint16_t* y,
                                   int64_t M, int64_t N, int64_t K, bool bf16, hipStream_t stream);
 
+// Device address of the library-owned scratch array on the current device
+// (looked up once per device), kNoallocScratchBytes long, 256-byte aligned.
+constexpr size_t kNoallocScratchBytes = 33816576;  // MQ_NOALLOC_SCRATCH_BYTES
+hipError_t noalloc_scratch(void** ptr);
+
 // Online KV-cache quantization of rows x [rows, head_dim] fp16 to codes
 // (uint8 [rows, head_dim] for 8 bits, packed [rows, head_dim/2] for 4) and
 // params fp32 [rows, 2] = (scale, min); head_dim a power of two in [8, 512];

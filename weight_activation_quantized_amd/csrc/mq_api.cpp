@@ -408,8 +408,13 @@ size_t mq_w8a8_linear_workspace_bytes(int64_t M, int64_t K) {
   return (static_cast<size_t>(M * K) + 255) / 256 * 256 + static_cast<size_t>(M) * 4;
 }
 
+static_assert(mq::kNoallocScratchBytes == MQ_NOALLOC_SCRATCH_BYTES, "scratch size in mq.h");
+
+// noalloc: the workspace is the library's scratch array, looked up after
+// every argument check passed (the only HIP call before the launches).
 static mq_status linear_impl(const uint16_t* x, const int8_t* wq, const float* s_ch, uint16_t* y, int64_t M,
-                             int64_t N, int64_t K, void* workspace, size_t workspace_bytes, bool bf16, void* stream) {
+                             int64_t N, int64_t K, void* workspace, size_t workspace_bytes, bool bf16, void* stream,
+                             bool noalloc = false) {
   mq_status s = check_mk(M, K, 16, kMaxKInt8, 16);
   if (s != MQ_OK) return s;
   if (N < 0 || N > kMaxDim) return fail(MQ_ERR_SHAPE, "N=%lld out of range", (long long)N);
@@ -422,7 +427,11 @@ static mq_status linear_impl(const uint16_t* x, const int8_t* wq, const float* s
     return fail(MQ_ERR_ALIGN, "x, wq and y must be 16-byte aligned");
   if (!aligned(s_ch, 4)) return fail(MQ_ERR_ALIGN, "s_ch must be 4-byte aligned");
   const size_t ws = mq_w8a8_linear_workspace_bytes(M, K);
-  if (ws > 0) {
+  if (noalloc) {
+    if (ws > MQ_NOALLOC_SCRATCH_BYTES)
+      return fail(MQ_ERR_WORKSPACE, "M*K=%lld needs %zu bytes of scratch; the allocation-free entry holds %zu",
+                  (long long)(M * K), ws, static_cast<size_t>(MQ_NOALLOC_SCRATCH_BYTES));
+  } else if (ws > 0) {
     if (!workspace || workspace_bytes < ws)
       return fail(MQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws,
                   workspace ? workspace_bytes : static_cast<size_t>(0));
@@ -431,10 +440,16 @@ static mq_status linear_impl(const uint16_t* x, const int8_t* wq, const float* s
   const Range in[] = {{x, static_cast<size_t>(M * K) * 2, "x"},
                       {wq, static_cast<size_t>(N * K), "wq"},
                       {s_ch, static_cast<size_t>(N) * 4, "s_ch"}};
-  const Range out[] = {{y, static_cast<size_t>(M * N) * 2, "y"}, {ws ? workspace : nullptr, ws, "workspace"}};
+  // (the library's scratch cannot overlap a caller's buffer)
+  const Range out[] = {{y, static_cast<size_t>(M * N) * 2, "y"},
+                       {ws && !noalloc ? workspace : nullptr, noalloc ? 0 : ws, "workspace"}};
   s = check_alias(in, out);
   if (s != MQ_OK) return s;
   if (M == 0 || N == 0) return ok();
+  if (noalloc && ws > 0) {
+    MQ_TRY(hip_status(mq::noalloc_scratch(&workspace), "w8a8_linear_noalloc scratch lookup"));
+    workspace_bytes = MQ_NOALLOC_SCRATCH_BYTES;
+  }
   if (mq::w8a8_use_fused(M, K))
     return hip_status(mq::launch_w8a8_gemv_fused(x, wq, s_ch, y, M, N, K, bf16, as_stream(stream)),
                       "w8a8_linear launch");
@@ -455,6 +470,11 @@ mq_status mq_w8a8_linear(const uint16_t* x, const int8_t* wq, const float* s_ch,
 mq_status mq_w8a8_linear_bf16(const uint16_t* x, const int8_t* wq, const float* s_ch, uint16_t* y, int64_t M,
                               int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
   return linear_impl(x, wq, s_ch, y, M, N, K, workspace, workspace_bytes, true, stream);
+}
+
+mq_status mq_w8a8_linear_noalloc(const uint16_t* x, const int8_t* wq, const float* s_ch, uint16_t* y, int64_t M,
+                                 int64_t N, int64_t K, void* stream) {
+  return linear_impl(x, wq, s_ch, y, M, N, K, nullptr, 0, false, stream, true);
 }
 
 mq_status mq_w4a16_block_weights(const int32_t* qweight, int32_t* qweight_blocked, int64_t N, int64_t K,
