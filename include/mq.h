@@ -311,8 +311,11 @@ size_t mq_w4a16_gemv_blocked_workspace_bytes(int64_t M, int64_t N, int64_t K, in
  * Each workgroup streams one 32-output strip over its K range as one
  * contiguous run of bytes; K is split across workgroups (fp32 partials in
  * `workspace`, added in split order by a second kernel) only when the layer
- * has too few strips for two workgroups per compute unit. Up to 32 tokens share one pass over
- * the weights; larger M takes one pass per 32 tokens. Deterministic.
+ * has too few strips for two workgroups per compute unit. All M <= 64 tokens share one pass
+ * over the weights. For 33-64 tokens the fragments are the weights themselves,
+ * rounded once to fp16 as in mq_w4a16_gemm (fp16((q - z) * s), the same range
+ * notes apply), accumulated in fp32; up to 32 tokens use the exact (q - z)
+ * form with s applied in fp32. Deterministic.
  *
  *   workspace   >= mq_w4a16_gemv_blocked_workspace_bytes(M, N, K, group)
  *               bytes, 16-byte aligned (may be NULL when that is 0); same

@@ -35,6 +35,21 @@ def test_layer_w4a16(name, shape, M):
     assert_fp16_close(host(y), ref, f"w4a16 {name} M={M}")
 
 
+@pytest.mark.parametrize("M", [m for m in MS if m <= mq.GEMV_MAX_M] + [33, 48])
+@pytest.mark.parametrize("name,shape", LAYERS, ids=[n for n, _ in LAYERS])
+def test_layer_w4a16_decode_layout(name, shape, M):
+    # decode through the layer entry with weights converted once to the
+    # decode layout (the path the layer-set timings take)
+    K, N = shape["K"], shape["N"]
+    d = synth.w4a16_inputs(M, K, N, group=128, outlier_frac=0.005, tag=150 + K + N, seed=M)
+    announce(f"layer w4a16 decode layout {name} M={M}")
+    qw = dev(d["qweight"])
+    y = mq.w4a16_linear(dev(d["x"]), qw, dev(d["scales"]), dev(d["qzeros"]), 128,
+                        qweight_blocked=mq.w4a16_block_weights(qw))
+    ref = oracle.w4a16_ref(d["x"], d["qweight"], d["scales"], d["qzeros"], 128)
+    assert_fp16_close(host(y), ref, f"w4a16 decode layout {name} M={M}")
+
+
 @pytest.mark.parametrize("M", MS)
 @pytest.mark.parametrize("name,shape", LAYERS, ids=[n for n, _ in LAYERS])
 def test_layer_w8a8(name, shape, M):

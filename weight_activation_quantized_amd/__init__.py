@@ -27,7 +27,8 @@ Entry points (same names as the C ABI, without the ``mq_`` prefix):
 
 and two compositions used by a model's linear layer:
 
-    w4a16_linear(x, qweight, scales, qzeros, group)  GEMV for M <= 64, else GEMM
+    w4a16_linear(x, qweight, scales, qzeros, group)  GEMV for M <= 64 (decode layout if qweight_blocked
+                                                     is given), else GEMM
     w8a8_linear(x, wq, s_ch)                         quantize x (fp16 or bf16) per token, then scaled GEMM
                                                      (one fused kernel for M = 1; a workspace otherwise)
     w8a8_linear_noalloc(x, wq, s_ch)                 the same (fp16) with the library's own scratch: no allocation
@@ -354,9 +355,14 @@ def w4a16_gemv_blocked(x, qweight_blocked, scales, qzeros, group=128, out=None, 
     return y
 
 
-def w4a16_linear(x, qweight, scales, qzeros, group=128, out=None, stream=None):
-    """W4A16 linear layer: the GEMV for M <= 64 (decode), the GEMM otherwise (prefill)."""
+def w4a16_linear(x, qweight, scales, qzeros, group=128, out=None, stream=None, qweight_blocked=None):
+    """W4A16 linear layer: a GEMV for M <= 64 (decode), the GEMM otherwise
+    (prefill). With ``qweight_blocked`` (``w4a16_block_weights(qweight)``,
+    converted once when the layer is loaded) decode runs the GEMV on the
+    decode layout, the faster one; without it, the GEMV on [K, N/8]."""
     if x.shape[0] <= GEMV_MAX_M:
+        if qweight_blocked is not None:
+            return w4a16_gemv_blocked(x, qweight_blocked, scales, qzeros, group, out=out, stream=stream)
         return w4a16_gemv(x, qweight, scales, qzeros, group, out=out, stream=stream)
     return w4a16_gemm(x, qweight, scales, qzeros, group, out=out, stream=stream)
 

@@ -27,14 +27,19 @@ namespace mq {
 // splits each (v & mask) | magic into v_and_b32 + v_or_b32; with register
 // operands it emits one v_and_or_b32 (a third fewer VALU ops in the unpack).
 // The values come from non-volatile asm the compiler can hoist out of loops.
+// magic64 is the pattern of 64.0 (0x5400): a field in bits 4-7 OR-ed into
+// it reads 64 + q (the mantissa step at 64 is 1/16), for kernels that
+// scale the fragments in fp16 and so need the high field without the
+// factor 16.
 struct NibConst {
-  uint32_t lo, hi, magic;
+  uint32_t lo, hi, magic, magic64;
 };
 __device__ __forceinline__ NibConst nib_const() {
   NibConst c;
   asm("v_mov_b32 %0, 0x000f000f" : "=v"(c.lo));
   asm("v_mov_b32 %0, 0x00f000f0" : "=v"(c.hi));
   asm("v_mov_b32 %0, 0x64006400" : "=v"(c.magic));
+  asm("v_mov_b32 %0, 0x54005400" : "=v"(c.magic64));
   return c;
 }
 

@@ -41,6 +41,10 @@
 // ones per block). The wavefronts' sums are added in LDS in wavefront
 // order, so results are deterministic. 32-output strips give 768
 // workgroups for a 24576-wide layer: every CU streams the same share.
+// With 33-64 tokens (three or four tiles) the kernel instead forms the
+// weights themselves, fp16((q - z) * s) rounded once, and accumulates the
+// MFMAs straight into the running sums: one pass over the weights for all
+// tokens, with several strips per workgroup sharing the x fragments.
 #include <algorithm>
 
 #include "device_common.h"
@@ -113,7 +117,7 @@ struct BChunk {
 struct BLane {
   const u32x4* qb;        // the lane's 16-byte slot of the strip's first pair
   size_t pair_stride;     // slots from one 64-row pair to the next (S * 64)
-  const uint16_t* x[2];   // token row of each tile (nullptr: row >= M)
+  const uint16_t* x[4];   // token row of each tile (nullptr: row >= M)
   const uint16_t* sc;     // scales + 8 * packed column + 2g
   const uint32_t* qz;     // qzeros + packed column
   int N, NP;
@@ -260,6 +264,66 @@ __device__ __forceinline__ void compute_chunk(const BChunk<kT, kBChunkRows / kGS
   }
 }
 
+// Pre-scaled B fragments (forms with three or four token tiles): as
+// unpack_block, but each fragment element is the weight itself,
+// fp16((q - z) * s), rounded once: field 2g reads 1024 + q (pattern of
+// 1024.0), field 2g+1 reads 64 + q (pattern of 64.0, no factor 16); adding
+// -(1024 + z) / -(64 + z) leaves q - z exactly, and one multiply by s rounds.
+// nz[f] / s2[f]: the encoded negated zero point and the scale of field f,
+// both replicated in the two fp16 halves.
+__device__ __forceinline__ void unpack_block_scaled(uint32_t w0, uint32_t w1, const NibConst& c,
+                                                    const uint32_t (&nz)[2], const uint32_t (&s2)[2],
+                                                    f16x8 (&bf)[2]) {
+  const uint32_t ws[2] = {w0, w1};
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t v = byte_perm(ws[q], ws[q], t ? 0x0C030C02u : 0x0C010C00u);
+      const f16x2 lo = (as_f16x2((v & c.lo) | c.magic) + as_f16x2(nz[0])) * as_f16x2(s2[0]);
+      const f16x2 hi = (as_f16x2((v & c.hi) | c.magic64) + as_f16x2(nz[1])) * as_f16x2(s2[1]);
+      bf[0][4 * q + 2 * t] = lo[0];
+      bf[0][4 * q + 2 * t + 1] = lo[1];
+      bf[1][4 * q + 2 * t] = hi[0];
+      bf[1][4 * q + 2 * t + 1] = hi[1];
+    }
+}
+
+// One chunk of the pre-scaled form: the MFMAs accumulate straight into the
+// running sums (the weights carry their scales), so no per-group partial
+// sums or sums of x are kept -- that is what lets three strips share every
+// x fragment of four token tiles within the register file.
+template <int kT, int kGS, int kSP>
+__device__ __forceinline__ void compute_chunk_scaled(const BChunk<kT, kBChunkRows / kGS, kSP>& ch,
+                                                     const NibConst& nc, int g_lane, f32x4 (&tot)[kT][kSP][2]) {
+  constexpr int kGPC = kBChunkRows / kGS;
+  constexpr int kBPG = kGS / 32;
+#pragma unroll
+  for (int g = 0; g < kGPC; ++g)
+#pragma unroll
+    for (int sp = 0; sp < kSP; ++sp) {
+      const f16x2 sv = as_f16x2(ch.sv[sp][g]);
+      const uint32_t zb = (ch.zw[sp][g] >> (8 * g_lane)) & 0xFFu;
+      f16x2 s_lo, s_hi;
+      s_lo[0] = s_lo[1] = sv[0];
+      s_hi[0] = s_hi[1] = sv[1];
+      const uint32_t e_lo = (zb & 0x0Fu) | 0xE400u, e_hi = (zb & 0xF0u) | 0xD400u;
+      const uint32_t nz[2] = {e_lo | (e_lo << 16), e_hi | (e_hi << 16)};
+      const uint32_t s2[2] = {as_u32(s_lo), as_u32(s_hi)};
+#pragma unroll
+      for (int bb = 0; bb < kBPG; ++bb) {
+        const int b = g * kBPG + bb;
+        f16x8 bf[2];
+        unpack_block_scaled(ch.w[sp][b >> 1][2 * (b & 1)], ch.w[sp][b >> 1][2 * (b & 1) + 1], nc, nz, s2, bf);
+#pragma unroll
+        for (int t = 0; t < kT; ++t)
+#pragma unroll
+          for (int f = 0; f < 2; ++f)
+            tot[t][sp][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ch.a[t][b], bf[f], tot[t][sp][f], 0, 0, 0);
+      }
+    }
+}
+
 // kT 16-token tiles, groups of kGS rows, kW wavefronts per workgroup, kSP
 // adjacent strips per workgroup (they share every x fragment a wavefront
 // loads). `units` counts kSP-strip units.
@@ -272,6 +336,9 @@ __device__ __forceinline__ void compute_chunk(const BChunk<kT, kBChunkRows / kGS
 // fragments and the group parameters from there, so the weight stream has
 // the vector-memory queue to itself (per-chunk x loads cost about 2 us and
 // the scale and zero-point loads about 0.7 us of a 13 us call at N = 24576).
+// Three or four tiles (33-64 tokens) take the pre-scaled form: one pass
+// over the weights for all tokens, the wavefronts' sums added in LDS one
+// wavefront after the other (same order, smaller buffer).
 template <int kT, int kGS, int kW, int kSP, bool kXL>
 __global__ __launch_bounds__(kW * 64)
 __attribute__((amdgpu_waves_per_eu(kT == 1 && kSP == 1 && kGS >= 64 ? 3 : 1))) void w4a16_gemv_blocked_kernel(
@@ -280,7 +347,9 @@ __attribute__((amdgpu_waves_per_eu(kT == 1 && kSP == 1 && kGS >= 64 ? 3 : 1))) v
     int units, int splits, XcdMap map) {
   constexpr int kGPC = kBChunkRows / kGS;
   constexpr int kUOut = kSP * kBOut;  // outputs per unit
-  __shared__ float s_red[kW * 16 * kT * kUOut];
+  constexpr bool kPS = kT >= 3;       // pre-scaled weights
+  static_assert(!(kPS && kXL), "the pre-scaled form loads x per chunk");
+  __shared__ float s_red[(kPS ? 1 : kW) * 16 * kT * kUOut];
   extern __shared__ __attribute__((aligned(16))) uint8_t x_dyn[];  // kXL: M rows of staged x
 
   int unit, split;
@@ -302,7 +371,7 @@ __attribute__((amdgpu_waves_per_eu(kT == 1 && kSP == 1 && kGS >= 64 ? 3 : 1))) v
   L.qb = qb + static_cast<size_t>(strip) * 64 + lane;
   L.pair_stride = static_cast<size_t>(NP / kBStrip) * 64;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < 4; ++t) {
     const int m = 16 * t + j;
     L.x[t] = (t < kT && m < M) ? x + static_cast<size_t>(m) * K + 8 * h : nullptr;
   }
@@ -379,44 +448,71 @@ __attribute__((amdgpu_waves_per_eu(kT == 1 && kSP == 1 && kGS >= 64 ? 3 : 1))) v
     };
     auto sl = [&](int chunk) -> const lds_u8* { return sc_lane + (chunk - kbase) * kGPC * kSP * 64; };
     auto zl = [&](int chunk) -> const lds_u8* { return z_lane + (chunk - kbase) * kGPC * kSP * 16; };
+    auto compute = [&](const BChunk<kT, kGPC, kSP>& ch, int chunk) {
+      if constexpr (kPS) {
+        compute_chunk_scaled<kT, kGS, kSP>(ch, nc, g, tot);
+      } else {
+        compute_chunk<kT, kGS, kSP, kXL>(ch, nc, ones, g, tot, xl(chunk), sl(chunk), zl(chunk));
+      }
+    };
     int i = 0;
     for (; i + 3 < cpw; i += 2) {
-      compute_chunk<kT, kGS, kSP, kXL>(ca, nc, ones, g, tot, xl(c0 + i), sl(c0 + i), zl(c0 + i));
+      compute(ca, c0 + i);
       load_chunk<kT, kGS, kSP, kXL>(ca, L, c0 + i + 2);
       __builtin_amdgcn_sched_barrier(0);
-      compute_chunk<kT, kGS, kSP, kXL>(cb, nc, ones, g, tot, xl(c0 + i + 1), sl(c0 + i + 1),
-                                                         zl(c0 + i + 1));
+      compute(cb, c0 + i + 1);
       load_chunk<kT, kGS, kSP, kXL>(cb, L, c0 + i + 3);
       __builtin_amdgcn_sched_barrier(0);
     }
     // chunks i and (if in range) i + 1 are in flight; at most i + 2 is left
-    compute_chunk<kT, kGS, kSP, kXL>(ca, nc, ones, g, tot, xl(c0 + i), sl(c0 + i), zl(c0 + i));
+    compute(ca, c0 + i);
     if (i + 2 < cpw) load_chunk<kT, kGS, kSP, kXL>(ca, L, c0 + i + 2);
     __builtin_amdgcn_sched_barrier(0);
-    if (i + 1 < cpw) compute_chunk<kT, kGS, kSP, kXL>(cb, nc, ones, g, tot, xl(c0 + i + 1), sl(c0 + i + 1),
-                                                         zl(c0 + i + 1));
-    if (i + 2 < cpw) compute_chunk<kT, kGS, kSP, kXL>(ca, nc, ones, g, tot, xl(c0 + i + 2), sl(c0 + i + 2),
-                                                         zl(c0 + i + 2));
+    if (i + 1 < cpw) compute(cb, c0 + i + 1);
+    if (i + 2 < cpw) compute(ca, c0 + i + 2);
   }
 
   // Add the wavefronts' sums in wavefront order. Lane (j, h) holds token
   // 16t + 4h + i of output 32sp + 8c + 2g + f of the unit in tot[t][sp][f][i].
+  if constexpr (kPS) {
+    // one buffer: wavefront 0 stores, then each next one adds its sums
+    for (int w = 0; w < kW; ++w) {
+      if (wave == w) {
 #pragma unroll
-  for (int t = 0; t < kT; ++t)
+        for (int t = 0; t < kT; ++t)
 #pragma unroll
-    for (int sp = 0; sp < kSP; ++sp)
+          for (int sp = 0; sp < kSP; ++sp)
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
+            for (int f = 0; f < 2; ++f)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          s_red[((wave * 16 * kT) + 16 * t + 4 * h + i) * kUOut + kBOut * sp + 8 * c + 2 * g + f] = tot[t][sp][f][i];
-  __syncthreads();
+              for (int i = 0; i < 4; ++i) {
+                float& r = s_red[(16 * t + 4 * h + i) * kUOut + kBOut * sp + 8 * c + 2 * g + f];
+                r = w == 0 ? tot[t][sp][f][i] : r + tot[t][sp][f][i];
+              }
+      }
+      __syncthreads();
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < kT; ++t)
+#pragma unroll
+      for (int sp = 0; sp < kSP; ++sp)
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            s_red[((wave * 16 * kT) + 16 * t + 4 * h + i) * kUOut + kBOut * sp + 8 * c + 2 * g + f] =
+                tot[t][sp][f][i];
+    __syncthreads();
+  }
   const int rows = min(M, 16 * kT);
   for (int idx = threadIdx.x; idx < rows * kUOut; idx += kW * 64) {
     const int m = idx / kUOut, n = idx % kUOut;
     float v = s_red[m * kUOut + n];
+    if constexpr (!kPS) {
 #pragma unroll
-    for (int w = 1; w < kW; ++w) v += s_red[(w * 16 * kT + m) * kUOut + n];
+      for (int w = 1; w < kW; ++w) v += s_red[(w * 16 * kT + m) * kUOut + n];
+    }
     const size_t o = static_cast<size_t>(strip) * kBOut + n;
     if (splits == 1) {
       y[static_cast<size_t>(m) * N + o] = __builtin_bit_cast(uint16_t, static_cast<f16>(v));
@@ -470,10 +566,28 @@ hipError_t launch_blocked_main(const uint16_t* x, const u32x4* qb, const uint16_
                                                 stream);
 }
 
+template <int kT, int kGS>
+hipError_t launch_blocked_scaled(const uint16_t* x, const u32x4* qb, const uint16_t* scales, const uint32_t* qz,
+                                 uint16_t* y, float* part, int m, int n, int k, const GemvPlan& plan, int units,
+                                 XcdMap map, dim3 grid, hipStream_t stream) {
+  if constexpr (kGS >= 64) {
+    if (plan.strips_per_unit == 3)
+      return launch_blocked_xl<kT, kGS, 3, false>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, 0,
+                                                  stream);
+    if (plan.strips_per_unit == 2)
+      return launch_blocked_xl<kT, kGS, 2, false>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, 0,
+                                                  stream);
+  }
+  return launch_blocked_xl<kT, kGS, 1, false>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, 0,
+                                              stream);
+}
+
 template <int kGS>
 hipError_t launch_blocked_group(const uint16_t* x, const u32x4* qb, const uint16_t* scales, const uint32_t* qz,
                                 uint16_t* y, float* part, int m, int n, int k, const GemvPlan& plan, int units,
                                 XcdMap map, dim3 grid, hipStream_t stream) {
+  if (m > 48) return launch_blocked_scaled<4, kGS>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+  if (m > 32) return launch_blocked_scaled<3, kGS>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
   if constexpr (kGS == 32) {
     // groups of 32: one strip per workgroup (the multi-strip forms do not
     // fit the register file with four groups per chunk)
@@ -499,19 +613,35 @@ hipError_t launch_blocked_group(const uint16_t* x, const u32x4* qb, const uint16
 
 }  // namespace
 
-constexpr int kBlockedMaxTokens = 32;  // tokens per pass over the weights (two 16-token tiles)
 constexpr int64_t kBlockedMinWgs = 512;  // two workgroups per CU before K is split
+constexpr int kCUs = 256;
 
 GemvPlan plan_w4a16_gemv_blocked(int64_t M, int64_t N, int64_t K, int64_t group) {
   GemvPlan plan{1, 1, 0, false, static_cast<int>(group)};
   const int64_t strips = N / kBOut;
   const int64_t chunks = K / kBChunkRows;
-  const int64_t mt = std::min(M, int64_t{kBlockedMaxTokens});
+  const int64_t mt = std::min(M, kGemvMaxM);
   // Every workgroup loads all of x for its K range, so with more than a few
   // tokens a workgroup takes several adjacent strips that share those loads
   // (three for one 16-token tile, two for two; what divides the strips).
+  // With three or four tiles a workgroup needs every register (one per
+  // CU), and the x fragments, read once per strip group, cost more than
+  // the weights: the unit takes the most strips (3, then 2) for which
+  // splitting K still reaches one workgroup per CU with at least two
+  // chunks per split (measured at 64 tokens, 8B layers: qkv 22.7 -> 18.3,
+  // o_proj 15.1 -> 13.5, down 30.7 -> 23.7 us against one strip per unit).
   int sp = 1;
-  if (mt > 4 && group >= 64) {
+  if (mt > 32) {
+    for (int cand = (group >= 64 ? 3 : 1); cand > 1; --cand) {
+      if (strips % cand) continue;
+      bool fits = false;
+      for (int64_t s = 1; s <= chunks / 2 && !fits; ++s) fits = chunks % s == 0 && (strips / cand) * s >= kCUs;
+      if (fits || strips / cand >= kCUs) {
+        sp = cand;
+        break;
+      }
+    }
+  } else if (mt > 4 && group >= 64) {
     if (mt <= 16 && strips % 3 == 0) {
       sp = 3;
     } else if (strips % 2 == 0) {
@@ -521,10 +651,10 @@ GemvPlan plan_w4a16_gemv_blocked(int64_t M, int64_t N, int64_t K, int64_t group)
   plan.strips_per_unit = sp;
   const int64_t units = strips / sp;
   // Split K only when there are too few units for two single-strip
-  // workgroups (one multi-strip workgroup) per CU: the smallest divisor of
-  // the chunk count that gets there (else the largest); four wavefronts per
-  // workgroup when the split's chunks allow.
-  const int64_t min_wgs = sp == 1 ? kBlockedMinWgs : kBlockedMinWgs / 2;
+  // workgroups (one multi-strip or many-token workgroup) per CU: the
+  // smallest divisor of the chunk count that gets there (else the largest);
+  // four wavefronts per workgroup when the split's chunks allow.
+  const int64_t min_wgs = sp == 1 && mt <= 32 ? kBlockedMinWgs : kBlockedMinWgs / 2;
   for (int64_t s = 1; s <= chunks; ++s) {
     if (chunks % s) continue;
     plan.splits = static_cast<int>(s);
@@ -537,12 +667,7 @@ GemvPlan plan_w4a16_gemv_blocked(int64_t M, int64_t N, int64_t K, int64_t group)
 }
 
 size_t w4a16_gemv_blocked_workspace(int64_t M, int64_t N, int64_t K, int64_t group) {
-  // the largest need over the 32-token passes
-  size_t ws = 0;
-  for (int64_t m0 = 0; m0 < M; m0 += kBlockedMaxTokens)
-    ws = std::max(ws, plan_w4a16_gemv_blocked(std::min(M - m0, int64_t{kBlockedMaxTokens}), N, K, group)
-                          .workspace_bytes);
-  return ws;
+  return plan_w4a16_gemv_blocked(M, N, K, group).workspace_bytes;
 }
 
 hipError_t launch_w4a16_block_weights(const int32_t* qweight, int32_t* blocked, int64_t N, int64_t K,
@@ -561,17 +686,6 @@ hipError_t launch_w4a16_gemv_blocked(const uint16_t* x, const int32_t* blocked, 
   if (N % kBOut || K % kBChunkRows || M < 1 || M > kGemvMaxM || plan.waves < 1) return hipErrorInvalidValue;
   if (plan.group != 32 && plan.group != 64 && plan.group != 128) return hipErrorInvalidValue;
   if ((K / kBChunkRows) % (static_cast<int64_t>(plan.splits) * plan.waves)) return hipErrorInvalidValue;
-  if (M > kBlockedMaxTokens) {
-    // Up to 32 tokens per pass over the weights; later passes re-read them.
-    for (int64_t m0 = 0; m0 < M; m0 += kBlockedMaxTokens) {
-      const int64_t ms = std::min(M - m0, int64_t{kBlockedMaxTokens});
-      const hipError_t e = launch_w4a16_gemv_blocked(x + m0 * K, blocked, scales, qzeros, y + m0 * N, ms, N, K,
-                                                     plan_w4a16_gemv_blocked(ms, N, K, plan.group), workspace,
-                                                     stream);
-      if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
-  }
   const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
   const int units = static_cast<int>(N / kBOut / plan.strips_per_unit);
   XcdMap map;
