@@ -329,6 +329,38 @@ mq_status mq_w4a16_gemv_blocked(const uint16_t* x, const int32_t* qweight_blocke
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * bf16 forms of the three W4A16 entries, for models whose activations are
+ * bf16. Source: pymllm Setup and Usage, Overview (BF16 is one of the
+ * runtime's schemes beside W4A16 and W8A8_INT8, and the W4A16 layer is
+ * chosen from a model's quantization config, so 4-bit layers sit among bf16
+ * activations). x and y are bf16 (raw bits); qweight, scales (fp16),
+ * qzeros, layouts, workspace sizes, requirements, errors and the kernels
+ * chosen are as in the fp16 entry. The definition is the same,
+ * y = sum_k x * (q - z) * s with x widened exactly to binary32, y rounded
+ * to nearest even as bf16; the arithmetic:
+ *   mq_w4a16_gemm_bf16: each weight (q - z) * s is formed exactly in
+ *     binary32 and rounded once to bf16 for the bf16 MFMA; fp32 sums.
+ *   mq_w4a16_gemv_bf16, mq_w4a16_gemv_blocked_bf16: fragments hold 128 + q
+ *     exactly in bf16 and per group the kernel adds, in binary32,
+ *     s * (sum(x * (128 + q)) - (128 + z) * sum(x)); on the decode layout
+ *     33-64 tokens round each weight once to bf16 as the GEMM does.
+ * Error bound, element by element, against the exact sum y64 (derived from
+ * that arithmetic: bf16 unit roundoff 2^-8, binary32 2^-24): weight-rounding
+ * forms |y - y64| <= 2^-8 |y64| + (2^-8 + K 2^-24) sum_k |x w| (1 + 2^-7);
+ * the 128 + q forms |y - y64| <= 2^-8 |y64| + 2^-15 * 143 sum_k |x s|.
+ * Scales must keep |(q - z) * s| within the bf16 normal range.
+ */
+mq_status mq_w4a16_gemm_bf16(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
+                             const int32_t* qzeros, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t group,
+                             void* workspace, size_t workspace_bytes, void* stream);
+mq_status mq_w4a16_gemv_bf16(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
+                             const int32_t* qzeros, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t group,
+                             void* workspace, size_t workspace_bytes, void* stream);
+mq_status mq_w4a16_gemv_blocked_bf16(const uint16_t* x, const int32_t* qweight_blocked, const uint16_t* scales,
+                                     const int32_t* qzeros, uint16_t* y, int64_t M, int64_t N, int64_t K,
+                                     int64_t group, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Online KV-cache quantization, per head and per token.
  * Source: LMDeploy toolkit overview, section 2.4 "KV Cache online
  * quantization" (fp16 KV cache quantized per head per token, asymmetric,

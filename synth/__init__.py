@@ -76,6 +76,30 @@ def w4a16_inputs(M, K, N, group=128, outlier_frac=0.0, tag=0, seed=0, scale_log2
     }
 
 
+def w4a16_inputs_bf16(M, K, N, group=128, outlier_frac=0.0, tag=0, seed=0, scale_log2=None):
+    """As ``w4a16_inputs`` with bf16 activations (the same draws rounded to
+    bf16 instead of fp16): dict(x_bits uint16 [M,K], x float32 [M,K] (the
+    same values), qweight, scales, qzeros)."""
+    if N % 8:
+        raise ValueError("N must be a multiple of 8")
+    G = K if group == -1 else group
+    if K % G:
+        raise ValueError("K must be a multiple of the group size")
+    r_x, r_idx, r_q, r_s, r_z = _children(tag, seed, 5)
+    x = r_x.standard_normal((M, K), dtype=np.float32)
+    n_out = int(round(outlier_frac * K))
+    if n_out:
+        idx = r_idx.choice(K, size=n_out, replace=False)
+        x[:, idx] *= np.float32(OUTLIER_GAIN)
+    bits = bf16_bits(x)
+    return {
+        "x_bits": bits, "x": bf16_values(bits),
+        "qweight": random_words(r_q, (K, N // 8)),
+        "scales": group_scales(r_s, (K // G, N), scale_log2),
+        "qzeros": random_words(r_z, (K // G, N // 8)),
+    }
+
+
 def w4a16_weights(K, N, group=128, tag=0, seed=0, scale_log2=None):
     """Weights only (qweight, scales, qzeros), drawn as in ``w4a16_inputs``."""
     G = K if group == -1 else group

@@ -41,7 +41,8 @@ def test_header_declares_the_boundary():
               "mq_w8a8_linear_workspace_bytes", "mq_w4a16_gemm_workspace_bytes", "mq_kv_quant", "mq_abi_version",
               "mq_status_string", "mq_last_error", "mq_int4_reorder", "mq_int4_transpose", "mq_u16_transpose",
               "mq_quant_per_token_int8_bf16", "mq_w8a8_scaled_mm_bf16", "mq_w8a8_linear_bf16",
-              "mq_kv_quant_bf16", "mq_w8a8_linear_noalloc"]:
+              "mq_kv_quant_bf16", "mq_w8a8_linear_noalloc", "mq_w4a16_gemm_bf16", "mq_w4a16_gemv_bf16",
+              "mq_w4a16_gemv_blocked_bf16"]:
         assert n in names
 
 
@@ -249,8 +250,8 @@ def test_w4a16_blocked_validation(lib):
     # a split divides the chunk count (K/128) and the workspace holds its partials
     for M, N, K in [(1, 6144, 4096), (16, 4096, 12288), (32, 3072, 1024), (64, 96, 640)]:
         b = ws(M, N, K, 128)
-        splits = b // (4 * min(M, 32) * N) or 1
-        assert b % (4 * min(M, 32) * N) == 0 and (K // 128) % splits == 0
+        splits = b // (4 * min(M, 64) * N) or 1
+        assert b % (4 * min(M, 64) * N) == 0 and (K // 128) % splits == 0
 
 
 @pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="lets a launch through; only meaningful without a GPU")

@@ -11,12 +11,12 @@ Entry points (same names as the C ABI, without the ``mq_`` prefix):
     quant_per_token_int8(x)                          -> (xq, s_tok); x fp16 or bf16
     w8a8_scaled_mm(xq, s_tok, wq, s_ch)              -> y  (fp16, or bf16 with out_dtype)
     w8a8_mm_i32(xq, wq)                              -> acc (int32)
-    w4a16_gemm(x, qweight, scales, qzeros, group)    -> y  (fp16); K split on small grids
+    w4a16_gemm(x, qweight, scales, qzeros, group)    -> y  (x's dtype: fp16 or bf16); K split on small grids
     w4a16_gemm_workspace_bytes(M, N, K, group)       -> int
-    w4a16_gemv(x, qweight, scales, qzeros, group)    -> y  (fp16), M <= 64
+    w4a16_gemv(x, qweight, scales, qzeros, group)    -> y  (x's dtype), M <= 64
     w4a16_gemv_workspace_bytes(M, N, K, group)       -> int
     w4a16_block_weights(qweight)                     -> qweight_blocked (decode layout, once per matrix)
-    w4a16_gemv_blocked(x, qweight_blocked, scales, qzeros, group) -> y (fp16), M <= 64
+    w4a16_gemv_blocked(x, qweight_blocked, scales, qzeros, group) -> y (x's dtype), M <= 64
     w4a16_gemv_blocked_workspace_bytes(M, N, K, group) -> int
 
     kv_quant(x, bits)                                -> (codes, params) per (token, head) row
@@ -99,6 +99,10 @@ _PROTOTYPES = {
     "mq_w4a16_gemv_blocked_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I64]),
     "mq_w4a16_gemv_blocked": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t,
                                              _P]),
+    "mq_w4a16_gemm_bf16": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
+    "mq_w4a16_gemv_bf16": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
+    "mq_w4a16_gemv_blocked_bf16": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P,
+                                                  ctypes.c_size_t, _P]),
 }
 
 
@@ -230,7 +234,7 @@ def w8a8_mm_i32(xq, wq, out=None, stream=None):
 
 def _w4a16_shapes(x, qweight, scales, qzeros, group):
     torch = _torch()
-    _dev_tensor(x, "x", torch.float16, 2)
+    _dev_tensor(x, "x", _half_dtype(x, "x"), 2)
     _dev_tensor(qweight, "qweight", torch.int32, 2)
     _dev_tensor(scales, "scales", torch.float16, 2)
     _dev_tensor(qzeros, "qzeros", torch.int32, 2)
@@ -252,14 +256,15 @@ def w4a16_gemm_workspace_bytes(M, N, K, group=128):
 
 
 def w4a16_gemm(x, qweight, scales, qzeros, group=128, out=None, workspace=None, stream=None):
-    """W4A16 GEMM: y[M, N] fp16 = x[M, K] . dequant(qweight, scales, qzeros).
+    """W4A16 GEMM: y[M, N] = x[M, K] . dequant(qweight, scales, qzeros), x and y
+    fp16 or bf16 (the weight rounded once to x's dtype).
 
     ``workspace``: a uint8 GPU tensor of at least ``w4a16_gemm_workspace_bytes``
     bytes (allocated if None and the shape splits K); ``False`` never splits.
     """
     torch = _torch()
     M, N, K = _w4a16_shapes(x, qweight, scales, qzeros, group)
-    y = _out(out, (M, N), torch.float16, x, "out")
+    y = _out(out, (M, N), x.dtype, x, "out")
     if workspace is False:
         workspace = None
     elif workspace is None:
@@ -268,9 +273,10 @@ def w4a16_gemm(x, qweight, scales, qzeros, group=128, out=None, workspace=None, 
             workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    fn = library().mq_w4a16_gemm_bf16 if x.dtype == torch.bfloat16 else library().mq_w4a16_gemm
     with torch.cuda.device(x.device):
-        _check(library().mq_w4a16_gemm(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), qzeros.data_ptr(),
-                                       y.data_ptr(), M, N, K, group, ws_ptr, ws_bytes, _stream_of(x, stream)))
+        _check(fn(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), qzeros.data_ptr(),
+                  y.data_ptr(), M, N, K, group, ws_ptr, ws_bytes, _stream_of(x, stream)))
     return y
 
 
@@ -280,7 +286,7 @@ def w4a16_gemv_workspace_bytes(M, N, K, group=128):
 
 
 def w4a16_gemv(x, qweight, scales, qzeros, group=128, out=None, workspace=None, stream=None):
-    """W4A16 GEMV for decode (M <= 64).
+    """W4A16 GEMV for decode (M <= 64); x and y fp16 or bf16.
 
     ``workspace``: a uint8 GPU tensor of at least ``w4a16_gemv_workspace_bytes``
     bytes (allocated if None); its contents do not matter. Calls sharing a
@@ -288,15 +294,16 @@ def w4a16_gemv(x, qweight, scales, qzeros, group=128, out=None, workspace=None, 
     """
     torch = _torch()
     M, N, K = _w4a16_shapes(x, qweight, scales, qzeros, group)
-    y = _out(out, (M, N), torch.float16, x, "out")
+    y = _out(out, (M, N), x.dtype, x, "out")
     need = w4a16_gemv_workspace_bytes(M, N, K, group)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    fn = library().mq_w4a16_gemv_bf16 if x.dtype == torch.bfloat16 else library().mq_w4a16_gemv
     with torch.cuda.device(x.device):
-        _check(library().mq_w4a16_gemv(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), qzeros.data_ptr(),
-                                       y.data_ptr(), M, N, K, group, ws_ptr, ws_bytes, _stream_of(x, stream)))
+        _check(fn(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), qzeros.data_ptr(),
+                  y.data_ptr(), M, N, K, group, ws_ptr, ws_bytes, _stream_of(x, stream)))
     return y
 
 
@@ -328,9 +335,9 @@ def w4a16_gemv_blocked_workspace_bytes(M, N, K, group=128):
 
 
 def w4a16_gemv_blocked(x, qweight_blocked, scales, qzeros, group=128, out=None, workspace=None, stream=None):
-    """W4A16 GEMV for decode (M <= 64) on weights from ``w4a16_block_weights``."""
+    """W4A16 GEMV for decode (M <= 64) on weights from ``w4a16_block_weights``; x and y fp16 or bf16."""
     torch = _torch()
-    _dev_tensor(x, "x", torch.float16, 2)
+    _dev_tensor(x, "x", _half_dtype(x, "x"), 2)
     _dev_tensor(qweight_blocked, "qweight_blocked", torch.int32, 2)
     _dev_tensor(scales, "scales", torch.float16, 2)
     _dev_tensor(qzeros, "qzeros", torch.int32, 2)
@@ -342,16 +349,16 @@ def w4a16_gemv_blocked(x, qweight_blocked, scales, qzeros, group=128, out=None, 
         raise ValueError("qweight_blocked must be [K/64, 8*N] (from w4a16_block_weights)")
     if tuple(scales.shape) != (K // group, N) or tuple(qzeros.shape) != (K // group, N // 8):
         raise ValueError("scales must be [K/G, N] and qzeros [K/G, N/8]")
-    y = _out(out, (M, N), torch.float16, x, "out")
+    y = _out(out, (M, N), x.dtype, x, "out")
     need = w4a16_gemv_blocked_workspace_bytes(M, N, K, group)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    fn = library().mq_w4a16_gemv_blocked_bf16 if x.dtype == torch.bfloat16 else library().mq_w4a16_gemv_blocked
     with torch.cuda.device(x.device):
-        _check(library().mq_w4a16_gemv_blocked(x.data_ptr(), qweight_blocked.data_ptr(), scales.data_ptr(),
-                                               qzeros.data_ptr(), y.data_ptr(), M, N, K, group, ws_ptr, ws_bytes,
-                                               _stream_of(x, stream)))
+        _check(fn(x.data_ptr(), qweight_blocked.data_ptr(), scales.data_ptr(), qzeros.data_ptr(), y.data_ptr(), M, N,
+                  K, group, ws_ptr, ws_bytes, _stream_of(x, stream)))
     return y
 
 

@@ -15,6 +15,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // LDS (address space 3) views for the direct global -> LDS loads.
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
@@ -38,6 +41,33 @@ __device__ __forceinline__ uint16_t half_bits(float v) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
   } else {
     return __builtin_bit_cast(uint16_t, static_cast<f16>(v));
+  }
+}
+
+// Two binary32 values rounded to nearest even as a bf16 pair (lo in bits
+// 0-15), one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+// 16-bit MFMAs on operands carried as f16x8 bit patterns: fp16, or bf16
+// when kBf16 (the same bits reinterpreted).
+template <bool kBf16>
+__device__ __forceinline__ f32x4 mfma_16x16x32(f16x8 a, f16x8 b, f32x4 c) {
+  if constexpr (kBf16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+}
+template <bool kBf16>
+__device__ __forceinline__ f32x16 mfma_32x32x16(f16x8 a, f16x8 b, f32x16 c) {
+  if constexpr (kBf16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
 }
 

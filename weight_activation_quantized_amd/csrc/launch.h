@@ -72,9 +72,11 @@ constexpr int64_t kU16TransposeMaxB = int64_t{1} << 30;
 // kernel); a NULL workspace never splits.
 int w4a16_gemm_splits(int64_t M, int64_t N, int64_t K);
 size_t w4a16_gemm_workspace(int64_t M, int64_t N, int64_t K);
+// bf16: x and y are bf16 (the weight is rounded once to bf16 instead of fp16).
 hipError_t launch_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                              const int32_t* qzeros, uint16_t* y,
-                             int64_t M, int64_t N, int64_t K, int64_t group, void* workspace, hipStream_t stream);
+                             int64_t M, int64_t N, int64_t K, int64_t group, void* workspace, bool bf16,
+                             hipStream_t stream);
 
 // Largest token count the W4A16 GEMV takes (four 16-token MFMA tiles).
 constexpr int64_t kGemvMaxM = 64;
@@ -99,11 +101,11 @@ GemvPlan plan_w4a16_gemv_blocked(int64_t M, int64_t N, int64_t K, int64_t group)
 size_t w4a16_gemv_blocked_workspace(int64_t M, int64_t N, int64_t K, int64_t group);
 hipError_t launch_w4a16_gemv_blocked(const uint16_t* x, const int32_t* blocked, const uint16_t* scales,
                                      const int32_t* qzeros, uint16_t* y, int64_t M, int64_t N, int64_t K,
-                                     const GemvPlan& plan, void* workspace, hipStream_t stream);
+                                     const GemvPlan& plan, void* workspace, bool bf16, hipStream_t stream);
 
 hipError_t launch_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                              const int32_t* qzeros, uint16_t* y,
                              int64_t M, int64_t N, int64_t K, const GemvPlan& plan,
-                             void* workspace, hipStream_t stream);
+                             void* workspace, bool bf16, hipStream_t stream);
 
 }  // namespace mq

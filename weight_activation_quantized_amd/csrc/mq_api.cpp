@@ -234,10 +234,9 @@ size_t mq_w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t gr
   return mq::w4a16_gemm_workspace(M, N, K);
 }
 
-mq_status mq_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
-                        const int32_t* qzeros, uint16_t* y,
-                        int64_t M, int64_t N, int64_t K, int64_t group,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+static mq_status w4a16_gemm_impl(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
+                                   const int32_t* qzeros, uint16_t* y, int64_t M, int64_t N, int64_t K,
+                                   int64_t group, void* workspace, size_t workspace_bytes, bool bf16, void* stream) {
   mq_status s = check_w4a16(x, qweight, scales, qzeros, y, M, N, K, group);
   if (s != MQ_OK) return s;
   if (M == 0) return ok();
@@ -261,7 +260,7 @@ mq_status mq_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_
       ws = workspace;
     }
   }
-  return hip_status(mq::launch_w4a16_gemm(x, qweight, scales, qzeros, y, M, N, K, group, ws, as_stream(stream)),
+  return hip_status(mq::launch_w4a16_gemm(x, qweight, scales, qzeros, y, M, N, K, group, ws, bf16, as_stream(stream)),
                     "w4a16_gemm launch");
 }
 
@@ -272,10 +271,9 @@ size_t mq_w4a16_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t gr
   return mq::plan_w4a16_gemv(M, N, K, group).workspace_bytes;
 }
 
-mq_status mq_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
-                        const int32_t* qzeros, uint16_t* y,
-                        int64_t M, int64_t N, int64_t K, int64_t group,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+static mq_status w4a16_gemv_impl(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
+                                   const int32_t* qzeros, uint16_t* y, int64_t M, int64_t N, int64_t K,
+                                   int64_t group, void* workspace, size_t workspace_bytes, bool bf16, void* stream) {
   mq_status s = check_w4a16(x, qweight, scales, qzeros, y, M, N, K, group);
   if (s != MQ_OK) return s;
   if (M > mq::kGemvMaxM)
@@ -298,7 +296,7 @@ mq_status mq_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const uint16_
     if (s != MQ_OK) return s;
   }
   return hip_status(mq::launch_w4a16_gemv(x, qweight, scales, qzeros, y, M, N, K, plan,
-                                          plan.workspace_bytes ? workspace : nullptr, as_stream(stream)),
+                                          plan.workspace_bytes ? workspace : nullptr, bf16, as_stream(stream)),
                     "w4a16_gemv launch");
 }
 
@@ -504,10 +502,10 @@ size_t mq_w4a16_gemv_blocked_workspace_bytes(int64_t M, int64_t N, int64_t K, in
   return mq::w4a16_gemv_blocked_workspace(M, N, K, group);
 }
 
-mq_status mq_w4a16_gemv_blocked(const uint16_t* x, const int32_t* qweight_blocked, const uint16_t* scales,
-                                const int32_t* qzeros, uint16_t* y,
-                                int64_t M, int64_t N, int64_t K, int64_t group,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+static mq_status w4a16_gemv_blocked_impl(const uint16_t* x, const int32_t* qweight_blocked,
+                                         const uint16_t* scales, const int32_t* qzeros, uint16_t* y, int64_t M,
+                                         int64_t N, int64_t K, int64_t group, void* workspace,
+                                         size_t workspace_bytes, bool bf16, void* stream) {
   mq_status s = check_w4a16(x, qweight_blocked, scales, qzeros, y, M, N, K, group);
   if (s != MQ_OK) return s;
   if (N % 32) return fail(MQ_ERR_SHAPE, "the blocked layout needs N %% 32 == 0 (got N=%lld)", (long long)N);
@@ -533,8 +531,22 @@ mq_status mq_w4a16_gemv_blocked(const uint16_t* x, const int32_t* qweight_blocke
   }
   const mq::GemvPlan plan = mq::plan_w4a16_gemv_blocked(M, N, K, group);
   return hip_status(mq::launch_w4a16_gemv_blocked(x, qweight_blocked, scales, qzeros, y, M, N, K, plan,
-                                                  need_ws ? workspace : nullptr, as_stream(stream)),
+                                                  need_ws ? workspace : nullptr, bf16, as_stream(stream)),
                     "w4a16_gemv_blocked launch");
 }
+
+#define MQ_W4A16_ENTRY(NAME, IMPL, BF, WNAME)                                                                  \
+  mq_status NAME(const uint16_t* x, const int32_t* WNAME, const uint16_t* scales, const int32_t* qzeros,       \
+                 uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t group, void* workspace,                  \
+                 size_t workspace_bytes, void* stream) {                                                        \
+    return IMPL(x, WNAME, scales, qzeros, y, M, N, K, group, workspace, workspace_bytes, BF, stream);         \
+  }
+MQ_W4A16_ENTRY(mq_w4a16_gemm, w4a16_gemm_impl, false, qweight)
+MQ_W4A16_ENTRY(mq_w4a16_gemm_bf16, w4a16_gemm_impl, true, qweight)
+MQ_W4A16_ENTRY(mq_w4a16_gemv, w4a16_gemv_impl, false, qweight)
+MQ_W4A16_ENTRY(mq_w4a16_gemv_bf16, w4a16_gemv_impl, true, qweight)
+MQ_W4A16_ENTRY(mq_w4a16_gemv_blocked, w4a16_gemv_blocked_impl, false, qweight_blocked)
+MQ_W4A16_ENTRY(mq_w4a16_gemv_blocked_bf16, w4a16_gemv_blocked_impl, true, qweight_blocked)
+#undef MQ_W4A16_ENTRY
 
 }  // extern "C"

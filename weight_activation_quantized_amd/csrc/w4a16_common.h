@@ -31,8 +31,12 @@ namespace mq {
 // it reads 64 + q (the mantissa step at 64 is 1/16), for kernels that
 // scale the fragments in fp16 and so need the high field without the
 // factor 16.
+// bmagic is the bf16 pattern of 128.0 (0x4300): a field in bits 0-3 OR-ed
+// into it reads 128 + q exactly (bf16 keeps 8 significant bits), the bf16
+// counterpart of 1024 + q. A bf16 exponent starts at bit 7, so a field in
+// bits 4-7 is first shifted down.
 struct NibConst {
-  uint32_t lo, hi, magic, magic64;
+  uint32_t lo, hi, magic, magic64, bmagic;
 };
 __device__ __forceinline__ NibConst nib_const() {
   NibConst c;
@@ -40,7 +44,16 @@ __device__ __forceinline__ NibConst nib_const() {
   asm("v_mov_b32 %0, 0x00f000f0" : "=v"(c.hi));
   asm("v_mov_b32 %0, 0x64006400" : "=v"(c.magic));
   asm("v_mov_b32 %0, 0x54005400" : "=v"(c.magic64));
+  asm("v_mov_b32 %0, 0x43004300" : "=v"(c.bmagic));
   return c;
+}
+
+// A fragment of eight 1.0 values (fp16 0x3C00 or bf16 0x3F80), for the MFMA
+// that sums x over a group.
+template <bool kBf16>
+__device__ __forceinline__ f16x8 ones_fragment() {
+  const uint32_t one2 = kBf16 ? 0x3F803F80u : 0x3C003C00u;
+  return __builtin_bit_cast(f16x8, u32x4{one2, one2, one2, one2});
 }
 
 // -(1024 + z_p) (even p) or -(1024 + 16 z_p) (odd p), replicated in both

@@ -97,18 +97,31 @@ struct GroupParams {
 // p / 2 of zw: OR-ed into the sign and exponent of -1024.0 (0xE400) or
 // -64.0 (0xD400) it reads as -(1024 + z) or -(64 + z), the same encodings
 // as the weight fields.
+// bf16 activations (kBF): the weight is formed in binary32 and rounded once
+// to bf16 instead; negz[q] then holds the binary32 bits of
+// -(1024 + z) * s (or -(64 + z) * s) and sc2[q] those of s, both exact
+// (an 11-bit integer times an 11-bit significand).
+template <bool kBF>
 __device__ __forceinline__ void make_group_params(uint32_t zw, u32x4 sv, int par, GroupParams& gp) {
   const uint32_t zmask = par ? 0xF0u : 0x0Fu;
   const uint32_t zbase = par ? 0xD400u : 0xE400u;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint32_t e = ((zw >> (8 * q)) & zmask) | zbase;
-    gp.negz[q] = e | (e << 16);
     const f16x2 s2 = as_f16x2(sv[q]);
-    f16x2 rep;
-    rep[0] = s2[par];
-    rep[1] = s2[par];
-    gp.sc2[q] = as_u32(rep);
+    if constexpr (kBF) {
+      const float sf = static_cast<float>(s2[par]);
+      const uint32_t zf = (zw >> (8 * q + 4 * par)) & 15u;
+      const float off = par ? 64.0f : 1024.0f;
+      gp.negz[q] = __builtin_bit_cast(uint32_t, -(off + static_cast<float>(zf)) * sf);
+      gp.sc2[q] = __builtin_bit_cast(uint32_t, sf);
+    } else {
+      const uint32_t e = ((zw >> (8 * q)) & zmask) | zbase;
+      gp.negz[q] = e | (e << 16);
+      f16x2 rep;
+      rep[0] = s2[par];
+      rep[1] = s2[par];
+      gp.sc2[q] = as_u32(rep);
+    }
   }
 }
 
@@ -117,6 +130,11 @@ __device__ __forceinline__ void make_group_params(uint32_t zw, u32x4 sv, int par
 // bytes 0-1 (2-3) of a row pair; field p sits in byte p / 2 of a word, low
 // nibble for even p, high nibble for odd p, selected by the lane's mask;
 // the lane's magic (1024.0 or 64.0) makes either read as an offset q.
+// kBF: the offset integer (an exact fp16) times s plus -(offset + z) * s in
+// one binary32 fused multiply-add (v_fma_mix_f32 reads the fp16 half
+// directly) is exactly (q - z) * s, rounded once to bf16 by the pair
+// conversion.
+template <bool kBF>
 __device__ __forceinline__ void unpack_fields(const uint32_t (&w)[8], const GroupParams& gp, uint32_t mask,
                                               uint32_t magic, f16x8 (&b)[4]) {
 #pragma unroll
@@ -127,7 +145,15 @@ __device__ __forceinline__ void unpack_fields(const uint32_t (&w)[8], const Grou
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint32_t v = (src[q] & mask) | magic;
-      const f16x2 d = (as_f16x2(v) + as_f16x2(gp.negz[q])) * as_f16x2(gp.sc2[q]);
+      f16x2 d;
+      if constexpr (kBF) {
+        const f16x2 o = as_f16x2(v);
+        const float sf = __builtin_bit_cast(float, gp.sc2[q]);
+        const float cf = __builtin_bit_cast(float, gp.negz[q]);
+        d = as_f16x2(bf16x2_bits(fmaf(static_cast<float>(o[0]), sf, cf), fmaf(static_cast<float>(o[1]), sf, cf)));
+      } else {
+        d = (as_f16x2(v) + as_f16x2(gp.negz[q])) * as_f16x2(gp.sc2[q]);
+      }
       b[q][2 * t] = d[0];
       b[q][2 * t + 1] = d[1];
     }
@@ -138,7 +164,7 @@ __device__ __forceinline__ void unpack_fields(const uint32_t (&w)[8], const Grou
 // With splits > 1 the workgroup takes K range `split` of `splits` equal
 // ranges and writes fp32 partial sums to partial[split, M, N] (a second
 // kernel adds them in split order); with splits == 1 it writes y.
-template <int kSPG>
+template <int kSPG, bool kBF>
 __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __restrict__ x,
                                                          const uint32_t* __restrict__ qw,
                                                          const uint16_t* __restrict__ scales,
@@ -276,12 +302,12 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
     const lds_i8* const sl_ = sm + ((S) % kStages) * kSlotBytes;                                 \
     const u32x4 sv_ = *(const lds_u32x4*)(sl_ + area + kBBytes + 16 * col_in_area);              \
     const uint32_t zw_ = *(const lds_word*)(sl_ + area + kBBytes + kSBytes + 4 * col_in_area);   \
-    make_group_params(zw_, sv_, par, GP);                                                        \
+    make_group_params<kBF>(zw_, sv_, par, GP);                                                        \
   } while (0)
 #define MQ_MFMAS(AF, B)                                                                          \
   do {                                                                                           \
     _Pragma("unroll") for (int a = 0; a < 2; ++a) _Pragma("unroll") for (int q = 0; q < 4; ++q)  \
-        acc[a][q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(AF[a], B[q], acc[a][q], 0, 0, 0);     \
+        acc[a][q] = mfma_32x32x16<kBF>(AF[a], B[q], acc[a][q]);     \
   } while (0)
 // Keeps the unpacked fragments in the block that computes them (otherwise
 // they are sunk next to their use, out of reach of the MFMAs they are meant
@@ -336,7 +362,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
     MQ_READ_GP(0, gp);
     MQ_READ_A(0, 0, a0);
     MQ_READ_W(0, 0, w);
-    unpack_fields(w, gp, mask, magic, b0);
+    unpack_fields<kBF>(w, gp, mask, magic, b0);
   }
   for (int s0 = 0; s0 < nst; s0 += 4) {
 #pragma unroll
@@ -349,10 +375,10 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
         uint32_t w[8];
         MQ_READ_A(s, 1, a1);
         MQ_READ_W(s, 1, w);
-        unpack_fields(w, gp, mask, magic, b1);
+        unpack_fields<kBF>(w, gp, mask, magic, b1);
         MQ_MFMAS(a0, b0);
         MQ_PIN(b1);
-        MQ_INTERLEAVE(10, 8);
+        MQ_INTERLEAVE(10, kBF ? 10 : 8);
         __builtin_amdgcn_sched_barrier(0);
       }
       // Stage s + 1 must have landed (every filler's share), and every wave
@@ -374,13 +400,13 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
         if (new_group) MQ_READ_GP(s + 1, gp);
         MQ_READ_A(s + 1, 0, a0);
         MQ_READ_W(s + 1, 0, w);
-        unpack_fields(w, gp, mask, magic, b0);
+        unpack_fields<kBF>(w, gp, mask, magic, b0);
         MQ_MFMAS(a1, b1);
         MQ_PIN(b0);
         if (new_group) {
-          MQ_INTERLEAVE(12, 10);
+          MQ_INTERLEAVE(12, kBF ? 12 : 10);
         } else {
-          MQ_INTERLEAVE(10, 8);
+          MQ_INTERLEAVE(10, kBF ? 10 : 8);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -440,10 +466,8 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
         const int mt = 32 * a + 8 * (r / 4) + 4 * hh + (r % 4);
         lds_i8* const row = sm + mt * kOutPitch;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f16 v = static_cast<f16>(acc[a][q][r]);
-          *(__attribute__((address_space(3))) f16*)(row + 2 * (ncol + 2 * q)) = v;
-        }
+        for (int q = 0; q < 4; ++q)
+          *(__attribute__((address_space(3))) uint16_t*)(row + 2 * (ncol + 2 * q)) = half_bits<kBF>(acc[a][q][r]);
       }
   }
   wait_counts<0, 0>();
@@ -459,8 +483,9 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
 }
 
 
-// Adds the splits' fp32 partial sums in split order and rounds to fp16;
-// one thread per 4 outputs.
+// Adds the splits' fp32 partial sums in split order and rounds to fp16 (or
+// bf16); one thread per 4 outputs.
+template <bool kBF>
 __global__ __launch_bounds__(256) void w4a16_gemm_reduce(const float* __restrict__ partial,
                                                          uint16_t* __restrict__ y, int64_t mn4, int splits) {
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -469,12 +494,9 @@ __global__ __launch_bounds__(256) void w4a16_gemm_reduce(const float* __restrict
   const float* src = partial + static_cast<size_t>(t) * 4;
   f32x4 acc = *reinterpret_cast<const f32x4*>(src);
   for (int sp = 1; sp < splits; ++sp) acc += *reinterpret_cast<const f32x4*>(src + sp * stride);
-  f16x2 lo, hi;
-  lo[0] = static_cast<f16>(acc[0]);
-  lo[1] = static_cast<f16>(acc[1]);
-  hi[0] = static_cast<f16>(acc[2]);
-  hi[1] = static_cast<f16>(acc[3]);
-  *reinterpret_cast<u32x2*>(y + static_cast<size_t>(t) * 4) = u32x2{as_u32(lo), as_u32(hi)};
+  const uint32_t lo = half_bits<kBF>(acc[0]) | (static_cast<uint32_t>(half_bits<kBF>(acc[1])) << 16);
+  const uint32_t hi = half_bits<kBF>(acc[2]) | (static_cast<uint32_t>(half_bits<kBF>(acc[3])) << 16);
+  *reinterpret_cast<u32x2*>(y + static_cast<size_t>(t) * 4) = u32x2{lo, hi};
 }
 
 }  // namespace
@@ -500,9 +522,10 @@ size_t w4a16_gemm_workspace(int64_t M, int64_t N, int64_t K) {
   return s > 1 ? static_cast<size_t>(s) * M * N * sizeof(float) : 0;
 }
 
-hipError_t launch_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
-                             const int32_t* qzeros, uint16_t* y,
-                             int64_t M, int64_t N, int64_t K, int64_t group, void* workspace, hipStream_t stream) {
+template <bool kBF>
+hipError_t launch_w4a16_gemm_t(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
+                               const int32_t* qzeros, uint16_t* y,
+                               int64_t M, int64_t N, int64_t K, int64_t group, void* workspace, hipStream_t stream) {
   if (K % 128 || (group != 32 && group != 64 && group != 128)) return hipErrorInvalidValue;
   const int splits = workspace ? w4a16_gemm_splits(M, N, K) : 1;
   const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
@@ -517,22 +540,29 @@ hipError_t launch_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const ui
   hipError_t err;
   switch (group) {
     case 32:
-      err = launch_kernel(w4a16_gemm_kernel<1>, grid, dim3(kThreads), 0, stream, x, qw, scales, qz, y, part, m, n, k,
+      err = launch_kernel(w4a16_gemm_kernel<1, kBF>, grid, dim3(kThreads), 0, stream, x, qw, scales, qz, y, part, m, n, k,
                           tiles_m, tiles_n, per_xcd, splits);
       break;
     case 64:
-      err = launch_kernel(w4a16_gemm_kernel<2>, grid, dim3(kThreads), 0, stream, x, qw, scales, qz, y, part, m, n, k,
+      err = launch_kernel(w4a16_gemm_kernel<2, kBF>, grid, dim3(kThreads), 0, stream, x, qw, scales, qz, y, part, m, n, k,
                           tiles_m, tiles_n, per_xcd, splits);
       break;
     default:
-      err = launch_kernel(w4a16_gemm_kernel<4>, grid, dim3(kThreads), 0, stream, x, qw, scales, qz, y, part, m, n, k,
+      err = launch_kernel(w4a16_gemm_kernel<4, kBF>, grid, dim3(kThreads), 0, stream, x, qw, scales, qz, y, part, m, n, k,
                           tiles_m, tiles_n, per_xcd, splits);
       break;
   }
   if (err != hipSuccess || splits == 1) return err;
   const int64_t mn4 = M * N / 4;
-  return launch_kernel(w4a16_gemm_reduce, dim3(static_cast<uint32_t>((mn4 + 255) / 256)), dim3(256), 0, stream,
+  return launch_kernel(w4a16_gemm_reduce<kBF>, dim3(static_cast<uint32_t>((mn4 + 255) / 256)), dim3(256), 0, stream,
                        part, y, mn4, splits);
+}
+
+hipError_t launch_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
+                             const int32_t* qzeros, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t group,
+                             void* workspace, bool bf16, hipStream_t stream) {
+  return bf16 ? launch_w4a16_gemm_t<true>(x, qweight, scales, qzeros, y, M, N, K, group, workspace, stream)
+              : launch_w4a16_gemm_t<false>(x, qweight, scales, qzeros, y, M, N, K, group, workspace, stream);
 }
 
 }  // namespace mq

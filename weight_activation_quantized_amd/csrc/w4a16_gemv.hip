@@ -49,21 +49,19 @@ namespace {
 
 constexpr int kWaveCols = 16;        // packed columns per wavefront (128 outputs)
 
+template <bool kBF>
 __device__ __forceinline__ void store_f16x8(uint16_t* dst, const float (&v)[8]) {
   u32x4 out;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    f16x2 pr;
-    pr[0] = static_cast<f16>(v[2 * t]);
-    pr[1] = static_cast<f16>(v[2 * t + 1]);
-    out[t] = as_u32(pr);
-  }
+  for (int t = 0; t < 4; ++t)
+    out[t] = half_bits<kBF>(v[2 * t]) | (static_cast<uint32_t>(half_bits<kBF>(v[2 * t + 1])) << 16);
   *reinterpret_cast<u32x4*>(dst) = out;
 }
 
 // Lane (j, h) holds tokens m0+4h..m0+4h+3 of packed column c in tot[p][q]
 // (field p, token m0 + 4h + q): write them as fp16 to y, or as fp32 to the
 // split's partial-sum slice.
+template <bool kBF>
 __device__ __forceinline__ void write_out(const f32x4 (&tot)[8], uint16_t* __restrict__ y,
                                           float* __restrict__ partial, int M, int N, int c, int h, int split,
                                           int splits, int m0 = 0) {
@@ -75,7 +73,7 @@ __device__ __forceinline__ void write_out(const f32x4 (&tot)[8], uint16_t* __res
       float v[8];
 #pragma unroll
       for (int p = 0; p < 8; ++p) v[p] = tot[p][q];
-      store_f16x8(y + static_cast<size_t>(m) * N + 8 * c, v);
+      store_f16x8<kBF>(y + static_cast<size_t>(m) * N + 8 * c, v);
     } else {
       float* dst = partial + (static_cast<size_t>(split) * M + m) * N + 8 * c;
       *reinterpret_cast<f32x4*>(dst) = f32x4{tot[0][q], tot[1][q], tot[2][q], tot[3][q]};
@@ -112,15 +110,36 @@ constexpr int lds_loads_per_stage() { return 2 + T; }
 // (v & mask) | magic as one v_and_or_b32 of its own; the fragments feed MFMA
 // operands, and only for its own instructions does the compiler insert the
 // wait states a VALU write needs before an MFMA reads the register.
+// kBF: bf16 fragments of 128 + q for every field (the high fields shifted
+// down first; see NibConst).
+template <bool kBF>
 __device__ __forceinline__ void unpack_step_biased(const uint32_t (&w)[8], const NibConst& c, f16x8 (&b)[8]) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const uint32_t lo = byte_perm(w[2 * t + 1], w[2 * t], 0x05040100u);  // bytes 0,1 of both rows
     const uint32_t hi = byte_perm(w[2 * t + 1], w[2 * t], 0x07060302u);  // bytes 2,3 of both rows
     const uint32_t lo8 = lo >> 8, hi8 = hi >> 8;
-    const uint32_t v[8] = {(lo & c.lo) | c.magic,  (lo & c.hi) | c.magic,  (lo8 & c.lo) | c.magic,
-                           (lo8 & c.hi) | c.magic, (hi & c.lo) | c.magic,  (hi & c.hi) | c.magic,
-                           (hi8 & c.lo) | c.magic, (hi8 & c.hi) | c.magic};
+    uint32_t v[8];
+    if constexpr (kBF) {
+      const uint32_t m = c.bmagic;
+      v[0] = (lo & c.lo) | m;
+      v[1] = ((lo >> 4) & c.lo) | m;
+      v[2] = (lo8 & c.lo) | m;
+      v[3] = ((lo >> 12) & c.lo) | m;
+      v[4] = (hi & c.lo) | m;
+      v[5] = ((hi >> 4) & c.lo) | m;
+      v[6] = (hi8 & c.lo) | m;
+      v[7] = ((hi >> 12) & c.lo) | m;
+    } else {
+      v[0] = (lo & c.lo) | c.magic;
+      v[1] = (lo & c.hi) | c.magic;
+      v[2] = (lo8 & c.lo) | c.magic;
+      v[3] = (lo8 & c.hi) | c.magic;
+      v[4] = (hi & c.lo) | c.magic;
+      v[5] = (hi & c.hi) | c.magic;
+      v[6] = (hi8 & c.lo) | c.magic;
+      v[7] = (hi8 & c.hi) | c.magic;
+    }
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const f16x2 d = as_f16x2(v[p]);
@@ -165,7 +184,7 @@ __device__ __forceinline__ void lds_issue_stage(int st, int row_begin, int NP, i
 // kT = number of 16-token tiles (M <= 16 kT); every weight fragment, once
 // unpacked, feeds the MFMAs of all kT tiles. kGS = group size (a multiple
 // of the 32-row step).
-template <int kT, int kGS>
+template <int kT, int kGS, bool kBF>
 __global__ __launch_bounds__(256) void w4a16_gemv_lds_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qz,
@@ -239,9 +258,7 @@ __global__ __launch_bounds__(256) void w4a16_gemv_lds_kernel(
   const int xread = j * 16 + ((h ^ ((j >> 2) & 3)) * 4);
   const int col = 16 * wave + j;  // packed column within the strip
   const NibConst nc = nib_const();
-  f16x8 ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = static_cast<f16>(1.0f);
+  const f16x8 ones = ones_fragment<kBF>();
 
   f32x4 tot[kT][8];
 #pragma unroll
@@ -274,26 +291,25 @@ __global__ __launch_bounds__(256) void w4a16_gemv_lds_kernel(
 #pragma unroll
       for (int t = 0; t < kT; ++t) a[t] = *reinterpret_cast<const f16x8*>(&s_x[(slot * kT + t) * kLXWords + xread]);
       f16x8 b[8];
-      unpack_step_biased(w, nc, b);
+      unpack_step_biased<kBF>(w, nc, b);
       const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < kT; ++t) {
-        accx[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], ones, ks == 0 ? zero4 : accx[t], 0, 0, 0);
+        accx[t] = mfma_16x16x32<kBF>(a[t], ones, ks == 0 ? zero4 : accx[t]);
 #pragma unroll
-        for (int p = 0; p < 8; ++p)
-          acc[t][p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], b[p], ks == 0 ? zero4 : acc[t][p], 0, 0, 0);
+        for (int p = 0; p < 8; ++p) acc[t][p] = mfma_16x16x32<kBF>(a[t], b[p], ks == 0 ? zero4 : acc[t][p]);
       }
     }
     // tot += s * (acc - (1024 + z) * X); odd fields carry 16 (q - z), so
-    // their scale is s / 16 (exact).
+    // their scale is s / 16 (exact). bf16: tot += s * (acc - (128 + z) * X).
     const uint32_t zw = s_z[gi * 64 + col];
     const u32x4 sv = *reinterpret_cast<const u32x4*>(&s_sc[gi * 256 + col * 4]);
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const f16x2 s2 = as_f16x2(sv[p >> 1]);
-      const float sc = static_cast<float>(s2[p & 1]) * ((p & 1) ? 0.0625f : 1.0f);
       const float zf = static_cast<float>((zw >> (4 * p)) & 15u);
-      const float bias = (p & 1) ? 1024.0f + 16.0f * zf : 1024.0f + zf;
+      const float sc = static_cast<float>(s2[p & 1]) * ((p & 1) && !kBF ? 0.0625f : 1.0f);
+      const float bias = kBF ? 128.0f + zf : ((p & 1) ? 1024.0f + 16.0f * zf : 1024.0f + zf);
 #pragma unroll
       for (int t = 0; t < kT; ++t)
 #pragma unroll
@@ -304,7 +320,7 @@ __global__ __launch_bounds__(256) void w4a16_gemv_lds_kernel(
   const int c = strip * kLStrip + col;
   if (c < NP) {
 #pragma unroll
-    for (int t = 0; t < kT; ++t) write_out(tot[t], y, partial, M, N, c, h, split, splits, 16 * t);
+    for (int t = 0; t < kT; ++t) write_out<kBF>(tot[t], y, partial, M, N, c, h, split, splits, 16 * t);
   }
 }
 
@@ -357,32 +373,56 @@ __device__ __forceinline__ void load_group(GroupRegs<S>& r, const GemvLane L, in
   r.sv = load_at<u32x4>(L.sc + static_cast<size_t>(g) * L.srow_bytes, L.s_off);
 }
 
-template <int S>
+// bf16 (kBF): bf16 has no packed subtraction to form q - z exactly, so the
+// fragments hold 128 + q and the group adds s * (acc - (128 + z) * X), with X
+// the per-token sum of x from one more MFMA against ones (as the LDS kernel).
+template <int S, bool kBF>
 __device__ __forceinline__ void compute_group(const GroupRegs<S>& r, f32x4 (&tot)[8]) {
-  uint32_t negz[8];
-  zero_bias(r.zw, negz);
+  const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 acc[8];
+  if constexpr (kBF) {
+    const NibConst nc = nib_const();
+    const f16x8 ones = ones_fragment<true>();
+    f32x4 accx;
 #pragma unroll
-  for (int ks = 0; ks < S; ++ks) {
-    f16x8 b[8];
-    unpack_step(r.w[ks], negz, b);
+    for (int ks = 0; ks < S; ++ks) {
+      f16x8 b[8];
+      unpack_step_biased<true>(r.w[ks], nc, b);
+      accx = mfma_16x16x32<true>(r.a[ks], ones, ks == 0 ? zero4 : accx);
 #pragma unroll
-    for (int p = 0; p < 8; ++p)
-      acc[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(r.a[ks], b[p],
-                                                     ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[p], 0, 0, 0);
-  }
+      for (int p = 0; p < 8; ++p) acc[p] = mfma_16x16x32<true>(r.a[ks], b[p], ks == 0 ? zero4 : acc[p]);
+    }
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const f16x2 s2 = as_f16x2(r.sv[p >> 1]);
-    const float sc = static_cast<float>(s2[p & 1]) * ((p & 1) ? 0.0625f : 1.0f);
+    for (int p = 0; p < 8; ++p) {
+      const f16x2 s2 = as_f16x2(r.sv[p >> 1]);
+      const float sc = static_cast<float>(s2[p & 1]);
+      const float bias = 128.0f + static_cast<float>((r.zw >> (4 * p)) & 15u);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) tot[p][q] = fmaf(acc[p][q], sc, tot[p][q]);
+      for (int q = 0; q < 4; ++q) tot[p][q] = fmaf(sc, fmaf(-bias, accx[q], acc[p][q]), tot[p][q]);
+    }
+  } else {
+    uint32_t negz[8];
+    zero_bias(r.zw, negz);
+#pragma unroll
+    for (int ks = 0; ks < S; ++ks) {
+      f16x8 b[8];
+      unpack_step(r.w[ks], negz, b);
+#pragma unroll
+      for (int p = 0; p < 8; ++p) acc[p] = mfma_16x16x32<false>(r.a[ks], b[p], ks == 0 ? zero4 : acc[p]);
+    }
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const f16x2 s2 = as_f16x2(r.sv[p >> 1]);
+      const float sc = static_cast<float>(s2[p & 1]) * ((p & 1) ? 0.0625f : 1.0f);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tot[p][q] = fmaf(acc[p][q], sc, tot[p][q]);
+    }
   }
 }
 
 // The wavefronts of a workgroup sit side by side in N (NWC x 64 contiguous
 // bytes per row) and walk the split's groups (of kGS rows) together.
-template <int NWC, int kGS>
+template <int NWC, int kGS, bool kBF>
 __global__ __launch_bounds__(NWC * 64) void w4a16_gemv_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qz,
@@ -433,21 +473,21 @@ __global__ __launch_bounds__(NWC * 64) void w4a16_gemv_kernel(
     for (; i + 2 < n; i += 2) {
       load_group(rb, L, g_begin + i + 1);
       __builtin_amdgcn_sched_barrier(0);
-      compute_group(ra, tot);
+      compute_group<kSPG, kBF>(ra, tot);
       load_group(ra, L, g_begin + i + 2);
       __builtin_amdgcn_sched_barrier(0);
-      compute_group(rb, tot);
+      compute_group<kSPG, kBF>(rb, tot);
     }
     if (i + 1 < n) {
       load_group(rb, L, g_begin + i + 1);
       __builtin_amdgcn_sched_barrier(0);
-      compute_group(ra, tot);
-      compute_group(rb, tot);
+      compute_group<kSPG, kBF>(ra, tot);
+      compute_group<kSPG, kBF>(rb, tot);
     } else {
-      compute_group(ra, tot);
+      compute_group<kSPG, kBF>(ra, tot);
     }
   }
-  if (cvalid) write_out(tot, y, partial, M, N, c, h, split, splits);
+  if (cvalid) write_out<kBF>(tot, y, partial, M, N, c, h, split, splits);
 }
 
 }  // namespace
@@ -507,35 +547,35 @@ GemvPlan plan_w4a16_gemv(int64_t M, int64_t N, int64_t K, int64_t group) {
 
 namespace {
 
-template <int kGS>
+template <int kGS, bool kBF>
 hipError_t launch_gemv_main(const uint16_t* x, const uint32_t* qw, const uint16_t* scales, const uint32_t* qz,
                             uint16_t* y, float* part, int m, int n, int k, const GemvPlan& plan, int strips,
                             XcdMap map, dim3 grid, hipStream_t stream) {
   if (plan.lds) {
     switch ((m + 15) / 16) {
       case 1:
-        return launch_kernel(w4a16_gemv_lds_kernel<1, kGS>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part,
+        return launch_kernel(w4a16_gemv_lds_kernel<1, kGS, kBF>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part,
                              m, n, k, strips, plan.splits, map);
       case 2:
-        return launch_kernel(w4a16_gemv_lds_kernel<2, kGS>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part,
+        return launch_kernel(w4a16_gemv_lds_kernel<2, kGS, kBF>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part,
                              m, n, k, strips, plan.splits, map);
       case 3:
-        return launch_kernel(w4a16_gemv_lds_kernel<3, kGS>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part,
+        return launch_kernel(w4a16_gemv_lds_kernel<3, kGS, kBF>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part,
                              m, n, k, strips, plan.splits, map);
       default:
-        return launch_kernel(w4a16_gemv_lds_kernel<4, kGS>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part,
+        return launch_kernel(w4a16_gemv_lds_kernel<4, kGS, kBF>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part,
                              m, n, k, strips, plan.splits, map);
     }
   }
   switch (plan.waves) {
     case 2:
-      return launch_kernel(w4a16_gemv_kernel<2, kGS>, grid, dim3(128), 0, stream, x, qw, scales, qz, y, part, m, n,
+      return launch_kernel(w4a16_gemv_kernel<2, kGS, kBF>, grid, dim3(128), 0, stream, x, qw, scales, qz, y, part, m, n,
                            k, strips, plan.splits, map);
     case 8:
-      return launch_kernel(w4a16_gemv_kernel<8, kGS>, grid, dim3(512), 0, stream, x, qw, scales, qz, y, part, m, n,
+      return launch_kernel(w4a16_gemv_kernel<8, kGS, kBF>, grid, dim3(512), 0, stream, x, qw, scales, qz, y, part, m, n,
                            k, strips, plan.splits, map);
     default:
-      return launch_kernel(w4a16_gemv_kernel<4, kGS>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part, m, n,
+      return launch_kernel(w4a16_gemv_kernel<4, kGS, kBF>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part, m, n,
                            k, strips, plan.splits, map);
   }
 }
@@ -545,7 +585,7 @@ hipError_t launch_gemv_main(const uint16_t* x, const uint32_t* qw, const uint16_
 hipError_t launch_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                              const int32_t* qzeros, uint16_t* y,
                              int64_t M, int64_t N, int64_t K, const GemvPlan& plan,
-                             void* workspace, hipStream_t stream) {
+                             void* workspace, bool bf16, hipStream_t stream) {
   const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
   const int64_t strip_cols = plan.lds ? int64_t{kLStrip} : int64_t{kWaveCols} * plan.waves;
   const int strips = static_cast<int>((N / 8 + strip_cols - 1) / strip_cols);
@@ -565,21 +605,30 @@ hipError_t launch_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const ui
     for (int64_t m0 = 0; m0 < M; m0 += 16) {
       const int64_t ms = M - m0 < 16 ? M - m0 : 16;
       const hipError_t e = launch_w4a16_gemv(x + m0 * K, qweight, scales, qzeros, y + m0 * N, ms, N, K,
-                                             plan_w4a16_gemv(ms, N, K, plan.group), workspace, stream);
+                                             plan_w4a16_gemv(ms, N, K, plan.group), workspace, bf16, stream);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
   }
   hipError_t err;
-  switch (plan.group) {
-    case 32:
-      err = launch_gemv_main<32>(x, qw, scales, qz, y, part, m, n, k, plan, strips, map, grid, stream);
-      break;
+  switch (plan.group * 2 + (bf16 ? 1 : 0)) {
     case 64:
-      err = launch_gemv_main<64>(x, qw, scales, qz, y, part, m, n, k, plan, strips, map, grid, stream);
+      err = launch_gemv_main<32, false>(x, qw, scales, qz, y, part, m, n, k, plan, strips, map, grid, stream);
+      break;
+    case 65:
+      err = launch_gemv_main<32, true>(x, qw, scales, qz, y, part, m, n, k, plan, strips, map, grid, stream);
+      break;
+    case 128:
+      err = launch_gemv_main<64, false>(x, qw, scales, qz, y, part, m, n, k, plan, strips, map, grid, stream);
+      break;
+    case 129:
+      err = launch_gemv_main<64, true>(x, qw, scales, qz, y, part, m, n, k, plan, strips, map, grid, stream);
+      break;
+    case 257:
+      err = launch_gemv_main<128, true>(x, qw, scales, qz, y, part, m, n, k, plan, strips, map, grid, stream);
       break;
     default:
-      err = launch_gemv_main<128>(x, qw, scales, qz, y, part, m, n, k, plan, strips, map, grid, stream);
+      err = launch_gemv_main<128, false>(x, qw, scales, qz, y, part, m, n, k, plan, strips, map, grid, stream);
       break;
   }
   if (err != hipSuccess || plan.splits == 1) return err;
@@ -589,23 +638,7 @@ hipError_t launch_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const ui
   const int blocks_per_xcd = static_cast<int>((units_per_xcd + 255) / 256);
   const dim3 rgrid(static_cast<uint32_t>(kXcds * blocks_per_xcd));
   const int sps = map.strips_per_xcd;
-  switch (plan.splits) {
-    case 2:
-      return launch_kernel(w4a16_gemv_reduce<2>, rgrid, dim3(256), 0, stream, part, y, m, n, cols8, sps,
-                           blocks_per_xcd, plan.splits);
-    case 4:
-      return launch_kernel(w4a16_gemv_reduce<4>, rgrid, dim3(256), 0, stream, part, y, m, n, cols8, sps,
-                           blocks_per_xcd, plan.splits);
-    case 8:
-      return launch_kernel(w4a16_gemv_reduce<8>, rgrid, dim3(256), 0, stream, part, y, m, n, cols8, sps,
-                           blocks_per_xcd, plan.splits);
-    case 16:
-      return launch_kernel(w4a16_gemv_reduce<16>, rgrid, dim3(256), 0, stream, part, y, m, n, cols8, sps,
-                           blocks_per_xcd, plan.splits);
-    default:
-      return launch_kernel(w4a16_gemv_reduce<0>, rgrid, dim3(256), 0, stream, part, y, m, n, cols8, sps,
-                           blocks_per_xcd, plan.splits);
-  }
+  return launch_gemv_reduce(part, y, m, n, cols8, sps, blocks_per_xcd, plan.splits, bf16, rgrid, stream);
 }
 
 }  // namespace mq

@@ -170,6 +170,9 @@ __device__ __forceinline__ void load_chunk(BChunk<kT, kBChunkRows / kGS, kSP>& c
 // its own instructions does the compiler insert the wait states a VALU
 // write needs before an MFMA reads the register (with an asm v_and_or_b32
 // the MFMA was measured to read the register's old value).
+// kBF: bf16 fragments of 128 + q for both fields (the high nibble shifted
+// down first).
+template <bool kBF>
 __device__ __forceinline__ void unpack_block(uint32_t w0, uint32_t w1, const NibConst& c, f16x8 (&bf)[2]) {
   const uint32_t ws[2] = {w0, w1};
 #pragma unroll
@@ -178,8 +181,8 @@ __device__ __forceinline__ void unpack_block(uint32_t w0, uint32_t w1, const Nib
     for (int t = 0; t < 2; ++t) {
       // bytes 2t, 2t+1 (rows 4q+2t, 4q+2t+1) into bits 0-7 and 16-23
       const uint32_t v = byte_perm(ws[q], ws[q], t ? 0x0C030C02u : 0x0C010C00u);
-      const f16x2 lo = as_f16x2((v & c.lo) | c.magic);
-      const f16x2 hi = as_f16x2((v & c.hi) | c.magic);
+      const f16x2 lo = as_f16x2((v & c.lo) | (kBF ? c.bmagic : c.magic));
+      const f16x2 hi = as_f16x2(kBF ? ((v >> 4) & c.lo) | c.bmagic : (v & c.hi) | c.magic);
       bf[0][4 * q + 2 * t] = lo[0];
       bf[0][4 * q + 2 * t + 1] = lo[1];
       bf[1][4 * q + 2 * t] = hi[0];
@@ -187,7 +190,7 @@ __device__ __forceinline__ void unpack_block(uint32_t w0, uint32_t w1, const Nib
     }
 }
 
-template <int kT, int kGS, int kSP, bool kXL>
+template <int kT, int kGS, int kSP, bool kXL, bool kBF>
 __device__ __forceinline__ void compute_chunk(const BChunk<kT, kBChunkRows / kGS, kSP>& ch, const NibConst& nc,
                                               const f16x8 ones, int g_lane, f32x4 (&tot)[kT][kSP][2],
                                               const lds_u8* xl, const lds_u8* scl, const lds_u8* zl) {
@@ -233,26 +236,25 @@ __device__ __forceinline__ void compute_chunk(const BChunk<kT, kBChunkRows / kGS
 #pragma unroll
       for (int sp = 0; sp < kSP; ++sp) {
         f16x8 bf[2];
-        unpack_block(ch.w[sp][b >> 1][2 * (b & 1)], ch.w[sp][b >> 1][2 * (b & 1) + 1], nc, bf);
+        unpack_block<kBF>(ch.w[sp][b >> 1][2 * (b & 1)], ch.w[sp][b >> 1][2 * (b & 1) + 1], nc, bf);
 #pragma unroll
         for (int t = 0; t < kT; ++t)
 #pragma unroll
           for (int f = 0; f < 2; ++f)
-            acc[t][sp][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[t][b], bf[f], bb == 0 ? zero4 : acc[t][sp][f],
-                                                                  0, 0, 0);
+            acc[t][sp][f] = mfma_16x16x32<kBF>(xa[t][b], bf[f], bb == 0 ? zero4 : acc[t][sp][f]);
       }
 #pragma unroll
-      for (int t = 0; t < kT; ++t)
-        accx[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[t][b], ones, bb == 0 ? zero4 : accx[t], 0, 0, 0);
+      for (int t = 0; t < kT; ++t) accx[t] = mfma_16x16x32<kBF>(xa[t][b], ones, bb == 0 ? zero4 : accx[t]);
     }
     // tot += s * (acc - (1024 + z) * X); field 2g+1 carries 16 (q - z), so
-    // its scale is s / 16 (exact).
+    // its scale is s / 16 (exact). bf16: both fields carry 128 + q.
 #pragma unroll
     for (int sp = 0; sp < kSP; ++sp) {
       const f16x2 s2 = as_f16x2(sv[sp][g]);
       const uint32_t zb = (zw[sp][g] >> (8 * g_lane)) & 0xFFu;
-      const float sc[2] = {static_cast<float>(s2[0]), static_cast<float>(s2[1]) * 0.0625f};
-      const float bias[2] = {1024.0f + static_cast<float>(zb & 15u), 1024.0f + static_cast<float>(zb & 0xF0u)};
+      const float sc[2] = {static_cast<float>(s2[0]), static_cast<float>(s2[1]) * (kBF ? 1.0f : 0.0625f)};
+      const float bias[2] = {(kBF ? 128.0f : 1024.0f) + static_cast<float>(zb & 15u),
+                             kBF ? 128.0f + static_cast<float>(zb >> 4) : 1024.0f + static_cast<float>(zb & 0xF0u)};
 #pragma unroll
       for (int f = 0; f < 2; ++f)
 #pragma unroll
@@ -271,6 +273,10 @@ __device__ __forceinline__ void compute_chunk(const BChunk<kT, kBChunkRows / kGS
 // -(1024 + z) / -(64 + z) leaves q - z exactly, and one multiply by s rounds.
 // nz[f] / s2[f]: the encoded negated zero point and the scale of field f,
 // both replicated in the two fp16 halves.
+// kBF: nz[f] / s2[f] hold binary32 bits of -(offset + z) * s and of s; one
+// fused multiply-add per weight gives (q - z) * s exactly in binary32 and
+// the pair conversion rounds it once to bf16.
+template <bool kBF>
 __device__ __forceinline__ void unpack_block_scaled(uint32_t w0, uint32_t w1, const NibConst& c,
                                                     const uint32_t (&nz)[2], const uint32_t (&s2)[2],
                                                     f16x8 (&bf)[2]) {
@@ -280,8 +286,17 @@ __device__ __forceinline__ void unpack_block_scaled(uint32_t w0, uint32_t w1, co
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const uint32_t v = byte_perm(ws[q], ws[q], t ? 0x0C030C02u : 0x0C010C00u);
-      const f16x2 lo = (as_f16x2((v & c.lo) | c.magic) + as_f16x2(nz[0])) * as_f16x2(s2[0]);
-      const f16x2 hi = (as_f16x2((v & c.hi) | c.magic64) + as_f16x2(nz[1])) * as_f16x2(s2[1]);
+      f16x2 lo, hi;
+      if constexpr (kBF) {
+        const f16x2 ol = as_f16x2((v & c.lo) | c.magic), oh = as_f16x2((v & c.hi) | c.magic64);
+        const float sl = __builtin_bit_cast(float, s2[0]), cl = __builtin_bit_cast(float, nz[0]);
+        const float sh = __builtin_bit_cast(float, s2[1]), ch = __builtin_bit_cast(float, nz[1]);
+        lo = as_f16x2(bf16x2_bits(fmaf(static_cast<float>(ol[0]), sl, cl), fmaf(static_cast<float>(ol[1]), sl, cl)));
+        hi = as_f16x2(bf16x2_bits(fmaf(static_cast<float>(oh[0]), sh, ch), fmaf(static_cast<float>(oh[1]), sh, ch)));
+      } else {
+        lo = (as_f16x2((v & c.lo) | c.magic) + as_f16x2(nz[0])) * as_f16x2(s2[0]);
+        hi = (as_f16x2((v & c.hi) | c.magic64) + as_f16x2(nz[1])) * as_f16x2(s2[1]);
+      }
       bf[0][4 * q + 2 * t] = lo[0];
       bf[0][4 * q + 2 * t + 1] = lo[1];
       bf[1][4 * q + 2 * t] = hi[0];
@@ -293,7 +308,7 @@ __device__ __forceinline__ void unpack_block_scaled(uint32_t w0, uint32_t w1, co
 // running sums (the weights carry their scales), so no per-group partial
 // sums or sums of x are kept -- that is what lets three strips share every
 // x fragment of four token tiles within the register file.
-template <int kT, int kGS, int kSP>
+template <int kT, int kGS, int kSP, bool kBF>
 __device__ __forceinline__ void compute_chunk_scaled(const BChunk<kT, kBChunkRows / kGS, kSP>& ch,
                                                      const NibConst& nc, int g_lane, f32x4 (&tot)[kT][kSP][2]) {
   constexpr int kGPC = kBChunkRows / kGS;
@@ -304,22 +319,32 @@ __device__ __forceinline__ void compute_chunk_scaled(const BChunk<kT, kBChunkRow
     for (int sp = 0; sp < kSP; ++sp) {
       const f16x2 sv = as_f16x2(ch.sv[sp][g]);
       const uint32_t zb = (ch.zw[sp][g] >> (8 * g_lane)) & 0xFFu;
-      f16x2 s_lo, s_hi;
-      s_lo[0] = s_lo[1] = sv[0];
-      s_hi[0] = s_hi[1] = sv[1];
-      const uint32_t e_lo = (zb & 0x0Fu) | 0xE400u, e_hi = (zb & 0xF0u) | 0xD400u;
-      const uint32_t nz[2] = {e_lo | (e_lo << 16), e_hi | (e_hi << 16)};
-      const uint32_t s2[2] = {as_u32(s_lo), as_u32(s_hi)};
+      uint32_t nz[2], s2[2];
+      if constexpr (kBF) {
+        const float sl = static_cast<float>(sv[0]), sh = static_cast<float>(sv[1]);
+        nz[0] = __builtin_bit_cast(uint32_t, -(1024.0f + static_cast<float>(zb & 15u)) * sl);
+        nz[1] = __builtin_bit_cast(uint32_t, -(64.0f + static_cast<float>(zb >> 4)) * sh);
+        s2[0] = __builtin_bit_cast(uint32_t, sl);
+        s2[1] = __builtin_bit_cast(uint32_t, sh);
+      } else {
+        f16x2 s_lo, s_hi;
+        s_lo[0] = s_lo[1] = sv[0];
+        s_hi[0] = s_hi[1] = sv[1];
+        const uint32_t e_lo = (zb & 0x0Fu) | 0xE400u, e_hi = (zb & 0xF0u) | 0xD400u;
+        nz[0] = e_lo | (e_lo << 16);
+        nz[1] = e_hi | (e_hi << 16);
+        s2[0] = as_u32(s_lo);
+        s2[1] = as_u32(s_hi);
+      }
 #pragma unroll
       for (int bb = 0; bb < kBPG; ++bb) {
         const int b = g * kBPG + bb;
         f16x8 bf[2];
-        unpack_block_scaled(ch.w[sp][b >> 1][2 * (b & 1)], ch.w[sp][b >> 1][2 * (b & 1) + 1], nc, nz, s2, bf);
+        unpack_block_scaled<kBF>(ch.w[sp][b >> 1][2 * (b & 1)], ch.w[sp][b >> 1][2 * (b & 1) + 1], nc, nz, s2, bf);
 #pragma unroll
         for (int t = 0; t < kT; ++t)
 #pragma unroll
-          for (int f = 0; f < 2; ++f)
-            tot[t][sp][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ch.a[t][b], bf[f], tot[t][sp][f], 0, 0, 0);
+          for (int f = 0; f < 2; ++f) tot[t][sp][f] = mfma_16x16x32<kBF>(ch.a[t][b], bf[f], tot[t][sp][f]);
       }
     }
 }
@@ -339,7 +364,7 @@ __device__ __forceinline__ void compute_chunk_scaled(const BChunk<kT, kBChunkRow
 // Three or four tiles (33-64 tokens) take the pre-scaled form: one pass
 // over the weights for all tokens, the wavefronts' sums added in LDS one
 // wavefront after the other (same order, smaller buffer).
-template <int kT, int kGS, int kW, int kSP, bool kXL>
+template <int kT, int kGS, int kW, int kSP, bool kXL, bool kBF>
 __global__ __launch_bounds__(kW * 64)
 __attribute__((amdgpu_waves_per_eu(kT == 1 && kSP == 1 && kGS >= 64 ? 3 : 1))) void w4a16_gemv_blocked_kernel(
     const uint16_t* __restrict__ x, const u32x4* __restrict__ qb, const uint16_t* __restrict__ scales,
@@ -381,9 +406,7 @@ __attribute__((amdgpu_waves_per_eu(kT == 1 && kSP == 1 && kGS >= 64 ? 3 : 1))) v
   L.NP = NP;
 
   const NibConst nc = nib_const();
-  f16x8 ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = static_cast<f16>(1.0f);
+  const f16x8 ones = ones_fragment<kBF>();
 
   f32x4 tot[kT][kSP][2];
 #pragma unroll
@@ -450,9 +473,9 @@ __attribute__((amdgpu_waves_per_eu(kT == 1 && kSP == 1 && kGS >= 64 ? 3 : 1))) v
     auto zl = [&](int chunk) -> const lds_u8* { return z_lane + (chunk - kbase) * kGPC * kSP * 16; };
     auto compute = [&](const BChunk<kT, kGPC, kSP>& ch, int chunk) {
       if constexpr (kPS) {
-        compute_chunk_scaled<kT, kGS, kSP>(ch, nc, g, tot);
+        compute_chunk_scaled<kT, kGS, kSP, kBF>(ch, nc, g, tot);
       } else {
-        compute_chunk<kT, kGS, kSP, kXL>(ch, nc, ones, g, tot, xl(chunk), sl(chunk), zl(chunk));
+        compute_chunk<kT, kGS, kSP, kXL, kBF>(ch, nc, ones, g, tot, xl(chunk), sl(chunk), zl(chunk));
       }
     };
     int i = 0;
@@ -515,26 +538,26 @@ __attribute__((amdgpu_waves_per_eu(kT == 1 && kSP == 1 && kGS >= 64 ? 3 : 1))) v
     }
     const size_t o = static_cast<size_t>(strip) * kBOut + n;
     if (splits == 1) {
-      y[static_cast<size_t>(m) * N + o] = __builtin_bit_cast(uint16_t, static_cast<f16>(v));
+      y[static_cast<size_t>(m) * N + o] = half_bits<kBF>(v);
     } else {
       partial[(static_cast<size_t>(split) * M + m) * N + o] = v;
     }
   }
 }
 
-template <int kT, int kGS, int kSP, bool kXL>
+template <int kT, int kGS, int kSP, bool kXL, bool kBF>
 hipError_t launch_blocked_xl(const uint16_t* x, const u32x4* qb, const uint16_t* scales, const uint32_t* qz,
                              uint16_t* y, float* part, int m, int n, int k, const GemvPlan& plan, int units,
                              XcdMap map, dim3 grid, size_t lds, hipStream_t stream) {
   switch (plan.waves) {
     case 1:
-      return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 1, kSP, kXL>, grid, dim3(64), lds, stream, x, qb,
+      return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 1, kSP, kXL, kBF>, grid, dim3(64), lds, stream, x, qb,
                            scales, qz, y, part, m, n, k, units, plan.splits, map);
     case 2:
-      return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 2, kSP, kXL>, grid, dim3(128), lds, stream, x, qb,
+      return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 2, kSP, kXL, kBF>, grid, dim3(128), lds, stream, x, qb,
                            scales, qz, y, part, m, n, k, units, plan.splits, map);
     default:
-      return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 4, kSP, kXL>, grid, dim3(256), lds, stream, x, qb,
+      return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 4, kSP, kXL, kBF>, grid, dim3(256), lds, stream, x, qb,
                            scales, qz, y, part, m, n, k, units, plan.splits, map);
   }
 }
@@ -552,62 +575,62 @@ int64_t blocked_x_lds_bytes(int64_t M, int64_t K, int64_t group, int splits, int
   return xb + szb;
 }
 
-template <int kT, int kGS, int kSP>
+template <int kT, int kGS, int kSP, bool kBF>
 hipError_t launch_blocked_main(const uint16_t* x, const u32x4* qb, const uint16_t* scales, const uint32_t* qz,
                                uint16_t* y, float* part, int m, int n, int k, const GemvPlan& plan, int units,
                                XcdMap map, dim3 grid, hipStream_t stream) {
   if constexpr (kT == 1) {
     const int64_t lds = blocked_x_lds_bytes(m, k, kGS, plan.splits, plan.waves, kSP);
     if (lds > 0)
-      return launch_blocked_xl<kT, kGS, kSP, true>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid,
+      return launch_blocked_xl<kT, kGS, kSP, true, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid,
                                                    static_cast<size_t>(lds), stream);
   }
-  return launch_blocked_xl<kT, kGS, kSP, false>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, 0,
+  return launch_blocked_xl<kT, kGS, kSP, false, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, 0,
                                                 stream);
 }
 
-template <int kT, int kGS>
+template <int kT, int kGS, bool kBF>
 hipError_t launch_blocked_scaled(const uint16_t* x, const u32x4* qb, const uint16_t* scales, const uint32_t* qz,
                                  uint16_t* y, float* part, int m, int n, int k, const GemvPlan& plan, int units,
                                  XcdMap map, dim3 grid, hipStream_t stream) {
   if constexpr (kGS >= 64) {
     if (plan.strips_per_unit == 3)
-      return launch_blocked_xl<kT, kGS, 3, false>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, 0,
+      return launch_blocked_xl<kT, kGS, 3, false, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, 0,
                                                   stream);
     if (plan.strips_per_unit == 2)
-      return launch_blocked_xl<kT, kGS, 2, false>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, 0,
+      return launch_blocked_xl<kT, kGS, 2, false, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, 0,
                                                   stream);
   }
-  return launch_blocked_xl<kT, kGS, 1, false>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, 0,
+  return launch_blocked_xl<kT, kGS, 1, false, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, 0,
                                               stream);
 }
 
-template <int kGS>
+template <int kGS, bool kBF>
 hipError_t launch_blocked_group(const uint16_t* x, const u32x4* qb, const uint16_t* scales, const uint32_t* qz,
                                 uint16_t* y, float* part, int m, int n, int k, const GemvPlan& plan, int units,
                                 XcdMap map, dim3 grid, hipStream_t stream) {
-  if (m > 48) return launch_blocked_scaled<4, kGS>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
-  if (m > 32) return launch_blocked_scaled<3, kGS>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+  if (m > 48) return launch_blocked_scaled<4, kGS, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+  if (m > 32) return launch_blocked_scaled<3, kGS, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
   if constexpr (kGS == 32) {
     // groups of 32: one strip per workgroup (the multi-strip forms do not
     // fit the register file with four groups per chunk)
     if (m <= 16)
-      return launch_blocked_main<1, kGS, 1>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
-    return launch_blocked_main<2, kGS, 1>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+      return launch_blocked_main<1, kGS, 1, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+    return launch_blocked_main<2, kGS, 1, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
   } else {
     if (m <= 16) {
       switch (plan.strips_per_unit) {
         case 3:
-          return launch_blocked_main<1, kGS, 3>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+          return launch_blocked_main<1, kGS, 3, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
         case 2:
-          return launch_blocked_main<1, kGS, 2>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+          return launch_blocked_main<1, kGS, 2, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
         default:
-          return launch_blocked_main<1, kGS, 1>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+          return launch_blocked_main<1, kGS, 1, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
       }
     }
     if (plan.strips_per_unit == 2)
-      return launch_blocked_main<2, kGS, 2>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
-    return launch_blocked_main<2, kGS, 1>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+      return launch_blocked_main<2, kGS, 2, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+    return launch_blocked_main<2, kGS, 1, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
   }
 }
 
@@ -682,7 +705,7 @@ hipError_t launch_w4a16_block_weights(const int32_t* qweight, int32_t* blocked, 
 
 hipError_t launch_w4a16_gemv_blocked(const uint16_t* x, const int32_t* blocked, const uint16_t* scales,
                                      const int32_t* qzeros, uint16_t* y, int64_t M, int64_t N, int64_t K,
-                                     const GemvPlan& plan, void* workspace, hipStream_t stream) {
+                                     const GemvPlan& plan, void* workspace, bool bf16, hipStream_t stream) {
   if (N % kBOut || K % kBChunkRows || M < 1 || M > kGemvMaxM || plan.waves < 1) return hipErrorInvalidValue;
   if (plan.group != 32 && plan.group != 64 && plan.group != 128) return hipErrorInvalidValue;
   if ((K / kBChunkRows) % (static_cast<int64_t>(plan.splits) * plan.waves)) return hipErrorInvalidValue;
@@ -695,15 +718,24 @@ hipError_t launch_w4a16_gemv_blocked(const uint16_t* x, const int32_t* blocked, 
   const uint32_t* qz = reinterpret_cast<const uint32_t*>(qzeros);
   float* part = static_cast<float*>(workspace);
   hipError_t err;
-  switch (plan.group) {
-    case 32:
-      err = launch_blocked_group<32>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
-      break;
+  switch (plan.group * 2 + (bf16 ? 1 : 0)) {
     case 64:
-      err = launch_blocked_group<64>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+      err = launch_blocked_group<32, false>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+      break;
+    case 65:
+      err = launch_blocked_group<32, true>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+      break;
+    case 128:
+      err = launch_blocked_group<64, false>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+      break;
+    case 129:
+      err = launch_blocked_group<64, true>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+      break;
+    case 257:
+      err = launch_blocked_group<128, true>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
       break;
     default:
-      err = launch_blocked_group<128>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+      err = launch_blocked_group<128, false>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
       break;
   }
   if (err != hipSuccess || plan.splits == 1) return err;
@@ -712,20 +744,7 @@ hipError_t launch_w4a16_gemv_blocked(const uint16_t* x, const int32_t* blocked, 
   const int blocks_per_xcd = static_cast<int>((units_per_xcd + 255) / 256);
   const dim3 rgrid(static_cast<uint32_t>(kXcds * blocks_per_xcd));
   const int sps = map.strips_per_xcd;
-  switch (plan.splits) {
-    case 2:
-      return launch_kernel(w4a16_gemv_reduce<2>, rgrid, dim3(256), 0, stream, part, y, m, n, cols8, sps,
-                           blocks_per_xcd, plan.splits);
-    case 4:
-      return launch_kernel(w4a16_gemv_reduce<4>, rgrid, dim3(256), 0, stream, part, y, m, n, cols8, sps,
-                           blocks_per_xcd, plan.splits);
-    case 8:
-      return launch_kernel(w4a16_gemv_reduce<8>, rgrid, dim3(256), 0, stream, part, y, m, n, cols8, sps,
-                           blocks_per_xcd, plan.splits);
-    default:
-      return launch_kernel(w4a16_gemv_reduce<0>, rgrid, dim3(256), 0, stream, part, y, m, n, cols8, sps,
-                           blocks_per_xcd, plan.splits);
-  }
+  return launch_gemv_reduce(part, y, m, n, cols8, sps, blocks_per_xcd, plan.splits, bf16, rgrid, stream);
 }
 
 }  // namespace mq

@@ -6,6 +6,7 @@
 #pragma once
 
 #include "device_common.h"
+#include "launch.h"
 
 namespace mq {
 namespace {
@@ -36,7 +37,7 @@ __device__ __forceinline__ bool decode_work(int block, int strips_per_xcd, int s
 // order. Thread t of the block sums 4 consecutive outputs of one token row
 // of one strip; blocks are mapped to the XCD that wrote that strip.
 // ---------------------------------------------------------------------------
-template <int S>
+template <int S, bool kBF>
 __global__ __launch_bounds__(256) void w4a16_gemv_reduce(const float* __restrict__ partial,
                                                          uint16_t* __restrict__ y, int M, int N,
                                                          int strip_cols, int strips_per_xcd,
@@ -62,12 +63,38 @@ __global__ __launch_bounds__(256) void w4a16_gemv_reduce(const float* __restrict
   } else {
     for (int s = 1; s < splits; ++s) acc += *reinterpret_cast<const f32x4*>(src + s * stride);
   }
-  f16x2 lo, hi;
-  lo[0] = static_cast<f16>(acc[0]);
-  lo[1] = static_cast<f16>(acc[1]);
-  hi[0] = static_cast<f16>(acc[2]);
-  hi[1] = static_cast<f16>(acc[3]);
-  *reinterpret_cast<u32x2*>(y + static_cast<size_t>(m) * N + n) = u32x2{as_u32(lo), as_u32(hi)};
+  const uint32_t lo = half_bits<kBF>(acc[0]) | (static_cast<uint32_t>(half_bits<kBF>(acc[1])) << 16);
+  const uint32_t hi = half_bits<kBF>(acc[2]) | (static_cast<uint32_t>(half_bits<kBF>(acc[3])) << 16);
+  *reinterpret_cast<u32x2*>(y + static_cast<size_t>(m) * N + n) = u32x2{lo, hi};
+}
+
+template <bool kBF>
+hipError_t launch_gemv_reduce_t(const float* part, uint16_t* y, int m, int n, int cols8, int sps, int bpx,
+                                int splits, dim3 rgrid, hipStream_t stream) {
+  switch (splits) {
+    case 2:
+      return launch_kernel(w4a16_gemv_reduce<2, kBF>, rgrid, dim3(256), 0, stream, part, y, m, n, cols8, sps, bpx,
+                           splits);
+    case 4:
+      return launch_kernel(w4a16_gemv_reduce<4, kBF>, rgrid, dim3(256), 0, stream, part, y, m, n, cols8, sps, bpx,
+                           splits);
+    case 8:
+      return launch_kernel(w4a16_gemv_reduce<8, kBF>, rgrid, dim3(256), 0, stream, part, y, m, n, cols8, sps, bpx,
+                           splits);
+    case 16:
+      return launch_kernel(w4a16_gemv_reduce<16, kBF>, rgrid, dim3(256), 0, stream, part, y, m, n, cols8, sps, bpx,
+                           splits);
+    default:
+      return launch_kernel(w4a16_gemv_reduce<0, kBF>, rgrid, dim3(256), 0, stream, part, y, m, n, cols8, sps, bpx,
+                           splits);
+  }
+}
+
+// The reduction for `splits` partial sums, output fp16 or (bf16) bf16.
+inline hipError_t launch_gemv_reduce(const float* part, uint16_t* y, int m, int n, int cols8, int sps, int bpx,
+                                     int splits, bool bf16, dim3 rgrid, hipStream_t stream) {
+  return bf16 ? launch_gemv_reduce_t<true>(part, y, m, n, cols8, sps, bpx, splits, rgrid, stream)
+              : launch_gemv_reduce_t<false>(part, y, m, n, cols8, sps, bpx, splits, rgrid, stream);
 }
 
 }  // namespace
