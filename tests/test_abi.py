@@ -208,7 +208,9 @@ def test_w8a8_linear_validation(lib):
     ws = lib.mq_w8a8_linear_workspace_bytes
     assert ws(1, 4096) == 0 and ws(1, 64) == 0 and ws(1, 81904) == 0  # fused: no workspace
     assert ws(1, 81920) > 0                              # the fused codes must fit 80 KB of LDS
-    assert ws(2, 4096) >= 2 * 4096 + 2 * 4                # two kernels: codes + scales
+    assert ws(2, 4096) == 0 and ws(2, 40944) == 0        # two tokens fused as well
+    assert ws(2, 40960) > 0
+    assert ws(3, 4096) >= 3 * 4096 + 3 * 4                # two kernels: codes + scales
     assert ws(17, 4096) >= 17 * 4096 + 17 * 4
     assert ws(17, 40) == 0                               # rejected shape (K % 16)
     assert f(A, B, C, E, 4, 64, 40, None, 0, None) == SHAPE     # K % 16

@@ -1,10 +1,12 @@
 """W8A8_INT8 linear layer from fp16 activations (mq_w8a8_linear) on an MI355X.
 
-For one token (while its codes fit 80 KB of LDS) the per-token quantizer
-runs inside the decode kernel; the result must equal mq_quant_per_token_int8
-followed by mq_w8a8_scaled_mm bit for bit (same codes, scales and int32
-accumulators, same epilogue), and the oracle within the fp16 tolerance. For
-more tokens the entry point runs the two kernels through its workspace.
+For one or two tokens (while their codes fit 80 KB of LDS) the per-token
+quantizer runs inside the decode kernel (with two tokens a grid of about two
+workgroups per CU walks the channel tiles, each workgroup forming the codes
+once); the result must equal mq_quant_per_token_int8 followed by
+mq_w8a8_scaled_mm bit for bit (same codes, scales and int32 accumulators,
+same epilogue), and the oracle within the fp16 tolerance. For more tokens
+the entry point runs the two kernels through its workspace.
 """
 
 import numpy as np
@@ -21,7 +23,9 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 4096), (1, 4096, 6144), (1, 4096, 24576), (1, 12288, 4096),
                                    (1, 16, 8), (1, 272, 300), (1, 1040, 37), (1, 81904, 64), (1, 133136, 48),
                                    (4, 4096, 24576), (16, 4096, 4096),
-                                   (2, 16, 8), (7, 272, 300), (13, 1040, 37), (16, 64, 4112),
+                                   (2, 16, 8), (2, 4096, 24576), (2, 4096, 6144), (2, 12288, 4096),
+                                   (2, 40000, 200), (2, 1040, 9000),
+                                   (7, 272, 300), (13, 1040, 37), (16, 64, 4112),
                                    (3, 133136, 48),
                                    # two kernels through the workspace
                                    (17, 512, 264), (64, 4096, 4096), (300, 1024, 640)])

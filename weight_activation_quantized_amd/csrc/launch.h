@@ -32,9 +32,11 @@ hipError_t launch_w8a8_gemv(const int8_t* xq, const float* s_tok, const int8_t* 
 // in one launch, bit-identical to the two separate calls, where
 // w8a8_use_fused(M, K): 1 <= M <= kW8A8FusedMaxM and the M x K codes fit a
 // workgroup's 80 KB of LDS. Every workgroup forms all M rows' scales and
-// codes itself, so the fused form pays only for one token (measured: 2-3 us
-// faster per layer at M = 1, 8-20 us slower at M = 8).
-constexpr int64_t kW8A8FusedMaxM = 1;
+// codes itself (once, walking several channel tiles when M > 1), so the
+// fused form pays only for one or two tokens (measured, 8B layers: 2-3 us
+// faster per layer at M = 1, 0.7-3 us at M = 2 except down, equal there;
+// 1-3 us slower at M = 4 on three of four layers, 5-8 us slower at M = 8).
+constexpr int64_t kW8A8FusedMaxM = 2;
 bool w8a8_use_fused(int64_t M, int64_t K);
 hipError_t launch_w8a8_gemv_fused(const uint16_t* x, const int8_t* wq, const float* s_ch, uint16_t* y,
                                   int64_t M, int64_t N, int64_t K, bool bf16, hipStream_t stream);
