@@ -29,10 +29,12 @@ Also reported (same line):
                FETCH_SIZE + WRITE_SIZE per call from a committed
                rocprofv3 counter summary when it matches the current kernel
                source, else null.
+  gemv_bf16    the headline steps with bf16 activations (decode layout).
   prefill      W8A8 prefill (per-token quant + scaled int8 GEMM, M=2048,
                K=N=4096; also with bf16 activations and output) and W4A16
-               prefill GEMMs (M=4096, K=4096/12288, N=4096): kernel time and
-               TOPS against the dense MFMA peaks.
+               prefill GEMMs (M=4096, K=4096/12288, N=4096; K=4096 also with
+               bf16 activations): kernel time and TOPS against the dense MFMA
+               peaks.
   layers       the linear layers of an 8B-shaped decoder layer (qkv 4096->6144,
                o_proj 4096->4096, gate_up 4096->24576, down 12288->4096) at
                M = 1, 8, 64 and 2048 under W4A16 (decode-layout GEMV up to 64
@@ -189,7 +191,28 @@ def bench_gemv(torch, mq, synth, args, log):
                                       workspace=wss[M])
         return run
 
+    # the same steps with bf16 activations (bf16 copies of the same x)
+    xs_bf = {M: xs[M].float().to(torch.bfloat16) for M in GEMV_MS}
+    ys_bf = {M: torch.empty((M, GEMV_N), dtype=torch.bfloat16, device=dev) for M in GEMV_MS}
+
+    def steps_bf16(n):
+        def run():
+            for _ in range(n):
+                for M in GEMV_MS:
+                    w = sets[counter[0] % len(sets)]
+                    counter[0] += 1
+                    mq.w4a16_gemv_blocked(xs_bf[M], w["qblocked"], w["scales"], w["qzeros"], GROUP, out=ys_bf[M],
+                                          workspace=wss[M])
+        return run
+
     res = {}
+    log("bf16 decode layout: capturing and timing")
+    g_warm = capture(torch, steps_bf16(max(args.warmup, 1)))
+    g_timed = capture(torch, steps_bf16(args.steps))
+    g_warm.replay()
+    torch.cuda.synchronize()
+    res["bf16"] = timed_replay(torch, g_timed)
+    del g_warm, g_timed
     for blocked in (True, False):
         name = "blocked" if blocked else "awq"
         log(f"{name}: capturing warmup ({args.warmup}) and timed ({args.steps}) steps")
@@ -205,6 +228,7 @@ def bench_gemv(torch, mq, synth, args, log):
     launches = args.steps * len(GEMV_MS)
     workspace_bytes = {M: mq.w4a16_gemv_blocked_workspace_bytes(M, GEMV_N, GEMV_K, GROUP) for M in GEMV_MS}
     awq_wall, awq_ev = res["awq"]
+    bf_wall, bf_ev = res["bf16"]
     return {
         "wall_s": wall, "event_s": ev, "step_bytes": step_bytes, "launches": launches,
         "kernel_avg_us": ev / launches * 1e6, "workspace_bytes": workspace_bytes,
@@ -212,6 +236,9 @@ def bench_gemv(torch, mq, synth, args, log):
         "awq_layout": {"GBps": round(step_bytes / (awq_wall / args.steps) / 1e9, 1),
                        "us_per_call": round(awq_ev / launches * 1e6, 3),
                        "kernel": "w4a16_gemv_lds_kernel + w4a16_gemv_reduce (K split 8 ways)"},
+        "bf16": {"GBps": round(step_bytes / (bf_wall / args.steps) / 1e9, 1),
+                 "us_per_call": round(bf_ev / launches * 1e6, 3),
+                 "kernel": "w4a16_gemv_blocked_kernel, bf16 activations (same steps, decode layout)"},
     }, sets, xs
 
 
@@ -275,6 +302,17 @@ def bench_prefill(torch, mq, synth, oracle_free_quant, args, log):
         out[name] = {"shape": [M, N, K], "gemm_us": tg * 1e6, "gemm_TFLOPS": ops / tg / 1e12,
                      "gemm_frac_fp16_peak": ops / tg / 1e12 / FP16_PEAK_TFLOPS}
         del t, y
+    # bf16 activations: the o_proj-shaped prefill GEMM (bf16 MFMA, same peak as fp16)
+    M, N, K = 4096, 4096, 4096
+    db = synth.w4a16_inputs_bf16(M, K, N, GROUP, tag=3)
+    xb = torch.from_numpy(db["x_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    t = {k: torch.from_numpy(db[k]).to(dev) for k in ("qweight", "scales", "qzeros")}
+    yb = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    log("prefill: w4a16_c3a_bf16")
+    tg = time_fn(lambda: mq.w4a16_gemm(xb, t["qweight"], t["scales"], t["qzeros"], GROUP, out=yb))
+    ops = 2.0 * M * N * K
+    out["w4a16_c3a_bf16"] = {"shape": [M, N, K], "gemm_us": tg * 1e6, "gemm_TFLOPS": ops / tg / 1e12,
+                             "gemm_frac_bf16_peak": ops / tg / 1e12 / FP16_PEAK_TFLOPS}
     return out
 
 
@@ -616,8 +654,8 @@ def prefill_roofline(prefill):
             counters = json.load(f).get("kernels", {})
     out = {}
     for key, kernel, peak, unit in (("w8a8_c2", "w8a8_gemm_kernel<true, false>", INT8_PEAK_TOPS, "TOP/s"),
-                                    ("w4a16_c3a", "w4a16_gemm_kernel<4>", FP16_PEAK_TFLOPS, "TFLOP/s"),
-                                    ("w4a16_c3b", "w4a16_gemm_kernel<4>", FP16_PEAK_TFLOPS, "TFLOP/s")):
+                                    ("w4a16_c3a", "w4a16_gemm_kernel<4, false>", FP16_PEAK_TFLOPS, "TFLOP/s"),
+                                    ("w4a16_c3b", "w4a16_gemm_kernel<4, false>", FP16_PEAK_TFLOPS, "TFLOP/s")):
         p = prefill.get(key)
         if not p:
             continue
@@ -701,6 +739,7 @@ def main(argv=None):
             "algorithmic_bytes_per_launch": res["bytes_per_launch_avg"],
         },
         "gemv_awq_layout": res["awq_layout"],
+        "gemv_bf16": res["bf16"],
     }
     if not args.no_prefill:
         line["prefill"] = bench_prefill(torch, mq, synth, mq.quant_per_token_int8, args, log)
