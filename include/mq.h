@@ -138,19 +138,20 @@ mq_status mq_w8a8_mm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc,
  * Source: pymllm Setup and Usage, section "W8A8 first-run JIT compilation"
  * (the per-token quantizer feeding the int8 scaled matmul) and Overview.
  * Same result, bit for bit, as mq_quant_per_token_int8 followed by
- * mq_w8a8_scaled_mm. For one or two tokens (M * (K + 16) <= 81920) it is one
- * kernel: every workgroup forms the tokens' scales itself and quantizes the
- * rows into LDS (IEEE binary32 quotient, round half to even, clamp to
- * [-127, 127]), so xq and s_tok never touch memory and no workspace is
- * needed. For larger M it runs the two kernels, with xq and s_tok in
- * `workspace`.
+ * mq_w8a8_scaled_mm. For one token on a wide layer (M = 1, N >= 16384,
+ * K <= 81904) it is one kernel: every workgroup forms the token's scale
+ * itself and quantizes the row into LDS (IEEE binary32 quotient, round half
+ * to even, clamp to [-127, 127]), once for the several channel tiles it
+ * walks, so xq and s_tok never touch memory and the workspace is not used.
+ * Otherwise it runs the two kernels, with xq and s_tok in `workspace`.
  *
  *   x          [M, K] fp16   in,  16-byte aligned
  *   wq, s_ch   as mq_w8a8_scaled_mm
  *   y          [M, N] fp16   out, 16-byte aligned
- *   workspace  >= mq_w8a8_linear_workspace_bytes(M, K) bytes (0 for the
- *              one-kernel cases: may be NULL), 16-byte aligned, not
- *              overlapping any operand; its contents on entry do not matter.
+ *   workspace  >= mq_w8a8_linear_workspace_bytes(M, K) bytes (the size of
+ *              the two-kernel path, which does not depend on N; may be NULL
+ *              in the one-kernel case), 16-byte aligned, not overlapping any
+ *              operand; its contents on entry do not matter.
  * Requires: as mq_w8a8_scaled_mm (K % 16 == 0, K <= 133136).
  */
 size_t mq_w8a8_linear_workspace_bytes(int64_t M, int64_t K);

@@ -74,11 +74,12 @@ def test_quant_bf16_edge_rows():
     assert np.array_equal(host(xq), xq_ref)
     assert np.array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
     assert host(xq)[0, 1:64].tolist() == [k + (k % 2) for k in range(63)]  # k + 1/2 -> even
-    # the one-token fused layer quantizes the same rows inside its kernel
+    # the one-token fused layer (a layer wide enough for it) quantizes the
+    # same rows inside its kernel
     import torch
     rng = np.random.default_rng(3)
-    wq = _dev(rng.integers(-127, 128, size=(64, K)).astype(np.int8))
-    s_ch = _dev(rng.uniform(0.001, 0.01, 64).astype(np.float32))
+    wq = _dev(rng.integers(-127, 128, size=(16384, K)).astype(np.int8))
+    s_ch = _dev(rng.uniform(0.001, 0.01, 16384).astype(np.float32))
     xd = _bf16_dev(bits)
     for r in range(len(rows)):
         y1 = mq.w8a8_linear(xd[r:r + 1].contiguous(), wq, s_ch)

@@ -214,6 +214,10 @@ def test_graph_replays_w8a8_bf16():
     wq_np, s_ch_np = oracle.quant_per_token_int8_ref(d["wf"])
     wq, s_ch = torch.from_numpy(wq_np).cuda(), torch.from_numpy(s_ch_np).cuda()
     xs = [torch.empty((M, K), dtype=torch.bfloat16, device="cuda") for M in (8, 300, 1)]
+    # the one-token layer on a layer wide enough for the fused kernel
+    NW = 16384
+    wq_w = torch.from_numpy(rng.integers(-127, 128, size=(NW, K)).astype(np.int8)).cuda()
+    s_w = torch.from_numpy(rng.uniform(0.001, 0.01, NW).astype(np.float32)).cuda()
 
     def outs():
         o = []
@@ -222,14 +226,14 @@ def test_graph_replays_w8a8_bf16():
             o += [torch.empty((M, K), dtype=torch.int8, device="cuda"),
                   torch.empty((M,), dtype=torch.float32, device="cuda"),
                   torch.empty((M, N), dtype=torch.bfloat16, device="cuda")]
-        o.append(torch.empty((1, N), dtype=torch.bfloat16, device="cuda"))
+        o.append(torch.empty((1, NW), dtype=torch.bfloat16, device="cuda"))
         return o
 
     def run(o):
         for i, x in enumerate(xs[:2]):
             mq.quant_per_token_int8(x, out=o[3 * i], s_out=o[3 * i + 1])
             mq.w8a8_scaled_mm(o[3 * i], o[3 * i + 1], wq, s_ch, out=o[3 * i + 2])
-        mq.w8a8_linear(xs[2], wq, s_ch, out=o[6])
+        mq.w8a8_linear(xs[2], wq_w, s_w, out=o[6])
 
     announce("graph w8a8 bf16")
     static = outs()

@@ -1,12 +1,12 @@
 """W8A8_INT8 linear layer from fp16 activations (mq_w8a8_linear) on an MI355X.
 
-For one or two tokens (while their codes fit 80 KB of LDS) the per-token
-quantizer runs inside the decode kernel (with two tokens a grid of about two
-workgroups per CU walks the channel tiles, each workgroup forming the codes
-once); the result must equal mq_quant_per_token_int8 followed by
-mq_w8a8_scaled_mm bit for bit (same codes, scales and int32 accumulators,
-same epilogue), and the oracle within the fp16 tolerance. For more tokens
-the entry point runs the two kernels through its workspace.
+For one token on a wide layer (N >= 16384, the codes within 80 KB of LDS)
+the per-token quantizer runs inside the decode kernel (a capped grid walks
+the channel tiles, each workgroup forming the codes once); the result must
+equal mq_quant_per_token_int8 followed by mq_w8a8_scaled_mm bit for bit
+(same codes, scales and int32 accumulators, same epilogue), and the oracle
+within the fp16 tolerance. Otherwise the entry point runs the two kernels
+through its workspace.
 """
 
 import numpy as np
@@ -21,6 +21,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 4096), (1, 4096, 6144), (1, 4096, 24576), (1, 12288, 4096),
+                                   (1, 16, 16384), (1, 272, 16392), (1, 1040, 16400), (1, 12288, 16384),
                                    (1, 16, 8), (1, 272, 300), (1, 1040, 37), (1, 81904, 64), (1, 133136, 48),
                                    (4, 4096, 24576), (16, 4096, 4096),
                                    (2, 16, 8), (2, 4096, 24576), (2, 4096, 6144), (2, 12288, 4096),
@@ -44,10 +45,32 @@ def test_w8a8_linear_matches_two_calls_and_oracle(M, K, N):
     assert_fp16_close(y, oracle.w8a8_ref(xq_ref, s_ref, wq, s_ch), f"w8a8_linear M={M} K={K} N={N}")
 
 
+@pytest.mark.parametrize("K", [81904, 65536, 4112])
+def test_w8a8_linear_fused_long_rows(K):
+    # the fused kernel at the longest rows its LDS holds, on a wide layer;
+    # weights are random codes (not from the quantizer) so the test stays
+    # light; bit-identical to the two kernels, the oracle on sampled columns
+    N = 16384
+    rng = np.random.default_rng(K)
+    x = (rng.standard_normal((1, K)) * 0.25).astype(np.float16)
+    wq = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    s_ch = rng.uniform(0.001, 0.01, N).astype(np.float32)
+    tx, tw, ts = dev(x), dev(wq), dev(s_ch)
+    announce(f"w8a8_linear fused long rows K={K}")
+    y = host(mq.w8a8_linear(tx, tw, ts))
+    xq, st = mq.quant_per_token_int8(tx)
+    y2 = host(mq.w8a8_scaled_mm(xq, st, tw, ts))
+    assert np.array_equal(y.view(np.uint16), y2.view(np.uint16)), "fused differs from quant + scaled_mm"
+    cols = rng.choice(N, size=64, replace=False)
+    xq_ref, s_ref = oracle.quant_per_token_int8_ref(x)
+    assert_fp16_close(y[:, cols], oracle.w8a8_ref(xq_ref, s_ref, wq[cols], s_ch[cols]), f"fused K={K}")
+
+
 def test_w8a8_linear_zero_and_tie_rows():
     # an all-zero token (s = 0, codes 0, output row 0) next to rows of exact
-    # ties (x = (j + 0.5) * s for a power-of-two s): the fused quantizer
-    # must round them half to even like the oracle
+    # ties (x = (j + 0.5) * s for a power-of-two s): the quantizer, separate
+    # or fused (one token at a time on a wide layer), must round them half to
+    # even like the oracle
     M, K, N = 5, 256, 96
     d = synth.w8a8_inputs(M, K, N, outlier_frac=0.0, tag=31)
     x = d["x"]
@@ -69,3 +92,11 @@ def test_w8a8_linear_zero_and_tie_rows():
     assert np.array_equal(host(xq), xq_ref)
     y2 = host(mq.w8a8_scaled_mm(xq, st, dev(wq), dev(s_ch)))
     assert np.array_equal(y.view(np.uint16), y2.view(np.uint16))
+    rng = np.random.default_rng(31)
+    ww = dev(rng.integers(-127, 128, size=(16384, K)).astype(np.int8))
+    sw = dev(rng.uniform(0.001, 0.01, 16384).astype(np.float32))
+    for r in range(M):
+        xr = dev(x[r:r + 1])
+        y1 = host(mq.w8a8_linear(xr, ww, sw))
+        q1, s1 = mq.quant_per_token_int8(xr)
+        assert np.array_equal(y1.view(np.uint16), host(mq.w8a8_scaled_mm(q1, s1, ww, sw)).view(np.uint16)), r

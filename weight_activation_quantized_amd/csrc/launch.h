@@ -30,14 +30,18 @@ hipError_t launch_w8a8_gemv(const int8_t* xq, const float* s_tok, const int8_t* 
 
 // Quantizer folded into the decode kernel: y = scaled_mm(quant(x), wq, s_ch)
 // in one launch, bit-identical to the two separate calls, where
-// w8a8_use_fused(M, K): 1 <= M <= kW8A8FusedMaxM and the M x K codes fit a
-// workgroup's 80 KB of LDS. Every workgroup forms all M rows' scales and
-// codes itself (once, walking several channel tiles when M > 1), so the
-// fused form pays only for one or two tokens (measured, 8B layers: 2-3 us
-// faster per layer at M = 1, 0.7-3 us at M = 2 except down, equal there;
-// 1-3 us slower at M = 4 on three of four layers, 5-8 us slower at M = 8).
-constexpr int64_t kW8A8FusedMaxM = 2;
-bool w8a8_use_fused(int64_t M, int64_t K);
+// w8a8_use_fused(M, N, K): one token, a layer wide enough that the capped
+// grid walks several channel tiles per workgroup (N >= kW8A8FusedMinN), and
+// the codes fit a workgroup's 80 KB of LDS. Every workgroup forms the
+// token's scale and codes itself, once for all its tiles; that beats the
+// quantizer launch only when each workgroup has several tiles to amortize it
+// over (measured with the workgroup-per-row quantizer, 8B layers at one
+// token: gate_up 23.3 us fused against 25.3 us in two kernels; qkv 12.0
+// against 11.8, o_proj 9.7 against 8.8, down 21.3 against 16.4; at two
+// tokens the two kernels win or tie on every layer).
+constexpr int64_t kW8A8FusedMaxM = 1;
+constexpr int64_t kW8A8FusedMinN = 16384;
+bool w8a8_use_fused(int64_t M, int64_t N, int64_t K);
 hipError_t launch_w8a8_gemv_fused(const uint16_t* x, const int8_t* wq, const float* s_ch, uint16_t* y,
                                   int64_t M, int64_t N, int64_t K, bool bf16, hipStream_t stream);
 

@@ -399,10 +399,11 @@ mq_status mq_u16_transpose(const uint16_t* src, uint16_t* dst, int64_t A, int64_
   return hip_status(mq::launch_u16_transpose(src, dst, A, B, as_stream(stream)), "u16_transpose launch");
 }
 
+// The workspace does not depend on N: it is sized for the two-kernel path,
+// which every M can take (the one-kernel path for one token on wide layers
+// leaves it unused).
 size_t mq_w8a8_linear_workspace_bytes(int64_t M, int64_t K) {
-  if (M < 0 || M > kMaxDim || K < 16 || K > kMaxKInt8 || K % 16 || M * K > kMaxElems || M == 0 ||
-      mq::w8a8_use_fused(M, K))
-    return 0;
+  if (M < 0 || M > kMaxDim || K < 16 || K > kMaxKInt8 || K % 16 || M * K > kMaxElems || M == 0) return 0;
   return (static_cast<size_t>(M * K) + 255) / 256 * 256 + static_cast<size_t>(M) * 4;
 }
 
@@ -424,7 +425,8 @@ static mq_status linear_impl(const uint16_t* x, const int8_t* wq, const float* s
   if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(y, 16))
     return fail(MQ_ERR_ALIGN, "x, wq and y must be 16-byte aligned");
   if (!aligned(s_ch, 4)) return fail(MQ_ERR_ALIGN, "s_ch must be 4-byte aligned");
-  const size_t ws = mq_w8a8_linear_workspace_bytes(M, K);
+  const bool fused = mq::w8a8_use_fused(M, N, K);
+  const size_t ws = fused ? 0 : mq_w8a8_linear_workspace_bytes(M, K);
   if (noalloc) {
     if (ws > MQ_NOALLOC_SCRATCH_BYTES)
       return fail(MQ_ERR_WORKSPACE, "M*K=%lld needs %zu bytes of scratch; the allocation-free entry holds %zu",
@@ -448,7 +450,7 @@ static mq_status linear_impl(const uint16_t* x, const int8_t* wq, const float* s
     MQ_TRY(hip_status(mq::noalloc_scratch(&workspace), "w8a8_linear_noalloc scratch lookup"));
     workspace_bytes = MQ_NOALLOC_SCRATCH_BYTES;
   }
-  if (mq::w8a8_use_fused(M, K))
+  if (fused)
     return hip_status(mq::launch_w8a8_gemv_fused(x, wq, s_ch, y, M, N, K, bf16, as_stream(stream)),
                       "w8a8_linear launch");
   int8_t* xq = static_cast<int8_t*>(workspace);

@@ -10,7 +10,8 @@
 //
 // x is fp16 or bf16 (both widen exactly to binary32, so the same codes and
 // scales follow from the same arithmetic).
-// One wavefront per row, four rows per workgroup. Each lane holds its share
+// Up to 128 rows: one workgroup per row (quant_row_wg). Otherwise one
+// wavefront per row, four rows per workgroup. Each lane holds its share
 // of the row in registers (16-byte chunks of 8 values), so x is read from HBM
 // exactly once: absmax by a wavefront butterfly, then quantize from registers
 // and store 8 codes per 8-byte store. Rows longer than 64*8*32 elements take
@@ -153,9 +154,64 @@ __global__ __launch_bounds__(256) void quant_rows_stream(const uint16_t* __restr
     *reinterpret_cast<u32x2*>(qr + 8 * c) = quant_chunk<kBf16>(*reinterpret_cast<const u32x4*>(xr + 8 * c), s, r);
 }
 
+// Few rows (decode batches): one workgroup of four wavefronts per row, CPT
+// 16-byte chunks per thread in registers, so a row's loads and codes are
+// spread over 256 lanes instead of 64 and the call's latency shrinks; the
+// absmax is a wavefront butterfly and then a maximum over the four
+// wavefronts through LDS (max is exact and order-free, so s is the same).
+template <int CPT, bool kBf16>
+__global__ __launch_bounds__(256) void quant_row_wg(const uint16_t* __restrict__ x, int8_t* __restrict__ xq,
+                                                    float* __restrict__ s_tok, int M, int K) {
+  __shared__ float wmax[4];
+  const int row = static_cast<int>(blockIdx.x);
+  const int nchunk = K >> 3;
+  const uint16_t* xr = x + static_cast<size_t>(row) * K;
+  int8_t* qr = xq + static_cast<size_t>(row) * K;
+  u32x4 v[CPT];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = static_cast<int>(threadIdx.x) + 256 * i;
+    v[i] = c < nchunk ? *reinterpret_cast<const u32x4*>(xr + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    amax = chunk_absmax<kBf16>(v[i], amax);
+  }
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float s = amax / 127.0f;
+  const float r = code_rcp(s);
+  if (threadIdx.x == 0) s_tok[row] = s;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = static_cast<int>(threadIdx.x) + 256 * i;
+    if (c < nchunk) *reinterpret_cast<u32x2*>(qr + 8 * c) = quant_chunk<kBf16>(v[i], s, r);
+  }
+  (void)M;
+}
+
+// Rows at or below which each row gets a workgroup of its own (fewer rows
+// than CUs leave most of the GPU idle with one wavefront per row).
+constexpr int64_t kRowWgMaxM = 128;
+
 template <bool kBf16>
 hipError_t launch_quant(const uint16_t* x, int8_t* xq, float* s_tok, int64_t M, int64_t K, hipStream_t stream) {
   const int m = static_cast<int>(M), k = static_cast<int>(K);
+  const int per_thread = ((k >> 3) + 255) / 256;
+  if (M <= kRowWgMaxM && per_thread <= 8) {
+    const dim3 grid(static_cast<uint32_t>(m)), block(256);
+    switch (per_thread) {
+      case 1:
+        return launch_kernel(quant_row_wg<1, kBf16>, grid, block, 0, stream, x, xq, s_tok, m, k);
+      case 2:
+        return launch_kernel(quant_row_wg<2, kBf16>, grid, block, 0, stream, x, xq, s_tok, m, k);
+      case 3:
+      case 4:
+        return launch_kernel(quant_row_wg<4, kBf16>, grid, block, 0, stream, x, xq, s_tok, m, k);
+      default:
+        return launch_kernel(quant_row_wg<8, kBf16>, grid, block, 0, stream, x, xq, s_tok, m, k);
+    }
+  }
   const dim3 grid((m + kRowsPerBlock - 1) / kRowsPerBlock), block(256);
   const int per_lane = ((k >> 3) + kWave - 1) / kWave;
   if (per_lane <= 1) {

@@ -195,20 +195,16 @@ __device__ __forceinline__ float fused_code(float v, float s, float r) {
 constexpr int kFusedLds = 80 * 1024;  // most bytes of codes a workgroup holds: M * (K + 16)
 // Workgroups of the fused kernel: a grid of at most this many walks the
 // tiles (measured, 24576 x 4096: one token 28.5 us with a workgroup per
-// tile, 23.6 us with 1024; two tokens 25.1 us with 512; the narrower layers
-// have fewer tiles than either cap).
-constexpr int64_t kFusedGridCap1 = 1024;
-constexpr int64_t kFusedGridCap = 512;
+// tile, 23.6 us with 1024).
+constexpr int64_t kFusedGridCap = 1024;
 
 // A workgroup takes all M <= 16 tokens and the 16-channel tiles blockIdx.x,
 // blockIdx.x + gridDim.x, ... Prologue (once per workgroup): the M
 // per-token scales, then the codes of all M x K activations into LDS (row
 // pitch K + 16 bytes, so the 16 token rows of a fragment read fall on
 // different bank groups). Per tile: as w8a8_gemv_kernel, with the B
-// fragments read from LDS. With one token the grid has a workgroup per tile;
-// with more, a grid of about two workgroups per CU walks the tiles, so the
-// codes are formed once per workgroup rather than once per tile, and x is
-// read from L2 once per workgroup instead of once per tile.
+// fragments read from LDS. The grid is capped, so a wide layer's workgroups
+// walk several tiles and form the codes once for all of them.
 template <bool kBf16>
 __global__ __launch_bounds__(256) void w8a8_gemv_fused_kernel(const uint16_t* __restrict__ x,
                                                               const int8_t* __restrict__ wq,
@@ -361,15 +357,15 @@ bool w8a8_use_gemv(int64_t M, int64_t N) {
   return M <= kW8A8GemvMaxM && N < 16384;
 }
 
-bool w8a8_use_fused(int64_t M, int64_t K) {
-  return M >= 1 && M <= kW8A8FusedMaxM && M * (K + 16) <= kFusedLds;
+bool w8a8_use_fused(int64_t M, int64_t N, int64_t K) {
+  return M >= 1 && M <= kW8A8FusedMaxM && N >= kW8A8FusedMinN && M * (K + 16) <= kFusedLds;
 }
 
 hipError_t launch_w8a8_gemv_fused(const uint16_t* x, const int8_t* wq, const float* s_ch, uint16_t* y,
                                   int64_t M, int64_t N, int64_t K, bool bf16, hipStream_t stream) {
-  if (!w8a8_use_fused(M, K)) return hipErrorInvalidValue;
+  if (!w8a8_use_fused(M, N, K)) return hipErrorInvalidValue;
   const int64_t tiles = (N + 15) / 16;
-  const int64_t cap = M == 1 ? kFusedGridCap1 : kFusedGridCap;
+  const int64_t cap = kFusedGridCap;
   const dim3 grid(static_cast<uint32_t>(tiles < cap ? tiles : cap)), block(256);
   const size_t lds = static_cast<size_t>(M * (K + 16));
   if (bf16)
