@@ -10,27 +10,31 @@
 //
 // Design:
 // - v_mfma_f32_32x32x16_f16 (on gfx950 about 1.5x the rate of the 16x16x32
-//   form). A workgroup computes 64 tokens x 1024 outputs with eight
-//   wavefronts side by side in N, two per SIMD; a wavefront owns 64 x 128
-//   (two 32-token A fragments x four B tiles, 128 fp32 accumulators per
-//   lane), so every weight is dequantized exactly once per workgroup and one
-//   wavefront's unpack overlaps the other's MFMAs on each SIMD.
-// - B tiles: lane (j = lane%32, h = lane/32) takes packed column j%16 of the
-//   wavefront's 16 and field parity j/16; it reads that column's words of
-//   rows 8h..8h+7 of a 16-row k-step and unpacks its four fields
-//   p = 2q + j/16 into four fp16 fragments, so tile q covers fields 2q and
-//   2q + 1 of the 16 columns. A field in bits 0-3 of a 16-bit half, OR-ed
-//   into the pattern of 1024.0, reads as 1024 + q; a field in bits 4-7,
-//   OR-ed into the pattern of 64.0, reads as 64 + q (the mantissa step at
-//   64 is 1/16). Subtracting 1024 + z (64 + z) leaves q - z exactly, and the
-//   one multiply by s rounds each weight once, to fp16((q - z) * s), for
-//   every fp16 scale (subnormal products included).
+//   form). A workgroup computes 128 tokens x 512 outputs with eight
+//   wavefronts side by side in N, two per SIMD; a wavefront owns 128 x 64
+//   (four 32-token A fragments x two B tiles, 128 fp32 accumulators per
+//   lane), so every weight is dequantized exactly once per workgroup and
+//   each dequantized fragment feeds four MFMAs. The unpack arithmetic is
+//   what bounds this kernel (the MFMAs of a k-step take 8 x 32 cycles per
+//   wavefront, its unpack about 4 vector operations per MFMA), and with two
+//   wavefronts per SIMD one's unpack runs under the other's MFMAs.
+// - B tiles: lane (j = lane%32, h = lane/32) of tile t takes packed column
+//   j%8 of the wavefront's 8 and field f = j/8 + 4t, rows 8h..8h+7 of a
+//   16-row k-step. Field f sits in byte f/2 of a word (low nibble for even
+//   f, high for odd), so for each row pair one byte permute per tile moves
+//   that byte of the two rows into the two fp16 halves. A field in bits 0-3
+//   of a half, OR-ed into the pattern of 1024.0, reads as 1024 + q; a field
+//   in bits 4-7, OR-ed into the pattern of 64.0, reads as 64 + q (the
+//   mantissa step at 64 is 1/16). Subtracting 1024 + z (64 + z) leaves
+//   q - z exactly, and the one multiply by s rounds each weight once, to
+//   fp16((q - z) * s), for every fp16 scale (subnormal products included).
 // - Everything moves HBM -> LDS with buffer_load ... lds through a ring of
 //   kStages 32-row stages: the x rows (shared by all wavefronts) and, per
 //   32-column area, its raw packed words, scales and zero points. The first
-//   four wavefronts issue all the fills, one area each; the other four only
-//   compute. Loads past a buffer descriptor's size return zero (ragged M);
-//   columns past N read valid memory and are never stored.
+//   four wavefronts issue all the fills (32 x rows and half an area's weight
+//   rows each); the other four only compute. Loads past a buffer
+//   descriptor's size return zero (ragged M); columns past N read valid
+//   memory and are never stored.
 // - x rows are 64 bytes per stage with the 16-byte chunk index XOR-swizzled
 //   by the row (conflict-free fragment reads). Raw weight rows are 128
 //   bytes; k-row r is stored at LDS row r with bits 0 and 3 swapped, so the
@@ -45,27 +49,30 @@
 namespace mq {
 namespace {
 
-constexpr int kBM = 64;         // tokens per workgroup tile
-constexpr int kAreas = 4;       // DMA areas of 32 packed columns (128-byte weight rows)
+constexpr int kBM = 128;        // tokens per workgroup tile
+constexpr int kAreas = 2;       // DMA areas of 32 packed columns (128-byte weight rows)
 constexpr int kAreaCols = 32;   // packed columns per area
-constexpr int kTileCols = kAreas * kAreaCols;  // 128 packed columns (1024 outputs)
-constexpr int kWaves = 8;       // two per area (16 packed columns each), two per SIMD
-constexpr int kWaveCols = 16;   // packed columns per wavefront
+constexpr int kTileCols = kAreas * kAreaCols;  // 64 packed columns (512 outputs)
+constexpr int kWaves = 8;       // four per area (8 packed columns each), two per SIMD
+constexpr int kWaveCols = 8;    // packed columns per wavefront
+constexpr int kFillers = 4;     // wavefronts that issue the fills
+constexpr int kAFrags = kBM / 32;  // 32-token A fragments per wavefront
 constexpr int kThreads = kWaves * 64;
 constexpr int kRows = 32;       // K rows per stage (two 16-row MFMA k-steps)
-constexpr int kStages = 6;      // LDS ring depth (stages)
-constexpr int kABytes = kBM * kRows * 2;         // x rows: 64 x 64 B
+constexpr int kStages = 8;      // LDS ring depth (stages)
+constexpr int kABytes = kBM * kRows * 2;         // x rows: 128 x 64 B
 constexpr int kBBytes = kRows * kAreaCols * 4;   // an area's raw words: 32 x 128 B
 constexpr int kSBytes = 1024;                    // an area's scales (512 B used)
 constexpr int kZBytes = 256;                     // an area's zero points (128 B used)
 constexpr int kAreaBytes = kBBytes + kSBytes + kZBytes;
 constexpr int kSlotBytes = kABytes + kAreas * kAreaBytes;
-constexpr int kLoadsW = 5;  // per filling wavefront (one per area) and stage: 1 x, 4 weights
-                            // (+ 1 scales and 1 zero-point load at a group's first stage)
+constexpr int kLoadsW = 4;  // per filling wavefront and stage: 2 x, 2 weights
+                            // (+ 1 scales or zero-point load at a group's first stage)
 constexpr int kOutPitch = kTileCols * 8 * 2 + 16;  // bytes per staged output row
-static_assert(kStages >= 2 && (kStages - 1) * (kLoadsW + 2) < 64, "ring depth / vmcnt range");
+static_assert(kStages >= 2 && (kStages - 1) * (kLoadsW + 1) < 64, "ring depth / vmcnt range");
 static_assert(kStages * kSlotBytes <= 160 * 1024, "LDS capacity");
 static_assert(kBM * kOutPitch <= kStages * kSlotBytes, "output staging fits the ring");
+static_assert(kFillers * 2 * 16 == kBM && kFillers == 2 * kAreas, "fill split: 32 x rows, half an area each");
 
 constexpr int kBufferFlags = 0x00020000;  // gfx9 buffer descriptor word 3 (raw 32-bit data)
 
@@ -86,78 +93,105 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(n), kBufferFlags);
 }
 
-// A lane handles one 4-bit field parity par (lanes 16-31 of each half-wave
-// the odd fields): its four fields are p = 2q + par, q = 0..3.
-struct GroupParams {
-  uint32_t negz[4];  // -(1024 + z_p) (even p) or -(64 + z_p) (odd p), both halves
-  uint32_t sc2[4];   // s_p, both halves
+// What a lane needs to unpack its fields: field f_t = f0 + 4t (t = 0, 1)
+// of its packed column sits in byte f0/2 + 2t of a word, in the low nibble
+// for even f0 and the high one for odd f0 (par). sel[t] is the byte-permute
+// selector that moves that byte of rows e and e + 1 into bytes 0 and 2;
+// mask keeps the field's nibble in each half and magic is the pattern of
+// 1024.0 (low nibble) or 64.0 (high nibble).
+struct LaneFields {
+  uint32_t sel[2];
+  uint32_t mask, magic;
+  int f0, par;
 };
 
-// Zero point z of field p sits in bits 0-3 (even p) or 4-7 (odd p) of byte
-// p / 2 of zw: OR-ed into the sign and exponent of -1024.0 (0xE400) or
-// -64.0 (0xD400) it reads as -(1024 + z) or -(64 + z), the same encodings
-// as the weight fields.
-// bf16 activations (kBF): the weight is formed in binary32 and rounded once
-// to bf16 instead; negz[q] then holds the binary32 bits of
-// -(1024 + z) * s (or -(64 + z) * s) and sc2[q] those of s, both exact
-// (an 11-bit integer times an 11-bit significand).
-template <bool kBF>
-__device__ __forceinline__ void make_group_params(uint32_t zw, u32x4 sv, int par, GroupParams& gp) {
-  const uint32_t zmask = par ? 0xF0u : 0x0Fu;
-  const uint32_t zbase = par ? 0xD400u : 0xE400u;
+__device__ __forceinline__ LaneFields lane_fields(int f0) {
+  LaneFields lf;
+  lf.f0 = f0;
+  lf.par = f0 & 1;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const f16x2 s2 = as_f16x2(sv[q]);
+  for (int t = 0; t < 2; ++t) {
+    const uint32_t b = static_cast<uint32_t>((f0 >> 1) + 2 * t);
+    lf.sel[t] = b | (0x0Cu << 8) | ((4u + b) << 16) | (0x0Cu << 24);  // 0x0C selects a zero byte
+  }
+  uint32_t mlo, mhi, glo, ghi;
+  asm("v_mov_b32 %0, 0x000f000f" : "=v"(mlo));
+  asm("v_mov_b32 %0, 0x00f000f0" : "=v"(mhi));
+  asm("v_mov_b32 %0, 0x64006400" : "=v"(glo));  // 1024.0: a field in bits 0-3 reads 1024 + q
+  asm("v_mov_b32 %0, 0x54005400" : "=v"(ghi));  // 64.0: a field in bits 4-7 reads 64 + q
+  lf.mask = lf.par ? mhi : mlo;
+  lf.magic = lf.par ? ghi : glo;
+  return lf;
+}
+
+// Per group and tile t: negz[t] = -(1024 + z) (even f0) or -(64 + z) (odd
+// f0) in both fp16 halves, and sc2[t] = s in both halves.
+// bf16 activations (kBF): the weight is formed in binary32 and rounded once
+// to bf16 instead; negz[t] then holds the binary32 bits of -(1024 + z) * s
+// (or -(64 + z) * s) and sc2[t] those of s, both exact (an 11-bit integer
+// times an 11-bit significand).
+struct GroupParams {
+  uint32_t negz[2];
+  uint32_t sc2[2];
+};
+
+// Zero point z of field f sits in bits 4f..4f+3 of zw: the byte f/2 masked
+// to its nibble and OR-ed into the sign and exponent of -1024.0 (0xE400) or
+// -64.0 (0xD400) reads as -(1024 + z) or -(64 + z), the same encodings as
+// the weight fields. sd[t] is the scale word holding field f_t's scale in
+// half par.
+template <bool kBF>
+__device__ __forceinline__ void make_group_params(uint32_t zw, const uint32_t (&sd)[2], const LaneFields& lf,
+                                                  GroupParams& gp) {
+  const uint32_t zmask = lf.par ? 0xF0u : 0x0Fu;
+  const uint32_t zbase = lf.par ? 0xD400u : 0xE400u;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint32_t sh = (sd[t] >> (16 * lf.par)) & 0xFFFFu;  // the field's fp16 scale
+    const int byte = (lf.f0 >> 1) + 2 * t;
     if constexpr (kBF) {
-      const float sf = static_cast<float>(s2[par]);
-      const uint32_t zf = (zw >> (8 * q + 4 * par)) & 15u;
-      const float off = par ? 64.0f : 1024.0f;
-      gp.negz[q] = __builtin_bit_cast(uint32_t, -(off + static_cast<float>(zf)) * sf);
-      gp.sc2[q] = __builtin_bit_cast(uint32_t, sf);
+      const float sf = static_cast<float>(__builtin_bit_cast(f16, static_cast<uint16_t>(sh)));
+      const uint32_t zf = (zw >> (8 * byte + 4 * lf.par)) & 15u;
+      const float off = lf.par ? 64.0f : 1024.0f;
+      gp.negz[t] = __builtin_bit_cast(uint32_t, -(off + static_cast<float>(zf)) * sf);
+      gp.sc2[t] = __builtin_bit_cast(uint32_t, sf);
     } else {
-      const uint32_t e = ((zw >> (8 * q)) & zmask) | zbase;
-      gp.negz[q] = e | (e << 16);
-      f16x2 rep;
-      rep[0] = s2[par];
-      rep[1] = s2[par];
-      gp.sc2[q] = as_u32(rep);
+      const uint32_t e = ((zw >> (8 * byte)) & zmask) | zbase;
+      gp.negz[t] = e | (e << 16);
+      gp.sc2[t] = sh | (sh << 16);
     }
   }
 }
 
-// Fragments fp16((q - z) * s) of the lane's four fields for one 16-row
-// k-step: w[e] is the lane's word of row 8h + e. The byte permute gathers
-// bytes 0-1 (2-3) of a row pair; field p sits in byte p / 2 of a word, low
-// nibble for even p, high nibble for odd p, selected by the lane's mask;
-// the lane's magic (1024.0 or 64.0) makes either read as an offset q.
+// Fragments fp16((q - z) * s) of the lane's two fields for one 16-row
+// k-step: w[e] is the lane's word of row 8h + e. For each row pair one byte
+// permute per tile gathers the field's byte of both rows, one v_and_or_b32
+// keeps the nibble under the magic pattern, and a packed add and multiply
+// subtract the zero point and apply the scale.
 // kBF: the offset integer (an exact fp16) times s plus -(offset + z) * s in
 // one binary32 fused multiply-add (v_fma_mix_f32 reads the fp16 half
 // directly) is exactly (q - z) * s, rounded once to bf16 by the pair
 // conversion.
 template <bool kBF>
-__device__ __forceinline__ void unpack_fields(const uint32_t (&w)[8], const GroupParams& gp, uint32_t mask,
-                                              uint32_t magic, f16x8 (&b)[4]) {
+__device__ __forceinline__ void unpack_fields(const uint32_t (&w)[8], const GroupParams& gp, const LaneFields& lf,
+                                              f16x8 (&b)[2]) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const uint32_t lo = byte_perm(w[2 * t + 1], w[2 * t], 0x05040100u);
-    const uint32_t hi = byte_perm(w[2 * t + 1], w[2 * t], 0x07060302u);
-    const uint32_t src[4] = {lo, lo >> 8, hi, hi >> 8};
+  for (int p = 0; p < 4; ++p)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t v = (src[q] & mask) | magic;
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t v = (byte_perm(w[2 * p + 1], w[2 * p], lf.sel[t]) & lf.mask) | lf.magic;
       f16x2 d;
       if constexpr (kBF) {
         const f16x2 o = as_f16x2(v);
-        const float sf = __builtin_bit_cast(float, gp.sc2[q]);
-        const float cf = __builtin_bit_cast(float, gp.negz[q]);
+        const float sf = __builtin_bit_cast(float, gp.sc2[t]);
+        const float cf = __builtin_bit_cast(float, gp.negz[t]);
         d = as_f16x2(bf16x2_bits(fmaf(static_cast<float>(o[0]), sf, cf), fmaf(static_cast<float>(o[1]), sf, cf)));
       } else {
-        d = (as_f16x2(v) + as_f16x2(gp.negz[q])) * as_f16x2(gp.sc2[q]);
+        d = (as_f16x2(v) + as_f16x2(gp.negz[t])) * as_f16x2(gp.sc2[t]);
       }
-      b[q][2 * t] = d[0];
-      b[q][2 * t + 1] = d[1];
+      b[t][2 * p] = d[0];
+      b[t][2 * p + 1] = d[1];
     }
-  }
 }
 
 // kSPG = 32-row stages per group (group size 32 kSPG).
@@ -201,22 +235,33 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
   // or, past the last row, zero.
   const __amdgpu_buffer_rsrc_t rx = rsrc(x + static_cast<size_t>(m0) * K, static_cast<int64_t>(min(kBM, M - m0)) * K * 2);
 
-  // DMA: wavefront a < kAreas fills area a (packed columns 32a .. 32a+31) and
-  // x rows 16a .. 16a+15 of every stage; the other four only compute.
-  const bool filler = wave < kAreas;
-  const int fa = filler ? wave : 0;
-  //  x: lane L -> row 16a + L/4, physical chunk L%4, which holds logical
-  //     chunk (L%4) ^ swizzle(row).
-  const int xa_row = 16 * fa + lane / 4;
-  const uint32_t xa_off = static_cast<uint32_t>(xa_row * K + 8 * ((lane % 4) ^ chunk_swizzle(xa_row))) * 2u;
-  //  weights: load u fills LDS rows 8u .. 8u+7 of the area; lane L -> LDS
-  //     row 8u + L/8 = k-row raw_row(.), 16-byte chunk L%8 (words 4(L%8)..).
-  uint32_t wr_off[4];
+  // DMA: wavefront f < kFillers fills x rows 32f .. 32f+31 and weight rows
+  // 16(f%2) .. 16(f%2)+15 of area f/2 of every stage, and at a group's first
+  // stage that area's scales (f even) or zero points (f odd); the other four
+  // only compute.
+  const bool filler = wave < kFillers;
+  const int ff = filler ? wave : 0;
+  const int fa = ff >> 1;  // area
+  //  x: load u fills rows 32f + 16u .. +15; lane L -> row 32f + 16u + L/4,
+  //     physical chunk L%4, which holds logical chunk (L%4) ^ swizzle(row).
+  uint32_t xa_off[2];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-    wr_off[u] = static_cast<uint32_t>(raw_row(8 * u + lane / 8) * NP + kAreaCols * fa + 4 * (lane % 8)) * 4u;
+  for (int u = 0; u < 2; ++u) {
+    const int row = 32 * ff + 16 * u + lane / 4;
+    xa_off[u] = static_cast<uint32_t>(row * K + 8 * ((lane % 4) ^ chunk_swizzle(row))) * 2u;
+  }
+  //  weights: load u fills LDS rows 8v .. 8v+7 of the area (v = 2(f%2) + u);
+  //     lane L -> LDS row 8v + L/8 = k-row raw_row(.), 16-byte chunk L%8
+  //     (words 4(L%8)..).
+  uint32_t wr_off[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int v = 2 * (ff & 1) + u;
+    wr_off[u] = static_cast<uint32_t>(raw_row(8 * v + lane / 8) * NP + kAreaCols * fa + 4 * (lane % 8)) * 4u;
+  }
   //  scales: lane L -> the 8 scales of packed column (L % 32) of the area;
   //  zero points: lane L -> word (L % 32).
+  const bool fills_scales = (ff & 1) == 0;
   const uint32_t s_off = static_cast<uint32_t>(8 * (kAreaCols * fa + lane % 32)) * 2u;
   const uint32_t z_off = static_cast<uint32_t>(kAreaCols * fa + lane % 32) * 4u;
   lds_i8* const fill_area = sm + kABytes + fa * kAreaBytes;  // + slot offset
@@ -228,68 +273,63 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
     const int so_ = ((ST) % kStages) * kSlotBytes;                                                   \
     const __amdgpu_buffer_rsrc_t rw_ =                                                               \
         rsrc(qw + static_cast<size_t>(k0_) * NP + c0, (static_cast<int64_t>(K - k0_) * NP - c0) * 4); \
-    const __amdgpu_buffer_rsrc_t rs_ = rsrc(scales + static_cast<size_t>(g_) * N + c0 * 8,           \
-                                            (static_cast<int64_t>(G - g_) * N - c0 * 8) * 2);         \
-    const __amdgpu_buffer_rsrc_t rz_ =                                                               \
-        rsrc(qz + static_cast<size_t>(g_) * NP + c0, (static_cast<int64_t>(G - g_) * NP - c0) * 4);  \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(sm + so_ + fa * 1024), 16,              \
-                                             xa_off + k0_ * 2, 0, 0, 0);                             \
-    _Pragma("unroll") for (int u = 0; u < 4; ++u)                                                    \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw_, (lds_void*)(fill_area + so_ + u * 1024), 16,   \
-                                                 wr_off[u], 0, 0, 0);                                \
+    _Pragma("unroll") for (int u = 0; u < 2; ++u)                                                    \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(sm + so_ + (2 * ff + u) * 1024), 16, \
+                                                 xa_off[u] + k0_ * 2, 0, 0, 0);                      \
+    _Pragma("unroll") for (int u = 0; u < 2; ++u)                                                    \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                    \
+            rw_, (lds_void*)(fill_area + so_ + (2 * (ff & 1) + u) * 1024), 16, wr_off[u], 0, 0, 0);  \
     if (SZ) {                                                                                        \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (lds_void*)(fill_area + so_ + kBBytes), 16,      \
-                                               s_off, 0, 0, 0);                                      \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rz_, (lds_void*)(fill_area + so_ + kBBytes + kSBytes), \
-                                               4, z_off, 0, 0, 0);                                   \
+      if (fills_scales) {                                                                            \
+        const __amdgpu_buffer_rsrc_t rs_ = rsrc(scales + static_cast<size_t>(g_) * N + c0 * 8,       \
+                                                (static_cast<int64_t>(G - g_) * N - c0 * 8) * 2);     \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (lds_void*)(fill_area + so_ + kBBytes), 16,    \
+                                                 s_off, 0, 0, 0);                                    \
+      } else {                                                                                       \
+        const __amdgpu_buffer_rsrc_t rz_ = rsrc(qz + static_cast<size_t>(g_) * NP + c0,              \
+                                                (static_cast<int64_t>(G - g_) * NP - c0) * 4);       \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rz_, (lds_void*)(fill_area + so_ + kBBytes + kSBytes), \
+                                                 4, z_off, 0, 0, 0);                                 \
+      }                                                                                              \
     }                                                                                                \
   } while (0)
 
-  // Compute: wavefront w takes packed columns 16w .. 16w+15 of the tile (half
-  // w % 2 of area w / 2). Lane (j = lane%32, h = lane/32) of a B fragment
-  // takes packed column 16w + j%16 and field parity par = j / 16, so MFMA
-  // tile q covers fields 2q (lanes j < 16) and 2q + 1 (j >= 16) of the
-  // wavefront's 16 columns: the eight fields of 16 columns in four tiles.
+  // Compute: wavefront w takes packed columns 8w .. 8w+7 of the tile
+  // (columns 8(w % 4) .. of area w / 4). Lane (j = lane%32, h = lane/32) of
+  // B tile t takes packed column 8w + j%8 and field j/8 + 4t, so the two
+  // tiles cover the eight fields of the wavefront's 8 columns.
   const int fi = lane & 31, fh = lane >> 5;
-  const int par = fi >> 4;
-  const int col_in_area = 16 * (wave & 1) + (fi & 15);
-  // x fragments: row fi (+32) of the tile, k-step t -> logical chunk 2t + fh.
-  int xoff[2][2];
+  const int col_in_area = kWaveCols * (wave & 3) + (fi & 7);
+  const LaneFields lf = lane_fields(fi >> 3);
+  // x fragments: row fi (+32a) of the tile, k-step t -> logical chunk 2t + fh.
+  int xoff[kAFrags][2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < kAFrags; ++a)
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int row = 32 * a + fi;
       xoff[a][t] = row * 64 + 16 * ((2 * t + fh) ^ chunk_swizzle(row));
     }
   // raw words: k-row 16t + 8fh + e of the lane's packed column.
-  const int area = kABytes + (wave >> 1) * kAreaBytes;
+  const int area = kABytes + (wave >> 2) * kAreaBytes;
   const int wbase = area + 4 * col_in_area;
-  uint32_t mask, magic;
-  {
-    uint32_t mlo, mhi, glo, ghi;
-    asm("v_mov_b32 %0, 0x000f000f" : "=v"(mlo));
-    asm("v_mov_b32 %0, 0x00f000f0" : "=v"(mhi));
-    asm("v_mov_b32 %0, 0x64006400" : "=v"(glo));  // 1024.0: a field in bits 0-3 reads 1024 + q
-    asm("v_mov_b32 %0, 0x54005400" : "=v"(ghi));  // 64.0: a field in bits 4-7 reads 64 + q
-    mask = par ? mhi : mlo;
-    magic = par ? ghi : glo;
-  }
+  // the lane's two scale words (fields f0 and f0 + 4 of its column)
+  const int sbase = area + kBBytes + 16 * col_in_area + 4 * (lf.f0 >> 1);
 
-  f32x16 acc[2][4];
+  f32x16 acc[kAFrags][2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < kAFrags; ++a)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[a][q] = f32x16{};
+    for (int t = 0; t < 2; ++t) acc[a][t] = f32x16{};
 
   const int nst = k_len / kRows;
 
-  // Operands of one 16-row k-step: the two x fragments and the four
+  // Operands of one 16-row k-step: the four x fragments and the two
   // dequantized weight fragments.
 #define MQ_READ_A(S, T, AF)                                                                      \
   do {                                                                                           \
     const lds_i8* const sl_ = sm + ((S) % kStages) * kSlotBytes;                                 \
-    _Pragma("unroll") for (int a = 0; a < 2; ++a) AF[a] = *(const lds_f16x8*)(sl_ + xoff[a][T]);  \
+    _Pragma("unroll") for (int a = 0; a < kAFrags; ++a) AF[a] = *(const lds_f16x8*)(sl_ + xoff[a][T]); \
   } while (0)
 #define MQ_READ_W(S, T, W)                                                                       \
   do {                                                                                           \
@@ -300,19 +340,19 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
 #define MQ_READ_GP(S, GP)                                                                        \
   do {                                                                                           \
     const lds_i8* const sl_ = sm + ((S) % kStages) * kSlotBytes;                                 \
-    const u32x4 sv_ = *(const lds_u32x4*)(sl_ + area + kBBytes + 16 * col_in_area);              \
+    const uint32_t sd_[2] = {*(const lds_word*)(sl_ + sbase), *(const lds_word*)(sl_ + sbase + 8)}; \
     const uint32_t zw_ = *(const lds_word*)(sl_ + area + kBBytes + kSBytes + 4 * col_in_area);   \
-    make_group_params<kBF>(zw_, sv_, par, GP);                                                        \
+    make_group_params<kBF>(zw_, sd_, lf, GP);                                                    \
   } while (0)
 #define MQ_MFMAS(AF, B)                                                                          \
   do {                                                                                           \
-    _Pragma("unroll") for (int a = 0; a < 2; ++a) _Pragma("unroll") for (int q = 0; q < 4; ++q)  \
-        acc[a][q] = mfma_32x32x16<kBF>(AF[a], B[q], acc[a][q]);     \
+    _Pragma("unroll") for (int a = 0; a < kAFrags; ++a) _Pragma("unroll") for (int t = 0; t < 2; ++t) \
+        acc[a][t] = mfma_32x32x16<kBF>(AF[a], B[t], acc[a][t]);                                  \
   } while (0)
 // Keeps the unpacked fragments in the block that computes them (otherwise
 // they are sunk next to their use, out of reach of the MFMAs they are meant
 // to overlap).
-#define MQ_PIN(B) _Pragma("unroll") for (int q_ = 0; q_ < 4; ++q_) asm volatile("" : "+v"(B[q_]))
+#define MQ_PIN(B) _Pragma("unroll") for (int t_ = 0; t_ < 2; ++t_) asm volatile("" : "+v"(B[t_]))
 // Schedule of a block: its LDS reads first, then the 8 MFMAs each followed
 // by a share of the unpack arithmetic.
 #define MQ_INTERLEAVE(NDS, NVALU)                                                                \
@@ -334,14 +374,14 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
   // first stage only and turned into the lanes' factors once per group. The
   // stage loop runs four stages per iteration, unrolled, so which stages
   // start a group is known at compile time (K % 128 == 0).
-  // Wait counts: a stage carries kLoadsW loads, plus 2 when it starts a
-  // group. Stages 1-5 may stay in flight after the prologue; stages s+2 ..
-  // s+5 in the loop, four consecutive stages of which exactly 4 / kSPG start
-  // a group.
-  static_assert(kStages == 6, "wait counts below assume 6 stages");
-  constexpr int kStartsIn1to5 = kSPG == 1 ? 5 : (kSPG == 2 ? 2 : 1);
-  constexpr int kWaitPrologue = 5 * kLoadsW + 2 * kStartsIn1to5;
-  constexpr int kWaitLoop = 4 * kLoadsW + 2 * (4 / kSPG);
+  // Wait counts: a stage carries kLoadsW loads, plus 1 when it starts a
+  // group. After the prologue stages 1 .. kStages-1 may stay in flight; in
+  // the loop stages s+2 .. s+kStages-1. Any run of n consecutive stages
+  // holds at least n / kSPG group starts, so waiting down to that many
+  // loads never leaves a load of stage s + 1 outstanding (at most one load
+  // of stage s + 2 is waited for too early).
+  constexpr int kWaitPrologue = (kStages - 1) * kLoadsW + (kStages - 1) / kSPG;
+  constexpr int kWaitLoop = (kStages - 2) * kLoadsW + (kStages - 2) / kSPG;
   static_assert(kWaitPrologue < 64 && kWaitLoop < 64, "vmcnt range");
   if (filler) {
 #pragma unroll
@@ -356,29 +396,29 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
   bare_barrier();
 
   GroupParams gp;
-  f16x8 a0[2], b0[4];
+  f16x8 a0[kAFrags], b0[2];
   {
     uint32_t w[8];
     MQ_READ_GP(0, gp);
     MQ_READ_A(0, 0, a0);
     MQ_READ_W(0, 0, w);
-    unpack_fields<kBF>(w, gp, mask, magic, b0);
+    unpack_fields<kBF>(w, gp, lf, b0);
   }
   for (int s0 = 0; s0 < nst; s0 += 4) {
 #pragma unroll
     for (int ss = 0; ss < 4; ++ss) {
       const int s = s0 + ss;
       // k-step 1 of stage s: unpack while k-step 0's MFMAs run.
-      f16x8 a1[2], b1[4];
+      f16x8 a1[kAFrags], b1[2];
       {
         __builtin_amdgcn_sched_barrier(0);
         uint32_t w[8];
         MQ_READ_A(s, 1, a1);
         MQ_READ_W(s, 1, w);
-        unpack_fields<kBF>(w, gp, mask, magic, b1);
+        unpack_fields<kBF>(w, gp, lf, b1);
         MQ_MFMAS(a0, b0);
         MQ_PIN(b1);
-        MQ_INTERLEAVE(10, kBF ? 10 : 8);
+        MQ_INTERLEAVE(12, kBF ? 5 : 4);
         __builtin_amdgcn_sched_barrier(0);
       }
       // Stage s + 1 must have landed (every filler's share), and every wave
@@ -400,13 +440,13 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
         if (new_group) MQ_READ_GP(s + 1, gp);
         MQ_READ_A(s + 1, 0, a0);
         MQ_READ_W(s + 1, 0, w);
-        unpack_fields<kBF>(w, gp, mask, magic, b0);
+        unpack_fields<kBF>(w, gp, lf, b0);
         MQ_MFMAS(a1, b1);
         MQ_PIN(b0);
         if (new_group) {
-          MQ_INTERLEAVE(12, kBF ? 12 : 10);
+          MQ_INTERLEAVE(15, kBF ? 6 : 5);
         } else {
-          MQ_INTERLEAVE(10, kBF ? 10 : 8);
+          MQ_INTERLEAVE(12, kBF ? 5 : 4);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -421,25 +461,25 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
 #undef MQ_ISSUE
 
   // Epilogue. D[m][j] of a 32x32 tile: lane (jj, hh) register r holds token
-  // 8 (r / 4) + 4 hh + r % 4 of B column jj, i.e. output 8 (16 w + jj % 16)
-  // + 2 q + jj / 16 of the tile. The tile is staged in LDS as fp16 and
-  // written out as whole rows with 16-byte stores (fp32 partial sums: two
-  // halves of 32 rows, staged and written the same way).
+  // 8 (r / 4) + 4 hh + r % 4 of B column jj, i.e. output 8 (8 w + jj % 8)
+  // + jj / 8 + 4 t of the tile. The tile is staged in LDS as fp16 and
+  // written out as whole rows with 16-byte stores (fp32 partial sums: 32
+  // rows at a time, staged and written the same way).
   wait_counts<0, 0>();
   bare_barrier();  // every wave is done reading the ring
+  const int jj = lane & 31, hh = lane >> 5;
+  const int ncol = 8 * (kWaveCols * wave + (jj & 7)) + (jj >> 3);
   if (splits > 1) {
     constexpr int kPitch32 = kTileCols * 8 * 4 + 16;  // bytes per staged fp32 row
-    static_assert(32 * kPitch32 <= kStages * kSlotBytes, "fp32 half tile fits the ring");
-    const int jj = lane & 31, hh = lane >> 5;
-    const int ncol = 8 * (kWaveCols * wave + (jj & 15)) + (jj >> 4);
+    static_assert(32 * kPitch32 <= kStages * kSlotBytes, "fp32 32-row block fits the ring");
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+    for (int a = 0; a < kAFrags; ++a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int lr = 8 * (r / 4) + 4 * hh + (r % 4);
         lds_i8* const row = sm + lr * kPitch32;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) *(__attribute__((address_space(3))) float*)(row + 4 * (ncol + 2 * q)) = acc[a][q][r];
+        for (int t = 0; t < 2; ++t) *(__attribute__((address_space(3))) float*)(row + 4 * (ncol + 4 * t)) = acc[a][t][r];
       }
       wait_counts<0, 0>();
       bare_barrier();
@@ -452,24 +492,20 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
             *(const lds_u32x4*)(sm + lr * kPitch32 + 16 * pc);
       }
       wait_counts<0, 0>();
-      bare_barrier();  // the next half reuses the staging rows
+      bare_barrier();  // the next block reuses the staging rows
     }
     return;
   }
-  {
-    const int jj = lane & 31, hh = lane >> 5;
-    const int ncol = 8 * (kWaveCols * wave + (jj & 15)) + (jj >> 4);
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < kAFrags; ++a)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int mt = 32 * a + 8 * (r / 4) + 4 * hh + (r % 4);
-        lds_i8* const row = sm + mt * kOutPitch;
+    for (int r = 0; r < 16; ++r) {
+      const int mt = 32 * a + 8 * (r / 4) + 4 * hh + (r % 4);
+      lds_i8* const row = sm + mt * kOutPitch;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *(__attribute__((address_space(3))) uint16_t*)(row + 2 * (ncol + 2 * q)) = half_bits<kBF>(acc[a][q][r]);
-      }
-  }
+      for (int t = 0; t < 2; ++t)
+        *(__attribute__((address_space(3))) uint16_t*)(row + 2 * (ncol + 4 * t)) = half_bits<kBF>(acc[a][t][r]);
+    }
   wait_counts<0, 0>();
   bare_barrier();
   constexpr int kPieces = kTileCols;  // 16-byte pieces (8 outputs) per row
