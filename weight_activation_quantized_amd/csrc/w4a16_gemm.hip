@@ -56,6 +56,7 @@ constexpr int kTileCols = kAreas * kAreaCols;  // 64 packed columns (512 outputs
 constexpr int kWaves = 8;       // four per area (8 packed columns each), two per SIMD
 constexpr int kWaveCols = 8;    // packed columns per wavefront
 constexpr int kFillers = 4;     // wavefronts that issue the fills
+constexpr int kGroupM = 8;      // token tiles per group in the tile order
 constexpr int kAFrags = kBM / 32;  // 32-token A fragments per wavefront
 constexpr int kThreads = kWaves * 64;
 constexpr int kRows = 32;       // K rows per stage (two 16-row MFMA k-steps)
@@ -209,15 +210,24 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
   __shared__ __attribute__((aligned(1024))) int8_t smem[kStages * kSlotBytes];
   lds_i8* const sm = (lds_i8*)(smem);
 
-  // Tile of this workgroup: each XCD takes a contiguous run of tiles, token
-  // tiles fastest, so its workgroups share weight tiles.
+  // Tile of this workgroup: each XCD takes a contiguous run of tile ids,
+  // and ids run over groups of kGroupM token tiles, token tiles fastest
+  // within a group. An XCD's 32 concurrent workgroups then cover a block of
+  // about 8 token tiles x 4 weight tiles, so its L2 fetches each x row block
+  // and each weight tile once for several workgroups (with whole columns of
+  // token tiles per XCD every XCD would stream all of x).
   const int w_id = static_cast<int>(blockIdx.x & 7) * per_xcd + static_cast<int>(blockIdx.x >> 3);
   const int tiles = tiles_m * tiles_n;
   if (w_id >= tiles * splits) return;
   const int split = w_id / tiles;
   const int t_id = w_id % tiles;
-  const int m0 = (t_id % tiles_m) * kBM;
-  const int c0 = (t_id / tiles_m) * kTileCols;  // first packed column
+  const int group_tiles = kGroupM * tiles_n;
+  const int tgroup = t_id / group_tiles;
+  const int first_m = tgroup * kGroupM;
+  const int gm = min(kGroupM, tiles_m - first_m);
+  const int in_group = t_id - tgroup * group_tiles;
+  const int m0 = (first_m + in_group % gm) * kBM;
+  const int c0 = (in_group / gm) * kTileCols;  // first packed column
   const int k_len = K / splits;                 // multiple of 128 (host plan)
   const int k_base = split * k_len;
   constexpr int kGS = kSPG * kRows;  // rows per group
