@@ -19,15 +19,16 @@
 //   wavefront, its unpack about 4 vector operations per MFMA), and with two
 //   wavefronts per SIMD one's unpack runs under the other's MFMAs.
 // - B tiles: lane (j = lane%32, h = lane/32) of tile t takes packed column
-//   j%8 of the wavefront's 8 and field f = j/8 + 4t, rows 8h..8h+7 of a
-//   16-row k-step. Field f sits in byte f/2 of a word (low nibble for even
-//   f, high for odd), so for each row pair one byte permute per tile moves
-//   that byte of the two rows into the two fp16 halves. A field in bits 0-3
-//   of a half, OR-ed into the pattern of 1024.0, reads as 1024 + q; a field
-//   in bits 4-7, OR-ed into the pattern of 64.0, reads as 64 + q (the
-//   mantissa step at 64 is 1/16). Subtracting 1024 + z (64 + z) leaves
-//   q - z exactly, and the one multiply by s rounds each weight once, to
-//   fp16((q - z) * s), for every fp16 scale (subnormal products included).
+//   j%8 of the wavefront's 8 and field f = 2(j/8) + t, rows 8h..8h+7 of a
+//   16-row k-step: the two tiles hold the two nibbles of byte j/8 of the
+//   lane's words. For each row pair one byte permute moves that byte of the
+//   two rows into the two fp16 halves, and it serves both tiles. A field in
+//   bits 0-3 of a half, OR-ed into the pattern of 1024.0, reads as
+//   1024 + q; a field in bits 4-7, OR-ed into the pattern of 64.0, reads as
+//   64 + q (the mantissa step at 64 is 1/16). Subtracting 1024 + z (64 + z)
+//   leaves q - z exactly, and the one multiply by s rounds each weight once,
+//   to fp16((q - z) * s), for every fp16 scale (subnormal products
+//   included).
 // - Everything moves HBM -> LDS with buffer_load ... lds through a ring of
 //   kStages 32-row stages: the x rows (shared by all wavefronts) and, per
 //   32-column area, its raw packed words, scales and zero points. The first
@@ -94,39 +95,33 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(n), kBufferFlags);
 }
 
-// What a lane needs to unpack its fields: field f_t = f0 + 4t (t = 0, 1)
-// of its packed column sits in byte f0/2 + 2t of a word, in the low nibble
-// for even f0 and the high one for odd f0 (par). sel[t] is the byte-permute
-// selector that moves that byte of rows e and e + 1 into bytes 0 and 2;
-// mask keeps the field's nibble in each half and magic is the pattern of
-// 1024.0 (low nibble) or 64.0 (high nibble).
+// What a lane needs to unpack its fields: fields 2g and 2g + 1 (tiles 0
+// and 1) of its packed column are the low and high nibble of byte g of a
+// word. sel is the byte-permute selector that moves byte g of rows e and
+// e + 1 into bytes 0 and 2; mask[t] keeps tile t's nibble in each half and
+// magic[t] is the pattern of 1024.0 (low nibble) or 64.0 (high nibble).
 struct LaneFields {
-  uint32_t sel[2];
-  uint32_t mask, magic;
-  int f0, par;
+  uint32_t sel;
+  uint32_t mask[2], magic[2];
+  int g;
 };
 
-__device__ __forceinline__ LaneFields lane_fields(int f0) {
+__device__ __forceinline__ LaneFields lane_fields(int g) {
   LaneFields lf;
-  lf.f0 = f0;
-  lf.par = f0 & 1;
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const uint32_t b = static_cast<uint32_t>((f0 >> 1) + 2 * t);
-    lf.sel[t] = b | (0x0Cu << 8) | ((4u + b) << 16) | (0x0Cu << 24);  // 0x0C selects a zero byte
-  }
-  uint32_t mlo, mhi, glo, ghi;
-  asm("v_mov_b32 %0, 0x000f000f" : "=v"(mlo));
-  asm("v_mov_b32 %0, 0x00f000f0" : "=v"(mhi));
-  asm("v_mov_b32 %0, 0x64006400" : "=v"(glo));  // 1024.0: a field in bits 0-3 reads 1024 + q
-  asm("v_mov_b32 %0, 0x54005400" : "=v"(ghi));  // 64.0: a field in bits 4-7 reads 64 + q
-  lf.mask = lf.par ? mhi : mlo;
-  lf.magic = lf.par ? ghi : glo;
+  lf.g = g;
+  const uint32_t b = static_cast<uint32_t>(g);
+  lf.sel = b | (0x0Cu << 8) | ((4u + b) << 16) | (0x0Cu << 24);  // 0x0C selects a zero byte
+  // In registers: gfx9 VOP3 takes no literal, so each nibble-to-fp16 step
+  // stays one v_and_or_b32.
+  asm("v_mov_b32 %0, 0x000f000f" : "=v"(lf.mask[0]));
+  asm("v_mov_b32 %0, 0x00f000f0" : "=v"(lf.mask[1]));
+  asm("v_mov_b32 %0, 0x64006400" : "=v"(lf.magic[0]));  // 1024.0: a field in bits 0-3 reads 1024 + q
+  asm("v_mov_b32 %0, 0x54005400" : "=v"(lf.magic[1]));  // 64.0: a field in bits 4-7 reads 64 + q
   return lf;
 }
 
-// Per group and tile t: negz[t] = -(1024 + z) (even f0) or -(64 + z) (odd
-// f0) in both fp16 halves, and sc2[t] = s in both halves.
+// Per group and tile t: negz[t] = -(1024 + z) (t = 0) or -(64 + z) (t = 1)
+// in both fp16 halves, and sc2[t] = s in both halves.
 // bf16 activations (kBF): the weight is formed in binary32 and rounded once
 // to bf16 instead; negz[t] then holds the binary32 bits of -(1024 + z) * s
 // (or -(64 + z) * s) and sc2[t] those of s, both exact (an 11-bit integer
@@ -136,28 +131,24 @@ struct GroupParams {
   uint32_t sc2[2];
 };
 
-// Zero point z of field f sits in bits 4f..4f+3 of zw: the byte f/2 masked
-// to its nibble and OR-ed into the sign and exponent of -1024.0 (0xE400) or
-// -64.0 (0xD400) reads as -(1024 + z) or -(64 + z), the same encodings as
-// the weight fields. sd[t] is the scale word holding field f_t's scale in
-// half par.
+// Zero point z of field 2g + t sits in nibble t of byte g of zw: masked in
+// place and OR-ed into the sign and exponent of -1024.0 (0xE400) or -64.0
+// (0xD400) it reads as -(1024 + z) or -(64 + z), the same encodings as the
+// weight fields. sd holds the scales of fields 2g and 2g + 1 in its halves.
 template <bool kBF>
-__device__ __forceinline__ void make_group_params(uint32_t zw, const uint32_t (&sd)[2], const LaneFields& lf,
-                                                  GroupParams& gp) {
-  const uint32_t zmask = lf.par ? 0xF0u : 0x0Fu;
-  const uint32_t zbase = lf.par ? 0xD400u : 0xE400u;
+__device__ __forceinline__ void make_group_params(uint32_t zw, uint32_t sd, const LaneFields& lf, GroupParams& gp) {
+  const uint32_t zb = (zw >> (8 * lf.g)) & 0xFFu;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const uint32_t sh = (sd[t] >> (16 * lf.par)) & 0xFFFFu;  // the field's fp16 scale
-    const int byte = (lf.f0 >> 1) + 2 * t;
+    const uint32_t sh = (sd >> (16 * t)) & 0xFFFFu;  // the field's fp16 scale
     if constexpr (kBF) {
       const float sf = static_cast<float>(__builtin_bit_cast(f16, static_cast<uint16_t>(sh)));
-      const uint32_t zf = (zw >> (8 * byte + 4 * lf.par)) & 15u;
-      const float off = lf.par ? 64.0f : 1024.0f;
+      const uint32_t zf = (zb >> (4 * t)) & 15u;
+      const float off = t ? 64.0f : 1024.0f;
       gp.negz[t] = __builtin_bit_cast(uint32_t, -(off + static_cast<float>(zf)) * sf);
       gp.sc2[t] = __builtin_bit_cast(uint32_t, sf);
     } else {
-      const uint32_t e = ((zw >> (8 * byte)) & zmask) | zbase;
+      const uint32_t e = (zb & (t ? 0xF0u : 0x0Fu)) | (t ? 0xD400u : 0xE400u);
       gp.negz[t] = e | (e << 16);
       gp.sc2[t] = sh | (sh << 16);
     }
@@ -166,8 +157,8 @@ __device__ __forceinline__ void make_group_params(uint32_t zw, const uint32_t (&
 
 // Fragments fp16((q - z) * s) of the lane's two fields for one 16-row
 // k-step: w[e] is the lane's word of row 8h + e. For each row pair one byte
-// permute per tile gathers the field's byte of both rows, one v_and_or_b32
-// keeps the nibble under the magic pattern, and a packed add and multiply
+// permute gathers byte g of both rows; per tile one v_and_or_b32 keeps the
+// tile's nibble under its magic pattern, and a packed add and multiply
 // subtract the zero point and apply the scale.
 // kBF: the offset integer (an exact fp16) times s plus -(offset + z) * s in
 // one binary32 fused multiply-add (v_fma_mix_f32 reads the fp16 half
@@ -177,10 +168,11 @@ template <bool kBF>
 __device__ __forceinline__ void unpack_fields(const uint32_t (&w)[8], const GroupParams& gp, const LaneFields& lf,
                                               f16x8 (&b)[2]) {
 #pragma unroll
-  for (int p = 0; p < 4; ++p)
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t r = byte_perm(w[2 * p + 1], w[2 * p], lf.sel);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const uint32_t v = (byte_perm(w[2 * p + 1], w[2 * p], lf.sel[t]) & lf.mask) | lf.magic;
+      const uint32_t v = (r & lf.mask[t]) | lf.magic[t];
       f16x2 d;
       if constexpr (kBF) {
         const f16x2 o = as_f16x2(v);
@@ -193,6 +185,7 @@ __device__ __forceinline__ void unpack_fields(const uint32_t (&w)[8], const Grou
       b[t][2 * p] = d[0];
       b[t][2 * p + 1] = d[1];
     }
+  }
 }
 
 // kSPG = 32-row stages per group (group size 32 kSPG).
@@ -306,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
 
   // Compute: wavefront w takes packed columns 8w .. 8w+7 of the tile
   // (columns 8(w % 4) .. of area w / 4). Lane (j = lane%32, h = lane/32) of
-  // B tile t takes packed column 8w + j%8 and field j/8 + 4t, so the two
+  // B tile t takes packed column 8w + j%8 and field 2(j/8) + t, so the two
   // tiles cover the eight fields of the wavefront's 8 columns.
   const int fi = lane & 31, fh = lane >> 5;
   const int col_in_area = kWaveCols * (wave & 3) + (fi & 7);
@@ -323,8 +316,8 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
   // raw words: k-row 16t + 8fh + e of the lane's packed column.
   const int area = kABytes + (wave >> 2) * kAreaBytes;
   const int wbase = area + 4 * col_in_area;
-  // the lane's two scale words (fields f0 and f0 + 4 of its column)
-  const int sbase = area + kBBytes + 16 * col_in_area + 4 * (lf.f0 >> 1);
+  // the lane's scale word (fields 2g and 2g + 1 of its column)
+  const int sbase = area + kBBytes + 16 * col_in_area + 4 * lf.g;
 
   f32x16 acc[kAFrags][2];
 #pragma unroll
@@ -350,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
 #define MQ_READ_GP(S, GP)                                                                        \
   do {                                                                                           \
     const lds_i8* const sl_ = sm + ((S) % kStages) * kSlotBytes;                                 \
-    const uint32_t sd_[2] = {*(const lds_word*)(sl_ + sbase), *(const lds_word*)(sl_ + sbase + 8)}; \
+    const uint32_t sd_ = *(const lds_word*)(sl_ + sbase);                                      \
     const uint32_t zw_ = *(const lds_word*)(sl_ + area + kBBytes + kSBytes + 4 * col_in_area);   \
     make_group_params<kBF>(zw_, sd_, lf, GP);                                                    \
   } while (0)
@@ -443,22 +436,21 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
       // block A
       f16x8 a1[kAFrags], b1[2];
       uint32_t wk0[8];  // raw words of (s + 1, k0)
-      uint32_t sd_next[2], zw_next;
+      uint32_t sd_next, zw_next;
       {
         __builtin_amdgcn_sched_barrier(0);
         MQ_READ_A(s, 1, a1);
         MQ_READ_W(s + 1, 0, wk0);
         if (new_group) {
           const lds_i8* const sl_ = sm + ((s + 1) % kStages) * kSlotBytes;
-          sd_next[0] = *(const lds_word*)(sl_ + sbase);
-          sd_next[1] = *(const lds_word*)(sl_ + sbase + 8);
+          sd_next = *(const lds_word*)(sl_ + sbase);
           zw_next = *(const lds_word*)(sl_ + area + kBBytes + kSBytes + 4 * col_in_area);
         }
         unpack_fields<kBF>(wk1, gp, lf, b1);
         MQ_MFMAS(a0, b0);
         MQ_PIN(b1);
         if (new_group) {
-          MQ_INTERLEAVE(15, kBF ? 5 : 4);
+          MQ_INTERLEAVE(14, kBF ? 5 : 4);
         } else {
           MQ_INTERLEAVE(12, kBF ? 5 : 4);
         }
@@ -492,13 +484,13 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
 
   // Epilogue. D[m][j] of a 32x32 tile: lane (jj, hh) register r holds token
   // 8 (r / 4) + 4 hh + r % 4 of B column jj, i.e. output 8 (8 w + jj % 8)
-  // + jj / 8 + 4 t of the tile. The tile is staged in LDS as fp16 and
+  // + 2 (jj / 8) + t of the tile. The tile is staged in LDS as fp16 and
   // written out as whole rows with 16-byte stores (fp32 partial sums: 32
   // rows at a time, staged and written the same way).
   wait_counts<0, 0>();
   bare_barrier();  // every wave is done reading the ring
   const int jj = lane & 31, hh = lane >> 5;
-  const int ncol = 8 * (kWaveCols * wave + (jj & 7)) + (jj >> 3);
+  const int ncol = 8 * (kWaveCols * wave + (jj & 7)) + 2 * (jj >> 3);
   if (splits > 1) {
     constexpr int kPitch32 = kTileCols * 8 * 4 + 16;  // bytes per staged fp32 row
     static_assert(32 * kPitch32 <= kStages * kSlotBytes, "fp32 32-row block fits the ring");
@@ -509,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
         const int lr = 8 * (r / 4) + 4 * hh + (r % 4);
         lds_i8* const row = sm + lr * kPitch32;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) *(__attribute__((address_space(3))) float*)(row + 4 * (ncol + 4 * t)) = acc[a][t][r];
+        for (int t = 0; t < 2; ++t) *(__attribute__((address_space(3))) float*)(row + 4 * (ncol + t)) = acc[a][t][r];
       }
       wait_counts<0, 0>();
       bare_barrier();
@@ -534,7 +526,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
       lds_i8* const row = sm + mt * kOutPitch;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
-        *(__attribute__((address_space(3))) uint16_t*)(row + 2 * (ncol + 4 * t)) = half_bits<kBF>(acc[a][t][r]);
+        *(__attribute__((address_space(3))) uint16_t*)(row + 2 * (ncol + t)) = half_bits<kBF>(acc[a][t][r]);
     }
   wait_counts<0, 0>();
   bare_barrier();
