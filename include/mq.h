@@ -311,9 +311,12 @@ size_t mq_w4a16_gemv_blocked_workspace_bytes(int64_t M, int64_t N, int64_t K, in
  * s * (sum - (1024 + z) * sum(x)) per group) and tolerance as mq_w4a16_gemv;
  * qweight_blocked is the output of mq_w4a16_block_weights for these weights.
  * Each workgroup streams one 32-output strip over its K range as one
- * contiguous run of bytes; K is split across workgroups (fp32 partials in
- * `workspace`, added in split order by a second kernel) only when the layer
- * has too few strips for two workgroups per compute unit. All M <= 64 tokens share one pass
+ * contiguous run of bytes. When the layer has too few strips for two
+ * workgroups per compute unit, up to 4 tokens with K/128 <= 32 take one
+ * workgroup of 8 or 16 wavefronts per strip (their sums added in LDS in
+ * wavefront order, no workspace); otherwise K is split across workgroups
+ * (fp32 partials in `workspace`, added in split order by a second kernel).
+ * All M <= 64 tokens share one pass
  * over the weights. For 33-64 tokens the fragments are the weights themselves,
  * rounded once to fp16 as in mq_w4a16_gemm (fp16((q - z) * s), the same range
  * notes apply), accumulated in fp32; up to 32 tokens use the exact (q - z)

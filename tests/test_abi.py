@@ -243,12 +243,16 @@ def test_w4a16_blocked_validation(lib):
     assert v(A, B, C, D, E, 1, 256, 256, 96, F, 1 << 20, None) == UNSUP
     assert v(A, B, C, D, E, 65, 256, 256, 128, F, 1 << 20, None) == UNSUP
     assert v(A, B, C, D, E, 0, 256, 256, 128, None, 0, None) == OK
-    # narrow layers split K: they need a workspace, wide ones do not
+    # wide layers need no workspace; narrow ones with up to 4 tokens and
+    # short K neither (one workgroup per strip takes all of K); narrow ones
+    # with long K or more tokens split K and need one
     assert ws(1, 24576, 4096, 128) == 0
-    need = ws(1, 4096, 4096, 128)
+    assert ws(1, 4096, 4096, 128) == 0 and ws(4, 6144, 4096, 128) == 0
+    assert ws(8, 4096, 4096, 128) > 0
+    need = ws(1, 4096, 12288, 128)
     assert need > 0 and need % (4 * 4096) == 0
-    assert v(A, B, C, D, E, 1, 4096, 4096, 128, None, 0, None) == WS
-    assert v(A, B, C, D, E, 1, 4096, 4096, 128, F, need - 4, None) == WS
+    assert v(A, B, C, D, E, 1, 4096, 12288, 128, None, 0, None) == WS
+    assert v(A, B, C, D, E, 1, 4096, 12288, 128, F, need - 4, None) == WS
     assert ws(1, 264, 4096, 128) == 0 and ws(65, 4096, 4096, 128) == 0
     # a split divides the chunk count (K/128) and the workspace holds its partials
     for M, N, K in [(1, 6144, 4096), (16, 4096, 12288), (32, 3072, 1024), (64, 96, 640)]:

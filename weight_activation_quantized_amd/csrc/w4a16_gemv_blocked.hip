@@ -366,7 +366,7 @@ __device__ __forceinline__ void compute_chunk_scaled(const BChunk<kT, kBChunkRow
 // wavefront after the other (same order, smaller buffer).
 template <int kT, int kGS, int kW, int kSP, bool kXL, bool kBF>
 __global__ __launch_bounds__(kW * 64)
-__attribute__((amdgpu_waves_per_eu(kT == 1 && kSP == 1 && kGS >= 64 ? 3 : 1))) void w4a16_gemv_blocked_kernel(
+__attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kGS >= 64 ? 3 : 1)))) void w4a16_gemv_blocked_kernel(
     const uint16_t* __restrict__ x, const u32x4* __restrict__ qb, const uint16_t* __restrict__ scales,
     const uint32_t* __restrict__ qz, uint16_t* __restrict__ y, float* __restrict__ partial, int M, int N, int K,
     int units, int splits, XcdMap map) {
@@ -556,6 +556,19 @@ hipError_t launch_blocked_xl(const uint16_t* x, const u32x4* qb, const uint16_t*
     case 2:
       return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 2, kSP, kXL, kBF>, grid, dim3(128), lds, stream, x, qb,
                            scales, qz, y, part, m, n, k, units, plan.splits, map);
+    case 8:
+    case 16:
+      // only the one-strip forms with x staged in LDS (up to 4 tokens,
+      // narrow layers) are built for 8 and 16 wavefronts
+      if constexpr (kT == 1 && kSP == 1 && kXL) {
+        if (plan.waves == 8)
+          return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 8, kSP, kXL, kBF>, grid, dim3(512), lds, stream, x,
+                               qb, scales, qz, y, part, m, n, k, units, plan.splits, map);
+        return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 16, kSP, kXL, kBF>, grid, dim3(1024), lds, stream, x,
+                             qb, scales, qz, y, part, m, n, k, units, plan.splits, map);
+      } else {
+        return hipErrorInvalidValue;
+      }
     default:
       return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 4, kSP, kXL, kBF>, grid, dim3(256), lds, stream, x, qb,
                            scales, qz, y, part, m, n, k, units, plan.splits, map);
@@ -673,6 +686,20 @@ GemvPlan plan_w4a16_gemv_blocked(int64_t M, int64_t N, int64_t K, int64_t group)
   }
   plan.strips_per_unit = sp;
   const int64_t units = strips / sp;
+  // Narrow layers with up to 4 tokens (fewer strips than CUs) and short K:
+  // one workgroup of 16 (else 8) wavefronts per strip takes all of K, each
+  // wavefront one or two chunks, and their sums meet in LDS. One launch
+  // with every chunk in flight at once, instead of K split across
+  // workgroups with fp32 partial sums and a second kernel to add them
+  // (8B qkv at one token 7.6 -> 6.3 us, o_proj 6.5 -> 5.8 us). With six
+  // chunks per wavefront (K = 12288) it measured slower than the split.
+  if (mt <= kXLdsMaxTokens && sp == 1 && strips < kCUs) {
+    for (int w : {16, 8}) {
+      if (chunks % w || chunks / w > 2 || blocked_x_lds_bytes(M, K, group, 1, w, 1) == 0) continue;
+      plan.waves = w;
+      return plan;  // splits = 1, no workspace
+    }
+  }
   // Split K only when there are too few units for two single-strip
   // workgroups (one multi-strip or many-token workgroup) per CU: the
   // smallest divisor of the chunk count that gets there (else the largest);
