@@ -312,7 +312,7 @@ size_t mq_w4a16_gemv_blocked_workspace_bytes(int64_t M, int64_t N, int64_t K, in
  * qweight_blocked is the output of mq_w4a16_block_weights for these weights.
  * Each workgroup streams one 32-output strip over its K range as one
  * contiguous run of bytes. When the layer has too few strips for two
- * workgroups per compute unit, up to 4 tokens with K/128 <= 32 take one
+ * workgroups per compute unit, up to 8 tokens with K/128 <= 32 take one
  * workgroup of 8 or 16 wavefronts per strip (their sums added in LDS in
  * wavefront order, no workspace); otherwise K is split across workgroups
  * (fp32 partials in `workspace`, added in split order by a second kernel).

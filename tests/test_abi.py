@@ -243,12 +243,12 @@ def test_w4a16_blocked_validation(lib):
     assert v(A, B, C, D, E, 1, 256, 256, 96, F, 1 << 20, None) == UNSUP
     assert v(A, B, C, D, E, 65, 256, 256, 128, F, 1 << 20, None) == UNSUP
     assert v(A, B, C, D, E, 0, 256, 256, 128, None, 0, None) == OK
-    # wide layers need no workspace; narrow ones with up to 4 tokens and
+    # wide layers need no workspace; narrow ones with up to 8 tokens and
     # short K neither (one workgroup per strip takes all of K); narrow ones
     # with long K or more tokens split K and need one
     assert ws(1, 24576, 4096, 128) == 0
     assert ws(1, 4096, 4096, 128) == 0 and ws(4, 6144, 4096, 128) == 0
-    assert ws(8, 4096, 4096, 128) > 0
+    assert ws(16, 4096, 4096, 128) > 0
     need = ws(1, 4096, 12288, 128)
     assert need > 0 and need % (4 * 4096) == 0
     assert v(A, B, C, D, E, 1, 4096, 12288, 128, None, 0, None) == WS

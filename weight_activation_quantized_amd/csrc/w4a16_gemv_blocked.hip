@@ -72,6 +72,7 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 // and 0.7 us.
 constexpr int kXLdsPad = 16;
 constexpr int64_t kXLdsMaxTokens = 4;
+constexpr int64_t kWideMaxTokens = 8;  // one-workgroup-per-strip form (see the plan)
 constexpr int64_t kLdsPerWorkgroup = 160 * 1024;
 
 // ---------------------------------------------------------------------------
@@ -584,7 +585,10 @@ int64_t blocked_x_lds_bytes(int64_t M, int64_t K, int64_t group, int splits, int
   const int64_t xb = std::min<int64_t>(M, 16) * (2 * kr + kXLdsPad);
   const int64_t szb = (kr / group) * strips_per_unit * (64 + 16);
   const int64_t red = int64_t{waves} * 16 * strips_per_unit * kBOut * 4;
-  if (M > kXLdsMaxTokens || xb + szb + red > kLdsPerWorkgroup) return 0;
+  // the one-workgroup-per-strip form (8 or 16 wavefronts) stages up to 8
+  // tokens: it has no stream to hold back before the copy
+  const int64_t max_tokens = waves >= 8 ? kWideMaxTokens : kXLdsMaxTokens;
+  if (M > max_tokens || xb + szb + red > kLdsPerWorkgroup) return 0;
   return xb + szb;
 }
 
@@ -657,6 +661,21 @@ GemvPlan plan_w4a16_gemv_blocked(int64_t M, int64_t N, int64_t K, int64_t group)
   const int64_t strips = N / kBOut;
   const int64_t chunks = K / kBChunkRows;
   const int64_t mt = std::min(M, kGemvMaxM);
+  // Narrow layers with up to 8 tokens (fewer strips than CUs) and short K:
+  // one workgroup of 16 (else 8) wavefronts per strip takes all of K, each
+  // wavefront one or two chunks, with x staged in LDS, and their sums meet
+  // in LDS. One launch with every chunk in flight at once, instead of K
+  // split across workgroups with fp32 partial sums and a second kernel to
+  // add them (8B qkv at one token 7.6 -> 6.3 us, o_proj 6.5 -> 5.8 us).
+  // With six chunks per wavefront (K = 12288) it measured slower than the
+  // split.
+  if (mt <= kWideMaxTokens && strips < kCUs) {
+    for (int w : {16, 8}) {
+      if (chunks % w || chunks / w > 2 || blocked_x_lds_bytes(M, K, group, 1, w, 1) == 0) continue;
+      plan.waves = w;
+      return plan;  // splits = 1, no workspace
+    }
+  }
   // Every workgroup loads all of x for its K range, so with more than a few
   // tokens a workgroup takes several adjacent strips that share those loads
   // (three for one 16-token tile, two for two; what divides the strips).
@@ -686,20 +705,6 @@ GemvPlan plan_w4a16_gemv_blocked(int64_t M, int64_t N, int64_t K, int64_t group)
   }
   plan.strips_per_unit = sp;
   const int64_t units = strips / sp;
-  // Narrow layers with up to 4 tokens (fewer strips than CUs) and short K:
-  // one workgroup of 16 (else 8) wavefronts per strip takes all of K, each
-  // wavefront one or two chunks, and their sums meet in LDS. One launch
-  // with every chunk in flight at once, instead of K split across
-  // workgroups with fp32 partial sums and a second kernel to add them
-  // (8B qkv at one token 7.6 -> 6.3 us, o_proj 6.5 -> 5.8 us). With six
-  // chunks per wavefront (K = 12288) it measured slower than the split.
-  if (mt <= kXLdsMaxTokens && sp == 1 && strips < kCUs) {
-    for (int w : {16, 8}) {
-      if (chunks % w || chunks / w > 2 || blocked_x_lds_bytes(M, K, group, 1, w, 1) == 0) continue;
-      plan.waves = w;
-      return plan;  // splits = 1, no workspace
-    }
-  }
   // Split K only when there are too few units for two single-strip
   // workgroups (one multi-strip or many-token workgroup) per CU: the
   // smallest divisor of the chunk count that gets there (else the largest);
