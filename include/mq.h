@@ -62,7 +62,7 @@ typedef enum mq_status {
   MQ_ERR_NULL = 1,        /* a required pointer is NULL */
   MQ_ERR_SHAPE = 2,       /* a size is negative, too large or breaks a divisibility rule */
   MQ_ERR_ALIGN = 3,       /* a pointer is not aligned as documented */
-  MQ_ERR_UNSUPPORTED = 4, /* valid in principle but not provided (e.g. group not in {32, 64, 128}, GEMV M > 64) */
+  MQ_ERR_UNSUPPORTED = 4, /* valid in principle but not provided (e.g. group not in {32, 64, 128, -1}, GEMV M > 64) */
   MQ_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
   MQ_ERR_ALIAS = 6,       /* an output overlaps an input or another output */
   MQ_ERR_HIP = 7          /* the HIP runtime refused the launch (message in mq_last_error) */
@@ -204,8 +204,13 @@ mq_status mq_w8a8_linear_noalloc(const uint16_t* x, const int8_t* wq, const floa
  * Source: LMDeploy toolkit overview, section 2.5 (4-bit AWQ weights, group
  * size 128); LMDeploy 4-bit deployment guide, section 2.2 (dequantization
  * fused into the matmul kernel) and section 3.2 (group size per layer: 64
- * for the vision tower's attention projection, 128 for the language model).
- * G = group: the number of consecutive k sharing one scale and zero point.
+ * for the vision tower's attention projection, 128 for the language model;
+ * -1 for no grouping).
+ * G = group: the number of consecutive k sharing one scale and zero point;
+ * group = -1 means G = K: one scale and zero point per output column
+ * (per-channel), scales [1, N] and qzeros [1, N/8]. Every W4A16 entry takes
+ * group = -1 and computes it as groups of 128 rows that all read that one
+ * row (same arithmetic, same bounds as group 128).
  *     q[k,n]  = field (n % 8) of qweight[k, n/8]     (field j = bits 4j..4j+3)
  *     z[g,n]  = field (n % 8) of qzeros[g, n/8]
  *     w[k,n]  = (q[k,n] - z[k/G,n]) * scales[k/G,n]
@@ -225,7 +230,7 @@ mq_status mq_w8a8_linear_noalloc(const uint16_t* x, const int8_t* wq, const floa
  *   scales   [K/G, N]   fp16   in
  *   qzeros   [K/G, N/8] int32  in   (unsigned 4-bit zero points, packed like qweight)
  *   y        [M, N]     fp16   out
- *   workspace  optional (may be NULL). When the 64-token x 1024-output
+ *   workspace  optional (may be NULL). When the 128-token x 512-output
  *              tiles alone leave most CUs idle (fewer than 192 tiles), K is
  *              split across workgroups if a workspace of at least
  *              mq_w4a16_gemm_workspace_bytes(M, N, K, group) bytes is given:
@@ -233,7 +238,7 @@ mq_status mq_w8a8_linear_noalloc(const uint16_t* x, const int8_t* wq, const floa
  *              stream adds them in split order (deterministic). NULL never
  *              splits. 16-byte aligned, not overlapping any operand; calls
  *              sharing it must be ordered.
- * Requires: group in {32, 64, 128} (anything else, -1 included ->
+ * Requires: group in {32, 64, 128, -1} (anything else ->
  * MQ_ERR_UNSUPPORTED); 0 <= M < 2^31; 8 <= N <= 2^27, N % 8 == 0;
  * 128 <= K <= 2^20, K % 128 == 0 (so K % group == 0); x, scales, y 16-byte
  * aligned; qweight, qzeros 4-byte aligned.

@@ -188,16 +188,17 @@ def check_dequant_exact_full_range(dequant):
 
 def _tiny_w4_case(seed, M=3, K=256, N=16, G=128):
     rng = np.random.default_rng(seed)
+    rows = 1 if G == -1 else K // G  # G = -1: one scale / zero point per column over all of K
     q = rng.integers(0, 16, size=(K, N))
-    z = rng.integers(0, 16, size=(K // G, N))
-    s = rng.uniform(0.005, 0.02, size=(K // G, N)).astype(np.float16)
+    z = rng.integers(0, 16, size=(rows, N))
+    s = rng.uniform(0.005, 0.02, size=(rows, N)).astype(np.float16)
     x = rng.standard_normal((M, K)).astype(np.float16)
     return x, q, z, s
 
 
 def check_w4a16_bruteforce(w4a16):
     for seed, (M, K, N, G) in enumerate([(3, 256, 16, 128), (2, 384, 24, 128), (1, 128, 8, 128),
-                                        (2, 64, 16, 32), (2, 256, 16, 64)]):
+                                        (2, 64, 16, 32), (2, 256, 16, 64), (2, 256, 16, -1), (1, 384, 8, -1)]):
         x, q, z, s = _tiny_w4_case(seed, M, K, N, G)
         qweight, qzeros = loop_pack(q), loop_pack(z)
         y = w4a16(x, qweight, s, qzeros, G)
@@ -206,9 +207,10 @@ def check_w4a16_bruteforce(w4a16):
             for n in range(N):
                 terms = []
                 for k in range(K):
+                    g = 0 if G == -1 else k // G  # per-channel: the one parameter row
                     qv = loop_field(qweight[k, n // 8], n % 8)
-                    zv = loop_field(qzeros[k // G, n // 8], n % 8)
-                    terms.append(float(x[m, k]) * (qv - zv) * float(s[k // G, n]))
+                    zv = loop_field(qzeros[g, n // 8], n % 8)
+                    terms.append(float(x[m, k]) * (qv - zv) * float(s[g, n]))
                 ref = math.fsum(terms)
                 assert abs(y[m, n] - ref) <= 1e-12 * (1.0 + abs(ref)), (m, n, y[m, n], ref)
 

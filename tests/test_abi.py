@@ -124,12 +124,13 @@ def test_w8a8_validation(lib):
 def test_w4a16_gemm_validation(lib):
     g = lib.mq_w4a16_gemm
     assert g(A, B, C, D, None, 4, 64, 256, 128, None, 0, None) == NULL
-    # groups of 32, 64 and 128 rows are provided; others (and -1, one group
-    # over all of K) are not
-    for group in (96, 256, 16, 0, -1):
+    # groups of 32, 64 and 128 rows and -1 (one scale / zero point per column
+    # over all of K) are provided; others are not
+    for group in (96, 256, 16, 0, -2):
         assert g(A, B, C, D, E, 4, 64, 256, group, None, 0, None) == UNSUP, group
     assert g(A, B, C, D, E, 4, 64, 192, 64, None, 0, None) == SHAPE      # K % 128, also for smaller groups
-    for group in (32, 64, 128):
+    assert g(A, B, C, D, E, 4, 64, 192, -1, None, 0, None) == SHAPE      # per-channel runs as groups of 128
+    for group in (32, 64, 128, -1):
         assert g(A, B, C, D, E, 0, 64, 256, group, None, 0, None) == OK
     # the workspace is optional; given for a small grid it must be large enough
     wsb = lib.mq_w4a16_gemm_workspace_bytes
@@ -171,7 +172,7 @@ def test_gemv_workspace_plan(lib):
     assert ws(0, 512, 512, 128) == 0
     assert ws(65, 512, 512, 128) == 0
     assert ws(4, 512, 512, 96) == 0
-    assert ws(4, 512, 512, -1) == 0
+    assert ws(4, 512, 512, -2) == 0
     # the workspace holds splits * M * N fp32 partial sums, with splits a
     # divisor of the group count K/G; the LDS-staged kernel (N % 32 == 0)
     # keeps at most 1024 rows per split
@@ -351,3 +352,20 @@ def test_w8a8_linear_noalloc_validation(lib):
     assert f(A, B, C, D, 4096, 8, 12288, None) == WS       # rejected before any HIP call
     assert "scratch" in _err(lib)
     assert f(A, B, C, D, 0, 8, 64, None) == OK             # empty problem: nothing enqueued, no lookup
+
+
+def test_per_channel_group(lib):
+    # group -1: every entry accepts it, and plans it as groups of 128 rows
+    # (the workspace sizes are those of group 128)
+    for fn in (lib.mq_w4a16_gemm, lib.mq_w4a16_gemv, lib.mq_w4a16_gemv_blocked,
+               lib.mq_w4a16_gemm_bf16, lib.mq_w4a16_gemv_bf16, lib.mq_w4a16_gemv_blocked_bf16):
+        assert fn(A, B, C, D, E, 0, 256, 512, -1, None, 0, None) == OK
+        assert fn(A, B, C, D, E, 0, 256, 512, -3, None, 0, None) == UNSUP
+    for M, N, K in [(2048, 4096, 4096), (300, 1032, 1024), (4096, 4096, 4096)]:
+        assert lib.mq_w4a16_gemm_workspace_bytes(M, N, K, -1) == lib.mq_w4a16_gemm_workspace_bytes(M, N, K, 128)
+    for M, N, K in [(1, 128, 4096), (16, 4096, 12288), (40, 4096, 4096)]:
+        assert lib.mq_w4a16_gemv_workspace_bytes(M, N, K, -1) == lib.mq_w4a16_gemv_workspace_bytes(M, N, K, 128)
+    for M, N, K in [(1, 4096, 12288), (16, 4096, 4096), (64, 6144, 4096), (1, 24576, 4096)]:
+        assert (lib.mq_w4a16_gemv_blocked_workspace_bytes(M, N, K, -1) ==
+                lib.mq_w4a16_gemv_blocked_workspace_bytes(M, N, K, 128))
+    assert lib.mq_w4a16_gemv_blocked_workspace_bytes(1, 4096, 12288, -2) == 0

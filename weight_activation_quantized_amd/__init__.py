@@ -343,11 +343,12 @@ def w4a16_gemv_blocked(x, qweight_blocked, scales, qzeros, group=128, out=None, 
     _dev_tensor(qzeros, "qzeros", torch.int32, 2)
     M, K = x.shape
     N = scales.shape[1]
-    if group <= 0 or K % group:
+    G = K if group == -1 else group
+    if G <= 0 or K % G:
         raise ValueError("K must be a multiple of the group size")
     if tuple(qweight_blocked.shape) != (K // 64, 8 * N) or N % 32:
         raise ValueError("qweight_blocked must be [K/64, 8*N] (from w4a16_block_weights)")
-    if tuple(scales.shape) != (K // group, N) or tuple(qzeros.shape) != (K // group, N // 8):
+    if tuple(scales.shape) != (K // G, N) or tuple(qzeros.shape) != (K // G, N // 8):
         raise ValueError("scales must be [K/G, N] and qzeros [K/G, N/8]")
     y = _out(out, (M, N), x.dtype, x, "out")
     need = w4a16_gemv_blocked_workspace_bytes(M, N, K, group)

@@ -79,10 +79,12 @@ constexpr int64_t kU16TransposeMaxB = int64_t{1} << 30;
 int w4a16_gemm_splits(int64_t M, int64_t N, int64_t K);
 size_t w4a16_gemm_workspace(int64_t M, int64_t N, int64_t K);
 // bf16: x and y are bf16 (the weight is rounded once to bf16 instead of fp16).
+// per_channel: scales / qzeros hold one row used for every group (the
+// kernel runs with `group` rows per group, 128 for per-channel layers).
 hipError_t launch_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                              const int32_t* qzeros, uint16_t* y,
-                             int64_t M, int64_t N, int64_t K, int64_t group, void* workspace, bool bf16,
-                             hipStream_t stream);
+                             int64_t M, int64_t N, int64_t K, int64_t group, bool per_channel, void* workspace,
+                             bool bf16, hipStream_t stream);
 
 // Largest token count the W4A16 GEMV takes (four 16-token MFMA tiles).
 constexpr int64_t kGemvMaxM = 64;
@@ -96,6 +98,7 @@ struct GemvPlan {
   bool lds;   // LDS-staged kernel (N % 32 == 0)
   int group;  // rows per group: 32, 64 or 128
   int strips_per_unit = 1;  // blocked GEMV: adjacent 32-output strips per workgroup
+  bool per_channel = false; // one scale / zero-point row for all of K (group runs as 128)
 };
 GemvPlan plan_w4a16_gemv(int64_t M, int64_t N, int64_t K, int64_t group);
 

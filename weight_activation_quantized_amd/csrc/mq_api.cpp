@@ -89,10 +89,17 @@ mq_status check_mk(int64_t M, int64_t K, int64_t k_min, int64_t k_max, int64_t k
   return MQ_OK;
 }
 
+// group -1: one scale and zero point per output column over all of K
+// (per-channel); the kernels run it as groups of 128 rows that all read the
+// one parameter row.
+bool w4a16_group_ok(int64_t group) { return group == 32 || group == 64 || group == 128 || group == -1; }
+int64_t kernel_group(int64_t group) { return group == -1 ? 128 : group; }
+size_t group_rows(int64_t K, int64_t group) { return group == -1 ? 1 : static_cast<size_t>(K / group); }
+
 mq_status check_w4a16(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                       const int32_t* qzeros, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t group) {
-  if (group != 32 && group != 64 && group != 128)
-    return fail(MQ_ERR_UNSUPPORTED, "group=%lld (32, 64 and 128 are provided)", (long long)group);
+  if (!w4a16_group_ok(group))
+    return fail(MQ_ERR_UNSUPPORTED, "group=%lld (32, 64, 128 and -1 = per-channel are provided)", (long long)group);
   MQ_TRY(check_mk(M, K, 128, kMaxK, 128));
   if (N < 8 || N > kMaxN4 || N % 8)
     return fail(MQ_ERR_SHAPE, "N=%lld must be a multiple of 8 in [8, 2^27]", (long long)N);
@@ -106,7 +113,7 @@ mq_status check_w4a16(const uint16_t* x, const int32_t* qweight, const uint16_t*
     return fail(MQ_ERR_ALIGN, "x, scales and y must be 16-byte aligned");
   if (!aligned(qweight, 4) || !aligned(qzeros, 4))
     return fail(MQ_ERR_ALIGN, "qweight and qzeros must be 4-byte aligned");
-  const size_t G = static_cast<size_t>(K / group);
+  const size_t G = group_rows(K, group);
   const Range in[] = {{x, static_cast<size_t>(M * K) * 2, "x"},
                       {qweight, static_cast<size_t>(K * (N / 8)) * 4, "qweight"},
                       {scales, G * static_cast<size_t>(N) * 2, "scales"},
@@ -228,7 +235,7 @@ mq_status mq_w8a8_mm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc,
 }
 
 size_t mq_w4a16_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group) {
-  if ((group != 32 && group != 64 && group != 128) || M < 1 || M > kMaxDim || N < 8 || N % 8 || N > kMaxN4 ||
+  if (!w4a16_group_ok(group) || M < 1 || M > kMaxDim || N < 8 || N % 8 || N > kMaxN4 ||
       K < 128 || K > kMaxK || K % 128 || M * N > kMaxElems)
     return 0;
   return mq::w4a16_gemm_workspace(M, N, K);
@@ -249,7 +256,7 @@ static mq_status w4a16_gemm_impl(const uint16_t* x, const int32_t* qweight, cons
       if (workspace_bytes < need)
         return fail(MQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
       if (!aligned(workspace, 16)) return fail(MQ_ERR_ALIGN, "workspace must be 16-byte aligned");
-      const size_t G = static_cast<size_t>(K / group);
+      const size_t G = group_rows(K, group);
       const Range in[] = {{x, static_cast<size_t>(M * K) * 2, "x"},
                           {qweight, static_cast<size_t>(K * (N / 8)) * 4, "qweight"},
                           {scales, G * static_cast<size_t>(N) * 2, "scales"},
@@ -260,15 +267,16 @@ static mq_status w4a16_gemm_impl(const uint16_t* x, const int32_t* qweight, cons
       ws = workspace;
     }
   }
-  return hip_status(mq::launch_w4a16_gemm(x, qweight, scales, qzeros, y, M, N, K, group, ws, bf16, as_stream(stream)),
+  return hip_status(mq::launch_w4a16_gemm(x, qweight, scales, qzeros, y, M, N, K, kernel_group(group), group == -1,
+                                          ws, bf16, as_stream(stream)),
                     "w4a16_gemm launch");
 }
 
 size_t mq_w4a16_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group) {
-  if ((group != 32 && group != 64 && group != 128) || M < 1 || M > mq::kGemvMaxM || N < 8 || N % 8 ||
+  if (!w4a16_group_ok(group) || M < 1 || M > mq::kGemvMaxM || N < 8 || N % 8 ||
       N > kMaxN4 || K < 128 || K > kMaxK || K % 128)
     return 0;
-  return mq::plan_w4a16_gemv(M, N, K, group).workspace_bytes;
+  return mq::plan_w4a16_gemv(M, N, K, kernel_group(group)).workspace_bytes;
 }
 
 static mq_status w4a16_gemv_impl(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
@@ -280,13 +288,14 @@ static mq_status w4a16_gemv_impl(const uint16_t* x, const int32_t* qweight, cons
     return fail(MQ_ERR_UNSUPPORTED, "GEMV needs M <= %lld (got %lld); use mq_w4a16_gemm",
                 (long long)mq::kGemvMaxM, (long long)M);
   if (M == 0) return ok();
-  const mq::GemvPlan plan = mq::plan_w4a16_gemv(M, N, K, group);
+  mq::GemvPlan plan = mq::plan_w4a16_gemv(M, N, K, kernel_group(group));
+  plan.per_channel = group == -1;
   if (plan.workspace_bytes > 0) {
     if (!workspace || workspace_bytes < plan.workspace_bytes)
       return fail(MQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.workspace_bytes,
                   workspace ? workspace_bytes : static_cast<size_t>(0));
     if (!aligned(workspace, 16)) return fail(MQ_ERR_ALIGN, "workspace must be 16-byte aligned");
-    const size_t G = static_cast<size_t>(K / group);
+    const size_t G = group_rows(K, group);
     const Range in[] = {{x, static_cast<size_t>(M * K) * 2, "x"},
                         {qweight, static_cast<size_t>(K * (N / 8)) * 4, "qweight"},
                         {scales, G * static_cast<size_t>(N) * 2, "scales"},
@@ -498,10 +507,10 @@ mq_status mq_w4a16_block_weights(const int32_t* qweight, int32_t* qweight_blocke
 }
 
 size_t mq_w4a16_gemv_blocked_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group) {
-  if ((group != 32 && group != 64 && group != 128) || M < 1 || M > mq::kGemvMaxM || N < 32 || N % 32 ||
+  if (!w4a16_group_ok(group) || M < 1 || M > mq::kGemvMaxM || N < 32 || N % 32 ||
       N > kMaxN4 || K < 128 || K > kMaxK || K % 128)
     return 0;
-  return mq::w4a16_gemv_blocked_workspace(M, N, K, group);
+  return mq::w4a16_gemv_blocked_workspace(M, N, K, kernel_group(group));
 }
 
 static mq_status w4a16_gemv_blocked_impl(const uint16_t* x, const int32_t* qweight_blocked,
@@ -516,13 +525,13 @@ static mq_status w4a16_gemv_blocked_impl(const uint16_t* x, const int32_t* qweig
     return fail(MQ_ERR_UNSUPPORTED, "GEMV needs M <= %lld (got %lld); use mq_w4a16_gemm",
                 (long long)mq::kGemvMaxM, (long long)M);
   if (M == 0) return ok();
-  const size_t need_ws = mq::w4a16_gemv_blocked_workspace(M, N, K, group);
+  const size_t need_ws = mq::w4a16_gemv_blocked_workspace(M, N, K, kernel_group(group));
   if (need_ws > 0) {
     if (!workspace || workspace_bytes < need_ws)
       return fail(MQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need_ws,
                   workspace ? workspace_bytes : static_cast<size_t>(0));
     if (!aligned(workspace, 16)) return fail(MQ_ERR_ALIGN, "workspace must be 16-byte aligned");
-    const size_t G = static_cast<size_t>(K / group);
+    const size_t G = group_rows(K, group);
     const Range in[] = {{x, static_cast<size_t>(M * K) * 2, "x"},
                         {qweight_blocked, static_cast<size_t>(K * (N / 8)) * 4, "qweight_blocked"},
                         {scales, G * static_cast<size_t>(N) * 2, "scales"},
@@ -531,7 +540,8 @@ static mq_status w4a16_gemv_blocked_impl(const uint16_t* x, const int32_t* qweig
     s = check_alias(in, out);
     if (s != MQ_OK) return s;
   }
-  const mq::GemvPlan plan = mq::plan_w4a16_gemv_blocked(M, N, K, group);
+  mq::GemvPlan plan = mq::plan_w4a16_gemv_blocked(M, N, K, kernel_group(group));
+  plan.per_channel = group == -1;
   return hip_status(mq::launch_w4a16_gemv_blocked(x, qweight_blocked, scales, qzeros, y, M, N, K, plan,
                                                   need_ws ? workspace : nullptr, bf16, as_stream(stream)),
                     "w4a16_gemv_blocked launch");

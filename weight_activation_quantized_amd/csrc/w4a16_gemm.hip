@@ -199,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
                                                          const uint32_t* __restrict__ qz,
                                                          uint16_t* __restrict__ y, float* __restrict__ partial,
                                                          int M, int N, int K, int tiles_m, int tiles_n,
-                                                         int per_xcd, int splits) {
+                                                         int per_xcd, int splits, int gstep) {
   __shared__ __attribute__((aligned(1024))) int8_t smem[kStages * kSlotBytes];
   lds_i8* const sm = (lds_i8*)(smem);
 
@@ -226,7 +226,9 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
   constexpr int kGS = kSPG * kRows;  // rows per group
   static_assert(4 % kSPG == 0, "a group is 1, 2 or 4 stages");
   const int NP = N >> 3;
-  const int G = K / kGS;
+  // gstep = 1: group g's scales and zero points are row g; gstep = 0
+  // (per-channel parameters): every group reads the one row.
+  const int G = gstep ? K / kGS : 1;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -272,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
 #define MQ_ISSUE(ST, SZ)                                                                             \
   do {                                                                                               \
     const int k0_ = k_base + (ST) * kRows;                                                           \
-    const int g_ = k0_ / kGS;                                                                        \
+    const int g_ = gstep * (k0_ / kGS);                                                              \
     const int so_ = ((ST) % kStages) * kSlotBytes;                                                   \
     const __amdgpu_buffer_rsrc_t rw_ =                                                               \
         rsrc(qw + static_cast<size_t>(k0_) * NP + c0, (static_cast<int64_t>(K - k0_) * NP - c0) * 4); \
@@ -583,7 +585,9 @@ size_t w4a16_gemm_workspace(int64_t M, int64_t N, int64_t K) {
 template <bool kBF>
 hipError_t launch_w4a16_gemm_t(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                                const int32_t* qzeros, uint16_t* y,
-                               int64_t M, int64_t N, int64_t K, int64_t group, void* workspace, hipStream_t stream) {
+                               int64_t M, int64_t N, int64_t K, int64_t group, bool per_channel, void* workspace,
+                               hipStream_t stream) {
+  const int gstep = per_channel ? 0 : 1;
   if (K % 128 || (group != 32 && group != 64 && group != 128)) return hipErrorInvalidValue;
   const int splits = workspace ? w4a16_gemm_splits(M, N, K) : 1;
   const int tiles_m = static_cast<int>((M + kBM - 1) / kBM);
@@ -599,15 +603,15 @@ hipError_t launch_w4a16_gemm_t(const uint16_t* x, const int32_t* qweight, const 
   switch (group) {
     case 32:
       err = launch_kernel(w4a16_gemm_kernel<1, kBF>, grid, dim3(kThreads), 0, stream, x, qw, scales, qz, y, part, m, n, k,
-                          tiles_m, tiles_n, per_xcd, splits);
+                          tiles_m, tiles_n, per_xcd, splits, gstep);
       break;
     case 64:
       err = launch_kernel(w4a16_gemm_kernel<2, kBF>, grid, dim3(kThreads), 0, stream, x, qw, scales, qz, y, part, m, n, k,
-                          tiles_m, tiles_n, per_xcd, splits);
+                          tiles_m, tiles_n, per_xcd, splits, gstep);
       break;
     default:
       err = launch_kernel(w4a16_gemm_kernel<4, kBF>, grid, dim3(kThreads), 0, stream, x, qw, scales, qz, y, part, m, n, k,
-                          tiles_m, tiles_n, per_xcd, splits);
+                          tiles_m, tiles_n, per_xcd, splits, gstep);
       break;
   }
   if (err != hipSuccess || splits == 1) return err;
@@ -618,9 +622,10 @@ hipError_t launch_w4a16_gemm_t(const uint16_t* x, const int32_t* qweight, const 
 
 hipError_t launch_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                              const int32_t* qzeros, uint16_t* y, int64_t M, int64_t N, int64_t K, int64_t group,
-                             void* workspace, bool bf16, hipStream_t stream) {
-  return bf16 ? launch_w4a16_gemm_t<true>(x, qweight, scales, qzeros, y, M, N, K, group, workspace, stream)
-              : launch_w4a16_gemm_t<false>(x, qweight, scales, qzeros, y, M, N, K, group, workspace, stream);
+                             bool per_channel, void* workspace, bool bf16, hipStream_t stream) {
+  return bf16 ? launch_w4a16_gemm_t<true>(x, qweight, scales, qzeros, y, M, N, K, group, per_channel, workspace, stream)
+              : launch_w4a16_gemm_t<false>(x, qweight, scales, qzeros, y, M, N, K, group, per_channel, workspace,
+                                           stream);
 }
 
 }  // namespace mq

@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256) void w4a16_gemv_lds_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qz,
     uint16_t* __restrict__ y, float* __restrict__ partial, int M, int N, int K, int strips, int splits,
-    XcdMap map) {
+    XcdMap map, int gstep) {
   constexpr int kLLoadsPerStage = lds_loads_per_stage<kT>();
   constexpr int kSPG = kGS / kLRows;             // 32-row steps per group
   constexpr int kMaxGroups = kLMaxRows / kGS;    // groups per split held in LDS
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(256) void w4a16_gemv_lds_kernel(
   {
     const int pc = min(lane, valid_cols - 1);
     for (int gi = wave; gi < Gs; gi += 4) {
-      const size_t g = static_cast<size_t>(g_begin + gi);
+      const size_t g = static_cast<size_t>(gstep) * static_cast<size_t>(g_begin + gi);  // gstep 0: per-channel
       const char* sp = reinterpret_cast<const char*>(scales) + (g * N + static_cast<size_t>(strip) * 512) * 2;
       __builtin_amdgcn_global_load_lds(sp + pc * 16, (lds_u32*)(s_sc) + gi * 256, 16, 0, 0);
       const char* zp = reinterpret_cast<const char*>(qz) + (g * NP + static_cast<size_t>(strip) * kLStrip) * 4;
@@ -351,7 +351,8 @@ struct GemvLane {
   uint32_t z_off;     // byte offset of the lane's word in a qzeros row
   uint32_t s_off;     // byte offset of the lane's 8 scales in a scales row
   size_t row_bytes;   // NP * 4
-  size_t srow_bytes;  // N * 2
+  size_t zrow_bytes;  // NP * 4, or 0 for per-channel zero points
+  size_t srow_bytes;  // N * 2, or 0 for per-channel scales
 };
 
 template <typename T>
@@ -369,7 +370,7 @@ __device__ __forceinline__ void load_group(GroupRegs<S>& r, const GemvLane L, in
   const char* xg = L.x + static_cast<size_t>(g) * (32 * S) * 2;
 #pragma unroll
   for (int ks = 0; ks < S; ++ks) r.a[ks] = load_at<f16x8>(xg + ks * 64, L.x_off);
-  r.zw = load_at<uint32_t>(L.qz + static_cast<size_t>(g) * L.row_bytes, L.z_off);
+  r.zw = load_at<uint32_t>(L.qz + static_cast<size_t>(g) * L.zrow_bytes, L.z_off);
   r.sv = load_at<u32x4>(L.sc + static_cast<size_t>(g) * L.srow_bytes, L.s_off);
 }
 
@@ -427,7 +428,7 @@ __global__ __launch_bounds__(NWC * 64) void w4a16_gemv_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qz,
     uint16_t* __restrict__ y, float* __restrict__ partial, int M, int N, int K, int strips, int splits,
-    XcdMap map) {
+    XcdMap map, int gstep) {
   int strip, split;
   if (!decode_work(blockIdx.x, map.strips_per_xcd, strips, splits, strip, split)) return;
   const int lane = threadIdx.x & 63;
@@ -453,7 +454,8 @@ __global__ __launch_bounds__(NWC * 64) void w4a16_gemv_kernel(
   L.z_off = static_cast<uint32_t>(cc) * 4u;
   L.s_off = static_cast<uint32_t>(cc) * 16u;
   L.row_bytes = static_cast<size_t>(NP) * 4;
-  L.srow_bytes = static_cast<size_t>(N) * 2;
+  L.zrow_bytes = static_cast<size_t>(gstep) * NP * 4;
+  L.srow_bytes = static_cast<size_t>(gstep) * N * 2;
 
   f32x4 tot[8];
 #pragma unroll
@@ -555,28 +557,28 @@ hipError_t launch_gemv_main(const uint16_t* x, const uint32_t* qw, const uint16_
     switch ((m + 15) / 16) {
       case 1:
         return launch_kernel(w4a16_gemv_lds_kernel<1, kGS, kBF>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part,
-                             m, n, k, strips, plan.splits, map);
+                             m, n, k, strips, plan.splits, map, plan.per_channel ? 0 : 1);
       case 2:
         return launch_kernel(w4a16_gemv_lds_kernel<2, kGS, kBF>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part,
-                             m, n, k, strips, plan.splits, map);
+                             m, n, k, strips, plan.splits, map, plan.per_channel ? 0 : 1);
       case 3:
         return launch_kernel(w4a16_gemv_lds_kernel<3, kGS, kBF>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part,
-                             m, n, k, strips, plan.splits, map);
+                             m, n, k, strips, plan.splits, map, plan.per_channel ? 0 : 1);
       default:
         return launch_kernel(w4a16_gemv_lds_kernel<4, kGS, kBF>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part,
-                             m, n, k, strips, plan.splits, map);
+                             m, n, k, strips, plan.splits, map, plan.per_channel ? 0 : 1);
     }
   }
   switch (plan.waves) {
     case 2:
       return launch_kernel(w4a16_gemv_kernel<2, kGS, kBF>, grid, dim3(128), 0, stream, x, qw, scales, qz, y, part, m, n,
-                           k, strips, plan.splits, map);
+                           k, strips, plan.splits, map, plan.per_channel ? 0 : 1);
     case 8:
       return launch_kernel(w4a16_gemv_kernel<8, kGS, kBF>, grid, dim3(512), 0, stream, x, qw, scales, qz, y, part, m, n,
-                           k, strips, plan.splits, map);
+                           k, strips, plan.splits, map, plan.per_channel ? 0 : 1);
     default:
       return launch_kernel(w4a16_gemv_kernel<4, kGS, kBF>, grid, dim3(256), 0, stream, x, qw, scales, qz, y, part, m, n,
-                           k, strips, plan.splits, map);
+                           k, strips, plan.splits, map, plan.per_channel ? 0 : 1);
   }
 }
 
@@ -604,8 +606,10 @@ hipError_t launch_w4a16_gemv(const uint16_t* x, const int32_t* qweight, const ui
     // consecutive 16-token slices (same stream, so they share the workspace).
     for (int64_t m0 = 0; m0 < M; m0 += 16) {
       const int64_t ms = M - m0 < 16 ? M - m0 : 16;
-      const hipError_t e = launch_w4a16_gemv(x + m0 * K, qweight, scales, qzeros, y + m0 * N, ms, N, K,
-                                             plan_w4a16_gemv(ms, N, K, plan.group), workspace, bf16, stream);
+      GemvPlan sub = plan_w4a16_gemv(ms, N, K, plan.group);
+      sub.per_channel = plan.per_channel;
+      const hipError_t e = launch_w4a16_gemv(x + m0 * K, qweight, scales, qzeros, y + m0 * N, ms, N, K, sub,
+                                             workspace, bf16, stream);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;

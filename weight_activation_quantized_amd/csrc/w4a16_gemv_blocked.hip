@@ -121,7 +121,7 @@ struct BLane {
   const uint16_t* x[4];   // token row of each tile (nullptr: row >= M)
   const uint16_t* sc;     // scales + 8 * packed column + 2g
   const uint32_t* qz;     // qzeros + packed column
-  int N, NP;
+  int N, NP;  // row strides of scales and qzeros between groups (0: per-channel)
 };
 
 template <int kT, int kGS, int kSP, bool kXL>
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(kW * 64)
 __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kGS >= 64 ? 3 : 1)))) void w4a16_gemv_blocked_kernel(
     const uint16_t* __restrict__ x, const u32x4* __restrict__ qb, const uint16_t* __restrict__ scales,
     const uint32_t* __restrict__ qz, uint16_t* __restrict__ y, float* __restrict__ partial, int M, int N, int K,
-    int units, int splits, XcdMap map) {
+    int units, int splits, XcdMap map, int gstep) {
   constexpr int kGPC = kBChunkRows / kGS;
   constexpr int kUOut = kSP * kBOut;  // outputs per unit
   constexpr bool kPS = kT >= 3;       // pre-scaled weights
@@ -403,8 +403,10 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
   }
   L.sc = scales + static_cast<size_t>(col) * 8 + 2 * g;
   L.qz = qz + col;
-  L.N = N;
-  L.NP = NP;
+  // gstep = 1: group g's scales and zero points are row g; gstep = 0
+  // (per-channel parameters): every group reads the one row.
+  L.N = gstep * N;
+  L.NP = gstep * NP;
 
   const NibConst nc = nib_const();
   const f16x8 ones = ones_fragment<kBF>();
@@ -456,10 +458,10 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
       const int grp0 = kbase * kGPC;
       for (int e = threadIdx.x; e < ngr * kSP * 4; e += kW * 64) {
         const int gl = e / (kSP * 4), sp = (e / 4) % kSP, v = e % 4;
-        const u32x4 val = *reinterpret_cast<const u32x4*>(scales + static_cast<size_t>(grp0 + gl) * N +
+        const u32x4 val = *reinterpret_cast<const u32x4*>(scales + static_cast<size_t>(grp0 + gl) * L.N +
                                                           (strip + sp) * kBOut + 8 * v);
         *(lds_u32x4*)(sct + (gl * kSP + sp) * 64 + 16 * v) = val;
-        const uint32_t zv = qz[static_cast<size_t>(grp0 + gl) * NP + (strip + sp) * kBStrip + v];
+        const uint32_t zv = qz[static_cast<size_t>(grp0 + gl) * L.NP + (strip + sp) * kBStrip + v];
         *(lds_u32*)(zt + (gl * kSP + sp) * 16 + 4 * v) = zv;
       }
       __syncthreads();
@@ -553,10 +555,10 @@ hipError_t launch_blocked_xl(const uint16_t* x, const u32x4* qb, const uint16_t*
   switch (plan.waves) {
     case 1:
       return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 1, kSP, kXL, kBF>, grid, dim3(64), lds, stream, x, qb,
-                           scales, qz, y, part, m, n, k, units, plan.splits, map);
+                           scales, qz, y, part, m, n, k, units, plan.splits, map, plan.per_channel ? 0 : 1);
     case 2:
       return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 2, kSP, kXL, kBF>, grid, dim3(128), lds, stream, x, qb,
-                           scales, qz, y, part, m, n, k, units, plan.splits, map);
+                           scales, qz, y, part, m, n, k, units, plan.splits, map, plan.per_channel ? 0 : 1);
     case 8:
     case 16:
       // only the one-strip forms with x staged in LDS (up to 4 tokens,
@@ -564,15 +566,15 @@ hipError_t launch_blocked_xl(const uint16_t* x, const u32x4* qb, const uint16_t*
       if constexpr (kT == 1 && kSP == 1 && kXL) {
         if (plan.waves == 8)
           return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 8, kSP, kXL, kBF>, grid, dim3(512), lds, stream, x,
-                               qb, scales, qz, y, part, m, n, k, units, plan.splits, map);
+                               qb, scales, qz, y, part, m, n, k, units, plan.splits, map, plan.per_channel ? 0 : 1);
         return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 16, kSP, kXL, kBF>, grid, dim3(1024), lds, stream, x,
-                             qb, scales, qz, y, part, m, n, k, units, plan.splits, map);
+                             qb, scales, qz, y, part, m, n, k, units, plan.splits, map, plan.per_channel ? 0 : 1);
       } else {
         return hipErrorInvalidValue;
       }
     default:
       return launch_kernel(w4a16_gemv_blocked_kernel<kT, kGS, 4, kSP, kXL, kBF>, grid, dim3(256), lds, stream, x, qb,
-                           scales, qz, y, part, m, n, k, units, plan.splits, map);
+                           scales, qz, y, part, m, n, k, units, plan.splits, map, plan.per_channel ? 0 : 1);
   }
 }
 
