@@ -19,6 +19,9 @@ Entry points (same names as the C ABI, without the ``mq_`` prefix):
     w4a16_gemv_blocked(x, qweight_blocked, scales, qzeros, group) -> y (x's dtype), M <= 64
     w4a16_gemv_blocked_workspace_bytes(M, N, K, group) -> int
 
+    (W4A16 group: 32, 64 or 128 rows per scale / zero point, or -1 for one
+    per output column over all of K: scales [1, N], qzeros [1, N/8].)
+
     kv_quant(x, bits)                                -> (codes, params) per (token, head) row
 
     int4_reorder(words, order)                       -> words in the library's field order
