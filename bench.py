@@ -94,7 +94,8 @@ GEMV_SOURCES = ["w4a16_gemv_blocked.hip", "w4a16_split.h", "w4a16_common.h", "de
 
 
 def w4a16_bytes(M, K, N, G=GROUP):
-    return M * K * 2 + K * N // 2 + (K // G) * N * 2 + (K // G) * (N // 8) * 4 + M * N * 2
+    rows = 1 if G == -1 else K // G  # group -1: one parameter row (per-channel)
+    return M * K * 2 + K * N // 2 + rows * N * 2 + rows * (N // 8) * 4 + M * N * 2
 
 
 def gemv_source_hash():
@@ -404,7 +405,8 @@ def bench_layers(torch, mq, synth, args, log):
 
 
 def bench_groups(torch, mq, synth, log):
-    """W4A16 with groups of 64 and 32 rows: GEMV and GEMM shapes, cold weights
+    """W4A16 with groups of 64 and 32 rows and with per-channel parameters
+    (group -1, reported as "per_channel"): GEMV and GEMM shapes, cold weights
     (copies totalling >= 640 MB), microseconds per call from graph replays."""
     dev = torch.device("cuda", 0)
     R = 20
@@ -418,11 +420,12 @@ def bench_groups(torch, mq, synth, log):
     out = {}
     shapes = [("gate_up", 4096, 24576, (1, 4, 16)), ("vit_qkv", 1024, 3072, (1, 16, 577, 4096)),
               ("o_proj_prefill", 4096, 4096, (4096,))]
-    for G in (64, 32):
-        out[f"g{G}"] = {}
+    for G in (64, 32, -1):
+        key = "per_channel" if G == -1 else f"g{G}"
+        out[key] = {}
         for name, K, N, Ms in shapes:
             log(f"groups: G={G} {name} K={K} N={N}")
-            w = {k: torch.from_numpy(v).to(dev) for k, v in synth.w4a16_weights(K, N, G, tag=400 + G).items()}
+            w = {k: torch.from_numpy(v).to(dev) for k, v in synth.w4a16_weights(K, N, G, tag=400 + abs(G)).items()}
             w["qblocked"] = mq.w4a16_block_weights(w["qweight"])
             wbytes = K * N // 2
             n = max(2, -(-640 * 2**20 // wbytes))
@@ -431,7 +434,7 @@ def bench_groups(torch, mq, synth, log):
             res = {}
             for M in Ms:
                 x = torch.from_numpy(synth.w4a16_inputs(M, K, 8, G, outlier_frac=0.005 if M <= 64 else 0.0,
-                                                        tag=410 + G, seed=M)["x"]).to(dev)
+                                                        tag=410 + abs(G), seed=M)["x"]).to(dev)
                 y = torch.empty((M, N), dtype=torch.float16, device=dev)
                 if M <= mq.GEMV_MAX_M:
                     ws = torch.zeros(max(mq.w4a16_gemv_blocked_workspace_bytes(M, N, K, G), 16), dtype=torch.uint8,
@@ -454,7 +457,7 @@ def bench_groups(torch, mq, synth, log):
                                "hbm_frac": round(nbytes / t / 1e9 / HBM_PEAK_GBPS, 4),
                                "TFLOPS": round(flops / t / 1e12, 1),
                                "fp16_frac": round(flops / t / 1e12 / FP16_PEAK_TFLOPS, 4)}
-            out[f"g{G}"][name] = res
+            out[key][name] = res
             del wsets
             torch.cuda.empty_cache()
     return out
