@@ -119,14 +119,23 @@ struct BLane {
   const u32x4* qb;        // the lane's 16-byte slot of the strip's first pair
   size_t pair_stride;     // slots from one 64-row pair to the next (S * 64)
   const uint16_t* x[4];   // token row of each tile (nullptr: row >= M)
+  // Pre-scaled form: x moves into the wavefront's LDS slot by DMA. xr covers
+  // the M token rows (rows past M read as zero); load q of a chunk fills
+  // slot rows 4q .. 4q+3 and reads from byte xdma[q % 4] + (q / 4) * xtile
+  // + 256 * chunk.
+  __amdgpu_buffer_rsrc_t xr;
+  uint32_t xdma[4];
+  uint32_t xtile;         // 16 token rows of x in bytes
   const uint16_t* sc;     // scales + 8 * packed column + 2g
   const uint32_t* qz;     // qzeros + packed column
   int N, NP;  // row strides of scales and qzeros between groups (0: per-channel)
 };
 
 template <int kT, int kGS, int kSP, bool kXL>
-__device__ __forceinline__ void load_chunk(BChunk<kT, kBChunkRows / kGS, kSP>& ch, const BLane& L, int chunk) {
+__device__ __forceinline__ void load_chunk(BChunk<kT, kBChunkRows / kGS, kSP>& ch, const BLane& L, int chunk,
+                                           lds_u8* xslot = nullptr) {
   constexpr int kGPC = kBChunkRows / kGS;
+  constexpr bool kPS = kT >= 3;  // pre-scaled form: x through the wavefront's LDS slot
   const u32x4* wp = L.qb + static_cast<size_t>(2 * chunk) * L.pair_stride;
   // The weights are read once per call: non-temporal loads (about 1% faster
   // than ordinary ones, measured) keep them from displacing cached data.
@@ -136,8 +145,18 @@ __device__ __forceinline__ void load_chunk(BChunk<kT, kBChunkRows / kGS, kSP>& c
     ch.w[sp][1] = __builtin_nontemporal_load(wp + L.pair_stride + 64 * sp);
   }
   // With x in LDS the fragments are read at use (compute_chunk); otherwise
-  // each lane loads its token row's 8 values of each 32-row block.
-  if constexpr (!kXL) {
+  // each lane loads its token row's 8 values of each 32-row block. The
+  // pre-scaled form (33-64 tokens) instead moves the chunk's 16 token rows
+  // per tile x 128 values into its slot by DMA, 1 KB per load: the slot's
+  // previous contents were read by the compute before this call, and
+  // lgkmcnt(0) makes sure those reads have returned.
+  if constexpr (kPS) {
+    wait_counts<63, 0>();
+#pragma unroll
+    for (int q = 0; q < 4 * kT; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(L.xr, (lds_void*)(xslot + 1024 * q), 16,
+                                               L.xdma[q % 4] + (q / 4) * L.xtile + 256u * chunk, 0, 0, 0);
+  } else if constexpr (!kXL) {
 #pragma unroll
     for (int t = 0; t < kT; ++t)
 #pragma unroll
@@ -309,45 +328,57 @@ __device__ __forceinline__ void unpack_block_scaled(uint32_t w0, uint32_t w1, co
 // running sums (the weights carry their scales), so no per-group partial
 // sums or sums of x are kept -- that is what lets three strips share every
 // x fragment of four token tiles within the register file.
+// xs: the lane's row (token j of tile 0) of the chunk in the wavefront's
+// slot (256 bytes per row, 16-byte chunk index XOR-ed with the row mod 16);
+// xo[b]: the byte offset of block b's 8 values of the lane (rows 8h..).
 template <int kT, int kGS, int kSP, bool kBF>
 __device__ __forceinline__ void compute_chunk_scaled(const BChunk<kT, kBChunkRows / kGS, kSP>& ch,
-                                                     const NibConst& nc, int g_lane, f32x4 (&tot)[kT][kSP][2]) {
+                                                     const NibConst& nc, int g_lane, f32x4 (&tot)[kT][kSP][2],
+                                                     const lds_u8* xs, const int (&xo)[4]) {
   constexpr int kGPC = kBChunkRows / kGS;
   constexpr int kBPG = kGS / 32;
 #pragma unroll
-  for (int g = 0; g < kGPC; ++g)
+  for (int g = 0; g < kGPC; ++g) {
+    uint32_t nz[kSP][2], s2[kSP][2];
 #pragma unroll
     for (int sp = 0; sp < kSP; ++sp) {
       const f16x2 sv = as_f16x2(ch.sv[sp][g]);
       const uint32_t zb = (ch.zw[sp][g] >> (8 * g_lane)) & 0xFFu;
-      uint32_t nz[2], s2[2];
       if constexpr (kBF) {
         const float sl = static_cast<float>(sv[0]), sh = static_cast<float>(sv[1]);
-        nz[0] = __builtin_bit_cast(uint32_t, -(1024.0f + static_cast<float>(zb & 15u)) * sl);
-        nz[1] = __builtin_bit_cast(uint32_t, -(64.0f + static_cast<float>(zb >> 4)) * sh);
-        s2[0] = __builtin_bit_cast(uint32_t, sl);
-        s2[1] = __builtin_bit_cast(uint32_t, sh);
+        nz[sp][0] = __builtin_bit_cast(uint32_t, -(1024.0f + static_cast<float>(zb & 15u)) * sl);
+        nz[sp][1] = __builtin_bit_cast(uint32_t, -(64.0f + static_cast<float>(zb >> 4)) * sh);
+        s2[sp][0] = __builtin_bit_cast(uint32_t, sl);
+        s2[sp][1] = __builtin_bit_cast(uint32_t, sh);
       } else {
         f16x2 s_lo, s_hi;
         s_lo[0] = s_lo[1] = sv[0];
         s_hi[0] = s_hi[1] = sv[1];
         const uint32_t e_lo = (zb & 0x0Fu) | 0xE400u, e_hi = (zb & 0xF0u) | 0xD400u;
-        nz[0] = e_lo | (e_lo << 16);
-        nz[1] = e_hi | (e_hi << 16);
-        s2[0] = as_u32(s_lo);
-        s2[1] = as_u32(s_hi);
+        nz[sp][0] = e_lo | (e_lo << 16);
+        nz[sp][1] = e_hi | (e_hi << 16);
+        s2[sp][0] = as_u32(s_lo);
+        s2[sp][1] = as_u32(s_hi);
       }
+    }
 #pragma unroll
-      for (int bb = 0; bb < kBPG; ++bb) {
-        const int b = g * kBPG + bb;
+    for (int bb = 0; bb < kBPG; ++bb) {
+      const int b = g * kBPG + bb;
+      f16x8 xa[kT];  // the block's x fragments, shared by the strips
+#pragma unroll
+      for (int t = 0; t < kT; ++t) xa[t] = *(const lds_f16x8*)(xs + 4096 * t + xo[b]);
+#pragma unroll
+      for (int sp = 0; sp < kSP; ++sp) {
         f16x8 bf[2];
-        unpack_block_scaled<kBF>(ch.w[sp][b >> 1][2 * (b & 1)], ch.w[sp][b >> 1][2 * (b & 1) + 1], nc, nz, s2, bf);
+        unpack_block_scaled<kBF>(ch.w[sp][b >> 1][2 * (b & 1)], ch.w[sp][b >> 1][2 * (b & 1) + 1], nc, nz[sp],
+                                 s2[sp], bf);
 #pragma unroll
         for (int t = 0; t < kT; ++t)
 #pragma unroll
-          for (int f = 0; f < 2; ++f) tot[t][sp][f] = mfma_16x16x32<kBF>(ch.a[t][b], bf[f], tot[t][sp][f]);
+          for (int f = 0; f < 2; ++f) tot[t][sp][f] = mfma_16x16x32<kBF>(xa[t], bf[f], tot[t][sp][f]);
       }
     }
+  }
 }
 
 // kT 16-token tiles, groups of kGS rows, kW wavefronts per workgroup, kSP
@@ -403,6 +434,30 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
   }
   L.sc = scales + static_cast<size_t>(col) * 8 + 2 * g;
   L.qz = qz + col;
+  // Pre-scaled form: each wavefront has two LDS slots (one per chunk buffer)
+  // of 16 kT rows x 256 bytes. Load q fills rows 4q .. 4q+3: lane l writes
+  // physical 16-byte chunk l % 16 of row 4q + l / 16 and fetches the logical
+  // chunk (l % 16) ^ (row % 16) there, so the fragment reads (16 rows of one
+  // logical chunk per 16 lanes) fall on 16 different bank groups.
+  lds_u8* xslot[2] = {nullptr, nullptr};
+  const lds_u8* xs[2] = {nullptr, nullptr};
+  int xo[4] = {0, 0, 0, 0};
+  if constexpr (kPS) {
+    L.xr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), 0, M * K * 2, 0x00020000);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int r = 4 * qq + lane / 16;  // row within a 16-row tile (= row mod 16)
+      L.xdma[qq] = static_cast<uint32_t>(r * K + 8 * ((lane % 16) ^ r)) * 2u;
+    }
+    L.xtile = static_cast<uint32_t>(16 * K) * 2u;
+    lds_u8* const base = (lds_u8*)(x_dyn) + wave * 2 * (kT * 4096);
+    xslot[0] = base;
+    xslot[1] = base + kT * 4096;
+    xs[0] = xslot[0] + 256 * j;
+    xs[1] = xslot[1] + 256 * j;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) xo[b] = 16 * ((4 * b + h) ^ j);
+  }
   // gstep = 1: group g's scales and zero points are row g; gstep = 0
   // (per-channel parameters): every group reads the one row.
   L.N = gstep * N;
@@ -431,8 +486,10 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
   // slower (see the layout notes).
   {
     BChunk<kT, kGPC, kSP> ca, cb;
-    load_chunk<kT, kGS, kSP, kXL>(ca, L, c0);
-    load_chunk<kT, kGS, kSP, kXL>(cb, L, min(c0 + 1, c0 + cpw - 1));
+    load_chunk<kT, kGS, kSP, kXL>(ca, L, c0, xslot[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    load_chunk<kT, kGS, kSP, kXL>(cb, L, min(c0 + 1, c0 + cpw - 1), xslot[1]);
+    __builtin_amdgcn_sched_barrier(0);
     // Staged x: the lane's row (token j, rows 8h.. of each block) at the
     // split's first chunk; lanes past the last token read nothing.
     const lds_u8* xrow = nullptr;
@@ -474,28 +531,42 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
     };
     auto sl = [&](int chunk) -> const lds_u8* { return sc_lane + (chunk - kbase) * kGPC * kSP * 64; };
     auto zl = [&](int chunk) -> const lds_u8* { return z_lane + (chunk - kbase) * kGPC * kSP * 16; };
-    auto compute = [&](const BChunk<kT, kGPC, kSP>& ch, int chunk) {
+    // Pre-scaled form: before a buffer's compute its DMA must have landed.
+    // Loads complete in issue order, and every load of the other buffer's
+    // next chunk was issued after this one's (sched_barrier between the
+    // requests): waiting down to that chunk's count (kChunkLoads) leaves
+    // only those in flight; where no later chunk was requested, wait for all.
+    constexpr int kChunkLoads = 2 * kSP + 4 * kT + 2 * kSP * kGPC;
+    static_assert(!kPS || kChunkLoads < 64, "vmcnt range");
+    auto compute = [&](const BChunk<kT, kGPC, kSP>& ch, int chunk, int buf) {
       if constexpr (kPS) {
-        compute_chunk_scaled<kT, kGS, kSP, kBF>(ch, nc, g, tot);
+        compute_chunk_scaled<kT, kGS, kSP, kBF>(ch, nc, g, tot, xs[buf], xo);
       } else {
         compute_chunk<kT, kGS, kSP, kXL, kBF>(ch, nc, ones, g, tot, xl(chunk), sl(chunk), zl(chunk));
       }
     };
     int i = 0;
     for (; i + 3 < cpw; i += 2) {
-      compute(ca, c0 + i);
-      load_chunk<kT, kGS, kSP, kXL>(ca, L, c0 + i + 2);
+      if constexpr (kPS) wait_counts<kChunkLoads, 15>();
+      compute(ca, c0 + i, 0);
       __builtin_amdgcn_sched_barrier(0);
-      compute(cb, c0 + i + 1);
-      load_chunk<kT, kGS, kSP, kXL>(cb, L, c0 + i + 3);
+      load_chunk<kT, kGS, kSP, kXL>(ca, L, c0 + i + 2, xslot[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kPS) wait_counts<kChunkLoads, 15>();
+      compute(cb, c0 + i + 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_chunk<kT, kGS, kSP, kXL>(cb, L, c0 + i + 3, xslot[1]);
       __builtin_amdgcn_sched_barrier(0);
     }
     // chunks i and (if in range) i + 1 are in flight; at most i + 2 is left
-    compute(ca, c0 + i);
-    if (i + 2 < cpw) load_chunk<kT, kGS, kSP, kXL>(ca, L, c0 + i + 2);
+    if constexpr (kPS) wait_counts<kChunkLoads, 15>();
+    compute(ca, c0 + i, 0);
     __builtin_amdgcn_sched_barrier(0);
-    if (i + 1 < cpw) compute(cb, c0 + i + 1);
-    if (i + 2 < cpw) compute(ca, c0 + i + 2);
+    if (i + 2 < cpw) load_chunk<kT, kGS, kSP, kXL>(ca, L, c0 + i + 2, xslot[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kPS) wait_counts<0, 15>();
+    if (i + 1 < cpw) compute(cb, c0 + i + 1, 1);
+    if (i + 2 < cpw) compute(ca, c0 + i + 2, 0);
   }
 
   // Add the wavefronts' sums in wavefront order. Lane (j, h) holds token
@@ -612,15 +683,17 @@ template <int kT, int kGS, bool kBF>
 hipError_t launch_blocked_scaled(const uint16_t* x, const u32x4* qb, const uint16_t* scales, const uint32_t* qz,
                                  uint16_t* y, float* part, int m, int n, int k, const GemvPlan& plan, int units,
                                  XcdMap map, dim3 grid, hipStream_t stream) {
+  // two LDS slots of 16 kT token rows x 256 bytes per wavefront (the x DMA)
+  const size_t lds = static_cast<size_t>(plan.waves) * 2 * kT * 4096;
   if constexpr (kGS >= 64) {
     if (plan.strips_per_unit == 3)
-      return launch_blocked_xl<kT, kGS, 3, false, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, 0,
+      return launch_blocked_xl<kT, kGS, 3, false, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, lds,
                                                   stream);
     if (plan.strips_per_unit == 2)
-      return launch_blocked_xl<kT, kGS, 2, false, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, 0,
+      return launch_blocked_xl<kT, kGS, 2, false, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, lds,
                                                   stream);
   }
-  return launch_blocked_xl<kT, kGS, 1, false, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, 0,
+  return launch_blocked_xl<kT, kGS, 1, false, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, lds,
                                               stream);
 }
 
