@@ -104,13 +104,11 @@ __global__ __launch_bounds__(256) void w4a16_block_weights_kernel(const uint32_t
 }
 
 // One chunk (128 rows) of a lane's operands for kSP adjacent strips: 32
-// weight bytes per strip (two 16-byte pair slots), the x fragments of each
-// token tile (rows 8h..8h+7 of each 32-row block, shared by the strips),
-// and per strip the two scales and the zero-point byte of each group.
+// weight bytes per strip (two 16-byte pair slots) and per strip the two
+// scales and the zero-point byte of each group (x comes from LDS).
 template <int kT, int kGPC, int kSP>
 struct BChunk {
   u32x4 w[kSP][2];
-  f16x8 a[kT][4];
   uint32_t sv[kSP][kGPC];  // fp16 pair: s of field 2g, s of field 2g+1
   uint32_t zw[kSP][kGPC];  // zero-point word of the packed column (byte g used)
 };
@@ -118,8 +116,7 @@ struct BChunk {
 struct BLane {
   const u32x4* qb;        // the lane's 16-byte slot of the strip's first pair
   size_t pair_stride;     // slots from one 64-row pair to the next (S * 64)
-  const uint16_t* x[4];   // token row of each tile (nullptr: row >= M)
-  // Pre-scaled form: x moves into the wavefront's LDS slot by DMA. xr covers
+  // Without kXL, x moves into the wavefront's LDS slot by DMA. xr covers
   // the M token rows (rows past M read as zero); load q of a chunk fills
   // slot rows 4q .. 4q+3 and reads from byte xdma[q % 4] + (q / 4) * xtile
   // + 256 * chunk.
@@ -135,7 +132,8 @@ template <int kT, int kGS, int kSP, bool kXL>
 __device__ __forceinline__ void load_chunk(BChunk<kT, kBChunkRows / kGS, kSP>& ch, const BLane& L, int chunk,
                                            lds_u8* xslot = nullptr) {
   constexpr int kGPC = kBChunkRows / kGS;
-  constexpr bool kPS = kT >= 3;  // pre-scaled form: x through the wavefront's LDS slot
+  // forms without x staged up front (kXL) move each chunk's x through the
+  // wavefront's LDS slot
   const u32x4* wp = L.qb + static_cast<size_t>(2 * chunk) * L.pair_stride;
   // The weights are read once per call: non-temporal loads (about 1% faster
   // than ordinary ones, measured) keep them from displacing cached data.
@@ -144,29 +142,18 @@ __device__ __forceinline__ void load_chunk(BChunk<kT, kBChunkRows / kGS, kSP>& c
     ch.w[sp][0] = __builtin_nontemporal_load(wp + 64 * sp);
     ch.w[sp][1] = __builtin_nontemporal_load(wp + L.pair_stride + 64 * sp);
   }
-  // With x in LDS the fragments are read at use (compute_chunk); otherwise
-  // each lane loads its token row's 8 values of each 32-row block. The
-  // pre-scaled form (33-64 tokens) instead moves the chunk's 16 token rows
-  // per tile x 128 values into its slot by DMA, 1 KB per load: the slot's
+  // With x staged up front (kXL) the fragments are read at use from there;
+  // otherwise the chunk's 16 token rows per tile x 128 values move into the
+  // wavefront's slot by DMA, 1 KB per load (full cache lines, where register
+  // loads of the fragments would each take 16 half lines): the slot's
   // previous contents were read by the compute before this call, and
   // lgkmcnt(0) makes sure those reads have returned.
-  if constexpr (kPS) {
+  if constexpr (!kXL) {
     wait_counts<63, 0>();
 #pragma unroll
     for (int q = 0; q < 4 * kT; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(L.xr, (lds_void*)(xslot + 1024 * q), 16,
                                                L.xdma[q % 4] + (q / 4) * L.xtile + 256u * chunk, 0, 0, 0);
-  } else if constexpr (!kXL) {
-#pragma unroll
-    for (int t = 0; t < kT; ++t)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        if (L.x[t]) {
-          ch.a[t][b] = *reinterpret_cast<const f16x8*>(L.x[t] + chunk * kBChunkRows + 32 * b);
-        } else {
-          ch.a[t][b] = f16x8{};
-        }
-      }
   }
   if constexpr (!kXL) {  // with kXL the scales and zero points are staged in LDS too
 #pragma unroll
@@ -213,7 +200,8 @@ __device__ __forceinline__ void unpack_block(uint32_t w0, uint32_t w1, const Nib
 template <int kT, int kGS, int kSP, bool kXL, bool kBF>
 __device__ __forceinline__ void compute_chunk(const BChunk<kT, kBChunkRows / kGS, kSP>& ch, const NibConst& nc,
                                               const f16x8 ones, int g_lane, f32x4 (&tot)[kT][kSP][2],
-                                              const lds_u8* xl, const lds_u8* scl, const lds_u8* zl) {
+                                              const lds_u8* xl, const lds_u8* scl, const lds_u8* zl,
+                                              const lds_u8* xs, const int (&xo)[4]) {
   constexpr int kGPC = kBChunkRows / kGS;  // groups per chunk
   constexpr int kBPG = kGS / 32;           // 32-row blocks per group
   const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -242,8 +230,8 @@ __device__ __forceinline__ void compute_chunk(const BChunk<kT, kBChunkRows / kGS
     for (int b = 0; b < 4; ++b) {
       if constexpr (kXL) {
         xa[t][b] = xl ? *reinterpret_cast<const lds_f16x8*>(xl + 64 * b) : f16x8{};
-      } else {
-        xa[t][b] = ch.a[t][b];
+      } else {  // the chunk's slot: token row 16t + j, rows 8h.. of block b
+        xa[t][b] = *(const lds_f16x8*)(xs + 4096 * t + xo[b]);
       }
     }
 #pragma unroll
@@ -405,7 +393,7 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
   constexpr int kGPC = kBChunkRows / kGS;
   constexpr int kUOut = kSP * kBOut;  // outputs per unit
   constexpr bool kPS = kT >= 3;       // pre-scaled weights
-  static_assert(!(kPS && kXL), "the pre-scaled form loads x per chunk");
+  static_assert(!(kPS && kXL), "the pre-scaled form takes x through the LDS slots");
   __shared__ float s_red[(kPS ? 1 : kW) * 16 * kT * kUOut];
   extern __shared__ __attribute__((aligned(16))) uint8_t x_dyn[];  // kXL: M rows of staged x
 
@@ -427,14 +415,9 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
   BLane L;
   L.qb = qb + static_cast<size_t>(strip) * 64 + lane;
   L.pair_stride = static_cast<size_t>(NP / kBStrip) * 64;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int m = 16 * t + j;
-    L.x[t] = (t < kT && m < M) ? x + static_cast<size_t>(m) * K + 8 * h : nullptr;
-  }
   L.sc = scales + static_cast<size_t>(col) * 8 + 2 * g;
   L.qz = qz + col;
-  // Pre-scaled form: each wavefront has two LDS slots (one per chunk buffer)
+  // Without kXL each wavefront has two LDS slots (one per chunk buffer)
   // of 16 kT rows x 256 bytes. Load q fills rows 4q .. 4q+3: lane l writes
   // physical 16-byte chunk l % 16 of row 4q + l / 16 and fetches the logical
   // chunk (l % 16) ^ (row % 16) there, so the fragment reads (16 rows of one
@@ -442,7 +425,7 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
   lds_u8* xslot[2] = {nullptr, nullptr};
   const lds_u8* xs[2] = {nullptr, nullptr};
   int xo[4] = {0, 0, 0, 0};
-  if constexpr (kPS) {
+  if constexpr (!kXL) {
     L.xr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), 0, M * K * 2, 0x00020000);
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
@@ -531,40 +514,40 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
     };
     auto sl = [&](int chunk) -> const lds_u8* { return sc_lane + (chunk - kbase) * kGPC * kSP * 64; };
     auto zl = [&](int chunk) -> const lds_u8* { return z_lane + (chunk - kbase) * kGPC * kSP * 16; };
-    // Pre-scaled form: before a buffer's compute its DMA must have landed.
+    // Without kXL, before a buffer's compute its DMA must have landed.
     // Loads complete in issue order, and every load of the other buffer's
     // next chunk was issued after this one's (sched_barrier between the
     // requests): waiting down to that chunk's count (kChunkLoads) leaves
     // only those in flight; where no later chunk was requested, wait for all.
     constexpr int kChunkLoads = 2 * kSP + 4 * kT + 2 * kSP * kGPC;
-    static_assert(!kPS || kChunkLoads < 64, "vmcnt range");
+    static_assert(kXL || kChunkLoads < 64, "vmcnt range");
     auto compute = [&](const BChunk<kT, kGPC, kSP>& ch, int chunk, int buf) {
       if constexpr (kPS) {
         compute_chunk_scaled<kT, kGS, kSP, kBF>(ch, nc, g, tot, xs[buf], xo);
       } else {
-        compute_chunk<kT, kGS, kSP, kXL, kBF>(ch, nc, ones, g, tot, xl(chunk), sl(chunk), zl(chunk));
+        compute_chunk<kT, kGS, kSP, kXL, kBF>(ch, nc, ones, g, tot, xl(chunk), sl(chunk), zl(chunk), xs[buf], xo);
       }
     };
     int i = 0;
     for (; i + 3 < cpw; i += 2) {
-      if constexpr (kPS) wait_counts<kChunkLoads, 15>();
+      if constexpr (!kXL) wait_counts<kChunkLoads, 15>();
       compute(ca, c0 + i, 0);
       __builtin_amdgcn_sched_barrier(0);
       load_chunk<kT, kGS, kSP, kXL>(ca, L, c0 + i + 2, xslot[0]);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (kPS) wait_counts<kChunkLoads, 15>();
+      if constexpr (!kXL) wait_counts<kChunkLoads, 15>();
       compute(cb, c0 + i + 1, 1);
       __builtin_amdgcn_sched_barrier(0);
       load_chunk<kT, kGS, kSP, kXL>(cb, L, c0 + i + 3, xslot[1]);
       __builtin_amdgcn_sched_barrier(0);
     }
     // chunks i and (if in range) i + 1 are in flight; at most i + 2 is left
-    if constexpr (kPS) wait_counts<kChunkLoads, 15>();
+    if constexpr (!kXL) wait_counts<kChunkLoads, 15>();
     compute(ca, c0 + i, 0);
     __builtin_amdgcn_sched_barrier(0);
     if (i + 2 < cpw) load_chunk<kT, kGS, kSP, kXL>(ca, L, c0 + i + 2, xslot[0]);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kPS) wait_counts<0, 15>();
+    if constexpr (!kXL) wait_counts<0, 15>();
     if (i + 1 < cpw) compute(cb, c0 + i + 1, 1);
     if (i + 2 < cpw) compute(ca, c0 + i + 2, 0);
   }
@@ -675,7 +658,9 @@ hipError_t launch_blocked_main(const uint16_t* x, const u32x4* qb, const uint16_
       return launch_blocked_xl<kT, kGS, kSP, true, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid,
                                                    static_cast<size_t>(lds), stream);
   }
-  return launch_blocked_xl<kT, kGS, kSP, false, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, 0,
+  // two LDS slots of 16 kT token rows x 256 bytes per wavefront (the x DMA)
+  const size_t lds = static_cast<size_t>(plan.waves) * 2 * kT * 4096;
+  return launch_blocked_xl<kT, kGS, kSP, false, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, lds,
                                                 stream);
 }
 
