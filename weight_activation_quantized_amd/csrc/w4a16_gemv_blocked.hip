@@ -63,15 +63,16 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) f16x8 lds_f16x8;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
-// x staged in LDS (one-tile forms): the workgroup's token rows over its K
-// range, row pitch = 2 * range + 16 bytes (the 16 spreads the rows over the
-// banks). Only for up to 4 tokens: the copy happens before the stream
-// starts, and with 16 tokens (128 KB per workgroup at K = 4096) it held the
-// stream back more than the per-chunk x loads did (13.9 against 12.3 us per
-// call averaged over 1, 4 and 16 tokens); with 1 and 4 tokens it saves 1.3
-// and 0.7 us.
+// x staged in LDS up front (one-tile, one-strip forms): the workgroup's
+// token rows over its K range, row pitch = 2 * range + 16 bytes (the 16
+// spreads the rows over the banks), plus its strips' scales and zero
+// points. Used for one token where a unit has a single strip (groups of 32,
+// or strip counts 3 does not divide): there the per-chunk x DMA was slower
+// (12.5 against 11.4 us at N = 24576), while with 2-4 tokens it was faster
+// (12.5 against 12.8 us). The one-workgroup-per-strip form of narrow layers
+// stages up to 8 tokens this way.
 constexpr int kXLdsPad = 16;
-constexpr int64_t kXLdsMaxTokens = 4;
+constexpr int64_t kXLdsMaxTokens = 1;
 constexpr int64_t kWideMaxTokens = 8;  // one-workgroup-per-strip form (see the plan)
 constexpr int64_t kLdsPerWorkgroup = 160 * 1024;
 
@@ -640,6 +641,9 @@ int64_t blocked_x_lds_bytes(int64_t M, int64_t K, int64_t group, int splits, int
   const int64_t kr = K / splits;
   const int64_t xb = std::min<int64_t>(M, 16) * (2 * kr + kXLdsPad);
   const int64_t szb = (kr / group) * strips_per_unit * (64 + 16);
+  // x staged up front only where a unit has a single strip (several strips
+  // share the per-chunk DMA slots instead)
+  if (strips_per_unit > 1) return 0;
   const int64_t red = int64_t{waves} * 16 * strips_per_unit * kBOut * 4;
   // the one-workgroup-per-strip form (8 or 16 wavefronts) stages up to 8
   // tokens: it has no stream to hold back before the copy
@@ -736,9 +740,11 @@ GemvPlan plan_w4a16_gemv_blocked(int64_t M, int64_t N, int64_t K, int64_t group)
       return plan;  // splits = 1, no workspace
     }
   }
-  // Every workgroup loads all of x for its K range, so with more than a few
-  // tokens a workgroup takes several adjacent strips that share those loads
-  // (three for one 16-token tile, two for two; what divides the strips).
+  // Every workgroup loads all of x for its K range, so a workgroup takes
+  // several adjacent strips that share those loads through its LDS slots
+  // (three for one 16-token tile, two for two; what divides the strips;
+  // at N = 24576: 4 tokens 12.8 -> 11.5 us, one token 11.9 -> 11.3 us with
+  // three strips against one strip with x staged up front).
   // With three or four tiles a workgroup needs every register (one per
   // CU), and the x fragments, read once per strip group, cost more than
   // the weights: the unit takes the most strips (3, then 2) for which
@@ -756,10 +762,10 @@ GemvPlan plan_w4a16_gemv_blocked(int64_t M, int64_t N, int64_t K, int64_t group)
         break;
       }
     }
-  } else if (mt > 4 && group >= 64) {
+  } else if (group >= 64) {
     if (mt <= 16 && strips % 3 == 0) {
       sp = 3;
-    } else if (strips % 2 == 0) {
+    } else if (mt > kXLdsMaxTokens && strips % 2 == 0) {
       sp = 2;
     }
   }
