@@ -62,6 +62,7 @@ constexpr int kBChunkRows = 128;    // rows per chunk (two 64-row pairs, four 32
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) f16x8 lds_f16x8;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
 // x staged in LDS up front (one-tile, one-strip forms): the workgroup's
 // token rows over its K range, row pitch = 2 * range + 16 bytes (the 16
@@ -395,7 +396,9 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
   constexpr int kUOut = kSP * kBOut;  // outputs per unit
   constexpr bool kPS = kT >= 3;       // pre-scaled weights
   static_assert(!(kPS && kXL), "the pre-scaled form takes x through the LDS slots");
-  __shared__ float s_red[(kPS ? 1 : kW) * 16 * kT * kUOut];
+  // kXL: the wavefronts' sums meet here (the other forms reuse their x slots)
+  __shared__ float s_red[kXL ? kW * 16 * kT * kUOut : 1];
+  static_assert(kXL || kSP <= 4, "a wavefront's sums must fit its two x slots");
   extern __shared__ __attribute__((aligned(16))) uint8_t x_dyn[];  // kXL: M rows of staged x
 
   int unit, split;
@@ -555,50 +558,61 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
 
   // Add the wavefronts' sums in wavefront order. Lane (j, h) holds token
   // 16t + 4h + i of output 32sp + 8c + 2g + f of the unit in tot[t][sp][f][i].
-  if constexpr (kPS) {
-    // one buffer: wavefront 0 stores, then each next one adds its sums
-    for (int w = 0; w < kW; ++w) {
-      if (wave == w) {
-#pragma unroll
-        for (int t = 0; t < kT; ++t)
-#pragma unroll
-          for (int sp = 0; sp < kSP; ++sp)
-#pragma unroll
-            for (int f = 0; f < 2; ++f)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                float& r = s_red[(16 * t + 4 * h + i) * kUOut + kBOut * sp + 8 * c + 2 * g + f];
-                r = w == 0 ? tot[t][sp][f][i] : r + tot[t][sp][f][i];
-              }
-      }
-      __syncthreads();
-    }
+  // Each wavefront stores its sums as one 16-byte vector (tokens 4h..4h+3)
+  // per lane and (t, sp, f), consecutive lanes at consecutive addresses (no
+  // bank conflicts), all wavefronts at once; after one barrier a thread adds
+  // the kW vectors of one (t, sp, lane) for both f and writes its four
+  // tokens' two adjacent outputs as pairs. Forms without x staged up front
+  // store into the wavefront's own x slots: every DMA into them has landed
+  // (the last computes waited for all vector-memory loads) and lgkmcnt(0)
+  // makes sure the slots' last reads have returned.
+  float* red;
+  if constexpr (kXL) {
+    red = s_red + wave * (16 * kT * kUOut);
   } else {
-#pragma unroll
-    for (int t = 0; t < kT; ++t)
-#pragma unroll
-      for (int sp = 0; sp < kSP; ++sp)
-#pragma unroll
-        for (int f = 0; f < 2; ++f)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            s_red[((wave * 16 * kT) + 16 * t + 4 * h + i) * kUOut + kBOut * sp + 8 * c + 2 * g + f] =
-                tot[t][sp][f][i];
-    __syncthreads();
+    wait_counts<63, 0>();
+    red = reinterpret_cast<float*>(x_dyn + wave * 2 * (kT * 4096));
   }
-  const int rows = min(M, 16 * kT);
-  for (int idx = threadIdx.x; idx < rows * kUOut; idx += kW * 64) {
-    const int m = idx / kUOut, n = idx % kUOut;
-    float v = s_red[m * kUOut + n];
-    if constexpr (!kPS) {
 #pragma unroll
-      for (int w = 1; w < kW; ++w) v += s_red[(w * 16 * kT + m) * kUOut + n];
+  for (int t = 0; t < kT; ++t)
+#pragma unroll
+    for (int sp = 0; sp < kSP; ++sp)
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+        *(lds_f32x4*)(red + (((t * kSP + sp) * 2 + f) * 64 + lane) * 4) = tot[t][sp][f];
+  __syncthreads();
+  const int rows = min(M, 16 * kT);
+  for (int e = threadIdx.x; e < kT * kSP * 64; e += kW * 64) {
+    const int ln = e & 63, tsp = e >> 6;  // tsp = t * kSP + sp
+    const int m0 = 16 * (tsp / kSP) + 4 * (ln >> 4);
+    if (m0 >= rows) continue;
+    f32x4 v[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const int off = ((tsp * 2 + f) * 64 + ln) * 4;
+      if constexpr (kXL) {
+        v[f] = *(const lds_f32x4*)(s_red + off);
+#pragma unroll
+        for (int w = 1; w < kW; ++w) v[f] += *(const lds_f32x4*)(s_red + w * (16 * kT * kUOut) + off);
+      } else {
+        v[f] = *(const lds_f32x4*)(reinterpret_cast<float*>(x_dyn) + off);
+#pragma unroll
+        for (int w = 1; w < kW; ++w)
+          v[f] += *(const lds_f32x4*)(reinterpret_cast<float*>(x_dyn + w * 2 * (kT * 4096)) + off);
+      }
     }
-    const size_t o = static_cast<size_t>(strip) * kBOut + n;
-    if (splits == 1) {
-      y[static_cast<size_t>(m) * N + o] = half_bits<kBF>(v);
-    } else {
-      partial[(static_cast<size_t>(split) * M + m) * N + o] = v;
+    const int jj = ln & 15;
+    const size_t o = static_cast<size_t>(strip) * kBOut + kBOut * (tsp % kSP) + 8 * (jj & 3) + 2 * (jj >> 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + i;
+      if (m >= rows) break;
+      if (splits == 1) {
+        *reinterpret_cast<uint32_t*>(y + static_cast<size_t>(m) * N + o) =
+            half_bits<kBF>(v[0][i]) | (static_cast<uint32_t>(half_bits<kBF>(v[1][i])) << 16);
+      } else {
+        *reinterpret_cast<f32x2*>(partial + (static_cast<size_t>(split) * M + m) * N + o) = f32x2{v[0][i], v[1][i]};
+      }
     }
   }
 }
