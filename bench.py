@@ -90,7 +90,8 @@ PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_gemm_counters.jso
 # Reading of "int8 weights from N(0, 0.02)": drawn in fp32, rounded to fp16 (the
 # served dtype), then quantized per output channel by the per-token quantizer.
 W8A8_WEIGHTS = "fp32 N(0, 0.02) rounded to fp16, then symmetric int8 per output channel (absmax/127)"
-GEMV_SOURCES = ["w4a16_gemv_blocked.hip", "w4a16_split.h", "w4a16_common.h", "device_common.h"]
+GEMV_SOURCES = ["w4a16_gemv_blocked.hip", "w4a16_gemv_blocked.h", "w4a16_split.h", "w4a16_common.h",
+                "device_common.h"]
 
 
 def w4a16_bytes(M, K, N, G=GROUP):

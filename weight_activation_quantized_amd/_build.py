@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(HERE, "libmq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["mq_api.cpp", "quant_int8.hip", "w8a8_gemm.hip", "w8a8_gemv.hip", "w4a16_gemv.hip",
-           "w4a16_gemv_blocked.hip", "w4a16_gemm.hip", "kv_quant.hip", "int4_layout.hip", "w8a8_noalloc.hip"]
+           "w4a16_gemv_blocked.hip", "w4a16_gemv_blocked_prescaled.hip", "w4a16_gemm.hip", "kv_quant.hip",
+           "int4_layout.hip", "w8a8_noalloc.hip"]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -38,11 +39,15 @@ FLAGS = [
     f"-I{CSRC}",
 ]
 
-# Per-source extra flags. The GEMV starts its nine MFMAs of a step from zero
-# every step; the VGPR form gives each its own destination (otherwise they
-# share one AGPR quad and wait on each other's copy-out).
+# Per-source extra flags: MFMA results in ordinary VGPRs. The GEMV starts its
+# nine MFMAs of a step from zero every step; the VGPR form gives each its own
+# destination (otherwise they share one AGPR quad and wait on each other's
+# copy-out). The decode-layout GEMV's one- and two-tile forms read their
+# per-group sums with VALU operations (no copies out of AGPRs); its forms
+# for 33-64 tokens (their own file) measured faster in the AGPR form.
 SOURCE_FLAGS = {
     "w4a16_gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "w4a16_gemv_blocked.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 
