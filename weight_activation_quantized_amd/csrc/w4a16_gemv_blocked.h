@@ -130,12 +130,13 @@ __device__ __forceinline__ void load_chunk(BChunk<kT, kBChunkRows / kGS, kSP>& c
   // loads of the fragments would each take 16 half lines): the slot's
   // previous contents were read by the compute before this call, and
   // lgkmcnt(0) makes sure those reads have returned. The last tile takes
-  // only its first kXQ loads (tokens 0 .. 4 kXQ - 1 of it); the kernel
-  // zeroes the slot rows past them once at its start.
+  // only its first kXQ loads (tokens 0 .. 4 kXQ - 1 of it; kXQ = 0: one
+  // load for a single token); the kernel zeroes the slot rows past them
+  // once at its start.
   if constexpr (!kXL) {
     wait_counts<63, 0>();
 #pragma unroll
-    for (int q = 0; q < 4 * (kT - 1) + kXQ; ++q)
+    for (int q = 0; q < 4 * (kT - 1) + (kXQ == 0 ? 1 : kXQ); ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(L.xr, (lds_void*)(xslot + 1024 * q), 16,
                                                L.xdma[q % 4] + (q / 4) * L.xtile + 256u * chunk, 0, 0, 0);
   }
@@ -181,7 +182,9 @@ __device__ __forceinline__ void unpack_block(uint32_t w0, uint32_t w1, const Nib
     }
 }
 
-template <int kT, int kGS, int kSP, bool kXL, bool kBF>
+// kLaneRows: tokens 4h .. 4h + kLaneRows - 1 of a lane's four are in use
+// (1 for a single token: the per-group update of the other three is skipped).
+template <int kT, int kGS, int kSP, bool kXL, bool kBF, int kLaneRows = 4>
 __device__ __forceinline__ void compute_chunk(const BChunk<kT, kBChunkRows / kGS, kSP>& ch, const NibConst& nc,
                                               const f16x8 ones, int g_lane, f32x4 (&tot)[kT][kSP][2],
                                               const lds_u8* xl, const lds_u8* scl, const lds_u8* zl,
@@ -252,7 +255,7 @@ __device__ __forceinline__ void compute_chunk(const BChunk<kT, kBChunkRows / kGS
 #pragma unroll
         for (int t = 0; t < kT; ++t)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < kLaneRows; ++i)
             tot[t][sp][f][i] = fmaf(sc[f], fmaf(-bias[f], accx[t][i], acc[t][sp][f][i]), tot[t][sp][f][i]);
     }
   }
@@ -425,12 +428,12 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
     xs[0] = xslot[0] + 256 * j;
     xs[1] = xslot[1] + 256 * j;
     if constexpr (kXQ < 4) {
-      // token rows 4 kXQ .. 15 of the last tile are never loaded: zero
-      // them in both slots (they only feed output rows that are not stored)
+      // token rows 4 max(kXQ, 1) .. 15 of the last tile are never loaded:
+      // zero them in both slots (they only feed output rows not stored)
 #pragma unroll
       for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
-        for (int r = 4 * kXQ; r < 16; r += 4)
+        for (int r = 4 * (kXQ == 0 ? 1 : kXQ); r < 16; r += 4)
           *(lds_u32x4*)(xslot[sl] + 4096 * (kT - 1) + 256 * (r + lane / 16) + 16 * (lane % 16)) = u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
@@ -514,13 +517,14 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
     // next chunk was issued after this one's (sched_barrier between the
     // requests): waiting down to that chunk's count (kChunkLoads) leaves
     // only those in flight; where no later chunk was requested, wait for all.
-    constexpr int kChunkLoads = 2 * kSP + 4 * (kT - 1) + kXQ + 2 * kSP * kGPC;
+    constexpr int kChunkLoads = 2 * kSP + 4 * (kT - 1) + (kXQ == 0 ? 1 : kXQ) + 2 * kSP * kGPC;
     static_assert(kXL || kChunkLoads < 64, "vmcnt range");
     auto compute = [&](const BChunk<kT, kGPC, kSP>& ch, int chunk, int buf) {
       if constexpr (kPS) {
         compute_chunk_scaled<kT, kGS, kSP, kBF>(ch, nc, g, tot, xs[buf], xo);
       } else {
-        compute_chunk<kT, kGS, kSP, kXL, kBF>(ch, nc, ones, g, tot, xl(chunk), sl(chunk), zl(chunk), xs[buf], xo);
+        compute_chunk<kT, kGS, kSP, kXL, kBF, kXQ == 0 ? 1 : 4>(ch, nc, ones, g, tot, xl(chunk), sl(chunk), zl(chunk),
+                                                             xs[buf], xo);
       }
     };
     int i = 0;

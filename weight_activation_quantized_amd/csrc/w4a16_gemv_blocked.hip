@@ -64,9 +64,13 @@ hipError_t launch_blocked_main(const uint16_t* x, const u32x4* qb, const uint16_
                                                    static_cast<size_t>(lds), stream);
   }
   // two LDS slots of 16 kT token rows x 256 bytes per wavefront (the x DMA);
-  // with up to 4 / 8 tokens one / two loads per chunk fill the rows in use
+  // with up to 4 / 8 tokens one / two loads per chunk fill the rows in use,
+  // and a single token also skips the per-group update of unused rows
   const size_t lds = static_cast<size_t>(plan.waves) * 2 * kT * 4096;
   if constexpr (kT == 1) {
+    if (m == 1)
+      return launch_blocked_xl<kT, kGS, kSP, false, kBF, 0>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid,
+                                                        lds, stream);
     if (m <= 4)
       return launch_blocked_xl<kT, kGS, kSP, false, kBF, 1>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid,
                                                         lds, stream);
