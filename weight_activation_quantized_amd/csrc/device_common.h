@@ -25,10 +25,29 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWave = 64;
 
+// A float from another lane of the same 16-lane row, by DPP control kCtrl
+// (every lane's source is valid for the controls used here).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float x) {
+  const int b = __builtin_bit_cast(int, x);
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, kCtrl, 0xF, 0xF, false));
+}
+
+// Maximum over the wavefront, the same value in every lane: DPP steps within
+// each row of 16 lanes (quad permutes, then the half-row and row mirrors),
+// then the four rows' maxima read from lanes 15, 31, 47 and 63. No LDS round
+// trips; max is exact and order-free.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
+  v = fmaxf(v, dpp_f32<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  v = fmaxf(v, dpp_f32<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  v = fmaxf(v, dpp_f32<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_f32<0x140>(v));  // row_mirror: every lane holds its row's maximum
+  const int b = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 15));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 31));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 47));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 63));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 __device__ __forceinline__ f16x2 as_f16x2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }

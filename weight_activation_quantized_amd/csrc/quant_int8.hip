@@ -37,64 +37,54 @@ __device__ __forceinline__ float chunk_absmax(u32x4 v, float m) {
 }
 
 // Distance from a half-integer below which an element takes the IEEE
-// division (see code_of).
+// division (see quant_chunk).
 constexpr float kTieMargin = 1.0f / 4096.0f;
 
-// rne(fl32(v / s)) for s > 0, |v| <= 127.5 s. The product p = v * r with
-// r = rcp(s) (within 1 ulp of 1/s) differs from the exact quotient by at
-// most 2^-22 relative, i.e. < 3.1e-5 for quotients up to 127.5, and the
-// correctly rounded quotient is within half an ulp (< 3.9e-6) of it. So when
-// p is more than kTieMargin away from every half-integer, the rounded
-// quotient lies on the same side of the nearest half-integer as p and rounds
-// to the same integer; only elements within the margin (about 1 in 2000)
-// take the IEEE division, whose correctly rounded result decides ties.
-// Written so that a non-finite p (a binary32-subnormal s, possible for bf16
-// rows with absmax below 127 * 2^-126, whose reciprocal overflows) also
-// takes the division.
-__device__ __forceinline__ float code_of(float v, float s, float r) {
-  const float p = v * r;
-  const float t = rintf(p);
-  if (!(0.5f - fabsf(p - t) >= kTieMargin)) return rintf(v / s);
-  return t;
-}
-
-// The reciprocal code_of multiplies by: rcp(s) for a normal s; infinity for a
-// binary32-subnormal s (then every product is non-finite and code_of divides).
+// The reciprocal quant_chunk multiplies by: rcp(s) for a normal s; infinity
+// for a binary32-subnormal s (then every product is non-finite and each
+// element takes the division).
 __device__ __forceinline__ float code_rcp(float s) {
   return s < 1.17549435e-38f ? __builtin_inff() : __builtin_amdgcn_rcpf(s);
 }
 
-__device__ __forceinline__ uint32_t quant4(float a0, float a1, float b0, float b1, float s, float r) {
-  // s > 0 here: the codes of the IEEE quotient, rounded half to even.
-  float q0 = code_of(a0, s, r);
-  float q1 = code_of(a1, s, r);
-  float q2 = code_of(b0, s, r);
-  float q3 = code_of(b1, s, r);
-  q0 = fminf(fmaxf(q0, -127.f), 127.f);
-  q1 = fminf(fmaxf(q1, -127.f), 127.f);
-  q2 = fminf(fmaxf(q2, -127.f), 127.f);
-  q3 = fminf(fmaxf(q3, -127.f), 127.f);
-  uint32_t packed = static_cast<uint32_t>(static_cast<int32_t>(q0)) & 0xFFu;
-  packed |= (static_cast<uint32_t>(static_cast<int32_t>(q1)) & 0xFFu) << 8;
-  packed |= (static_cast<uint32_t>(static_cast<int32_t>(q2)) & 0xFFu) << 16;
-  packed |= (static_cast<uint32_t>(static_cast<int32_t>(q3)) & 0xFFu) << 24;
-  return packed;
-}
-
+// Codes of one 16-byte chunk (8 values) as 8 bytes: rne(fl32(v / s)) for
+// s > 0, clamped to [-127, 127]; 0 for s = 0. Each element forms
+// u = rint(v * r + 128) with one fused multiply-add (r = rcp(s), within 1 ulp
+// of 1/s). The product differs from the exact quotient v / s by at most 2^-22
+// relative (< 3.1e-5 for quotients up to 127.5), the rounded sum adds at most
+// 2^-17, and the correctly rounded quotient is within half an ulp (< 3.9e-6)
+// of the exact one. So when v * r + 128 is more than kTieMargin away from
+// every half-integer, the rounded quotient lies on the same side of the
+// nearest half-integer and u - 128 is its code; the rest (about 1 element in
+// 2000, and every non-finite product) take the IEEE division, whose correctly
+// rounded result decides ties. Codes in [-127, 127] are u in [1, 255]; one
+// unsigned 8-bit conversion per element packs u, and flipping bit 7 of each
+// byte gives the two's-complement code u - 128.
 template <bool kBf16>
 __device__ __forceinline__ u32x2 quant_chunk(u32x4 v, float s, float r) {
-  u32x2 out;
-  if (s > 0.f) {
-    float f[8];
+  if (!(s > 0.f)) return u32x2{0u, 0u};
+  float f[8], u[8];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) word_to_floats<kBf16>(v[w], f[2 * w], f[2 * w + 1]);
-    out[0] = quant4(f[0], f[1], f[2], f[3], s, r);
-    out[1] = quant4(f[4], f[5], f[6], f[7], s, r);
-  } else {
-    out[0] = 0u;
-    out[1] = 0u;
+  for (int w = 0; w < 4; ++w) word_to_floats<kBf16>(v[w], f[2 * w], f[2 * w + 1]);
+  bool slow = false;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float p = fmaf(f[e], r, 128.f);
+    u[e] = rintf(p);
+    slow |= !(fabsf(p - u[e]) <= 0.5f - kTieMargin);
   }
-  return out;
+  if (slow) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = fmaf(f[e], r, 128.f);
+      if (!(fabsf(p - u[e]) <= 0.5f - kTieMargin)) u[e] = rintf(f[e] / s) + 128.f;
+    }
+  }
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    w[e >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_fmed3f(u[e], 1.f, 255.f), e & 3, w[e >> 2]);
+  return u32x2{w[0] ^ 0x80808080u, w[1] ^ 0x80808080u};
 }
 
 // CPL = 16-byte chunks per lane kept in registers (row length <= 512*CPL).
