@@ -53,7 +53,10 @@ def test_gemv_blocked_decode_gate_up(M):
                                    (33, 1024, 3072), (63, 256, 384), (5, 128, 128), (1, 128, 24576),
                                    (2, 640, 640), (7, 384, 32), (40, 640, 96), (1, 4096, 24608),
                                    # workgroups of three (5..16 tokens) or two (17..32) adjacent strips
-                                   (12, 640, 96), (9, 4096, 24576), (5, 1024, 3072), (24, 512, 4096)])
+                                   (12, 640, 96), (9, 4096, 24576), (5, 1024, 3072), (24, 512, 4096),
+                                   # 33-64 tokens: six and ten 64-row steps per wavefront (the
+                                   # four-step pipeline's tail after zero and one steady rounds)
+                                   (48, 3072, 4096), (40, 5120, 8192)])
 def test_gemv_blocked_shapes(M, K, N, G):
     d = synth.w4a16_inputs(M, K, N, group=G, outlier_frac=0.005, tag=M + K + N + G)
     assert_fp16_close(_run(d, G, "shape"), _ref(d, G), f"gemv_blocked G={G} M={M} K={K} N={N}")

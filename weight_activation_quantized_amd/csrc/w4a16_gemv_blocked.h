@@ -41,15 +41,16 @@
 // ones per block). The wavefronts' sums are added in LDS in wavefront
 // order, so results are deterministic. 32-output strips give 768
 // workgroups for a 24576-wide layer: every CU streams the same share.
-// With 33-64 tokens (three or four tiles) the kernel instead forms the
-// weights themselves, fp16((q - z) * s) rounded once, and accumulates the
-// MFMAs straight into the running sums: one pass over the weights for all
-// tokens, with several strips per workgroup sharing the x fragments.
+// With 33-64 tokens (three or four tiles) a second kernel
+// (w4a16_gemv_blocked_prescaled.hip) forms the weights themselves,
+// fp16((q - z) * s) rounded once, and accumulates the MFMAs straight into
+// the running sums: one pass over the weights for all tokens, with several
+// strips per workgroup sharing the x fragments.
 //
-// This header holds the kernel and what its two translation units share:
-// w4a16_gemv_blocked.hip (layout conversion, plan, one or two token tiles)
-// and w4a16_gemv_blocked_prescaled.hip (three or four tiles), built with
-// different register forms for the MFMA results.
+// This header holds the one- and two-tile kernel and what the two
+// translation units share: w4a16_gemv_blocked.hip (layout conversion, plan,
+// one or two token tiles) and w4a16_gemv_blocked_prescaled.hip (three or
+// four tiles), built with different register forms for the MFMA results.
 #pragma once
 
 #include <algorithm>
@@ -261,96 +262,57 @@ __device__ __forceinline__ void compute_chunk(const BChunk<kT, kBChunkRows / kGS
   }
 }
 
-// Pre-scaled B fragments (forms with three or four token tiles): as
-// unpack_block, but each fragment element is the weight itself,
-// fp16((q - z) * s), rounded once: field 2g reads 1024 + q (pattern of
-// 1024.0), field 2g+1 reads 64 + q (pattern of 64.0, no factor 16); adding
-// -(1024 + z) / -(64 + z) leaves q - z exactly, and one multiply by s rounds.
-// nz[f] / s2[f]: the encoded negated zero point and the scale of field f,
-// both replicated in the two fp16 halves.
-// kBF: nz[f] / s2[f] hold binary32 bits of -(offset + z) * s and of s; one
-// fused multiply-add per weight gives (q - z) * s exactly in binary32 and
-// the pair conversion rounds it once to bf16.
-template <bool kBF>
-__device__ __forceinline__ void unpack_block_scaled(uint32_t w0, uint32_t w1, const NibConst& c,
-                                                    const uint32_t (&nz)[2], const uint32_t (&s2)[2],
-                                                    f16x8 (&bf)[2]) {
-  const uint32_t ws[2] = {w0, w1};
+// The end of a call: add the sums of wavefronts 0 .. kR-1 of a unit in
+// wavefront order and store them (kW wavefronts in the workgroup take part;
+// kR = kW unless the caller has folded the others in first). Lane (j, h)
+// holds token 16t + 4h + i of output 32sp + 8c + 2g + f of the unit in
+// tot[t][sp][f][i]. Each of those wavefronts stores its sums as one 16-byte
+// vector (tokens 4h..4h+3) per lane and (t, sp, f) into its own region
+// (region_bytes apart from base, at least kT * kSP * 2 KB), consecutive
+// lanes at consecutive addresses (no bank conflicts), all at once; after one
+// barrier a thread adds the kR vectors of one (t, sp, lane) for both f and
+// writes its four tokens' two adjacent outputs as pairs (fp16 / bf16 pairs,
+// or fp32 partial sums of split `split` when K is split). The caller makes
+// sure the regions are free.
+template <int kT, int kSP, int kW, bool kBF, int kR = kW>
+__device__ __forceinline__ void store_unit_sums(const f32x4 (&tot)[kT][kSP][2], lds_u8* base, int region_bytes,
+                                                int wave, int lane, int M, int N, int strip, int split, int splits,
+                                                uint16_t* __restrict__ y, float* __restrict__ partial) {
+  if (wave < kR) {
+    lds_u8* const red = base + wave * region_bytes;
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
+    for (int t = 0; t < kT; ++t)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const uint32_t v = byte_perm(ws[q], ws[q], t ? 0x0C030C02u : 0x0C010C00u);
-      f16x2 lo, hi;
-      if constexpr (kBF) {
-        const f16x2 ol = as_f16x2((v & c.lo) | c.magic), oh = as_f16x2((v & c.hi) | c.magic64);
-        const float sl = __builtin_bit_cast(float, s2[0]), cl = __builtin_bit_cast(float, nz[0]);
-        const float sh = __builtin_bit_cast(float, s2[1]), ch = __builtin_bit_cast(float, nz[1]);
-        lo = as_f16x2(bf16x2_bits(fmaf(static_cast<float>(ol[0]), sl, cl), fmaf(static_cast<float>(ol[1]), sl, cl)));
-        hi = as_f16x2(bf16x2_bits(fmaf(static_cast<float>(oh[0]), sh, ch), fmaf(static_cast<float>(oh[1]), sh, ch)));
-      } else {
-        lo = (as_f16x2((v & c.lo) | c.magic) + as_f16x2(nz[0])) * as_f16x2(s2[0]);
-        hi = (as_f16x2((v & c.hi) | c.magic64) + as_f16x2(nz[1])) * as_f16x2(s2[1]);
-      }
-      bf[0][4 * q + 2 * t] = lo[0];
-      bf[0][4 * q + 2 * t + 1] = lo[1];
-      bf[1][4 * q + 2 * t] = hi[0];
-      bf[1][4 * q + 2 * t + 1] = hi[1];
+      for (int sp = 0; sp < kSP; ++sp)
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+          *(lds_f32x4*)(red + (((t * kSP + sp) * 2 + f) * 64 + lane) * 16) = tot[t][sp][f];
+  }
+  __syncthreads();
+  const int rows = min(M, 16 * kT);
+  for (int e = threadIdx.x; e < kT * kSP * 64; e += kW * 64) {
+    const int ln = e & 63, tsp = e >> 6;  // tsp = t * kSP + sp
+    const int m0 = 16 * (tsp / kSP) + 4 * (ln >> 4);
+    if (m0 >= rows) continue;
+    f32x4 v[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const int off = ((tsp * 2 + f) * 64 + ln) * 16;
+      v[f] = *(const lds_f32x4*)(base + off);
+#pragma unroll
+      for (int w = 1; w < kR; ++w) v[f] += *(const lds_f32x4*)(base + w * region_bytes + off);
     }
-}
-
-// One chunk of the pre-scaled form: the MFMAs accumulate straight into the
-// running sums (the weights carry their scales), so no per-group partial
-// sums or sums of x are kept -- that is what lets three strips share every
-// x fragment of four token tiles within the register file.
-// xs: the lane's row (token j of tile 0) of the chunk in the wavefront's
-// slot (256 bytes per row, 16-byte chunk index XOR-ed with the row mod 16);
-// xo[b]: the byte offset of block b's 8 values of the lane (rows 8h..).
-template <int kT, int kGS, int kSP, bool kBF>
-__device__ __forceinline__ void compute_chunk_scaled(const BChunk<kT, kBChunkRows / kGS, kSP>& ch,
-                                                     const NibConst& nc, int g_lane, f32x4 (&tot)[kT][kSP][2],
-                                                     const lds_u8* xs, const int (&xo)[4]) {
-  constexpr int kGPC = kBChunkRows / kGS;
-  constexpr int kBPG = kGS / 32;
+    const int jj = ln & 15;
+    const size_t o = static_cast<size_t>(strip) * kBOut + kBOut * (tsp % kSP) + 8 * (jj & 3) + 2 * (jj >> 2);
 #pragma unroll
-  for (int g = 0; g < kGPC; ++g) {
-    uint32_t nz[kSP][2], s2[kSP][2];
-#pragma unroll
-    for (int sp = 0; sp < kSP; ++sp) {
-      const f16x2 sv = as_f16x2(ch.sv[sp][g]);
-      const uint32_t zb = (ch.zw[sp][g] >> (8 * g_lane)) & 0xFFu;
-      if constexpr (kBF) {
-        const float sl = static_cast<float>(sv[0]), sh = static_cast<float>(sv[1]);
-        nz[sp][0] = __builtin_bit_cast(uint32_t, -(1024.0f + static_cast<float>(zb & 15u)) * sl);
-        nz[sp][1] = __builtin_bit_cast(uint32_t, -(64.0f + static_cast<float>(zb >> 4)) * sh);
-        s2[sp][0] = __builtin_bit_cast(uint32_t, sl);
-        s2[sp][1] = __builtin_bit_cast(uint32_t, sh);
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + i;
+      if (m >= rows) break;
+      if (splits == 1) {
+        *reinterpret_cast<uint32_t*>(y + static_cast<size_t>(m) * N + o) =
+            half_bits<kBF>(v[0][i]) | (static_cast<uint32_t>(half_bits<kBF>(v[1][i])) << 16);
       } else {
-        f16x2 s_lo, s_hi;
-        s_lo[0] = s_lo[1] = sv[0];
-        s_hi[0] = s_hi[1] = sv[1];
-        const uint32_t e_lo = (zb & 0x0Fu) | 0xE400u, e_hi = (zb & 0xF0u) | 0xD400u;
-        nz[sp][0] = e_lo | (e_lo << 16);
-        nz[sp][1] = e_hi | (e_hi << 16);
-        s2[sp][0] = as_u32(s_lo);
-        s2[sp][1] = as_u32(s_hi);
-      }
-    }
-#pragma unroll
-    for (int bb = 0; bb < kBPG; ++bb) {
-      const int b = g * kBPG + bb;
-      f16x8 xa[kT];  // the block's x fragments, shared by the strips
-#pragma unroll
-      for (int t = 0; t < kT; ++t) xa[t] = *(const lds_f16x8*)(xs + 4096 * t + xo[b]);
-#pragma unroll
-      for (int sp = 0; sp < kSP; ++sp) {
-        f16x8 bf[2];
-        unpack_block_scaled<kBF>(ch.w[sp][b >> 1][2 * (b & 1)], ch.w[sp][b >> 1][2 * (b & 1) + 1], nc, nz[sp],
-                                 s2[sp], bf);
-#pragma unroll
-        for (int t = 0; t < kT; ++t)
-#pragma unroll
-          for (int f = 0; f < 2; ++f) tot[t][sp][f] = mfma_16x16x32<kBF>(xa[t], bf[f], tot[t][sp][f]);
+        *reinterpret_cast<f32x2*>(partial + (static_cast<size_t>(split) * M + m) * N + o) = f32x2{v[0][i], v[1][i]};
       }
     }
   }
@@ -368,9 +330,8 @@ __device__ __forceinline__ void compute_chunk_scaled(const BChunk<kT, kBChunkRow
 // fragments and the group parameters from there, so the weight stream has
 // the vector-memory queue to itself (per-chunk x loads cost about 2 us and
 // the scale and zero-point loads about 0.7 us of a 13 us call at N = 24576).
-// Three or four tiles (33-64 tokens) take the pre-scaled form: one pass
-// over the weights for all tokens, the wavefronts' sums added in LDS one
-// wavefront after the other (same order, smaller buffer).
+// Three or four tiles (33-64 tokens) take the pre-scaled kernel of
+// w4a16_gemv_blocked_prescaled.hip instead.
 template <int kT, int kGS, int kW, int kSP, bool kXL, bool kBF, int kXQ>
 __global__ __launch_bounds__(kW * 64)
 __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kGS >= 64 ? 3 : 1)))) void w4a16_gemv_blocked_kernel(
@@ -379,8 +340,7 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
     int units, int splits, XcdMap map, int gstep) {
   constexpr int kGPC = kBChunkRows / kGS;
   constexpr int kUOut = kSP * kBOut;  // outputs per unit
-  constexpr bool kPS = kT >= 3;       // pre-scaled weights
-  static_assert(!(kPS && kXL), "the pre-scaled form takes x through the LDS slots");
+  static_assert(kT <= 2, "three or four tiles take the pre-scaled kernel");
   // kXL: the wavefronts' sums meet here (the other forms reuse their x slots)
   __shared__ float s_red[kXL ? kW * 16 * kT * kUOut : 1];
   static_assert(kXL || kSP <= 4, "a wavefront's sums must fit its two x slots");
@@ -520,12 +480,8 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
     constexpr int kChunkLoads = 2 * kSP + 4 * (kT - 1) + (kXQ == 0 ? 1 : kXQ) + 2 * kSP * kGPC;
     static_assert(kXL || kChunkLoads < 64, "vmcnt range");
     auto compute = [&](const BChunk<kT, kGPC, kSP>& ch, int chunk, int buf) {
-      if constexpr (kPS) {
-        compute_chunk_scaled<kT, kGS, kSP, kBF>(ch, nc, g, tot, xs[buf], xo);
-      } else {
-        compute_chunk<kT, kGS, kSP, kXL, kBF, kXQ == 0 ? 1 : 4>(ch, nc, ones, g, tot, xl(chunk), sl(chunk), zl(chunk),
-                                                             xs[buf], xo);
-      }
+      compute_chunk<kT, kGS, kSP, kXL, kBF, kXQ == 0 ? 1 : 4>(ch, nc, ones, g, tot, xl(chunk), sl(chunk), zl(chunk),
+                                                           xs[buf], xo);
     };
     int i = 0;
     for (; i + 3 < cpw; i += 2) {
@@ -551,64 +507,17 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
     if (i + 2 < cpw) compute(ca, c0 + i + 2, 0);
   }
 
-  // Add the wavefronts' sums in wavefront order. Lane (j, h) holds token
-  // 16t + 4h + i of output 32sp + 8c + 2g + f of the unit in tot[t][sp][f][i].
-  // Each wavefront stores its sums as one 16-byte vector (tokens 4h..4h+3)
-  // per lane and (t, sp, f), consecutive lanes at consecutive addresses (no
-  // bank conflicts), all wavefronts at once; after one barrier a thread adds
-  // the kW vectors of one (t, sp, lane) for both f and writes its four
-  // tokens' two adjacent outputs as pairs. Forms without x staged up front
-  // store into the wavefront's own x slots: every DMA into them has landed
-  // (the last computes waited for all vector-memory loads) and lgkmcnt(0)
-  // makes sure the slots' last reads have returned.
-  float* red;
+  // Add the wavefronts' sums and store (see store_unit_sums). Forms
+  // without x staged up front store into the wavefront's own x slots: every
+  // DMA into them has landed (the last computes waited for all vector-memory
+  // loads) and lgkmcnt(0) makes sure the slots' last reads have returned.
   if constexpr (kXL) {
-    red = s_red + wave * (16 * kT * kUOut);
+    store_unit_sums<kT, kSP, kW, kBF>(tot, (lds_u8*)(s_red), 16 * kT * kUOut * 4, wave, lane, M, N, strip, split,
+                                      splits, y, partial);
   } else {
     wait_counts<63, 0>();
-    red = reinterpret_cast<float*>(x_dyn + wave * 2 * (kT * 4096));
-  }
-#pragma unroll
-  for (int t = 0; t < kT; ++t)
-#pragma unroll
-    for (int sp = 0; sp < kSP; ++sp)
-#pragma unroll
-      for (int f = 0; f < 2; ++f)
-        *(lds_f32x4*)(red + (((t * kSP + sp) * 2 + f) * 64 + lane) * 4) = tot[t][sp][f];
-  __syncthreads();
-  const int rows = min(M, 16 * kT);
-  for (int e = threadIdx.x; e < kT * kSP * 64; e += kW * 64) {
-    const int ln = e & 63, tsp = e >> 6;  // tsp = t * kSP + sp
-    const int m0 = 16 * (tsp / kSP) + 4 * (ln >> 4);
-    if (m0 >= rows) continue;
-    f32x4 v[2];
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      const int off = ((tsp * 2 + f) * 64 + ln) * 4;
-      if constexpr (kXL) {
-        v[f] = *(const lds_f32x4*)(s_red + off);
-#pragma unroll
-        for (int w = 1; w < kW; ++w) v[f] += *(const lds_f32x4*)(s_red + w * (16 * kT * kUOut) + off);
-      } else {
-        v[f] = *(const lds_f32x4*)(reinterpret_cast<float*>(x_dyn) + off);
-#pragma unroll
-        for (int w = 1; w < kW; ++w)
-          v[f] += *(const lds_f32x4*)(reinterpret_cast<float*>(x_dyn + w * 2 * (kT * 4096)) + off);
-      }
-    }
-    const int jj = ln & 15;
-    const size_t o = static_cast<size_t>(strip) * kBOut + kBOut * (tsp % kSP) + 8 * (jj & 3) + 2 * (jj >> 2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + i;
-      if (m >= rows) break;
-      if (splits == 1) {
-        *reinterpret_cast<uint32_t*>(y + static_cast<size_t>(m) * N + o) =
-            half_bits<kBF>(v[0][i]) | (static_cast<uint32_t>(half_bits<kBF>(v[1][i])) << 16);
-      } else {
-        *reinterpret_cast<f32x2*>(partial + (static_cast<size_t>(split) * M + m) * N + o) = f32x2{v[0][i], v[1][i]};
-      }
-    }
+    store_unit_sums<kT, kSP, kW, kBF>(tot, (lds_u8*)(x_dyn), 2 * (kT * 4096), wave, lane, M, N, strip, split, splits,
+                                      y, partial);
   }
 }
 

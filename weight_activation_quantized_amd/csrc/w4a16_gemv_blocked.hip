@@ -177,6 +177,9 @@ GemvPlan plan_w4a16_gemv_blocked(int64_t M, int64_t N, int64_t K, int64_t group)
   }
   const int64_t cps = chunks / plan.splits;
   plan.waves = cps % 4 == 0 ? 4 : (cps % 2 == 0 ? 2 : 1);
+  // 33-64 tokens: eight wavefronts (two per SIMD) where the split's chunks
+  // allow
+  if (mt > 32 && cps % 8 == 0) plan.waves = 8;
   plan.workspace_bytes = plan.splits > 1 ? static_cast<size_t>(plan.splits) * mt * N * sizeof(float) : 0;
   return plan;
 }
