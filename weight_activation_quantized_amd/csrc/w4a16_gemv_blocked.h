@@ -41,16 +41,16 @@
 // ones per block). The wavefronts' sums are added in LDS in wavefront
 // order, so results are deterministic. 32-output strips give 768
 // workgroups for a 24576-wide layer: every CU streams the same share.
-// With 33-64 tokens (three or four tiles) a second kernel
+// With 17-64 tokens (two to four tiles) a second kernel
 // (w4a16_gemv_blocked_prescaled.hip) forms the weights themselves,
 // fp16((q - z) * s) rounded once, and accumulates the MFMAs straight into
 // the running sums: one pass over the weights for all tokens, with several
 // strips per workgroup sharing the x fragments.
 //
-// This header holds the one- and two-tile kernel and what the two
-// translation units share: w4a16_gemv_blocked.hip (layout conversion, plan,
-// one or two token tiles) and w4a16_gemv_blocked_prescaled.hip (three or
-// four tiles), built with different register forms for the MFMA results.
+// This header holds the one-tile kernel and what the two translation units
+// share: w4a16_gemv_blocked.hip (layout conversion, plan, up to 16 tokens)
+// and w4a16_gemv_blocked_prescaled.hip (17-64 tokens), built with different
+// register forms for the MFMA results.
 #pragma once
 
 #include <algorithm>
@@ -330,7 +330,7 @@ __device__ __forceinline__ void store_unit_sums(const f32x4 (&tot)[kT][kSP][2], 
 // fragments and the group parameters from there, so the weight stream has
 // the vector-memory queue to itself (per-chunk x loads cost about 2 us and
 // the scale and zero-point loads about 0.7 us of a 13 us call at N = 24576).
-// Three or four tiles (33-64 tokens) take the pre-scaled kernel of
+// Two to four tiles (17-64 tokens) take the pre-scaled kernel of
 // w4a16_gemv_blocked_prescaled.hip instead.
 template <int kT, int kGS, int kW, int kSP, bool kXL, bool kBF, int kXQ>
 __global__ __launch_bounds__(kW * 64)
@@ -340,7 +340,7 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
     int units, int splits, XcdMap map, int gstep) {
   constexpr int kGPC = kBChunkRows / kGS;
   constexpr int kUOut = kSP * kBOut;  // outputs per unit
-  static_assert(kT <= 2, "three or four tiles take the pre-scaled kernel");
+  static_assert(kT == 1, "two to four tiles take the pre-scaled kernel");
   // kXL: the wavefronts' sums meet here (the other forms reuse their x slots)
   __shared__ float s_red[kXL ? kW * 16 * kT * kUOut : 1];
   static_assert(kXL || kSP <= 4, "a wavefront's sums must fit its two x slots");

@@ -86,26 +86,20 @@ template <int kGS, bool kBF>
 hipError_t launch_blocked_group(const uint16_t* x, const u32x4* qb, const uint16_t* scales, const uint32_t* qz,
                                 uint16_t* y, float* part, int m, int n, int k, const GemvPlan& plan, int units,
                                 XcdMap map, dim3 grid, hipStream_t stream) {
+  if (m > 16) return hipErrorInvalidValue;  // 17-64 tokens: the pre-scaled kernel
   if constexpr (kGS == 32) {
     // groups of 32: one strip per workgroup (the multi-strip forms do not
     // fit the register file with four groups per chunk)
-    if (m <= 16)
-      return launch_blocked_main<1, kGS, 1, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
-    return launch_blocked_main<2, kGS, 1, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+    return launch_blocked_main<1, kGS, 1, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
   } else {
-    if (m <= 16) {
-      switch (plan.strips_per_unit) {
-        case 3:
-          return launch_blocked_main<1, kGS, 3, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
-        case 2:
-          return launch_blocked_main<1, kGS, 2, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
-        default:
-          return launch_blocked_main<1, kGS, 1, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
-      }
+    switch (plan.strips_per_unit) {
+      case 3:
+        return launch_blocked_main<1, kGS, 3, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+      case 2:
+        return launch_blocked_main<1, kGS, 2, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+      default:
+        return launch_blocked_main<1, kGS, 1, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
     }
-    if (plan.strips_per_unit == 2)
-      return launch_blocked_main<2, kGS, 2, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
-    return launch_blocked_main<2, kGS, 1, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
   }
 }
 
@@ -136,17 +130,18 @@ GemvPlan plan_w4a16_gemv_blocked(int64_t M, int64_t N, int64_t K, int64_t group)
   }
   // Every workgroup loads all of x for its K range, so a workgroup takes
   // several adjacent strips that share those loads through its LDS slots
-  // (three for one 16-token tile, two for two; what divides the strips;
-  // at N = 24576: 4 tokens 12.8 -> 11.5 us, one token 11.9 -> 11.3 us with
+  // (three for one 16-token tile, where that divides the strips; at
+  // N = 24576: 4 tokens 12.8 -> 11.5 us, one token 11.9 -> 11.3 us with
   // three strips against one strip with x staged up front).
-  // With three or four tiles a workgroup needs every register (one per
-  // CU), and the x fragments, read once per strip group, cost more than
-  // the weights: the unit takes the most strips (3, then 2) for which
-  // splitting K still reaches one workgroup per CU with at least two
-  // chunks per split (measured at 64 tokens, 8B layers: qkv 22.7 -> 18.3,
-  // o_proj 15.1 -> 13.5, down 30.7 -> 23.7 us against one strip per unit).
+  // With two to four tiles (17-64 tokens, the pre-scaled kernel) a
+  // workgroup takes most of a CU, and the x fragments, read once per strip
+  // group, cost more than the weights: the unit takes the most strips (3,
+  // then 2) for which splitting K still reaches one workgroup per CU with
+  // at least two chunks per split (measured at 64 tokens, 8B layers: qkv
+  // 22.7 -> 18.3, o_proj 15.1 -> 13.5, down 30.7 -> 23.7 us against one
+  // strip per unit).
   int sp = 1;
-  if (mt > 32) {
+  if (mt > 16) {
     for (int cand = (group >= 64 ? 3 : 1); cand > 1; --cand) {
       if (strips % cand) continue;
       bool fits = false;
@@ -157,7 +152,7 @@ GemvPlan plan_w4a16_gemv_blocked(int64_t M, int64_t N, int64_t K, int64_t group)
       }
     }
   } else if (group >= 64) {
-    if (mt <= 16 && strips % 3 == 0) {
+    if (strips % 3 == 0) {
       sp = 3;
     } else if (mt > kXLdsMaxTokens && strips % 2 == 0) {
       sp = 2;
@@ -177,9 +172,9 @@ GemvPlan plan_w4a16_gemv_blocked(int64_t M, int64_t N, int64_t K, int64_t group)
   }
   const int64_t cps = chunks / plan.splits;
   plan.waves = cps % 4 == 0 ? 4 : (cps % 2 == 0 ? 2 : 1);
-  // 33-64 tokens: eight wavefronts (two per SIMD) where the split's chunks
+  // 17-64 tokens: eight wavefronts (two per SIMD) where the split's chunks
   // allow
-  if (mt > 32 && cps % 8 == 0) plan.waves = 8;
+  if (mt > 16 && cps % 8 == 0) plan.waves = 8;
   plan.workspace_bytes = plan.splits > 1 ? static_cast<size_t>(plan.splits) * mt * N * sizeof(float) : 0;
   return plan;
 }
@@ -213,7 +208,7 @@ hipError_t launch_w4a16_gemv_blocked(const uint16_t* x, const int32_t* blocked, 
   const uint32_t* qz = reinterpret_cast<const uint32_t*>(qzeros);
   float* part = static_cast<float*>(workspace);
   hipError_t err;
-  if (m > 32) {
+  if (m > 16) {  // two to four token tiles
     err = launch_w4a16_gemv_blocked_prescaled(x, qb, scales, qz, y, part, m, n, k, plan, units, map.strips_per_xcd,
                                               grid, bf16, stream);
   } else {

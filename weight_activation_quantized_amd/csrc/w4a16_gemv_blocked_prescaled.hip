@@ -1,10 +1,10 @@
-// W4A16 decode GEMV on the column-blocked layout, 33-64 tokens (three or four
+// W4A16 decode GEMV on the column-blocked layout, 17-64 tokens (two to four
 // 16-token tiles). Same operation and layout as w4a16_gemv_blocked.h (LMDeploy
 // 4-bit deployment guide, section 2.2: scale and weight consumed in one
 // kernel): y[m,n] = sum_k x[m,k] * fp16((q - z) * s) over groups of G rows.
 //
-// The two-tile form's per-group partial sums and sums of x do not fit the
-// register file with four tiles and several strips, so this kernel forms the
+// The one-tile kernel's per-group partial sums and sums of x do not fit the
+// register file with several tiles and strips, so this kernel forms the
 // weight fragments themselves, fp16((q - z) * s) rounded once (the GEMM's
 // arithmetic, with the 64 + q high field), and accumulates the MFMAs straight
 // into the running sums: one pass over the weights for all tokens, several
@@ -17,9 +17,9 @@
 // in registers, the step's x rows (all token tiles x 64 values) and group
 // parameters in one of its two LDS slots by DMA.
 //
-// Kept in its own translation unit: its MFMA results stay in accumulation
-// registers (the VGPR form of the one- and two-tile kernel measured slower
-// here).
+// Kept in its own translation unit: built without the VGPR form of MFMA
+// results that the one-tile kernel uses (with eight wavefronts the compiler
+// keeps these accumulators in VGPRs anyway).
 #include "w4a16_gemv_blocked.h"
 
 namespace mq {
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(kW >= 8
   constexpr int kLn = kHalf ? kSP + 2 * kT : kLp;
   constexpr int kWaitEven = kLn;  // before an even step: the next (odd) step's loads
   constexpr int kWaitOdd = kLp;   // before an odd step
-  static_assert(kT >= 3 && kT <= 4 && kSP >= 1 && kSP <= 4, "33-64 tokens, at most four strips");
+  static_assert(kT >= 2 && kT <= 4 && kSP >= 1 && kSP <= 4, "17-64 tokens, at most four strips");
   static_assert(kRing == 2 && kLp + kLn <= 63, "loads in flight within the vmcnt range");
   constexpr int kSlot = slot_bytes<kT, kGS, kSP>();  // bytes per step and wavefront
   extern __shared__ __attribute__((aligned(16))) uint8_t x_dyn[];  // kW * kRing slots
@@ -401,7 +401,8 @@ hipError_t launch_ps_group(const uint16_t* x, const u32x4* qb, const uint16_t* s
                            uint16_t* y, float* part, int m, int n, int k, const GemvPlan& plan, int units, XcdMap map,
                            dim3 grid, hipStream_t stream) {
   if (m > 48) return launch_ps_strips<4, kGS, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
-  return launch_ps_strips<3, kGS, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+  if (m > 32) return launch_ps_strips<3, kGS, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
+  return launch_ps_strips<2, kGS, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid, stream);
 }
 
 }  // namespace
@@ -410,7 +411,7 @@ hipError_t launch_w4a16_gemv_blocked_prescaled(const uint16_t* x, const u32x4* q
                                                const uint32_t* qz, uint16_t* y, float* part, int m, int n, int k,
                                                const GemvPlan& plan, int units, int strips_per_xcd, dim3 grid,
                                                bool bf16, hipStream_t stream) {
-  if (m <= 32 || m > kGemvMaxM) return hipErrorInvalidValue;
+  if (m <= 16 || m > kGemvMaxM) return hipErrorInvalidValue;
   XcdMap map;
   map.strips_per_xcd = strips_per_xcd;
   switch (plan.group * 2 + (bf16 ? 1 : 0)) {
