@@ -321,11 +321,11 @@ size_t mq_w4a16_gemv_blocked_workspace_bytes(int64_t M, int64_t N, int64_t K, in
  * workgroup of 8 or 16 wavefronts per strip (their sums added in LDS in
  * wavefront order, no workspace); otherwise K is split across workgroups
  * (fp32 partials in `workspace`, added in split order by a second kernel).
- * All M <= 64 tokens share one pass
- * over the weights. For 33-64 tokens the fragments are the weights themselves,
- * rounded once to fp16 as in mq_w4a16_gemm (fp16((q - z) * s), the same range
- * notes apply), accumulated in fp32; up to 32 tokens use the exact (q - z)
- * form with s applied in fp32. Deterministic.
+ * All M <= 64 tokens share one pass over the weights. For 17-64 tokens the
+ * fragments are the weights themselves, rounded once to fp16 as in
+ * mq_w4a16_gemm (fp16((q - z) * s), the same range notes apply), accumulated
+ * in fp32; up to 16 tokens use the exact (q - z) form with s applied in fp32.
+ * Deterministic.
  *
  *   workspace   >= mq_w4a16_gemv_blocked_workspace_bytes(M, N, K, group)
  *               bytes, 16-byte aligned (may be NULL when that is 0); same
@@ -353,7 +353,7 @@ mq_status mq_w4a16_gemv_blocked(const uint16_t* x, const int32_t* qweight_blocke
  *   mq_w4a16_gemv_bf16, mq_w4a16_gemv_blocked_bf16: fragments hold 128 + q
  *     exactly in bf16 and per group the kernel adds, in binary32,
  *     s * (sum(x * (128 + q)) - (128 + z) * sum(x)); on the decode layout
- *     33-64 tokens round each weight once to bf16 as the GEMM does.
+ *     17-64 tokens round each weight once to bf16 as the GEMM does.
  * Error bound, element by element, against the exact sum y64 (derived from
  * that arithmetic: bf16 unit roundoff 2^-8, binary32 2^-24): weight-rounding
  * forms |y - y64| <= 2^-8 |y64| + (2^-8 + K 2^-24) sum_k |x w| (1 + 2^-7);

@@ -54,8 +54,8 @@ def test_gemv_blocked_decode_gate_up(M):
                                    (2, 640, 640), (7, 384, 32), (40, 640, 96), (1, 4096, 24608),
                                    # workgroups of three (5..16 tokens) or two (17..32) adjacent strips
                                    (12, 640, 96), (9, 4096, 24576), (5, 1024, 3072), (24, 512, 4096),
-                                   # 33-64 tokens: six and ten 64-row steps per wavefront (the
-                                   # four-step pipeline's tail after zero and one steady rounds)
+                                   # 17-64 tokens: six and ten 64-row steps per wavefront (the
+                                   # two-step pipeline's tail after two and four steady rounds)
                                    (48, 3072, 4096), (40, 5120, 8192)])
 def test_gemv_blocked_shapes(M, K, N, G):
     d = synth.w4a16_inputs(M, K, N, group=G, outlier_frac=0.005, tag=M + K + N + G)

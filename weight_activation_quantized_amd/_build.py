@@ -42,9 +42,9 @@ FLAGS = [
 # Per-source extra flags: MFMA results in ordinary VGPRs. The GEMV starts its
 # nine MFMAs of a step from zero every step; the VGPR form gives each its own
 # destination (otherwise they share one AGPR quad and wait on each other's
-# copy-out). The decode-layout GEMV's one- and two-tile forms read their
-# per-group sums with VALU operations (no copies out of AGPRs); its forms
-# for 33-64 tokens (their own file) measured faster in the AGPR form.
+# copy-out). The decode-layout GEMV's one-tile kernel reads its per-group
+# sums with VALU operations (no copies out of AGPRs); its kernel for 17-64
+# tokens lives in its own file, built without this flag.
 SOURCE_FLAGS = {
     "w4a16_gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "w4a16_gemv_blocked.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],

@@ -553,7 +553,7 @@ hipError_t launch_blocked_xl(const uint16_t* x, const u32x4* qb, const uint16_t*
 
 }  // namespace
 
-// The forms with three or four token tiles (33-64 tokens), defined in
+// The forms with two to four token tiles (17-64 tokens), defined in
 // w4a16_gemv_blocked_prescaled.hip.
 hipError_t launch_w4a16_gemv_blocked_prescaled(const uint16_t* x, const u32x4* qb, const uint16_t* scales,
                                                const uint32_t* qz, uint16_t* y, float* part, int m, int n, int k,
