@@ -15,7 +15,8 @@
 // row (one 16-byte load of 8 values per lane, up to two rows in flight per
 // group), min and max come from a butterfly within the group, and each lane
 // writes its 8 codes (8 bytes, or 4 packed bytes for INT4). The codes come
-// from a reciprocal product, with the IEEE division only near half-integers.
+// from a reciprocal product, with the IEEE division only near half-integers
+// (one branch per lane's 8 values); min and max within 16-lane rows by DPP.
 // x is fp16 or bf16 (both widen exactly to binary32). x is read once;
 // nothing else is.
 #include "device_common.h"
@@ -24,17 +25,19 @@
 namespace mq {
 namespace {
 
-template <int kL>
-__device__ __forceinline__ float group_min(float v) {
+// Minimum / maximum over a group of kL consecutive lanes (every lane of the
+// group gets it): DPP steps within 16-lane rows (quad permutes, half-row and
+// row mirrors) for up to 16 lanes, then shuffles across rows. Exact and
+// order-free.
+template <int kL, bool kMax>
+__device__ __forceinline__ float group_reduce(float v) {
+  auto op = [](float a, float b) { return kMax ? fmaxf(a, b) : fminf(a, b); };
+  if constexpr (kL >= 2) v = op(v, dpp_f32<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  if constexpr (kL >= 4) v = op(v, dpp_f32<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  if constexpr (kL >= 8) v = op(v, dpp_f32<0x141>(v));  // row_half_mirror
+  if constexpr (kL >= 16) v = op(v, dpp_f32<0x140>(v));  // row_mirror
 #pragma unroll
-  for (int off = kL / 2; off >= 1; off >>= 1) v = fminf(v, __shfl_xor(v, off, kWave));
-  return v;
-}
-
-template <int kL>
-__device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int off = kL / 2; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  for (int off = 16; off < kL; off <<= 1) v = op(v, __shfl_xor(v, off, kWave));
   return v;
 }
 
@@ -47,13 +50,30 @@ __device__ __forceinline__ float group_max(float v) {
 // the margin (ties among them) take the division.
 constexpr float kKvTieMargin = 1.0f / 4096.0f;
 
-// Written so that a non-finite p also divides: a binary32-subnormal scale
-// (possible for bf16 rows) gets an infinite reciprocal (kv_rcp).
-__device__ __forceinline__ float kv_code(float d, float scale, float r) {
-  const float p = d * r;
-  const float t = rintf(p);
-  if (!(0.5f - fabsf(p - t) >= kKvTieMargin)) return rintf(d / scale);
-  return t;
+// Codes of the 8 values d[] = x - min of a lane, clamped to [0, kQmax]: the
+// reciprocal product everywhere, then, in one branch per 8 values, the IEEE
+// division for those within the margin (written so that a non-finite p also
+// divides: a binary32-subnormal scale, possible for bf16 rows, gets an
+// infinite reciprocal from kv_rcp).
+template <int kBits>
+__device__ __forceinline__ void kv_codes(const float (&d)[8], float scale, float r, float (&q)[8]) {
+  constexpr float kQmax = static_cast<float>((1 << kBits) - 1);
+  bool slow = false;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float p = d[e] * r;
+    q[e] = rintf(p);
+    slow |= !(fabsf(p - q[e]) <= 0.5f - kKvTieMargin);
+  }
+  if (slow) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = d[e] * r;
+      if (!(fabsf(p - q[e]) <= 0.5f - kKvTieMargin)) q[e] = rintf(d[e] / scale);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) q[e] = __builtin_amdgcn_fmed3f(q[e], 0.f, kQmax);
 }
 
 __device__ __forceinline__ float kv_rcp(float scale) {
@@ -92,27 +112,30 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(const uint16_t* __restric
       mx = fmaxf(mx, f[e]);
     }
     // every lane of a group takes part; a zero minimum or maximum becomes +0
-    mn = group_min<kL>(mn) + 0.0f;
-    mx = group_max<kL>(mx) + 0.0f;
+    mn = group_reduce<kL, false>(mn) + 0.0f;
+    mx = group_reduce<kL, true>(mx) + 0.0f;
     if (row >= rows) continue;
     const float scale = (mx - mn) / kQmax;  // IEEE binary32 subtraction and division
-    uint32_t q[8];
+    float q[8];
     if (scale > 0.f) {
-      const float rs = kv_rcp(scale);
+      float d[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        q[e] = static_cast<uint32_t>(fminf(fmaxf(kv_code(f[e] - mn, scale, rs), 0.f), kQmax));
+      for (int e = 0; e < 8; ++e) d[e] = f[e] - mn;
+      kv_codes<kBits>(d, scale, kv_rcp(scale), q);
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) q[e] = 0u;
+      for (int e = 0; e < 8; ++e) q[e] = 0.f;
     }
     if constexpr (kBits == 8) {
-      const u32x2 out = u32x2{q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24),
-                              q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24)};
-      __builtin_nontemporal_store(out, reinterpret_cast<u32x2*>(codes + row * kD + 8 * lig));
+      // codes in [0, 255]: one unsigned 8-bit conversion per code packs them
+      uint32_t w[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(q[e], e & 3, w[e >> 2]);
+      __builtin_nontemporal_store(u32x2{w[0], w[1]}, reinterpret_cast<u32x2*>(codes + row * kD + 8 * lig));
     } else {
-      const uint32_t out = (q[0] | (q[1] << 4)) | ((q[2] | (q[3] << 4)) << 8) | ((q[4] | (q[5] << 4)) << 16) |
-                           ((q[6] | (q[7] << 4)) << 24);
+      uint32_t out = 0u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out |= static_cast<uint32_t>(q[e]) << (4 * e);
       __builtin_nontemporal_store(out, reinterpret_cast<uint32_t*>(codes + row * (kD / 2) + 4 * lig));
     }
     if (lig == 0) {
