@@ -330,7 +330,8 @@ size_t mq_w4a16_gemv_blocked_workspace_bytes(int64_t M, int64_t N, int64_t K, in
  *   workspace   >= mq_w4a16_gemv_blocked_workspace_bytes(M, N, K, group)
  *               bytes, 16-byte aligned (may be NULL when that is 0); same
  *               rules as mq_w4a16_gemv's workspace.
- * Requires: as mq_w4a16_gemv, and N % 32 == 0 (-> MQ_ERR_SHAPE),
+ * Requires: as mq_w4a16_gemv, and N % 32 == 0 and a scale table
+ * (K/group or 1 rows of N fp16) under 2^31 bytes (-> MQ_ERR_SHAPE),
  * qweight_blocked 16-byte aligned.
  */
 mq_status mq_w4a16_gemv_blocked(const uint16_t* x, const int32_t* qweight_blocked, const uint16_t* scales,

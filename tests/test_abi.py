@@ -244,6 +244,9 @@ def test_w4a16_blocked_validation(lib):
     assert v(A, B, C, D, E, 1, 256, 256, 96, F, 1 << 20, None) == UNSUP
     assert v(A, B, C, D, E, 65, 256, 256, 128, F, 1 << 20, None) == UNSUP
     assert v(A, B, C, D, E, 0, 256, 256, 128, None, 0, None) == OK
+    # scale tables of 2^31 bytes or more (32-bit offsets in the kernels)
+    assert v(A, B, C, D, E, 1, 32768, 1 << 20, 32, F, 1 << 40, None) == SHAPE and "scales" in _err(lib)
+    assert ws(1, 32768, 1 << 20, 32) == 0
     # wide layers need no workspace; narrow ones with up to 8 tokens and
     # short K neither (one workgroup per strip takes all of K); narrow ones
     # with long K or more tokens split K and need one

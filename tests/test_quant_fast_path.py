@@ -61,7 +61,7 @@ def test_fast_path_codes_equal_the_oracle():
             codes, fast = _fast_codes(x, s, r)
             assert np.array_equal(codes[fast], q_ref.astype(np.int32)[fast])
             # on the workload the division is the exception (about 1 element
-            # in 2000); the near-boundary rows put 60% of theirs inside the margin
+            # in 2000); the near-boundary rows put about 40% of theirs inside it
             assert fast.mean() > 0.999 if x.shape[0] == 2048 else 0.3 < fast.mean() < 0.5
 
 

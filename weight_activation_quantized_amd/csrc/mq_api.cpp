@@ -506,9 +506,16 @@ mq_status mq_w4a16_block_weights(const int32_t* qweight, int32_t* qweight_blocke
                     "w4a16_block_weights launch");
 }
 
+// The decode-layout kernels address the scale and zero-point tables with
+// 32-bit buffer offsets.
+constexpr size_t kMaxScaleBytes = (size_t{1} << 31) - 1;
+static bool blocked_scales_fit(int64_t N, int64_t K, int64_t group) {
+  return group_rows(K, group) * static_cast<size_t>(N) * 2 <= kMaxScaleBytes;
+}
+
 size_t mq_w4a16_gemv_blocked_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t group) {
   if (!w4a16_group_ok(group) || M < 1 || M > mq::kGemvMaxM || N < 32 || N % 32 ||
-      N > kMaxN4 || K < 128 || K > kMaxK || K % 128)
+      N > kMaxN4 || K < 128 || K > kMaxK || K % 128 || !blocked_scales_fit(N, K, group))
     return 0;
   return mq::w4a16_gemv_blocked_workspace(M, N, K, kernel_group(group));
 }
@@ -520,6 +527,9 @@ static mq_status w4a16_gemv_blocked_impl(const uint16_t* x, const int32_t* qweig
   mq_status s = check_w4a16(x, qweight_blocked, scales, qzeros, y, M, N, K, group);
   if (s != MQ_OK) return s;
   if (N % 32) return fail(MQ_ERR_SHAPE, "the blocked layout needs N %% 32 == 0 (got N=%lld)", (long long)N);
+  if (!blocked_scales_fit(N, K, group))
+    return fail(MQ_ERR_SHAPE, "scales of %zu bytes: the decode-layout GEMV takes at most 2^31 - 1",
+                group_rows(K, group) * static_cast<size_t>(N) * 2);
   if (!aligned(qweight_blocked, 16)) return fail(MQ_ERR_ALIGN, "qweight_blocked must be 16-byte aligned");
   if (M > mq::kGemvMaxM)
     return fail(MQ_ERR_UNSUPPORTED, "GEMV needs M <= %lld (got %lld); use mq_w4a16_gemm",
