@@ -28,9 +28,9 @@
 //   neighbouring memory (as a sweep over the rows of [K, N/8] does).
 //
 // Kernel: a workgroup owns one strip (and, for narrow layers, one of
-// `splits` K ranges); its wavefronts take consecutive 128-row chunks of that
-// range, each streaming its own contiguous bytes into registers (two chunks
-// in flight). Lane (j, h) of an MFMA B fragment (v_mfma_f32_16x16x32_f16,
+// `splits` K ranges); its wavefronts take that range's 128-row chunks in
+// turn (wavefront w: chunks w, w + W, ...), each chunk a contiguous run of
+// bytes streamed into registers (two chunks in flight per wavefront). Lane (j, h) of an MFMA B fragment (v_mfma_f32_16x16x32_f16,
 // column j, k = 8h..8h+7 of a 32-row block) gets from its 8 bytes of the
 // block both field 2g (tile 0) and field 2g+1 (tile 1) of packed column c:
 // one byte permute per row pair spreads two bytes into the two fp16 halves,
@@ -358,7 +358,13 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
   const int chunks = K / kBChunkRows;
   const int cps = chunks / splits;  // chunks per split (plan: divides)
   const int cpw = cps / kW;         // chunks per wavefront (plan: divides, >= 1)
-  const int c0 = split * cps + wave * cpw;
+  // Wavefront w takes chunks w, w + kW, w + 2 kW, ... of the split, so the
+  // workgroup's requests in flight fall on neighbouring rows of the weights
+  // (one narrow band of memory for all workgroups) rather than on kW bands a
+  // quarter of the range apart: 1 / 4 / 16 tokens at N = 24576 went from
+  // 11.06 / 11.42 / 12.12 to 10.61 / 10.96 / 11.83 us.
+  const int c0 = split * cps + wave;
+  auto chunk_of = [&](int i) { return c0 + i * kW; };
   const int col = strip * kBStrip + c;  // packed column of the lane
 
   BLane L;
@@ -427,9 +433,9 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
   // slower (see the layout notes).
   {
     BChunk<kT, kGPC, kSP> ca, cb;
-    load_chunk<kT, kGS, kSP, kXL, kXQ>(ca, L, c0, xslot[0]);
+    load_chunk<kT, kGS, kSP, kXL, kXQ>(ca, L, chunk_of(0), xslot[0]);
     __builtin_amdgcn_sched_barrier(0);
-    load_chunk<kT, kGS, kSP, kXL, kXQ>(cb, L, min(c0 + 1, c0 + cpw - 1), xslot[1]);
+    load_chunk<kT, kGS, kSP, kXL, kXQ>(cb, L, chunk_of(min(1, cpw - 1)), xslot[1]);
     __builtin_amdgcn_sched_barrier(0);
     // Staged x: the lane's row (token j, rows 8h.. of each block) at the
     // split's first chunk; lanes past the last token read nothing.
@@ -486,25 +492,25 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
     int i = 0;
     for (; i + 3 < cpw; i += 2) {
       if constexpr (!kXL) wait_counts<kChunkLoads, 15>();
-      compute(ca, c0 + i, 0);
+      compute(ca, chunk_of(i), 0);
       __builtin_amdgcn_sched_barrier(0);
-      load_chunk<kT, kGS, kSP, kXL, kXQ>(ca, L, c0 + i + 2, xslot[0]);
+      load_chunk<kT, kGS, kSP, kXL, kXQ>(ca, L, chunk_of(i + 2), xslot[0]);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (!kXL) wait_counts<kChunkLoads, 15>();
-      compute(cb, c0 + i + 1, 1);
+      compute(cb, chunk_of(i + 1), 1);
       __builtin_amdgcn_sched_barrier(0);
-      load_chunk<kT, kGS, kSP, kXL, kXQ>(cb, L, c0 + i + 3, xslot[1]);
+      load_chunk<kT, kGS, kSP, kXL, kXQ>(cb, L, chunk_of(i + 3), xslot[1]);
       __builtin_amdgcn_sched_barrier(0);
     }
     // chunks i and (if in range) i + 1 are in flight; at most i + 2 is left
     if constexpr (!kXL) wait_counts<kChunkLoads, 15>();
-    compute(ca, c0 + i, 0);
+    compute(ca, chunk_of(i), 0);
     __builtin_amdgcn_sched_barrier(0);
-    if (i + 2 < cpw) load_chunk<kT, kGS, kSP, kXL, kXQ>(ca, L, c0 + i + 2, xslot[0]);
+    if (i + 2 < cpw) load_chunk<kT, kGS, kSP, kXL, kXQ>(ca, L, chunk_of(i + 2), xslot[0]);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (!kXL) wait_counts<0, 15>();
-    if (i + 1 < cpw) compute(cb, c0 + i + 1, 1);
-    if (i + 2 < cpw) compute(ca, c0 + i + 2, 0);
+    if (i + 1 < cpw) compute(cb, chunk_of(i + 1), 1);
+    if (i + 2 < cpw) compute(ca, chunk_of(i + 2), 0);
   }
 
   // Add the wavefronts' sums and store (see store_unit_sums). Forms
