@@ -120,11 +120,12 @@ __device__ __forceinline__ void load_chunk(BChunk<kT, kBChunkRows / kGS, kSP>& c
   const u32x4* wp = L.qb + static_cast<size_t>(2 * chunk) * L.pair_stride;
   // The weights are read once per call: non-temporal loads (about 1% faster
   // than ordinary ones, measured) keep them from displacing cached data.
+  // The unit's strips are adjacent in a pair, so each pair's slots go out as
+  // one contiguous run of requests (pair 0 of every strip, then pair 1).
 #pragma unroll
-  for (int sp = 0; sp < kSP; ++sp) {  // adjacent strips' slots are adjacent
-    ch.w[sp][0] = __builtin_nontemporal_load(wp + 64 * sp);
-    ch.w[sp][1] = __builtin_nontemporal_load(wp + L.pair_stride + 64 * sp);
-  }
+  for (int sp = 0; sp < kSP; ++sp) ch.w[sp][0] = __builtin_nontemporal_load(wp + 64 * sp);
+#pragma unroll
+  for (int sp = 0; sp < kSP; ++sp) ch.w[sp][1] = __builtin_nontemporal_load(wp + L.pair_stride + 64 * sp);
   // With x staged up front (kXL) the fragments are read at use from there;
   // otherwise the chunk's 16 token rows per tile x 128 values move into the
   // wavefront's slot by DMA, 1 KB per load (full cache lines, where register
