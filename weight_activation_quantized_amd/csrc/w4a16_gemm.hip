@@ -488,7 +488,8 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
   // 8 (r / 4) + 4 hh + r % 4 of B column jj, i.e. output 8 (8 w + jj % 8)
   // + 2 (jj / 8) + t of the tile. The tile is staged in LDS as fp16 and
   // written out as whole rows with 16-byte stores (fp32 partial sums: 32
-  // rows at a time, staged and written the same way).
+  // rows at a time, staged and written the same way); the fp16 rows go out
+  // as non-temporal stores (about 1% faster at 4096^3, same-box A/B).
   wait_counts<0, 0>();
   bare_barrier();  // every wave is done reading the ring
   const int jj = lane & 31, hh = lane >> 5;
@@ -537,8 +538,8 @@ __global__ __launch_bounds__(kThreads) void w4a16_gemm_kernel(const uint16_t* __
     const int mt = i / kPieces, pc = i % kPieces;
     const int m = m0 + mt, c = c0 + pc;
     if (m >= M || c >= NP) continue;
-    *reinterpret_cast<u32x4*>(y + static_cast<size_t>(m) * N + 8 * c) =
-        *(const lds_u32x4*)(sm + mt * kOutPitch + 16 * pc);
+    const u32x4 v_ = *(const lds_u32x4*)(sm + mt * kOutPitch + 16 * pc);
+    __builtin_nontemporal_store(v_, reinterpret_cast<u32x4*>(y + static_cast<size_t>(m) * N + 8 * c));
   }
 }
 

