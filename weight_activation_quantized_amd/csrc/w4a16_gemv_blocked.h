@@ -111,21 +111,22 @@ struct BLane {
   int N, NP;  // row strides of scales and qzeros between groups (0: per-channel)
 };
 
-template <int kT, int kGS, int kSP, bool kXL, int kXQ>
-__device__ __forceinline__ void load_chunk(BChunk<kT, kBChunkRows / kGS, kSP>& ch, const BLane& L, int chunk,
-                                           lds_u8* xslot = nullptr) {
+// Half kHalf of a chunk's loads. Half 0: pair 0 of every strip's slot and,
+// without kXL, the chunk's x rows by DMA; half 1: pair 1 and the group
+// parameters. The steady loop issues half 0 of the next chunk in this
+// buffer as soon as the compute has used pair 0 and half 1 when it is done,
+// so fewer requests wait behind the math.
+template <int kHalf, int kT, int kGS, int kSP, bool kXL, int kXQ>
+__device__ __forceinline__ void load_half(BChunk<kT, kBChunkRows / kGS, kSP>& ch, const BLane& L, int chunk,
+                                          lds_u8* xslot) {
   constexpr int kGPC = kBChunkRows / kGS;
-  // forms without x staged up front (kXL) move each chunk's x through the
-  // wavefront's LDS slot
-  const u32x4* wp = L.qb + static_cast<size_t>(2 * chunk) * L.pair_stride;
+  const u32x4* wp = L.qb + static_cast<size_t>(2 * chunk + kHalf) * L.pair_stride;
   // The weights are read once per call: non-temporal loads (about 1% faster
   // than ordinary ones, measured) keep them from displacing cached data.
   // The unit's strips are adjacent in a pair, so each pair's slots go out as
-  // one contiguous run of requests (pair 0 of every strip, then pair 1).
+  // one contiguous run of requests.
 #pragma unroll
-  for (int sp = 0; sp < kSP; ++sp) ch.w[sp][0] = __builtin_nontemporal_load(wp + 64 * sp);
-#pragma unroll
-  for (int sp = 0; sp < kSP; ++sp) ch.w[sp][1] = __builtin_nontemporal_load(wp + L.pair_stride + 64 * sp);
+  for (int sp = 0; sp < kSP; ++sp) ch.w[sp][kHalf] = __builtin_nontemporal_load(wp + 64 * sp);
   // With x staged up front (kXL) the fragments are read at use from there;
   // otherwise the chunk's 16 token rows per tile x 128 values move into the
   // wavefront's slot by DMA, 1 KB per load (full cache lines, where register
@@ -135,14 +136,14 @@ __device__ __forceinline__ void load_chunk(BChunk<kT, kBChunkRows / kGS, kSP>& c
   // only its first kXQ loads (tokens 0 .. 4 kXQ - 1 of it; kXQ = 0: one
   // load for a single token); the kernel zeroes the slot rows past them
   // once at its start.
-  if constexpr (!kXL) {
+  if constexpr (kHalf == 0 && !kXL) {
     wait_counts<63, 0>();
 #pragma unroll
     for (int q = 0; q < 4 * (kT - 1) + (kXQ == 0 ? 1 : kXQ); ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(L.xr, (lds_void*)(xslot + 1024 * q), 16,
                                                L.xdma[q % 4] + (q / 4) * L.xtile + 256u * chunk, 0, 0, 0);
   }
-  if constexpr (!kXL) {  // with kXL the scales and zero points are staged in LDS too
+  if constexpr (kHalf == 1 && !kXL) {  // with kXL the scales and zero points are staged in LDS too
 #pragma unroll
     for (int g = 0; g < kGPC; ++g) {
       const size_t grp = static_cast<size_t>(chunk) * kGPC + g;
@@ -153,6 +154,13 @@ __device__ __forceinline__ void load_chunk(BChunk<kT, kBChunkRows / kGS, kSP>& c
       }
     }
   }
+}
+
+template <int kT, int kGS, int kSP, bool kXL, int kXQ>
+__device__ __forceinline__ void load_chunk(BChunk<kT, kBChunkRows / kGS, kSP>& ch, const BLane& L, int chunk,
+                                           lds_u8* xslot = nullptr) {
+  load_half<0, kT, kGS, kSP, kXL, kXQ>(ch, L, chunk, xslot);
+  load_half<1, kT, kGS, kSP, kXL, kXQ>(ch, L, chunk, xslot);
 }
 
 // B fragments of one 32-row block from the lane's two words of it (rows
@@ -184,71 +192,70 @@ __device__ __forceinline__ void unpack_block(uint32_t w0, uint32_t w1, const Nib
     }
 }
 
-// kLaneRows: tokens 4h .. 4h + kLaneRows - 1 of a lane's four are in use
-// (1 for a single token: the per-group update of the other three is skipped).
-template <int kT, int kGS, int kSP, bool kXL, bool kBF, int kLaneRows = 4>
-__device__ __forceinline__ void compute_chunk(const BChunk<kT, kBChunkRows / kGS, kSP>& ch, const NibConst& nc,
-                                              const f16x8 ones, int g_lane, f32x4 (&tot)[kT][kSP][2],
-                                              const lds_u8* xl, const lds_u8* scl, const lds_u8* zl,
-                                              const lds_u8* xs, const int (&xo)[4]) {
-  constexpr int kGPC = kBChunkRows / kGS;  // groups per chunk
-  constexpr int kBPG = kGS / 32;           // 32-row blocks per group
-  const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
-  // xl: the lane's 16 bytes of block 0 of this chunk in the staged x (its
-  // token row, rows 8h..8h+7), or nullptr for lanes past the last token.
-  // scl / zl (kXL): the lane's scale pair and zero-point word of the chunk's
-  // first group for strip 0 in the staged tables (groups kSP * 64 / kSP * 16
-  // bytes apart, strips 64 / 16 bytes apart).
-  uint32_t sv[kSP][kGPC], zw[kSP][kGPC];
-#pragma unroll
-  for (int sp = 0; sp < kSP; ++sp)
-#pragma unroll
-    for (int g = 0; g < kGPC; ++g) {
-      if constexpr (kXL) {
-        sv[sp][g] = *(const lds_u32*)(scl + (g * kSP + sp) * 64);
-        zw[sp][g] = *(const lds_u32*)(zl + (g * kSP + sp) * 16);
-      } else {
-        sv[sp][g] = ch.sv[sp][g];
-        zw[sp][g] = ch.zw[sp][g];
-      }
-    }
-  f16x8 xa[kT][4];
+// The x fragments of a chunk (all four 32-row blocks): from the staged x
+// (kXL; xl is the lane's 16 bytes of block 0, its token row, rows 8h..8h+7,
+// or nullptr for lanes past the last token) or from the chunk's slot (token
+// row 16t + j, rows 8h.. of block b at xs + xo[b]).
+template <int kT, bool kXL>
+__device__ __forceinline__ void read_x(f16x8 (&xa)[kT][4], const lds_u8* xl, const lds_u8* xs, const int (&xo)[4]) {
 #pragma unroll
   for (int t = 0; t < kT; ++t)
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       if constexpr (kXL) {
         xa[t][b] = xl ? *reinterpret_cast<const lds_f16x8*>(xl + 64 * b) : f16x8{};
-      } else {  // the chunk's slot: token row 16t + j, rows 8h.. of block b
+      } else {
         xa[t][b] = *(const lds_f16x8*)(xs + 4096 * t + xo[b]);
       }
     }
+}
+
+// Blocks kB0 .. kB1 - 1 of a chunk: MFMAs into the group's sums acc (and
+// accx, the sums of x against ones), and at each group's last block
+// tot += s * (acc - (1024 + z) * X). acc and accx are carried between the
+// two halves of a chunk when a group spans both (groups of 128).
+// kLaneRows: tokens 4h .. 4h + kLaneRows - 1 of a lane's four are in use
+// (1 for a single token: the per-group update of the other three is
+// skipped). scl / zl (kXL): the lane's scale pair and zero-point word of the
+// chunk's first group for strip 0 in the staged tables (groups kSP * 64 /
+// kSP * 16 bytes apart, strips 64 / 16 bytes apart).
+template <int kB0, int kB1, int kT, int kGS, int kSP, bool kXL, bool kBF, int kLaneRows>
+__device__ __forceinline__ void compute_blocks(const BChunk<kT, kBChunkRows / kGS, kSP>& ch, const NibConst& nc,
+                                               const f16x8 ones, int g_lane, f32x4 (&tot)[kT][kSP][2],
+                                               f32x4 (&acc)[kT][kSP][2], f32x4 (&accx)[kT],
+                                               const f16x8 (&xa)[kT][4], const lds_u8* scl, const lds_u8* zl) {
+  constexpr int kBPG = kGS / 32;  // 32-row blocks per group
+  const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int g = 0; g < kGPC; ++g) {
-    f32x4 acc[kT][kSP][2];
-    f32x4 accx[kT];
+  for (int b = kB0; b < kB1; ++b) {  // block within the chunk: pair b / 2, half b % 2
+    const int g = b / kBPG, bb = b % kBPG;
 #pragma unroll
-    for (int bb = 0; bb < kBPG; ++bb) {
-      const int b = g * kBPG + bb;  // block within the chunk: pair b / 2, half b % 2
+    for (int sp = 0; sp < kSP; ++sp) {
+      f16x8 bf[2];
+      unpack_block<kBF>(ch.w[sp][b >> 1][2 * (b & 1)], ch.w[sp][b >> 1][2 * (b & 1) + 1], nc, bf);
 #pragma unroll
-      for (int sp = 0; sp < kSP; ++sp) {
-        f16x8 bf[2];
-        unpack_block<kBF>(ch.w[sp][b >> 1][2 * (b & 1)], ch.w[sp][b >> 1][2 * (b & 1) + 1], nc, bf);
+      for (int t = 0; t < kT; ++t)
 #pragma unroll
-        for (int t = 0; t < kT; ++t)
-#pragma unroll
-          for (int f = 0; f < 2; ++f)
-            acc[t][sp][f] = mfma_16x16x32<kBF>(xa[t][b], bf[f], bb == 0 ? zero4 : acc[t][sp][f]);
-      }
-#pragma unroll
-      for (int t = 0; t < kT; ++t) accx[t] = mfma_16x16x32<kBF>(xa[t][b], ones, bb == 0 ? zero4 : accx[t]);
+        for (int f = 0; f < 2; ++f)
+          acc[t][sp][f] = mfma_16x16x32<kBF>(xa[t][b], bf[f], bb == 0 ? zero4 : acc[t][sp][f]);
     }
+#pragma unroll
+    for (int t = 0; t < kT; ++t) accx[t] = mfma_16x16x32<kBF>(xa[t][b], ones, bb == 0 ? zero4 : accx[t]);
+    if (bb != kBPG - 1) continue;
     // tot += s * (acc - (1024 + z) * X); field 2g+1 carries 16 (q - z), so
     // its scale is s / 16 (exact). bf16: both fields carry 128 + q.
 #pragma unroll
     for (int sp = 0; sp < kSP; ++sp) {
-      const f16x2 s2 = as_f16x2(sv[sp][g]);
-      const uint32_t zb = (zw[sp][g] >> (8 * g_lane)) & 0xFFu;
+      uint32_t sv, zw;
+      if constexpr (kXL) {
+        sv = *(const lds_u32*)(scl + (g * kSP + sp) * 64);
+        zw = *(const lds_u32*)(zl + (g * kSP + sp) * 16);
+      } else {
+        sv = ch.sv[sp][g];
+        zw = ch.zw[sp][g];
+      }
+      const f16x2 s2 = as_f16x2(sv);
+      const uint32_t zb = (zw >> (8 * g_lane)) & 0xFFu;
       const float sc[2] = {static_cast<float>(s2[0]), static_cast<float>(s2[1]) * (kBF ? 1.0f : 0.0625f)};
       const float bias[2] = {(kBF ? 128.0f : 1024.0f) + static_cast<float>(zb & 15u),
                              kBF ? 128.0f + static_cast<float>(zb >> 4) : 1024.0f + static_cast<float>(zb & 0xF0u)};
@@ -486,22 +493,36 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
     // only those in flight; where no later chunk was requested, wait for all.
     constexpr int kChunkLoads = 2 * kSP + 4 * (kT - 1) + (kXQ == 0 ? 1 : kXQ) + 2 * kSP * kGPC;
     static_assert(kXL || kChunkLoads < 64, "vmcnt range");
+    constexpr int kLR = kXQ == 0 ? 1 : 4;
+    // a whole chunk (the last two or three of a wavefront)
     auto compute = [&](const BChunk<kT, kGPC, kSP>& ch, int chunk, int buf) {
-      compute_chunk<kT, kGS, kSP, kXL, kBF, kXQ == 0 ? 1 : 4>(ch, nc, ones, g, tot, xl(chunk), sl(chunk), zl(chunk),
-                                                           xs[buf], xo);
+      f32x4 acc[kT][kSP][2], accx[kT];
+      f16x8 xa[kT][4];
+      read_x<kT, kXL>(xa, xl(chunk), xs[buf], xo);
+      compute_blocks<0, 4, kT, kGS, kSP, kXL, kBF, kLR>(ch, nc, ones, g, tot, acc, accx, xa, sl(chunk), zl(chunk));
+    };
+    // a chunk of the steady loop: the buffer's next chunk is requested in
+    // two halves, pair 0 and x as soon as the compute has used pair 0, the
+    // rest when it is done (the x fragments were read into registers first)
+    auto compute_refill = [&](BChunk<kT, kGPC, kSP>& ch, int chunk, int buf, int next) {
+      f32x4 acc[kT][kSP][2], accx[kT];
+      f16x8 xa[kT][4];
+      read_x<kT, kXL>(xa, xl(chunk), xs[buf], xo);
+      compute_blocks<0, 2, kT, kGS, kSP, kXL, kBF, kLR>(ch, nc, ones, g, tot, acc, accx, xa, sl(chunk), zl(chunk));
+      __builtin_amdgcn_sched_barrier(0);
+      load_half<0, kT, kGS, kSP, kXL, kXQ>(ch, L, next, xslot[buf]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_blocks<2, 4, kT, kGS, kSP, kXL, kBF, kLR>(ch, nc, ones, g, tot, acc, accx, xa, sl(chunk), zl(chunk));
+      __builtin_amdgcn_sched_barrier(0);
+      load_half<1, kT, kGS, kSP, kXL, kXQ>(ch, L, next, xslot[buf]);
+      __builtin_amdgcn_sched_barrier(0);
     };
     int i = 0;
     for (; i + 3 < cpw; i += 2) {
       if constexpr (!kXL) wait_counts<kChunkLoads, 15>();
-      compute(ca, chunk_of(i), 0);
-      __builtin_amdgcn_sched_barrier(0);
-      load_chunk<kT, kGS, kSP, kXL, kXQ>(ca, L, chunk_of(i + 2), xslot[0]);
-      __builtin_amdgcn_sched_barrier(0);
+      compute_refill(ca, chunk_of(i), 0, chunk_of(i + 2));
       if constexpr (!kXL) wait_counts<kChunkLoads, 15>();
-      compute(cb, chunk_of(i + 1), 1);
-      __builtin_amdgcn_sched_barrier(0);
-      load_chunk<kT, kGS, kSP, kXL, kXQ>(cb, L, chunk_of(i + 3), xslot[1]);
-      __builtin_amdgcn_sched_barrier(0);
+      compute_refill(cb, chunk_of(i + 1), 1, chunk_of(i + 3));
     }
     // chunks i and (if in range) i + 1 are in flight; at most i + 2 is left
     if constexpr (!kXL) wait_counts<kChunkLoads, 15>();
