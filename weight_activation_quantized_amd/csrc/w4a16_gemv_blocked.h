@@ -111,22 +111,26 @@ struct BLane {
   int N, NP;  // row strides of scales and qzeros between groups (0: per-channel)
 };
 
-// Half kHalf of a chunk's loads. Half 0: pair 0 of every strip's slot and,
-// without kXL, the chunk's x rows by DMA; half 1: pair 1 and the group
-// parameters. The steady loop issues half 0 of the next chunk in this
-// buffer as soon as the compute has used pair 0 and half 1 when it is done,
-// so fewer requests wait behind the math.
-template <int kHalf, int kT, int kGS, int kSP, bool kXL, int kXQ>
-__device__ __forceinline__ void load_half(BChunk<kT, kBChunkRows / kGS, kSP>& ch, const BLane& L, int chunk,
+// Part kPart of a chunk's loads. Part 0: without kXL, the chunk's x rows by
+// DMA; part 1: pair 0 of every strip's slot; part 2: pair 1 and the group
+// parameters. The steady loop issues part 0 of the next chunk in a buffer
+// once the compute has read its x fragments, part 1 once it has used pair 0
+// and part 2 when it is done, so fewer requests wait behind the math. (The
+// parameters go last: copying them out of the registers the next chunk's
+// loads write would make the loop wait for those loads.)
+template <int kPart, int kT, int kGS, int kSP, bool kXL, int kXQ>
+__device__ __forceinline__ void load_part(BChunk<kT, kBChunkRows / kGS, kSP>& ch, const BLane& L, int chunk,
                                           lds_u8* xslot) {
   constexpr int kGPC = kBChunkRows / kGS;
-  const u32x4* wp = L.qb + static_cast<size_t>(2 * chunk + kHalf) * L.pair_stride;
   // The weights are read once per call: non-temporal loads (about 1% faster
   // than ordinary ones, measured) keep them from displacing cached data.
   // The unit's strips are adjacent in a pair, so each pair's slots go out as
   // one contiguous run of requests.
+  if constexpr (kPart > 0) {
+    const u32x4* wp = L.qb + static_cast<size_t>(2 * chunk + kPart - 1) * L.pair_stride;
 #pragma unroll
-  for (int sp = 0; sp < kSP; ++sp) ch.w[sp][kHalf] = __builtin_nontemporal_load(wp + 64 * sp);
+    for (int sp = 0; sp < kSP; ++sp) ch.w[sp][kPart - 1] = __builtin_nontemporal_load(wp + 64 * sp);
+  }
   // With x staged up front (kXL) the fragments are read at use from there;
   // otherwise the chunk's 16 token rows per tile x 128 values move into the
   // wavefront's slot by DMA, 1 KB per load (full cache lines, where register
@@ -136,14 +140,14 @@ __device__ __forceinline__ void load_half(BChunk<kT, kBChunkRows / kGS, kSP>& ch
   // only its first kXQ loads (tokens 0 .. 4 kXQ - 1 of it; kXQ = 0: one
   // load for a single token); the kernel zeroes the slot rows past them
   // once at its start.
-  if constexpr (kHalf == 0 && !kXL) {
+  if constexpr (kPart == 0 && !kXL) {
     wait_counts<63, 0>();
 #pragma unroll
     for (int q = 0; q < 4 * (kT - 1) + (kXQ == 0 ? 1 : kXQ); ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(L.xr, (lds_void*)(xslot + 1024 * q), 16,
                                                L.xdma[q % 4] + (q / 4) * L.xtile + 256u * chunk, 0, 0, 0);
   }
-  if constexpr (kHalf == 1 && !kXL) {  // with kXL the scales and zero points are staged in LDS too
+  if constexpr (kPart == 2 && !kXL) {  // with kXL the scales and zero points are staged in LDS too
 #pragma unroll
     for (int g = 0; g < kGPC; ++g) {
       const size_t grp = static_cast<size_t>(chunk) * kGPC + g;
@@ -159,8 +163,9 @@ __device__ __forceinline__ void load_half(BChunk<kT, kBChunkRows / kGS, kSP>& ch
 template <int kT, int kGS, int kSP, bool kXL, int kXQ>
 __device__ __forceinline__ void load_chunk(BChunk<kT, kBChunkRows / kGS, kSP>& ch, const BLane& L, int chunk,
                                            lds_u8* xslot = nullptr) {
-  load_half<0, kT, kGS, kSP, kXL, kXQ>(ch, L, chunk, xslot);
-  load_half<1, kT, kGS, kSP, kXL, kXQ>(ch, L, chunk, xslot);
+  load_part<1, kT, kGS, kSP, kXL, kXQ>(ch, L, chunk, xslot);
+  load_part<0, kT, kGS, kSP, kXL, kXQ>(ch, L, chunk, xslot);
+  load_part<2, kT, kGS, kSP, kXL, kXQ>(ch, L, chunk, xslot);
 }
 
 // B fragments of one 32-row block from the lane's two words of it (rows
@@ -430,7 +435,10 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
       for (int f = 0; f < 2; ++f) tot[t][sp][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Two chunks in flight per wavefront: a buffer's next chunk is requested
-  // as soon as the buffer has been consumed; sched_barrier keeps each
+  // part by part as the buffer is consumed (x once its fragments are in
+  // registers, pair 0 once blocks 0-1 are done, the rest at the end: 1 / 8
+  // / 16 tokens at N = 24576 10.64 / 11.12 / 11.69 -> 10.51 / 10.85 / 11.42
+  // us against the whole chunk after the compute); sched_barrier keeps each
   // request ahead of the math it is meant to overlap. The steady loop only
   // runs while both of its requests are in range, so they are
   // unconditional (a conditional request inside the loop makes the compiler
@@ -502,19 +510,23 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
       compute_blocks<0, 4, kT, kGS, kSP, kXL, kBF, kLR>(ch, nc, ones, g, tot, acc, accx, xa, sl(chunk), zl(chunk));
     };
     // a chunk of the steady loop: the buffer's next chunk is requested in
-    // two halves, pair 0 and x as soon as the compute has used pair 0, the
-    // rest when it is done (the x fragments were read into registers first)
+    // three parts, x once this chunk's x fragments are in registers, pair 0
+    // once the compute has used pair 0, pair 1 and the parameters when it is
+    // done
     auto compute_refill = [&](BChunk<kT, kGPC, kSP>& ch, int chunk, int buf, int next) {
       f32x4 acc[kT][kSP][2], accx[kT];
       f16x8 xa[kT][4];
       read_x<kT, kXL>(xa, xl(chunk), xs[buf], xo);
+      __builtin_amdgcn_sched_barrier(0);
+      load_part<0, kT, kGS, kSP, kXL, kXQ>(ch, L, next, xslot[buf]);
+      __builtin_amdgcn_sched_barrier(0);
       compute_blocks<0, 2, kT, kGS, kSP, kXL, kBF, kLR>(ch, nc, ones, g, tot, acc, accx, xa, sl(chunk), zl(chunk));
       __builtin_amdgcn_sched_barrier(0);
-      load_half<0, kT, kGS, kSP, kXL, kXQ>(ch, L, next, xslot[buf]);
+      load_part<1, kT, kGS, kSP, kXL, kXQ>(ch, L, next, xslot[buf]);
       __builtin_amdgcn_sched_barrier(0);
       compute_blocks<2, 4, kT, kGS, kSP, kXL, kBF, kLR>(ch, nc, ones, g, tot, acc, accx, xa, sl(chunk), zl(chunk));
       __builtin_amdgcn_sched_barrier(0);
-      load_half<1, kT, kGS, kSP, kXL, kXQ>(ch, L, next, xslot[buf]);
+      load_part<2, kT, kGS, kSP, kXL, kXQ>(ch, L, next, xslot[buf]);
       __builtin_amdgcn_sched_barrier(0);
     };
     int i = 0;
