@@ -30,8 +30,9 @@
 // Kernel: a workgroup owns one strip (and, for narrow layers, one of
 // `splits` K ranges); its wavefronts take that range's 128-row chunks in
 // turn (wavefront w: chunks w, w + W, ...), each chunk a contiguous run of
-// bytes streamed into registers (two chunks in flight per wavefront). Lane (j, h) of an MFMA B fragment (v_mfma_f32_16x16x32_f16,
-// column j, k = 8h..8h+7 of a 32-row block) gets from its 8 bytes of the
+// bytes streamed into registers (two chunks in flight per wavefront). Lane
+// (j, h) of an MFMA B fragment (v_mfma_f32_16x16x32_f16, column j,
+// k = 8h..8h+7 of a 32-row block) gets from its 8 bytes of the
 // block both field 2g (tile 0) and field 2g+1 (tile 1) of packed column c:
 // one byte permute per row pair spreads two bytes into the two fp16 halves,
 // and one v_and_or_b32 per field makes 1024 + q (low nibble) or 1024 + 16 q
@@ -445,8 +446,8 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
   // copy the buffer at the back edge, which waits for every load in
   // flight); the last two or three chunks are finished after the loop with
   // at most one more request. No chunk is requested twice (except when a
-  // wavefront has a single chunk). More in flight per wavefront measured
-  // slower (see the layout notes).
+  // wavefront has a single chunk). More bytes in flight per wavefront
+  // (a third buffer, or eight wavefronts per workgroup) measured slower.
   {
     BChunk<kT, kGPC, kSP> ca, cb;
     load_chunk<kT, kGS, kSP, kXL, kXQ>(ca, L, chunk_of(0), xslot[0]);
