@@ -423,6 +423,7 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
   // (per-channel parameters): every group reads the one row.
   L.N = gstep * N;
   L.NP = gstep * NP;
+  const int sN = L.N, sNP = L.NP;
 
   const NibConst nc = nib_const();
   const f16x8 ones = ones_fragment<kBF>();
@@ -461,30 +462,55 @@ __attribute__((amdgpu_waves_per_eu(kW >= 8 ? kW / 4 : (kT == 1 && kSP == 1 && kG
     const lds_u8* z_lane = nullptr;
     const int kbase = split * cps;  // first chunk of the split
     if constexpr (kXL) {
+      // The token rows of x (1 KB per load: row m, bytes 1024 v ..), the
+      // unit's scale pairs ([group][32] fp16, 16 groups per load) and
+      // zero-point words ([group][4], 16 groups per load) over the K range
+      // move into LDS by DMA right behind the first weight requests. Nothing
+      // waits for them before the compute, which needs those weights anyway
+      // (register loads of the same values made the copy wait for the
+      // weights first and then start its own requests).
+      static_assert(!kXL || kSP == 1, "x is staged up front only for one-strip units");
       lds_u8* const xs = (lds_u8*)(x_dyn);
-      const int kr = cps * kBChunkRows;  // K range of the split
+      const int kr = cps * kBChunkRows;  // K range of the split (host: a multiple of 512)
       const int pitch = 2 * kr + kXLdsPad;
       const int mt = min(M, 16);
-      const int vpr = kr / 8;  // 16-byte vectors per row
-      for (int e = threadIdx.x; e < mt * vpr; e += kW * 64) {
-        const int m = e / vpr, v = e % vpr;
-        const u32x4 val = *reinterpret_cast<const u32x4*>(x + static_cast<size_t>(m) * K + kbase * kBChunkRows + 8 * v);
-        *(lds_u32x4*)(xs + m * pitch + 16 * v) = val;
-      }
-      // The unit's scales ([group][strip][32] fp16, 64 bytes per strip) and
-      // zero-point words ([group][strip][4], 16 bytes) over the K range.
       const int ngr = kr / kGS;
+      const int ngr16 = (ngr + 15) / 16 * 16;  // the tables are allocated in steps of 16 groups
       lds_u8* const sct = xs + mt * pitch;
-      lds_u8* const zt = sct + ngr * kSP * 64;
+      lds_u8* const zt = sct + ngr16 * 64;
       const int grp0 = kbase * kGPC;
-      for (int e = threadIdx.x; e < ngr * kSP * 4; e += kW * 64) {
-        const int gl = e / (kSP * 4), sp = (e / 4) % kSP, v = e % 4;
-        const u32x4 val = *reinterpret_cast<const u32x4*>(scales + static_cast<size_t>(grp0 + gl) * L.N +
-                                                          (strip + sp) * kBOut + 8 * v);
-        *(lds_u32x4*)(sct + (gl * kSP + sp) * 64 + 16 * v) = val;
-        const uint32_t zv = qz[static_cast<size_t>(grp0 + gl) * L.NP + (strip + sp) * kBStrip + v];
-        *(lds_u32*)(zt + (gl * kSP + sp) * 16 + 4 * v) = zv;
+      const int grows = gstep ? K / kGS : 1;
+      const __amdgpu_buffer_rsrc_t rsx =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), 0, M * K * 2, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rss =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(scales), 0, grows * N * 2, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rsz =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(qz), 0, grows * NP * 4, 0x00020000);
+      const int xper = kr / 512;  // 1 KB loads per row
+      const int nx = mt * xper, ns = ngr16 / 16;
+      for (int q = wave; q < nx + 2 * ns; q += kW) {
+        if (q < nx) {
+          const int m = q / xper, v = q % xper;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rsx, (lds_void*)(xs + m * pitch + 1024 * v), 16,
+              static_cast<uint32_t>(m * K + kbase * kBChunkRows + 512 * v + 8 * lane) * 2u, 0, 0, 0);
+        } else if (q < nx + ns) {
+          // groups past the range (padding, never read) may wrap to any
+          // offset: the descriptor's size turns reads past the table into 0
+          const int gl = 16 * (q - nx) + lane / 4;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rss, (lds_void*)(sct + 1024 * (q - nx)), 16,
+              (static_cast<uint32_t>(grp0 + gl) * static_cast<uint32_t>(sN) + strip * kBOut + 8 * (lane % 4)) * 2u,
+              0, 0, 0);
+        } else {
+          const int gl = 16 * (q - nx - ns) + lane / 4;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rsz, (lds_void*)(zt + 256 * (q - nx - ns)), 4,
+              (static_cast<uint32_t>(grp0 + gl) * static_cast<uint32_t>(sNP) + strip * kBStrip + lane % 4) * 4u,
+              0, 0, 0);
+        }
       }
+      wait_counts<0, 15>();
       __syncthreads();
       if (j < M) xrow = xs + j * pitch + 16 * h;
       sc_lane = sct + 16 * c + 4 * g;

@@ -41,10 +41,11 @@ __global__ __launch_bounds__(256) void w4a16_block_weights_kernel(const uint32_t
 int64_t blocked_x_lds_bytes(int64_t M, int64_t K, int64_t group, int splits, int waves, int strips_per_unit) {
   const int64_t kr = K / splits;
   const int64_t xb = std::min<int64_t>(M, 16) * (2 * kr + kXLdsPad);
-  const int64_t szb = (kr / group) * strips_per_unit * (64 + 16);
+  // the tables take whole 16-group loads
+  const int64_t szb = ((kr / group + 15) / 16 * 16) * strips_per_unit * (64 + 16);
   // x staged up front only where a unit has a single strip (several strips
-  // share the per-chunk DMA slots instead)
-  if (strips_per_unit > 1) return 0;
+  // share the per-chunk DMA slots instead), and in whole 1 KB loads per row
+  if (strips_per_unit > 1 || kr % 512) return 0;
   const int64_t red = int64_t{waves} * 16 * strips_per_unit * kBOut * 4;
   // the one-workgroup-per-strip form (8 or 16 wavefronts) stages up to 8
   // tokens: it has no stream to hold back before the copy
@@ -57,7 +58,7 @@ template <int kT, int kGS, int kSP, bool kBF>
 hipError_t launch_blocked_main(const uint16_t* x, const u32x4* qb, const uint16_t* scales, const uint32_t* qz,
                                uint16_t* y, float* part, int m, int n, int k, const GemvPlan& plan, int units,
                                XcdMap map, dim3 grid, hipStream_t stream) {
-  if constexpr (kT == 1) {
+  if constexpr (kT == 1 && kSP == 1) {  // x staged up front: one-strip units only
     const int64_t lds = blocked_x_lds_bytes(m, k, kGS, plan.splits, plan.waves, kSP);
     if (lds > 0)
       return launch_blocked_xl<kT, kGS, kSP, true, kBF>(x, qb, scales, qz, y, part, m, n, k, plan, units, map, grid,
