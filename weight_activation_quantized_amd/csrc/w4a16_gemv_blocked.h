@@ -338,9 +338,10 @@ __device__ __forceinline__ void store_unit_sums(const f32x4 (&tot)[kT][kSP][2], 
 // Three wavefronts per SIMD for the one-strip, one-tile forms with groups of
 // 64 or 128: a 24576-wide layer has three such workgroups per CU, and all of
 // them must be resident at once for every CU to stream an equal share.
-// kXL (one-tile forms): the workgroup first copies its token rows of x over
-// its K range (rows of 2 * range + 16 bytes), then its strips' scales and
-// zero-point words, into LDS (dynamic shared memory), and reads the MFMA A
+// kXL (one-tile, one-strip forms): right behind its first weight requests
+// the workgroup moves its token rows of x over its K range (rows of
+// 2 * range + 16 bytes), then its strip's scales and zero-point words, into
+// LDS (dynamic shared memory) by DMA, and reads the MFMA A
 // fragments and the group parameters from there, so the weight stream has
 // the vector-memory queue to itself (per-chunk x loads cost about 2 us and
 // the scale and zero-point loads about 0.7 us of a 13 us call at N = 24576).
