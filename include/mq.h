@@ -138,11 +138,11 @@ mq_status mq_w8a8_mm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc,
  * Source: pymllm Setup and Usage, section "W8A8 first-run JIT compilation"
  * (the per-token quantizer feeding the int8 scaled matmul) and Overview.
  * Same result, bit for bit, as mq_quant_per_token_int8 followed by
- * mq_w8a8_scaled_mm. For one token on a wide layer (M = 1, N >= 16384,
- * K <= 81904) it is one kernel: every workgroup forms the token's scale
- * itself and quantizes the row into LDS (IEEE binary32 quotient, round half
- * to even, clamp to [-127, 127]), once for the several channel tiles it
- * walks, so xq and s_tok never touch memory and the workspace is not used.
+ * mq_w8a8_scaled_mm. For one token (M = 1, K <= 12288) it is one kernel:
+ * every workgroup forms the token's scale itself and quantizes the row into
+ * LDS (IEEE binary32 quotient, round half to even, clamp to [-127, 127]),
+ * once for the channel tiles it walks, so xq and s_tok never touch memory
+ * and the workspace is not used.
  * Otherwise it runs the two kernels, with xq and s_tok in `workspace`.
  *
  *   x          [M, K] fp16   in,  16-byte aligned

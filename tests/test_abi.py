@@ -207,8 +207,8 @@ def test_kv_quant_validation(lib):
 def test_w8a8_linear_validation(lib):
     f = lib.mq_w8a8_linear
     ws = lib.mq_w8a8_linear_workspace_bytes
-    # sized for the two kernels at every M (the fused one-token path on wide
-    # layers leaves it unused)
+    # sized for the two kernels at every M (the fused one-token path, K <=
+    # 12288, leaves it unused)
     assert ws(1, 4096) >= 4096 + 4 and ws(2, 4096) >= 2 * 4096 + 2 * 4
     assert ws(3, 4096) >= 3 * 4096 + 3 * 4                # codes + scales
     assert ws(17, 4096) >= 17 * 4096 + 17 * 4
@@ -220,7 +220,7 @@ def test_w8a8_linear_validation(lib):
     assert f(A, B, C + 2, E, 4, 64, 64, None, 0, None) == ALIGN
     assert f(A, B, C, A + 16, 1, 64, 64, F, ws(1, 64), None) == ALIAS
     assert f(A, B, C, A + 16, 1, 16384, 64, None, 0, None) == ALIAS   # fused one-token form: no workspace
-    assert f(A, B, C, E, 1, 64, 64, None, 0, None) == WS              # one token, narrow layer: two kernels
+    assert f(A, B, C, E, 1, 64, 12304, None, 0, None) == WS           # one token, K > 12288: two kernels
     need = ws(32, 64)
     assert f(A, B, C, E, 32, 64, 64, None, 0, None) == WS
     assert f(A, B, C, E, 32, 64, 64, F, need - 4, None) == WS

@@ -1,8 +1,9 @@
 """W8A8_INT8 linear layer from fp16 activations (mq_w8a8_linear) on an MI355X.
 
-For one token on a wide layer (N >= 16384, the codes within 80 KB of LDS)
-the per-token quantizer runs inside the decode kernel (a capped grid walks
-the channel tiles, each workgroup forming the codes once); the result must
+For one token with K <= 12288 (the token row held in registers, two, four
+or six 16-byte chunks per thread) the per-token quantizer runs inside the
+decode kernel (a capped grid walks the channel tiles, each workgroup
+forming the codes once); the result must
 equal mq_quant_per_token_int8 followed by mq_w8a8_scaled_mm bit for bit
 (same codes, scales and int32 accumulators, same epilogue), and the oracle
 within the fp16 tolerance. Otherwise the entry point runs the two kernels
@@ -45,11 +46,13 @@ def test_w8a8_linear_matches_two_calls_and_oracle(M, K, N):
     assert_fp16_close(y, oracle.w8a8_ref(xq_ref, s_ref, wq, s_ch), f"w8a8_linear M={M} K={K} N={N}")
 
 
-@pytest.mark.parametrize("K", [81904, 65536, 4112])
+@pytest.mark.parametrize("K", [12288, 8208, 8192, 4112, 4096, 12304])
 def test_w8a8_linear_fused_long_rows(K):
-    # the fused kernel at the longest rows its LDS holds, on a wide layer;
-    # weights are random codes (not from the quantizer) so the test stays
-    # light; bit-identical to the two kernels, the oracle on sampled columns
+    # the fused kernel at the row lengths where its register count changes
+    # (K = 4096 / 8192 / 12288 the most each form holds; 12304 takes the two
+    # kernels), on a wide layer; weights are random codes (not from the
+    # quantizer) so the test stays light; bit-identical to the two kernels,
+    # the oracle on sampled columns
     N = 16384
     rng = np.random.default_rng(K)
     x = (rng.standard_normal((1, K)) * 0.25).astype(np.float16)

@@ -33,7 +33,7 @@ and two compositions used by a model's linear layer:
     w4a16_linear(x, qweight, scales, qzeros, group)  GEMV for M <= 64 (decode layout if qweight_blocked
                                                      is given), else GEMM
     w8a8_linear(x, wq, s_ch)                         quantize x (fp16 or bf16) per token, then scaled GEMM
-                                                     (one fused kernel for one token on wide layers; a workspace otherwise)
+                                                     (one fused kernel for one token, K <= 12288; a workspace otherwise)
     w8a8_linear_noalloc(x, wq, s_ch)                 the same (fp16) with the library's own scratch: no allocation
 """
 
@@ -379,7 +379,7 @@ def w4a16_linear(x, qweight, scales, qzeros, group=128, out=None, stream=None, q
 
 
 def w8a8_linear_workspace_bytes(M, K):
-    """Workspace bytes ``w8a8_linear`` needs for the two-kernel path (the one-token fused path on wide layers
+    """Workspace bytes ``w8a8_linear`` needs for the two-kernel path (the one-token fused path
     leaves it unused)."""
     return int(library().mq_w8a8_linear_workspace_bytes(M, K))
 
@@ -387,7 +387,7 @@ def w8a8_linear_workspace_bytes(M, K):
 def w8a8_linear(x, wq, s_ch, out=None, workspace=None, stream=None):
     """W8A8_INT8 linear layer from fp16 or bf16 x (y in x's dtype): per-token
     int8 quantization, then the scaled int8 GEMM (one fused kernel for one
-    token on wide layers). Bit-identical to ``w8a8_scaled_mm(*quant_per_token_int8(x), wq,
+    token, K <= 12288). Bit-identical to ``w8a8_scaled_mm(*quant_per_token_int8(x), wq,
     s_ch, out_dtype=x.dtype)``."""
     torch = _torch()
     dt = _half_dtype(x, "x")

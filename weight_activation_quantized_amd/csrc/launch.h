@@ -30,17 +30,12 @@ hipError_t launch_w8a8_gemv(const int8_t* xq, const float* s_tok, const int8_t* 
 
 // Quantizer folded into the decode kernel: y = scaled_mm(quant(x), wq, s_ch)
 // in one launch, bit-identical to the two separate calls, where
-// w8a8_use_fused(M, N, K): one token, a layer wide enough that the capped
-// grid walks several channel tiles per workgroup (N >= kW8A8FusedMinN), and
-// the codes fit a workgroup's 80 KB of LDS. Every workgroup forms the
-// token's scale and codes itself, once for all its tiles; that beats the
-// quantizer launch only when each workgroup has several tiles to amortize it
-// over (measured with the workgroup-per-row quantizer, 8B layers at one
-// token: gate_up 23.3 us fused against 25.3 us in two kernels; qkv 12.0
-// against 11.8, o_proj 9.7 against 8.8, down 21.3 against 16.4; at two
-// tokens the two kernels win or tie on every layer).
-constexpr int64_t kW8A8FusedMaxM = 1;
-constexpr int64_t kW8A8FusedMinN = 16384;
+// w8a8_use_fused(M, N, K): one token and K <= 12288 (the token row fits six
+// 16-byte chunks per thread of a 256-thread workgroup, held in registers).
+// Every workgroup forms the token's scale and codes itself, once for all
+// its tiles, while its first weight requests are in flight; that beats the
+// quantizer launch on every 8B layer at one token (two tokens: the two
+// kernels win or tie on every layer, so the fused form takes one token).
 bool w8a8_use_fused(int64_t M, int64_t N, int64_t K);
 hipError_t launch_w8a8_gemv_fused(const uint16_t* x, const int8_t* wq, const float* s_ch, uint16_t* y,
                                   int64_t M, int64_t N, int64_t K, bool bf16, hipStream_t stream);
