@@ -138,8 +138,9 @@ mq_status mq_w8a8_mm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc,
  * Source: pymllm Setup and Usage, section "W8A8 first-run JIT compilation"
  * (the per-token quantizer feeding the int8 scaled matmul) and Overview.
  * Same result, bit for bit, as mq_quant_per_token_int8 followed by
- * mq_w8a8_scaled_mm. For one token (M = 1, K <= 12288) it is one kernel:
- * every workgroup forms the token's scale itself and quantizes the row into
+ * mq_w8a8_scaled_mm. For one token with K <= 12288, two with K <= 8192,
+ * and three or four with K <= 4096 and N >= 6144 it is one kernel: every
+ * workgroup forms the tokens' scales itself and quantizes the rows into
  * LDS (IEEE binary32 quotient, round half to even, clamp to [-127, 127]),
  * once for the channel tiles it walks, so xq and s_tok never touch memory
  * and the workspace is not used.

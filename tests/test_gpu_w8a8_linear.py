@@ -1,10 +1,11 @@
 """W8A8_INT8 linear layer from fp16 activations (mq_w8a8_linear) on an MI355X.
 
-For one token with K <= 12288 (the token row held in registers, two, four
-or six 16-byte chunks per thread) the per-token quantizer runs inside the
-decode kernel (a capped grid walks the channel tiles, each workgroup
-forming the codes once); the result must
-equal mq_quant_per_token_int8 followed by mq_w8a8_scaled_mm bit for bit
+For one token with K <= 12288, two with K <= 8192 and three or four with
+K <= 4096 and N >= 6144 (the token rows held in registers, two, four or
+six 16-byte chunks per thread and row) the per-token quantizer runs inside
+the decode kernel (a capped grid walks the channel tiles, each workgroup
+forming the codes once); the result must equal mq_quant_per_token_int8
+followed by mq_w8a8_scaled_mm bit for bit
 (same codes, scales and int32 accumulators, same epilogue), and the oracle
 within the fp16 tolerance. Otherwise the entry point runs the two kernels
 through its workspace.
@@ -29,6 +30,11 @@ pytestmark = pytest.mark.gpu
                                    (2, 40000, 200), (2, 1040, 9000),
                                    (7, 272, 300), (13, 1040, 37), (16, 64, 4112),
                                    (3, 133136, 48),
+                                   # fused for 2 tokens up to K = 8192 and 3-4 tokens up to K = 4096
+                                   # with N >= 6144 (a fourth row of zeros for 3 tokens); past those,
+                                   # two kernels
+                                   (3, 1040, 6160), (3, 4096, 4096), (4, 4096, 6144), (4, 4112, 6144),
+                                   (2, 8192, 1024), (2, 8208, 64),
                                    # two kernels through the workspace
                                    (17, 512, 264), (64, 4096, 4096), (300, 1024, 640)])
 def test_w8a8_linear_matches_two_calls_and_oracle(M, K, N):

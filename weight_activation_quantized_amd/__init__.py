@@ -33,7 +33,7 @@ and two compositions used by a model's linear layer:
     w4a16_linear(x, qweight, scales, qzeros, group)  GEMV for M <= 64 (decode layout if qweight_blocked
                                                      is given), else GEMM
     w8a8_linear(x, wq, s_ch)                         quantize x (fp16 or bf16) per token, then scaled GEMM
-                                                     (one fused kernel for one token, K <= 12288; a workspace otherwise)
+                                                     (one fused kernel for 1-4 tokens, see mq.h; a workspace otherwise)
     w8a8_linear_noalloc(x, wq, s_ch)                 the same (fp16) with the library's own scratch: no allocation
 """
 
@@ -387,7 +387,7 @@ def w8a8_linear_workspace_bytes(M, K):
 def w8a8_linear(x, wq, s_ch, out=None, workspace=None, stream=None):
     """W8A8_INT8 linear layer from fp16 or bf16 x (y in x's dtype): per-token
     int8 quantization, then the scaled int8 GEMM (one fused kernel for one
-    token, K <= 12288). Bit-identical to ``w8a8_scaled_mm(*quant_per_token_int8(x), wq,
+    to four tokens, see mq.h). Bit-identical to ``w8a8_scaled_mm(*quant_per_token_int8(x), wq,
     s_ch, out_dtype=x.dtype)``."""
     torch = _torch()
     dt = _half_dtype(x, "x")

@@ -30,12 +30,11 @@ hipError_t launch_w8a8_gemv(const int8_t* xq, const float* s_tok, const int8_t* 
 
 // Quantizer folded into the decode kernel: y = scaled_mm(quant(x), wq, s_ch)
 // in one launch, bit-identical to the two separate calls, where
-// w8a8_use_fused(M, N, K): one token and K <= 12288 (the token row fits six
-// 16-byte chunks per thread of a 256-thread workgroup, held in registers).
-// Every workgroup forms the token's scale and codes itself, once for all
-// its tiles, while its first weight requests are in flight; that beats the
-// quantizer launch on every 8B layer at one token (two tokens: the two
-// kernels win or tie on every layer, so the fused form takes one token).
+// w8a8_use_fused(M, N, K): one token with K <= 12288, two with K <= 8192,
+// three or four with K <= 4096 and N >= 6144 (the token rows held in a
+// 256-thread workgroup's registers). Every workgroup forms the tokens'
+// scales and codes itself, once for all its tiles, while its first weight
+// requests are in flight, which beats the quantizer launch there.
 bool w8a8_use_fused(int64_t M, int64_t N, int64_t K);
 hipError_t launch_w8a8_gemv_fused(const uint16_t* x, const int8_t* wq, const float* s_ch, uint16_t* y,
                                   int64_t M, int64_t N, int64_t K, bool bf16, hipStream_t stream);

@@ -409,7 +409,7 @@ mq_status mq_u16_transpose(const uint16_t* src, uint16_t* dst, int64_t A, int64_
 }
 
 // The workspace does not depend on N: it is sized for the two-kernel path,
-// which every M can take (the one-kernel path for one token leaves it
+// which every M can take (the one-kernel path for 1-4 tokens leaves it
 // unused).
 size_t mq_w8a8_linear_workspace_bytes(int64_t M, int64_t K) {
   if (M < 0 || M > kMaxDim || K < 16 || K > kMaxKInt8 || K % 16 || M * K > kMaxElems || M == 0) return 0;

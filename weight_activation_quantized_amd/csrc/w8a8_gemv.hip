@@ -197,28 +197,31 @@ __device__ __forceinline__ float fused_code(float v, float s, float r) {
 // tile, 23.6 us with 1024).
 constexpr int64_t kFusedGridCap = 1024;
 
-// One token (M = 1) and the 16-channel tiles blockIdx.x, blockIdx.x +
-// gridDim.x, ... per workgroup. The token row of x is loaded into registers
-// (kXR 16-byte chunks per thread: K <= 2048 kXR, at most 12288) and the
-// first tile's first weight set is requested right behind it, so the weight
-// stream starts while the workgroup forms the scale (maximum over the
-// workgroup) and the codes (into LDS) from those registers (8B layers at
-// one token, against a prologue that read x twice before the first weight
-// request and two kernels for the narrow layers: gate_up 23.1 -> 20.1 us,
-// qkv 11.7 -> 8.2, o_proj 8.7 -> 6.2, down 15.2 -> 13.5). Per tile: as
+// Up to four tokens (kM rows, M rounded up to 1, 2 or 4) and the 16-channel
+// tiles blockIdx.x, blockIdx.x + gridDim.x, ... per workgroup. The token
+// rows of x are loaded into registers (kXR 16-byte chunks per thread and
+// row: K <= 2048 kXR) and the first tile's first weight set is requested
+// right behind them, so the weight stream starts while the workgroup forms
+// the scales (maxima over the workgroup) and the codes (into LDS) from
+// those registers (8B layers at one token, against a prologue that read x
+// twice before the first weight request and two kernels for the narrow
+// layers: gate_up 23.1 -> 20.1 us, qkv 11.7 -> 8.2, o_proj 8.7 -> 6.2, down
+// 15.2 -> 13.5; at two tokens against two kernels: gate_up 25.2 -> 19.7,
+// qkv 11.6 -> 8.8, o_proj 8.6 -> 7.1). Per tile: as
 // w8a8_gemv_kernel, with the B fragments read from LDS. The grid is capped,
 // so a wide layer's workgroups walk several tiles and form the codes once
 // for all of them.
 constexpr int kFusedMaxXR = 6;
 
-template <int kXR, bool kBf16>
+template <int kM, int kXR, bool kBf16>
 __global__ __launch_bounds__(256) void w8a8_gemv_fused_kernel(const uint16_t* __restrict__ x,
                                                               const int8_t* __restrict__ wq,
                                                               const float* __restrict__ s_ch,
-                                                              uint16_t* __restrict__ y, int N, int K) {
+                                                              uint16_t* __restrict__ y, int M, int N, int K) {
   __shared__ int32_t part[kQuarters][16][16];
-  __shared__ float s_wave[kQuarters];
-  extern __shared__ __attribute__((aligned(16))) int8_t codes[];  // K bytes (launch)
+  __shared__ float s_wave[kQuarters][kM];
+  extern __shared__ __attribute__((aligned(16))) int8_t codes[];  // kM * (K + 16) bytes (launch)
+  const int pitch = K + 16;  // token rows of codes fall on different bank groups
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -253,58 +256,68 @@ __global__ __launch_bounds__(256) void w8a8_gemv_fused_kernel(const uint16_t* __
     for (int u = 0; u < kU; ++u) {
       const int kc = wk.chunk(j0 + u, h);
       i32x4 b = i32x4{0, 0, 0, 0};
-      if (i == 0 && kc >= 0) b = *reinterpret_cast<const i32x4*>(&codes[kc]);
+      if (i < kM && kc >= 0) b = *reinterpret_cast<const i32x4*>(&codes[i * pitch + kc]);
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[u], b, acc, 0, 0, 0);
     }
   };
 
-  // The token row in registers, then the first tile's first weight set.
+  // The token rows in registers (rows M .. kM - 1 are zero: scale 0, codes
+  // 0, never stored), then the first tile's first weight set.
   const int nc = K / 8;
-  const u32x4* const row = reinterpret_cast<const u32x4*>(x);
-  u32x4 xv[kXR];
+  u32x4 xv[kM][kXR];
 #pragma unroll
-  for (int r = 0; r < kXR; ++r) {
-    const int c = threadIdx.x + 256 * r;
-    xv[r] = c < nc ? row[c] : u32x4{0u, 0u, 0u, 0u};
+  for (int m = 0; m < kM; ++m) {
+    const u32x4* const row = reinterpret_cast<const u32x4*>(x + static_cast<size_t>(m < M ? m : 0) * K);
+#pragma unroll
+    for (int r = 0; r < kXR; ++r) {
+      const int c = threadIdx.x + 256 * r;
+      xv[m][r] = (m < M && c < nc) ? row[c] : u32x4{0u, 0u, 0u, 0u};
+    }
   }
   set_tile(tile);
   issue_w(wa, 0);
   __builtin_amdgcn_sched_barrier(0);
-  // s = fl32(absmax(x) / 127) (max is exact and order-free), then the codes
-  float amax = 0.f;
+  // s = fl32(absmax(x) / 127) per row (max is exact and order-free), then
+  // the codes
+  float sm[kM];
 #pragma unroll
-  for (int r = 0; r < kXR; ++r)
+  for (int m = 0; m < kM; ++m) {
+    float amax = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      float lo, hi;
-      word_to_floats<kBf16>(xv[r][w], lo, hi);
-      amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
-    }
-  amax = wave_max(amax);
-  if (lane == 0) s_wave[wave] = amax;
+    for (int r = 0; r < kXR; ++r)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float lo, hi;
+        word_to_floats<kBf16>(xv[m][r][w], lo, hi);
+        amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
+      }
+    amax = wave_max(amax);
+    if (lane == 0) s_wave[wave][m] = amax;
+  }
   __syncthreads();
-  const float sm = fmaxf(fmaxf(s_wave[0], s_wave[1]), fmaxf(s_wave[2], s_wave[3])) / 127.0f;  // IEEE division
-  {
+#pragma unroll
+  for (int m = 0; m < kM; ++m) {
+    sm[m] = fmaxf(fmaxf(s_wave[0][m], s_wave[1][m]), fmaxf(s_wave[2][m], s_wave[3][m])) / 127.0f;  // IEEE division
     // a binary32-subnormal scale: infinite reciprocal, so fused_code divides
-    const float rc = sm < 1.17549435e-38f ? __builtin_inff() : __builtin_amdgcn_rcpf(sm);
+    const float rc = sm[m] < 1.17549435e-38f ? __builtin_inff() : __builtin_amdgcn_rcpf(sm[m]);
 #pragma unroll
     for (int r = 0; r < kXR; ++r) {
       const int c = threadIdx.x + 256 * r;
       if (c >= nc) continue;
       uint32_t packed[2] = {0u, 0u};
-      if (sm > 0.f) {
+      if (sm[m] > 0.f) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           float lo, hi;
-          word_to_floats<kBf16>(xv[r][w], lo, hi);
-          const float q0 = fminf(fmaxf(fused_code(lo, sm, rc), -127.f), 127.f);
-          const float q1 = fminf(fmaxf(fused_code(hi, sm, rc), -127.f), 127.f);
+          word_to_floats<kBf16>(xv[m][r][w], lo, hi);
+          const float q0 = fminf(fmaxf(fused_code(lo, sm[m], rc), -127.f), 127.f);
+          const float q1 = fminf(fmaxf(fused_code(hi, sm[m], rc), -127.f), 127.f);
           const uint32_t b = (static_cast<uint32_t>(static_cast<int32_t>(q0)) & 0xFFu) |
                              ((static_cast<uint32_t>(static_cast<int32_t>(q1)) & 0xFFu) << 8);
           packed[w >> 1] |= b << (16 * (w & 1));
         }
       }
-      *reinterpret_cast<u32x2*>(&codes[8 * c]) = u32x2{packed[0], packed[1]};
+      *reinterpret_cast<u32x2*>(&codes[m * pitch + 8 * c]) = u32x2{packed[0], packed[1]};
     }
   }
   __syncthreads();
@@ -327,12 +340,12 @@ __global__ __launch_bounds__(256) void w8a8_gemv_fused_kernel(const uint16_t* __
 #pragma unroll
     for (int r = 0; r < 4; ++r) part[wave][4 * h + r][i] = acc[r];
     __syncthreads();
-    if (threadIdx.x < 16) {
-      const int nl = threadIdx.x, n = n0 + nl;
-      if (n < N) {
-        const int32_t v = part[0][nl][0] + part[1][nl][0] + part[2][nl][0] + part[3][nl][0];
-        const float f = (static_cast<float>(v) * sm) * s_ch[n];
-        y[n] = half_bits<kBf16>(f);
+    if (threadIdx.x < 16 * kM) {
+      const int nl = threadIdx.x % 16, m = threadIdx.x / 16, n = n0 + nl;
+      if (m < M && n < N) {
+        const int32_t v = part[0][nl][m] + part[1][nl][m] + part[2][nl][m] + part[3][nl][m];
+        const float f = (static_cast<float>(v) * sm[m]) * s_ch[n];
+        y[static_cast<size_t>(m) * N + n] = half_bits<kBf16>(f);
       }
     }
     __syncthreads();  // the next tile rewrites part
@@ -377,7 +390,12 @@ bool w8a8_use_gemv(int64_t M, int64_t N) {
 }
 
 bool w8a8_use_fused(int64_t M, int64_t N, int64_t K) {
-  return M == 1 && N >= 1 && K <= 256 * 8 * kFusedMaxXR;
+  // Where the fused form measured faster than the quantizer and the decode
+  // kernel (8B layers at 1-4 tokens): one or two tokens on every layer whose
+  // rows fit the registers; three or four only on layers of 6144 or more
+  // channels (o_proj, 4096, at four tokens 8.9 -> 9.3 us fused).
+  return N >= 1 && ((M == 1 && K <= 256 * 8 * kFusedMaxXR) || (M == 2 && K <= 256 * 8 * 4) ||
+                    (M >= 3 && M <= 4 && K <= 256 * 8 * 2 && N >= 6144));
 }
 
 hipError_t launch_w8a8_gemv_fused(const uint16_t* x, const int8_t* wq, const float* s_ch, uint16_t* y,
@@ -386,15 +404,25 @@ hipError_t launch_w8a8_gemv_fused(const uint16_t* x, const int8_t* wq, const flo
   const int64_t tiles = (N + 15) / 16;
   const int64_t cap = kFusedGridCap;
   const dim3 grid(static_cast<uint32_t>(tiles < cap ? tiles : cap)), block(256);
-  const size_t lds = static_cast<size_t>(K);
-  const int n = static_cast<int>(N), k = static_cast<int>(K);
-  // registers for the token row: 2, 4 or 6 16-byte chunks per thread
-  auto go = [&](auto kernel) { return launch_kernel(kernel, grid, block, lds, stream, x, wq, s_ch, y, n, k); };
+  const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+  // kM token rows (M rounded up to 1, 2 or 4) of 2, 4 or 6 16-byte chunks
+  // per thread in registers, their codes in LDS
+  auto go = [&](auto kernel, int kM) {
+    return launch_kernel(kernel, grid, block, static_cast<size_t>(kM) * (K + 16), stream, x, wq, s_ch, y, m, n, k);
+  };
+  if (M > 2)  // 3 or 4 tokens, K <= 4096
+    return bf16 ? go(w8a8_gemv_fused_kernel<4, 2, true>, 4) : go(w8a8_gemv_fused_kernel<4, 2, false>, 4);
+  if (M == 2) {
+    if (K <= 2048 * 2)
+      return bf16 ? go(w8a8_gemv_fused_kernel<2, 2, true>, 2) : go(w8a8_gemv_fused_kernel<2, 2, false>, 2);
+    return bf16 ? go(w8a8_gemv_fused_kernel<2, 4, true>, 2) : go(w8a8_gemv_fused_kernel<2, 4, false>, 2);
+  }
   if (K <= 2048 * 2)
-    return bf16 ? go(w8a8_gemv_fused_kernel<2, true>) : go(w8a8_gemv_fused_kernel<2, false>);
+    return bf16 ? go(w8a8_gemv_fused_kernel<1, 2, true>, 1) : go(w8a8_gemv_fused_kernel<1, 2, false>, 1);
   if (K <= 2048 * 4)
-    return bf16 ? go(w8a8_gemv_fused_kernel<4, true>) : go(w8a8_gemv_fused_kernel<4, false>);
-  return bf16 ? go(w8a8_gemv_fused_kernel<kFusedMaxXR, true>) : go(w8a8_gemv_fused_kernel<kFusedMaxXR, false>);
+    return bf16 ? go(w8a8_gemv_fused_kernel<1, 4, true>, 1) : go(w8a8_gemv_fused_kernel<1, 4, false>, 1);
+  return bf16 ? go(w8a8_gemv_fused_kernel<1, kFusedMaxXR, true>, 1)
+              : go(w8a8_gemv_fused_kernel<1, kFusedMaxXR, false>, 1);
 }
 
 hipError_t launch_w8a8_gemv(const int8_t* xq, const float* s_tok, const int8_t* wq,
