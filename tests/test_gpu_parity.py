@@ -90,7 +90,10 @@ def _w8a8_operands(M, K, N, tag, outliers=0.01):
                                    # decode-shaped: one, two and four 16-token tiles, ragged N and K
                                    (1, 6144, 4096), (8, 4096, 12288), (17, 24576, 4096), (33, 1000, 400),
                                    (5, 130, 48), (64, 4096, 16), (16, 17, 4112), (32, 4096, 12288),
-                                   (48, 6144, 4096), (20, 6200, 272), (64, 24576, 128)])
+                                   (48, 6144, 4096), (20, 6200, 272), (64, 24576, 128),
+                                   # up to 16 tokens on 6144+ channels with the codes staged in LDS
+                                   (8, 6144, 4096), (5, 24576, 4096), (3, 6160, 12288), (16, 8192, 2048),
+                                   (9, 6144, 1024)])
 def test_w8a8_acc_bitexact(M, N, K):
     xq, _, wq, _ = _w8a8_operands(M, K, N, tag=M + N + K)
     announce(f"w8a8 i32 M={M} N={N} K={K}")

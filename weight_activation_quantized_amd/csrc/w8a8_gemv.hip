@@ -169,16 +169,131 @@ __global__ __launch_bounds__(256) void w8a8_gemv_kernel(const int8_t* __restrict
   }
 }
 
+// Workgroups of the capped-grid kernels below: a grid of at most this many
+// walks the 16-channel tiles (measured, 24576 x 4096: one token 28.5 us
+// with a workgroup per tile, 23.6 us with 1024).
+constexpr int64_t kFusedGridCap = 1024;
+
+// Up to 16 tokens with codes already formed, where they fit LDS: a
+// workgroup moves the M rows of xq into LDS by DMA once (right behind its
+// first weight set) and a capped grid walks the 16-channel tiles, so the
+// codes are read from L2 once per workgroup rather than at every k-step of
+// every tile. Otherwise as w8a8_gemv_kernel (same sums, same epilogue).
+template <bool kScaled, bool kBf16>
+__global__ __launch_bounds__(256) void w8a8_gemv_staged_kernel(const int8_t* __restrict__ xq,
+                                                               const float* __restrict__ s_tok,
+                                                               const int8_t* __restrict__ wq,
+                                                               const float* __restrict__ s_ch,
+                                                               uint16_t* __restrict__ y,
+                                                               int32_t* __restrict__ acc_out, int M, int N, int K) {
+  __shared__ int32_t part[kQuarters][16][16];
+  extern __shared__ __attribute__((aligned(16))) int8_t codes[];  // M * (K + 16) bytes (launch)
+  const int pitch = K + 16;  // token rows of codes fall on different bank groups
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = lane & 15, h = lane >> 4;
+  const int tiles = (N + 15) / 16;
+
+  Walk wk;
+  const int kq = (K / kQuarters + 63) / 64 * 64;
+  wk.k_begin = wave * kq;
+  wk.k_end = min(K, wk.k_begin + kq);
+  wk.n64 = (wk.k_end - wk.k_begin + 63) / 64;
+  constexpr int kU = 8;
+  const int sets = (wk.n64 + kU - 1) / kU;
+
+  int tile = static_cast<int>(blockIdx.x);  // < tiles: the grid is at most the tile count
+  __amdgpu_buffer_rsrc_t rw;
+  auto set_tile = [&](int t) {
+    rw = rsrc(wq + static_cast<size_t>(t) * 16 * K, static_cast<int64_t>(min(16, N - 16 * t)) * K);
+  };
+  i32x4 wa[kU], wb[kU];
+  i32x4 acc;
+  auto issue_w = [&](i32x4 (&w)[kU], int j0) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int kc = wk.chunk(j0 + u, h);
+      w[u] = __builtin_bit_cast(
+          i32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, kc >= 0 ? static_cast<uint32_t>(i * K + kc) : kOob, 0, 0));
+    }
+  };
+  auto mma = [&](const i32x4 (&w)[kU], int j0) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int kc = wk.chunk(j0 + u, h);
+      i32x4 b = i32x4{0, 0, 0, 0};
+      if (i < M && kc >= 0) b = *reinterpret_cast<const i32x4*>(&codes[i * pitch + kc]);
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[u], b, acc, 0, 0, 0);
+    }
+  };
+
+  set_tile(tile);
+  issue_w(wa, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    // 1 KB per load: row m, bytes 1024 v .. (K % 1024 == 0, host)
+    const __amdgpu_buffer_rsrc_t rx = rsrc(xq, static_cast<int64_t>(M) * K);
+    const int per = K / 1024;
+    for (int q = wave; q < M * per; q += kQuarters) {
+      const int m = q / per, v = q % per;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(codes + m * pitch + 1024 * v), 16,
+                                               static_cast<uint32_t>(m * K + 1024 * v + 16 * lane), 0, 0, 0);
+    }
+  }
+  wait_counts<0, 15>();  // the codes (and the first weight set, needed next anyway)
+  __syncthreads();
+
+  for (;;) {
+    const int n0 = tile * 16;
+    acc = i32x4{0, 0, 0, 0};
+    for (int st = 0; st < sets; st += 2) {
+      issue_w(wb, (st + 1) * kU);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(wa, st * kU);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_w(wa, (st + 2) * kU);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(wb, (st + 1) * kU);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // D[n][m]: lane (j, hh) register r holds channel 4 hh + r of token j.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[wave][4 * h + r][i] = acc[r];
+    __syncthreads();
+    for (int e = threadIdx.x; e < 16 * M; e += 256) {
+      const int nl = e % 16, m = e / 16, n = n0 + nl;
+      if (n >= N) continue;
+      const int32_t v = part[0][nl][m] + part[1][nl][m] + part[2][nl][m] + part[3][nl][m];
+      const size_t o = static_cast<size_t>(m) * N + n;
+      if constexpr (kScaled) {
+        const float f = (static_cast<float>(v) * s_tok[m]) * s_ch[n];
+        y[o] = half_bits<kBf16>(f);
+      } else {
+        acc_out[o] = v;
+      }
+    }
+    __syncthreads();  // the next tile rewrites part
+    tile += static_cast<int>(gridDim.x);
+    if (tile >= tiles) break;
+    set_tile(tile);
+    issue_w(wa, 0);
+  }
+}
+
+// Staged codes: M rows of K + 16 bytes within this much LDS (four
+// workgroups of a capped grid per CU).
+constexpr int64_t kStagedLds = 40 * 1024;
+
 // ---------------------------------------------------------------------------
-// Fused decode layer for a single token (the kernel takes M <= 16; every
-// workgroup redoes the M rows' scales and codes, which pays only at M = 1):
-// per-token quantization folded into the weight-streaming kernel (pymllm Setup and Usage, "W8A8 first-run JIT
-// compilation": the quantizer feeds the scaled matmul). Every workgroup
-// first forms s[m] = fl32(absmax(x[m,:]) / 127) for the M rows (x is small
-// and L2-resident at these M), then quantizes the x fragments it streams:
-// q = clamp(rne(fl32(x / s)), -127, 127) with the IEEE binary32 division,
-// s = 0 giving q = 0. Codes, scales, accumulators and outputs are therefore
-// bit-identical to mq_quant_per_token_int8 followed by mq_w8a8_scaled_mm.
+// Fused decode layer for one to four tokens: per-token quantization folded
+// into the weight-streaming kernel (pymllm Setup and Usage, "W8A8 first-run
+// JIT compilation": the quantizer feeds the scaled matmul). Every workgroup
+// forms s[m] = fl32(absmax(x[m,:]) / 127) for the M rows (x is small and
+// L2-resident at these M) and the codes q = clamp(rne(fl32(x / s)), -127,
+// 127) with the IEEE binary32 quotient, s = 0 giving q = 0. Codes, scales,
+// accumulators and outputs are therefore bit-identical to
+// mq_quant_per_token_int8 followed by mq_w8a8_scaled_mm.
 // ---------------------------------------------------------------------------
 
 // Codes of the IEEE binary32 quotient v / s rounded half to even, for s > 0:
@@ -191,11 +306,6 @@ __device__ __forceinline__ float fused_code(float v, float s, float r) {
   if (!(0.5f - fabsf(p - t) >= 1.0f / 4096.0f)) return rintf(v / s);  // non-finite p: divide
   return t;
 }
-
-// Workgroups of the fused kernel: a grid of at most this many walks the
-// tiles (measured, 24576 x 4096: one token 28.5 us with a workgroup per
-// tile, 23.6 us with 1024).
-constexpr int64_t kFusedGridCap = 1024;
 
 // Up to four tokens (kM rows, M rounded up to 1, 2 or 4) and the 16-channel
 // tiles blockIdx.x, blockIdx.x + gridDim.x, ... per workgroup. The token
@@ -371,6 +481,15 @@ hipError_t launch_tiles(const int8_t* xq, const float* s_tok, const int8_t* wq, 
   // (from L2): 32 channels per workgroup halves that, but only pays while
   // the grid still has about 192 or more workgroups.
   const bool wide = N >= 32 * 192;
+  // Staged codes where they measured faster (8B layers at 3-16 tokens): on
+  // layers of 6144+ channels (gate_up at 8 tokens 27.6 -> 24.3 us, qkv
+  // 12.8 -> 12.2); on 4096-channel layers 0.4-0.5 us slower.
+  if (M <= 16 && N >= 6144 && K % 1024 == 0 && static_cast<int64_t>(M) * (K + 16) <= kStagedLds) {
+    const int64_t tiles = (N + 15) / 16;
+    const dim3 grid(static_cast<uint32_t>(tiles < kFusedGridCap ? tiles : kFusedGridCap)), block(256);
+    return launch_kernel(w8a8_gemv_staged_kernel<kScaled, kBf16>, grid, block, static_cast<size_t>(M) * (K + 16),
+                         stream, xq, s_tok, wq, s_ch, y, acc, M, N, K);
+  }
   if (M <= 16) return launch_one<kScaled, 1, 1, kBf16>(xq, s_tok, wq, s_ch, y, acc, M, N, K, stream);
   if (M <= 32)
     return wide ? launch_one<kScaled, 2, 2, kBf16>(xq, s_tok, wq, s_ch, y, acc, M, N, K, stream)
