@@ -93,7 +93,7 @@ def _w8a8_operands(M, K, N, tag, outliers=0.01):
                                    (48, 6144, 4096), (20, 6200, 272), (64, 24576, 128),
                                    # up to 16 tokens on 6144+ channels with the codes staged in LDS
                                    (8, 6144, 4096), (5, 24576, 4096), (3, 6160, 12288), (16, 8192, 2048),
-                                   (9, 6144, 1024)])
+                                   (9, 6144, 1024), (16, 6144, 4096), (6, 6144, 12288)])
 def test_w8a8_acc_bitexact(M, N, K):
     xq, _, wq, _ = _w8a8_operands(M, K, N, tag=M + N + K)
     announce(f"w8a8 i32 M={M} N={N} K={K}")
