@@ -44,7 +44,11 @@ def test_quant_prefill_c2():
 
 
 @pytest.mark.parametrize("M,K", [(1, 16), (37, 272), (5, 512), (3, 4096), (2, 12288),
-                                 (3, 16384), (5, 20480), (1, 4096)])
+                                 (3, 16384), (5, 20480), (1, 4096),
+                                 # ragged rows at the row-per-workgroup forms' edges
+                                 # (256 / 512 / 1024 threads) and past 128 rows
+                                 (7, 2064), (9, 4112), (128, 12304), (4, 16368),
+                                 (129, 4096)])
 def test_quant_shapes(M, K):
     rng = np.random.default_rng(M * 100003 + K)
     x = (rng.standard_normal((M, K)) * rng.uniform(0.01, 30, size=(M, 1))).astype(np.float16)
